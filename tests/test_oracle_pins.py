@@ -1,0 +1,613 @@
+"""Pins for the CPU oracle: closed forms, invariants, worked numbers from the
+pages, library routines and finite differences.  None of these retypes the
+oracle's formulas; each is chosen so that a plausible slip (a dropped term, a
+wrong sign or index, a transposed operand) fails at least one of them."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import slt_workloads as W
+
+
+def tiny(block="llama", H=4, Hkv=4, act="f32", **kw):
+    base = dict(name="tiny", V=23, C=16, H=H, Hkv=Hkv, L=2, T=7, B=2, F=24,
+                R=16 // H, rope_mode="half", block=block, act=act,
+                tokens="uniform", scale_out=False)
+    if block == "parallel":
+        base.update(rope_mode="pairs", R=2)   # partial: 2 of head dim 4
+    base.update(kw)
+    return W.Config(**base)
+
+
+def rand_params(cfg, seed=0, std=0.3):
+    """Weights large enough that every term of the step matters; gains and
+    shifts randomised too so their gradients are exercised."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape, init in W.param_specs(cfg):
+        if init == "ones":
+            out[name] = 1.0 + 0.2 * rng.standard_normal(shape)
+        elif init == "zeros":
+            out[name] = 0.2 * rng.standard_normal(shape)
+        else:
+            out[name] = std * rng.standard_normal(shape)
+    return out
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding against a library conversion (torch, fp32 -> bfloat16 RNE)
+# --------------------------------------------------------------------------
+def test_bf16_round_matches_torch_conversion():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2 ** 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
+    # ties: low 16 bits exactly 0x8000, both parities of bit 16
+    ties = (rng.integers(0, 2 ** 16, size=20000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    special = np.array([0, 0x80000000, 0x00000001, 0x007FFFFF, 0x00800000, 0x7F7FFFFF,
+                        0x7F7F8000, 0x7F7F7FFF, 0xFF7FFFFF, 0x3F808000, 0x3F818000], np.uint32)
+    bits = np.concatenate([bits, ties, special])
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    got = O.bf16_round(f.astype(np.float64))
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), (f[~same][:5], got[~same][:5], ref[~same][:5])
+
+
+def test_bf16_round_ties_to_even_worked_values():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties go to the even one (1).
+    assert O.bf16_round(1.0 + 2.0 ** -8) == 1.0
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even).
+    assert O.bf16_round(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert O.bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+
+
+# --------------------------------------------------------------------------
+# Parameter counts printed on the Hephaistos page ("What you'll see": 1,049,216
+# for 4L/4H/C128/V1024; "The bigger run": 15.74M for 8L/8H/C384/V2048).
+# --------------------------------------------------------------------------
+def test_param_counts_match_hephaistos_page():
+    small = W.Config("h", V=1024, C=128, H=4, Hkv=4, L=4, T=64, B=1, F=(8 * 128) // 3, R=32,
+                     rope_mode="half", block="llama", act="f32", tokens="uniform", scale_out=False)
+    assert W.n_params(small) == 1049216
+    big = small.with_(V=2048, C=384, H=8, Hkv=8, L=8, T=256, F=(8 * 384) // 3, R=48)
+    assert round(W.n_params(big) / 1e6, 2) == 15.74
+
+
+def test_config_param_counts():
+    assert [W.n_params(c) for c in W.CONFIGS] == [3952, 4974848, 17308032, 245924864, 356558848]
+
+
+# --------------------------------------------------------------------------
+# Finite-difference gradient checks at float64 (Hephaistos, "Why it's
+# interesting" / "Tests": every parameter tensor against central differences;
+# strata: f64 gradcheck of every backward rule)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("family", ["llama_mha", "llama_gqa", "parallel_partial_rope"])
+def test_full_model_gradcheck_every_tensor(family):
+    cfg = {"llama_mha": tiny(), "llama_gqa": tiny(H=4, Hkv=2),
+           "parallel_partial_rope": tiny(block="parallel")}[family]
+    params = rand_params(cfg, seed=3)
+    tokens = np.random.default_rng(4).integers(0, cfg.V, size=(cfg.B, cfg.T + 1))
+    loss, cache = O.forward(cfg, params, tokens)
+    grads = O.backward(cfg, cache)
+    assert set(grads) == set(params)
+    rng = np.random.default_rng(5)
+    h = 1e-6
+    worst = 0.0
+    for name, p in params.items():
+        flat = p.reshape(-1)
+        idx = rng.choice(flat.size, size=min(6, flat.size), replace=False)
+        if name == "wte":   # include rows that occur in the batch
+            idx = np.concatenate([idx, tokens[0, :3] * cfg.C])
+        for i in idx:
+            old = flat[i]
+            flat[i] = old + h
+            lp, _ = O.forward(cfg, params, tokens)
+            flat[i] = old - h
+            lm, _ = O.forward(cfg, params, tokens)
+            flat[i] = old
+            num = (lp - lm) / (2 * h)
+            ana = grads[name].reshape(-1)[i]
+            # central differences carry ~eps*|loss|/h = 3e-10 of rounding noise
+            err = abs(ana - num) / max(abs(ana), abs(num), 1e-4)
+            worst = max(worst, err)
+            assert err < 1e-5, (name, i, ana, num)
+    assert worst < 1e-5
+
+
+def test_cross_entropy_gradcheck():
+    rng = np.random.default_rng(0)
+    z = rng.standard_normal((5, 7)) * 2
+    y = rng.integers(0, 7, 5)
+    _, dz, _ = O.cross_entropy(z, y)
+    h = 1e-6
+    for i in range(5):
+        for j in range(7):
+            zp, zm = z.copy(), z.copy()
+            zp[i, j] += h
+            zm[i, j] -= h
+            num = (O.cross_entropy(zp, y)[0] - O.cross_entropy(zm, y)[0]) / (2 * h)
+            assert abs(num - dz[i, j]) < 1e-8
+
+
+# --------------------------------------------------------------------------
+# Cross-check against an independent torch float64 autograd model (strata,
+# rules: PyTorch allowed as a test oracle).  Library softmax, silu, gelu(tanh)
+# and cross_entropy; autograd instead of hand-written backward.
+# --------------------------------------------------------------------------
+def torch_reference(cfg, params, tokens):
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    P = {k: torch.tensor(np.asarray(v, np.float64), requires_grad=True) for k, v in params.items()}
+    tok = torch.tensor(np.asarray(tokens, np.int64))
+    B, T = tok.shape[0], tok.shape[1] - 1
+    C, H, Hkv = cfg.C, cfg.H, cfg.Hkv
+    d = C // H
+    R = cfg.R
+    pos = torch.arange(T, dtype=torch.float64)
+    inv = cfg.base ** (-torch.arange(0, R, 2, dtype=torch.float64) / R)
+    ang = pos[:, None] * inv[None, :]
+    cs, sn = torch.cos(ang), torch.sin(ang)
+
+    def rope(u):  # u [B, nh, T, d]; rotate as complex numbers
+        if cfg.rope_mode == "half":
+            re, im = u[..., :R // 2], u[..., R // 2:R]
+        else:
+            re, im = u[..., 0:R:2], u[..., 1:R:2]
+        zc = torch.complex(re, im) * torch.polar(torch.ones_like(ang), ang)
+        if cfg.rope_mode == "half":
+            rot = torch.cat([zc.real, zc.imag], dim=-1)
+        else:
+            rot = torch.stack([zc.real, zc.imag], dim=-1).flatten(-2)
+        return torch.cat([rot, u[..., R:]], dim=-1)
+
+    def rms(x, g):
+        return x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + cfg.eps) * g
+
+    def ln(x, g, b):
+        return F.layer_norm(x, (C,), g, b, cfg.eps)
+
+    def attn(n, w):
+        qkv = n @ w.T
+        q = qkv[..., :H * d].reshape(B, T, H, d).transpose(1, 2)
+        k = qkv[..., H * d:(H + Hkv) * d].reshape(B, T, Hkv, d).transpose(1, 2)
+        v = qkv[..., (H + Hkv) * d:].reshape(B, T, Hkv, d).transpose(1, 2)
+        q, k = rope(q), rope(k)
+        k = k.repeat_interleave(H // Hkv, dim=1)
+        v = v.repeat_interleave(H // Hkv, dim=1)
+        s = (q @ k.transpose(-1, -2)) / math.sqrt(d)
+        s = s.masked_fill(~torch.ones(T, T, dtype=torch.bool).tril(), float("-inf"))
+        o = torch.softmax(s, dim=-1) @ v
+        return o.transpose(1, 2).reshape(B, T, H * d)
+
+    x = P["wte"][tok[:, :T]]
+    for l in range(cfg.L):
+        p = f"h{l}."
+        if cfg.block == "llama":
+            x = x + attn(rms(x, P[p + "attn_norm"]), P[p + "qkvw"]) @ P[p + "w_o"].T
+            n = rms(x, P[p + "mlp_norm"])
+            x = x + (F.silu(n @ P[p + "w1"].T) * (n @ P[p + "w3"].T)) @ P[p + "w2"].T
+        else:
+            n = ln(x, P[p + "ln_g"], P[p + "ln_b"])
+            a = F.gelu(n @ P[p + "fc_in"].T, approximate="tanh")
+            x = x + torch.cat([attn(n, P[p + "qkvw"]), a], dim=-1) @ P[p + "w_out"].T
+    nf = rms(x, P["norm_f"]) if cfg.block == "llama" else ln(x, P["lnf_g"], P["lnf_b"])
+    z = nf @ P["lm_head"].T
+    loss = F.cross_entropy(z.reshape(-1, cfg.V), tok[:, 1:].reshape(-1))
+    loss.backward()
+    return float(loss.detach()), {k: v.grad.numpy() for k, v in P.items()}
+
+
+@pytest.mark.parametrize("family", ["cfg1", "llama_gqa", "parallel_partial_rope", "cfg2_small_batch"])
+def test_oracle_matches_torch_autograd(family):
+    if family == "cfg1":
+        cfg = W.get_config(1)
+    elif family == "llama_gqa":
+        cfg = tiny(H=8, Hkv=2, C=32, T=12, L=2)
+    elif family == "parallel_partial_rope":
+        cfg = tiny(block="parallel", C=32, H=4, R=4, T=12)
+    else:
+        cfg = W.get_config(2).with_(B=2, T=64, L=2)
+    params = rand_params(cfg, seed=11, std=0.1)
+    tokens = np.random.default_rng(12).integers(0, cfg.V, size=(cfg.B, cfg.T + 1))
+    loss, cache = O.forward(cfg, params, tokens)
+    grads = O.backward(cfg, cache)
+    tloss, tgrads = torch_reference(cfg, params, tokens)
+    assert abs(loss - tloss) <= 1e-12 * abs(tloss)
+    for k in params:
+        err = np.linalg.norm(grads[k] - tgrads[k]) / max(np.linalg.norm(tgrads[k]), 1e-300)
+        assert err < 1e-10, (k, err)
+
+
+# --------------------------------------------------------------------------
+# Closed forms of the whole step
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("block", ["llama", "parallel"])
+def test_zero_head_gives_ln_v_and_zero_lower_gradients(block):
+    cfg = tiny(block=block)
+    params = rand_params(cfg, seed=7)
+    params["lm_head"][:] = 0.0
+    tokens = np.random.default_rng(8).integers(0, cfg.V, size=(cfg.B, cfg.T + 1))
+    loss, cache = O.forward(cfg, params, tokens)
+    assert loss == pytest.approx(math.log(cfg.V), rel=1e-15, abs=0)
+    N = cfg.B * cfg.T
+    expect = np.full((N, cfg.V), 1.0 / cfg.V)
+    expect[np.arange(N), tokens[:, 1:].reshape(-1)] -= 1.0
+    np.testing.assert_allclose(cache["dz"], expect / N, rtol=1e-14, atol=1e-17)
+    grads = O.backward(cfg, cache)
+    for k, g in grads.items():
+        if k != "lm_head":
+            assert np.all(g == 0.0), k
+    assert np.linalg.norm(grads["lm_head"]) > 0
+
+
+def test_identity_blocks_reduce_to_closed_form_bigram():
+    """With zero output projections each block is the identity; with one-hot
+    embeddings of size alpha and lm_head = beta * I the logits are
+    s * e_x with s = alpha * beta / sqrt(alpha^2 / C + eps), so the loss of a
+    position is log(e^s + V - 1) - s [y == x]."""
+    V = C = 16
+    cfg = tiny(V=V, C=C)
+    params = rand_params(cfg, seed=2)
+    for l in range(cfg.L):
+        params[f"h{l}.w_o"][:] = 0.0
+        params[f"h{l}.w2"][:] = 0.0
+    params["norm_f"][:] = 1.0
+    alpha, beta = 1.7, 0.9
+    params["wte"] = alpha * np.eye(V)
+    params["lm_head"] = beta * np.eye(V)
+    tokens = np.random.default_rng(3).integers(0, V, size=(cfg.B, cfg.T + 1))
+    tokens[0, 1] = tokens[0, 0]     # make sure some targets equal their inputs
+    loss, _ = O.forward(cfg, params, tokens)
+    s = alpha * beta / math.sqrt(alpha ** 2 / C + cfg.eps)
+    x, y = tokens[:, :-1].reshape(-1), tokens[:, 1:].reshape(-1)
+    per = np.log(np.exp(s) + V - 1) - s * (x == y)
+    assert loss == pytest.approx(per.mean(), rel=1e-14)
+
+
+@pytest.mark.parametrize("block,H,Hkv", [("llama", 4, 4), ("llama", 4, 2), ("parallel", 4, 4)])
+def test_prefix_forward_gate(block, H, Hkv):
+    """strata rule: a decoder fed a prefix must reproduce the full forward's
+    rows for that prefix (the cache-free form of the KV-cache gate); this
+    pins causality and absolute positions starting at 0."""
+    cfg = tiny(block=block, H=H, Hkv=Hkv, T=9, B=1)
+    params = rand_params(cfg, seed=21)
+    tokens = np.random.default_rng(22).integers(0, cfg.V, size=(1, cfg.T + 1))
+    _, full = O.forward(cfg, params, tokens)
+    for i in range(cfg.T):
+        _, pre = O.forward(cfg, params, tokens[:, :i + 2])
+        np.testing.assert_allclose(pre["z"][-1], full["z"][i], rtol=1e-12, atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    """strata, "GPT-2 to modern": one attention op with independent n_head and
+    n_kv_head; GQA is MHA whose KV heads are shared.  Forward equal; the GQA
+    gradient of a KV row is the sum over its copies."""
+    g = tiny(H=4, Hkv=2, T=6)
+    m = tiny(H=4, Hkv=4, T=6)
+    d = g.C // g.H
+    pg = rand_params(g, seed=31)
+    pm = {k: v.copy() for k, v in pg.items() if not k.endswith("qkvw")}
+    for l in range(g.L):
+        w = pg[f"h{l}.qkvw"]
+        q = w[:g.H * d]
+        k = w[g.H * d:(g.H + g.Hkv) * d].reshape(g.Hkv, d, g.C)
+        v = w[(g.H + g.Hkv) * d:].reshape(g.Hkv, d, g.C)
+        rep = g.H // g.Hkv
+        pm[f"h{l}.qkvw"] = np.concatenate([q, np.repeat(k, rep, 0).reshape(-1, g.C),
+                                           np.repeat(v, rep, 0).reshape(-1, g.C)])
+    tokens = np.random.default_rng(32).integers(0, g.V, size=(g.B, g.T + 1))
+    lg, cg = O.forward(g, pg, tokens)
+    lm, cm = O.forward(m, pm, tokens)
+    assert lg == pytest.approx(lm, rel=1e-13)
+    gg, gm = O.backward(g, cg), O.backward(m, cm)
+    for l in range(g.L):
+        a = gg[f"h{l}.qkvw"]
+        b = gm[f"h{l}.qkvw"]
+        rep = g.H // g.Hkv
+        np.testing.assert_allclose(a[:g.H * d], b[:g.H * d], rtol=1e-10, atol=1e-14)
+        for part in range(2):
+            sa = a[(g.H + part * g.Hkv) * d:(g.H + (part + 1) * g.Hkv) * d].reshape(g.Hkv, d, g.C)
+            sb = b[(g.H + part * g.H) * d:(g.H + (part + 1) * g.H) * d].reshape(g.Hkv, rep, d, g.C)
+            np.testing.assert_allclose(sa, sb.sum(1), rtol=1e-10, atol=1e-14)
+
+
+def test_initial_loss_close_to_ln_vocab():
+    """Hephaistos, "What you'll see": untrained loss ~ ln V (6.9847 vs 6.9315);
+    strata lab 01: 3.1126 vs 3.1355.  With N(0, 0.02) weights the excess is
+    about 2e-4 * C."""
+    cfg = W.get_config(1)
+    params = W.make_params(cfg, 1001)
+    tokens = W.make_tokens(cfg, 1001)
+    loss, _ = O.forward(cfg, params, tokens)
+    assert abs(loss - math.log(cfg.V)) < 0.05
+
+
+# --------------------------------------------------------------------------
+# Norms
+# --------------------------------------------------------------------------
+def test_rmsnorm_worked_value_and_invariants():
+    x = np.array([[3.0, 4.0]])
+    y, r = O.rmsnorm_fwd(x, np.ones(2), 1e-5)
+    assert r[0] == pytest.approx(1.0 / math.sqrt(12.5 + 1e-5), rel=1e-15)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((6, 32)) * 3
+    y, r = O.rmsnorm_fwd(x, np.ones(32), 1e-5)
+    ms = np.mean(x * x, 1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, 1)), np.sqrt(ms / (ms + 1e-5)), rtol=1e-13)
+    y0, _ = O.rmsnorm_fwd(x, np.ones(32), 0.0)
+    y1, _ = O.rmsnorm_fwd(7.5 * x, np.ones(32), 0.0)
+    np.testing.assert_allclose(y0, y1, rtol=1e-13)
+    g = rng.standard_normal(32)
+    _, r0 = O.rmsnorm_fwd(x, g, 0.0)
+    dx, _ = O.rmsnorm_bwd(x, g, r0, rng.standard_normal((6, 32)))
+    np.testing.assert_allclose(np.sum(x * dx, 1), 0.0, atol=1e-12)
+
+
+def test_layernorm_invariants():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 24)) * 2 + 3
+    gm, bt = np.ones(24), np.zeros(24)
+    y, mu, r = O.layernorm_fwd(x, gm, bt, 1e-5)
+    np.testing.assert_allclose(y.mean(1), 0.0, atol=1e-13)
+    var = ((x - x.mean(1, keepdims=True)) ** 2).mean(1)
+    np.testing.assert_allclose((y * y).mean(1), var / (var + 1e-5), rtol=1e-12)
+    y2, _, _ = O.layernorm_fwd(x + 11.0, gm, bt, 1e-5)
+    np.testing.assert_allclose(y, y2, rtol=1e-9, atol=1e-12)
+    g = rng.standard_normal(24)
+    _, mu0, r0 = O.layernorm_fwd(x, g, bt, 0.0)
+    dx, _, dbeta = O.layernorm_bwd(x, g, mu0, r0, rng.standard_normal((5, 24)))
+    np.testing.assert_allclose(dx.sum(1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(np.sum(x * dx, 1), 0.0, atol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# RoPE
+# --------------------------------------------------------------------------
+def test_rope_worked_angles():
+    # R = 2: theta_0 = 1, so position 1 turns (1, 0) into (cos 1, sin 1).
+    cos, sin = O.rope_tables(3, 2, 10000.0)
+    u = np.zeros((3, 2))
+    u[:, 0] = 1.0
+    out = O.rope_apply(u, cos, sin, 2, "half")
+    np.testing.assert_allclose(out[1], [math.cos(1.0), math.sin(1.0)], rtol=1e-15)
+    np.testing.assert_allclose(out[2], [math.cos(2.0), math.sin(2.0)], rtol=1e-15)
+    # R = 4: theta_1 = 10000^(-1/2) = 0.01; position 100 turns pair 1 by 1 rad.
+    cos, sin = O.rope_tables(101, 4, 10000.0)
+    u = np.zeros((101, 4))
+    u[:, 1] = 1.0      # rotate-half: pair 1 is dims (1, 3)
+    out = O.rope_apply(u, cos, sin, 4, "half")
+    np.testing.assert_allclose(out[100, [1, 3]], [math.cos(1.0), math.sin(1.0)], rtol=1e-12)
+    np.testing.assert_allclose(out[100, [0, 2]], 0.0, atol=0)
+    v = np.zeros((101, 4))
+    v[:, 2] = 1.0      # even-odd: pair 1 is dims (2, 3)
+    out = O.rope_apply(v, cos, sin, 4, "pairs")
+    np.testing.assert_allclose(out[100, [2, 3]], [math.cos(1.0), math.sin(1.0)], rtol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["half", "pairs"])
+def test_rope_invariants(mode):
+    T, d = 12, 8
+    cos, sin = O.rope_tables(T, d, 10000.0)
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    rq = O.rope_apply(q, cos, sin, d, mode)
+    np.testing.assert_allclose(rq[0], q[0], rtol=0, atol=0)                 # R_0 = I
+    np.testing.assert_allclose(np.linalg.norm(rq, axis=1), np.linalg.norm(q, axis=1), rtol=1e-14)
+    # strata: <R_i q, R_j k> depends only on i - j
+    qq = np.repeat(q[:1], T, 0)
+    kk = np.repeat(k[:1], T, 0)
+    a = O.rope_apply(qq, cos, sin, d, mode)
+    b = O.rope_apply(kk, cos, sin, d, mode)
+    for i, j, s in [(5, 2, 4), (7, 7, 3), (3, 9, 2)]:
+        assert a[i] @ b[j] == pytest.approx(a[i + s] @ b[j + s], rel=1e-12)
+    back = O.rope_apply(rq, cos, sin, d, mode, inverse=True)
+    np.testing.assert_allclose(back, q, rtol=1e-13, atol=1e-14)
+
+
+def test_rope_rotate_half_equals_interleaved_after_permutation():
+    """Hephaistos, GGUF export: rotate-half and interleaved layouts differ by a
+    fixed permutation of each head's q/k rows."""
+    T, d = 10, 8
+    cos, sin = O.rope_tables(T, d, 10000.0)
+    u = np.random.default_rng(3).standard_normal((T, d))
+    perm = np.empty(d, int)
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2
+    np.testing.assert_allclose(O.rope_apply(u, cos, sin, d, "half")[:, perm],
+                               O.rope_apply(u[:, perm], cos, sin, d, "pairs"), rtol=1e-15)
+
+
+def test_partial_rope_leaves_tail_and_full_case():
+    T, d = 6, 8
+    u = np.random.default_rng(4).standard_normal((T, d))
+    cos, sin = O.rope_tables(T, 4, 10000.0)
+    out = O.rope_apply(u, cos, sin, 4, "pairs")
+    np.testing.assert_array_equal(out[:, 4:], u[:, 4:])
+    np.testing.assert_allclose(out[:, :4], O.rope_apply(u[:, :4], cos, sin, 4, "pairs"), rtol=0)
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+def test_attention_two_position_closed_form():
+    """Row 1 of a causal 2-position attention mixes v0 and v1 with weights
+    sigmoid(s10 - s11), sigmoid(s11 - s10), s = q.k / sqrt(d); row 0 is v0."""
+    rng = np.random.default_rng(5)
+    d = 4
+    q = rng.standard_normal((1, 1, 2, d))
+    k = rng.standard_normal((1, 1, 2, d))
+    v = rng.standard_normal((1, 1, 2, d))
+    o, lse = O.attention_fwd(q, k, v)
+    s10 = q[0, 0, 1] @ k[0, 0, 0] / 2.0
+    s11 = q[0, 0, 1] @ k[0, 0, 1] / 2.0
+    w0 = 1.0 / (1.0 + math.exp(s11 - s10))
+    np.testing.assert_allclose(o[0, 0, 0], v[0, 0, 0], rtol=1e-15)
+    np.testing.assert_allclose(o[0, 0, 1], w0 * v[0, 0, 0] + (1 - w0) * v[0, 0, 1], rtol=1e-13)
+    assert lse[0, 0, 1] == pytest.approx(math.log(math.exp(s10) + math.exp(s11)), rel=1e-14)
+
+
+def test_attention_zero_query_is_prefix_mean():
+    rng = np.random.default_rng(6)
+    B, H, T, d = 2, 3, 9, 4
+    v = rng.standard_normal((B, H, T, d))
+    o, _ = O.attention_fwd(np.zeros((B, H, T, d)), rng.standard_normal((B, H, T, d)), v)
+    expect = np.cumsum(v, axis=2) / np.arange(1, T + 1)[None, None, :, None]
+    np.testing.assert_allclose(o, expect, rtol=1e-13)
+
+
+def test_attention_backward_finite_differences():
+    rng = np.random.default_rng(7)
+    B, H, Hkv, T, d = 1, 4, 2, 5, 4
+    q = rng.standard_normal((B, H, T, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    w = rng.standard_normal((B, H, T, d))
+    dq, dk, dv = O.attention_bwd(q, k, v, w)
+    h = 1e-6
+    for arr, grad in [(q, dq), (k, dk), (v, dv)]:
+        for _ in range(6):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            old = arr[idx]
+            arr[idx] = old + h
+            fp = np.sum(O.attention_fwd(q, k, v)[0] * w)
+            arr[idx] = old - h
+            fm = np.sum(O.attention_fwd(q, k, v)[0] * w)
+            arr[idx] = old
+            assert (fp - fm) / (2 * h) == pytest.approx(grad[idx], rel=1e-6, abs=1e-9)
+
+
+def test_online_softmax_tiled_attention_equals_materialized():
+    """strata: flash-style attention (online softmax over key blocks) matches
+    the materialized softmax.  The tiled loop is written here, independent of
+    the oracle's one-shot softmax."""
+    rng = np.random.default_rng(8)
+    T, d, blk = 37, 8, 5
+    q, k, v = (rng.standard_normal((T, d)) * 2 for _ in range(3))
+    out = np.zeros((T, d))
+    for i in range(T):
+        m, l, acc = -np.inf, 0.0, np.zeros(d)
+        for j0 in range(0, i + 1, blk):
+            js = np.arange(j0, min(j0 + blk, i + 1))
+            s = k[js] @ q[i] / math.sqrt(d)
+            m_new = max(m, s.max())
+            corr = math.exp(m - m_new) if np.isfinite(m) else 0.0
+            e = np.exp(s - m_new)
+            l = l * corr + e.sum()
+            acc = acc * corr + e @ v[js]
+            m = m_new
+        out[i] = acc / l
+    o, _ = O.attention_fwd(q[None, None], k[None, None], v[None, None])
+    np.testing.assert_allclose(o[0, 0], out, rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# MLP activations
+# --------------------------------------------------------------------------
+def test_swiglu_values():
+    assert O.swiglu_fwd(1.0, 1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert O.swiglu_fwd(0.0, 5.0) == 0.0
+    da, db = O.swiglu_bwd(np.array([0.0]), np.array([1.0]), np.array([1.0]))
+    assert da[0] == pytest.approx(0.5) and db[0] == 0.0
+    a = np.random.default_rng(9).standard_normal(50)
+    da, db = O.swiglu_bwd(a, np.zeros(50), np.ones(50))
+    assert np.all(da == 0.0) and np.all(O.swiglu_fwd(a, np.zeros(50)) == 0.0)
+    b = np.random.default_rng(10).standard_normal(50)
+    h = 1e-6
+    num_a = (O.swiglu_fwd(a + h, b) - O.swiglu_fwd(a - h, b)) / (2 * h)
+    num_b = (O.swiglu_fwd(a, b + h) - O.swiglu_fwd(a, b - h)) / (2 * h)
+    da, db = O.swiglu_bwd(a, b, np.ones(50))
+    np.testing.assert_allclose(da, num_a, rtol=1e-7, atol=1e-9)
+    np.testing.assert_allclose(db, num_b, rtol=1e-7, atol=1e-9)
+
+
+def test_gelu_against_library_and_erf_form():
+    torch = pytest.importorskip("torch")
+    a = np.linspace(-6, 6, 1001)
+    ref = torch.nn.functional.gelu(torch.tensor(a), approximate="tanh").numpy()
+    np.testing.assert_allclose(O.gelu_fwd(a), ref, rtol=1e-13, atol=1e-15)
+    phi = np.array([0.5 * (1 + math.erf(x / math.sqrt(2))) for x in a])
+    assert np.max(np.abs(O.gelu_fwd(a) - a * phi)) < 1e-3
+    h = 1e-6
+    np.testing.assert_allclose(O.gelu_bwd(a, np.ones_like(a)),
+                               (O.gelu_fwd(a + h) - O.gelu_fwd(a - h)) / (2 * h), rtol=1e-7, atol=1e-9)
+    assert O.gelu_bwd(np.array([0.0]), np.array([1.0]))[0] == pytest.approx(0.5)
+
+
+# --------------------------------------------------------------------------
+# Cross-entropy
+# --------------------------------------------------------------------------
+def test_cross_entropy_worked_values():
+    loss, dz, lse = O.cross_entropy(np.array([[0.0, math.log(3.0)]]), np.array([0]))
+    assert loss == pytest.approx(math.log(4.0), rel=1e-15)
+    np.testing.assert_allclose(dz, [[0.25 - 1.0, 0.75]], rtol=1e-15)
+    z = np.random.default_rng(11).standard_normal((7, 13)) * 4
+    loss, dz, _ = O.cross_entropy(z, np.arange(7))
+    np.testing.assert_allclose(dz.sum(1), 0.0, atol=1e-16)
+    loss2, _, _ = O.cross_entropy(z + 100.0, np.arange(7))
+    assert loss2 == pytest.approx(loss, rel=1e-13)
+    assert O.cross_entropy(np.zeros((3, 27)), np.array([1, 2, 3]))[0] == pytest.approx(math.log(27), rel=1e-15)
+
+
+# --------------------------------------------------------------------------
+# AdamW
+# --------------------------------------------------------------------------
+def test_adamw_first_steps_closed_forms():
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.999, 1e-8, 0.1
+    th0 = np.array([0.5, -0.25, 0.0, 1.0])
+    g1 = np.array([0.3, -2.0, 1e-3, 0.0])
+    th1, m1, v1 = O.adamw(th0, g1, 0, 0, 1, lr, b1, b2, eps, wd)
+    # at t = 1 bias correction makes m_hat = g and v_hat = g^2
+    np.testing.assert_allclose(th1, th0 - lr * (g1 / (np.abs(g1) + eps) + wd * th0), rtol=1e-14)
+    np.testing.assert_allclose(m1, 0.1 * g1, rtol=1e-15)
+    np.testing.assert_allclose(v1, 0.001 * g1 ** 2, rtol=1e-14)
+    assert th1[3] == th0[3] * (1 - lr * wd)        # g = 0: pure decay
+    g2 = np.array([-0.1, 1.0, 2e-3, 0.5])
+    th2, _, _ = O.adamw(th1, g2, m1, v1, 2, lr, b1, b2, eps, wd)
+    mh = (0.09 * g1 + 0.1 * g2) / 0.19
+    vh = (0.000999 * g1 ** 2 + 0.001 * g2 ** 2) / 0.001999
+    np.testing.assert_allclose(th2, th1 - lr * (mh / (np.sqrt(vh) + eps) + wd * th1), rtol=1e-12)
+    thm, _, _ = O.adamw(th0, g1, 0, 0, 1, lr, b1, b2, eps, wd, decay=np.array([0, 1, 0, 1]))
+    np.testing.assert_allclose(thm[0], th0[0] - lr * g1[0] / (abs(g1[0]) + eps), rtol=1e-14)
+
+
+def test_adamw_converges_on_quadratic():
+    """strata: AdamW converges on a quadratic."""
+    c = np.array([1.0, -2.0, 0.5, 3.0])
+    th = np.zeros(4)
+    m = v = np.zeros(4)
+    for t in range(1, 3001):
+        th, m, v = O.adamw(th, th - c, m, v, t, 1e-2, 0.9, 0.999, 1e-8, 0.0)
+    np.testing.assert_allclose(th, c, atol=1e-3)
+
+
+# --------------------------------------------------------------------------
+# Embedding
+# --------------------------------------------------------------------------
+def test_embedding_backward_unseen_rows_and_repeats():
+    rng = np.random.default_rng(12)
+    ids = np.array([3, 3, 3, 5, 3])
+    dx = rng.standard_normal((5, 6))
+    g = O.embedding_bwd(dx, ids, 8)
+    np.testing.assert_allclose(g[3], dx[[0, 1, 2, 4]].sum(0), rtol=1e-15)
+    np.testing.assert_array_equal(g[5], dx[3])
+    assert np.all(g[[0, 1, 2, 4, 6, 7]] == 0.0)
+
+
+# --------------------------------------------------------------------------
+# bf16 storage emulation: the rounded forward stays close to the exact one
+# --------------------------------------------------------------------------
+def test_bf16_forward_close_to_exact():
+    cfg = tiny(act="bf16", C=32, H=4, R=8)
+    params = rand_params(cfg, seed=41, std=0.1)
+    tokens = np.random.default_rng(42).integers(0, cfg.V, size=(cfg.B, cfg.T + 1))
+    lb, cb = O.forward(cfg, params, tokens)
+    lf, cf = O.forward(cfg.with_(act="f32"), params, tokens)
+    assert abs(lb - lf) < 1e-2 * lf
+    assert lb != lf
+    gb, gf = O.backward(cfg, cb), O.backward(cfg.with_(act="f32"), cf)
+    for k in gf:
+        assert np.linalg.norm(gb[k] - gf[k]) <= 0.05 * np.linalg.norm(gf[k]) + 1e-12, k
