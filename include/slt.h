@@ -1,0 +1,283 @@
+/*
+ * slt.h - C ABI of the MI355X (gfx950) training-step library for a small
+ * bias-free decoder: token embedding, per block norm / RoPE causal attention
+ * (MHA or GQA) / MLP, final norm, untied lm_head, cross-entropy, the
+ * hand-written backward and AdamW.
+ *
+ * Sources (page title, section):
+ *   Hephaistos, "Architecture at a glance": the Llama block
+ *     x + Attn(RMSNorm(x)), then x + SwiGLU(RMSNorm(x)); RoPE on q and k;
+ *     causal attention with a stable softmax; SwiGLU (silu(x W1) * x W3) W2;
+ *     untied lm_head; AdamW with decoupled decay and bias correction.
+ *   Hephaistos, "Design notes": one flat parameter buffer and one activation
+ *     arena, each tensor addressed by (offset, length); the forward caches
+ *     what the backward needs; the backward is a reverse walk.
+ *   strata, capability tables: the matmul family A.B, A.B^T, A^T.B; backward
+ *     rules for matmul, LayerNorm, RMSNorm, GELU, SiLU, embedding,
+ *     cross-entropy and causal attention taking n_head and n_kv_head
+ *     independently with optional RoPE; the compile-time planner of parameter
+ *     and memory sizes with static validation.
+ *   Transformer in Rust, "CodeGen: Parallel Sub-Block Design": one LayerNorm
+ *     feeds attention and a GELU MLP whose outputs join the residual in one
+ *     add; "Key Features": RoPE on even-odd pairs; "Model Configurations":
+ *     rotary_dim 32 of head dim 64.
+ *   randyGPT, "Training (Metal GPU path)": cross-entropy over all positions,
+ *     AdamW moments resident on the device.
+ *
+ * Conventions for every call:
+ *   - Matrices are row-major; weights are [out, in], so a projection is
+ *     y = x W^T.
+ *   - "bf16" storage is the upper 16 bits of an IEEE binary32 (uint16_t in
+ *     this header); rounding to it is to nearest, ties to even.
+ *   - Device pointers point to memory the caller allocated and owns; the
+ *     library allocates no device memory and keeps no device state.
+ *   - Calls taking a stream only enqueue work on it (a hipStream_t passed as
+ *     void*; NULL is the null stream) and return without synchronising.
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Return value: SLT_OK, or an error code after which nothing was enqueued
+ *     (argument errors are found on the host before any launch) - except
+ *     SLT_EHIP, which reports a failed launch.  slt_last_error() gives a
+ *     message for the calling thread.
+ *   - Gradients are written, not accumulated.
+ */
+#ifndef SLT_H
+#define SLT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLT_OK = 0,
+  SLT_EINVAL = 1,        /* bad argument, shape or configuration           */
+  SLT_EUNSUPPORTED = 2,  /* valid but not supported combination            */
+  SLT_EHIP = 3           /* a HIP runtime call or kernel launch failed      */
+} slt_status;
+
+typedef enum { SLT_F32 = 0, SLT_BF16 = 1 } slt_dtype;
+typedef enum { SLT_ROPE_HALF = 0, SLT_ROPE_PAIRS = 1 } slt_rope_mode;
+typedef enum { SLT_BLOCK_LLAMA = 0, SLT_BLOCK_PARALLEL = 1 } slt_block;
+
+/* Model and workload shape.  d = C / H is the head dimension. */
+typedef struct {
+  int32_t V, C, H, Hkv, L, T, B, F, R; /* vocab, width, heads, kv heads, layers,
+                                          sequence, batch, MLP width, rotary dims */
+  int32_t rope_mode;  /* slt_rope_mode: HALF pairs (j, j+R/2); PAIRS (2j, 2j+1) */
+  int32_t block;      /* slt_block: LLAMA (RMSNorm, SwiGLU) or PARALLEL (LayerNorm, GELU) */
+  int32_t act;        /* slt_dtype of activations and of the compute copy of weights */
+  float eps;          /* norm epsilon, added inside the square root (1e-5)          */
+  float rope_base;    /* RoPE base (10000)                                           */
+} slt_config;
+
+/* One tensor of the flat parameter buffer.  rows/cols describe a matrix
+ * [rows, cols]; vectors have rows = 1.  decay is 1 when weight decay applies. */
+typedef struct {
+  char name[40];
+  int64_t offset;   /* in elements */
+  int64_t numel;
+  int64_t rows, cols;
+  int32_t decay;
+} slt_tensor;
+
+/* Thread-local message describing the last error of the calling thread. */
+const char* slt_last_error(void);
+
+/* Library version string. */
+const char* slt_version(void);
+
+/* ------------------------------------------------------------------------
+ * Planning (host only; strata, the compile-time planner with static
+ * validation)
+ * ---------------------------------------------------------------------- */
+
+/* Checks a configuration: all sizes positive, C = H*d, H a multiple of Hkv,
+ * R even and R <= d, rope_mode/block/act valid, C <= 4096.  SLT_EINVAL with a
+ * message otherwise. */
+slt_status slt_validate(const slt_config* cfg);
+
+/* Parameter layout (Hephaistos, "Design notes": flat buffer, (offset, len)).
+ * Order: wte [V,C]; per layer (LLAMA) attn_norm [C], qkvw [(H+2Hkv)d, C],
+ * w_o [C, Hd], mlp_norm [C], w1 [F,C], w3 [F,C], w2 [C,F]; (PARALLEL) ln_g [C],
+ * ln_b [C], qkvw, fc_in [F,C], w_out [C, Hd+F] = [W_o | W_fc2]; then norm_f [C]
+ * (LLAMA) or lnf_g, lnf_b [C] (PARALLEL); lm_head [V,C].  Layer tensors are
+ * named "h<l>.<name>".  out may be NULL (only counts); otherwise it receives
+ * min(cap, n) entries.  *n_tensors and *n_params are always set. */
+slt_status slt_param_layout(const slt_config* cfg, slt_tensor* out, int32_t cap,
+                            int32_t* n_tensors, int64_t* n_params);
+
+/* Bytes of the activation arena (kept from forward to backward) and of the
+ * scratch area (used inside one call) that the step calls need.  Both are
+ * caller-allocated device memory, 256-byte aligned. */
+slt_status slt_workspace_bytes(const slt_config* cfg, int64_t* act_bytes, int64_t* scratch_bytes);
+
+/* Philox-4x32-10 counter-based generator (Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011), host side; the
+ * device copy draws the normals of slt_model_init.  out = philox(ctr, key). */
+void slt_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+
+/* ------------------------------------------------------------------------
+ * Whole-step calls
+ * ---------------------------------------------------------------------- */
+
+/* Initialises the fp32 master parameters on the device: matrices
+ * N(0, std^2) (output projections w_o, w2, w_out times out_scale), gains 1,
+ * LayerNorm shifts 0.  Normal draws are Box-Muller on Philox-4x32-10
+ * counters keyed by seed, so the result depends only on (seed, index). */
+slt_status slt_model_init(const slt_config* cfg, uint64_t seed, float std, float out_scale,
+                          float* master, void* stream);
+
+/* bf16 compute copy of fp32 values: dst[i] = bf16(src[i]), n elements. */
+slt_status slt_cast_bf16(const float* src, uint16_t* dst, int64_t n, void* stream);
+
+/* Forward pass and mean cross-entropy over the B*T positions.
+ * params: the compute copy of the flat parameters in cfg->act (fp32 master for
+ *   F32 configs, its bf16 copy for BF16 configs), layout of slt_param_layout.
+ * tokens: int32 [B, T+1] on the device; inputs are columns 0..T-1 and the
+ *   next-token targets columns 1..T; every id must lie in [0, V).
+ * acts: activation arena, scratch: scratch area (slt_workspace_bytes).
+ * loss: device float, receives the mean loss.
+ * On return the arena holds what slt_backward reads, including the logit
+ * gradient, which overwrites the logits in place. */
+slt_status slt_forward_loss(const slt_config* cfg, const void* params, const int32_t* tokens,
+                            void* acts, void* scratch, float* loss, void* stream);
+
+/* Backward pass after slt_forward_loss with the same params/tokens/acts.
+ * grads: fp32 flat buffer in the parameter layout, every element written. */
+slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t* tokens,
+                        void* acts, void* scratch, float* grads, void* stream);
+
+/* AdamW on n flat fp32 elements at step t >= 1 (Hephaistos, "Architecture at a
+ * glance"; strata, "AdamW (decoupled decay, bias-corrected)"):
+ *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   theta -= lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd theta)
+ * with wd applied where decay_mask[i] != 0 (all elements when decay_mask is
+ * NULL).  When shadow is not NULL it receives bf16(theta).  master, m, v are
+ * updated in place. */
+slt_status slt_adamw_step(int64_t n, float* master, uint16_t* shadow, const float* grads,
+                          float* m, float* v, int64_t t, float lr, float beta1, float beta2,
+                          float eps, float wd, const uint8_t* decay_mask, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Per-op calls.  dtype is the storage type of the activation operands
+ * (SLT_F32 or SLT_BF16); statistics, weight gradients and losses are fp32.
+ * ---------------------------------------------------------------------- */
+
+/* GEMM of the matmul family (strata, "A.B, A.B^T, A^T.B"):
+ *   C[m, n] = sum_k A(m, k) B(n, k)  (+ R[m, n] when R is not NULL)
+ * A(m, k) = A[m*lda + k] if a_kmajor else A[k*lda + m];
+ * B(n, k) = B[n*ldb + k] if b_kmajor else B[k*ldb + n].
+ * A and B have type in_dtype; C and R have type out_dtype (R may equal C).
+ * So y = x W^T is (a_kmajor=1, b_kmajor=1), dX = dY W is (1, 0) and
+ * dW = dY^T X is (0, 0).  workspace (fp32, workspace_bytes) lets the library
+ * split K across workgroups with a fixed-order reduction; NULL disables it. */
+slt_status slt_gemm(int32_t M, int32_t N, int32_t K,
+                    const void* A, int64_t lda, int32_t a_kmajor,
+                    const void* B, int64_t ldb, int32_t b_kmajor,
+                    void* C, int64_t ldc, const void* R, int64_t ldr,
+                    int32_t in_dtype, int32_t out_dtype,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
+/* x[b*T + t, :] = wte[tokens[b*ld_tokens + t], :] for t < T. */
+slt_status slt_embedding_fwd(const int32_t* tokens, int32_t B, int32_t T, int64_t ld_tokens,
+                             const void* wte, void* x, int32_t V, int32_t C, int32_t dtype,
+                             void* stream);
+
+/* dwte[v, :] = sum of dx[i, :] over positions i whose id is v, summed in
+ * increasing position order (deterministic); rows of absent ids are 0.
+ * workspace: at least slt_embedding_bwd_workspace(B*T, V) bytes. */
+int64_t slt_embedding_bwd_workspace(int64_t N, int32_t V);
+slt_status slt_embedding_bwd(const int32_t* tokens, int32_t B, int32_t T, int64_t ld_tokens,
+                             const void* dx, float* dwte, int32_t V, int32_t C, int32_t dtype,
+                             void* workspace, void* stream);
+
+/* RMSNorm (Hephaistos, "Architecture at a glance"; MicroGPT in Rust,
+ * "RMSNorm"): r = (mean_c x^2 + eps)^-1/2, y = x r g.  x, y: [rows, C];
+ * g: [C] in dtype; rstd: fp32 [rows]. */
+slt_status slt_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd,
+                           int32_t rows, int32_t C, float eps, int32_t dtype, void* stream);
+
+/* RMSNorm backward: dx = dres + r (dy g - xh mean(dy g xh)) with xh = x r;
+ * dg = sum_rows dy xh (fp32, fixed-order two-stage reduction).  dres may be
+ * NULL (treated as 0) and may equal dx.  workspace: at least
+ * slt_norm_bwd_workspace(rows, C) bytes. */
+int64_t slt_norm_bwd_workspace(int32_t rows, int32_t C);
+slt_status slt_rmsnorm_bwd(const void* x, const void* g, const float* rstd, const void* dy,
+                           const void* dres, void* dx, float* dg, int32_t rows, int32_t C,
+                           int32_t dtype, void* workspace, void* stream);
+
+/* LayerNorm (strata, GPT-2 reference; Transformer in Rust, "CodeGen: Parallel
+ * Sub-Block Design"): mu = mean x, r = (mean (x-mu)^2 + eps)^-1/2,
+ * y = (x - mu) r gamma + beta; mean, rstd fp32 [rows]. */
+slt_status slt_layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y,
+                             float* mean, float* rstd, int32_t rows, int32_t C, float eps,
+                             int32_t dtype, void* stream);
+
+/* LayerNorm backward: dx = dres + r (dxh - mean dxh - xh mean(dxh xh)),
+ * dxh = dy gamma; dgamma = sum dy xh, dbeta = sum dy (fp32). */
+slt_status slt_layernorm_bwd(const void* x, const void* gamma, const float* mean,
+                             const float* rstd, const void* dy, const void* dres, void* dx,
+                             float* dgamma, float* dbeta, int32_t rows, int32_t C, int32_t dtype,
+                             void* workspace, void* stream);
+
+/* RoPE table: cs[t*R + 2j] = cos(t theta_j), cs[t*R + 2j + 1] = sin(t theta_j),
+ * theta_j = base^(-2j/R), angles in float64 then rounded to fp32; fp32
+ * [T, R] on the device. */
+slt_status slt_rope_table(int32_t T, int32_t R, float base, float* cs, void* stream);
+
+/* Causal attention forward, RoPE applied to q and k as they are loaded
+ * (Hephaistos, "Architecture at a glance"; strata, flash-style attention with
+ * online softmax and no T x T scores).  Head h of token b*T+t reads
+ * q[(b*T+t)*ldq + h*d ...], k and v of KV head h*Hkv/H likewise with ldk/ldv,
+ * and writes o[(b*T+t)*ldo + h*d ...].  lse: fp32 [B, H, T], the natural log
+ * of the softmax denominator of each query row (scores scaled by 1/sqrt(d)).
+ * cs: the RoPE table of slt_rope_table for (T, R); R = 0 disables RoPE. */
+slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                             int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R,
+                             int32_t rope_mode, const float* cs, int32_t dtype, void* stream);
+
+/* Causal attention backward (recomputing probabilities from lse): writes dq
+ * (of the un-rotated q), dk (un-rotated k; summed over the query heads of each
+ * KV head) and dv with the same addressing as q, k, v.  workspace: at least
+ * slt_attention_bwd_workspace(B, H, T) bytes. */
+int64_t slt_attention_bwd_workspace(int32_t B, int32_t H, int32_t T);
+slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t lddo,
+                             int64_t lddq, int64_t lddk, int64_t lddv,
+                             int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R,
+                             int32_t rope_mode, const float* cs, int32_t dtype, void* workspace,
+                             void* stream);
+
+/* SwiGLU (Hephaistos, "Architecture at a glance"): h = silu(a) * b on
+ * [rows, F] operands with row strides lda, ldb, ldh. */
+slt_status slt_swiglu_fwd(const void* a, const void* b, void* h, int32_t rows, int32_t F,
+                          int64_t lda, int64_t ldb, int64_t ldh, int32_t dtype, void* stream);
+
+/* da = dh b sigmoid(a) (1 + a (1 - sigmoid(a))), db = dh silu(a). */
+slt_status slt_swiglu_bwd(const void* a, const void* b, const void* dh, void* da, void* db,
+                          int32_t rows, int32_t F, int64_t lda, int64_t ldb, int64_t lddh,
+                          int64_t ldda, int64_t lddb, int32_t dtype, void* stream);
+
+/* GELU, tanh form: u = a/2 (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))). */
+slt_status slt_gelu_fwd(const void* a, void* u, int32_t rows, int32_t F, int64_t lda,
+                        int64_t ldu, int32_t dtype, void* stream);
+slt_status slt_gelu_bwd(const void* a, const void* du, void* da, int32_t rows, int32_t F,
+                        int64_t lda, int64_t lddu, int64_t ldda, int32_t dtype, void* stream);
+
+/* Fused softmax cross-entropy over rows of logits z [rows, V] (row stride ldz)
+ * with int32 targets (targets[i * ld_targets_row + col] addressing of
+ * slt_forward_loss: row i = b*T + t reads tokens[b*ld_tokens + t + 1]).
+ * loss (device fp32) = mean_i (lse_i - z[i, y_i]); z is overwritten with
+ * dz = (softmax(z_i) - onehot(y_i)) / rows.  lse (fp32 [rows]) may be NULL.
+ * workspace: at least 4*rows bytes (per-row losses, summed in fixed order). */
+slt_status slt_softmax_xent(void* z, int64_t ldz, const int32_t* tokens, int32_t B, int32_t T,
+                            int64_t ld_tokens, int32_t V, float* loss, float* lse, int32_t dtype,
+                            void* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLT_H */

@@ -1,0 +1,683 @@
+// C ABI of libslt: argument checks, the planner (parameter layout, activation
+// arena and scratch offsets), and the forward / backward walks that enqueue the
+// kernels of rowops.hip, gemm.hip and attention.hip on the caller's stream.
+//
+// Hephaistos, "Design notes": flat parameter buffer with per-tensor (offset,
+// length), an activation arena filled by the forward, the backward as a
+// straight reverse walk over it.  strata: a planner that sizes parameters and
+// memory and validates the configuration before anything runs.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "slt_internal.h"
+
+namespace slt {
+
+static thread_local std::string g_err;
+
+void set_error(const std::string& msg) { g_err = msg; }
+
+slt_status fail(slt_status code, const std::string& msg) {
+  set_error(msg);
+  return code;
+}
+
+slt_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SLT_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+  return SLT_OK;
+}
+
+#define SLT_TRY(expr)                    \
+  do {                                   \
+    slt_status _st = (expr);             \
+    if (_st != SLT_OK) return _st;       \
+  } while (0)
+
+static inline int64_t a256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// ---------------------------------------------------------------------------
+// Planner
+// ---------------------------------------------------------------------------
+struct LayerP {
+  int64_t norm1 = -1, norm1b = -1, qkvw = -1, wo = -1, norm2 = -1, w1 = -1, w3 = -1, w2 = -1, fcin = -1, wout = -1;
+};
+
+struct LayerA {
+  int64_t n1, r1, mu1, qkv, o, lse, n2, r2, ab, h;  // byte offsets in the arena
+};
+
+struct Plan {
+  slt_config c;
+  int d, N, qd, kd, qkv_w, in_w, ou_w;
+  bool llama, bf;
+  int64_t es;  // element size of activations / compute weights
+  std::vector<slt_tensor> tensors;
+  std::vector<LayerP> lp;
+  int64_t wte, normf, normfb = -1, head, n_params;
+  // arena
+  std::vector<int64_t> xs;
+  std::vector<LayerA> la;
+  int64_t nf, rf, muf, z, cs, act_bytes;
+  // scratch
+  int64_t rowloss, dx, dbig, dmid, dn, delta, normws, embws, gemmws, gemmws_bytes, scratch_bytes;
+  int dbig_w, dmid_w;
+};
+
+static slt_status validate(const slt_config* c) {
+  if (!c) return fail(SLT_EINVAL, "config is NULL");
+  if (c->V <= 0 || c->C <= 0 || c->H <= 0 || c->Hkv <= 0 || c->L <= 0 || c->T <= 0 || c->B <= 0 || c->F <= 0)
+    return fail(SLT_EINVAL, "all of V, C, H, Hkv, L, T, B, F must be positive");
+  if (c->C % c->H) return fail(SLT_EINVAL, "C must be a multiple of H (C = H * d)");
+  if (c->H % c->Hkv) return fail(SLT_EINVAL, "H must be a multiple of Hkv");
+  const int d = c->C / c->H;
+  if (c->R < 0 || c->R > d || (c->R & 1)) return fail(SLT_EINVAL, "R must be even and 0 <= R <= d");
+  if (d > 64) return fail(SLT_EUNSUPPORTED, "head dimension above 64");
+  if (c->rope_mode != SLT_ROPE_HALF && c->rope_mode != SLT_ROPE_PAIRS) return fail(SLT_EINVAL, "bad rope_mode");
+  if (c->block != SLT_BLOCK_LLAMA && c->block != SLT_BLOCK_PARALLEL) return fail(SLT_EINVAL, "bad block");
+  if (c->act != SLT_F32 && c->act != SLT_BF16) return fail(SLT_EINVAL, "bad act dtype");
+  if (c->C > 4096 || (c->C % 8 && c->C > 512)) return fail(SLT_EUNSUPPORTED, "C above 4096 (or above 512 unaligned)");
+  if (!(c->eps >= 0.f) || !(c->rope_base > 0.f)) return fail(SLT_EINVAL, "eps must be >= 0 and rope_base > 0");
+  const int64_t N = (int64_t)c->B * c->T;
+  if (N > (1 << 30) || (int64_t)c->V * c->C > ((int64_t)1 << 40)) return fail(SLT_EUNSUPPORTED, "sizes too large");
+  return SLT_OK;
+}
+
+static void add_tensor(Plan& p, const std::string& name, int64_t rows, int64_t cols, int32_t decay, int64_t& off) {
+  slt_tensor t;
+  memset(&t, 0, sizeof(t));
+  snprintf(t.name, sizeof(t.name), "%s", name.c_str());
+  t.offset = off;
+  t.rows = rows;
+  t.cols = cols;
+  t.numel = rows * cols;
+  t.decay = decay;
+  p.tensors.push_back(t);
+  off += t.numel;
+}
+
+static slt_status make_plan(const slt_config* cfg, Plan& p) {
+  SLT_TRY(validate(cfg));
+  const slt_config& c = *cfg;
+  p.c = c;
+  p.d = c.C / c.H;
+  p.N = c.B * c.T;
+  p.qd = c.H * p.d;
+  p.kd = c.Hkv * p.d;
+  p.qkv_w = p.qd + 2 * p.kd;
+  p.llama = c.block == SLT_BLOCK_LLAMA;
+  p.bf = c.act == SLT_BF16;
+  p.es = p.bf ? 2 : 4;
+  p.in_w = p.llama ? 2 * c.F : p.qkv_w + c.F;
+  p.ou_w = p.qd + c.F;
+
+  // parameters (every tensor decays: the pages exclude none)
+  int64_t off = 0;
+  p.tensors.clear();
+  p.lp.assign(c.L, LayerP{});
+  p.wte = off;
+  add_tensor(p, "wte", c.V, c.C, 1, off);
+  for (int l = 0; l < c.L; ++l) {
+    const std::string pre = "h" + std::to_string(l) + ".";
+    LayerP& L = p.lp[l];
+    if (p.llama) {
+      L.norm1 = off; add_tensor(p, pre + "attn_norm", 1, c.C, 1, off);
+      L.qkvw = off; add_tensor(p, pre + "qkvw", p.qkv_w, c.C, 1, off);
+      L.wo = off; add_tensor(p, pre + "w_o", c.C, p.qd, 1, off);
+      L.norm2 = off; add_tensor(p, pre + "mlp_norm", 1, c.C, 1, off);
+      L.w1 = off; add_tensor(p, pre + "w1", c.F, c.C, 1, off);
+      L.w3 = off; add_tensor(p, pre + "w3", c.F, c.C, 1, off);
+      L.w2 = off; add_tensor(p, pre + "w2", c.C, c.F, 1, off);
+    } else {
+      L.norm1 = off; add_tensor(p, pre + "ln_g", 1, c.C, 1, off);
+      L.norm1b = off; add_tensor(p, pre + "ln_b", 1, c.C, 1, off);
+      L.qkvw = off; add_tensor(p, pre + "qkvw", p.qkv_w, c.C, 1, off);
+      L.fcin = off; add_tensor(p, pre + "fc_in", c.F, c.C, 1, off);
+      L.wout = off; add_tensor(p, pre + "w_out", c.C, p.ou_w, 1, off);
+    }
+  }
+  if (p.llama) {
+    p.normf = off; add_tensor(p, "norm_f", 1, c.C, 1, off);
+  } else {
+    p.normf = off; add_tensor(p, "lnf_g", 1, c.C, 1, off);
+    p.normfb = off; add_tensor(p, "lnf_b", 1, c.C, 1, off);
+  }
+  p.head = off;
+  add_tensor(p, "lm_head", c.V, c.C, 1, off);
+  p.n_params = off;
+
+  // activation arena
+  const int64_t N = p.N, es = p.es, C = c.C;
+  int64_t a = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = a;
+    a += a256(bytes);
+    return o;
+  };
+  const int nx = p.llama ? 2 * c.L + 1 : c.L + 1;
+  p.xs.resize(nx);
+  for (int i = 0; i < nx; ++i) p.xs[i] = take(N * C * es);
+  p.la.resize(c.L);
+  for (int l = 0; l < c.L; ++l) {
+    LayerA& A = p.la[l];
+    A.n1 = take(N * C * es);
+    A.r1 = take(N * 4);
+    A.mu1 = p.llama ? -1 : take(N * 4);
+    A.lse = take((int64_t)c.B * c.H * c.T * 4);
+    if (p.llama) {
+      A.qkv = take(N * p.qkv_w * es);
+      A.o = take(N * p.qd * es);
+      A.n2 = take(N * C * es);
+      A.r2 = take(N * 4);
+      A.ab = take(N * 2 * c.F * es);
+      A.h = take(N * c.F * es);
+    } else {
+      A.qkv = take(N * p.in_w * es);   // [q | k | v | fc_in pre-activation]
+      A.o = take(N * p.ou_w * es);     // [attention output | gelu output]
+      A.n2 = A.r2 = A.ab = A.h = -1;
+    }
+  }
+  p.nf = take(N * C * es);
+  p.rf = take(N * 4);
+  p.muf = p.llama ? -1 : take(N * 4);
+  p.z = take(N * (int64_t)c.V * es);
+  p.cs = take((int64_t)c.T * std::max(c.R, 2) * 4);
+  p.act_bytes = a;
+
+  // scratch
+  p.dbig_w = p.llama ? std::max(2 * c.F, p.qkv_w) : p.in_w;
+  p.dmid_w = p.llama ? std::max(c.F, p.qd) : p.ou_w;
+  int64_t s = 0;
+  auto takes = [&](int64_t bytes) {
+    const int64_t o = s;
+    s += a256(bytes);
+    return o;
+  };
+  p.rowloss = takes(N * 4);
+  p.dx = takes(N * C * es);
+  p.dbig = takes(N * p.dbig_w * es);
+  p.dmid = takes(N * p.dmid_w * es);
+  p.dn = takes(N * C * es);
+  p.delta = takes(attention_bwd_ws(c.B, c.H, c.T));
+  p.normws = takes(norm_bwd_ws(p.N, c.C));
+  p.embws = takes(embedding_bwd_ws(N, c.V));
+  // split-K partials of the weight gradients
+  p.gemmws_bytes = 64ll << 20;
+  p.gemmws = takes(p.gemmws_bytes);
+  p.scratch_bytes = s;
+  return SLT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM helpers for the three forms
+// ---------------------------------------------------------------------------
+struct Ctx {
+  const Plan& p;
+  hipStream_t s;
+  char* acts;
+  char* scr;
+  const char* params;
+  int dt;  // activation dtype
+  void* A(int64_t off) const { return acts + off; }
+  void* S(int64_t off) const { return scr + off; }
+  const void* P(int64_t off) const { return params + off * p.es; }
+};
+
+// y[M, N] = x[M, K] W[N, K]^T (+ R)
+static slt_status proj(const Ctx& x, int M, int N, int K, const void* X, int64_t ldx, const void* W, void* Y,
+                       int64_t ldy, const void* R, int64_t ldr) {
+  GemmArgs g{M, N, K, X, ldx, true, W, (int64_t)K, true, Y, ldy, R, ldr, x.dt, x.dt, nullptr, 0};
+  return launch_gemm(g, x.s);
+}
+
+// dX[M, K] = dY[M, N] W[N, K]   (W row stride ldw)
+static slt_status proj_dx(const Ctx& x, int M, int N, int K, const void* dY, int64_t lddy, const void* W,
+                          int64_t ldw, void* dX, int64_t lddx) {
+  GemmArgs g{M, K, N, dY, lddy, true, W, ldw, false, dX, lddx, nullptr, 0, x.dt, x.dt, nullptr, 0};
+  return launch_gemm(g, x.s);
+}
+
+// dW[N, K] = dY[M, N]^T X[M, K]  (fp32 out, row stride ldw)
+static slt_status proj_dw(const Ctx& x, int M, int N, int K, const void* dY, int64_t lddy, const void* X,
+                          int64_t ldx, float* dW, int64_t ldw) {
+  GemmArgs g{N, K, M, dY, lddy, false, X, ldx, false, dW, ldw, nullptr, 0, x.dt, SLT_F32,
+             reinterpret_cast<float*>(x.S(x.p.gemmws)), x.p.gemmws_bytes};
+  return launch_gemm(g, x.s);
+}
+
+// ---------------------------------------------------------------------------
+// Forward and backward walks
+// ---------------------------------------------------------------------------
+static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float* loss) {
+  const slt_config& c = p.c;
+  const int N = p.N, C = c.C;
+  const int64_t ldt = c.T + 1;
+  float* cs = reinterpret_cast<float*>(x.A(p.cs));
+  if (c.R > 0) SLT_TRY(launch_rope_table(c.T, c.R, c.rope_base, cs, x.s));
+  SLT_TRY(launch_embedding_fwd(tok, c.B, c.T, ldt, x.P(p.wte), x.A(p.xs[0]), c.V, C, x.dt, x.s));
+  for (int l = 0; l < c.L; ++l) {
+    const LayerP& W = p.lp[l];
+    const LayerA& A = p.la[l];
+    AttnArgs at{};
+    at.B = c.B; at.T = c.T; at.H = c.H; at.Hkv = c.Hkv; at.d = p.d; at.R = c.R; at.rope_mode = c.rope_mode;
+    at.dtype = x.dt; at.cs = cs;
+    at.lse = reinterpret_cast<float*>(x.A(A.lse));
+    if (p.llama) {
+      void* xin = x.A(p.xs[2 * l]);
+      void* xmid = x.A(p.xs[2 * l + 1]);
+      void* xout = x.A(p.xs[2 * l + 2]);
+      SLT_TRY(launch_rmsnorm_fwd(xin, x.P(W.norm1), x.A(A.n1), (float*)x.A(A.r1), N, C, c.eps, x.dt, x.s));
+      SLT_TRY(proj(x, N, p.qkv_w, C, x.A(A.n1), C, x.P(W.qkvw), x.A(A.qkv), p.qkv_w, nullptr, 0));
+      char* qkv = (char*)x.A(A.qkv);
+      at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
+      at.ldq = at.ldk = at.ldv = p.qkv_w;
+      at.out = x.A(A.o); at.ldo = p.qd;
+      SLT_TRY(launch_attention_fwd(at, x.s));
+      SLT_TRY(proj(x, N, C, p.qd, x.A(A.o), p.qd, x.P(W.wo), xmid, C, xin, C));
+      SLT_TRY(launch_rmsnorm_fwd(xmid, x.P(W.norm2), x.A(A.n2), (float*)x.A(A.r2), N, C, c.eps, x.dt, x.s));
+      SLT_TRY(proj(x, N, 2 * c.F, C, x.A(A.n2), C, x.P(W.w1), x.A(A.ab), 2 * c.F, nullptr, 0));
+      char* ab = (char*)x.A(A.ab);
+      SLT_TRY(launch_swiglu_fwd(ab, ab + c.F * p.es, x.A(A.h), N, c.F, 2 * c.F, 2 * c.F, c.F, x.dt, x.s));
+      SLT_TRY(proj(x, N, C, c.F, x.A(A.h), c.F, x.P(W.w2), xout, C, xmid, C));
+    } else {
+      void* xin = x.A(p.xs[l]);
+      void* xout = x.A(p.xs[l + 1]);
+      SLT_TRY(launch_layernorm_fwd(xin, x.P(W.norm1), x.P(W.norm1b), x.A(A.n1), (float*)x.A(A.mu1),
+                                   (float*)x.A(A.r1), N, C, c.eps, x.dt, x.s));
+      SLT_TRY(proj(x, N, p.in_w, C, x.A(A.n1), C, x.P(W.qkvw), x.A(A.qkv), p.in_w, nullptr, 0));
+      char* qkv = (char*)x.A(A.qkv);
+      char* ou = (char*)x.A(A.o);
+      at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
+      at.ldq = at.ldk = at.ldv = p.in_w;
+      at.out = ou; at.ldo = p.ou_w;
+      SLT_TRY(launch_attention_fwd(at, x.s));
+      SLT_TRY(launch_gelu_fwd(qkv + p.qkv_w * p.es, ou + p.qd * p.es, N, c.F, p.in_w, p.ou_w, x.dt, x.s));
+      SLT_TRY(proj(x, N, C, p.ou_w, ou, p.ou_w, x.P(W.wout), xout, C, xin, C));
+    }
+  }
+  void* xf = x.A(p.xs.back());
+  if (p.llama)
+    SLT_TRY(launch_rmsnorm_fwd(xf, x.P(p.normf), x.A(p.nf), (float*)x.A(p.rf), N, C, c.eps, x.dt, x.s));
+  else
+    SLT_TRY(launch_layernorm_fwd(xf, x.P(p.normf), x.P(p.normfb), x.A(p.nf), (float*)x.A(p.muf),
+                                 (float*)x.A(p.rf), N, C, c.eps, x.dt, x.s));
+  SLT_TRY(proj(x, N, c.V, C, x.A(p.nf), C, x.P(p.head), x.A(p.z), c.V, nullptr, 0));
+  SLT_TRY(launch_softmax_xent(x.A(p.z), c.V, tok, c.B, c.T, ldt, c.V, loss, nullptr, x.dt, x.S(p.rowloss), x.s));
+  return SLT_OK;
+}
+
+static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, float* grads) {
+  const slt_config& c = p.c;
+  const int N = p.N, C = c.C;
+  const int64_t ldt = c.T + 1;
+  const float* cs = reinterpret_cast<const float*>(x.A(p.cs));
+  void* dx = x.S(p.dx);
+  void* dn = x.S(p.dn);
+  char* dbig = (char*)x.S(p.dbig);
+  char* dmid = (char*)x.S(p.dmid);
+  void* nws = x.S(p.normws);
+
+  // lm_head and final norm
+  SLT_TRY(proj_dw(x, N, c.V, C, x.A(p.z), c.V, x.A(p.nf), C, grads + p.head, C));
+  SLT_TRY(proj_dx(x, N, c.V, C, x.A(p.z), c.V, x.P(p.head), C, dn, C));
+  if (p.llama)
+    SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.rf), dn, nullptr, dx,
+                               grads + p.normf, N, C, x.dt, nws, x.s));
+  else
+    SLT_TRY(launch_layernorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.muf),
+                                 (const float*)x.A(p.rf), dn, nullptr, dx, grads + p.normf, grads + p.normfb, N, C,
+                                 x.dt, nws, x.s));
+
+  for (int l = c.L - 1; l >= 0; --l) {
+    const LayerP& W = p.lp[l];
+    const LayerA& A = p.la[l];
+    AttnArgs at{};
+    at.B = c.B; at.T = c.T; at.H = c.H; at.Hkv = c.Hkv; at.d = p.d; at.R = c.R; at.rope_mode = c.rope_mode;
+    at.dtype = x.dt; at.cs = cs;
+    at.lse_in = (const float*)x.A(A.lse);
+    at.delta = (float*)x.S(p.delta);
+    char* qkv = (char*)x.A(A.qkv);
+    if (p.llama) {
+      // x_out = x_mid + h W2^T
+      SLT_TRY(proj_dw(x, N, C, c.F, dx, C, x.A(A.h), c.F, grads + W.w2, c.F));
+      SLT_TRY(proj_dx(x, N, C, c.F, dx, C, x.P(W.w2), c.F, dmid, c.F));
+      char* ab = (char*)x.A(A.ab);
+      SLT_TRY(launch_swiglu_bwd(ab, ab + c.F * p.es, dmid, dbig, dbig + c.F * p.es, N, c.F, 2 * c.F, 2 * c.F, c.F,
+                                2 * c.F, 2 * c.F, x.dt, x.s));
+      SLT_TRY(proj_dw(x, N, 2 * c.F, C, dbig, 2 * c.F, x.A(A.n2), C, grads + W.w1, C));
+      SLT_TRY(proj_dx(x, N, 2 * c.F, C, dbig, 2 * c.F, x.P(W.w1), C, dn, C));
+      SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l + 1]), x.P(W.norm2), (const float*)x.A(A.r2), dn, dx, dx,
+                                 grads + W.norm2, N, C, x.dt, nws, x.s));
+      // x_mid = x_in + o W_o^T
+      SLT_TRY(proj_dw(x, N, C, p.qd, dx, C, x.A(A.o), p.qd, grads + W.wo, p.qd));
+      SLT_TRY(proj_dx(x, N, C, p.qd, dx, C, x.P(W.wo), p.qd, dmid, p.qd));
+      at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
+      at.ldq = at.ldk = at.ldv = p.qkv_w;
+      at.o = x.A(A.o); at.ldo = p.qd;
+      at.dout = dmid; at.lddo = p.qd;
+      at.dq = dbig; at.dk = dbig + p.qd * p.es; at.dv = dbig + (p.qd + p.kd) * p.es;
+      at.lddq = at.lddk = at.lddv = p.qkv_w;
+      SLT_TRY(launch_attention_bwd(at, x.s));
+      SLT_TRY(proj_dw(x, N, p.qkv_w, C, dbig, p.qkv_w, x.A(A.n1), C, grads + W.qkvw, C));
+      SLT_TRY(proj_dx(x, N, p.qkv_w, C, dbig, p.qkv_w, x.P(W.qkvw), C, dn, C));
+      SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l]), x.P(W.norm1), (const float*)x.A(A.r1), dn, dx, dx,
+                                 grads + W.norm1, N, C, x.dt, nws, x.s));
+    } else {
+      char* ou = (char*)x.A(A.o);
+      // x_out = x_in + [o | u] W_out^T
+      SLT_TRY(proj_dw(x, N, C, p.ou_w, dx, C, ou, p.ou_w, grads + W.wout, p.ou_w));
+      SLT_TRY(proj_dx(x, N, C, p.ou_w, dx, C, x.P(W.wout), p.ou_w, dmid, p.ou_w));
+      SLT_TRY(launch_gelu_bwd(qkv + p.qkv_w * p.es, dmid + p.qd * p.es, dbig + p.qkv_w * p.es, N, c.F, p.in_w,
+                              p.ou_w, p.in_w, x.dt, x.s));
+      at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
+      at.ldq = at.ldk = at.ldv = p.in_w;
+      at.o = ou; at.ldo = p.ou_w;
+      at.dout = dmid; at.lddo = p.ou_w;
+      at.dq = dbig; at.dk = dbig + p.qd * p.es; at.dv = dbig + (p.qd + p.kd) * p.es;
+      at.lddq = at.lddk = at.lddv = p.in_w;
+      SLT_TRY(launch_attention_bwd(at, x.s));
+      SLT_TRY(proj_dw(x, N, p.in_w, C, dbig, p.in_w, x.A(A.n1), C, grads + W.qkvw, C));
+      SLT_TRY(proj_dx(x, N, p.in_w, C, dbig, p.in_w, x.P(W.qkvw), C, dn, C));
+      SLT_TRY(launch_layernorm_bwd(x.A(p.xs[l]), x.P(W.norm1), (const float*)x.A(A.mu1), (const float*)x.A(A.r1),
+                                   dn, dx, dx, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws, x.s));
+    }
+  }
+  SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, dx, grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s));
+  return SLT_OK;
+}
+
+static bool is_dtype(int32_t d) { return d == SLT_F32 || d == SLT_BF16; }
+
+}  // namespace slt
+
+using namespace slt;
+
+// ---------------------------------------------------------------------------
+// Exported entry points
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char* slt_last_error(void) { return g_err.c_str(); }
+
+const char* slt_version(void) { return "slt 0.1 (gfx950)"; }
+
+slt_status slt_validate(const slt_config* cfg) { return validate(cfg); }
+
+slt_status slt_param_layout(const slt_config* cfg, slt_tensor* out, int32_t cap, int32_t* n_tensors,
+                            int64_t* n_params) {
+  Plan p;
+  SLT_TRY(make_plan(cfg, p));
+  if (!n_tensors || !n_params) return fail(SLT_EINVAL, "n_tensors and n_params must not be NULL");
+  *n_tensors = (int32_t)p.tensors.size();
+  *n_params = p.n_params;
+  if (out) {
+    if (cap < 0) return fail(SLT_EINVAL, "cap must be >= 0");
+    for (int i = 0; i < (int)p.tensors.size() && i < cap; ++i) out[i] = p.tensors[i];
+  }
+  return SLT_OK;
+}
+
+slt_status slt_workspace_bytes(const slt_config* cfg, int64_t* act_bytes, int64_t* scratch_bytes) {
+  Plan p;
+  SLT_TRY(make_plan(cfg, p));
+  if (!act_bytes || !scratch_bytes) return fail(SLT_EINVAL, "output pointers must not be NULL");
+  *act_bytes = p.act_bytes;
+  *scratch_bytes = p.scratch_bytes;
+  return SLT_OK;
+}
+
+slt_status slt_model_init(const slt_config* cfg, uint64_t seed, float std, float out_scale, float* master,
+                          void* stream) {
+  Plan p;
+  SLT_TRY(make_plan(cfg, p));
+  if (!master) return fail(SLT_EINVAL, "master is NULL");
+  hipStream_t s = as_stream(stream);
+  for (const slt_tensor& t : p.tensors) {
+    const std::string name(t.name);
+    auto ends = [&](const char* suf) {
+      const size_t n = strlen(suf);
+      return name.size() >= n && name.compare(name.size() - n, n, suf) == 0;
+    };
+    int kind = 0;
+    float v = std;
+    if (ends("norm") || ends("norm_f") || ends("ln_g") || ends("lnf_g")) {
+      kind = 1; v = 1.0f;
+    } else if (ends("ln_b") || ends("lnf_b")) {
+      kind = 1; v = 0.0f;
+    } else if (ends("w_o") || ends("w2") || ends("w_out")) {
+      v = std * out_scale;
+    }
+    SLT_TRY(launch_model_init_range(master + t.offset, t.numel, t.offset, seed, v, kind, s));
+  }
+  return SLT_OK;
+}
+
+slt_status slt_cast_bf16(const float* src, uint16_t* dst, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!src || !dst))) return fail(SLT_EINVAL, "cast: bad arguments");
+  if (n == 0) return SLT_OK;
+  return launch_cast_bf16(src, dst, n, as_stream(stream));
+}
+
+slt_status slt_forward_loss(const slt_config* cfg, const void* params, const int32_t* tokens, void* acts,
+                            void* scratch, float* loss, void* stream) {
+  Plan p;
+  SLT_TRY(make_plan(cfg, p));
+  if (!params || !tokens || !acts || !scratch || !loss) return fail(SLT_EINVAL, "forward_loss: NULL pointer");
+  Ctx x{p, as_stream(stream), (char*)acts, (char*)scratch, (const char*)params, cfg->act};
+  return forward(p, x, tokens, loss);
+}
+
+slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t* tokens, void* acts, void* scratch,
+                        float* grads, void* stream) {
+  Plan p;
+  SLT_TRY(make_plan(cfg, p));
+  if (!params || !tokens || !acts || !scratch || !grads) return fail(SLT_EINVAL, "backward: NULL pointer");
+  Ctx x{p, as_stream(stream), (char*)acts, (char*)scratch, (const char*)params, cfg->act};
+  return backward(p, x, tokens, grads);
+}
+
+slt_status slt_adamw_step(int64_t n, float* master, uint16_t* shadow, const float* grads, float* m, float* v,
+                          int64_t t, float lr, float beta1, float beta2, float eps, float wd,
+                          const uint8_t* decay_mask, void* stream) {
+  if (n < 0) return fail(SLT_EINVAL, "adamw: n < 0");
+  if (n == 0) return SLT_OK;
+  if (!master || !grads || !m || !v) return fail(SLT_EINVAL, "adamw: NULL pointer");
+  if (t < 1) return fail(SLT_EINVAL, "adamw: t must be >= 1");
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps >= 0.f))
+    return fail(SLT_EINVAL, "adamw: betas must lie in [0, 1) and eps >= 0");
+  auto al16 = [](const void* q) { return q == nullptr || reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  if (!al16(master) || !al16(grads) || !al16(m) || !al16(v) || (shadow && reinterpret_cast<uintptr_t>(shadow) % 8) ||
+      (decay_mask && reinterpret_cast<uintptr_t>(decay_mask) % 4))
+    return fail(SLT_EINVAL, "adamw: buffers must be 16-byte aligned (shadow 8, mask 4)");
+  return launch_adamw(n, master, shadow, grads, m, v, t, lr, beta1, beta2, eps, wd, decay_mask, as_stream(stream));
+}
+
+slt_status slt_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_kmajor, const void* B,
+                    int64_t ldb, int32_t b_kmajor, void* C, int64_t ldc, const void* R, int64_t ldr,
+                    int32_t in_dtype, int32_t out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return fail(SLT_EINVAL, "gemm: negative size");
+  if (!is_dtype(in_dtype) || !is_dtype(out_dtype)) return fail(SLT_EINVAL, "gemm: bad dtype");
+  if (M == 0 || N == 0) return SLT_OK;
+  if (!C || (K > 0 && (!A || !B))) return fail(SLT_EINVAL, "gemm: NULL operand");
+  if (ldc < N || (R && ldr < N)) return fail(SLT_EINVAL, "gemm: ldc/ldr smaller than N");
+  if (K > 0) {
+    if (a_kmajor ? lda < K : lda < M) return fail(SLT_EINVAL, "gemm: lda too small");
+    if (b_kmajor ? ldb < K : ldb < N) return fail(SLT_EINVAL, "gemm: ldb too small");
+  }
+  if (workspace_bytes < 0 || (workspace && reinterpret_cast<uintptr_t>(workspace) % 16))
+    return fail(SLT_EINVAL, "gemm: workspace must be 16-byte aligned");
+  GemmArgs g{M, N, K, A, lda, a_kmajor != 0, B, ldb, b_kmajor != 0, C, ldc, R, ldr, in_dtype, out_dtype,
+             static_cast<float*>(workspace), workspace ? workspace_bytes : 0};
+  return launch_gemm(g, as_stream(stream));
+}
+
+slt_status slt_embedding_fwd(const int32_t* tokens, int32_t B, int32_t T, int64_t ld_tokens, const void* wte,
+                             void* x, int32_t V, int32_t C, int32_t dtype, void* stream) {
+  if (B < 0 || T < 0 || V <= 0 || C <= 0 || ld_tokens < T || !is_dtype(dtype))
+    return fail(SLT_EINVAL, "embedding_fwd: bad sizes");
+  if ((int64_t)B * T == 0) return SLT_OK;
+  if (!tokens || !wte || !x) return fail(SLT_EINVAL, "embedding_fwd: NULL pointer");
+  return launch_embedding_fwd(tokens, B, T, ld_tokens, wte, x, V, C, dtype, as_stream(stream));
+}
+
+int64_t slt_embedding_bwd_workspace(int64_t N, int32_t V) { return embedding_bwd_ws(N, V); }
+
+slt_status slt_embedding_bwd(const int32_t* tokens, int32_t B, int32_t T, int64_t ld_tokens, const void* dx,
+                             float* dwte, int32_t V, int32_t C, int32_t dtype, void* workspace, void* stream) {
+  if (B < 0 || T < 0 || V <= 0 || C <= 0 || C > 4096 || ld_tokens < T || !is_dtype(dtype))
+    return fail(SLT_EINVAL, "embedding_bwd: bad sizes");
+  if (!dwte || !workspace || ((int64_t)B * T > 0 && (!tokens || !dx)))
+    return fail(SLT_EINVAL, "embedding_bwd: NULL pointer");
+  if ((int64_t)B * T == 0) return launch_fill_f32(dwte, 0.f, (int64_t)V * C, as_stream(stream));
+  return launch_embedding_bwd(tokens, B, T, ld_tokens, dx, dwte, V, C, dtype, workspace, as_stream(stream));
+}
+
+slt_status slt_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd, int32_t rows, int32_t C, float eps,
+                           int32_t dtype, void* stream) {
+  if (rows < 0 || C <= 0 || !is_dtype(dtype)) return fail(SLT_EINVAL, "rmsnorm_fwd: bad sizes");
+  if (rows == 0) return SLT_OK;
+  if (!x || !g || !y || !rstd) return fail(SLT_EINVAL, "rmsnorm_fwd: NULL pointer");
+  return launch_rmsnorm_fwd(x, g, y, rstd, rows, C, eps, dtype, as_stream(stream));
+}
+
+int64_t slt_norm_bwd_workspace(int32_t rows, int32_t C) { return norm_bwd_ws(rows, C); }
+
+slt_status slt_rmsnorm_bwd(const void* x, const void* g, const float* rstd, const void* dy, const void* dres,
+                           void* dx, float* dg, int32_t rows, int32_t C, int32_t dtype, void* workspace,
+                           void* stream) {
+  if (rows < 0 || C <= 0 || !is_dtype(dtype)) return fail(SLT_EINVAL, "rmsnorm_bwd: bad sizes");
+  if (!dg || !workspace) return fail(SLT_EINVAL, "rmsnorm_bwd: NULL pointer");
+  if (rows == 0) return launch_fill_f32(dg, 0.f, C, as_stream(stream));
+  if (!x || !g || !rstd || !dy || !dx) return fail(SLT_EINVAL, "rmsnorm_bwd: NULL pointer");
+  return launch_rmsnorm_bwd(x, g, rstd, dy, dres, dx, dg, rows, C, dtype, workspace, as_stream(stream));
+}
+
+slt_status slt_layernorm_fwd(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
+                             int32_t rows, int32_t C, float eps, int32_t dtype, void* stream) {
+  if (rows < 0 || C <= 0 || !is_dtype(dtype)) return fail(SLT_EINVAL, "layernorm_fwd: bad sizes");
+  if (rows == 0) return SLT_OK;
+  if (!x || !gamma || !beta || !y || !mean || !rstd) return fail(SLT_EINVAL, "layernorm_fwd: NULL pointer");
+  return launch_layernorm_fwd(x, gamma, beta, y, mean, rstd, rows, C, eps, dtype, as_stream(stream));
+}
+
+slt_status slt_layernorm_bwd(const void* x, const void* gamma, const float* mean, const float* rstd,
+                             const void* dy, const void* dres, void* dx, float* dgamma, float* dbeta, int32_t rows,
+                             int32_t C, int32_t dtype, void* workspace, void* stream) {
+  if (rows < 0 || C <= 0 || !is_dtype(dtype)) return fail(SLT_EINVAL, "layernorm_bwd: bad sizes");
+  if (!dgamma || !dbeta || !workspace) return fail(SLT_EINVAL, "layernorm_bwd: NULL pointer");
+  if (rows == 0) {
+    SLT_TRY(launch_fill_f32(dgamma, 0.f, C, as_stream(stream)));
+    return launch_fill_f32(dbeta, 0.f, C, as_stream(stream));
+  }
+  if (!x || !gamma || !mean || !rstd || !dy || !dx) return fail(SLT_EINVAL, "layernorm_bwd: NULL pointer");
+  return launch_layernorm_bwd(x, gamma, mean, rstd, dy, dres, dx, dgamma, dbeta, rows, C, dtype, workspace,
+                              as_stream(stream));
+}
+
+slt_status slt_rope_table(int32_t T, int32_t R, float base, float* cs, void* stream) {
+  if (T < 0 || R < 0 || (R & 1) || !(base > 0.f)) return fail(SLT_EINVAL, "rope_table: bad arguments");
+  if (T == 0 || R == 0) return SLT_OK;
+  if (!cs) return fail(SLT_EINVAL, "rope_table: NULL pointer");
+  return launch_rope_table(T, R, base, cs, as_stream(stream));
+}
+
+static slt_status attn_check(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R, int32_t mode,
+                             int32_t dtype, const float* cs) {
+  if (B < 0 || T < 0 || H <= 0 || Hkv <= 0 || d <= 0 || H % Hkv || !is_dtype(dtype))
+    return fail(SLT_EINVAL, "attention: bad sizes");
+  if (d > 64) return fail(SLT_EUNSUPPORTED, "attention: head dim above 64");
+  if (R < 0 || R > d || (R & 1)) return fail(SLT_EINVAL, "attention: R must be even and <= d");
+  if (mode != SLT_ROPE_HALF && mode != SLT_ROPE_PAIRS) return fail(SLT_EINVAL, "attention: bad rope_mode");
+  if (R > 0 && !cs) return fail(SLT_EINVAL, "attention: RoPE table is NULL");
+  return SLT_OK;
+}
+
+slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t ldq,
+                             int64_t ldk, int64_t ldv, int64_t ldo, int32_t B, int32_t T, int32_t H, int32_t Hkv,
+                             int32_t d, int32_t R, int32_t rope_mode, const float* cs, int32_t dtype,
+                             void* stream) {
+  SLT_TRY(attn_check(B, T, H, Hkv, d, R, rope_mode, dtype, cs));
+  if ((int64_t)B * T == 0) return SLT_OK;
+  if (!q || !k || !v || !o || !lse) return fail(SLT_EINVAL, "attention_fwd: NULL pointer");
+  if (ldq < (int64_t)H * d || ldk < (int64_t)Hkv * d || ldv < (int64_t)Hkv * d || ldo < (int64_t)H * d)
+    return fail(SLT_EINVAL, "attention_fwd: row stride smaller than the heads it holds");
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = o; a.lse = lse;
+  a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo;
+  a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.d = d; a.R = R; a.rope_mode = rope_mode; a.dtype = dtype; a.cs = cs;
+  return launch_attention_fwd(a, as_stream(stream));
+}
+
+int64_t slt_attention_bwd_workspace(int32_t B, int32_t H, int32_t T) { return attention_bwd_ws(B, H, T); }
+
+slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv, int64_t ldq, int64_t ldk, int64_t ldv,
+                             int64_t ldo, int64_t lddo, int64_t lddq, int64_t lddk, int64_t lddv, int32_t B,
+                             int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R, int32_t rope_mode,
+                             const float* cs, int32_t dtype, void* workspace, void* stream) {
+  SLT_TRY(attn_check(B, T, H, Hkv, d, R, rope_mode, dtype, cs));
+  if ((int64_t)B * T == 0) return SLT_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return fail(SLT_EINVAL, "attention_bwd: NULL pointer");
+  const int64_t hd = (int64_t)H * d, kvd = (int64_t)Hkv * d;
+  if (ldq < hd || ldo < hd || lddo < hd || lddq < hd || ldk < kvd || ldv < kvd || lddk < kvd || lddv < kvd)
+    return fail(SLT_EINVAL, "attention_bwd: row stride smaller than the heads it holds");
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse_in = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.lddo = lddo; a.lddq = lddq; a.lddk = lddk; a.lddv = lddv;
+  a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.d = d; a.R = R; a.rope_mode = rope_mode; a.dtype = dtype; a.cs = cs;
+  a.delta = static_cast<float*>(workspace);
+  return launch_attention_bwd(a, as_stream(stream));
+}
+
+slt_status slt_swiglu_fwd(const void* a, const void* b, void* h, int32_t rows, int32_t F, int64_t lda, int64_t ldb,
+                          int64_t ldh, int32_t dtype, void* stream) {
+  if (rows < 0 || F < 0 || lda < F || ldb < F || ldh < F || !is_dtype(dtype))
+    return fail(SLT_EINVAL, "swiglu_fwd: bad sizes");
+  if ((int64_t)rows * F == 0) return SLT_OK;
+  if (!a || !b || !h) return fail(SLT_EINVAL, "swiglu_fwd: NULL pointer");
+  return launch_swiglu_fwd(a, b, h, rows, F, lda, ldb, ldh, dtype, as_stream(stream));
+}
+
+slt_status slt_swiglu_bwd(const void* a, const void* b, const void* dh, void* da, void* db, int32_t rows, int32_t F,
+                          int64_t lda, int64_t ldb, int64_t lddh, int64_t ldda, int64_t lddb, int32_t dtype,
+                          void* stream) {
+  if (rows < 0 || F < 0 || lda < F || ldb < F || lddh < F || ldda < F || lddb < F || !is_dtype(dtype))
+    return fail(SLT_EINVAL, "swiglu_bwd: bad sizes");
+  if ((int64_t)rows * F == 0) return SLT_OK;
+  if (!a || !b || !dh || !da || !db) return fail(SLT_EINVAL, "swiglu_bwd: NULL pointer");
+  return launch_swiglu_bwd(a, b, dh, da, db, rows, F, lda, ldb, lddh, ldda, lddb, dtype, as_stream(stream));
+}
+
+slt_status slt_gelu_fwd(const void* a, void* u, int32_t rows, int32_t F, int64_t lda, int64_t ldu, int32_t dtype,
+                        void* stream) {
+  if (rows < 0 || F < 0 || lda < F || ldu < F || !is_dtype(dtype)) return fail(SLT_EINVAL, "gelu_fwd: bad sizes");
+  if ((int64_t)rows * F == 0) return SLT_OK;
+  if (!a || !u) return fail(SLT_EINVAL, "gelu_fwd: NULL pointer");
+  return launch_gelu_fwd(a, u, rows, F, lda, ldu, dtype, as_stream(stream));
+}
+
+slt_status slt_gelu_bwd(const void* a, const void* du, void* da, int32_t rows, int32_t F, int64_t lda, int64_t lddu,
+                        int64_t ldda, int32_t dtype, void* stream) {
+  if (rows < 0 || F < 0 || lda < F || lddu < F || ldda < F || !is_dtype(dtype))
+    return fail(SLT_EINVAL, "gelu_bwd: bad sizes");
+  if ((int64_t)rows * F == 0) return SLT_OK;
+  if (!a || !du || !da) return fail(SLT_EINVAL, "gelu_bwd: NULL pointer");
+  return launch_gelu_bwd(a, du, da, rows, F, lda, lddu, ldda, dtype, as_stream(stream));
+}
+
+slt_status slt_softmax_xent(void* z, int64_t ldz, const int32_t* tokens, int32_t B, int32_t T, int64_t ld_tokens,
+                            int32_t V, float* loss, float* lse, int32_t dtype, void* workspace, void* stream) {
+  if (B <= 0 || T <= 0 || V <= 0 || ldz < V || ld_tokens < T + 1 || !is_dtype(dtype))
+    return fail(SLT_EINVAL, "softmax_xent: bad sizes");
+  if (!z || !tokens || !loss || !workspace) return fail(SLT_EINVAL, "softmax_xent: NULL pointer");
+  return launch_softmax_xent(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtype, workspace, as_stream(stream));
+}
+
+}  // extern "C"

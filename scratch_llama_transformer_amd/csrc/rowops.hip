@@ -1,0 +1,1042 @@
+// Bandwidth-bound kernels of the training step: embedding, norms, MLP
+// activations, fused softmax cross-entropy, AdamW, casts and the RoPE table.
+//
+// Layout rules: one 64-lane wavefront per row for the norms (rows are at most
+// a few KB, so a row is read with 16-byte vector loads by one wave and reduced
+// with cross-lane shuffles); flat vectorised grid-stride loops for the
+// elementwise kernels; one 256-thread block per row for the loss, whose rows
+// are up to 100 KB.  Every reduction runs in a fixed order, so results do not
+// depend on scheduling (Hephaistos, "Design notes": results independent of the
+// thread count).
+#include "slt_internal.h"
+
+#include <math.h>
+
+#include <algorithm>
+#include <initializer_list>
+#include <type_traits>
+
+namespace slt {
+
+namespace {
+
+constexpr int kWave = 64;
+
+template <typename T, int VEC>
+struct alignas(sizeof(T) * VEC) Pack {
+  T e[VEC];
+};
+
+template <typename T, int VEC>
+__device__ __forceinline__ void load_f(const T* p, float (&f)[VEC]) {
+  Pack<T, VEC> pk = *reinterpret_cast<const Pack<T, VEC>*>(p);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) f[i] = to_f32(pk.e[i]);
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void store_f(T* p, const float (&f)[VEC]) {
+  Pack<T, VEC> pk;
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) pk.e[i] = from_f32<T>(f[i]);
+  *reinterpret_cast<Pack<T, VEC>*>(p) = pk;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+inline bool aligned(const void* p, int bytes) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+
+inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// ---------------------------------------------------------------------------
+// Embedding forward: x[i, :] = wte[id_i, :].  An id outside [0, V) yields a
+// NaN row instead of an out-of-bounds read.
+// ---------------------------------------------------------------------------
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void embedding_fwd_k(const int32_t* __restrict__ tok, int T_, int64_t ld,
+                                                       const T* __restrict__ wte, T* __restrict__ x, int N,
+                                                       int V, int C) {
+  const int cv = C / VEC;
+  const int64_t total = (int64_t)N * cv;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int i = (int)(idx / cv);
+    const int c = (int)(idx % cv) * VEC;
+    const int id = tok[(int64_t)(i / T_) * ld + (i % T_)];
+    float f[VEC];
+    if (id >= 0 && id < V) {
+      load_f<T, VEC>(wte + (int64_t)id * C + c, f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) f[e] = __builtin_nanf("");
+    }
+    store_f<T, VEC>(x + (int64_t)i * C + c, f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Embedding backward, deterministic:
+//  1. per chunk of 256 positions: rank of each position among earlier equal
+//     ids of the chunk, and the count of each id in the chunk;
+//  2. per id: exclusive prefix of the chunk counts (in chunk order) and total;
+//  3. exclusive scan of the totals -> start of each id in the sorted order;
+//  4. scatter: position i goes to start[id] + prefix[chunk][id] + rank
+//     (a stable counting sort by id, so positions of an id are increasing);
+//  5. tiles of 16 sorted entries: one wave sums each run of equal ids in
+//     order; runs wholly inside a tile are final, the others leave a head or
+//     tail partial;
+//  6. per id: zero if absent; for ids spanning tiles, tail + heads in tile
+//     order.
+// ---------------------------------------------------------------------------
+constexpr int kEmbChunk = 256;
+constexpr int kEmbTile = 16;
+
+struct EmbWs {
+  int32_t* cnt;     // [nchunk][V]
+  int32_t* rank;    // [N]
+  int32_t* start;   // [V + 1]
+  int32_t* total;   // [V]
+  int32_t* sorted;  // [N]
+  float* head;      // [ntile][C]
+  float* tail;      // [ntile][C]
+};
+
+inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+EmbWs emb_ws_layout(void* base, int64_t N, int V, int C) {
+  char* p = static_cast<char*>(base);
+  const int64_t nchunk = (N + kEmbChunk - 1) / kEmbChunk;
+  const int64_t ntile = (N + kEmbTile - 1) / kEmbTile;
+  EmbWs w;
+  w.cnt = reinterpret_cast<int32_t*>(p); p += align256(nchunk * V * 4);
+  w.rank = reinterpret_cast<int32_t*>(p); p += align256(N * 4);
+  w.start = reinterpret_cast<int32_t*>(p); p += align256((int64_t)(V + 1) * 4);
+  w.total = reinterpret_cast<int32_t*>(p); p += align256((int64_t)V * 4);
+  w.sorted = reinterpret_cast<int32_t*>(p); p += align256(N * 4);
+  w.head = reinterpret_cast<float*>(p); p += align256(ntile * C * 4);
+  w.tail = reinterpret_cast<float*>(p); p += align256(ntile * C * 4);
+  return w;
+}
+
+int64_t emb_ws_bytes(int64_t N, int V, int C) {
+  const int64_t nchunk = (N + kEmbChunk - 1) / kEmbChunk;
+  const int64_t ntile = (N + kEmbTile - 1) / kEmbTile;
+  return align256(nchunk * V * 4) + 2 * align256(N * 4) + align256((int64_t)(V + 1) * 4) +
+         align256((int64_t)V * 4) + 2 * align256(ntile * C * 4);
+}
+
+__global__ void fill_i32_k(int32_t* p, int32_t v, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ __launch_bounds__(kEmbChunk) void emb_chunk_rank_k(const int32_t* __restrict__ tok, int T_,
+                                                               int64_t ld, int N, int V, EmbWs w) {
+  __shared__ int32_t ids[kEmbChunk];
+  const int t = threadIdx.x;
+  const int i = blockIdx.x * kEmbChunk + t;
+  int id = -1;
+  if (i < N) {
+    id = tok[(int64_t)(i / T_) * ld + (i % T_)];
+    if (id < 0 || id >= V) id = -1;
+  }
+  ids[t] = id;
+  __syncthreads();
+  if (id < 0) return;
+  int before = 0, after = 0;
+  for (int j = 0; j < kEmbChunk; ++j) {
+    const int o = ids[j];
+    before += (o == id) & (j < t);
+    after += (o == id) & (j > t);
+  }
+  w.rank[i] = before;
+  if (after == 0) w.cnt[(int64_t)blockIdx.x * V + id] = before + 1;
+}
+
+__global__ void emb_col_prefix_k(int V, int nchunk, EmbWs w) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= V) return;
+  int run = 0;
+  for (int c = 0; c < nchunk; ++c) {
+    const int64_t k = (int64_t)c * V + v;
+    const int x = w.cnt[k];
+    w.cnt[k] = run;
+    run += x;
+  }
+  w.total[v] = run;
+}
+
+// Exclusive scan of total[0..V) into start[0..V] by one 1024-thread block.
+__global__ __launch_bounds__(1024) void emb_scan_k(int V, EmbWs w) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int per = (V + 1023) / 1024;
+  const int b = t * per, e = min(V, b + per);
+  int s = 0;
+  for (int k = b; k < e; ++k) s += w.total[k];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
+    const int add = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int run = t == 0 ? 0 : part[t - 1];
+  for (int k = b; k < e; ++k) {
+    w.start[k] = run;
+    run += w.total[k];
+  }
+  if (t == 1023) w.start[V] = part[1023];
+}
+
+__global__ void emb_scatter_k(const int32_t* __restrict__ tok, int T_, int64_t ld, int N, int V, EmbWs w) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N) return;
+  const int id = tok[(int64_t)(i / T_) * ld + (i % T_)];
+  if (id < 0 || id >= V) return;
+  const int chunk = i / kEmbChunk;
+  w.sorted[w.start[id] + w.cnt[(int64_t)chunk * V + id] + w.rank[i]] = i;
+}
+
+// One wave per tile of kEmbTile sorted entries; lane owns VEC-column groups.
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict__ tok, int T_, int64_t ld,
+                                                      const T* __restrict__ dx, float* __restrict__ dwte,
+                                                      int N, int V_, int C, EmbWs w) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int tile = blockIdx.x * 4 + wave;
+  const int s = tile * kEmbTile;
+  const int nvalid = min(N, w.start[V_]);  // ids outside [0, V) are not sorted
+  if (s >= nvalid) return;
+  const int e = min(nvalid, s + kEmbTile);
+  int pos[kEmbTile], ids[kEmbTile];
+#pragma unroll
+  for (int k = 0; k < kEmbTile; ++k) {
+    pos[k] = s + k < e ? w.sorted[s + k] : 0;
+    ids[k] = s + k < e ? tok[(int64_t)(pos[k] / T_) * ld + (pos[k] % T_)] : -1;
+  }
+  for (int c0 = lane * VEC; c0 < C; c0 += kWave * VEC) {
+    float acc[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kEmbTile; ++k) {
+      if (s + k < e) {
+        float f[VEC];
+        load_f<T, VEC>(dx + (int64_t)pos[k] * C + c0, f);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) acc[q] += f[q];
+        const bool last = (k == kEmbTile - 1) || (s + k + 1 >= e) || (ids[k + 1] != ids[k]);
+        if (last) {
+          const int id = ids[k];
+          const int rs = w.start[id], re = w.start[id + 1];
+          float* dst;
+          if (rs < s) dst = w.head + (int64_t)tile * C;          // continues from an earlier tile
+          else if (re > e) dst = w.tail + (int64_t)tile * C;     // continues into a later tile
+          else dst = dwte + (int64_t)id * C;                     // complete inside this tile
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) {
+            dst[c0 + q] = acc[q];
+            acc[q] = 0.f;
+          }
+        }
+      }
+    }
+  }
+}
+
+// One wave per vocabulary row: zero rows, and rows spanning several tiles.
+__global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte, int V, int C, EmbWs w) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int v = blockIdx.x * 4 + wave;
+  if (v >= V) return;
+  const int rs = w.start[v], re = w.start[v + 1];
+  float* row = dwte + (int64_t)v * C;
+  if (re == rs) {
+    for (int c = lane; c < C; c += kWave) row[c] = 0.f;
+    return;
+  }
+  const int t0 = rs / kEmbTile, t1 = (re - 1) / kEmbTile;
+  if (t0 == t1) return;
+  for (int c = lane; c < C; c += kWave) {
+    float acc = w.tail[(int64_t)t0 * C + c];
+    for (int t = t0 + 1; t <= t1; ++t) acc += w.head[(int64_t)t * C + c];
+    row[c] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm and LayerNorm: one wave per row.  VEC-wide groups of columns; lane
+// l owns groups l, l+64, ... (at most NCH of them).
+// ---------------------------------------------------------------------------
+template <typename T, int VEC, int NCH>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_k(const T* __restrict__ x, const T* __restrict__ g,
+                                                     T* __restrict__ y, float* __restrict__ rstd,
+                                                     int rows, int C, float eps) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const T* xr = x + (int64_t)row * C;
+  float xv[NCH][VEC];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (lane + j * kWave) * VEC;
+    if (c < C) {
+      load_f<T, VEC>(xr + c, xv[j]);
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) ss += xv[j][q] * xv[j][q];
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)C + eps);
+  if (lane == 0) rstd[row] = r;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (lane + j * kWave) * VEC;
+    if (c < C) {
+      float gv[VEC], out[VEC];
+      load_f<T, VEC>(g + c, gv);
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) out[q] = xv[j][q] * r * gv[q];
+      store_f<T, VEC>(y + (int64_t)row * C + c, out);
+    }
+  }
+}
+
+template <typename T, int VEC, int NCH>
+__global__ __launch_bounds__(256) void layernorm_fwd_k(const T* __restrict__ x, const T* __restrict__ gm,
+                                                       const T* __restrict__ bt, T* __restrict__ y,
+                                                       float* __restrict__ mean, float* __restrict__ rstd,
+                                                       int rows, int C, float eps) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const T* xr = x + (int64_t)row * C;
+  float xv[NCH][VEC];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (lane + j * kWave) * VEC;
+    if (c < C) {
+      load_f<T, VEC>(xr + c, xv[j]);
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) s += xv[j][q];
+    }
+  }
+  const float mu = wave_sum(s) / (float)C;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (lane + j * kWave) * VEC;
+    if (c < C) {
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) {
+        const float d = xv[j][q] - mu;
+        ss += d * d;
+      }
+    }
+  }
+  const float r = 1.0f / sqrtf(wave_sum(ss) / (float)C + eps);
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = r;
+  }
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (lane + j * kWave) * VEC;
+    if (c < C) {
+      float gv[VEC], bv[VEC], out[VEC];
+      load_f<T, VEC>(gm + c, gv);
+      load_f<T, VEC>(bt + c, bv);
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) out[q] = (xv[j][q] - mu) * r * gv[q] + bv[q];
+      store_f<T, VEC>(y + (int64_t)row * C + c, out);
+    }
+  }
+}
+
+// Norm backward.  Block b (4 waves) handles rows b*4 + wave + k*gridDim*4 and
+// leaves per-column partial sums of dy*xh (and dy for LayerNorm) in
+// part[b][C] (and part[nb + b][C]); norm_colsum_k adds the partials in block
+// order.
+template <typename T, int VEC, int NCH, bool LN>
+__global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const T* __restrict__ g,
+                                                  const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                  const T* __restrict__ dy, const T* dres, T* dx,
+                                                  float* __restrict__ part, int rows, int C) {
+  extern __shared__ float red[];  // [C] (x2 for LayerNorm)
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  float pg[NCH][VEC], pb[NCH][VEC];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j)
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) pg[j][q] = pb[j][q] = 0.f;
+
+  for (int row = blockIdx.x * 4 + wave; row < rows; row += gridDim.x * 4) {
+    const int64_t base = (int64_t)row * C;
+    const float r = rstd[row];
+    const float mu = LN ? mean[row] : 0.f;
+    float xh[NCH][VEC], dxh[NCH][VEC];
+    float s1 = 0.f, s2 = 0.f;  // sum dxh, sum dxh*xh
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = (lane + j * kWave) * VEC;
+      if (c < C) {
+        float xv[VEC], dv[VEC], gv[VEC];
+        load_f<T, VEC>(x + base + c, xv);
+        load_f<T, VEC>(dy + base + c, dv);
+        load_f<T, VEC>(g + c, gv);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) {
+          xh[j][q] = (xv[q] - mu) * r;
+          dxh[j][q] = dv[q] * gv[q];
+          s1 += dxh[j][q];
+          s2 += dxh[j][q] * xh[j][q];
+          pg[j][q] += dv[q] * xh[j][q];
+          pb[j][q] += dv[q];
+        }
+      }
+    }
+    const float m2 = wave_sum(s2) / (float)C;
+    const float m1 = LN ? wave_sum(s1) / (float)C : 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = (lane + j * kWave) * VEC;
+      if (c < C) {
+        float out[VEC];
+        float rv[VEC];
+        if (dres != nullptr) {
+          load_f<T, VEC>(dres + base + c, rv);
+        } else {
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) rv[q] = 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) out[q] = rv[q] + r * (dxh[j][q] - m1 - xh[j][q] * m2);
+        store_f<T, VEC>(dx + base + c, out);
+      }
+    }
+  }
+  // Combine the 4 waves' column partials in wave order, then write this
+  // block's partial row.
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int c = (lane + j * kWave) * VEC;
+        if (c < C) {
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) {
+            red[c + q] = (w == 0 ? 0.f : red[c + q]) + pg[j][q];
+            if (LN) red[C + c + q] = (w == 0 ? 0.f : red[C + c + q]) + pb[j][q];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    part[(int64_t)blockIdx.x * C + c] = red[c];
+    if (LN) part[(int64_t)(gridDim.x + blockIdx.x) * C + c] = red[C + c];
+  }
+}
+
+__global__ void norm_colsum_k(const float* __restrict__ part, int nb, int C, float* __restrict__ out) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float s = 0.f;
+  for (int b = 0; b < nb; ++b) s += part[(int64_t)b * C + c];
+  out[c] = s;
+}
+
+constexpr int kNormBwdBlocks = 1024;
+
+// ---------------------------------------------------------------------------
+// SwiGLU and GELU on [rows, F] with row strides.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void swiglu_fwd_k(const T* __restrict__ a, const T* __restrict__ b,
+                                                    T* __restrict__ h, int rows, int F, int64_t lda,
+                                                    int64_t ldb, int64_t ldh) {
+  const int fv = F / VEC;
+  const int64_t total = (int64_t)rows * fv;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / fv;
+    const int c = (int)(idx % fv) * VEC;
+    float av[VEC], bv[VEC], out[VEC];
+    load_f<T, VEC>(a + r * lda + c, av);
+    load_f<T, VEC>(b + r * ldb + c, bv);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) out[q] = av[q] * sigmoidf_(av[q]) * bv[q];
+    store_f<T, VEC>(h + r * ldh + c, out);
+  }
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void swiglu_bwd_k(const T* __restrict__ a, const T* __restrict__ b,
+                                                    const T* __restrict__ dh, T* __restrict__ da,
+                                                    T* __restrict__ db, int rows, int F, int64_t lda,
+                                                    int64_t ldb, int64_t lddh, int64_t ldda, int64_t lddb) {
+  const int fv = F / VEC;
+  const int64_t total = (int64_t)rows * fv;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / fv;
+    const int c = (int)(idx % fv) * VEC;
+    float av[VEC], bv[VEC], hv[VEC], oa[VEC], ob[VEC];
+    load_f<T, VEC>(a + r * lda + c, av);
+    load_f<T, VEC>(b + r * ldb + c, bv);
+    load_f<T, VEC>(dh + r * lddh + c, hv);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      const float sg = sigmoidf_(av[q]);
+      ob[q] = hv[q] * av[q] * sg;
+      oa[q] = hv[q] * bv[q] * sg * (1.0f + av[q] * (1.0f - sg));
+    }
+    store_f<T, VEC>(da + r * ldda + c, oa);
+    store_f<T, VEC>(db + r * lddb + c, ob);
+  }
+}
+
+constexpr float kGeluK = 0.7978845608028654f;  // sqrt(2/pi)
+constexpr float kGeluC = 0.044715f;
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void gelu_fwd_k(const T* __restrict__ a, T* __restrict__ u, int rows, int F,
+                                                  int64_t lda, int64_t ldu) {
+  const int fv = F / VEC;
+  const int64_t total = (int64_t)rows * fv;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / fv;
+    const int c = (int)(idx % fv) * VEC;
+    float av[VEC], out[VEC];
+    load_f<T, VEC>(a + r * lda + c, av);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      const float x = av[q];
+      out[q] = 0.5f * x * (1.0f + tanhf(kGeluK * (x + kGeluC * x * x * x)));
+    }
+    store_f<T, VEC>(u + r * ldu + c, out);
+  }
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void gelu_bwd_k(const T* __restrict__ a, const T* __restrict__ du,
+                                                  T* __restrict__ da, int rows, int F, int64_t lda,
+                                                  int64_t lddu, int64_t ldda) {
+  const int fv = F / VEC;
+  const int64_t total = (int64_t)rows * fv;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / fv;
+    const int c = (int)(idx % fv) * VEC;
+    float av[VEC], gv[VEC], out[VEC];
+    load_f<T, VEC>(a + r * lda + c, av);
+    load_f<T, VEC>(du + r * lddu + c, gv);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      const float x = av[q];
+      const float t = tanhf(kGeluK * (x + kGeluC * x * x * x));
+      const float dt = (1.0f - t * t) * kGeluK * (1.0f + 3.0f * kGeluC * x * x);
+      out[q] = gv[q] * (0.5f * (1.0f + t) + 0.5f * x * dt);
+    }
+    store_f<T, VEC>(da + r * ldda + c, out);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused softmax cross-entropy: one 256-thread block per row.  Pass 1 keeps a
+// running (max, sum of exp) per thread and merges them across the block;
+// pass 2 overwrites the logits with (softmax - onehot) / rows.  The row loss
+// lse - z[y] goes to rowloss[]; xent_mean_k adds those in index order.
+// ---------------------------------------------------------------------------
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void xent_rows_k(T* z, int64_t ldz, const int32_t* __restrict__ tok, int T_,
+                                                   int64_t ld, int V, int rows, float* __restrict__ rowloss,
+                                                   float* lse_out) {
+  __shared__ float sm[8], ss[8];
+  __shared__ float zy_s;
+  const int row = blockIdx.x;
+  T* zr = z + (int64_t)row * ldz;
+  const int y = tok[(int64_t)(row / T_) * ld + (row % T_) + 1];
+  const int t = threadIdx.x;
+  if (t == 0) zy_s = (y >= 0 && y < V) ? to_f32(zr[y]) : __builtin_nanf("");
+  float m = -INFINITY, s = 0.f;
+  for (int c = t * VEC; c < V; c += 256 * VEC) {
+    float f[VEC];
+    load_f<T, VEC>(zr + c, f);
+    float mx = f[0];
+#pragma unroll
+    for (int q = 1; q < VEC; ++q) mx = fmaxf(mx, f[q]);
+    const float mn = fmaxf(m, mx);
+    float add = 0.f;
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) add += __expf(f[q] - mn);
+    s = s * __expf(m - mn) + add;
+    m = mn;
+  }
+  // merge (m, s) over the wave, then over the 4 waves
+  const float wm = wave_max(m);
+  float wsum = wave_sum(m == -INFINITY ? 0.f : s * __expf(m - wm));
+  const int wave = t / kWave, lane = t % kWave;
+  if (lane == 0) {
+    sm[wave] = wm;
+    ss[wave] = wsum;
+  }
+  __syncthreads();
+  float M = sm[0];
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w]);
+  float S = 0.f;
+  for (int w = 0; w < 4; ++w) S += ss[w] * __expf(sm[w] - M);
+  const float lse = M + logf(S);
+  const float inv_rows = 1.0f / (float)rows;
+  if (t == 0) {
+    rowloss[row] = lse - zy_s;
+    if (lse_out) lse_out[row] = lse;
+  }
+  for (int c = t * VEC; c < V; c += 256 * VEC) {
+    float f[VEC];
+    load_f<T, VEC>(zr + c, f);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) f[q] = (__expf(f[q] - lse) - (c + q == y ? 1.0f : 0.0f)) * inv_rows;
+    store_f<T, VEC>(zr + c, f);
+  }
+}
+
+__global__ __launch_bounds__(1024) void xent_mean_k(const float* __restrict__ rowloss, int rows,
+                                                    float* __restrict__ loss) {
+  __shared__ float part[1024];
+  const int t = threadIdx.x;
+  float s = 0.f;
+  for (int i = t; i < rows; i += 1024) s += rowloss[i];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (t < off) part[t] += part[t + off];
+    __syncthreads();
+  }
+  if (t == 0) *loss = part[0] / (float)rows;
+}
+
+// ---------------------------------------------------------------------------
+// AdamW over a flat fp32 buffer, 4 elements per thread per step.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void adamw_one(float& th, float g, float& m, float& v, float b1, float b2,
+                                          float ib1, float ib2, float lr, float eps, float wd) {
+  m = b1 * m + (1.0f - b1) * g;
+  v = b2 * v + (1.0f - b2) * g * g;
+  const float mh = m * ib1;
+  const float vh = v * ib2;
+  th = th - lr * (mh / (sqrtf(vh) + eps) + wd * th);
+}
+
+__global__ __launch_bounds__(256) void adamw_k(int64_t n, float* __restrict__ th, uint16_t* __restrict__ shadow,
+                                               const float* __restrict__ g, float* __restrict__ m,
+                                               float* __restrict__ v, float b1, float b2, float ib1, float ib2,
+                                               float lr, float eps, float wd, const uint8_t* __restrict__ mask) {
+  const int64_t n4 = n / 4;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    float4 t4 = reinterpret_cast<float4*>(th)[i];
+    const float4 g4 = reinterpret_cast<const float4*>(g)[i];
+    float4 m4 = reinterpret_cast<float4*>(m)[i];
+    float4 v4 = reinterpret_cast<float4*>(v)[i];
+    float w[4] = {wd, wd, wd, wd};
+    if (mask) {
+      const uchar4 k = reinterpret_cast<const uchar4*>(mask)[i];
+      w[0] = k.x ? wd : 0.f; w[1] = k.y ? wd : 0.f; w[2] = k.z ? wd : 0.f; w[3] = k.w ? wd : 0.f;
+    }
+    adamw_one(t4.x, g4.x, m4.x, v4.x, b1, b2, ib1, ib2, lr, eps, w[0]);
+    adamw_one(t4.y, g4.y, m4.y, v4.y, b1, b2, ib1, ib2, lr, eps, w[1]);
+    adamw_one(t4.z, g4.z, m4.z, v4.z, b1, b2, ib1, ib2, lr, eps, w[2]);
+    adamw_one(t4.w, g4.w, m4.w, v4.w, b1, b2, ib1, ib2, lr, eps, w[3]);
+    reinterpret_cast<float4*>(th)[i] = t4;
+    reinterpret_cast<float4*>(m)[i] = m4;
+    reinterpret_cast<float4*>(v)[i] = v4;
+    if (shadow) {
+      ushort4 s4;
+      s4.x = f32_to_bf16_bits(t4.x); s4.y = f32_to_bf16_bits(t4.y);
+      s4.z = f32_to_bf16_bits(t4.z); s4.w = f32_to_bf16_bits(t4.w);
+      reinterpret_cast<ushort4*>(shadow)[i] = s4;
+    }
+  }
+  // tail elements
+  const int64_t i = n4 * 4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (blockIdx.x == 0 && i < n) {
+    float t1 = th[i], m1 = m[i], v1 = v[i];
+    adamw_one(t1, g[i], m1, v1, b1, b2, ib1, ib2, lr, eps, (mask && !mask[i]) ? 0.f : wd);
+    th[i] = t1; m[i] = m1; v[i] = v1;
+    if (shadow) shadow[i] = f32_to_bf16_bits(t1);
+  }
+}
+
+__global__ __launch_bounds__(256) void cast_bf16_k(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                                   int64_t n) {
+  const int64_t n4 = n / 4;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 f = reinterpret_cast<const float4*>(src)[i];
+    ushort4 s;
+    s.x = f32_to_bf16_bits(f.x); s.y = f32_to_bf16_bits(f.y);
+    s.z = f32_to_bf16_bits(f.z); s.w = f32_to_bf16_bits(f.w);
+    reinterpret_cast<ushort4*>(dst)[i] = s;
+  }
+  const int64_t i = n4 * 4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (blockIdx.x == 0 && i < n) dst[i] = f32_to_bf16_bits(src[i]);
+}
+
+__global__ void fill_f32_k(float* p, float v, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// RoPE table from float64 angles: cs[t*R + 2j] = cos, cs[t*R + 2j + 1] = sin.
+__global__ void rope_table_k(int T_, int R, double base, float* cs) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = R / 2;
+  if (idx >= T_ * h) return;
+  const int t = idx / h, j = idx % h;
+  const double theta = pow(base, -2.0 * (double)j / (double)R);
+  const double ang = (double)t * theta;
+  cs[(int64_t)t * R + 2 * j] = (float)cos(ang);
+  cs[(int64_t)t * R + 2 * j + 1] = (float)sin(ang);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Philox-4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64 multiplies with the
+// key bumped by the Weyl constants between rounds.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline void philox4x32_10(const uint32_t in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  uint32_t c0 = in[0], c1 = in[1], c2 = in[2], c3 = in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+namespace {
+// kind 0: N(0, std^2) by Box-Muller on the first two Philox outputs of
+// counter (index, 0, 0, 0); kind 1: constant std (used for ones and zeros).
+__global__ void model_init_k(float* dst, int64_t n, int64_t index0, uint32_t k0, uint32_t k1, float std,
+                             int kind) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    if (kind == 1) {
+      dst[i] = std;
+      continue;
+    }
+    const uint64_t idx = (uint64_t)(index0 + i);
+    const uint32_t ctr[4] = {(uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u};
+    const uint32_t key[2] = {k0, k1};
+    uint32_t r[4];
+    philox4x32_10(ctr, key, r);
+    const float u1 = ((float)r[0] + 0.5f) * 2.3283064365386963e-10f;  // (0, 1)
+    const float u2 = ((float)r[1] + 0.5f) * 2.3283064365386963e-10f;
+    const float z = sqrtf(-2.0f * logf(u1)) * cosf(6.283185307179586f * u2);
+    dst[i] = z * std;
+  }
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static int grid_for(int64_t work, int per_block = 256, int cap = 65536) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+template <typename T>
+static constexpr int full_vec() { return 16 / (int)sizeof(T); }
+
+slt_status launch_embedding_fwd(const int32_t* tok, int B, int T_, int64_t ld, const void* wte, void* x, int V,
+                                int C, int dtype, hipStream_t s) {
+  const int N = B * T_;
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    constexpr int VEC = full_vec<T>();
+    if (C % VEC == 0 && aligned(wte, 16) && aligned(x, 16))
+      embedding_fwd_k<T, VEC><<<grid_for((int64_t)N * C / VEC), 256, 0, s>>>(
+          tok, T_, ld, (const T*)wte, (T*)x, N, V, C);
+    else
+      embedding_fwd_k<T, 1><<<grid_for((int64_t)N * C), 256, 0, s>>>(tok, T_, ld, (const T*)wte, (T*)x, N, V, C);
+  };
+  if (dtype == SLT_BF16) go(bf16{}); else go(float{});
+  return check_launch("embedding_fwd");
+}
+
+int64_t embedding_bwd_ws(int64_t N, int V) {
+  // head/tail partials are sized for C up to 4096
+  return emb_ws_bytes(N, V, 4096);
+}
+
+slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, const void* dx, float* dwte, int V,
+                                int C, int dtype, void* ws, hipStream_t s) {
+  const int N = B * T_;
+  EmbWs w = emb_ws_layout(ws, N, V, 4096);
+  const int nchunk = cdiv(N, kEmbChunk);
+  const int ntile = cdiv(N, kEmbTile);
+  fill_i32_k<<<grid_for((int64_t)nchunk * V), 256, 0, s>>>(w.cnt, 0, (int64_t)nchunk * V);
+  emb_chunk_rank_k<<<nchunk, kEmbChunk, 0, s>>>(tok, T_, ld, N, V, w);
+  emb_col_prefix_k<<<cdiv(V, 256), 256, 0, s>>>(V, nchunk, w);
+  emb_scan_k<<<1, 1024, 0, s>>>(V, w);
+  emb_scatter_k<<<cdiv(N, 256), 256, 0, s>>>(tok, T_, ld, N, V, w);
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    constexpr int VEC = full_vec<T>();
+    if (C % VEC == 0 && aligned(dx, 16))
+      emb_tile_sum_k<T, VEC><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w);
+    else
+      emb_tile_sum_k<T, 1><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w);
+  };
+  if (dtype == SLT_BF16) go(bf16{}); else go(float{});
+  emb_row_finish_k<<<cdiv(V, 4), 256, 0, s>>>(dwte, V, C, w);
+  return check_launch("embedding_bwd");
+}
+
+// Picks VEC (16-byte groups when C allows) and NCH = groups per lane.
+template <typename T, typename F>
+static slt_status norm_dispatch(int C, bool vec_ok, F&& f) {
+  constexpr int FV = full_vec<T>();
+  if (vec_ok && C % FV == 0) {
+    const int nch = cdiv(C, 64 * FV);
+    if (nch <= 1) return f(std::integral_constant<int, FV>{}, std::integral_constant<int, 1>{});
+    if (nch <= 2) return f(std::integral_constant<int, FV>{}, std::integral_constant<int, 2>{});
+    if (nch <= 4) return f(std::integral_constant<int, FV>{}, std::integral_constant<int, 4>{});
+    if (nch <= 8) return f(std::integral_constant<int, FV>{}, std::integral_constant<int, 8>{});
+    return fail(SLT_EUNSUPPORTED, "norm: C too large");
+  }
+  const int nch = cdiv(C, 64);
+  if (nch <= 1) return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+  if (nch <= 2) return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+  if (nch <= 4) return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{});
+  if (nch <= 8) return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{});
+  return fail(SLT_EUNSUPPORTED, "norm: C too large for an unaligned row");
+}
+
+slt_status launch_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd, int rows, int C, float eps,
+                              int dtype, hipStream_t s) {
+  auto go = [&](auto tag) -> slt_status {
+    using T = decltype(tag);
+    const bool ok = aligned(x, 16) && aligned(g, 16) && aligned(y, 16);
+    return norm_dispatch<T>(C, ok, [&](auto vec, auto nch) -> slt_status {
+      rmsnorm_fwd_k<T, decltype(vec)::value, decltype(nch)::value><<<cdiv(rows, 4), 256, 0, s>>>(
+          (const T*)x, (const T*)g, (T*)y, rstd, rows, C, eps);
+      return check_launch("rmsnorm_fwd");
+    });
+  };
+  return dtype == SLT_BF16 ? go(bf16{}) : go(float{});
+}
+
+slt_status launch_layernorm_fwd(const void* x, const void* gm, const void* bt, void* y, float* mean, float* rstd,
+                                int rows, int C, float eps, int dtype, hipStream_t s) {
+  auto go = [&](auto tag) -> slt_status {
+    using T = decltype(tag);
+    const bool ok = aligned(x, 16) && aligned(gm, 16) && aligned(bt, 16) && aligned(y, 16);
+    return norm_dispatch<T>(C, ok, [&](auto vec, auto nch) -> slt_status {
+      layernorm_fwd_k<T, decltype(vec)::value, decltype(nch)::value><<<cdiv(rows, 4), 256, 0, s>>>(
+          (const T*)x, (const T*)gm, (const T*)bt, (T*)y, mean, rstd, rows, C, eps);
+      return check_launch("layernorm_fwd");
+    });
+  };
+  return dtype == SLT_BF16 ? go(bf16{}) : go(float{});
+}
+
+int64_t norm_bwd_ws(int rows, int C) {
+  const int nb = std::min(kNormBwdBlocks, cdiv(rows, 4));
+  return (int64_t)2 * nb * C * 4;
+}
+
+template <bool LN>
+static slt_status norm_bwd_common(const void* x, const void* g, const float* mean, const float* rstd,
+                                  const void* dy, const void* dres, void* dx, float* dg, float* db, int rows,
+                                  int C, int dtype, void* ws, hipStream_t s) {
+  const int nb = std::max(1, std::min(kNormBwdBlocks, cdiv(rows, 4)));
+  float* part = static_cast<float*>(ws);
+  const size_t smem = (size_t)(LN ? 2 : 1) * C * sizeof(float);
+  auto go = [&](auto tag) -> slt_status {
+    using T = decltype(tag);
+    const bool ok = aligned(x, 16) && aligned(g, 16) && aligned(dy, 16) && aligned(dres, 16) && aligned(dx, 16);
+    return norm_dispatch<T>(C, ok, [&](auto vec, auto nch) -> slt_status {
+      norm_bwd_k<T, decltype(vec)::value, decltype(nch)::value, LN><<<nb, 256, smem, s>>>(
+          (const T*)x, (const T*)g, mean, rstd, (const T*)dy, (const T*)dres, (T*)dx, part, rows, C);
+      return check_launch("norm_bwd");
+    });
+  };
+  slt_status st = dtype == SLT_BF16 ? go(bf16{}) : go(float{});
+  if (st != SLT_OK) return st;
+  norm_colsum_k<<<cdiv(C, 256), 256, 0, s>>>(part, nb, C, dg);
+  if (LN) norm_colsum_k<<<cdiv(C, 256), 256, 0, s>>>(part + (int64_t)nb * C, nb, C, db);
+  return check_launch("norm_colsum");
+}
+
+slt_status launch_rmsnorm_bwd(const void* x, const void* g, const float* rstd, const void* dy, const void* dres,
+                              void* dx, float* dg, int rows, int C, int dtype, void* ws, hipStream_t s) {
+  return norm_bwd_common<false>(x, g, nullptr, rstd, dy, dres, dx, dg, nullptr, rows, C, dtype, ws, s);
+}
+
+slt_status launch_layernorm_bwd(const void* x, const void* gm, const float* mean, const float* rstd,
+                                const void* dy, const void* dres, void* dx, float* dgm, float* dbt, int rows,
+                                int C, int dtype, void* ws, hipStream_t s) {
+  return norm_bwd_common<true>(x, gm, mean, rstd, dy, dres, dx, dgm, dbt, rows, C, dtype, ws, s);
+}
+
+slt_status launch_rope_table(int T_, int R, float base, float* cs, hipStream_t s) {
+  const int n = T_ * (R / 2);
+  if (n == 0) return SLT_OK;
+  rope_table_k<<<cdiv(n, 256), 256, 0, s>>>(T_, R, (double)base, cs);
+  return check_launch("rope_table");
+}
+
+template <typename T>
+static bool ew_vec_ok(int F, std::initializer_list<int64_t> lds, std::initializer_list<const void*> ptrs) {
+  constexpr int FV = full_vec<T>();
+  if (F % FV) return false;
+  for (auto l : lds)
+    if (l % FV) return false;
+  for (auto p : ptrs)
+    if (!aligned(p, 16)) return false;
+  return true;
+}
+
+slt_status launch_swiglu_fwd(const void* a, const void* b, void* h, int rows, int F, int64_t lda, int64_t ldb,
+                             int64_t ldh, int dtype, hipStream_t s) {
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    constexpr int FV = full_vec<T>();
+    if (ew_vec_ok<T>(F, {lda, ldb, ldh}, {a, b, h}))
+      swiglu_fwd_k<T, FV><<<grid_for((int64_t)rows * F / FV), 256, 0, s>>>((const T*)a, (const T*)b, (T*)h, rows,
+                                                                          F, lda, ldb, ldh);
+    else
+      swiglu_fwd_k<T, 1><<<grid_for((int64_t)rows * F), 256, 0, s>>>((const T*)a, (const T*)b, (T*)h, rows, F, lda,
+                                                                     ldb, ldh);
+  };
+  if (dtype == SLT_BF16) go(bf16{}); else go(float{});
+  return check_launch("swiglu_fwd");
+}
+
+slt_status launch_swiglu_bwd(const void* a, const void* b, const void* dh, void* da, void* db, int rows, int F,
+                             int64_t lda, int64_t ldb, int64_t lddh, int64_t ldda, int64_t lddb, int dtype,
+                             hipStream_t s) {
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    constexpr int FV = full_vec<T>();
+    if (ew_vec_ok<T>(F, {lda, ldb, lddh, ldda, lddb}, {a, b, dh, da, db}))
+      swiglu_bwd_k<T, FV><<<grid_for((int64_t)rows * F / FV), 256, 0, s>>>(
+          (const T*)a, (const T*)b, (const T*)dh, (T*)da, (T*)db, rows, F, lda, ldb, lddh, ldda, lddb);
+    else
+      swiglu_bwd_k<T, 1><<<grid_for((int64_t)rows * F), 256, 0, s>>>(
+          (const T*)a, (const T*)b, (const T*)dh, (T*)da, (T*)db, rows, F, lda, ldb, lddh, ldda, lddb);
+  };
+  if (dtype == SLT_BF16) go(bf16{}); else go(float{});
+  return check_launch("swiglu_bwd");
+}
+
+slt_status launch_gelu_fwd(const void* a, void* u, int rows, int F, int64_t lda, int64_t ldu, int dtype,
+                           hipStream_t s) {
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    constexpr int FV = full_vec<T>();
+    if (ew_vec_ok<T>(F, {lda, ldu}, {a, u}))
+      gelu_fwd_k<T, FV><<<grid_for((int64_t)rows * F / FV), 256, 0, s>>>((const T*)a, (T*)u, rows, F, lda, ldu);
+    else
+      gelu_fwd_k<T, 1><<<grid_for((int64_t)rows * F), 256, 0, s>>>((const T*)a, (T*)u, rows, F, lda, ldu);
+  };
+  if (dtype == SLT_BF16) go(bf16{}); else go(float{});
+  return check_launch("gelu_fwd");
+}
+
+slt_status launch_gelu_bwd(const void* a, const void* du, void* da, int rows, int F, int64_t lda, int64_t lddu,
+                           int64_t ldda, int dtype, hipStream_t s) {
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    constexpr int FV = full_vec<T>();
+    if (ew_vec_ok<T>(F, {lda, lddu, ldda}, {a, du, da}))
+      gelu_bwd_k<T, FV><<<grid_for((int64_t)rows * F / FV), 256, 0, s>>>((const T*)a, (const T*)du, (T*)da, rows,
+                                                                        F, lda, lddu, ldda);
+    else
+      gelu_bwd_k<T, 1><<<grid_for((int64_t)rows * F), 256, 0, s>>>((const T*)a, (const T*)du, (T*)da, rows, F,
+                                                                   lda, lddu, ldda);
+  };
+  if (dtype == SLT_BF16) go(bf16{}); else go(float{});
+  return check_launch("gelu_bwd");
+}
+
+slt_status launch_softmax_xent(void* z, int64_t ldz, const int32_t* tok, int B, int T_, int64_t ld, int V,
+                               float* loss, float* lse, int dtype, void* ws, hipStream_t s) {
+  const int rows = B * T_;
+  float* rowloss = static_cast<float*>(ws);
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    constexpr int FV = full_vec<T>();
+    if (V % FV == 0 && ldz % FV == 0 && aligned(z, 16))
+      xent_rows_k<T, FV><<<rows, 256, 0, s>>>((T*)z, ldz, tok, T_, ld, V, rows, rowloss, lse);
+    else
+      xent_rows_k<T, 1><<<rows, 256, 0, s>>>((T*)z, ldz, tok, T_, ld, V, rows, rowloss, lse);
+  };
+  if (dtype == SLT_BF16) go(bf16{}); else go(float{});
+  xent_mean_k<<<1, 1024, 0, s>>>(rowloss, rows, loss);
+  return check_launch("softmax_xent");
+}
+
+slt_status launch_adamw(int64_t n, float* master, uint16_t* shadow, const float* g, float* m, float* v, int64_t t,
+                        float lr, float b1, float b2, float eps, float wd, const uint8_t* mask, hipStream_t s) {
+  const double bc1 = 1.0 - pow((double)b1, (double)t);
+  const double bc2 = 1.0 - pow((double)b2, (double)t);
+  adamw_k<<<grid_for(n / 4 + 1, 256, 8192), 256, 0, s>>>(n, master, shadow, g, m, v, b1, b2, (float)(1.0 / bc1),
+                                                           (float)(1.0 / bc2), lr, eps, wd, mask);
+  return check_launch("adamw");
+}
+
+slt_status launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {
+  cast_bf16_k<<<grid_for(n / 4 + 1, 256, 8192), 256, 0, s>>>(src, dst, n);
+  return check_launch("cast_bf16");
+}
+
+slt_status launch_fill_f32(float* dst, float value, int64_t n, hipStream_t s) {
+  fill_f32_k<<<grid_for(n, 256, 8192), 256, 0, s>>>(dst, value, n);
+  return check_launch("fill_f32");
+}
+
+slt_status launch_model_init_range(float* dst, int64_t n, int64_t index0, uint64_t seed, float std, int kind,
+                                   hipStream_t s) {
+  model_init_k<<<grid_for(n, 256, 8192), 256, 0, s>>>(dst, n, index0, (uint32_t)seed, (uint32_t)(seed >> 32), std,
+                                                      kind);
+  return check_launch("model_init");
+}
+
+}  // namespace slt
+
+extern "C" void slt_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  slt::philox4x32_10(ctr, key, out);
+}

@@ -1,0 +1,108 @@
+// Internal declarations shared by the HIP translation units of libslt.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "../../include/slt.h"
+
+namespace slt {
+
+// ---------------------------------------------------------------------------
+// Storage types.  bf16 is the upper half of an IEEE binary32.
+// ---------------------------------------------------------------------------
+struct bf16 {
+  uint16_t u;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(((uint32_t)x.u) << 16); }
+
+// Round to nearest, ties to even, from the binary32 bit pattern: add half an
+// ulp of the 16-bit result (0x7fff) plus the result's lowest bit so that exact
+// halves move to the even neighbour; NaNs stay quiet NaNs.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return bf16{f32_to_bf16_bits(x)}; }
+
+// ---------------------------------------------------------------------------
+// Error reporting (thread-local message)
+// ---------------------------------------------------------------------------
+void set_error(const std::string& msg);
+slt_status fail(slt_status code, const std::string& msg);
+slt_status check_launch(const char* what);
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (return hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+struct GemmArgs {
+  int M, N, K;
+  const void* A; int64_t lda; bool a_kmajor;
+  const void* B; int64_t ldb; bool b_kmajor;
+  void* C; int64_t ldc;
+  const void* R; int64_t ldr;
+  int in_dtype, out_dtype;
+  float* workspace; int64_t workspace_bytes;
+};
+slt_status launch_gemm(const GemmArgs& g, hipStream_t s);
+
+slt_status launch_embedding_fwd(const int32_t* tok, int B, int T, int64_t ld, const void* wte,
+                                void* x, int V, int C, int dtype, hipStream_t s);
+int64_t embedding_bwd_ws(int64_t N, int V);
+slt_status launch_embedding_bwd(const int32_t* tok, int B, int T, int64_t ld, const void* dx,
+                                float* dwte, int V, int C, int dtype, void* ws, hipStream_t s);
+int64_t norm_bwd_ws(int rows, int C);
+slt_status launch_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd, int rows, int C,
+                              float eps, int dtype, hipStream_t s);
+slt_status launch_rmsnorm_bwd(const void* x, const void* g, const float* rstd, const void* dy,
+                              const void* dres, void* dx, float* dg, int rows, int C, int dtype,
+                              void* ws, hipStream_t s);
+slt_status launch_layernorm_fwd(const void* x, const void* gm, const void* bt, void* y, float* mean,
+                                float* rstd, int rows, int C, float eps, int dtype, hipStream_t s);
+slt_status launch_layernorm_bwd(const void* x, const void* gm, const float* mean, const float* rstd,
+                                const void* dy, const void* dres, void* dx, float* dgm, float* dbt,
+                                int rows, int C, int dtype, void* ws, hipStream_t s);
+slt_status launch_rope_table(int T, int R, float base, float* cs, hipStream_t s);
+slt_status launch_swiglu_fwd(const void* a, const void* b, void* h, int rows, int F, int64_t lda,
+                             int64_t ldb, int64_t ldh, int dtype, hipStream_t s);
+slt_status launch_swiglu_bwd(const void* a, const void* b, const void* dh, void* da, void* db,
+                             int rows, int F, int64_t lda, int64_t ldb, int64_t lddh, int64_t ldda,
+                             int64_t lddb, int dtype, hipStream_t s);
+slt_status launch_gelu_fwd(const void* a, void* u, int rows, int F, int64_t lda, int64_t ldu,
+                           int dtype, hipStream_t s);
+slt_status launch_gelu_bwd(const void* a, const void* du, void* da, int rows, int F, int64_t lda,
+                           int64_t lddu, int64_t ldda, int dtype, hipStream_t s);
+slt_status launch_softmax_xent(void* z, int64_t ldz, const int32_t* tok, int B, int T, int64_t ld,
+                               int V, float* loss, float* lse, int dtype, void* ws, hipStream_t s);
+slt_status launch_adamw(int64_t n, float* master, uint16_t* shadow, const float* g, float* m,
+                        float* v, int64_t t, float lr, float b1, float b2, float eps, float wd,
+                        const uint8_t* mask, hipStream_t s);
+slt_status launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
+slt_status launch_fill_f32(float* dst, float value, int64_t n, hipStream_t s);
+slt_status launch_model_init_range(float* dst, int64_t n, int64_t index0, uint64_t seed, float std,
+                                   int kind, hipStream_t s);
+
+struct AttnArgs {
+  const void *q, *k, *v, *o, *dout;
+  void *dq, *dk, *dv, *out;
+  float* lse;
+  const float* lse_in;
+  int64_t ldq, ldk, ldv, ldo, lddo, lddq, lddk, lddv;
+  int B, T, H, Hkv, d, R, rope_mode, dtype;
+  const float* cs;
+  float* delta;  // workspace [B, H, T] for the backward
+};
+slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s);
+slt_status launch_attention_bwd(const AttnArgs& a, hipStream_t s);
+int64_t attention_bwd_ws(int B, int H, int T);
+
+}  // namespace slt

@@ -1,0 +1,81 @@
+"""Device buffers for one model and the three step calls.
+
+Holds the fp32 master weights, their bf16 copy (bf16 configurations), the
+AdamW moments, the gradient buffer, the activation arena and the scratch area,
+all allocated with torch on the current GPU, and calls the library's
+slt_forward_loss / slt_backward / slt_adamw_step on the current stream.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+class TrainStep:
+    def __init__(self, wcfg, params: dict | None = None, seed: int = 0, device: str = "cuda"):
+        self.w = wcfg
+        self.cfg = B.make_config(wcfg)
+        B.slt_validate(self.cfg)
+        self.layout, self.n = B.slt_param_layout(self.cfg)
+        self.device = torch.device(device)
+        self.bf16 = wcfg.act == "bf16"
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.master = torch.zeros(self.n, **f32)
+        if params is not None:
+            self.load_params(params)
+        else:
+            out_scale = float(1.0 / np.sqrt(2.0 * wcfg.L)) if wcfg.scale_out else 1.0
+            B.slt_model_init(self.cfg, seed, wcfg.init_std, out_scale, self.master)
+        self.shadow = torch.empty(self.n, dtype=torch.int16, device=self.device) if self.bf16 else None
+        self.m = torch.zeros(self.n, **f32)
+        self.v = torch.zeros(self.n, **f32)
+        self.grads = torch.empty(self.n, **f32)
+        act, scr = B.slt_workspace_bytes(self.cfg)
+        self.acts = torch.empty(act, dtype=torch.uint8, device=self.device)
+        self.scratch = torch.empty(scr, dtype=torch.uint8, device=self.device)
+        self.loss = torch.zeros(1, **f32)
+        self.t = 0
+        self.refresh_shadow()
+
+    # -- parameters ---------------------------------------------------------
+    def load_params(self, params: dict) -> None:
+        host = np.zeros(self.n, np.float32)
+        for t in self.layout:
+            a = np.asarray(params[t["name"]], np.float32).reshape(-1)
+            if a.size != t["numel"]:
+                raise ValueError(f"{t['name']}: {a.size} elements, layout says {t['numel']}")
+            host[t["offset"]:t["offset"] + t["numel"]] = a
+        self.master.copy_(torch.from_numpy(host))
+
+    def unpack(self, flat: torch.Tensor) -> dict:
+        host = flat.detach().float().cpu().numpy()
+        return {t["name"]: host[t["offset"]:t["offset"] + t["numel"]].reshape(
+            (t["cols"],) if t["rows"] == 1 else (t["rows"], t["cols"])) for t in self.layout}
+
+    def refresh_shadow(self) -> None:
+        if self.bf16:
+            B.slt_cast_bf16(self.master, self.shadow, self.n)
+
+    @property
+    def compute_params(self) -> torch.Tensor:
+        return self.shadow if self.bf16 else self.master
+
+    # -- the step -----------------------------------------------------------
+    def forward(self, tokens: torch.Tensor) -> None:
+        B.slt_forward_loss(self.cfg, self.compute_params, tokens, self.acts, self.scratch, self.loss)
+
+    def backward(self, tokens: torch.Tensor) -> None:
+        B.slt_backward(self.cfg, self.compute_params, tokens, self.acts, self.scratch, self.grads)
+
+    def adamw(self, lr=None, wd=None) -> None:
+        self.t += 1
+        w = self.w
+        B.slt_adamw_step(self.n, self.master, self.shadow, self.grads, self.m, self.v, self.t,
+                         w.lr if lr is None else lr, w.beta1, w.beta2, w.adam_eps, w.wd if wd is None else wd)
+
+    def step(self, tokens: torch.Tensor) -> None:
+        self.forward(tokens)
+        self.backward(tokens)
+        self.adamw()

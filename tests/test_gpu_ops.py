@@ -1,0 +1,390 @@
+"""Per-op parity of the HIP kernels with the oracle, through the C ABI.
+
+Each case prints its name before launching.  Inputs are seeded; bf16 inputs
+are bf16 values, so the oracle sees exactly what the kernel reads."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from parity import check, normwise, rms
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from scratch_llama_transformer_amd import binding
+    binding.load()
+    return binding
+
+
+def dev(a, dtype):
+    """host float64 array -> device tensor of dtype (bf16 rounds to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    return t.to(torch.bfloat16 if dtype == BF16 else torch.float32).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rnd(rng, shape, dtype, scale=1.0):
+    a = rng.standard_normal(shape) * scale
+    return O.bf16_round(a) if dtype == BF16 else a.astype(np.float32).astype(np.float64)
+
+
+def act(dtype):
+    return "bf16" if dtype == BF16 else "f32"
+
+
+def ref_round(x, dtype):
+    return O.bf16_round(x) if dtype == BF16 else x
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+def gemm_case(B, rng, M, N, K, a_k, b_k, ind, outd, resid=False, ws=False, sample=None):
+    say("gemm", M, N, K, a_k, b_k, ind, outd, resid, ws)
+    A = rnd(rng, (M, K) if a_k else (K, M), ind)
+    Bm = rnd(rng, (N, K) if b_k else (K, N), ind)
+    dA, dB = dev(A, ind), dev(Bm, ind)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16 if outd == BF16 else torch.float32, device="cuda")
+    R = None
+    Rh = None
+    if resid:
+        Rh = rnd(rng, (M, N), outd)
+        R = dev(Rh, outd)
+    W = torch.empty(64 << 20, dtype=torch.uint8, device="cuda") if ws else None
+    B.slt_gemm(M, N, K, dA, A.shape[1], a_k, dB, Bm.shape[1], b_k, C, N, R, N, ind, outd,
+               W, W.numel() if ws else 0)
+    got = host(C)
+    Am = A if a_k else A.T
+    Bn = Bm if b_k else Bm.T
+    rows = np.arange(M) if sample is None else np.unique(rng.integers(0, M, sample))
+    ref = Am[rows] @ Bn.T
+    if resid:
+        ref = ref + Rh[rows]
+    check(got[rows], ref_round(ref, outd), act(outd) if ind == outd else "bf16" if ind == BF16 else "f32",
+          f"gemm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("a_k,b_k", [(1, 1), (1, 0), (0, 0), (0, 1)])
+@pytest.mark.parametrize("ind,outd", [(BF16, BF16), (BF16, F32), (F32, F32)])
+def test_gemm_small_ragged(B, a_k, b_k, ind, outd):
+    rng = np.random.default_rng(1)
+    for (M, N, K) in [(37, 50, 29), (1, 1, 1), (130, 260, 96), (256, 128, 64), (200, 136, 520)]:
+        gemm_case(B, rng, M, N, K, a_k, b_k, ind, outd)
+    gemm_case(B, rng, 131, 77, 45, a_k, b_k, ind, outd, resid=True)
+    gemm_case(B, rng, 96, 72, 3000, a_k, b_k, ind, outd, ws=True)
+    gemm_case(B, rng, 96, 72, 3000, a_k, b_k, ind, outd, ws=True, resid=True)
+
+
+def test_gemm_zero_k_gives_residual_or_zero(B):
+    rng = np.random.default_rng(2)
+    gemm_case(B, rng, 17, 9, 0, 1, 1, F32, F32)
+    gemm_case(B, rng, 17, 9, 0, 1, 1, BF16, BF16, resid=True)
+
+
+@pytest.mark.parametrize("shape", [
+    # (M, N, K, a_k, b_k, in, out, residual, workspace): the step's products at full size
+    (16384, 1152, 384, 1, 1, BF16, BF16, False, False),     # qkv projection
+    (16384, 384, 1024, 1, 1, BF16, BF16, True, False),      # W2 with residual
+    (16384, 384, 2048, 1, 0, BF16, BF16, False, False),     # dX of [W1;W3]
+    (1152, 384, 16384, 0, 0, BF16, F32, False, True),       # dW of qkv (split K)
+    (4096, 384, 16384, 0, 0, BF16, F32, False, True),       # dW of lm_head
+    (16384, 1364, 256, 1, 1, F32, F32, False, False),       # fp32 [W1;W3], ragged N
+    (256, 682, 16384, 0, 0, F32, F32, False, True),         # fp32 dW of W2, ragged
+])
+def test_gemm_full_size_sampled_rows(B, shape):
+    rng = np.random.default_rng(3)
+    M, N, K, a_k, b_k, ind, outd, resid, ws = shape
+    gemm_case(B, rng, M, N, K, a_k, b_k, ind, outd, resid, ws, sample=48)
+
+
+# ---------------------------------------------------------------------------
+# Embedding
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("Bn,T,V,C,zipf", [(1, 16, 27, 16, False), (3, 37, 50, 24, False),
+                                          (64, 256, 4096, 384, True), (16, 1024, 32000, 1024, False)])
+def test_embedding_fwd_bwd(B, dtype, Bn, T, V, C, zipf):
+    say("embedding", Bn, T, V, C, zipf, dtype)
+    import slt_workloads as W
+    rng = np.random.default_rng(4)
+    tok = W.zipf_tokens(5, Bn, T + 1, V) if zipf else W.uniform_tokens(5, Bn, T + 1, V)
+    wte = rnd(rng, (V, C), dtype, 0.02)
+    dt = torch.from_numpy(tok).cuda()
+    x = torch.empty((Bn * T, C), dtype=torch.bfloat16 if dtype == BF16 else torch.float32, device="cuda")
+    B.slt_embedding_fwd(dt, Bn, T, T + 1, dev(wte, dtype), x, V, C, dtype)
+    ids = tok[:, :T].reshape(-1)
+    np.testing.assert_array_equal(host(x), wte[ids])
+    dx = rnd(rng, (Bn * T, C), dtype)
+    ws = torch.empty(B.slt_embedding_bwd_workspace(Bn * T, V), dtype=torch.uint8, device="cuda")
+    out = torch.full((V, C), float("nan"), device="cuda")
+    ddx = dev(dx, dtype)
+    B.slt_embedding_bwd(dt, Bn, T, T + 1, ddx, out, V, C, dtype, ws)
+    got = host(out)
+    ref = O.embedding_bwd(dx, ids, V)
+    unseen = np.setdiff1d(np.arange(V), ids)
+    assert np.all(got[unseen] == 0.0)
+    assert normwise(got, ref) < 1e-6
+    # deterministic: a second run is bitwise identical
+    out2 = torch.full((V, C), float("nan"), device="cuda")
+    B.slt_embedding_bwd(dt, Bn, T, T + 1, ddx, out2, V, C, dtype, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+# ---------------------------------------------------------------------------
+# Norms
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("rows,C", [(1, 16), (37, 42), (513, 384), (16384, 384), (2048, 1024)])
+def test_rmsnorm(B, dtype, rows, C):
+    say("rmsnorm", rows, C, dtype)
+    rng = np.random.default_rng(6)
+    x = rnd(rng, (rows, C), dtype, 2.0)
+    g = rnd(rng, (C,), dtype) * 0.3 + ref_round(np.ones(C), dtype)
+    g = ref_round(g, dtype)
+    y = torch.empty((rows, C), dtype=torch.bfloat16 if dtype == BF16 else torch.float32, device="cuda")
+    r = torch.empty(rows, device="cuda")
+    dx_, dg_ = dev(x, dtype), dev(g, dtype)
+    B.slt_rmsnorm_fwd(dx_, dg_, y, r, rows, C, 1e-5, dtype)
+    yr, rr = O.rmsnorm_fwd(x, g, 1e-5)
+    check(host(y), ref_round(yr, dtype), act(dtype), "rmsnorm y")
+    check(host(r), rr, "f32", "rmsnorm rstd")
+    dy = rnd(rng, (rows, C), dtype)
+    dres = rnd(rng, (rows, C), dtype)
+    ddx = torch.empty_like(y)
+    dg = torch.empty(C, device="cuda")
+    ws = torch.empty(B.slt_norm_bwd_workspace(rows, C), dtype=torch.uint8, device="cuda")
+    B.slt_rmsnorm_bwd(dx_, dg_, r, dev(dy, dtype), dev(dres, dtype), ddx, dg, rows, C, dtype, ws)
+    dxr, dgr = O.rmsnorm_bwd(x, g, rr, dy)
+    check(host(ddx), ref_round(dxr + dres, dtype), act(dtype), "rmsnorm dx")
+    check(host(dg), dgr, "f32" if dtype == F32 else "bf16", "rmsnorm dg")
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("rows,C", [(5, 16), (77, 40), (4096, 1024)])
+def test_layernorm(B, dtype, rows, C):
+    say("layernorm", rows, C, dtype)
+    rng = np.random.default_rng(7)
+    x = rnd(rng, (rows, C), dtype, 2.0) + ref_round(np.full((rows, C), 0.5), dtype)
+    x = ref_round(x, dtype)
+    g = ref_round(1.0 + 0.3 * rng.standard_normal(C), dtype)
+    bt = ref_round(0.2 * rng.standard_normal(C), dtype)
+    y = torch.empty((rows, C), dtype=torch.bfloat16 if dtype == BF16 else torch.float32, device="cuda")
+    mu = torch.empty(rows, device="cuda")
+    r = torch.empty(rows, device="cuda")
+    tx, tg, tb = dev(x, dtype), dev(g, dtype), dev(bt, dtype)
+    B.slt_layernorm_fwd(tx, tg, tb, y, mu, r, rows, C, 1e-5, dtype)
+    yr, mur, rr = O.layernorm_fwd(x, g, bt, 1e-5)
+    check(host(y), ref_round(yr, dtype), act(dtype), "ln y")
+    check(host(r), rr, "f32", "ln rstd")
+    dy = rnd(rng, (rows, C), dtype)
+    ddx = torch.empty_like(y)
+    dgm = torch.empty(C, device="cuda")
+    dbt = torch.empty(C, device="cuda")
+    ws = torch.empty(B.slt_norm_bwd_workspace(rows, C), dtype=torch.uint8, device="cuda")
+    B.slt_layernorm_bwd(tx, tg, mu, r, dev(dy, dtype), None, ddx, dgm, dbt, rows, C, dtype, ws)
+    dxr, dgr, dbr = O.layernorm_bwd(x, g, mur, rr, dy)
+    check(host(ddx), ref_round(dxr, dtype), act(dtype), "ln dx")
+    check(host(dgm), dgr, "f32" if dtype == F32 else "bf16", "ln dgamma")
+    check(host(dbt), dbr, "f32" if dtype == F32 else "bf16", "ln dbeta")
+
+
+# ---------------------------------------------------------------------------
+# RoPE table and attention
+# ---------------------------------------------------------------------------
+def test_rope_table(B):
+    for T, R in [(16, 4), (2048, 32), (1024, 64)]:
+        cs = torch.empty((T, R), device="cuda")
+        B.slt_rope_table(T, R, 10000.0, cs)
+        c, s = O.rope_tables(T, R, 10000.0)
+        got = host(cs)
+        np.testing.assert_allclose(got[:, 0::2], c.astype(np.float32), rtol=0, atol=6e-8)
+        np.testing.assert_allclose(got[:, 1::2], s.astype(np.float32), rtol=0, atol=6e-8)
+
+
+ATTN_CASES = [
+    # Bn, T, H, Hkv, d, R, mode, dtype
+    (1, 16, 4, 4, 4, 4, "half", F32),
+    (2, 77, 4, 2, 16, 16, "half", F32),
+    (2, 256, 8, 8, 32, 32, "half", F32),
+    (2, 256, 8, 8, 48, 48, "half", BF16),
+    (1, 130, 16, 4, 64, 64, "half", BF16),
+    (1, 200, 4, 4, 64, 32, "pairs", BF16),
+    (2, 64, 2, 1, 48, 0, "half", BF16),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_attention_fwd_bwd(B, case):
+    Bn, T, H, Hkv, d, R, mode, dtype = case
+    say("attention", case)
+    rng = np.random.default_rng(8)
+    qd, kd = H * d, Hkv * d
+    ld = qd + 2 * kd + 3          # padded row stride exercises the strides
+    qkv = rnd(rng, (Bn * T, ld), dtype)
+    tq = dev(qkv, dtype)
+    es = 2 if dtype == BF16 else 4
+    mode_i = 0 if mode == "half" else 1
+    cs = torch.empty((T, max(R, 2)), device="cuda")
+    if R:
+        B.slt_rope_table(T, R, 10000.0, cs)
+    o = torch.full((Bn * T, qd), float("nan"), dtype=tq.dtype, device="cuda")
+    lse = torch.empty((Bn, H, T), device="cuda")
+    base = tq.data_ptr()
+    B.slt_attention_fwd(base, base + qd * es, base + (qd + kd) * es, o, lse, ld, ld, ld, qd,
+                        Bn, T, H, Hkv, d, R, mode_i, cs, dtype)
+
+    def heads(x, nh):
+        return x.reshape(Bn, T, nh, d).transpose(0, 2, 1, 3)
+
+    c, s = O.rope_tables(T, max(R, 2), 10000.0)
+    q = heads(qkv[:, :qd], H)
+    k = heads(qkv[:, qd:qd + kd], Hkv)
+    v = heads(qkv[:, qd + kd:qd + 2 * kd], Hkv)
+    if R:
+        q = O.rope_apply(q, c, s, R, mode)
+        k = O.rope_apply(k, c, s, R, mode)
+    o_ref, lse_ref = O.attention_fwd(q, k, v)
+    o_ref2 = o_ref.transpose(0, 2, 1, 3).reshape(Bn * T, qd)
+    check(host(o), ref_round(o_ref2, dtype), act(dtype), "attn o")
+    check(host(lse), lse_ref, act(dtype), "attn lse")
+
+    do = rnd(rng, (Bn * T, qd), dtype)
+    o_dev = dev(ref_round(o_ref2, dtype), dtype)   # the backward reads o; give it the exact one
+    dqkv = torch.full((Bn * T, ld), float("nan"), dtype=tq.dtype, device="cuda")
+    ws = torch.empty(B.slt_attention_bwd_workspace(Bn, H, T), dtype=torch.uint8, device="cuda")
+    db = dqkv.data_ptr()
+    B.slt_attention_bwd(base, base + qd * es, base + (qd + kd) * es, o_dev, dev(do, dtype), lse,
+                        db, db + qd * es, db + (qd + kd) * es, ld, ld, ld, qd, qd, ld, ld, ld,
+                        Bn, T, H, Hkv, d, R, mode_i, cs, dtype, ws)
+    dq, dk, dv = O.attention_bwd(q, k, v, heads(do, H))
+    if R:
+        dq = O.rope_apply(dq, c, s, R, mode, inverse=True)
+        dk = O.rope_apply(dk, c, s, R, mode, inverse=True)
+    got = host(dqkv)
+    un = lambda x: x.transpose(0, 2, 1, 3).reshape(Bn * T, -1)
+    check(got[:, :qd], ref_round(un(dq), dtype), act(dtype), "attn dq")
+    check(got[:, qd:qd + kd], ref_round(un(dk), dtype), act(dtype), "attn dk")
+    check(got[:, qd + kd:qd + 2 * kd], ref_round(un(dv), dtype), act(dtype), "attn dv")
+
+
+# ---------------------------------------------------------------------------
+# MLP activations
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("rows,F", [(16, 42), (300, 682), (4096, 1024)])
+def test_swiglu_and_gelu(B, dtype, rows, F):
+    say("swiglu/gelu", rows, F, dtype)
+    rng = np.random.default_rng(9)
+    ab = rnd(rng, (rows, 2 * F), dtype, 2.0)
+    tab = dev(ab, dtype)
+    es = 2 if dtype == BF16 else 4
+    h = torch.empty((rows, F), dtype=tab.dtype, device="cuda")
+    B.slt_swiglu_fwd(tab, tab.data_ptr() + F * es, h, rows, F, 2 * F, 2 * F, F, dtype)
+    a, b = ab[:, :F], ab[:, F:]
+    check(host(h), ref_round(O.swiglu_fwd(a, b), dtype), act(dtype), "swiglu h")
+    dh = rnd(rng, (rows, F), dtype)
+    dab = torch.empty_like(tab)
+    B.slt_swiglu_bwd(tab, tab.data_ptr() + F * es, dev(dh, dtype), dab, dab.data_ptr() + F * es, rows, F,
+                     2 * F, 2 * F, F, 2 * F, 2 * F, dtype)
+    da, db = O.swiglu_bwd(a, b, dh)
+    got = host(dab)
+    check(got[:, :F], ref_round(da, dtype), act(dtype), "swiglu da")
+    check(got[:, F:], ref_round(db, dtype), act(dtype), "swiglu db")
+    u = torch.empty((rows, F), dtype=tab.dtype, device="cuda")
+    B.slt_gelu_fwd(tab, u, rows, F, 2 * F, F, dtype)
+    check(host(u), ref_round(O.gelu_fwd(a), dtype), act(dtype), "gelu u")
+    da2 = torch.empty((rows, F), dtype=tab.dtype, device="cuda")
+    B.slt_gelu_bwd(tab, dev(dh, dtype), da2, rows, F, 2 * F, F, F, dtype)
+    check(host(da2), ref_round(O.gelu_bwd(a, dh), dtype), act(dtype), "gelu da")
+
+
+# ---------------------------------------------------------------------------
+# Cross-entropy
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("Bn,T,V", [(1, 16, 27), (4, 33, 500), (8, 256, 4096), (2, 32, 51200)])
+def test_softmax_xent(B, dtype, Bn, T, V):
+    say("xent", Bn, T, V, dtype)
+    rng = np.random.default_rng(10)
+    z = rnd(rng, (Bn * T, V), dtype, 3.0)
+    tok = rng.integers(0, V, size=(Bn, T + 1)).astype(np.int32)
+    tz = dev(z, dtype)
+    loss = torch.empty(1, device="cuda")
+    lse = torch.empty(Bn * T, device="cuda")
+    ws = torch.empty(4 * Bn * T, dtype=torch.uint8, device="cuda")
+    B.slt_softmax_xent(tz, V, torch.from_numpy(tok).cuda(), Bn, T, T + 1, V, loss, lse, dtype, ws)
+    lref, dz, lser = O.cross_entropy(z, tok[:, 1:].reshape(-1))
+    assert abs(host(loss)[0] - lref) <= 1e-6 * abs(lref)
+    check(host(lse), lser, "f32", "xent lse")
+    check(host(tz), ref_round(dz, dtype), act(dtype), "xent dz")
+
+
+# ---------------------------------------------------------------------------
+# AdamW, cast, init
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 7, 1000003])
+def test_adamw_flat(B, n):
+    say("adamw", n)
+    rng = np.random.default_rng(11)
+    th = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (np.abs(rng.standard_normal(n)) * 1e-7).astype(np.float32)
+    mask = (rng.random(n) < 0.7).astype(np.uint8)
+    t_th, t_m, t_v = (torch.from_numpy(a.copy()).cuda() for a in (th, m, v))
+    sh = torch.empty(n, dtype=torch.int16, device="cuda")
+    B.slt_adamw_step(n, t_th, sh, torch.from_numpy(g).cuda(), t_m, t_v, 5, 1e-3, 0.9, 0.999, 1e-8, 0.1,
+                     torch.from_numpy(mask).cuda())
+    rth, rm, rv = O.adamw(th, g, m, v, 5, 1e-3, 0.9, 0.999, 1e-8, 0.1, decay=mask)
+    check(host(t_m), rm, "f32", "adamw m", tol=1e-6)
+    check(host(t_v), rv, "f32", "adamw v", tol=1e-6)
+    got = host(t_th)
+    assert np.max(np.abs(got - rth) / (np.abs(rth) + rms(rth))) < 1e-5
+    shadow = host(sh.view(torch.bfloat16))
+    np.testing.assert_array_equal(shadow, O.bf16_round(got))
+
+
+def test_cast_bf16_matches_oracle_rounding(B):
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal(100003) * 10.0 ** rng.integers(-30, 30, 100003)).astype(np.float32)
+    d = torch.empty(x.size, dtype=torch.int16, device="cuda")
+    B.slt_cast_bf16(torch.from_numpy(x).cuda(), d, x.size)
+    np.testing.assert_array_equal(host(d.view(torch.bfloat16)), O.bf16_round(x.astype(np.float64)))
+
+
+def test_model_init_statistics(B):
+    import slt_workloads as W
+    w = W.get_config(2)
+    cfg = B.make_config(w)
+    layout, n = B.slt_param_layout(cfg)
+    master = torch.full((n,), float("nan"), device="cuda")
+    B.slt_model_init(cfg, 1234, 0.02, 1.0 / math.sqrt(2 * w.L), master)
+    h = host(master)
+    by = {t["name"]: h[t["offset"]:t["offset"] + t["numel"]] for t in layout}
+    assert np.all(by["h0.attn_norm"] == 1.0) and np.all(by["norm_f"] == 1.0)
+    for name, std in [("wte", 0.02), ("h3.qkvw", 0.02), ("h1.w2", 0.02 / math.sqrt(12)), ("lm_head", 0.02)]:
+        a = by[name]
+        assert abs(a.mean()) < 4 * std / math.sqrt(a.size), name
+        assert abs(a.std() / std - 1) < 4 / math.sqrt(2 * a.size) + 1e-3, name
+    again = torch.empty_like(master)
+    B.slt_model_init(cfg, 1234, 0.02, 1.0 / math.sqrt(2 * w.L), again)
+    torch.cuda.synchronize()
+    assert torch.equal(master, again)
