@@ -232,19 +232,22 @@ slt_status slt_rope_table(int32_t T, int32_t R, float base, float* cs, void* str
  * q[(b*T+t)*ldq + h*d ...], k and v of KV head h*Hkv/H likewise with ldk/ldv,
  * and writes o[(b*T+t)*ldo + h*d ...].  lse: fp32 [B, H, T], the natural log
  * of the softmax denominator of each query row (scores scaled by 1/sqrt(d)).
+ * o_res (may be NULL): dense [B*T, H*d] in dtype, receives o - round(o), the
+ * part of the output its storage type dropped; the backward uses it.
  * cs: the RoPE table of slt_rope_table for (T, R); R = 0 disables RoPE. */
 slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                             int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                             void* o_res, int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
                              int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R,
                              int32_t rope_mode, const float* cs, int32_t dtype, void* stream);
 
 /* Causal attention backward (recomputing probabilities from lse): writes dq
  * (of the un-rotated q), dk (un-rotated k; summed over the query heads of each
- * KV head) and dv with the same addressing as q, k, v.  workspace: at least
+ * KV head) and dv with the same addressing as q, k, v.  o_res: the residual
+ * written by the forward, or NULL.  workspace: at least
  * slt_attention_bwd_workspace(B, H, T) bytes. */
 int64_t slt_attention_bwd_workspace(int32_t B, int32_t H, int32_t T);
 slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const void* o,
-                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             const void* o_res, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                              int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t lddo,
                              int64_t lddq, int64_t lddk, int64_t lddv,
                              int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R,

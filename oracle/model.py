@@ -81,9 +81,23 @@ def _identity(x):
     return x
 
 
-def store_fn(act: str):
-    """The storage rounding for an activation type ("bf16" or "f32")."""
-    return bf16_round if act == "bf16" else _identity
+def store_fn(act: str, jitter: float = 0.0, seed: int = 0):
+    """The storage rounding for an activation type ("bf16" or "f32").
+
+    jitter > 0 multiplies every value by (1 + jitter * N(0, 1)) before it is
+    rounded: with jitter = 2^-24 this mimics another fp32 summation order in
+    front of each bf16 store, so the spread between a plain and a jittered run
+    measures how far two valid bf16 computations of the same step may differ."""
+    if act != "bf16":
+        return _identity
+    if jitter == 0.0:
+        return bf16_round
+    rng = np.random.default_rng(seed)
+
+    def jittered(x):
+        x = np.asarray(x, np.float64)
+        return bf16_round(x * (1.0 + jitter * rng.standard_normal(x.shape)))
+    return jittered
 
 
 # ----------------------------------------------------------------------------
@@ -363,7 +377,7 @@ def _unheads(x4d):
     return x4d.transpose(0, 2, 1, 3).reshape(B * T, nh * d)
 
 
-def forward(cfg, params, tokens):
+def forward(cfg, params, tokens, jitter=0.0, seed=0):
     """Forward pass and loss.
 
     cfg: a workload config (V, C, H, Hkv, L, T, F, R, rope_mode, block, act,
@@ -374,8 +388,9 @@ def forward(cfg, params, tokens):
                  x += W_2 (silu(a) * b) with a, b = RMSNorm(x) W_1^T, RMSNorm(x) W_3^T.
     Parallel block: n = LayerNorm(x); x += [attn(n) | gelu(n W_in^T)] W_out^T.
     Final norm, then z = n_f W_head^T and the mean cross-entropy.
+    jitter/seed: see store_fn (0 for the reference computation).
     Returns (loss, cache) where cache holds what the backward reads."""
-    S = store_fn(cfg.act)
+    S = store_fn(cfg.act, jitter, seed)
     W = {k: S(np.asarray(v, np.float64)) for k, v in params.items()}
     tokens = np.asarray(tokens)
     B, T = tokens.shape[0], tokens.shape[1] - 1
@@ -429,7 +444,7 @@ def forward(cfg, params, tokens):
     nf = S(nf)
     z = S(nf @ W["lm_head"].T)
     loss, dz, lse_z = cross_entropy(z, Y)
-    cache = dict(W=W, X=X, Y=Y, B=B, T=T, cos=cos, sin=sin, layers=layers,
+    cache = dict(store=S, W=W, X=X, Y=Y, B=B, T=T, cos=cos, sin=sin, layers=layers,
                  x_f=x_f, nf=nf, rf=rf, muf=muf, z=z, dz=dz, lse_z=lse_z)
     return loss, cache
 
@@ -438,7 +453,7 @@ def backward(cfg, cache):
     """Hand-written backward: a reverse walk over the cached forward.
     Matrix rules dX = dY W and dW = dY^T X; every weight gradient is written
     (not accumulated).  Returns dict name -> float64 gradient."""
-    S = store_fn(cfg.act)
+    S = cache["store"]
     W = cache["W"]
     B, T = cache["B"], cache["T"]
     C, H, Hkv, d, R = cfg.C, cfg.H, cfg.Hkv, cfg.C // cfg.H, cfg.R
@@ -496,10 +511,10 @@ def backward(cfg, cache):
 
 
 def train_step(cfg, params, tokens, t=1, m=None, v=None, decay=None,
-               lr=None, beta1=None, beta2=None, adam_eps=None, wd=None):
+               lr=None, beta1=None, beta2=None, adam_eps=None, wd=None, jitter=0.0, seed=0):
     """forward -> backward -> AdamW on every tensor.  m and v default to zero
     (first step).  Returns dict(loss, grads, params, m, v)."""
-    loss, cache = forward(cfg, params, tokens)
+    loss, cache = forward(cfg, params, tokens, jitter, seed)
     grads = backward(cfg, cache)
     lr = cfg.lr if lr is None else lr
     beta1 = cfg.beta1 if beta1 is None else beta1

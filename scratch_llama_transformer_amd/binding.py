@@ -65,10 +65,10 @@ SIGNATURES = {
     "slt_layernorm_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _F, _I32, _P]),
     "slt_layernorm_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P]),
     "slt_rope_table": (_I32, [_I32, _I32, _F, _P, _P]),
-    "slt_attention_fwd": (_I32, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
+    "slt_attention_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
                                  _I32, _I32, _I32, _P, _I32, _P]),
     "slt_attention_bwd_workspace": (_I64, [_I32, _I32, _I32]),
-    "slt_attention_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+    "slt_attention_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
                                  _I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32,
                                  _P, _P]),
     "slt_swiglu_fwd": (_I32, [_P, _P, _P, _I32, _I32, _I64, _I64, _I64, _I32, _P]),
@@ -239,16 +239,18 @@ def slt_rope_table(T, R, base, cs, stream=None):
     _check("slt_rope_table", load().slt_rope_table(T, R, base, _ptr(cs), _stream(stream)))
 
 
-def slt_attention_fwd(q, k, v, o, lse, ldq, ldk, ldv, ldo, B, T, H, Hkv, d, R, rope_mode, cs, dtype, stream=None):
-    _check("slt_attention_fwd", load().slt_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), ldq, ldk,
+def slt_attention_fwd(q, k, v, o, lse, o_res, ldq, ldk, ldv, ldo, B, T, H, Hkv, d, R, rope_mode, cs, dtype,
+                      stream=None):
+    _check("slt_attention_fwd", load().slt_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o_res),
+                                                         ldq, ldk,
                                                          ldv, ldo, B, T, H, Hkv, d, R, rope_mode, _ptr(cs), dtype,
                                                          _stream(stream)))
 
 
-def slt_attention_bwd(q, k, v, o, dout, lse, dq, dk, dv, ldq, ldk, ldv, ldo, lddo, lddq, lddk, lddv,
+def slt_attention_bwd(q, k, v, o, o_res, dout, lse, dq, dk, dv, ldq, ldk, ldv, ldo, lddo, lddq, lddk, lddv,
                       B, T, H, Hkv, d, R, rope_mode, cs, dtype, workspace, stream=None):
     _check("slt_attention_bwd", load().slt_attention_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), ldq, ldk, ldv,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_res), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), ldq, ldk, ldv,
         ldo, lddo, lddq, lddk, lddv, B, T, H, Hkv, d, R, rope_mode, _ptr(cs), dtype, _ptr(workspace),
         _stream(stream)))
 

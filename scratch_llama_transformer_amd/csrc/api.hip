@@ -49,7 +49,7 @@ struct LayerP {
 };
 
 struct LayerA {
-  int64_t n1, r1, mu1, qkv, o, lse, n2, r2, ab, h;  // byte offsets in the arena
+  int64_t n1, r1, mu1, qkv, o, ores, lse, n2, r2, ab, h;  // byte offsets in the arena (-1: absent)
 };
 
 struct Plan {
@@ -169,6 +169,7 @@ static slt_status make_plan(const slt_config* cfg, Plan& p) {
     A.r1 = take(N * 4);
     A.mu1 = p.llama ? -1 : take(N * 4);
     A.lse = take((int64_t)c.B * c.H * c.T * 4);
+    A.ores = p.bf ? take(N * p.qd * es) : -1;  // bf16 rounding residual of the attention output
     if (p.llama) {
       A.qkv = take(N * p.qkv_w * es);
       A.o = take(N * p.qd * es);
@@ -267,6 +268,7 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
     at.B = c.B; at.T = c.T; at.H = c.H; at.Hkv = c.Hkv; at.d = p.d; at.R = c.R; at.rope_mode = c.rope_mode;
     at.dtype = x.dt; at.cs = cs;
     at.lse = reinterpret_cast<float*>(x.A(A.lse));
+    at.ores_out = A.ores >= 0 ? x.A(A.ores) : nullptr;
     if (p.llama) {
       void* xin = x.A(p.xs[2 * l]);
       void* xmid = x.A(p.xs[2 * l + 1]);
@@ -341,6 +343,7 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     at.dtype = x.dt; at.cs = cs;
     at.lse_in = (const float*)x.A(A.lse);
     at.delta = (float*)x.S(p.delta);
+    at.ores_in = A.ores >= 0 ? x.A(A.ores) : nullptr;
     char* qkv = (char*)x.A(A.qkv);
     if (p.llama) {
       // x_out = x_mid + h W2^T
@@ -597,7 +600,7 @@ static slt_status attn_check(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32
   return SLT_OK;
 }
 
-slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t ldq,
+slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* o_res, int64_t ldq,
                              int64_t ldk, int64_t ldv, int64_t ldo, int32_t B, int32_t T, int32_t H, int32_t Hkv,
                              int32_t d, int32_t R, int32_t rope_mode, const float* cs, int32_t dtype,
                              void* stream) {
@@ -607,7 +610,7 @@ slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* 
   if (ldq < (int64_t)H * d || ldk < (int64_t)Hkv * d || ldv < (int64_t)Hkv * d || ldo < (int64_t)H * d)
     return fail(SLT_EINVAL, "attention_fwd: row stride smaller than the heads it holds");
   AttnArgs a{};
-  a.q = q; a.k = k; a.v = v; a.out = o; a.lse = lse;
+  a.q = q; a.k = k; a.v = v; a.out = o; a.lse = lse; a.ores_out = o_res;
   a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo;
   a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.d = d; a.R = R; a.rope_mode = rope_mode; a.dtype = dtype; a.cs = cs;
   return launch_attention_fwd(a, as_stream(stream));
@@ -615,7 +618,8 @@ slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* 
 
 int64_t slt_attention_bwd_workspace(int32_t B, int32_t H, int32_t T) { return attention_bwd_ws(B, H, T); }
 
-slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const void* o, const void* o_res,
+                             const void* dout,
                              const float* lse, void* dq, void* dk, void* dv, int64_t ldq, int64_t ldk, int64_t ldv,
                              int64_t ldo, int64_t lddo, int64_t lddq, int64_t lddk, int64_t lddv, int32_t B,
                              int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R, int32_t rope_mode,
@@ -628,7 +632,7 @@ slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const 
   if (ldq < hd || ldo < hd || lddo < hd || lddq < hd || ldk < kvd || ldv < kvd || lddk < kvd || lddv < kvd)
     return fail(SLT_EINVAL, "attention_bwd: row stride smaller than the heads it holds");
   AttnArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse_in = lse;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.ores_in = o_res; a.dout = dout; a.lse_in = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.lddo = lddo; a.lddq = lddq; a.lddk = lddk; a.lddv = lddv;
   a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.d = d; a.R = R; a.rope_mode = rope_mode; a.dtype = dtype; a.cs = cs;

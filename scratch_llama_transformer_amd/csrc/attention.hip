@@ -60,6 +60,15 @@ __device__ __forceinline__ Pk<T, 4> pack4(float a, float b, float c, float d) {
   return p;
 }
 
+// Second term of a two-term bf16 expansion v ~ hi + lo (zero for fp32).  The
+// probability-gradient dS sums to zero along each row, so one bf16 rounding
+// per element would leave an error proportional to the mean key or query;
+// feeding hi and lo to the MFMA keeps ~16 significant bits.
+template <typename T>
+__device__ __forceinline__ Pk<T, 4> low_part(const Pk<T, 4>& hi, const float (&v)[4]) {
+  return pack4<T>(v[0] - to_f32(hi.e[0]), v[1] - to_f32(hi.e[1]), v[2] - to_f32(hi.e[2]), v[3] - to_f32(hi.e[3]));
+}
+
 template <typename T>
 __device__ __forceinline__ Pk<T, 4> lds4(const T* p) {
   return *reinterpret_cast<const Pk<T, 4>*>(p);
@@ -117,20 +126,30 @@ __device__ __forceinline__ float rope_elem_f(const float* u, int j, int t, int R
 // to DP columns, optionally rotated, into a row-major copy X[r][j] (row stride
 // XS) and/or a transposed copy Xt[j][r] (row stride XTS).  Rows >= T and
 // columns >= d are zero.
+// Xlo / Xtlo (optional, strides XS / XTS) receive the bf16 rounding residual
+// of the rotated value, for products that need it beyond bf16.
 template <typename T, int DP, bool ROT>
 __device__ __forceinline__ void stage_tile(const T* base, int64_t ld, int col0, int row0, int T_, int d, int R,
-                                           int mode, const float* cs, T* X, int XS, T* Xt, int XTS) {
+                                           int mode, const float* cs, T* X, int XS, T* Xt, int XTS,
+                                           T* Xlo = nullptr, T* Xtlo = nullptr) {
   for (int idx = threadIdx.x; idx < TQ * DP; idx += blockDim.x) {
     const int r = idx / DP, j = idx % DP;
     const int t = row0 + r;
-    T val = zero_v<T>();
+    T val = zero_v<T>(), lo = zero_v<T>();
     if (t < T_ && j < d) {
       const T* row = base + (int64_t)t * ld + col0;
-      if (ROT && R > 0) val = from_f32<T>(rope_elem<T>(row, j, t, R, mode, cs, 1.0f));
-      else val = row[j];
+      if (ROT && R > 0) {
+        const float f = rope_elem<T>(row, j, t, R, mode, cs, 1.0f);
+        val = from_f32<T>(f);
+        lo = from_f32<T>(f - to_f32(val));
+      } else {
+        val = row[j];
+      }
     }
     if (X) X[r * XS + j] = val;
     if (Xt) Xt[j * XTS + r] = val;
+    if (Xlo) Xlo[r * XS + j] = lo;
+    if (Xtlo) Xtlo[j * XTS + r] = lo;
   }
 }
 
@@ -145,6 +164,7 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
   constexpr int KS = DP + kPad;      // Ks row stride
   constexpr int VS = TQ + kPad;      // Vt row stride
   __shared__ __attribute__((aligned(16))) T Ks[TQ * KS];
+  __shared__ __attribute__((aligned(16))) T Ksl[sizeof(T) == 2 ? TQ * KS : 4];  // rotated k, low part
   __shared__ __attribute__((aligned(16))) T Vt[DP * VS];
 
   const int b = blockIdx.z, h = blockIdx.y, q0 = blockIdx.x * TQ;
@@ -159,8 +179,8 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
   const T* kb = static_cast<const T*>(a.k) + (int64_t)b * T_ * a.ldk + kvh * d;
   const T* vb = static_cast<const T*>(a.v) + (int64_t)b * T_ * a.ldv + kvh * d;
 
-  // Q fragments (rotated): lane holds Q[qi][16c + g4 + i]
-  Pk<T, 4> qf[NC];
+  // Q fragments (rotated): lane holds Q[qi][16c + g4 + i] as hi + lo
+  Pk<T, 4> qf[NC], qfl[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float f[4];
@@ -174,6 +194,7 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
       }
     }
     qf[c] = pack4<T>(f[0], f[1], f[2], f[3]);
+    qfl[c] = low_part<T>(qf[c], f);
   }
 
   float m = -INFINITY, l = 0.f;
@@ -186,7 +207,8 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * TQ;
     __syncthreads();
-    stage_tile<T, DP, true>(kb, a.ldk, 0, k0, T_, d, a.R, a.rope_mode, a.cs, Ks, KS, nullptr, 0);
+    stage_tile<T, DP, true>(kb, a.ldk, 0, k0, T_, d, a.R, a.rope_mode, a.cs, Ks, KS, nullptr, 0,
+                            sizeof(T) == 2 ? Ksl : nullptr);
     stage_tile<T, DP, false>(vb, a.ldv, 0, k0, T_, d, 0, 0, nullptr, nullptr, 0, Vt, VS);
     __syncthreads();
 
@@ -196,7 +218,14 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc = mma16(lds4(&Ks[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]), qf[c], acc);
+      for (int c = 0; c < NC; ++c) {
+        const Pk<T, 4> k4 = lds4(&Ks[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]);
+        acc = mma16(k4, qf[c], acc);
+        if constexpr (sizeof(T) == 2) {
+          acc = mma16(k4, qfl[c], acc);
+          acc = mma16(lds4(&Ksl[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]), qf[c], acc);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = k0 + ks * 16 + g4 + r;
@@ -237,35 +266,27 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
   if (qi < T_) {
     const float inv = 1.0f / l;
     T* ob = static_cast<T*>(a.out) + ((int64_t)b * T_ + qi) * a.ldo + h * d;
+    T* rb = a.ores_out ? static_cast<T*>(a.ores_out) + ((int64_t)b * T_ + qi) * ((int64_t)a.H * d) + h * d
+                       : nullptr;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * c + g4 + r;
-        if (j < d) ob[j] = from_f32<T>(oacc[c][r] * inv);
+        if (j < d) {
+          const float val = oacc[c][r] * inv;
+          const T hi = from_f32<T>(val);
+          ob[j] = hi;
+          if (rb) rb[j] = from_f32<T>(val - to_f32(hi));
+        }
       }
     if (lane < 16) a.lse[((int64_t)b * a.H + h) * T_ + qi] = (m + log2f(l)) * kLn2;
   }
 }
 
-// D[b, h, t] = sum_j dout[t, h*d + j] * o[t, h*d + j]  (one thread per row)
-template <typename T>
-__global__ __launch_bounds__(256) void attn_delta_k(AttnArgs a) {
-  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.H * a.T;
-  if (idx >= total) return;
-  const int t = (int)(idx % a.T);
-  const int h = (int)((idx / a.T) % a.H);
-  const int b = (int)(idx / ((int64_t)a.T * a.H));
-  const T* o = static_cast<const T*>(a.o) + ((int64_t)b * a.T + t) * a.ldo + h * a.d;
-  const T* g = static_cast<const T*>(a.dout) + ((int64_t)b * a.T + t) * a.lddo + h * a.d;
-  float s = 0.f;
-  for (int j = 0; j < a.d; ++j) s += to_f32(o[j]) * to_f32(g[j]);
-  a.delta[idx] = s;
-}
-
 // ---------------------------------------------------------------------------
 // dQ.  grid (ceil(T/64), H, B); wave w owns queries q0 + 16w + l%16.
+//   D = dO . O (written for the dK/dV kernel, which runs after this one),
 //   S^T = K Q^T, P = exp(S/sqrt(d) - lse), dP^T = V dO^T,
 //   dS = P (dP - D), dQ^T += K^T dS^T, then dq = rotate^T(dQ) / sqrt(d).
 // ---------------------------------------------------------------------------
@@ -275,8 +296,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
   constexpr int KS = DP + kPad;
   constexpr int TS = TQ + kPad;
   __shared__ __attribute__((aligned(16))) T Ks[TQ * KS];
+  __shared__ __attribute__((aligned(16))) T Ksl[sizeof(T) == 2 ? TQ * KS : 4];  // rotated k, low part
   __shared__ __attribute__((aligned(16))) T Vs[TQ * KS];
   __shared__ __attribute__((aligned(16))) T Kt[DP * TS];
+  __shared__ __attribute__((aligned(16))) T Ktl[sizeof(T) == 2 ? DP * TS : 4];  // rotated k, low part
   __shared__ float dqs[TQ * (DP + 1)];
 
   const int b = blockIdx.z, h = blockIdx.y, q0 = blockIdx.x * TQ;
@@ -293,7 +316,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
   const T* vb = static_cast<const T*>(a.v) + (int64_t)b * T_ * a.ldv + kvh * d;
   const T* gb = static_cast<const T*>(a.dout) + (int64_t)b * T_ * a.lddo + h * d;
 
-  Pk<T, 4> qf[NC], gf[NC];
+  // Q (rotated, hi + lo) and dO fragments; D = dO . O for this lane's query,
+  // with O taken with its bf16 rounding residual (D multiplies the weighted
+  // mean key, so its error is not averaged away over the keys).
+  Pk<T, 4> qf[NC], qfl[NC], gf[NC];
+  const T* ob = static_cast<const T*>(a.o) + (int64_t)b * T_ * a.ldo + h * d;
+  const T* rbase = a.ores_in ? static_cast<const T*>(a.ores_in) + (int64_t)b * T_ * ((int64_t)a.H * d) + h * d
+                             : nullptr;
+  float dpart = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float f[4], g[4];
@@ -305,14 +335,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
         const T* row = qb + (int64_t)qi * a.ldq;
         f[i] = a.R > 0 ? rope_elem<T>(row, j, qi, a.R, a.rope_mode, a.cs, 1.0f) : to_f32(row[j]);
         g[i] = to_f32(gb[(int64_t)qi * a.lddo + j]);
+        float ov = to_f32(ob[(int64_t)qi * a.ldo + j]);
+        if (rbase) ov += to_f32(rbase[(int64_t)qi * ((int64_t)a.H * d) + j]);
+        dpart += ov * g[i];
       }
     }
     qf[c] = pack4<T>(f[0], f[1], f[2], f[3]);
+    qfl[c] = low_part<T>(qf[c], f);
     gf[c] = pack4<T>(g[0], g[1], g[2], g[3]);
   }
+  dpart += __shfl_xor(dpart, 16, 64);
+  dpart += __shfl_xor(dpart, 32, 64);
+  const float Dq = dpart;
   const int64_t srow = ((int64_t)b * a.H + h) * T_;
+  if (qi < T_ && lane < 16) a.delta[srow + qi] = Dq;   // read by the dK/dV kernel
   const float lse2 = qi < T_ ? a.lse_in[srow + qi] * kLog2e : 0.f;
-  const float Dq = qi < T_ ? a.delta[srow + qi] : 0.f;
 
   f32x4 dqacc[NC];
 #pragma unroll
@@ -323,7 +360,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * TQ;
     __syncthreads();
-    stage_tile<T, DP, true>(kb, a.ldk, 0, k0, T_, d, a.R, a.rope_mode, a.cs, Ks, KS, Kt, TS);
+    stage_tile<T, DP, true>(kb, a.ldk, 0, k0, T_, d, a.R, a.rope_mode, a.cs, Ks, KS, Kt, TS,
+                            sizeof(T) == 2 ? Ksl : nullptr, sizeof(T) == 2 ? Ktl : nullptr);
     stage_tile<T, DP, false>(vb, a.ldv, 0, k0, T_, d, 0, 0, nullptr, Vs, KS, nullptr, 0);
     __syncthreads();
 #pragma unroll
@@ -332,7 +370,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
       f32x4 pacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        sacc = mma16(lds4(&Ks[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]), qf[c], sacc);
+        const Pk<T, 4> k4 = lds4(&Ks[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]);
+        sacc = mma16(k4, qf[c], sacc);
+        if constexpr (sizeof(T) == 2) {
+          sacc = mma16(k4, qfl[c], sacc);
+          sacc = mma16(lds4(&Ksl[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]), qf[c], sacc);
+        }
         pacc = mma16(lds4(&Vs[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]), gf[c], pacc);
       }
       float ds[4];
@@ -344,9 +387,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
         ds[r] = p * (pacc[r] - Dq);
       }
       const Pk<T, 4> dsf = pack4<T>(ds[0], ds[1], ds[2], ds[3]);
+      const Pk<T, 4> dsl = low_part<T>(dsf, ds);
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        dqacc[c] = mma16(lds4(&Kt[(16 * c + (lane & 15)) * TS + ks * 16 + g4]), dsf, dqacc[c]);
+      for (int c = 0; c < NC; ++c) {
+        const Pk<T, 4> kt4 = lds4(&Kt[(16 * c + (lane & 15)) * TS + ks * 16 + g4]);
+        dqacc[c] = mma16(kt4, dsf, dqacc[c]);
+        if constexpr (sizeof(T) == 2) {
+          dqacc[c] = mma16(kt4, dsl, dqacc[c]);
+          dqacc[c] = mma16(lds4(&Ktl[(16 * c + (lane & 15)) * TS + ks * 16 + g4]), dsf, dqacc[c]);
+        }
+      }
     }
   }
   // dq~ (rotated frame) -> LDS, then rotate back and store.
@@ -379,8 +429,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
   constexpr int XS = DP + kPad;
   constexpr int TS = TQ + kPad;
   __shared__ __attribute__((aligned(16))) T Qs[TQ * XS];
+  __shared__ __attribute__((aligned(16))) T Qsl[sizeof(T) == 2 ? TQ * XS : 4];  // rotated q, low part
   __shared__ __attribute__((aligned(16))) T Gs[TQ * XS];
   __shared__ __attribute__((aligned(16))) T Qt[DP * TS];
+  __shared__ __attribute__((aligned(16))) T Qtl[sizeof(T) == 2 ? DP * TS : 4];  // rotated q^T, low part
   __shared__ __attribute__((aligned(16))) T Gt[DP * TS];
   __shared__ float lse2s[TQ], Ds[TQ];
 
@@ -396,7 +448,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
   const T* kb = static_cast<const T*>(a.k) + (int64_t)b * T_ * a.ldk + kvh * d;
   const T* vb = static_cast<const T*>(a.v) + (int64_t)b * T_ * a.ldv + kvh * d;
 
-  Pk<T, 4> kf[NC], vf[NC];
+  Pk<T, 4> kf[NC], kfl[NC], vf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float f[4], g[4];
@@ -411,6 +463,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
       }
     }
     kf[c] = pack4<T>(f[0], f[1], f[2], f[3]);
+    kfl[c] = low_part<T>(kf[c], f);
     vf[c] = pack4<T>(g[0], g[1], g[2], g[3]);
   }
 
@@ -427,7 +480,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
     for (int qt = blockIdx.x; qt < nqt; ++qt) {
       const int q0 = qt * TQ;
       __syncthreads();
-      stage_tile<T, DP, true>(qb, a.ldq, 0, q0, T_, d, a.R, a.rope_mode, a.cs, Qs, XS, Qt, TS);
+      stage_tile<T, DP, true>(qb, a.ldq, 0, q0, T_, d, a.R, a.rope_mode, a.cs, Qs, XS, Qt, TS,
+                              sizeof(T) == 2 ? Qsl : nullptr, sizeof(T) == 2 ? Qtl : nullptr);
       stage_tile<T, DP, false>(gb, a.lddo, 0, q0, T_, d, 0, 0, nullptr, Gs, XS, Gt, TS);
       if (threadIdx.x < TQ) {
         const int t = q0 + threadIdx.x;
@@ -441,7 +495,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
         f32x4 pacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          sacc = mma16(lds4(&Qs[(qs * 16 + (lane & 15)) * XS + 16 * c + g4]), kf[c], sacc);
+          const Pk<T, 4> q4 = lds4(&Qs[(qs * 16 + (lane & 15)) * XS + 16 * c + g4]);
+          sacc = mma16(q4, kf[c], sacc);
+          if constexpr (sizeof(T) == 2) {
+            sacc = mma16(lds4(&Qsl[(qs * 16 + (lane & 15)) * XS + 16 * c + g4]), kf[c], sacc);
+            sacc = mma16(q4, kfl[c], sacc);
+          }
           pacc = mma16(lds4(&Gs[(qs * 16 + (lane & 15)) * XS + 16 * c + g4]), vf[c], pacc);
         }
         float p[4], ds[4];
@@ -455,10 +514,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
         }
         const Pk<T, 4> pf = pack4<T>(p[0], p[1], p[2], p[3]);
         const Pk<T, 4> dsf = pack4<T>(ds[0], ds[1], ds[2], ds[3]);
+        const Pk<T, 4> dsl = low_part<T>(dsf, ds);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           dv[c] = mma16(lds4(&Gt[(16 * c + (lane & 15)) * TS + qs * 16 + g4]), pf, dv[c]);
-          dk[c] = mma16(lds4(&Qt[(16 * c + (lane & 15)) * TS + qs * 16 + g4]), dsf, dk[c]);
+          const Pk<T, 4> qt4 = lds4(&Qt[(16 * c + (lane & 15)) * TS + qs * 16 + g4]);
+          dk[c] = mma16(qt4, dsf, dk[c]);
+          if constexpr (sizeof(T) == 2) {
+            dk[c] = mma16(qt4, dsl, dk[c]);
+            dk[c] = mma16(lds4(&Qtl[(16 * c + (lane & 15)) * TS + qs * 16 + g4]), dsf, dk[c]);
+          }
         }
       }
     }
@@ -514,8 +579,6 @@ static slt_status attn_fwd_t(const AttnArgs& a, hipStream_t s) {
 
 template <typename T>
 static slt_status attn_bwd_t(const AttnArgs& a, hipStream_t s) {
-  const int64_t rows = (int64_t)a.B * a.H * a.T;
-  attn_delta_k<T><<<(int)((rows + 255) / 256), 256, 0, s>>>(a);
   dim3 gq((a.T + TQ - 1) / TQ, a.H, a.B);
   dim3 gk((a.T + TQ - 1) / TQ, a.Hkv, a.B);
   const int nc = (a.d + 15) / 16;

@@ -258,23 +258,52 @@ __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict_
   }
 }
 
-// One wave per vocabulary row: zero rows, and rows spanning several tiles.
+// One 256-thread block per vocabulary row: zero rows, and rows spanning
+// several tiles.  For the latter the 4 waves take contiguous quarters of the
+// tiles (tail of the first tile, then heads in tile order), each summing with
+// 4 interleaved accumulators; the quarters are added in order.
 __global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte, int V, int C, EmbWs w) {
+  __shared__ float part[4][256];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int v = blockIdx.x * 4 + wave;
-  if (v >= V) return;
+  const int v = blockIdx.x;
   const int rs = w.start[v], re = w.start[v + 1];
   float* row = dwte + (int64_t)v * C;
   if (re == rs) {
-    for (int c = lane; c < C; c += kWave) row[c] = 0.f;
+    for (int c = threadIdx.x; c < C; c += blockDim.x) row[c] = 0.f;
     return;
   }
   const int t0 = rs / kEmbTile, t1 = (re - 1) / kEmbTile;
   if (t0 == t1) return;
-  for (int c = lane; c < C; c += kWave) {
-    float acc = w.tail[(int64_t)t0 * C + c];
-    for (int t = t0 + 1; t <= t1; ++t) acc += w.head[(int64_t)t * C + c];
-    row[c] = acc;
+  // pieces: index 0 = tail[t0], index k >= 1 = head[t0 + k]
+  const int np = t1 - t0 + 1;
+  const int per = (np + 3) / 4;
+  const int pb = wave * per, pe = min(np, pb + per);
+  for (int c0 = 0; c0 < C; c0 += kWave * 4) {
+    float acc[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[u][q] = 0.f;
+    for (int k = pb; k < pe; k += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kk = k + u;
+        if (kk < pe) {
+          const float* src = kk == 0 ? w.tail + (int64_t)t0 * C : w.head + (int64_t)(t0 + kk) * C;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = c0 + q * kWave + lane;
+            if (c < C) acc[u][q] += src[c];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) part[wave][q * kWave + lane] = (acc[0][q] + acc[1][q]) + (acc[2][q] + acc[3][q]);
+    __syncthreads();
+    for (int c = threadIdx.x; c < kWave * 4; c += blockDim.x)
+      if (c0 + c < C) row[c0 + c] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+    __syncthreads();
   }
 }
 
@@ -455,15 +484,29 @@ __global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const
   }
 }
 
-__global__ void norm_colsum_k(const float* __restrict__ part, int nb, int C, float* __restrict__ out) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= C) return;
+// out[c] = sum_b part[b][c].  A 1024-thread block owns 32 columns: thread
+// (g, c) adds partials g, g+32, ... in order, then the 32 group sums are added
+// in a fixed tree.
+__global__ __launch_bounds__(1024) void norm_colsum_k(const float* __restrict__ part, int nb, int C,
+                                                       float* __restrict__ out) {
+  __shared__ float red[32][33];
+  const int tc = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int c = blockIdx.x * 32 + tc;
   float s = 0.f;
-  for (int b = 0; b < nb; ++b) s += part[(int64_t)b * C + c];
-  out[c] = s;
+  if (c < C) {
+#pragma unroll 8
+    for (int b = g; b < nb; b += 32) s += part[(int64_t)b * C + c];
+  }
+  red[g][tc] = s;
+  __syncthreads();
+  for (int off = 16; off > 0; off >>= 1) {
+    if (g < off) red[g][tc] += red[g + off][tc];
+    __syncthreads();
+  }
+  if (g == 0 && c < C) out[c] = red[0][tc];
 }
 
-constexpr int kNormBwdBlocks = 1024;
+constexpr int kNormBwdBlocks = 512;
 
 // ---------------------------------------------------------------------------
 // SwiGLU and GELU on [rows, F] with row strides.
@@ -820,7 +863,7 @@ slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, c
       emb_tile_sum_k<T, 1><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w);
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
-  emb_row_finish_k<<<cdiv(V, 4), 256, 0, s>>>(dwte, V, C, w);
+  emb_row_finish_k<<<V, 256, 0, s>>>(dwte, V, C, w);
   return check_launch("embedding_bwd");
 }
 
@@ -895,8 +938,8 @@ static slt_status norm_bwd_common(const void* x, const void* g, const float* mea
   };
   slt_status st = dtype == SLT_BF16 ? go(bf16{}) : go(float{});
   if (st != SLT_OK) return st;
-  norm_colsum_k<<<cdiv(C, 256), 256, 0, s>>>(part, nb, C, dg);
-  if (LN) norm_colsum_k<<<cdiv(C, 256), 256, 0, s>>>(part + (int64_t)nb * C, nb, C, db);
+  norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part, nb, C, dg);
+  if (LN) norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part + (int64_t)nb * C, nb, C, db);
   return check_launch("norm_colsum");
 }
 

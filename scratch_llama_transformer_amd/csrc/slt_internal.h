@@ -99,7 +99,9 @@ struct AttnArgs {
   int64_t ldq, ldk, ldv, ldo, lddo, lddq, lddk, lddv;
   int B, T, H, Hkv, d, R, rope_mode, dtype;
   const float* cs;
-  float* delta;  // workspace [B, H, T] for the backward
+  float* delta;        // workspace [B, H, T] for the backward
+  void* ores_out;      // forward: optional o - bf16(o), dense [B*T, H*d]
+  const void* ores_in; // backward: that residual (NULL: treat as 0)
 };
 slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s);
 slt_status launch_attention_bwd(const AttnArgs& a, hipStream_t s);

@@ -247,8 +247,9 @@ def test_attention_fwd_bwd(B, case):
         B.slt_rope_table(T, R, 10000.0, cs)
     o = torch.full((Bn * T, qd), float("nan"), dtype=tq.dtype, device="cuda")
     lse = torch.empty((Bn, H, T), device="cuda")
+    ores = torch.full((Bn * T, qd), float("nan"), dtype=tq.dtype, device="cuda") if dtype == BF16 else None
     base = tq.data_ptr()
-    B.slt_attention_fwd(base, base + qd * es, base + (qd + kd) * es, o, lse, ld, ld, ld, qd,
+    B.slt_attention_fwd(base, base + qd * es, base + (qd + kd) * es, o, lse, ores, ld, ld, ld, qd,
                         Bn, T, H, Hkv, d, R, mode_i, cs, dtype)
 
     def heads(x, nh):
@@ -265,13 +266,21 @@ def test_attention_fwd_bwd(B, case):
     o_ref2 = o_ref.transpose(0, 2, 1, 3).reshape(Bn * T, qd)
     check(host(o), ref_round(o_ref2, dtype), act(dtype), "attn o")
     check(host(lse), lse_ref, act(dtype), "attn lse")
+    if ores is not None:
+        # the residual is what rounding o to bf16 dropped: at most half a bf16 ulp of o
+        oh, rh = host(o), host(ores)
+        assert np.all(np.abs(rh) <= 2.0 ** -8 * np.abs(oh) + 1e-30)
+        check(oh + rh, o_ref2, "bf16", "attn o + residual")
 
     do = rnd(rng, (Bn * T, qd), dtype)
-    o_dev = dev(ref_round(o_ref2, dtype), dtype)   # the backward reads o; give it the exact one
+    # the backward reads o (and its rounding residual): give it the oracle's
+    o_hi = ref_round(o_ref2, dtype)
+    o_dev = dev(o_hi, dtype)
+    ores_dev = dev(O.bf16_round(o_ref2 - o_hi), dtype) if dtype == BF16 else None
     dqkv = torch.full((Bn * T, ld), float("nan"), dtype=tq.dtype, device="cuda")
     ws = torch.empty(B.slt_attention_bwd_workspace(Bn, H, T), dtype=torch.uint8, device="cuda")
     db = dqkv.data_ptr()
-    B.slt_attention_bwd(base, base + qd * es, base + (qd + kd) * es, o_dev, dev(do, dtype), lse,
+    B.slt_attention_bwd(base, base + qd * es, base + (qd + kd) * es, o_dev, ores_dev, dev(do, dtype), lse,
                         db, db + qd * es, db + (qd + kd) * es, ld, ld, ld, qd, qd, ld, ld, ld,
                         Bn, T, H, Hkv, d, R, mode_i, cs, dtype, ws)
     dq, dk, dv = O.attention_bwd(q, k, v, heads(do, H))
