@@ -18,6 +18,19 @@
 //
 // Tiling: 64 queries (or keys) per workgroup, 16 per wave; key (or query)
 // tiles of 64 staged in LDS; head dimension padded to a multiple of 16.
+//
+// Staging: RoPE is applied while a tile is copied from HBM to LDS.  On the
+// vector path a thread takes 4 rows x 16 bytes of dims, loads the partner
+// dims of each pair and the (cos, sin) table entries as vectors, rotates in
+// fp32, and writes the rows (16-byte stores) and, for operands needed
+// transposed, the 4-row columns (8-byte stores).  Shapes whose pairs do not
+// fall on 16-byte groups take the element-wise path.
+//
+// Precision (bf16): the rotated q and k, and the probability gradient dS,
+// enter their products as bf16 hi + lo pairs: dS sums to zero along a row and
+// the score differences set the softmax, so a single rounding of either would
+// leave errors proportional to the mean key / query rather than to the
+// result.  D = dO.O uses O with its bf16 rounding residual (see the forward).
 #include "slt_internal.h"
 
 #include <math.h>
@@ -28,7 +41,7 @@ namespace {
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TQ = 64;        // rows per workgroup
+constexpr int TQ = 64;  // rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -40,6 +53,9 @@ struct alignas(sizeof(T) * N) Pk {
 template <typename T> __device__ __forceinline__ T zero_v();
 template <> __device__ __forceinline__ bf16 zero_v<bf16>() { return bf16{0}; }
 template <> __device__ __forceinline__ float zero_v<float>() { return 0.f; }
+
+template <typename T> constexpr bool kBf = sizeof(T) == 2;
+template <typename T> constexpr int kG = 16 / (int)sizeof(T);  // elements per 16 bytes
 
 __device__ __forceinline__ f32x4 mma16(const Pk<bf16, 4>& a, const Pk<bf16, 4>& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a), __builtin_bit_cast(bf16x4_t, b),
@@ -54,19 +70,20 @@ __device__ __forceinline__ f32x4 mma16(const Pk<float, 4>& a, const Pk<float, 4>
 }
 
 template <typename T>
-__device__ __forceinline__ Pk<T, 4> pack4(float a, float b, float c, float d) {
+__device__ __forceinline__ Pk<T, 4> pack4(const float (&v)[4]) {
   Pk<T, 4> p;
-  p.e[0] = from_f32<T>(a); p.e[1] = from_f32<T>(b); p.e[2] = from_f32<T>(c); p.e[3] = from_f32<T>(d);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p.e[i] = from_f32<T>(v[i]);
   return p;
 }
 
-// Second term of a two-term bf16 expansion v ~ hi + lo (zero for fp32).  The
-// probability-gradient dS sums to zero along each row, so one bf16 rounding
-// per element would leave an error proportional to the mean key or query;
-// feeding hi and lo to the MFMA keeps ~16 significant bits.
+// Second term of a two-term bf16 expansion v ~ hi + lo.
 template <typename T>
 __device__ __forceinline__ Pk<T, 4> low_part(const Pk<T, 4>& hi, const float (&v)[4]) {
-  return pack4<T>(v[0] - to_f32(hi.e[0]), v[1] - to_f32(hi.e[1]), v[2] - to_f32(hi.e[2]), v[3] - to_f32(hi.e[3]));
+  Pk<T, 4> p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p.e[i] = from_f32<T>(v[i] - to_f32(hi.e[i]));
+  return p;
 }
 
 template <typename T>
@@ -74,11 +91,11 @@ __device__ __forceinline__ Pk<T, 4> lds4(const T* p) {
   return *reinterpret_cast<const Pk<T, 4>*>(p);
 }
 
-// Value of dim j of a row u at position t after RoPE (sign = +1) or after the
-// transposed rotation (sign = -1, the backward of RoPE).  Dims >= R pass
-// through.  cs: [T][R] with (cos, sin) of angle t * theta_i at 2i, 2i+1.
-template <typename T>
-__device__ __forceinline__ float rope_elem(const T* u, int j, int t, int R, int mode, const float* cs, float sign) {
+// Dim j of row u at position t after RoPE (sign +1) or after the transposed
+// rotation (sign -1, the backward of RoPE); dims >= R pass through.
+// cs: [T][R] with (cos, sin) of angle t * theta_i at 2i, 2i+1.
+template <typename U>
+__device__ __forceinline__ float rope_elem(const U* u, int j, int t, int R, int mode, const float* cs, float sign) {
   const float x = to_f32(u[j]);
   if (j >= R) return x;
   int i, p;
@@ -99,79 +116,222 @@ __device__ __forceinline__ float rope_elem(const T* u, int j, int t, int R, int 
   return first ? x * c - y * s : x * c + y * s;
 }
 
-// Same for an fp32 row held in LDS.
-__device__ __forceinline__ float rope_elem_f(const float* u, int j, int t, int R, int mode, const float* cs,
-                                             float sign) {
-  const float x = u[j];
-  if (j >= R) return x;
-  int i, p;
-  bool first;
+// G consecutive dims j0..j0+G-1 of row u at position t, rotated (sign +1) or
+// rotated back (sign -1).  Requires j0 % G == 0 and pairs aligned to G
+// (half mode: (R/2) % G == 0; pairs mode: R % G == 0 with G even), which the
+// host checks before choosing the vector path.
+template <int G, typename U>
+__device__ __forceinline__ void rope_group(const U* u, int j0, int t, int R, int mode, const float* cs, float sign,
+                                           float (&out)[G]) {
+  Pk<U, G> own = *reinterpret_cast<const Pk<U, G>*>(u + j0);
+#pragma unroll
+  for (int e = 0; e < G; ++e) out[e] = to_f32(own.e[e]);
+  if (R == 0 || j0 >= R) return;
+  const float2* tb = reinterpret_cast<const float2*>(cs + (int64_t)t * R);
   if (mode == SLT_ROPE_HALF) {
     const int h = R >> 1;
-    first = j < h;
-    i = first ? j : j - h;
-    p = first ? j + h : j - h;
+    const bool first = j0 < h;
+    const int i0 = first ? j0 : j0 - h;
+    Pk<U, G> par = *reinterpret_cast<const Pk<U, G>*>(u + (first ? j0 + h : j0 - h));
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const float2 c = tb[i0 + e];
+      const float x = out[e], y = to_f32(par.e[e]);
+      out[e] = first ? x * c.x - y * (sign * c.y) : x * c.x + y * (sign * c.y);
+    }
   } else {
-    first = (j & 1) == 0;
-    i = j >> 1;
-    p = j ^ 1;
+#pragma unroll
+    for (int e = 0; e < G; e += 2) {
+      const float2 c = tb[(j0 + e) >> 1];
+      const float x = out[e], y = out[e + 1];
+      out[e] = x * c.x - y * (sign * c.y);
+      out[e + 1] = y * c.x + x * (sign * c.y);
+    }
   }
-  const float c = cs[(int64_t)t * R + 2 * i];
-  const float s = sign * cs[(int64_t)t * R + 2 * i + 1];
-  const float y = u[p];
-  return first ? x * c - y * s : x * c + y * s;
 }
 
-// Stage a 64-row tile of a [rows of the sequence] x d operand into LDS, padded
-// to DP columns, optionally rotated, into a row-major copy X[r][j] (row stride
-// XS) and/or a transposed copy Xt[j][r] (row stride XTS).  Rows >= T and
-// columns >= d are zero.
-// Xlo / Xtlo (optional, strides XS / XTS) receive the bf16 rounding residual
-// of the rotated value, for products that need it beyond bf16.
-template <typename T, int DP, bool ROT>
-__device__ __forceinline__ void stage_tile(const T* base, int64_t ld, int col0, int row0, int T_, int d, int R,
-                                           int mode, const float* cs, T* X, int XS, T* Xt, int XTS,
-                                           T* Xlo = nullptr, T* Xtlo = nullptr) {
-  for (int idx = threadIdx.x; idx < TQ * DP; idx += blockDim.x) {
-    const int r = idx / DP, j = idx % DP;
-    const int t = row0 + r;
-    T val = zero_v<T>(), lo = zero_v<T>();
-    if (t < T_ && j < d) {
-      const T* row = base + (int64_t)t * ld + col0;
-      if (ROT && R > 0) {
-        const float f = rope_elem<T>(row, j, t, R, mode, cs, 1.0f);
-        val = from_f32<T>(f);
-        lo = from_f32<T>(f - to_f32(val));
+// The 4 dims j0 .. j0+3 of row `row` at position t (zero when not valid or
+// beyond d), rotated when ROT.
+template <typename T, bool VEC, bool ROT>
+__device__ __forceinline__ void frag_load(const T* row, bool valid, int j0, int d, int t, int R, int mode,
+                                          const float* cs, float (&f)[4]) {
+  if (VEC) {
+    if (valid && j0 < d) {
+      if (ROT) {
+        rope_group<4>(row, j0, t, R, mode, cs, 1.0f, f);
       } else {
-        val = row[j];
+        Pk<T, 4> p = *reinterpret_cast<const Pk<T, 4>*>(row + j0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = to_f32(p.e[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + i;
+      f[i] = (valid && j < d) ? (ROT && R > 0 ? rope_elem(row, j, t, R, mode, cs, 1.0f) : to_f32(row[j])) : 0.f;
+    }
+  }
+}
+
+// Stage rows [row0, row0 + 64) of a [T, d] operand (row stride ld) into LDS,
+// dims padded to DP, rows >= T and dims >= d zero.  Outputs, each optional:
+// X[r*XS + j] (bf16-rounded value), Xl (its rounding residual, rotated
+// operands only), Xt[j*XTS + r] and Xtl (the same transposed).
+template <typename T, int DP, bool ROT, bool VEC>
+__device__ __forceinline__ void stage(const T* base, int64_t ld, int row0, int T_, int d, int R, int mode,
+                                      const float* cs, T* X, T* Xl, int XS, T* Xt, T* Xtl, int XTS) {
+  if constexpr (VEC) {
+    constexpr int G = kG<T>;
+    constexpr int NCH = DP / G;
+    for (int item = threadIdx.x; item < (TQ / 4) * NCH; item += blockDim.x) {
+      const int rg = item / NCH, j0 = (item % NCH) * G;
+      float v[4][G];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = row0 + 4 * rg + rr;
+        if (t < T_ && j0 < d) {
+          const T* row = base + (int64_t)t * ld;
+          if (ROT) {
+            rope_group<G>(row, j0, t, R, mode, cs, 1.0f, v[rr]);
+          } else {
+            Pk<T, G> p = *reinterpret_cast<const Pk<T, G>*>(row + j0);
+#pragma unroll
+            for (int e = 0; e < G; ++e) v[rr][e] = to_f32(p.e[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < G; ++e) v[rr][e] = 0.f;
+        }
+      }
+      Pk<T, G> hi[4], lo[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+          hi[rr].e[e] = from_f32<T>(v[rr][e]);
+          lo[rr].e[e] = from_f32<T>(v[rr][e] - to_f32(hi[rr].e[e]));
+        }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        if (X) *reinterpret_cast<Pk<T, G>*>(X + (4 * rg + rr) * XS + j0) = hi[rr];
+        if (Xl) *reinterpret_cast<Pk<T, G>*>(Xl + (4 * rg + rr) * XS + j0) = lo[rr];
+      }
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        if (Xt) {
+          Pk<T, 4> col;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) col.e[rr] = hi[rr].e[e];
+          *reinterpret_cast<Pk<T, 4>*>(Xt + (j0 + e) * XTS + 4 * rg) = col;
+        }
+        if (Xtl) {
+          Pk<T, 4> col;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) col.e[rr] = lo[rr].e[e];
+          *reinterpret_cast<Pk<T, 4>*>(Xtl + (j0 + e) * XTS + 4 * rg) = col;
+        }
       }
     }
-    if (X) X[r * XS + j] = val;
-    if (Xt) Xt[j * XTS + r] = val;
-    if (Xlo) Xlo[r * XS + j] = lo;
-    if (Xtlo) Xtlo[j * XTS + r] = lo;
+  } else {
+    for (int idx = threadIdx.x; idx < TQ * DP; idx += blockDim.x) {
+      const int r = idx / DP, j = idx % DP;
+      const int t = row0 + r;
+      float f = 0.f;
+      if (t < T_ && j < d) {
+        const T* row = base + (int64_t)t * ld;
+        f = (ROT && R > 0) ? rope_elem(row, j, t, R, mode, cs, 1.0f) : to_f32(row[j]);
+      }
+      const T hv = from_f32<T>(f);
+      const T lv = from_f32<T>(f - to_f32(hv));
+      if (X) X[r * XS + j] = hv;
+      if (Xl) Xl[r * XS + j] = lv;
+      if (Xt) Xt[j * XTS + r] = hv;
+      if (Xtl) Xtl[j * XTS + r] = lv;
+    }
   }
 }
 
-constexpr int kPad = 4;
+// Rotate back rows held in LDS as fp32 (F[r*FS + j], r < 64) and store them
+// to out[(row0 + r) * ld + j] for rows < T.
+template <typename T, bool VEC>
+__device__ __forceinline__ void store_unrotated(const float* F, int FS, T* out, int64_t ld, int row0, int T_, int d,
+                                                int R, int mode, const float* cs) {
+  if (VEC) {
+    const int ng = d / 4;
+    for (int idx = threadIdx.x; idx < TQ * ng; idx += blockDim.x) {
+      const int r = idx / ng, j0 = (idx % ng) * 4;
+      const int t = row0 + r;
+      if (t >= T_) continue;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = F[r * FS + j0 + i];
+      if (R > 0 && j0 < R) {
+        // the partner dims of this group, read from the fp32 row in LDS
+        const float2* tb = reinterpret_cast<const float2*>(cs + (int64_t)t * R);
+        if (mode == SLT_ROPE_HALF) {
+          const int h = R >> 1;
+          const bool first = j0 < h;
+          const int i0 = first ? j0 : j0 - h, p0 = first ? j0 + h : j0 - h;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float2 c = tb[i0 + i];
+            const float x = v[i], y = F[r * FS + p0 + i];
+            v[i] = first ? x * c.x + y * c.y : x * c.x - y * c.y;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float2 c = tb[(j0 + i) >> 1];
+            const float x = v[i], y = v[i + 1];
+            v[i] = x * c.x + y * c.y;
+            v[i + 1] = y * c.x - x * c.y;
+          }
+        }
+      }
+      *reinterpret_cast<Pk<T, 4>*>(out + (int64_t)t * ld + j0) = pack4<T>(v);
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < TQ * d; idx += blockDim.x) {
+      const int r = idx / d, j = idx % d;
+      const int t = row0 + r;
+      if (t >= T_) continue;
+      const float v = R > 0 ? rope_elem(&F[r * FS], j, t, R, mode, cs, -1.0f) : F[r * FS + j];
+      out[(int64_t)t * ld + j] = from_f32<T>(v);
+    }
+  }
+}
+
+template <typename T, int NC>
+struct Geo {
+  static constexpr int DP = NC * 16;
+  static constexpr int XS = DP + kG<T>;   // row stride of row-major tiles (16-byte aligned rows)
+  static constexpr int TS = TQ + kG<T>;   // row stride of transposed tiles
+  static constexpr int TILE = TQ * XS;    // elements of a row-major tile
+  static constexpr int TTILE = DP * TS;   // elements of a transposed tile
+  static constexpr int FS = DP + 1;       // fp32 scratch row stride
+};
 
 // ---------------------------------------------------------------------------
 // Forward.  grid (ceil(T/64), H, B); wave w owns queries q0 + 16w + l%16.
 // ---------------------------------------------------------------------------
-template <typename T, int NC>
+template <typename T, int NC, bool VEC>
 __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
-  constexpr int DP = NC * 16;
-  constexpr int KS = DP + kPad;      // Ks row stride
-  constexpr int VS = TQ + kPad;      // Vt row stride
-  __shared__ __attribute__((aligned(16))) T Ks[TQ * KS];
-  __shared__ __attribute__((aligned(16))) T Ksl[sizeof(T) == 2 ? TQ * KS : 4];  // rotated k, low part
-  __shared__ __attribute__((aligned(16))) T Vt[DP * VS];
+  using Gm = Geo<T, NC>;
+  constexpr int DP = Gm::DP, XS = Gm::XS, TS = Gm::TS;
+  __shared__ __attribute__((aligned(16))) T smem[2 * Gm::TILE + Gm::TTILE];
+  T* Ks = smem;                 // rotated k (bf16-rounded)
+  T* Ksl = smem + Gm::TILE;     // its residual (bf16 only)
+  T* Vt = smem + 2 * Gm::TILE;  // v transposed
 
   const int b = blockIdx.z, h = blockIdx.y, q0 = blockIdx.x * TQ;
   const int T_ = a.T, d = a.d;
   const int kvh = h / (a.H / a.Hkv);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int qi = q0 + wave * 16 + (lane & 15);   // this lane's query
+  const int qi = q0 + wave * 16 + (lane & 15);
   const int g4 = (lane >> 4) * 4;
   const float scale2 = kLog2e / sqrtf((float)d);
 
@@ -179,21 +339,12 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
   const T* kb = static_cast<const T*>(a.k) + (int64_t)b * T_ * a.ldk + kvh * d;
   const T* vb = static_cast<const T*>(a.v) + (int64_t)b * T_ * a.ldv + kvh * d;
 
-  // Q fragments (rotated): lane holds Q[qi][16c + g4 + i] as hi + lo
   Pk<T, 4> qf[NC], qfl[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float f[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 16 * c + g4 + i;
-      f[i] = 0.f;
-      if (qi < T_ && j < d) {
-        const T* row = qb + (int64_t)qi * a.ldq;
-        f[i] = a.R > 0 ? rope_elem<T>(row, j, qi, a.R, a.rope_mode, a.cs, 1.0f) : to_f32(row[j]);
-      }
-    }
-    qf[c] = pack4<T>(f[0], f[1], f[2], f[3]);
+    frag_load<T, VEC, true>(qb + (int64_t)qi * a.ldq, qi < T_, 16 * c + g4, d, qi, a.R, a.rope_mode, a.cs, f);
+    qf[c] = pack4<T>(f);
     qfl[c] = low_part<T>(qf[c], f);
   }
 
@@ -202,14 +353,13 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int last_q = min(T_, q0 + TQ) - 1;
-  const int ntiles = last_q / TQ + 1;
+  const int ntiles = (min(T_, q0 + TQ) - 1) / TQ + 1;
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * TQ;
     __syncthreads();
-    stage_tile<T, DP, true>(kb, a.ldk, 0, k0, T_, d, a.R, a.rope_mode, a.cs, Ks, KS, nullptr, 0,
-                            sizeof(T) == 2 ? Ksl : nullptr);
-    stage_tile<T, DP, false>(vb, a.ldv, 0, k0, T_, d, 0, 0, nullptr, nullptr, 0, Vt, VS);
+    stage<T, DP, true, VEC>(kb, a.ldk, k0, T_, d, a.R, a.rope_mode, a.cs, Ks, kBf<T> ? Ksl : nullptr, XS, nullptr,
+                            nullptr, TS);
+    stage<T, DP, false, VEC>(vb, a.ldv, k0, T_, d, 0, 0, nullptr, nullptr, nullptr, XS, Vt, nullptr, TS);
     __syncthreads();
 
     float s[4][4];
@@ -219,11 +369,12 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const Pk<T, 4> k4 = lds4(&Ks[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]);
+        const int off = (ks * 16 + (lane & 15)) * XS + 16 * c + g4;
+        const Pk<T, 4> k4 = lds4(&Ks[off]);
         acc = mma16(k4, qf[c], acc);
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (kBf<T>) {
           acc = mma16(k4, qfl[c], acc);
-          acc = mma16(lds4(&Ksl[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]), qf[c], acc);
+          acc = mma16(lds4(&Ksl[off]), qf[c], acc);
         }
       }
 #pragma unroll
@@ -248,7 +399,7 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
         p[r] = exp2f(s[ks][r] - mn);
         rs += p[r];
       }
-      pf[ks] = pack4<T>(p[0], p[1], p[2], p[3]);
+      pf[ks] = pack4<T>(p);
     }
     rs += __shfl_xor(rs, 16, 64);
     rs += __shfl_xor(rs, 32, 64);
@@ -259,27 +410,35 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
       oacc[c] *= alpha;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        oacc[c] = mma16(lds4(&Vt[(16 * c + (lane & 15)) * VS + ks * 16 + g4]), pf[ks], oacc[c]);
+        oacc[c] = mma16(lds4(&Vt[(16 * c + (lane & 15)) * TS + ks * 16 + g4]), pf[ks], oacc[c]);
     }
   }
 
+  // o: lane holds O[qi][16c + g4 + r]; the residual o - bf16(o) goes to ores_out.
   if (qi < T_) {
     const float inv = 1.0f / l;
     T* ob = static_cast<T*>(a.out) + ((int64_t)b * T_ + qi) * a.ldo + h * d;
     T* rb = a.ores_out ? static_cast<T*>(a.ores_out) + ((int64_t)b * T_ + qi) * ((int64_t)a.H * d) + h * d
                        : nullptr;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c) {
+      const int j0 = 16 * c + g4;
+      if (j0 >= d) continue;
+      float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * c + g4 + r;
-        if (j < d) {
-          const float val = oacc[c][r] * inv;
-          const T hi = from_f32<T>(val);
-          ob[j] = hi;
-          if (rb) rb[j] = from_f32<T>(val - to_f32(hi));
+      for (int r = 0; r < 4; ++r) v[r] = oacc[c][r] * inv;
+      const Pk<T, 4> hi = pack4<T>(v);
+      const Pk<T, 4> lo = low_part<T>(hi, v);
+      if (VEC) {
+        *reinterpret_cast<Pk<T, 4>*>(ob + j0) = hi;
+        if (rb) *reinterpret_cast<Pk<T, 4>*>(rb + j0) = lo;
+      } else {
+        for (int r = 0; r < 4 && j0 + r < d; ++r) {
+          ob[j0 + r] = hi.e[r];
+          if (rb) rb[j0 + r] = lo.e[r];
         }
       }
+    }
     if (lane < 16) a.lse[((int64_t)b * a.H + h) * T_ + qi] = (m + log2f(l)) * kLn2;
   }
 }
@@ -290,17 +449,20 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
 //   S^T = K Q^T, P = exp(S/sqrt(d) - lse), dP^T = V dO^T,
 //   dS = P (dP - D), dQ^T += K^T dS^T, then dq = rotate^T(dQ) / sqrt(d).
 // ---------------------------------------------------------------------------
-template <typename T, int NC>
+template <typename T, int NC, bool VEC>
 __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
-  constexpr int DP = NC * 16;
-  constexpr int KS = DP + kPad;
-  constexpr int TS = TQ + kPad;
-  __shared__ __attribute__((aligned(16))) T Ks[TQ * KS];
-  __shared__ __attribute__((aligned(16))) T Ksl[sizeof(T) == 2 ? TQ * KS : 4];  // rotated k, low part
-  __shared__ __attribute__((aligned(16))) T Vs[TQ * KS];
-  __shared__ __attribute__((aligned(16))) T Kt[DP * TS];
-  __shared__ __attribute__((aligned(16))) T Ktl[sizeof(T) == 2 ? DP * TS : 4];  // rotated k, low part
-  __shared__ float dqs[TQ * (DP + 1)];
+  using Gm = Geo<T, NC>;
+  constexpr int DP = Gm::DP, XS = Gm::XS, TS = Gm::TS, FS = Gm::FS;
+  constexpr int TILES = 3 * Gm::TILE + 2 * Gm::TTILE;
+  constexpr int FBYTES = TQ * FS * 4;
+  constexpr int SBYTES = TILES * (int)sizeof(T) > FBYTES ? TILES * (int)sizeof(T) : FBYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SBYTES];
+  T* Ks = reinterpret_cast<T*>(smem);
+  T* Ksl = Ks + Gm::TILE;
+  T* Vs = Ks + 2 * Gm::TILE;
+  T* Kt = Ks + 3 * Gm::TILE;
+  T* Ktl = Kt + Gm::TTILE;
+  float* dqs = reinterpret_cast<float*>(smem);  // reused after the last tile
 
   const int b = blockIdx.z, h = blockIdx.y, q0 = blockIdx.x * TQ;
   const int T_ = a.T, d = a.d;
@@ -315,54 +477,49 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
   const T* kb = static_cast<const T*>(a.k) + (int64_t)b * T_ * a.ldk + kvh * d;
   const T* vb = static_cast<const T*>(a.v) + (int64_t)b * T_ * a.ldv + kvh * d;
   const T* gb = static_cast<const T*>(a.dout) + (int64_t)b * T_ * a.lddo + h * d;
-
-  // Q (rotated, hi + lo) and dO fragments; D = dO . O for this lane's query,
-  // with O taken with its bf16 rounding residual (D multiplies the weighted
-  // mean key, so its error is not averaged away over the keys).
-  Pk<T, 4> qf[NC], qfl[NC], gf[NC];
   const T* ob = static_cast<const T*>(a.o) + (int64_t)b * T_ * a.ldo + h * d;
   const T* rbase = a.ores_in ? static_cast<const T*>(a.ores_in) + (int64_t)b * T_ * ((int64_t)a.H * d) + h * d
                              : nullptr;
+
+  Pk<T, 4> qf[NC], qfl[NC], gf[NC];
   float dpart = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    float f[4], g[4];
+    const int j0 = 16 * c + g4;
+    float f[4], g[4], o[4], r4[4];
+    frag_load<T, VEC, true>(qb + (int64_t)qi * a.ldq, qi < T_, j0, d, qi, a.R, a.rope_mode, a.cs, f);
+    frag_load<T, VEC, false>(gb + (int64_t)qi * a.lddo, qi < T_, j0, d, qi, 0, 0, nullptr, g);
+    frag_load<T, VEC, false>(ob + (int64_t)qi * a.ldo, qi < T_, j0, d, qi, 0, 0, nullptr, o);
+    if (rbase) {
+      frag_load<T, VEC, false>(rbase + (int64_t)qi * ((int64_t)a.H * d), qi < T_, j0, d, qi, 0, 0, nullptr, r4);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 16 * c + g4 + i;
-      f[i] = g[i] = 0.f;
-      if (qi < T_ && j < d) {
-        const T* row = qb + (int64_t)qi * a.ldq;
-        f[i] = a.R > 0 ? rope_elem<T>(row, j, qi, a.R, a.rope_mode, a.cs, 1.0f) : to_f32(row[j]);
-        g[i] = to_f32(gb[(int64_t)qi * a.lddo + j]);
-        float ov = to_f32(ob[(int64_t)qi * a.ldo + j]);
-        if (rbase) ov += to_f32(rbase[(int64_t)qi * ((int64_t)a.H * d) + j]);
-        dpart += ov * g[i];
-      }
+      for (int i = 0; i < 4; ++i) r4[i] = 0.f;
     }
-    qf[c] = pack4<T>(f[0], f[1], f[2], f[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dpart += (o[i] + r4[i]) * g[i];
+    qf[c] = pack4<T>(f);
     qfl[c] = low_part<T>(qf[c], f);
-    gf[c] = pack4<T>(g[0], g[1], g[2], g[3]);
+    gf[c] = pack4<T>(g);
   }
   dpart += __shfl_xor(dpart, 16, 64);
   dpart += __shfl_xor(dpart, 32, 64);
   const float Dq = dpart;
   const int64_t srow = ((int64_t)b * a.H + h) * T_;
-  if (qi < T_ && lane < 16) a.delta[srow + qi] = Dq;   // read by the dK/dV kernel
+  if (qi < T_ && lane < 16) a.delta[srow + qi] = Dq;  // read by the dK/dV kernel
   const float lse2 = qi < T_ ? a.lse_in[srow + qi] * kLog2e : 0.f;
 
   f32x4 dqacc[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) dqacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int last_q = min(T_, q0 + TQ) - 1;
-  const int ntiles = last_q / TQ + 1;
+  const int ntiles = (min(T_, q0 + TQ) - 1) / TQ + 1;
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * TQ;
     __syncthreads();
-    stage_tile<T, DP, true>(kb, a.ldk, 0, k0, T_, d, a.R, a.rope_mode, a.cs, Ks, KS, Kt, TS,
-                            sizeof(T) == 2 ? Ksl : nullptr, sizeof(T) == 2 ? Ktl : nullptr);
-    stage_tile<T, DP, false>(vb, a.ldv, 0, k0, T_, d, 0, 0, nullptr, Vs, KS, nullptr, 0);
+    stage<T, DP, true, VEC>(kb, a.ldk, k0, T_, d, a.R, a.rope_mode, a.cs, Ks, kBf<T> ? Ksl : nullptr, XS, Kt,
+                            kBf<T> ? Ktl : nullptr, TS);
+    stage<T, DP, false, VEC>(vb, a.ldv, k0, T_, d, 0, 0, nullptr, Vs, nullptr, XS, nullptr, nullptr, TS);
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -370,13 +527,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
       f32x4 pacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const Pk<T, 4> k4 = lds4(&Ks[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]);
+        const int off = (ks * 16 + (lane & 15)) * XS + 16 * c + g4;
+        const Pk<T, 4> k4 = lds4(&Ks[off]);
         sacc = mma16(k4, qf[c], sacc);
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (kBf<T>) {
           sacc = mma16(k4, qfl[c], sacc);
-          sacc = mma16(lds4(&Ksl[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]), qf[c], sacc);
+          sacc = mma16(lds4(&Ksl[off]), qf[c], sacc);
         }
-        pacc = mma16(lds4(&Vs[(ks * 16 + (lane & 15)) * KS + 16 * c + g4]), gf[c], pacc);
+        pacc = mma16(lds4(&Vs[off]), gf[c], pacc);
       }
       float ds[4];
 #pragma unroll
@@ -386,35 +544,29 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
         const float p = ok ? exp2f(sacc[r] * scale2 - lse2) : 0.f;
         ds[r] = p * (pacc[r] - Dq);
       }
-      const Pk<T, 4> dsf = pack4<T>(ds[0], ds[1], ds[2], ds[3]);
+      const Pk<T, 4> dsf = pack4<T>(ds);
       const Pk<T, 4> dsl = low_part<T>(dsf, ds);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const Pk<T, 4> kt4 = lds4(&Kt[(16 * c + (lane & 15)) * TS + ks * 16 + g4]);
+        const int toff = (16 * c + (lane & 15)) * TS + ks * 16 + g4;
+        const Pk<T, 4> kt4 = lds4(&Kt[toff]);
         dqacc[c] = mma16(kt4, dsf, dqacc[c]);
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (kBf<T>) {
           dqacc[c] = mma16(kt4, dsl, dqacc[c]);
-          dqacc[c] = mma16(lds4(&Ktl[(16 * c + (lane & 15)) * TS + ks * 16 + g4]), dsf, dqacc[c]);
+          dqacc[c] = mma16(lds4(&Ktl[toff]), dsf, dqacc[c]);
         }
       }
     }
   }
   // dq~ (rotated frame) -> LDS, then rotate back and store.
   __syncthreads();
-  constexpr int QS = DP + 1;
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dqs[(wave * 16 + (lane & 15)) * QS + 16 * c + g4 + r] = dqacc[c][r] * scale;
+    for (int r = 0; r < 4; ++r) dqs[(wave * 16 + (lane & 15)) * FS + 16 * c + g4 + r] = dqacc[c][r] * scale;
   __syncthreads();
-  T* db = static_cast<T*>(a.dq) + (int64_t)b * T_ * a.lddq + h * d;
-  for (int idx = threadIdx.x; idx < TQ * d; idx += blockDim.x) {
-    const int r = idx / d, j = idx % d;
-    const int t = q0 + r;
-    if (t >= T_) continue;
-    const float v = a.R > 0 ? rope_elem_f(&dqs[r * QS], j, t, a.R, a.rope_mode, a.cs, -1.0f) : dqs[r * QS + j];
-    db[(int64_t)t * a.lddq + j] = from_f32<T>(v);
-  }
+  T* dqb = static_cast<T*>(a.dq) + (int64_t)b * T_ * a.lddq + h * d;
+  store_unrotated<T, VEC>(dqs, FS, dqb, a.lddq, q0, T_, d, a.R, a.rope_mode, a.cs);
 }
 
 // ---------------------------------------------------------------------------
@@ -423,24 +575,28 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
 // its key tile:  S = Q K^T, P = exp(S/sqrt(d) - lse), dP = dO V^T,
 // dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
 // ---------------------------------------------------------------------------
-template <typename T, int NC>
+template <typename T, int NC, bool VEC>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
-  constexpr int DP = NC * 16;
-  constexpr int XS = DP + kPad;
-  constexpr int TS = TQ + kPad;
-  __shared__ __attribute__((aligned(16))) T Qs[TQ * XS];
-  __shared__ __attribute__((aligned(16))) T Qsl[sizeof(T) == 2 ? TQ * XS : 4];  // rotated q, low part
-  __shared__ __attribute__((aligned(16))) T Gs[TQ * XS];
-  __shared__ __attribute__((aligned(16))) T Qt[DP * TS];
-  __shared__ __attribute__((aligned(16))) T Qtl[sizeof(T) == 2 ? DP * TS : 4];  // rotated q^T, low part
-  __shared__ __attribute__((aligned(16))) T Gt[DP * TS];
+  using Gm = Geo<T, NC>;
+  constexpr int DP = Gm::DP, XS = Gm::XS, TS = Gm::TS, FS = Gm::FS;
+  constexpr int TILES = 3 * Gm::TILE + 3 * Gm::TTILE;
+  constexpr int FBYTES = TQ * FS * 4;
+  constexpr int SBYTES = TILES * (int)sizeof(T) > FBYTES ? TILES * (int)sizeof(T) : FBYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SBYTES];
   __shared__ float lse2s[TQ], Ds[TQ];
+  T* Qs = reinterpret_cast<T*>(smem);
+  T* Qsl = Qs + Gm::TILE;
+  T* Gs = Qs + 2 * Gm::TILE;
+  T* Qt = Qs + 3 * Gm::TILE;
+  T* Qtl = Qt + Gm::TTILE;
+  T* Gt = Qt + 2 * Gm::TTILE;
+  float* dks = reinterpret_cast<float*>(smem);  // reused after the last tile
 
   const int b = blockIdx.z, kvh = blockIdx.y, k0 = blockIdx.x * TQ;
   const int T_ = a.T, d = a.d;
   const int rep = a.H / a.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ki = k0 + wave * 16 + (lane & 15);   // this lane's key
+  const int ki = k0 + wave * 16 + (lane & 15);  // this lane's key
   const int g4 = (lane >> 4) * 4;
   const float scale = 1.0f / sqrtf((float)d);
   const float scale2 = kLog2e * scale;
@@ -452,19 +608,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     float f[4], g[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 16 * c + g4 + i;
-      f[i] = g[i] = 0.f;
-      if (ki < T_ && j < d) {
-        const T* row = kb + (int64_t)ki * a.ldk;
-        f[i] = a.R > 0 ? rope_elem<T>(row, j, ki, a.R, a.rope_mode, a.cs, 1.0f) : to_f32(row[j]);
-        g[i] = to_f32(vb[(int64_t)ki * a.ldv + j]);
-      }
-    }
-    kf[c] = pack4<T>(f[0], f[1], f[2], f[3]);
+    frag_load<T, VEC, true>(kb + (int64_t)ki * a.ldk, ki < T_, 16 * c + g4, d, ki, a.R, a.rope_mode, a.cs, f);
+    frag_load<T, VEC, false>(vb + (int64_t)ki * a.ldv, ki < T_, 16 * c + g4, d, ki, 0, 0, nullptr, g);
+    kf[c] = pack4<T>(f);
     kfl[c] = low_part<T>(kf[c], f);
-    vf[c] = pack4<T>(g[0], g[1], g[2], g[3]);
+    vf[c] = pack4<T>(g);
   }
 
   f32x4 dk[NC], dv[NC];
@@ -480,9 +628,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
     for (int qt = blockIdx.x; qt < nqt; ++qt) {
       const int q0 = qt * TQ;
       __syncthreads();
-      stage_tile<T, DP, true>(qb, a.ldq, 0, q0, T_, d, a.R, a.rope_mode, a.cs, Qs, XS, Qt, TS,
-                              sizeof(T) == 2 ? Qsl : nullptr, sizeof(T) == 2 ? Qtl : nullptr);
-      stage_tile<T, DP, false>(gb, a.lddo, 0, q0, T_, d, 0, 0, nullptr, Gs, XS, Gt, TS);
+      stage<T, DP, true, VEC>(qb, a.ldq, q0, T_, d, a.R, a.rope_mode, a.cs, Qs, kBf<T> ? Qsl : nullptr, XS, Qt,
+                              kBf<T> ? Qtl : nullptr, TS);
+      stage<T, DP, false, VEC>(gb, a.lddo, q0, T_, d, 0, 0, nullptr, Gs, nullptr, XS, Gt, nullptr, TS);
       if (threadIdx.x < TQ) {
         const int t = q0 + threadIdx.x;
         lse2s[threadIdx.x] = t < T_ ? a.lse_in[srow + t] * kLog2e : 0.f;
@@ -495,13 +643,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
         f32x4 pacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const Pk<T, 4> q4 = lds4(&Qs[(qs * 16 + (lane & 15)) * XS + 16 * c + g4]);
+          const int off = (qs * 16 + (lane & 15)) * XS + 16 * c + g4;
+          const Pk<T, 4> q4 = lds4(&Qs[off]);
           sacc = mma16(q4, kf[c], sacc);
-          if constexpr (sizeof(T) == 2) {
-            sacc = mma16(lds4(&Qsl[(qs * 16 + (lane & 15)) * XS + 16 * c + g4]), kf[c], sacc);
+          if constexpr (kBf<T>) {
+            sacc = mma16(lds4(&Qsl[off]), kf[c], sacc);
             sacc = mma16(q4, kfl[c], sacc);
           }
-          pacc = mma16(lds4(&Gs[(qs * 16 + (lane & 15)) * XS + 16 * c + g4]), vf[c], pacc);
+          pacc = mma16(lds4(&Gs[off]), vf[c], pacc);
         }
         float p[4], ds[4];
 #pragma unroll
@@ -512,17 +661,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
           p[r] = ok ? exp2f(sacc[r] * scale2 - lse2s[ql]) : 0.f;
           ds[r] = p[r] * (pacc[r] - Ds[ql]);
         }
-        const Pk<T, 4> pf = pack4<T>(p[0], p[1], p[2], p[3]);
-        const Pk<T, 4> dsf = pack4<T>(ds[0], ds[1], ds[2], ds[3]);
+        const Pk<T, 4> pf = pack4<T>(p);
+        const Pk<T, 4> dsf = pack4<T>(ds);
         const Pk<T, 4> dsl = low_part<T>(dsf, ds);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          dv[c] = mma16(lds4(&Gt[(16 * c + (lane & 15)) * TS + qs * 16 + g4]), pf, dv[c]);
-          const Pk<T, 4> qt4 = lds4(&Qt[(16 * c + (lane & 15)) * TS + qs * 16 + g4]);
+          const int toff = (16 * c + (lane & 15)) * TS + qs * 16 + g4;
+          dv[c] = mma16(lds4(&Gt[toff]), pf, dv[c]);
+          const Pk<T, 4> qt4 = lds4(&Qt[toff]);
           dk[c] = mma16(qt4, dsf, dk[c]);
-          if constexpr (sizeof(T) == 2) {
+          if constexpr (kBf<T>) {
             dk[c] = mma16(qt4, dsl, dk[c]);
-            dk[c] = mma16(lds4(&Qtl[(16 * c + (lane & 15)) * TS + qs * 16 + g4]), dsf, dk[c]);
+            dk[c] = mma16(lds4(&Qtl[toff]), dsf, dk[c]);
           }
         }
       }
@@ -533,60 +683,74 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
   if (ki < T_) {
     T* dvb = static_cast<T*>(a.dv) + ((int64_t)b * T_ + ki) * a.lddv + kvh * d;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * c + g4 + r;
-        if (j < d) dvb[j] = from_f32<T>(dv[c][r]);
+    for (int c = 0; c < NC; ++c) {
+      const int j0 = 16 * c + g4;
+      if (j0 >= d) continue;
+      float v[4] = {dv[c][0], dv[c][1], dv[c][2], dv[c][3]};
+      const Pk<T, 4> pk = pack4<T>(v);
+      if (VEC) {
+        *reinterpret_cast<Pk<T, 4>*>(dvb + j0) = pk;
+      } else {
+        for (int r = 0; r < 4 && j0 + r < d; ++r) dvb[j0 + r] = pk.e[r];
       }
+    }
   }
-  // dk~ -> LDS (reusing Qs/Gs space as fp32), rotate back, store.
+  // dk~ -> LDS (reusing the tile space), rotate back, store.
   __syncthreads();
-  constexpr int QS2 = DP + 1;
-  __shared__ float dkbuf[TQ * QS2];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dkbuf[(wave * 16 + (lane & 15)) * QS2 + 16 * c + g4 + r] = dk[c][r] * scale;
+    for (int r = 0; r < 4; ++r) dks[(wave * 16 + (lane & 15)) * FS + 16 * c + g4 + r] = dk[c][r] * scale;
   __syncthreads();
   T* dkb = static_cast<T*>(a.dk) + (int64_t)b * T_ * a.lddk + kvh * d;
-  for (int idx = threadIdx.x; idx < TQ * d; idx += blockDim.x) {
-    const int r = idx / d, j = idx % d;
-    const int t = k0 + r;
-    if (t >= T_) continue;
-    const float v = a.R > 0 ? rope_elem_f(&dkbuf[r * QS2], j, t, a.R, a.rope_mode, a.cs, -1.0f) : dkbuf[r * QS2 + j];
-    dkb[(int64_t)t * a.lddk + j] = from_f32<T>(v);
+  store_unrotated<T, VEC>(dks, FS, dkb, a.lddk, k0, T_, d, a.R, a.rope_mode, a.cs);
+}
+
+// The vector path needs every row group of 16 bytes (and the fragment groups
+// of 4) to be aligned and the RoPE pairs not to straddle a group.
+template <typename T>
+bool vec_path_ok(const AttnArgs& a, bool bwd) {
+  constexpr int G = kG<T>;
+  auto al = [](const void* p) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  if (a.d % G) return false;
+  if (a.R > 0 && (a.rope_mode == SLT_ROPE_HALF ? (a.R / 2) % G : a.R % G)) return false;
+  for (int64_t ld : {a.ldq, a.ldk, a.ldv, a.ldo})
+    if (ld % G) return false;
+  if (!al(a.q) || !al(a.k) || !al(a.v) || !al(a.out) || !al(a.ores_out) || !al(a.cs)) return false;
+  if (bwd) {
+    for (int64_t ld : {a.lddo, a.lddq, a.lddk, a.lddv})
+      if (ld % G) return false;
+    if (!al(a.o) || !al(a.dout) || !al(a.dq) || !al(a.dk) || !al(a.dv) || !al(a.ores_in)) return false;
   }
+  return true;
 }
 
 }  // namespace
 
 int64_t attention_bwd_ws(int B, int H, int T) { return (int64_t)B * H * T * 4; }
 
-template <typename T>
+template <typename T, bool VEC>
 static slt_status attn_fwd_t(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.T + TQ - 1) / TQ, a.H, a.B);
-  const int nc = (a.d + 15) / 16;
-  switch (nc) {
-    case 1: attn_fwd_k<T, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: attn_fwd_k<T, 2><<<grid, 256, 0, s>>>(a); break;
-    case 3: attn_fwd_k<T, 3><<<grid, 256, 0, s>>>(a); break;
-    case 4: attn_fwd_k<T, 4><<<grid, 256, 0, s>>>(a); break;
+  switch ((a.d + 15) / 16) {
+    case 1: attn_fwd_k<T, 1, VEC><<<grid, 256, 0, s>>>(a); break;
+    case 2: attn_fwd_k<T, 2, VEC><<<grid, 256, 0, s>>>(a); break;
+    case 3: attn_fwd_k<T, 3, VEC><<<grid, 256, 0, s>>>(a); break;
+    case 4: attn_fwd_k<T, 4, VEC><<<grid, 256, 0, s>>>(a); break;
     default: return fail(SLT_EUNSUPPORTED, "attention: head dim above 64");
   }
   return check_launch("attention_fwd");
 }
 
-template <typename T>
+template <typename T, bool VEC>
 static slt_status attn_bwd_t(const AttnArgs& a, hipStream_t s) {
   dim3 gq((a.T + TQ - 1) / TQ, a.H, a.B);
   dim3 gk((a.T + TQ - 1) / TQ, a.Hkv, a.B);
-  const int nc = (a.d + 15) / 16;
-  switch (nc) {
-#define SLT_ATT_BWD(NCv)                                  \
-  case NCv:                                               \
-    attn_bwd_dq_k<T, NCv><<<gq, 256, 0, s>>>(a);          \
-    attn_bwd_dkdv_k<T, NCv><<<gk, 256, 0, s>>>(a);        \
+  switch ((a.d + 15) / 16) {
+#define SLT_ATT_BWD(NCv)                                   \
+  case NCv:                                                \
+    attn_bwd_dq_k<T, NCv, VEC><<<gq, 256, 0, s>>>(a);      \
+    attn_bwd_dkdv_k<T, NCv, VEC><<<gk, 256, 0, s>>>(a);    \
     break;
     SLT_ATT_BWD(1) SLT_ATT_BWD(2) SLT_ATT_BWD(3) SLT_ATT_BWD(4)
 #undef SLT_ATT_BWD
@@ -597,12 +761,16 @@ static slt_status attn_bwd_t(const AttnArgs& a, hipStream_t s) {
 
 slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return SLT_OK;
-  return a.dtype == SLT_BF16 ? attn_fwd_t<bf16>(a, s) : attn_fwd_t<float>(a, s);
+  if (a.dtype == SLT_BF16)
+    return vec_path_ok<bf16>(a, false) ? attn_fwd_t<bf16, true>(a, s) : attn_fwd_t<bf16, false>(a, s);
+  return vec_path_ok<float>(a, false) ? attn_fwd_t<float, true>(a, s) : attn_fwd_t<float, false>(a, s);
 }
 
 slt_status launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return SLT_OK;
-  return a.dtype == SLT_BF16 ? attn_bwd_t<bf16>(a, s) : attn_bwd_t<float>(a, s);
+  if (a.dtype == SLT_BF16)
+    return vec_path_ok<bf16>(a, true) ? attn_bwd_t<bf16, true>(a, s) : attn_bwd_t<bf16, false>(a, s);
+  return vec_path_ok<float>(a, true) ? attn_bwd_t<float, true>(a, s) : attn_bwd_t<float, false>(a, s);
 }
 
 }  // namespace slt
