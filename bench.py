@@ -4,10 +4,11 @@
 One step = slt_forward_loss + slt_backward + slt_adamw_step over one batch of
 synthetic tokens for the Llama-style decoder d=384, 8 layers, 8 heads,
 T=256, B=64, V=4096, SwiGLU 1024 (bf16 activations, fp32 master weights and
-moments), inputs resident in HBM.  Prints one JSON line: tokens/s, the
-roofline position of the dominant kernel (timed live with HIP events on the
-stream it runs on) and the CPU oracle timed on a bounded sample of the same
-workload.
+moments), inputs resident in HBM.  Prints one JSON line with tokens/s, a
+per-class kernel breakdown (each class re-launched through the C ABI with the
+step's shapes and timed with HIP events on the current stream, the one the
+library launches on), the roofline position of the dominant class, and the CPU
+oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -22,25 +23,53 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"bf16_tflops": 2500.0, "f32_tflops": 157.3, "hbm_gbs": 8000.0}
+PEAK = {"bf16": 2500.0, "f32": 157.3, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s (vendor figures)
 
 
-def step_flops(w) -> float:
-    """Algorithmic FLOPs of one step: 6 per matmul parameter per token
-    (forward, dX, dW) plus causal attention 6 L C (T+1) per token."""
+def shapes(w):
+    """The step's GEMM launches as (M, N, K, residual) per class: forward
+    projections (k-major operands), activation gradients dX = dY W and
+    weight gradients dW = dY^T X."""
     d = w.C // w.H
-    qkv = (w.H + 2 * w.Hkv) * d
-    if w.block == "llama":
-        per_layer = w.C * qkv + w.C * w.H * d + 3 * w.C * w.F
-    else:
-        per_layer = w.C * qkv + w.C * w.F + w.C * (w.H * d + w.F)
-    mat = w.L * per_layer + w.V * w.C
-    return w.N * (6.0 * mat + 6.0 * w.L * w.C * (w.T + 1))
+    qd, kd = w.H * d, w.Hkv * d
+    qkv = qd + 2 * kd
+    N, C, F, V = w.N, w.C, w.F, w.V
+    fwd, dx, dw = [], [], []
+    for _ in range(w.L):
+        if w.block == "llama":
+            fwd += [(N, qkv, C, 0), (N, C, qd, 1), (N, 2 * F, C, 0), (N, C, F, 1)]
+            dx += [(N, F, C, 0), (N, C, 2 * F, 0), (N, qd, C, 0), (N, C, qkv, 0)]
+            dw += [(C, F, N, 0), (2 * F, C, N, 0), (C, qd, N, 0), (qkv, C, N, 0)]
+        else:
+            iw, ow = qkv + F, qd + F
+            fwd += [(N, iw, C, 0), (N, C, ow, 1)]
+            dx += [(N, ow, C, 0), (N, C, iw, 0)]
+            dw += [(C, ow, N, 0), (iw, C, N, 0)]
+    fwd.append((N, V, C, 0))
+    dx.append((N, C, V, 0))
+    dw.append((V, C, N, 0))
+    return {"gemm_fwd": fwd, "gemm_dx": dx, "gemm_dw": dw}
 
 
-def time_launches(fn, reps: int, torch) -> float:
-    """Average duration (s) of fn() over reps launches, HIP events on the
-    current stream (the one the library launches on)."""
+def attn_flops(w):
+    """Algorithmic causal attention FLOPs (forward, backward) of one step: per
+    (b, h) the forward has two products over the T(T+1)/2 causal pairs (S and
+    P V), the backward four (dP, dV, dK, dQ); recomputing S is not counted."""
+    f = 4.0 * w.B * w.H * (w.T * (w.T + 1) / 2) * (w.C // w.H) * w.L
+    return f, 2.0 * f
+
+
+def step_flops(w):
+    """Algorithmic FLOPs of one step: 6 per matmul parameter per token plus
+    causal attention (3x its forward products)."""
+    g = sum(2.0 * M * N * K for cls in shapes(w).values() for (M, N, K, _) in cls)
+    fa, ba = attn_flops(w)
+    return g + fa + ba
+
+
+def time_block(fn, reps, torch):
+    """Average seconds of fn() (which enqueues on the current stream), HIP
+    events on that stream."""
     s = torch.cuda.current_stream()
     fn()
     torch.cuda.synchronize()
@@ -54,35 +83,86 @@ def time_launches(fn, reps: int, torch) -> float:
     return a.elapsed_time(b) / 1e3 / reps
 
 
-def dominant_kernel(w, ts, torch, reps):
-    """The step's most expensive launch class is its largest GEMM family; time
-    the [W1;W3] projection (M=N_tok, N=2F, K=C, bf16 in/out) exactly as the
-    forward launches it, on the step's own buffers."""
+def kernel_classes(w, ts, torch, reps):
+    """Per-class time of one step, each class re-run through the C ABI with
+    the step's shapes on fresh buffers."""
     from scratch_llama_transformer_amd import binding as B
     dt = B.BF16 if w.act == "bf16" else B.F32
+    tdt = torch.bfloat16 if dt == B.BF16 else torch.float32
+    peak = PEAK["bf16"] if dt == B.BF16 else PEAK["f32"]
     es = 2 if dt == B.BF16 else 4
-    M, N, K = w.N, 2 * w.F, w.C
-    layout = {t["name"]: t for t in ts.layout}
-    wptr = ts.compute_params.data_ptr() + layout["h0.w1"]["offset"] * es
-    x = torch.empty((M, K), dtype=torch.bfloat16 if dt == B.BF16 else torch.float32, device="cuda").normal_()
-    y = torch.empty((M, N), dtype=x.dtype, device="cuda")
+    out = {}
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    for cls, launches in shapes(w).items():
+        bufs = []
+        for (M, N, K, res) in launches:
+            if cls == "gemm_fwd":
+                A = torch.empty((M, K), dtype=tdt, device="cuda").normal_()
+                Bm = torch.empty((N, K), dtype=tdt, device="cuda").normal_()
+                Cm = torch.empty((M, N), dtype=tdt, device="cuda")
+                R = torch.empty((M, N), dtype=tdt, device="cuda").normal_() if res else None
+                bufs.append((M, N, K, A, K, 1, Bm, K, 1, Cm, N, R, N, dt, dt, None, 0))
+            elif cls == "gemm_dx":
+                A = torch.empty((M, K), dtype=tdt, device="cuda").normal_()
+                Bm = torch.empty((K, N), dtype=tdt, device="cuda").normal_()
+                Cm = torch.empty((M, N), dtype=tdt, device="cuda")
+                bufs.append((M, N, K, A, K, 1, Bm, N, 0, Cm, N, None, 0, dt, dt, None, 0))
+            else:
+                A = torch.empty((K, M), dtype=tdt, device="cuda").normal_()
+                Bm = torch.empty((K, N), dtype=tdt, device="cuda").normal_()
+                Cm = torch.empty((M, N), dtype=torch.float32, device="cuda")
+                bufs.append((M, N, K, A, M, 0, Bm, N, 0, Cm, N, None, 0, dt, B.F32, ws, ws.numel()))
 
-    def fn():
-        B.slt_gemm(M, N, K, x, K, 1, wptr, K, 1, y, N, None, 0, dt, dt)
+        def run(bufs=bufs):
+            for args in bufs:
+                B.slt_gemm(*args)
 
-    sec = time_launches(fn, reps, torch)
-    flops = 2.0 * M * N * K
-    peak = PEAK["bf16_tflops"] if dt == B.BF16 else PEAK["f32_tflops"]
-    ach = flops / sec / 1e12
-    return {"kernel": f"gemm_k NT {M}x{N}x{K} ([W1;W3] forward projection)", "bound": "mfma",
-            "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-            "traffic": None, "avg_launch_us": round(sec * 1e6, 2)}
+        sec = time_block(run, reps, torch)
+        flops = sum(2.0 * M * N * K for (M, N, K, _) in launches)
+        out[cls] = {"ms_per_step": sec * 1e3, "launches": len(launches), "tflops": flops / sec / 1e12,
+                    "frac_of_peak": flops / sec / 1e12 / peak, "flops": flops, "avg_launch_us": sec * 1e6 / len(launches),
+                    "bound": "mfma", "peak": peak}
+        del bufs
+    # attention: forward, and backward (dQ then dK/dV) on the step's strides
+    d = w.C // w.H
+    qd, kd = w.H * d, w.Hkv * d
+    ld = qd + 2 * kd + (w.F if w.block != "llama" else 0)
+    qkv = torch.empty((w.N, ld), dtype=tdt, device="cuda").normal_()
+    o = torch.empty((w.N, qd), dtype=tdt, device="cuda")
+    ores = torch.empty((w.N, qd), dtype=tdt, device="cuda") if dt == B.BF16 else None
+    lse = torch.empty((w.B, w.H, w.T), device="cuda")
+    cs = torch.empty((w.T, max(w.R, 2)), device="cuda")
+    B.slt_rope_table(w.T, w.R, w.base, cs)
+    g = torch.empty((w.N, qd), dtype=tdt, device="cuda").normal_()
+    dqkv = torch.empty_like(qkv)
+    aws = torch.empty(B.slt_attention_bwd_workspace(w.B, w.H, w.T), dtype=torch.uint8, device="cuda")
+    p, dp = qkv.data_ptr(), dqkv.data_ptr()
+    mode = B.ROPE_HALF if w.rope_mode == "half" else B.ROPE_PAIRS
+
+    def fwd():
+        for _ in range(w.L):
+            B.slt_attention_fwd(p, p + qd * es, p + (qd + kd) * es, o, lse, ores, ld, ld, ld, qd,
+                                w.B, w.T, w.H, w.Hkv, d, w.R, mode, cs, dt)
+
+    def bwd():
+        for _ in range(w.L):
+            B.slt_attention_bwd(p, p + qd * es, p + (qd + kd) * es, o, ores, g, lse, dp, dp + qd * es,
+                                dp + (qd + kd) * es, ld, ld, ld, qd, qd, ld, ld, ld, w.B, w.T, w.H, w.Hkv, d, w.R,
+                                mode, cs, dt, aws)
+
+    fa, ba = attn_flops(w)
+    for name, fn, fl, nl in [("attention_fwd", fwd, fa, w.L), ("attention_bwd", bwd, ba, 2 * w.L)]:
+        sec = time_block(fn, reps, torch)
+        out[name] = {"ms_per_step": sec * 1e3, "launches": nl, "tflops": fl / sec / 1e12,
+                     "frac_of_peak": fl / sec / 1e12 / peak, "flops": fl, "avg_launch_us": sec * 1e6 / nl,
+                     "bound": "mfma", "peak": peak}
+    return out
 
 
-def cpu_baseline(w, seconds_hint=20.0):
+def cpu_baseline(w):
     """The oracle (numpy float64) on a bounded sample of the same workload:
-    one full step (forward, backward, AdamW) on B_s sequences of the batch."""
-    import numpy as np
+    one full step (forward, backward, AdamW) on up to 64 of the batch's
+    sequences (all of them for the d=384 workload, about 10-30 s of CPU)."""
     import oracle as O
     import slt_workloads as W
     try:
@@ -90,7 +170,7 @@ def cpu_baseline(w, seconds_hint=20.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    Bs = 8
+    Bs = min(w.B, 64)
     ws = w.with_(B=Bs)
     params = W.make_params(ws, 1003)
     tokens = W.make_tokens(ws, 1003)
@@ -98,8 +178,8 @@ def cpu_baseline(w, seconds_hint=20.0):
     O.train_step(ws, params, tokens)
     dt = time.perf_counter() - t0
     return {"value": round(Bs * w.T / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full step (forward, backward, AdamW on all {W.n_params(ws)} parameters) "
-                      f"on {Bs} of the {w.B} sequences ({Bs * w.T} tokens), float64 numpy; {dt:.1f} s"}
+            "sample": f"one full step (forward, backward, AdamW on all {W.n_params(ws)} parameters) on {Bs} of "
+                      f"the {w.B} sequences ({Bs * w.T} tokens), float64 numpy; {dt:.1f} s"}
 
 
 def main():
@@ -108,8 +188,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index (3 = the headline shape)")
-    ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -140,10 +221,9 @@ def main():
     loss = float(ts.loss.item())
     tps = w.N / (ms / 1e3)
     flops = step_flops(w)
-    peak = PEAK["bf16_tflops"] if w.act == "bf16" else PEAK["f32_tflops"]
-    roof = dominant_kernel(w, ts, torch, args.kernel_reps)
+    peak = PEAK["bf16"] if w.act == "bf16" else PEAK["f32"]
     out = {
-        "metric": "train tokens/s (fwd+bwd+AdamW) d=384 8L T=256 B=64",
+        "metric": "train tokens/s (fwd+bwd+AdamW) d=384 8L T=256 B=64; MFMA util %, HBM GB/s",
         "value": round(tps, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -161,8 +241,19 @@ def main():
         "mfma_util_pct": round(100.0 * flops / (ms / 1e3) / 1e12 / peak, 2),
         "step_tflops": round(flops / (ms / 1e3) / 1e12, 2),
         "loss_after_steps": round(loss, 5),
-        "roofline": roof,
     }
+    del ts
+    torch.cuda.empty_cache()
+    if not args.no_breakdown:
+        cl = kernel_classes(w, None, torch, args.kernel_reps)
+        out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
+                              if kk in ("ms_per_step", "launches", "tflops", "frac_of_peak", "avg_launch_us")}
+                          for k, v in cl.items()}
+        dom = max(cl, key=lambda k: cl[k]["ms_per_step"])
+        c = cl[dom]
+        out["roofline"] = {"kernel": dom, "bound": c["bound"], "achieved": round(c["tflops"], 2),
+                           "peak": c["peak"], "unit": "TFLOP/s", "frac": round(c["tflops"] / c["peak"], 4),
+                           "traffic": None, "avg_launch_us": round(c["avg_launch_us"], 2)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -31,8 +31,8 @@ def flags() -> list[str]:
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str, obj: str) -> None:
-    cmd = [_hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj: str, defines=()) -> None:
+    cmd = [_hipcc(), *flags(), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -41,21 +41,23 @@ def _compile(src: str, obj: str) -> None:
         print(msg, file=sys.stderr)
 
 
-def build(verbose: bool = True) -> str:
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = True, defines=(), out: str = LIB) -> str:
+    """Compile every source and link ``out``.  ``defines`` are extra -D
+    macros (kernel tuning constants; the defaults are the tuned values)."""
+    objdir = os.path.join(HERE, "_build", "_".join(defines) if defines else "default")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        list(ex.map(_compile, SOURCES, objs))
-    tmp = LIB + ".tmp"
+        list(ex.map(lambda so: _compile(so[0], so[1], defines), zip(SOURCES, objs)))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -19,9 +19,21 @@
 //  * Split-K for small output grids (the weight gradients, whose K is the
 //    token count): partial tiles go to a fp32 workspace and a second kernel
 //    adds them in split order, so the result is deterministic.
+//  * XCD-aware tile order: workgroups are dispatched round-robin over the 8
+//    XCDs, each with its own L2, so workgroup i is given tile
+//    (i % 8) * (tiles / 8) + i / 8: every XCD works on a contiguous band of
+//    output rows and reads each A row-block into its L2 once.
 #include "slt_internal.h"
 
 #include <algorithm>
+
+// k-step depth as a multiple of one MFMA depth (32 bf16 / 16 fp32 elements)
+#ifndef SLT_GEMM_BKX
+#define SLT_GEMM_BKX 2
+#endif
+#ifndef SLT_GEMM_XCD
+#define SLT_GEMM_XCD 1
+#endif
 
 namespace slt {
 namespace {
@@ -32,10 +44,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 128, BN = 128, NT = 256;
 
 template <typename T> struct Tr;
-template <> struct Tr<bf16> { static constexpr int BK = 32, EPV = 8, KV = 4; };
-template <> struct Tr<float> { static constexpr int BK = 16, EPV = 4, KV = 2; };
+template <> struct Tr<bf16> { static constexpr int EPV = 8, BK = 32 * SLT_GEMM_BKX, KV = BK / 8; };
+template <> struct Tr<float> { static constexpr int EPV = 4, BK = 16 * SLT_GEMM_BKX, KV = BK / 8; };
 
-template <typename T> constexpr int kStride = Tr<T>::BK + Tr<T>::EPV;  // padded LDS row (80 bytes)
+// MFMA depth steps per k-step; padded LDS row (one extra 16-byte group)
+template <typename T> constexpr int kSub = Tr<T>::BK / (4 * Tr<T>::EPV);
+template <typename T> constexpr int kStride = Tr<T>::BK + Tr<T>::EPV;
 
 template <typename T, int N>
 struct alignas(sizeof(T) * N) Pk {
@@ -65,14 +79,24 @@ template <typename T, bool KMAJOR> struct Stage;
 
 template <typename T> struct Stage<T, true> {
   static constexpr int EPV = Tr<T>::EPV;
-  Pk<T, EPV> r[2];
+  static constexpr int VPR = Tr<T>::BK / EPV;      // 16-byte vectors per tile row
+  static constexpr int NV = BM * VPR / NT;         // vectors per thread
+  Pk<T, EPV> r[NV];
   template <bool VEC>
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows, int K, int row0, int k0, int tid) {
+    if (VEC && row0 + BM <= rows && k0 + Tr<T>::BK <= K) {  // whole tile inside: no bounds checks
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
+      for (int v = 0; v < NV; ++v) {
+        const int idx = tid + v * NT;
+        r[v] = *reinterpret_cast<const Pk<T, EPV>*>(g + (int64_t)(row0 + idx / VPR) * ld + k0 + (idx % VPR) * EPV);
+      }
+      return;
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
       const int idx = tid + v * NT;
-      const int row = row0 + (idx >> 2);
-      const int k = k0 + (idx & 3) * EPV;
+      const int row = row0 + idx / VPR;
+      const int k = k0 + (idx % VPR) * EPV;
       if (VEC) {
         if (row < rows && k < K) {
           r[v] = *reinterpret_cast<const Pk<T, EPV>*>(g + (int64_t)row * ld + k);
@@ -89,9 +113,9 @@ template <typename T> struct Stage<T, true> {
   }
   __device__ __forceinline__ void store(T* s, int tid) const {
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
+    for (int v = 0; v < NV; ++v) {
       const int idx = tid + v * NT;
-      *reinterpret_cast<Pk<T, EPV>*>(s + (idx >> 2) * kStride<T> + (idx & 3) * EPV) = r[v];
+      *reinterpret_cast<Pk<T, EPV>*>(s + (idx / VPR) * kStride<T> + (idx % VPR) * EPV) = r[v];
     }
   }
 };
@@ -103,6 +127,11 @@ template <typename T> struct Stage<T, false> {
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows, int K, int row0, int k0, int tid) {
     const int mn = row0 + 4 * (tid >> 3);
     const int kg = k0 + (tid & 7) * KV;
+    if (VEC && row0 + BM <= rows && k0 + Tr<T>::BK <= K) {  // whole tile inside: no bounds checks
+#pragma unroll
+      for (int kk = 0; kk < KV; ++kk) r[kk] = *reinterpret_cast<const Pk<T, 4>*>(g + (int64_t)(kg + kk) * ld + mn);
+      return;
+    }
 #pragma unroll
     for (int kk = 0; kk < KV; ++kk) {
       const int k = kg + kk;
@@ -141,7 +170,7 @@ struct KArgs {
   const void* R; int64_t ldr;
   float* ws;          // split-K partials [splits][M][N]
   int kchunk;         // k range per split (multiple of BK)
-  int tiles_n;
+  int tiles_n, tiles;
   bool evec;          // 4-wide epilogue stores allowed
 };
 
@@ -169,7 +198,12 @@ __global__ __launch_bounds__(NT) void gemm_k(KArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
+  int tile = blockIdx.x;
+  if (SLT_GEMM_XCD) {
+    const int q = a.tiles >> 3, r = a.tiles & 7, x = tile & 7;
+    tile = x * q + min(x, r) + (tile >> 3);
+  }
+  const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = SPLIT ? blockIdx.z * a.kchunk : 0;
   const int kend = SPLIT ? min(a.K, kbeg + a.kchunk) : a.K;
@@ -202,17 +236,21 @@ __global__ __launch_bounds__(NT) void gemm_k(KArgs a) {
       sa.template load<VEC>(A, a.lda, a.M, a.K, m0, k, tid);
       sb.template load<VEC>(B, a.ldb, a.N, a.K, n0, k, tid);
     }
-    uint4 af[4], bfr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const uint4*>(&As[cur][(wm * 64 + i * 16 + (lane & 15)) * STR + (lane >> 4) * EPV]);
+    for (int ks = 0; ks < kSub<T>; ++ks) {
+      uint4 af[4], bfr[4];
+      const int ko = ks * 4 * EPV + (lane >> 4) * EPV;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bfr[j] = *reinterpret_cast<const uint4*>(&Bs[cur][(wn * 64 + j * 16 + (lane & 15)) * STR + (lane >> 4) * EPV]);
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const uint4*>(&As[cur][(wm * 64 + i * 16 + (lane & 15)) * STR + ko]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const uint4*>(&Bs[cur][(wn * 64 + j * 16 + (lane & 15)) * STR + ko]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma(bfr[j], af[i], acc[i][j], T{});
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma(bfr[j], af[i], acc[i][j], T{});
+    }
     if (more) {
       sa.store(As[cur ^ 1], tid);
       sb.store(Bs[cur ^ 1], tid);
@@ -275,6 +313,171 @@ __global__ __launch_bounds__(256) void splitk_reduce_k(const float* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant for bf16 operands that are both k-major (C = A B^T):
+// tiles are copied from HBM/L2 into LDS by global_load_lds_dwordx4 (lane i of
+// an instruction lands at LDS base + 16 i), so no registers stage them; three
+// LDS stages keep two k-steps of loads in flight while one is multiplied,
+// which the register-staged kernel cannot afford without losing occupancy.
+// LDS tile: 128 rows x 4 chunks of 16 bytes (32 bf16); the chunk position is
+// XOR-swizzled with (row >> 2) & 3 so that the 16 rows one MFMA fragment read
+// touches fall in distinct banks.  Rows past M (N) are read from the last
+// valid row: they only feed output rows (columns) that are never stored.
+// ---------------------------------------------------------------------------
+constexpr int DL_BK = 32;
+constexpr int DL_S = 3;
+constexpr int DL_TILE = BM * DL_BK;  // elements per operand tile
+
+__device__ __forceinline__ int dl_swz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
+                                         int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = (wave * 2 + i) * 64 + lane;  // 16-byte chunk index in the tile
+    const int r = p >> 2;
+    const int lc = (p & 3) ^ dl_swz(r);
+    const int row = min(row0 + r, rows - 1);
+    const bf16* src = g + (int64_t)row * ld + k0 + lc * 8;
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                     (void __attribute__((address_space(3)))*)(tile + (wave * 2 + i) * 512), 16,
+                                     0, 0);
+  }
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte offset of a pointer into a __shared__ array: the generic address
+// is the LDS aperture (upper 32 bits) plus the offset.
+__device__ __forceinline__ unsigned lds_off(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
+}
+
+// The 4 A and 4 B fragments of one k-step (rows 16 apart = 1 KiB apart).
+// Written as one asm block that also waits for its own reads: the compiler
+// cannot tell which LDS stage a global_load_lds copy targets and would
+// otherwise wait for every copy in flight before any LDS read.
+__device__ __forceinline__ void dl_read(unsigned a_addr, unsigned b_addr, u32x4 (&af)[4], u32x4 (&bf)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %9\n\t"
+      "ds_read_b128 %5, %9 offset:1024\n\t"
+      "ds_read_b128 %6, %9 offset:2048\n\t"
+      "ds_read_b128 %7, %9 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]),
+        "=&v"(bf[3])
+      : "v"(a_addr), "v"(b_addr)
+      : "memory");
+}
+
+// Workgroup barrier that orders LDS accesses only: global_load_lds writes
+// are waited for explicitly (vmcnt) by each wave before it arrives.
+__device__ __forceinline__ void dl_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One k-step: wait for this wave's part of tile `it`, barrier, read the
+// current stage, refill the stage freed in step it-1 with tile it+2, multiply.
+__device__ __forceinline__ void dl_step(const KArgs& a, const bf16* A, const bf16* B, int m0, int n0, int nk, int it,
+                                        const bf16* As, const bf16* Bs, bf16* An, bf16* Bn, int wave, int lane,
+                                        f32x4 (&acc)[4][4]) {
+  __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt(4): only the 4 loads of tile it+1 may still fly
+  dl_barrier();
+  const int wm = wave >> 1, wn = wave & 1;
+  const int frow = lane & 15, fch = lane >> 4;
+  // fragment i (j) of this wave starts 16 rows after fragment i-1, and the
+  // swizzle depends on (row >> 2) & 3 only, so it is one address + 1 KiB steps
+  const int ra = wm * 64 + frow, rb = wn * 64 + frow;
+  u32x4 af[4], bfr[4];
+  dl_read(lds_off(As) + (ra * 4 + (fch ^ dl_swz(ra))) * 16, lds_off(Bs) + (rb * 4 + (fch ^ dl_swz(rb))) * 16, af, bfr);
+  // past the end the last tile is copied again into the free stage, which
+  // keeps exactly 4 copies in flight per step; that stage is never read
+  const int kn = min(it + 2, nk - 1) * DL_BK;
+  dl_issue(A, a.lda, a.M, m0, kn, An, wave, lane);
+  dl_issue(B, a.ldb, a.N, n0, kn, Bn, wave, lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[j]),
+                                                          __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
+}
+
+template <typename TO>
+__global__ __launch_bounds__(NT) void gemm_dl_k(KArgs a) {
+  // three stages as distinct LDS objects, so that reads of one stage need not
+  // wait for copies still landing in another
+  __shared__ __attribute__((aligned(16))) bf16 A0[DL_TILE], A1[DL_TILE], A2[DL_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 B0[DL_TILE], B1[DL_TILE], B2[DL_TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tile = blockIdx.x;
+  if (SLT_GEMM_XCD) {
+    const int q = a.tiles >> 3, r = a.tiles & 7, x = tile & 7;
+    tile = x * q + min(x, r) + (tile >> 3);
+  }
+  const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = a.K / DL_BK;
+  const bf16* A = static_cast<const bf16*>(a.A);
+  const bf16* B = static_cast<const bf16*>(a.B);
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  dl_issue(A, a.lda, a.M, m0, 0, A0, wave, lane);
+  dl_issue(B, a.ldb, a.N, n0, 0, B0, wave, lane);
+  dl_issue(A, a.lda, a.M, m0, min(1, nk - 1) * DL_BK, A1, wave, lane);
+  dl_issue(B, a.ldb, a.N, n0, min(1, nk - 1) * DL_BK, B1, wave, lane);
+  for (int it = 0; it < nk; it += 3) {
+    dl_step(a, A, B, m0, n0, nk, it, A0, B0, A2, B2, wave, lane, acc);
+    if (it + 1 < nk) dl_step(a, A, B, m0, n0, nk, it + 1, A1, B1, A0, B0, wave, lane, acc);
+    if (it + 2 < nk) dl_step(a, A, B, m0, n0, nk, it + 2, A2, B2, A1, B1, wave, lane, acc);
+  }
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): no copy may land after the block ends
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 64 + i * 16 + (lane & 15);
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+      if (n >= a.N) continue;
+      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      TO* dst = static_cast<TO*>(a.C) + (int64_t)m * a.ldc + n;
+      const TO* res = a.R ? static_cast<const TO*>(a.R) + (int64_t)m * a.ldr + n : nullptr;
+      if (a.evec && n + 3 < a.N) {
+        if (res) {
+          float rv[4];
+          load4<TO>(res, rv);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] += rv[r];
+        }
+        store4<TO>(dst, v);
+      } else {
+        for (int r = 0; r < 4 && n + r < a.N; ++r) {
+          float x = v[r];
+          if (res) x += to_f32(res[r]);
+          dst[r] = from_f32<TO>(x);
+        }
+      }
+    }
+  }
+}
+
 inline bool al(const void* p, int b) { return (reinterpret_cast<uintptr_t>(p) % b) == 0; }
 
 template <typename T, typename TO, bool AK, bool BKM, bool VEC, bool SPLIT>
@@ -292,6 +495,7 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   ka.tiles_n = tiles_n;
   const int tiles = tiles_m * tiles_n;
+  ka.tiles = tiles;
 
   // Vector loads need every vector wholly inside or outside the operand.
   auto op_ok = [&](const void* p, int64_t ld, bool kmajor, int rows) {
@@ -299,6 +503,18 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
     return rows % 4 == 0 && ld % 4 == 0 && al(p, 4 * (int)sizeof(T));
   };
   const bool vec = op_ok(g.A, g.lda, g.a_kmajor, g.M) && op_ok(g.B, g.ldb, g.b_kmajor, g.N);
+
+  // Direct-to-LDS path: bf16, both operands k-major, K a multiple of 32,
+  // 16-byte aligned rows, and enough tiles to fill the chip without split-K.
+  if constexpr (sizeof(T) == 2) {
+    if (g.a_kmajor && g.b_kmajor && g.K > 0 && g.K % DL_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+        al(g.A, 16) && al(g.B, 16) && (tiles >= 256 || g.workspace == nullptr)) {
+      ka.evec = g.N % 4 == 0 && g.ldc % 4 == 0 && al(g.C, 4 * (int)sizeof(TO)) &&
+                (g.R == nullptr || (g.ldr % 4 == 0 && al(g.R, 4 * (int)sizeof(TO))));
+      gemm_dl_k<TO><<<tiles, NT, 0, s>>>(ka);
+      return check_launch("gemm");
+    }
+  }
 
   // Split K when the output grid cannot fill the 256 compute units and K is
   // long; the partials must fit the workspace.
