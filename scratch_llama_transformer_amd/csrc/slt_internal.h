@@ -18,14 +18,17 @@ struct bf16 {
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(((uint32_t)x.u) << 16); }
 
-// Round to nearest, ties to even, from the binary32 bit pattern: add half an
-// ulp of the 16-bit result (0x7fff) plus the result's lowest bit so that exact
-// halves move to the even neighbour; NaNs stay quiet NaNs.
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32 (what clang
+// emits for a float -> __bf16 conversion) rounds in the IEEE default mode,
+// keeps binary32 subnormals (the default f32 denormal mode preserves them)
+// and turns NaNs into quiet NaNs.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two values in one conversion: a in the low half, b in the high half.
+typedef __bf16 slt_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float slt_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(slt_f32x2{a, b}, slt_bf16x2));
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);

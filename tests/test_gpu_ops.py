@@ -386,6 +386,14 @@ def test_adamw_flat(B, n):
 def test_cast_bf16_matches_oracle_rounding(B):
     rng = np.random.default_rng(12)
     x = (rng.standard_normal(100003) * 10.0 ** rng.integers(-30, 30, 100003)).astype(np.float32)
+    # random bit patterns (NaNs dropped), subnormals, exact ties either side
+    # of even, values that round up to the next binade or to infinity
+    bits = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0x00000001, 0x00007fff, 0x00008000, 0x00018000, 0x007fffff, 0x00800000, 0x3f808000,
+                        0x3f818000, 0x3f80ffff, 0x3fffffff, 0x7f7f7fff, 0x7f7f8000, 0x7f7fffff, 0x7f800000,
+                        0x80000000, 0x80008000, 0xff7fffff, 0xff800000, 0], dtype=np.uint32)
+    more = np.concatenate([bits, special]).view(np.float32)
+    x = np.concatenate([x, more[np.isfinite(more) | np.isinf(more)]])
     d = torch.empty(x.size, dtype=torch.int16, device="cuda")
     B.slt_cast_bf16(torch.from_numpy(x).cuda(), d, x.size)
     np.testing.assert_array_equal(host(d.view(torch.bfloat16)), O.bf16_round(x.astype(np.float64)))
