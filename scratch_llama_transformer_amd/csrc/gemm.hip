@@ -314,38 +314,34 @@ __global__ __launch_bounds__(256) void splitk_reduce_k(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant for bf16 operands that are both k-major (C = A B^T):
-// tiles are copied from HBM/L2 into LDS by global_load_lds_dwordx4 (lane i of
-// an instruction lands at LDS base + 16 i), so no registers stage them; three
-// LDS stages keep two k-steps of loads in flight while one is multiplied,
-// which the register-staged kernel cannot afford without losing occupancy.
-// LDS tile: 128 rows x 4 chunks of 16 bytes (32 bf16); the chunk position is
-// XOR-swizzled with (row >> 2) & 3 so that the 16 rows one MFMA fragment read
-// touches fall in distinct banks.  Rows past M (N) are read from the last
-// valid row: they only feed output rows (columns) that are never stored.
+// Direct-to-LDS kernel for bf16 operands in any layout.  Operand tiles are
+// copied HBM/L2 -> LDS by global_load_lds_dwordx4 (lane i of an instruction
+// lands at LDS base + 16 i, so the LDS layout is fixed by which global chunk
+// each lane fetches); no registers stage them, and three LDS stages keep two
+// k-steps of copies in flight while one is multiplied.
+//
+// k-major operand (rows of K contiguous): LDS tile of 128 rows x 4 chunks of
+// 16 bytes (32 k), chunk position XOR (row >> 2) & 3; a fragment is one
+// ds_read_b128 per lane (row l%16, k 8(l/16)..+7).
+// m/n-major operand (rows of M or N contiguous): LDS tile of 32 k-rows x 16
+// chunks (8 m each), chunk position XOR f(k-row); a fragment is two
+// ds_read_b64_tr_b16.  That instruction hands lane 16g+i element j of the
+// 8-byte row supplied by lane 16g+4j+i/4, at position i%4; so lane 16g+4j+q
+// supplies (k = 8g+j, m = 4q..4q+3) and receives k = 8g..8g+3 at its own m,
+// the MFMA operand layout (the second read covers k + 4).  The rows one read
+// touches are k = 8g+j (+4); f spreads the chunk pairs of those rows over the
+// banks.
+// Rows (columns) past M (N) are read from a valid row: they only feed outputs
+// that are never stored.
 // ---------------------------------------------------------------------------
 constexpr int DL_BK = 32;
-constexpr int DL_S = 3;
-constexpr int DL_TILE = BM * DL_BK;  // elements per operand tile
-
-__device__ __forceinline__ int dl_swz(int r) { return (r >> 2) & 3; }
-
-__device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
-                                         int lane) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = (wave * 2 + i) * 64 + lane;  // 16-byte chunk index in the tile
-    const int r = p >> 2;
-    const int lc = (p & 3) ^ dl_swz(r);
-    const int row = min(row0 + r, rows - 1);
-    const bf16* src = g + (int64_t)row * ld + k0 + lc * 8;
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                     (void __attribute__((address_space(3)))*)(tile + (wave * 2 + i) * 512), 16,
-                                     0, 0);
-  }
-}
+constexpr int DL_TILE = BM * DL_BK;  // elements per operand tile (8 KiB)
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int dl_swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int dl_swz_mn(int kr) { return 2 * ((kr & 3) | (((kr >> 3) & 1) << 2)); }
 
 // LDS byte offset of a pointer into a __shared__ array: the generic address
 // is the LDS aperture (upper 32 bits) plus the offset.
@@ -353,26 +349,122 @@ __device__ __forceinline__ unsigned lds_off(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
 }
 
-// The 4 A and 4 B fragments of one k-step (rows 16 apart = 1 KiB apart).
-// Written as one asm block that also waits for its own reads: the compiler
-// cannot tell which LDS stage a global_load_lds copy targets and would
-// otherwise wait for every copy in flight before any LDS read.
-__device__ __forceinline__ void dl_read(unsigned a_addr, unsigned b_addr, u32x4 (&af)[4], u32x4 (&bf)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:1024\n\t"
-      "ds_read_b128 %2, %8 offset:2048\n\t"
-      "ds_read_b128 %3, %8 offset:3072\n\t"
-      "ds_read_b128 %4, %9\n\t"
-      "ds_read_b128 %5, %9 offset:1024\n\t"
-      "ds_read_b128 %6, %9 offset:2048\n\t"
-      "ds_read_b128 %7, %9 offset:3072\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]),
-        "=&v"(bf[3])
-      : "v"(a_addr), "v"(b_addr)
-      : "memory");
+__device__ __forceinline__ void dl_copy(const bf16* src, bf16* dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
 }
+
+// Copy the 128 x 32 tile at (row0, k0) of an operand into `tile`: 2 copies per
+// wave (512 chunks of 16 bytes over 4 waves).
+template <bool KM>
+__device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
+                                         int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = (wave * 2 + i) * 64 + lane;  // 16-byte chunk position in the tile
+    const bf16* src;
+    if constexpr (KM) {
+      const int r = p >> 2;
+      const int lc = (p & 3) ^ dl_swz(r);
+      src = g + (int64_t)min(row0 + r, rows - 1) * ld + k0 + lc * 8;
+    } else {
+      const int kr = p >> 4;
+      const int c = (p & 15) ^ dl_swz_mn(kr);
+      src = g + (int64_t)(k0 + kr) * ld + min(row0 + c * 8, rows - 8);
+    }
+    dl_copy(src, tile + (wave * 2 + i) * 512);
+  }
+}
+
+// Per-lane LDS byte addresses of this wave's fragments within a tile (w0 =
+// first row or column of the wave's 64): k-major: one address, fragments at
+// +1 KiB steps; m/n-major: four addresses (one per fragment), the second
+// read of each at +1 KiB (4 k-rows of 256 bytes further).
+template <bool KM> struct DlAddr;
+template <> struct DlAddr<true> {
+  unsigned a;
+  __device__ __forceinline__ DlAddr(int w0, int lane) {
+    const int r = w0 + (lane & 15);
+    a = (r * 4 + ((lane >> 4) ^ dl_swz(r))) * 16;
+  }
+  __device__ __forceinline__ DlAddr<true> at(unsigned base) const { DlAddr<true> x = *this; x.a += base; return x; }
+};
+template <> struct DlAddr<false> {
+  unsigned a[4];
+  __device__ __forceinline__ DlAddr(int w0, int lane) {
+    const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+    const int kr = 8 * g + j;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = (w0 + 16 * i) / 8 + (q >> 1);
+      a[i] = (kr * 16 + (c ^ dl_swz_mn(kr))) * 16 + (q & 1) * 8;
+    }
+  }
+  __device__ __forceinline__ DlAddr<false> at(unsigned base) const {
+    DlAddr<false> x = *this;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.a[i] += base;
+    return x;
+  }
+};
+
+#define DL_KM(X)                                       \
+  "ds_read_b128 %[" #X "0], %[" #X "a]\n\t"            \
+  "ds_read_b128 %[" #X "1], %[" #X "a] offset:1024\n\t" \
+  "ds_read_b128 %[" #X "2], %[" #X "a] offset:2048\n\t" \
+  "ds_read_b128 %[" #X "3], %[" #X "a] offset:3072\n\t"
+#define DL_MN(X)                                                     \
+  "ds_read_b64_tr_b16 %[" #X "0l], %[" #X "a0]\n\t"                  \
+  "ds_read_b64_tr_b16 %[" #X "0h], %[" #X "a0] offset:1024\n\t"      \
+  "ds_read_b64_tr_b16 %[" #X "1l], %[" #X "a1]\n\t"                  \
+  "ds_read_b64_tr_b16 %[" #X "1h], %[" #X "a1] offset:1024\n\t"      \
+  "ds_read_b64_tr_b16 %[" #X "2l], %[" #X "a2]\n\t"                  \
+  "ds_read_b64_tr_b16 %[" #X "2h], %[" #X "a2] offset:1024\n\t"      \
+  "ds_read_b64_tr_b16 %[" #X "3l], %[" #X "a3]\n\t"                  \
+  "ds_read_b64_tr_b16 %[" #X "3h], %[" #X "a3] offset:1024\n\t"
+#define DL_OUT_KM(X, f) [X##0] "=&v"(f[0]), [X##1] "=&v"(f[1]), [X##2] "=&v"(f[2]), [X##3] "=&v"(f[3])
+#define DL_OUT_MN(X, l, h)                                                                                   \
+  [X##0l] "=&v"(l[0]), [X##0h] "=&v"(h[0]), [X##1l] "=&v"(l[1]), [X##1h] "=&v"(h[1]), [X##2l] "=&v"(l[2]), \
+      [X##2h] "=&v"(h[2]), [X##3l] "=&v"(l[3]), [X##3h] "=&v"(h[3])
+#define DL_IN_KM(X, d) [X##a] "v"(d.a)
+#define DL_IN_MN(X, d) [X##a0] "v"(d.a[0]), [X##a1] "v"(d.a[1]), [X##a2] "v"(d.a[2]), [X##a3] "v"(d.a[3])
+
+// The 4 A and 4 B fragments of one k-step, as one asm block that also waits
+// for its own reads: the compiler cannot tell which LDS stage a
+// global_load_lds copy targets and would otherwise wait for every copy in
+// flight before any LDS read.
+template <bool AK, bool BK>
+__device__ __forceinline__ void dl_read(const DlAddr<AK>& da, const DlAddr<BK>& db, u32x4 (&af)[4],
+                                        u32x4 (&bf)[4]) {
+  u32x2 al[4], ah[4], bl[4], bh[4];
+  if constexpr (AK && BK) {
+    asm volatile(DL_KM(a) DL_KM(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_KM(a, af), DL_OUT_KM(b, bf) : DL_IN_KM(a, da), DL_IN_KM(b, db) : "memory");
+  } else if constexpr (AK && !BK) {
+    asm volatile(DL_KM(a) DL_MN(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_KM(a, af), DL_OUT_MN(b, bl, bh) : DL_IN_KM(a, da), DL_IN_MN(b, db) : "memory");
+  } else if constexpr (!AK && BK) {
+    asm volatile(DL_MN(a) DL_KM(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_MN(a, al, ah), DL_OUT_KM(b, bf) : DL_IN_MN(a, da), DL_IN_KM(b, db) : "memory");
+  } else {
+    asm volatile(DL_MN(a) DL_MN(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_MN(a, al, ah), DL_OUT_MN(b, bl, bh) : DL_IN_MN(a, da), DL_IN_MN(b, db) : "memory");
+  }
+  if constexpr (!AK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = u32x4{al[i][0], al[i][1], ah[i][0], ah[i][1]};
+  }
+  if constexpr (!BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bf[i] = u32x4{bl[i][0], bl[i][1], bh[i][0], bh[i][1]};
+  }
+}
+#undef DL_KM
+#undef DL_MN
+#undef DL_OUT_KM
+#undef DL_OUT_MN
+#undef DL_IN_KM
+#undef DL_IN_MN
 
 // Workgroup barrier that orders LDS accesses only: global_load_lds writes
 // are waited for explicitly (vmcnt) by each wave before it arrives.
@@ -383,25 +475,27 @@ __device__ __forceinline__ void dl_barrier() {
   asm volatile("" ::: "memory");
 }
 
+struct DlCtx {
+  const bf16* A;
+  const bf16* B;
+  int64_t lda, ldb;
+  int M, N, m0, n0, kbeg, nk, wave, lane;
+};
+
 // One k-step: wait for this wave's part of tile `it`, barrier, read the
-// current stage, refill the stage freed in step it-1 with tile it+2, multiply.
-__device__ __forceinline__ void dl_step(const KArgs& a, const bf16* A, const bf16* B, int m0, int n0, int nk, int it,
-                                        const bf16* As, const bf16* Bs, bf16* An, bf16* Bn, int wave, int lane,
-                                        f32x4 (&acc)[4][4]) {
-  __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt(4): only the 4 loads of tile it+1 may still fly
+// current stage, refill the stage freed in step it-1 with tile it+2 (past the
+// end: the last tile again, into a stage nobody reads, so that exactly 4
+// copies per wave are in flight at every wait), multiply.
+template <bool AK, bool BK>
+__device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK>& da, const DlAddr<BK>& db,
+                                        unsigned as, unsigned bs, bf16* An, bf16* Bn, f32x4 (&acc)[4][4]) {
+  __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt(4): only the 4 copies of tile it+1 may still fly
   dl_barrier();
-  const int wm = wave >> 1, wn = wave & 1;
-  const int frow = lane & 15, fch = lane >> 4;
-  // fragment i (j) of this wave starts 16 rows after fragment i-1, and the
-  // swizzle depends on (row >> 2) & 3 only, so it is one address + 1 KiB steps
-  const int ra = wm * 64 + frow, rb = wn * 64 + frow;
   u32x4 af[4], bfr[4];
-  dl_read(lds_off(As) + (ra * 4 + (fch ^ dl_swz(ra))) * 16, lds_off(Bs) + (rb * 4 + (fch ^ dl_swz(rb))) * 16, af, bfr);
-  // past the end the last tile is copied again into the free stage, which
-  // keeps exactly 4 copies in flight per step; that stage is never read
-  const int kn = min(it + 2, nk - 1) * DL_BK;
-  dl_issue(A, a.lda, a.M, m0, kn, An, wave, lane);
-  dl_issue(B, a.ldb, a.N, n0, kn, Bn, wave, lane);
+  dl_read<AK, BK>(da.at(as), db.at(bs), af, bfr);
+  const int kn = c.kbeg + min(it + 2, c.nk - 1) * DL_BK;
+  dl_issue<AK>(c.A, c.lda, c.M, c.m0, kn, An, c.wave, c.lane);
+  dl_issue<BK>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -410,10 +504,9 @@ __device__ __forceinline__ void dl_step(const KArgs& a, const bf16* A, const bf1
                                                           __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
 }
 
-template <typename TO>
+template <typename TO, bool AK, bool BK, bool SPLIT>
 __global__ __launch_bounds__(NT) void gemm_dl_k(KArgs a) {
-  // three stages as distinct LDS objects, so that reads of one stage need not
-  // wait for copies still landing in another
+  // three stages as distinct LDS objects
   __shared__ __attribute__((aligned(16))) bf16 A0[DL_TILE], A1[DL_TILE], A2[DL_TILE];
   __shared__ __attribute__((aligned(16))) bf16 B0[DL_TILE], B1[DL_TILE], B2[DL_TILE];
 
@@ -426,10 +519,21 @@ __global__ __launch_bounds__(NT) void gemm_dl_k(KArgs a) {
     tile = x * q + min(x, r) + (tile >> 3);
   }
   const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = a.K / DL_BK;
-  const bf16* A = static_cast<const bf16*>(a.A);
-  const bf16* B = static_cast<const bf16*>(a.B);
+  DlCtx c;
+  c.A = static_cast<const bf16*>(a.A);
+  c.B = static_cast<const bf16*>(a.B);
+  c.lda = a.lda;
+  c.ldb = a.ldb;
+  c.M = a.M;
+  c.N = a.N;
+  c.m0 = tm * BM;
+  c.n0 = tn * BN;
+  c.kbeg = SPLIT ? blockIdx.z * a.kchunk : 0;
+  c.nk = (min(a.K, c.kbeg + a.kchunk) - c.kbeg) / DL_BK;
+  c.wave = wave;
+  c.lane = lane;
+  const DlAddr<AK> da(wm * 64, lane);
+  const DlAddr<BK> db(wn * 64, lane);
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -437,17 +541,20 @@ __global__ __launch_bounds__(NT) void gemm_dl_k(KArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  dl_issue(A, a.lda, a.M, m0, 0, A0, wave, lane);
-  dl_issue(B, a.ldb, a.N, n0, 0, B0, wave, lane);
-  dl_issue(A, a.lda, a.M, m0, min(1, nk - 1) * DL_BK, A1, wave, lane);
-  dl_issue(B, a.ldb, a.N, n0, min(1, nk - 1) * DL_BK, B1, wave, lane);
-  for (int it = 0; it < nk; it += 3) {
-    dl_step(a, A, B, m0, n0, nk, it, A0, B0, A2, B2, wave, lane, acc);
-    if (it + 1 < nk) dl_step(a, A, B, m0, n0, nk, it + 1, A1, B1, A0, B0, wave, lane, acc);
-    if (it + 2 < nk) dl_step(a, A, B, m0, n0, nk, it + 2, A2, B2, A1, B1, wave, lane, acc);
+  dl_issue<AK>(c.A, c.lda, c.M, c.m0, c.kbeg, A0, wave, lane);
+  dl_issue<BK>(c.B, c.ldb, c.N, c.n0, c.kbeg, B0, wave, lane);
+  dl_issue<AK>(c.A, c.lda, c.M, c.m0, c.kbeg + min(1, c.nk - 1) * DL_BK, A1, wave, lane);
+  dl_issue<BK>(c.B, c.ldb, c.N, c.n0, c.kbeg + min(1, c.nk - 1) * DL_BK, B1, wave, lane);
+  const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
+  const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
+  for (int it = 0; it < c.nk; it += 3) {
+    dl_step<AK, BK>(c, it, da, db, a0, b0, A2, B2, acc);
+    if (it + 1 < c.nk) dl_step<AK, BK>(c, it + 1, da, db, a1, b1, A0, B0, acc);
+    if (it + 2 < c.nk) dl_step<AK, BK>(c, it + 2, da, db, a2, b2, A1, B1, acc);
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): no copy may land after the block ends
 
+  const int m0 = c.m0, n0 = c.n0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + wm * 64 + i * 16 + (lane & 15);
@@ -457,6 +564,15 @@ __global__ __launch_bounds__(NT) void gemm_dl_k(KArgs a) {
       const int n = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
       if (n >= a.N) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      if (SPLIT) {
+        float* dst = a.ws + ((int64_t)blockIdx.z * a.M + m) * a.N + n;
+        if (a.evec && n + 3 < a.N) {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          for (int r = 0; r < 4 && n + r < a.N; ++r) dst[r] = v[r];
+        }
+        continue;
+      }
       TO* dst = static_cast<TO*>(a.C) + (int64_t)m * a.ldc + n;
       const TO* res = a.R ? static_cast<const TO*>(a.R) + (int64_t)m * a.ldr + n : nullptr;
       if (a.evec && n + 3 < a.N) {
@@ -485,6 +601,19 @@ void launch_one(const KArgs& ka, dim3 grid, hipStream_t s) {
   gemm_k<T, TO, AK, BKM, VEC, SPLIT><<<grid, NT, 0, s>>>(ka);
 }
 
+// After the main kernel: the fixed-order sum of split-K partials, if any.
+template <typename TO>
+slt_status finish(const GemmArgs& g, bool split, int splits, hipStream_t s) {
+  if (slt_status st = check_launch("gemm"); st != SLT_OK) return st;
+  if (split) {
+    const int64_t total = (int64_t)g.M * g.N;
+    int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
+    splitk_reduce_k<TO><<<blocks, 256, 0, s>>>(g.workspace, splits, g.M, g.N, static_cast<TO*>(g.C), g.ldc,
+                                               static_cast<const TO*>(g.R), g.ldr);
+  }
+  return check_launch("gemm split-K reduction");
+}
+
 template <typename T, typename TO>
 slt_status run(const GemmArgs& g, hipStream_t s) {
   constexpr int BK = Tr<T>::BK, EPV = Tr<T>::EPV;
@@ -503,18 +632,6 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
     return rows % 4 == 0 && ld % 4 == 0 && al(p, 4 * (int)sizeof(T));
   };
   const bool vec = op_ok(g.A, g.lda, g.a_kmajor, g.M) && op_ok(g.B, g.ldb, g.b_kmajor, g.N);
-
-  // Direct-to-LDS path: bf16, both operands k-major, K a multiple of 32,
-  // 16-byte aligned rows, and enough tiles to fill the chip without split-K.
-  if constexpr (sizeof(T) == 2) {
-    if (g.a_kmajor && g.b_kmajor && g.K > 0 && g.K % DL_BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
-        al(g.A, 16) && al(g.B, 16) && (tiles >= 256 || g.workspace == nullptr)) {
-      ka.evec = g.N % 4 == 0 && g.ldc % 4 == 0 && al(g.C, 4 * (int)sizeof(TO)) &&
-                (g.R == nullptr || (g.ldr % 4 == 0 && al(g.R, 4 * (int)sizeof(TO))));
-      gemm_dl_k<TO><<<tiles, NT, 0, s>>>(ka);
-      return check_launch("gemm");
-    }
-  }
 
   // Split K when the output grid cannot fill the 256 compute units and K is
   // long; the partials must fit the workspace.
@@ -541,6 +658,29 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
   }
   dim3 grid(tiles, 1, split ? splits : 1);
 
+  // Direct-to-LDS path (bf16): K a multiple of 32 (and of each split's
+  // range), 16-byte aligned rows, m/n-major operands at least 8 wide in
+  // whole 16-byte chunks.
+  if constexpr (sizeof(T) == 2) {
+    auto dl_ok = [&](const void* p, int64_t ld, bool kmajor, int rows) {
+      return al(p, 16) && ld % 8 == 0 && (kmajor || (rows % 8 == 0 && rows >= 8));
+    };
+    if (g.K > 0 && g.K % DL_BK == 0 && ka.kchunk % DL_BK == 0 && dl_ok(g.A, g.lda, g.a_kmajor, g.M) &&
+        dl_ok(g.B, g.ldb, g.b_kmajor, g.N)) {
+#define SLT_DL_GO(AKv, BKv)                                                          \
+  do {                                                                               \
+    if (split) gemm_dl_k<float, AKv, BKv, true><<<grid, NT, 0, s>>>(ka);             \
+    else gemm_dl_k<TO, AKv, BKv, false><<<grid, NT, 0, s>>>(ka);                     \
+  } while (0)
+      if (g.a_kmajor && g.b_kmajor) SLT_DL_GO(true, true);
+      else if (g.a_kmajor) SLT_DL_GO(true, false);
+      else if (g.b_kmajor) SLT_DL_GO(false, true);
+      else SLT_DL_GO(false, false);
+#undef SLT_DL_GO
+      return finish<TO>(g, split, splits, s);
+    }
+  }
+
 #define SLT_GEMM_GO(AKv, BKv)                                                     \
   do {                                                                            \
     if (split) {                                                                  \
@@ -557,14 +697,7 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
   else if (g.b_kmajor) SLT_GEMM_GO(false, true);
   else SLT_GEMM_GO(false, false);
 #undef SLT_GEMM_GO
-
-  if (split) {
-    const int64_t total = (int64_t)g.M * g.N;
-    int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
-    splitk_reduce_k<TO><<<blocks, 256, 0, s>>>(g.workspace, splits, g.M, g.N, static_cast<TO*>(g.C), g.ldc,
-                                               static_cast<const TO*>(g.R), g.ldr);
-  }
-  return check_launch("gemm");
+  return finish<TO>(g, split, splits, s);
 }
 
 }  // namespace

@@ -92,16 +92,20 @@ def test_gemm_small_ragged(B, a_k, b_k, ind, outd):
     gemm_case(B, rng, 96, 72, 3000, a_k, b_k, ind, outd, ws=True, resid=True)
 
 
+@pytest.mark.parametrize("a_k,b_k", [(1, 1), (1, 0), (0, 0), (0, 1)])
 @pytest.mark.parametrize("outd", [BF16, F32])
-def test_gemm_direct_lds_path(B, outd):
-    # bf16 with both operands k-major and K a multiple of 32 takes the path
-    # that copies tiles straight into a 3-stage LDS ring: cover 1..5 k-steps
-    # (every position of the ring's unrolled loop), ragged M and N, residual
+def test_gemm_direct_lds_path(B, a_k, b_k, outd):
+    # bf16 with K a multiple of 32 (and m/n-major operands 8-aligned) takes
+    # the path that copies tiles straight into a 3-stage LDS ring: cover 1..5
+    # k-steps (every position of the ring's unrolled loop), ragged M and N,
+    # residual, and split K through the workspace
     rng = np.random.default_rng(5)
-    for (M, N, K) in [(37, 50, 32), (129, 257, 64), (130, 260, 96), (200, 136, 128), (256, 384, 160),
-                      (1, 300, 32)]:
-        gemm_case(B, rng, M, N, K, 1, 1, BF16, outd)
-        gemm_case(B, rng, M, N, K, 1, 1, BF16, outd, resid=True)
+    for (M, N, K) in [(40, 56, 32), (136, 264, 64), (128, 256, 96), (200, 136, 128), (256, 384, 160),
+                      (8, 296, 32), (37, 56, 64)]:
+        gemm_case(B, rng, M, N, K, a_k, b_k, BF16, outd)
+        gemm_case(B, rng, M, N, K, a_k, b_k, BF16, outd, resid=True)
+    gemm_case(B, rng, 96, 72, 3008, a_k, b_k, BF16, outd, ws=True)
+    gemm_case(B, rng, 264, 136, 4096, a_k, b_k, BF16, outd, ws=True, resid=True)
 
 
 def test_gemm_zero_k_gives_residual_or_zero(B):
