@@ -135,14 +135,16 @@ def kernel_classes(w, ts, torch, reps):
     B.slt_rope_table(w.T, w.R, w.base, cs)
     g = torch.empty((w.N, qd), dtype=tdt, device="cuda").normal_()
     dqkv = torch.empty_like(qkv)
-    aws = torch.empty(B.slt_attention_bwd_workspace(w.B, w.H, w.T), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(B.slt_attention_bwd_workspace(w.B, w.T, w.H, w.Hkv, d, dt), dtype=torch.uint8, device="cuda")
+    fws = B.slt_attention_fwd_workspace(w.B, w.T, w.H, w.Hkv, d, dt)
+    fw = torch.empty(fws, dtype=torch.uint8, device="cuda") if fws else None
     p, dp = qkv.data_ptr(), dqkv.data_ptr()
     mode = B.ROPE_HALF if w.rope_mode == "half" else B.ROPE_PAIRS
 
     def fwd():
         for _ in range(w.L):
             B.slt_attention_fwd(p, p + qd * es, p + (qd + kd) * es, o, lse, ores, ld, ld, ld, qd,
-                                w.B, w.T, w.H, w.Hkv, d, w.R, mode, cs, dt)
+                                w.B, w.T, w.H, w.Hkv, d, w.R, mode, cs, dt, fw)
 
     def bwd():
         for _ in range(w.L):

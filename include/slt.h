@@ -234,18 +234,28 @@ slt_status slt_rope_table(int32_t T, int32_t R, float base, float* cs, void* str
  * of the softmax denominator of each query row (scores scaled by 1/sqrt(d)).
  * o_res (may be NULL): dense [B*T, H*d] in dtype, receives o - round(o), the
  * part of the output its storage type dropped; the backward uses it.
- * cs: the RoPE table of slt_rope_table for (T, R); R = 0 disables RoPE. */
+ * cs: the RoPE table of slt_rope_table for (T, R); R = 0 disables RoPE.
+ * workspace: slt_attention_fwd_workspace(...) bytes of device memory owned by
+ * the caller (16-byte aligned; NULL allowed when that size is 0), scratch for
+ * the call only: bf16 operands with d a multiple of 16 (d <= 64) rotate q and
+ * k once into it before the tiled kernel runs. */
+int64_t slt_attention_fwd_workspace(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d,
+                                    int32_t dtype);
 slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                              void* o_res, int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
                              int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R,
-                             int32_t rope_mode, const float* cs, int32_t dtype, void* stream);
+                             int32_t rope_mode, const float* cs, int32_t dtype, void* workspace,
+                             void* stream);
 
 /* Causal attention backward (recomputing probabilities from lse): writes dq
  * (of the un-rotated q), dk (un-rotated k; summed over the query heads of each
  * KV head) and dv with the same addressing as q, k, v.  o_res: the residual
  * written by the forward, or NULL.  workspace: at least
- * slt_attention_bwd_workspace(B, H, T) bytes. */
-int64_t slt_attention_bwd_workspace(int32_t B, int32_t H, int32_t T);
+ * slt_attention_bwd_workspace(B, T, H, Hkv, d, dtype) bytes of caller-owned,
+ * 16-byte aligned device memory (per-row D = dO.O, and for bf16 the rotated
+ * q/k copies), scratch for the call only. */
+int64_t slt_attention_bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d,
+                                    int32_t dtype);
 slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const void* o,
                              const void* o_res, const void* dout, const float* lse, void* dq, void* dk, void* dv,
                              int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t lddo,

@@ -65,9 +65,10 @@ SIGNATURES = {
     "slt_layernorm_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _F, _I32, _P]),
     "slt_layernorm_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P]),
     "slt_rope_table": (_I32, [_I32, _I32, _F, _P, _P]),
+    "slt_attention_fwd_workspace": (_I64, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "slt_attention_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
-                                 _I32, _I32, _I32, _P, _I32, _P]),
-    "slt_attention_bwd_workspace": (_I64, [_I32, _I32, _I32]),
+                                 _I32, _I32, _I32, _P, _I32, _P, _P]),
+    "slt_attention_bwd_workspace": (_I64, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "slt_attention_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64,
                                  _I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32,
                                  _P, _P]),
@@ -165,8 +166,12 @@ def slt_norm_bwd_workspace(rows, C) -> int:
     return int(load().slt_norm_bwd_workspace(rows, C))
 
 
-def slt_attention_bwd_workspace(B, H, T) -> int:
-    return int(load().slt_attention_bwd_workspace(B, H, T))
+def slt_attention_fwd_workspace(B, T, H, Hkv, d, dtype) -> int:
+    return int(load().slt_attention_fwd_workspace(B, T, H, Hkv, d, dtype))
+
+
+def slt_attention_bwd_workspace(B, T, H, Hkv, d, dtype) -> int:
+    return int(load().slt_attention_bwd_workspace(B, T, H, Hkv, d, dtype))
 
 
 # ---------------------------------------------------------------------------
@@ -240,11 +245,11 @@ def slt_rope_table(T, R, base, cs, stream=None):
 
 
 def slt_attention_fwd(q, k, v, o, lse, o_res, ldq, ldk, ldv, ldo, B, T, H, Hkv, d, R, rope_mode, cs, dtype,
-                      stream=None):
+                      workspace=None, stream=None):
     _check("slt_attention_fwd", load().slt_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o_res),
                                                          ldq, ldk,
                                                          ldv, ldo, B, T, H, Hkv, d, R, rope_mode, _ptr(cs), dtype,
-                                                         _stream(stream)))
+                                                         _ptr(workspace), _stream(stream)))
 
 
 def slt_attention_bwd(q, k, v, o, o_res, dout, lse, dq, dk, dv, ldq, ldk, ldv, ldo, lddo, lddq, lddk, lddv,

@@ -49,7 +49,7 @@ struct LayerP {
 };
 
 struct LayerA {
-  int64_t n1, r1, mu1, qkv, o, ores, lse, n2, r2, ab, h;  // byte offsets in the arena (-1: absent)
+  int64_t n1, r1, mu1, qkv, o, ores, lse, n2, r2, ab, h, rot;  // byte offsets in the arena (-1: absent)
 };
 
 struct Plan {
@@ -170,6 +170,8 @@ static slt_status make_plan(const slt_config* cfg, Plan& p) {
     A.mu1 = p.llama ? -1 : take(N * 4);
     A.lse = take((int64_t)c.B * c.H * c.T * 4);
     A.ores = p.bf ? take(N * p.qd * es) : -1;  // bf16 rounding residual of the attention output
+    // rotated hi/lo copies of q and k, made by the forward, reused by the backward
+    A.rot = flash_eligible(c.act, p.d) ? take(flash_rot_elems(c.B, c.T, c.H, c.Hkv) * 2) : -1;
     if (p.llama) {
       A.qkv = take(N * p.qkv_w * es);
       A.o = take(N * p.qd * es);
@@ -269,6 +271,8 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
     at.dtype = x.dt; at.cs = cs;
     at.lse = reinterpret_cast<float*>(x.A(A.lse));
     at.ores_out = A.ores >= 0 ? x.A(A.ores) : nullptr;
+    at.rot = A.rot >= 0 ? x.A(A.rot) : nullptr;
+    at.rot_ready = false;
     if (p.llama) {
       void* xin = x.A(p.xs[2 * l]);
       void* xmid = x.A(p.xs[2 * l + 1]);
@@ -344,6 +348,8 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     at.lse_in = (const float*)x.A(A.lse);
     at.delta = (float*)x.S(p.delta);
     at.ores_in = A.ores >= 0 ? x.A(A.ores) : nullptr;
+    at.rot = A.rot >= 0 ? x.A(A.rot) : nullptr;
+    at.rot_ready = true;
     char* qkv = (char*)x.A(A.qkv);
     if (p.llama) {
       // x_out = x_mid + h W2^T
@@ -600,10 +606,19 @@ static slt_status attn_check(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32
   return SLT_OK;
 }
 
+static int64_t attn_rot_bytes(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || Hkv <= 0 || !flash_eligible(dtype, d)) return 0;
+  return a256(flash_rot_elems(B, T, H, Hkv) * 2);
+}
+
+int64_t slt_attention_fwd_workspace(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t dtype) {
+  return attn_rot_bytes(B, T, H, Hkv, d, dtype);
+}
+
 slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* o_res, int64_t ldq,
                              int64_t ldk, int64_t ldv, int64_t ldo, int32_t B, int32_t T, int32_t H, int32_t Hkv,
                              int32_t d, int32_t R, int32_t rope_mode, const float* cs, int32_t dtype,
-                             void* stream) {
+                             void* workspace, void* stream) {
   SLT_TRY(attn_check(B, T, H, Hkv, d, R, rope_mode, dtype, cs));
   if ((int64_t)B * T == 0) return SLT_OK;
   if (!q || !k || !v || !o || !lse) return fail(SLT_EINVAL, "attention_fwd: NULL pointer");
@@ -613,10 +628,17 @@ slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* 
   a.q = q; a.k = k; a.v = v; a.out = o; a.lse = lse; a.ores_out = o_res;
   a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo;
   a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.d = d; a.R = R; a.rope_mode = rope_mode; a.dtype = dtype; a.cs = cs;
+  if (attn_rot_bytes(B, T, H, Hkv, d, dtype) > 0 && !workspace)
+    return fail(SLT_EINVAL, "attention_fwd: workspace is NULL (slt_attention_fwd_workspace is non-zero)");
+  a.rot = workspace;
+  a.rot_ready = false;
   return launch_attention_fwd(a, as_stream(stream));
 }
 
-int64_t slt_attention_bwd_workspace(int32_t B, int32_t H, int32_t T) { return attention_bwd_ws(B, H, T); }
+int64_t slt_attention_bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t dtype) {
+  if (B <= 0 || T <= 0 || H <= 0) return 0;
+  return a256(attention_bwd_ws(B, H, T)) + attn_rot_bytes(B, T, H, Hkv, d, dtype);
+}
 
 slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const void* o, const void* o_res,
                              const void* dout,
@@ -637,6 +659,9 @@ slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const 
   a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.lddo = lddo; a.lddq = lddq; a.lddk = lddk; a.lddv = lddv;
   a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.d = d; a.R = R; a.rope_mode = rope_mode; a.dtype = dtype; a.cs = cs;
   a.delta = static_cast<float*>(workspace);
+  a.rot = attn_rot_bytes(B, T, H, Hkv, d, dtype) > 0 ? static_cast<char*>(workspace) + a256(attention_bwd_ws(B, H, T))
+                                                      : nullptr;
+  a.rot_ready = false;
   return launch_attention_bwd(a, as_stream(stream));
 }
 

@@ -662,12 +662,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
           ds[r] = p[r] * (pacc[r] - Ds[ql]);
         }
         const Pk<T, 4> pf = pack4<T>(p);
+        const Pk<T, 4> pfl = low_part<T>(pf, p);  // dV sums over the whole group: P as hi + lo
         const Pk<T, 4> dsf = pack4<T>(ds);
         const Pk<T, 4> dsl = low_part<T>(dsf, ds);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int toff = (16 * c + (lane & 15)) * TS + qs * 16 + g4;
-          dv[c] = mma16(lds4(&Gt[toff]), pf, dv[c]);
+          const Pk<T, 4> gt4 = lds4(&Gt[toff]);
+          dv[c] = mma16(gt4, pf, dv[c]);
+          if constexpr (kBf<T>) dv[c] = mma16(gt4, pfl, dv[c]);
           const Pk<T, 4> qt4 = lds4(&Qt[toff]);
           dk[c] = mma16(qt4, dsf, dk[c]);
           if constexpr (kBf<T>) {
@@ -761,6 +764,7 @@ static slt_status attn_bwd_t(const AttnArgs& a, hipStream_t s) {
 
 slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return SLT_OK;
+  if (flash_ok(a, false)) return flash_fwd(a, s);
   if (a.dtype == SLT_BF16)
     return vec_path_ok<bf16>(a, false) ? attn_fwd_t<bf16, true>(a, s) : attn_fwd_t<bf16, false>(a, s);
   return vec_path_ok<float>(a, false) ? attn_fwd_t<float, true>(a, s) : attn_fwd_t<float, false>(a, s);
@@ -768,6 +772,7 @@ slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
 
 slt_status launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return SLT_OK;
+  if (flash_ok(a, true)) return flash_bwd(a, s);
   if (a.dtype == SLT_BF16)
     return vec_path_ok<bf16>(a, true) ? attn_bwd_t<bf16, true>(a, s) : attn_bwd_t<bf16, false>(a, s);
   return vec_path_ok<float>(a, true) ? attn_bwd_t<float, true>(a, s) : attn_bwd_t<float, false>(a, s);

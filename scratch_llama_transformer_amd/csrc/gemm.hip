@@ -343,16 +343,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int dl_swz(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int dl_swz_mn(int kr) { return 2 * ((kr & 3) | (((kr >> 3) & 1) << 2)); }
 
-// LDS byte offset of a pointer into a __shared__ array: the generic address
-// is the LDS aperture (upper 32 bits) plus the offset.
-__device__ __forceinline__ unsigned lds_off(const void* p) {
-  return static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
-}
-
-__device__ __forceinline__ void dl_copy(const bf16* src, bf16* dst) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                   (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
-}
 
 // Copy the 128 x 32 tile at (row0, k0) of an operand into `tile`: 2 copies per
 // wave (512 chunks of 16 bytes over 4 waves).
@@ -372,7 +362,7 @@ __device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, in
       const int c = (p & 15) ^ dl_swz_mn(kr);
       src = g + (int64_t)(k0 + kr) * ld + min(row0 + c * 8, rows - 8);
     }
-    dl_copy(src, tile + (wave * 2 + i) * 512);
+    lds_copy16(src, tile + (wave * 2 + i) * 512);
   }
 }
 
@@ -466,15 +456,6 @@ __device__ __forceinline__ void dl_read(const DlAddr<AK>& da, const DlAddr<BK>& 
 #undef DL_IN_KM
 #undef DL_IN_MN
 
-// Workgroup barrier that orders LDS accesses only: global_load_lds writes
-// are waited for explicitly (vmcnt) by each wave before it arrives.
-__device__ __forceinline__ void dl_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 struct DlCtx {
   const bf16* A;
   const bf16* B;
@@ -489,8 +470,8 @@ struct DlCtx {
 template <bool AK, bool BK>
 __device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK>& da, const DlAddr<BK>& db,
                                         unsigned as, unsigned bs, bf16* An, bf16* Bn, f32x4 (&acc)[4][4]) {
-  __builtin_amdgcn_s_waitcnt(0xF74);  // vmcnt(4): only the 4 copies of tile it+1 may still fly
-  dl_barrier();
+  SLT_WAIT_VMCNT(4);  // only the 4 copies of tile it+1 may still fly
+  lds_barrier();
   u32x4 af[4], bfr[4];
   dl_read<AK, BK>(da.at(as), db.at(bs), af, bfr);
   const int kn = c.kbeg + min(it + 2, c.nk - 1) * DL_BK;
@@ -552,7 +533,7 @@ __global__ __launch_bounds__(NT) void gemm_dl_k(KArgs a) {
     if (it + 1 < c.nk) dl_step<AK, BK>(c, it + 1, da, db, a1, b1, A0, B0, acc);
     if (it + 2 < c.nk) dl_step<AK, BK>(c, it + 2, da, db, a2, b2, A1, B1, acc);
   }
-  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): no copy may land after the block ends
+  SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
 
   const int m0 = c.m0, n0 = c.n0;
 #pragma unroll

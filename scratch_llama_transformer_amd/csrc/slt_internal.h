@@ -36,6 +36,34 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return bf16{f32_to_bf16_bits(x)}; }
 
 // ---------------------------------------------------------------------------
+// Direct HBM -> LDS copies (gfx950 global_load_lds_dwordx4).  Lane i of one
+// instruction writes the 16 bytes it fetched to LDS at (dst of lane 0) + 16 i:
+// the LDS layout is decided by which global chunk each lane fetches.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+}
+
+// LDS byte offset of a pointer into a __shared__ array: the generic address
+// is the LDS aperture (upper 32 bits) plus the offset.
+__device__ __forceinline__ unsigned lds_off(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Workgroup barrier that orders LDS accesses only; copies into LDS are
+// waited for explicitly (vmcnt) by each wave before it arrives.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+#define SLT_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt((((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14)))
+
+// ---------------------------------------------------------------------------
 // Error reporting (thread-local message)
 // ---------------------------------------------------------------------------
 void set_error(const std::string& msg);
@@ -105,9 +133,18 @@ struct AttnArgs {
   float* delta;        // workspace [B, H, T] for the backward
   void* ores_out;      // forward: optional o - bf16(o), dense [B*T, H*d]
   const void* ores_in; // backward: that residual (NULL: treat as 0)
+  void* rot;           // bf16 path: rotated hi/lo copies of q and k (flash_rot_elems bf16 values)
+  bool rot_ready;      // rot already holds them for these q, k (skip the RoPE pass)
 };
 slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s);
 slt_status launch_attention_bwd(const AttnArgs& a, hipStream_t s);
 int64_t attention_bwd_ws(int B, int H, int T);
+// bf16 attention with pre-rotated q/k copies and LDS tiles copied straight
+// from HBM (flash.hip)
+int64_t flash_rot_elems(int B, int T, int H, int Hkv);
+bool flash_eligible(int dtype, int d);
+bool flash_ok(const AttnArgs& a, bool bwd);
+slt_status flash_fwd(const AttnArgs& a, hipStream_t s);
+slt_status flash_bwd(const AttnArgs& a, hipStream_t s);
 
 }  // namespace slt

@@ -112,5 +112,10 @@ def test_host_calls_reject_bad_arguments_before_launch():
     assert lib.slt_gemm(4, 4, 4, None, 4, 1, None, 4, 1, None, 4, None, 0, 1, 1, None, 0, None) == 1
     assert lib.slt_adamw_step(10, None, None, None, None, None, 1, 1e-3, 0.9, 0.999, 1e-8, 0.1, None, None) == 1
     assert lib.slt_attention_fwd(None, None, None, None, None, None, 8, 8, 8, 8, 1, 4, 2, 1, 128, 0, 0, None, 1,
-                                 None) == 2
+                                 None, None) == 2
+    # a bf16 head dim the rotated-copy path takes needs its workspace
+    assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 48, 1) == 2 * 2 * 6 * 64 * 64 * 2
+    assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 48, 0) == 0
+    assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 24, 1) == 0
+    assert B.slt_attention_bwd_workspace(2, 64, 4, 2, 24, 1) == 2 * 4 * 64 * 4
     assert lib.slt_softmax_xent(None, 10, None, 1, 4, 5, 10, None, None, 1, None, None) == 1

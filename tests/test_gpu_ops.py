@@ -244,16 +244,25 @@ ATTN_CASES = [
     (1, 130, 16, 4, 64, 64, "half", BF16),
     (1, 200, 4, 4, 64, 32, "pairs", BF16),
     (2, 64, 2, 1, 48, 0, "half", BF16),
+    (1, 1, 2, 2, 64, 64, "half", BF16),
+    (1, 37, 2, 2, 16, 16, "half", BF16),
+    (2, 100, 4, 2, 32, 8, "pairs", BF16),
+    (1, 1024, 4, 1, 64, 64, "half", BF16),
+    (1, 40, 2, 2, 24, 24, "half", BF16),      # head dim not a multiple of 16: register-staged kernels
 ]
 
 
+@pytest.mark.parametrize("pad", [3, 8])
 @pytest.mark.parametrize("case", ATTN_CASES)
-def test_attention_fwd_bwd(B, case):
+def test_attention_fwd_bwd(B, case, pad):
+    # pad 3: rows not 16-byte aligned (register-staged kernels); pad 8: the
+    # step's alignment, which bf16 head dims that are multiples of 16 take
+    # through the rotated-copy kernels with tiles copied straight into LDS
     Bn, T, H, Hkv, d, R, mode, dtype = case
-    say("attention", case)
+    say("attention", case, pad)
     rng = np.random.default_rng(8)
     qd, kd = H * d, Hkv * d
-    ld = qd + 2 * kd + 3          # padded row stride exercises the strides
+    ld = qd + 2 * kd + pad
     qkv = rnd(rng, (Bn * T, ld), dtype)
     tq = dev(qkv, dtype)
     es = 2 if dtype == BF16 else 4
@@ -265,8 +274,11 @@ def test_attention_fwd_bwd(B, case):
     lse = torch.empty((Bn, H, T), device="cuda")
     ores = torch.full((Bn * T, qd), float("nan"), dtype=tq.dtype, device="cuda") if dtype == BF16 else None
     base = tq.data_ptr()
+    fws = B.slt_attention_fwd_workspace(Bn, T, H, Hkv, d, dtype)
+    assert (fws > 0) == (dtype == BF16 and d % 16 == 0)
+    fw = torch.empty(fws, dtype=torch.uint8, device="cuda") if fws else None
     B.slt_attention_fwd(base, base + qd * es, base + (qd + kd) * es, o, lse, ores, ld, ld, ld, qd,
-                        Bn, T, H, Hkv, d, R, mode_i, cs, dtype)
+                        Bn, T, H, Hkv, d, R, mode_i, cs, dtype, fw)
 
     def heads(x, nh):
         return x.reshape(Bn, T, nh, d).transpose(0, 2, 1, 3)
@@ -294,7 +306,7 @@ def test_attention_fwd_bwd(B, case):
     o_dev = dev(o_hi, dtype)
     ores_dev = dev(O.bf16_round(o_ref2 - o_hi), dtype) if dtype == BF16 else None
     dqkv = torch.full((Bn * T, ld), float("nan"), dtype=tq.dtype, device="cuda")
-    ws = torch.empty(B.slt_attention_bwd_workspace(Bn, H, T), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(B.slt_attention_bwd_workspace(Bn, T, H, Hkv, d, dtype), dtype=torch.uint8, device="cuda")
     db = dqkv.data_ptr()
     B.slt_attention_bwd(base, base + qd * es, base + (qd + kd) * es, o_dev, ores_dev, dev(do, dtype), lse,
                         db, db + qd * es, db + (qd + kd) * es, ld, ld, ld, qd, qd, ld, ld, ld,
