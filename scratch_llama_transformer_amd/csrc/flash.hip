@@ -192,7 +192,12 @@ struct FlArgs {
 // ---------------------------------------------------------------------------
 // RoPE once: q and k heads -> hi/lo rotated copies.  Item = (b, t, head
 // slot, 8-dim chunk); slots 0..H-1 are query heads, H..H+Hkv-1 key heads.
+// VEC: every chunk is wholly rotated or wholly past R and its partner chunk
+// is 16-byte aligned ((R/2) % 8 == 0 for rotate-half, R % 8 == 0 for
+// pairs), so a chunk is three 16-byte loads (own, partner, table) and two
+// 16-byte stores; otherwise element by element.
 // ---------------------------------------------------------------------------
+template <bool VEC>
 __global__ __launch_bounds__(256) void fl_prep_k(const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ k,
                                                  int64_t ldk, bf16* qh, bf16* ql, bf16* kh, bf16* kl, int B, int T,
                                                  int H, int Hkv, int d, int R, int mode, const float* cs) {
@@ -211,31 +216,72 @@ __global__ __launch_bounds__(256) void fl_prep_k(const bf16* __restrict__ q, int
     bf16* dh = (isq ? qh : kh) + drow;
     bf16* dl = (isq ? ql : kl) + drow;
     uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
-    if (c * 8 < d) {
+    const int j0 = c * 8;
+    if (j0 < d) {
       const bf16* u = isq ? q + bt * ldq + (int64_t)hd * d : k + bt * ldk + (int64_t)hd * d;
       float x[8];
+      if (VEC) {
+        const uint4 own = *reinterpret_cast<const uint4*>(u + j0);
+        const uint32_t ow[4] = {own.x, own.y, own.z, own.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = c * 8 + e;
-        float v = to_f32(u[j]);
-        if (j < R) {
-          int ii, p;
-          bool first;
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = __uint_as_float(ow[e] << 16);
+          x[2 * e + 1] = __uint_as_float(ow[e] & 0xffff0000u);
+        }
+        if (j0 < R) {
+          const float* tb = cs + (int64_t)t * R;
           if (mode == SLT_ROPE_HALF) {
             const int hr = R >> 1;
-            first = j < hr;
-            ii = first ? j : j - hr;
-            p = first ? j + hr : j - hr;
+            const bool first = j0 < hr;
+            const int i0 = first ? j0 : j0 - hr;
+            const uint4 par = *reinterpret_cast<const uint4*>(u + (first ? j0 + hr : j0 - hr));
+            const uint32_t pw[4] = {par.x, par.y, par.z, par.w};
+            const float4* t4 = reinterpret_cast<const float4*>(tb + 2 * i0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float4 cs2 = t4[e];  // (cos, sin) of dims i0 + 2e, i0 + 2e + 1
+              const float y0 = __uint_as_float(pw[e] << 16), y1 = __uint_as_float(pw[e] & 0xffff0000u);
+              const float x0 = x[2 * e], x1 = x[2 * e + 1];
+              x[2 * e] = first ? x0 * cs2.x - y0 * cs2.y : x0 * cs2.x + y0 * cs2.y;
+              x[2 * e + 1] = first ? x1 * cs2.z - y1 * cs2.w : x1 * cs2.z + y1 * cs2.w;
+            }
           } else {
-            first = (j & 1) == 0;
-            ii = j >> 1;
-            p = j ^ 1;
+            const float4* t4 = reinterpret_cast<const float4*>(tb + j0);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float4 cs2 = t4[e];  // pairs (j0 + 4e, +1) and (j0 + 4e + 2, +3)
+              const float a0 = x[4 * e], a1 = x[4 * e + 1], b0 = x[4 * e + 2], b1 = x[4 * e + 3];
+              x[4 * e] = a0 * cs2.x - a1 * cs2.y;
+              x[4 * e + 1] = a1 * cs2.x + a0 * cs2.y;
+              x[4 * e + 2] = b0 * cs2.z - b1 * cs2.w;
+              x[4 * e + 3] = b1 * cs2.z + b0 * cs2.w;
+            }
           }
-          const float cth = cs[(int64_t)t * R + 2 * ii], sth = cs[(int64_t)t * R + 2 * ii + 1];
-          const float y = to_f32(u[p]);
-          v = first ? v * cth - y * sth : v * cth + y * sth;
         }
-        x[e] = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + e;
+          float v = to_f32(u[j]);
+          if (j < R) {
+            int ii, p;
+            bool first;
+            if (mode == SLT_ROPE_HALF) {
+              const int hr = R >> 1;
+              first = j < hr;
+              ii = first ? j : j - hr;
+              p = first ? j + hr : j - hr;
+            } else {
+              first = (j & 1) == 0;
+              ii = j >> 1;
+              p = j ^ 1;
+            }
+            const float cth = cs[(int64_t)t * R + 2 * ii], sth = cs[(int64_t)t * R + 2 * ii + 1];
+            const float y = to_f32(u[p]);
+            v = first ? v * cth - y * sth : v * cth + y * sth;
+          }
+          x[e] = v;
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -764,7 +810,10 @@ FlArgs to_fl(const AttnArgs& a) {
 slt_status prep(const AttnArgs& a, const FlArgs& f, hipStream_t s) {
   const int64_t items = (int64_t)a.B * a.T * (a.H + a.Hkv) * 8;
   const int blocks = (int)std::min<int64_t>((items + 255) / 256, 16384);
-  fl_prep_k<<<blocks, 256, 0, s>>>(static_cast<const bf16*>(a.q), a.ldq, static_cast<const bf16*>(a.k), a.ldk,
+  const bool vec = al(a.q, 16) && al(a.k, 16) && a.ldq % 8 == 0 && a.ldk % 8 == 0 && (a.R == 0 || a.cs != nullptr) &&
+                   (a.R == 0 || (a.rope_mode == SLT_ROPE_HALF ? (a.R / 2) % 8 == 0 : a.R % 8 == 0));
+  auto* kern = vec ? fl_prep_k<true> : fl_prep_k<false>;
+  kern<<<blocks, 256, 0, s>>>(static_cast<const bf16*>(a.q), a.ldq, static_cast<const bf16*>(a.k), a.ldk,
                                    const_cast<bf16*>(f.qh), const_cast<bf16*>(f.ql), const_cast<bf16*>(f.kh),
                                    const_cast<bf16*>(f.kl), a.B, a.T, a.H, a.Hkv, a.d, a.R, a.rope_mode, a.cs);
   return check_launch("attention rope prep");
