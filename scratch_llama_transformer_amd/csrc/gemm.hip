@@ -340,7 +340,11 @@ constexpr int DL_TILE = BM * DL_BK;  // elements per operand tile (8 KiB)
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ int dl_swz(int r) { return (r >> 2) & 3; }
+// k-major tile: chunk position XOR (r >> 1) & 3.  A fragment read takes rows
+// r0..r0+15 (r0 a multiple of 16) at one logical chunk per 16-lane group;
+// measured with the SQ_LDS_BANK_CONFLICT counter on gfx950, this swizzle
+// reads them conflict-free where (r >> 2) & 3 costs 4 extra cycles per read.
+__device__ __forceinline__ int dl_swz(int r) { return (r >> 1) & 3; }
 __device__ __forceinline__ int dl_swz_mn(int kr) { return 2 * ((kr & 3) | (((kr >> 3) & 1) << 2)); }
 
 
@@ -372,12 +376,18 @@ __device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, in
 // read of each at +1 KiB (4 k-rows of 256 bytes further).
 template <bool KM> struct DlAddr;
 template <> struct DlAddr<true> {
+  // fragment f reads rows w0 + 16 f + l%16, whose swizzle is that of l%16:
+  // one address, fragments 1 KiB apart
   unsigned a;
   __device__ __forceinline__ DlAddr(int w0, int lane) {
-    const int r = w0 + (lane & 15);
-    a = (r * 4 + ((lane >> 4) ^ dl_swz(r))) * 16;
+    const int i = lane & 15;
+    a = (w0 + i) * 64 + ((lane >> 4) ^ dl_swz(i)) * 16;
   }
-  __device__ __forceinline__ DlAddr<true> at(unsigned base) const { DlAddr<true> x = *this; x.a += base; return x; }
+  __device__ __forceinline__ DlAddr<true> at(unsigned base) const {
+    DlAddr<true> x = *this;
+    x.a += base;
+    return x;
+  }
 };
 template <> struct DlAddr<false> {
   unsigned a[4];
@@ -398,10 +408,10 @@ template <> struct DlAddr<false> {
   }
 };
 
-#define DL_KM(X)                                       \
-  "ds_read_b128 %[" #X "0], %[" #X "a]\n\t"            \
-  "ds_read_b128 %[" #X "1], %[" #X "a] offset:1024\n\t" \
-  "ds_read_b128 %[" #X "2], %[" #X "a] offset:2048\n\t" \
+#define DL_KM(X)                                         \
+  "ds_read_b128 %[" #X "0], %[" #X "a]\n\t"              \
+  "ds_read_b128 %[" #X "1], %[" #X "a] offset:1024\n\t"  \
+  "ds_read_b128 %[" #X "2], %[" #X "a] offset:2048\n\t"  \
   "ds_read_b128 %[" #X "3], %[" #X "a] offset:3072\n\t"
 #define DL_MN(X)                                                     \
   "ds_read_b64_tr_b16 %[" #X "0l], %[" #X "a0]\n\t"                  \
