@@ -31,6 +31,9 @@
 #ifndef SLT_GEMM_BKX
 #define SLT_GEMM_BKX 2
 #endif
+#ifndef SLT_GEMM_BIG
+#define SLT_GEMM_BIG 1
+#endif
 #ifndef SLT_GEMM_XCD
 #define SLT_GEMM_XCD 1
 #endif
@@ -370,101 +373,113 @@ __device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, in
   }
 }
 
-// Per-lane LDS byte addresses of this wave's fragments within a tile (w0 =
-// first row or column of the wave's 64): k-major: one address, fragments at
-// +1 KiB steps; m/n-major: four addresses (one per fragment), the second
-// read of each at +1 KiB (4 k-rows of 256 bytes further).
-template <bool KM> struct DlAddr;
-template <> struct DlAddr<true> {
-  // fragment f reads rows w0 + 16 f + l%16, whose swizzle is that of l%16:
-  // one address, fragments 1 KiB apart
+// Per-lane LDS byte addresses of a wave's F fragments (16 rows or columns
+// each) starting at row w0 of an operand tile made of 128-row sub-tiles
+// (8 KiB each): k-major: one address, fragments 1 KiB apart; m/n-major: one
+// address per fragment, the second read of each at +1 KiB (4 k-rows of 256
+// bytes further).  w0 is a multiple of 16 F, so the fragments stay inside
+// one sub-tile.
+template <bool KM, int F> struct DlAddr;
+template <int F> struct DlAddr<true, F> {
   unsigned a;
   __device__ __forceinline__ DlAddr(int w0, int lane) {
     const int i = lane & 15;
-    a = (w0 + i) * 64 + ((lane >> 4) ^ dl_swz(i)) * 16;
+    a = (w0 >> 7) * 8192 + ((w0 & 127) + i) * 64 + ((lane >> 4) ^ dl_swz(i)) * 16;
   }
-  __device__ __forceinline__ DlAddr<true> at(unsigned base) const {
-    DlAddr<true> x = *this;
+  __device__ __forceinline__ DlAddr at(unsigned base) const {
+    DlAddr x = *this;
     x.a += base;
     return x;
   }
 };
-template <> struct DlAddr<false> {
-  unsigned a[4];
+template <int F> struct DlAddr<false, F> {
+  unsigned a[F];
   __device__ __forceinline__ DlAddr(int w0, int lane) {
     const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
     const int kr = 8 * g + j;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = (w0 + 16 * i) / 8 + (q >> 1);
-      a[i] = (kr * 16 + (c ^ dl_swz_mn(kr))) * 16 + (q & 1) * 8;
+    for (int f = 0; f < F; ++f) {
+      const int c = ((w0 & 127) + 16 * f) / 8 + (q >> 1);
+      a[f] = (w0 >> 7) * 8192 + (kr * 16 + (c ^ dl_swz_mn(kr))) * 16 + (q & 1) * 8;
     }
   }
-  __device__ __forceinline__ DlAddr<false> at(unsigned base) const {
-    DlAddr<false> x = *this;
+  __device__ __forceinline__ DlAddr at(unsigned base) const {
+    DlAddr x = *this;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x.a[i] += base;
+    for (int f = 0; f < F; ++f) x.a[f] += base;
     return x;
   }
 };
 
-#define DL_KM(X)                                         \
-  "ds_read_b128 %[" #X "0], %[" #X "a]\n\t"              \
-  "ds_read_b128 %[" #X "1], %[" #X "a] offset:1024\n\t"  \
-  "ds_read_b128 %[" #X "2], %[" #X "a] offset:2048\n\t"  \
-  "ds_read_b128 %[" #X "3], %[" #X "a] offset:3072\n\t"
-#define DL_MN(X)                                                     \
-  "ds_read_b64_tr_b16 %[" #X "0l], %[" #X "a0]\n\t"                  \
-  "ds_read_b64_tr_b16 %[" #X "0h], %[" #X "a0] offset:1024\n\t"      \
-  "ds_read_b64_tr_b16 %[" #X "1l], %[" #X "a1]\n\t"                  \
-  "ds_read_b64_tr_b16 %[" #X "1h], %[" #X "a1] offset:1024\n\t"      \
-  "ds_read_b64_tr_b16 %[" #X "2l], %[" #X "a2]\n\t"                  \
-  "ds_read_b64_tr_b16 %[" #X "2h], %[" #X "a2] offset:1024\n\t"      \
-  "ds_read_b64_tr_b16 %[" #X "3l], %[" #X "a3]\n\t"                  \
-  "ds_read_b64_tr_b16 %[" #X "3h], %[" #X "a3] offset:1024\n\t"
-#define DL_OUT_KM(X, f) [X##0] "=&v"(f[0]), [X##1] "=&v"(f[1]), [X##2] "=&v"(f[2]), [X##3] "=&v"(f[3])
-#define DL_OUT_MN(X, l, h)                                                                                   \
-  [X##0l] "=&v"(l[0]), [X##0h] "=&v"(h[0]), [X##1l] "=&v"(l[1]), [X##1h] "=&v"(h[1]), [X##2l] "=&v"(l[2]), \
-      [X##2h] "=&v"(h[2]), [X##3l] "=&v"(l[3]), [X##3h] "=&v"(h[3])
-#define DL_IN_KM(X, d) [X##a] "v"(d.a)
-#define DL_IN_MN(X, d) [X##a0] "v"(d.a[0]), [X##a1] "v"(d.a[1]), [X##a2] "v"(d.a[2]), [X##a3] "v"(d.a[3])
+#define DL_R128(X, f, off) "ds_read_b128 %[" #X #f "], %[" #X "p] offset:" #off "\n\t"
+#define DL_KM4(X) DL_R128(X, 0, 0) DL_R128(X, 1, 1024) DL_R128(X, 2, 2048) DL_R128(X, 3, 3072)
+#define DL_KM8(X) DL_KM4(X) DL_R128(X, 4, 4096) DL_R128(X, 5, 5120) DL_R128(X, 6, 6144) DL_R128(X, 7, 7168)
+#define DL_RTR(X, f)                                                  \
+  "ds_read_b64_tr_b16 %[" #X #f "l], %[" #X "p" #f "]\n\t"            \
+  "ds_read_b64_tr_b16 %[" #X #f "h], %[" #X "p" #f "] offset:1024\n\t"
+#define DL_MN4(X) DL_RTR(X, 0) DL_RTR(X, 1) DL_RTR(X, 2) DL_RTR(X, 3)
+#define DL_OKM(X, f, v) [X##f] "=&v"(v[f])
+#define DL_OUT_KM4(X, v) DL_OKM(X, 0, v), DL_OKM(X, 1, v), DL_OKM(X, 2, v), DL_OKM(X, 3, v)
+#define DL_OUT_KM8(X, v) DL_OUT_KM4(X, v), DL_OKM(X, 4, v), DL_OKM(X, 5, v), DL_OKM(X, 6, v), DL_OKM(X, 7, v)
+#define DL_OMN(X, f, lo, hi) [X##f##l] "=&v"(lo[f]), [X##f##h] "=&v"(hi[f])
+#define DL_OUT_MN4(X, lo, hi) DL_OMN(X, 0, lo, hi), DL_OMN(X, 1, lo, hi), DL_OMN(X, 2, lo, hi), DL_OMN(X, 3, lo, hi)
+#define DL_IN_KM(X, d) [X##p] "v"(d.a)
+#define DL_IN_MN4(X, d) [X##p0] "v"(d.a[0]), [X##p1] "v"(d.a[1]), [X##p2] "v"(d.a[2]), [X##p3] "v"(d.a[3])
 
-// The 4 A and 4 B fragments of one k-step, as one asm block that also waits
-// for its own reads: the compiler cannot tell which LDS stage a
-// global_load_lds copy targets and would otherwise wait for every copy in
-// flight before any LDS read.
-template <bool AK, bool BK>
-__device__ __forceinline__ void dl_read(const DlAddr<AK>& da, const DlAddr<BK>& db, u32x4 (&af)[4],
-                                        u32x4 (&bf)[4]) {
-  u32x2 al[4], ah[4], bl[4], bh[4];
-  if constexpr (AK && BK) {
-    asm volatile(DL_KM(a) DL_KM(b) "s_waitcnt lgkmcnt(0)"
-                 : DL_OUT_KM(a, af), DL_OUT_KM(b, bf) : DL_IN_KM(a, da), DL_IN_KM(b, db) : "memory");
-  } else if constexpr (AK && !BK) {
-    asm volatile(DL_KM(a) DL_MN(b) "s_waitcnt lgkmcnt(0)"
-                 : DL_OUT_KM(a, af), DL_OUT_MN(b, bl, bh) : DL_IN_KM(a, da), DL_IN_MN(b, db) : "memory");
-  } else if constexpr (!AK && BK) {
-    asm volatile(DL_MN(a) DL_KM(b) "s_waitcnt lgkmcnt(0)"
-                 : DL_OUT_MN(a, al, ah), DL_OUT_KM(b, bf) : DL_IN_MN(a, da), DL_IN_KM(b, db) : "memory");
+// The A and B fragments of one k-step, as one asm block that also waits for
+// its own reads: the compiler cannot tell which LDS stage a global_load_lds
+// copy targets and would otherwise wait for every copy in flight before any
+// LDS read.  Supported shapes: 4 fragments per side, and 8 on the side of a
+// k-major operand whose partner has 4.
+template <bool AK, bool BK, int FA, int FB>
+__device__ __forceinline__ void dl_read(const DlAddr<AK, FA>& da, const DlAddr<BK, FB>& db, u32x4 (&af)[FA],
+                                        u32x4 (&bf)[FB]) {
+  u32x2 al[FA], ah[FA], bl[FB], bh[FB];
+  if constexpr (AK && BK && FA == 4 && FB == 4) {
+    asm volatile(DL_KM4(a) DL_KM4(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_KM4(a, af), DL_OUT_KM4(b, bf) : DL_IN_KM(a, da), DL_IN_KM(b, db) : "memory");
+  } else if constexpr (AK && BK && FA == 8 && FB == 4) {
+    asm volatile(DL_KM8(a) DL_KM4(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_KM8(a, af), DL_OUT_KM4(b, bf) : DL_IN_KM(a, da), DL_IN_KM(b, db) : "memory");
+  } else if constexpr (AK && BK && FA == 4 && FB == 8) {
+    asm volatile(DL_KM4(a) DL_KM8(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_KM4(a, af), DL_OUT_KM8(b, bf) : DL_IN_KM(a, da), DL_IN_KM(b, db) : "memory");
+  } else if constexpr (AK && !BK && FA == 4 && FB == 4) {
+    asm volatile(DL_KM4(a) DL_MN4(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_KM4(a, af), DL_OUT_MN4(b, bl, bh) : DL_IN_KM(a, da), DL_IN_MN4(b, db) : "memory");
+  } else if constexpr (AK && !BK && FA == 8 && FB == 4) {
+    asm volatile(DL_KM8(a) DL_MN4(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_KM8(a, af), DL_OUT_MN4(b, bl, bh) : DL_IN_KM(a, da), DL_IN_MN4(b, db) : "memory");
+  } else if constexpr (!AK && BK && FA == 4 && FB == 4) {
+    asm volatile(DL_MN4(a) DL_KM4(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_MN4(a, al, ah), DL_OUT_KM4(b, bf) : DL_IN_MN4(a, da), DL_IN_KM(b, db) : "memory");
+  } else if constexpr (!AK && !BK && FA == 4 && FB == 4) {
+    asm volatile(DL_MN4(a) DL_MN4(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_MN4(a, al, ah), DL_OUT_MN4(b, bl, bh) : DL_IN_MN4(a, da), DL_IN_MN4(b, db) : "memory");
   } else {
-    asm volatile(DL_MN(a) DL_MN(b) "s_waitcnt lgkmcnt(0)"
-                 : DL_OUT_MN(a, al, ah), DL_OUT_MN(b, bl, bh) : DL_IN_MN(a, da), DL_IN_MN(b, db) : "memory");
+    static_assert(AK && BK && FA == 4 && FB == 4, "unsupported fragment shape");
   }
   if constexpr (!AK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = u32x4{al[i][0], al[i][1], ah[i][0], ah[i][1]};
+    for (int i = 0; i < FA; ++i) af[i] = u32x4{al[i][0], al[i][1], ah[i][0], ah[i][1]};
   }
   if constexpr (!BK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bf[i] = u32x4{bl[i][0], bl[i][1], bh[i][0], bh[i][1]};
+    for (int i = 0; i < FB; ++i) bf[i] = u32x4{bl[i][0], bl[i][1], bh[i][0], bh[i][1]};
   }
 }
-#undef DL_KM
-#undef DL_MN
-#undef DL_OUT_KM
-#undef DL_OUT_MN
+#undef DL_R128
+#undef DL_KM4
+#undef DL_KM8
+#undef DL_RTR
+#undef DL_MN4
+#undef DL_OKM
+#undef DL_OUT_KM4
+#undef DL_OUT_KM8
+#undef DL_OMN
+#undef DL_OUT_MN4
 #undef DL_IN_KM
-#undef DL_IN_MN
+#undef DL_IN_MN4
 
 struct DlCtx {
   const bf16* A;
@@ -473,33 +488,45 @@ struct DlCtx {
   int M, N, m0, n0, kbeg, nk, wave, lane;
 };
 
+// Copy the (NS x 128) x 32 operand tile at (row0, k0) into NS sub-tiles.
+template <bool KM, int NS>
+__device__ __forceinline__ void dl_issue_tile(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile,
+                                              int wave, int lane) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) dl_issue<KM>(g, ld, rows, row0 + 128 * s, k0, tile + s * DL_TILE, wave, lane);
+}
+
 // One k-step: wait for this wave's part of tile `it`, barrier, read the
 // current stage, refill the stage freed in step it-1 with tile it+2 (past the
-// end: the last tile again, into a stage nobody reads, so that exactly 4
-// copies per wave are in flight at every wait), multiply.
-template <bool AK, bool BK>
-__device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK>& da, const DlAddr<BK>& db,
-                                        unsigned as, unsigned bs, bf16* An, bf16* Bn, f32x4 (&acc)[4][4]) {
-  SLT_WAIT_VMCNT(4);  // only the 4 copies of tile it+1 may still fly
+// end: the last tile again, into a stage nobody reads, so that the same
+// number of copies per wave is in flight at every wait), multiply.
+template <bool AK, bool BK, int FM, int FN>
+__device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK, FM>& da, const DlAddr<BK, FN>& db,
+                                        unsigned as, unsigned bs, bf16* An, bf16* Bn, f32x4 (&acc)[FM][FN]) {
+  constexpr int NSA = FM / 4, NSB = FN / 4;
+  SLT_WAIT_VMCNT(2 * (NSA + NSB));  // only the copies of tile it+1 may still fly
   lds_barrier();
-  u32x4 af[4], bfr[4];
-  dl_read<AK, BK>(da.at(as), db.at(bs), af, bfr);
+  u32x4 af[FM], bfr[FN];
+  dl_read<AK, BK, FM, FN>(da.at(as), db.at(bs), af, bfr);
   const int kn = c.kbeg + min(it + 2, c.nk - 1) * DL_BK;
-  dl_issue<AK>(c.A, c.lda, c.M, c.m0, kn, An, c.wave, c.lane);
-  dl_issue<BK>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
+  dl_issue_tile<AK, NSA>(c.A, c.lda, c.M, c.m0, kn, An, c.wave, c.lane);
+  dl_issue_tile<BK, NSB>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[j]),
                                                           __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
 }
 
-template <typename TO, bool AK, bool BK, bool SPLIT>
-__global__ __launch_bounds__(NT) void gemm_dl_k(KArgs a) {
+// Block tile (32 FM) x (32 FN): 2 x 2 waves, each 16 FM x 16 FN.
+template <typename TO, bool AK, bool BK, bool SPLIT, int FM, int FN>
+__global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a) {
+  constexpr int NSA = FM / 4, NSB = FN / 4;
+  constexpr int TBM = 32 * FM, TBN = 32 * FN;
   // three stages as distinct LDS objects
-  __shared__ __attribute__((aligned(16))) bf16 A0[DL_TILE], A1[DL_TILE], A2[DL_TILE];
-  __shared__ __attribute__((aligned(16))) bf16 B0[DL_TILE], B1[DL_TILE], B2[DL_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 A0[NSA * DL_TILE], A1[NSA * DL_TILE], A2[NSA * DL_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 B0[NSB * DL_TILE], B1[NSB * DL_TILE], B2[NSB * DL_TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -517,42 +544,42 @@ __global__ __launch_bounds__(NT) void gemm_dl_k(KArgs a) {
   c.ldb = a.ldb;
   c.M = a.M;
   c.N = a.N;
-  c.m0 = tm * BM;
-  c.n0 = tn * BN;
+  c.m0 = tm * TBM;
+  c.n0 = tn * TBN;
   c.kbeg = SPLIT ? blockIdx.z * a.kchunk : 0;
   c.nk = (min(a.K, c.kbeg + a.kchunk) - c.kbeg) / DL_BK;
   c.wave = wave;
   c.lane = lane;
-  const DlAddr<AK> da(wm * 64, lane);
-  const DlAddr<BK> db(wn * 64, lane);
+  const DlAddr<AK, FM> da(wm * 16 * FM, lane);
+  const DlAddr<BK, FN> db(wn * 16 * FN, lane);
 
-  f32x4 acc[4][4];
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  dl_issue<AK>(c.A, c.lda, c.M, c.m0, c.kbeg, A0, wave, lane);
-  dl_issue<BK>(c.B, c.ldb, c.N, c.n0, c.kbeg, B0, wave, lane);
-  dl_issue<AK>(c.A, c.lda, c.M, c.m0, c.kbeg + min(1, c.nk - 1) * DL_BK, A1, wave, lane);
-  dl_issue<BK>(c.B, c.ldb, c.N, c.n0, c.kbeg + min(1, c.nk - 1) * DL_BK, B1, wave, lane);
+  dl_issue_tile<AK, NSA>(c.A, c.lda, c.M, c.m0, c.kbeg, A0, wave, lane);
+  dl_issue_tile<BK, NSB>(c.B, c.ldb, c.N, c.n0, c.kbeg, B0, wave, lane);
+  dl_issue_tile<AK, NSA>(c.A, c.lda, c.M, c.m0, c.kbeg + min(1, c.nk - 1) * DL_BK, A1, wave, lane);
+  dl_issue_tile<BK, NSB>(c.B, c.ldb, c.N, c.n0, c.kbeg + min(1, c.nk - 1) * DL_BK, B1, wave, lane);
   const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
   const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
   for (int it = 0; it < c.nk; it += 3) {
-    dl_step<AK, BK>(c, it, da, db, a0, b0, A2, B2, acc);
-    if (it + 1 < c.nk) dl_step<AK, BK>(c, it + 1, da, db, a1, b1, A0, B0, acc);
-    if (it + 2 < c.nk) dl_step<AK, BK>(c, it + 2, da, db, a2, b2, A1, B1, acc);
+    dl_step<AK, BK, FM, FN>(c, it, da, db, a0, b0, A2, B2, acc);
+    if (it + 1 < c.nk) dl_step<AK, BK, FM, FN>(c, it + 1, da, db, a1, b1, A0, B0, acc);
+    if (it + 2 < c.nk) dl_step<AK, BK, FM, FN>(c, it + 2, da, db, a2, b2, A1, B1, acc);
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
 
   const int m0 = c.m0, n0 = c.n0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 64 + i * 16 + (lane & 15);
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * 16 * FM + i * 16 + (lane & 15);
     if (m >= a.M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * 16 * FN + j * 16 + 4 * (lane >> 4);
       if (n >= a.N) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       if (SPLIT) {
@@ -658,15 +685,38 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
     };
     if (g.K > 0 && g.K % DL_BK == 0 && ka.kchunk % DL_BK == 0 && dl_ok(g.A, g.lda, g.a_kmajor, g.M) &&
         dl_ok(g.B, g.ldb, g.b_kmajor, g.N)) {
-#define SLT_DL_GO(AKv, BKv)                                                          \
-  do {                                                                               \
-    if (split) gemm_dl_k<float, AKv, BKv, true><<<grid, NT, 0, s>>>(ka);             \
-    else gemm_dl_k<TO, AKv, BKv, false><<<grid, NT, 0, s>>>(ka);                     \
+#define SLT_DL_GO(AKv, BKv, FMv, FNv)                                                          \
+  do {                                                                                         \
+    if (split) gemm_dl_k<float, AKv, BKv, true, FMv, FNv><<<grid, NT, 0, s>>>(ka);             \
+    else gemm_dl_k<TO, AKv, BKv, false, FMv, FNv><<<grid, NT, 0, s>>>(ka);                     \
   } while (0)
-      if (g.a_kmajor && g.b_kmajor) SLT_DL_GO(true, true);
-      else if (g.a_kmajor) SLT_DL_GO(true, false);
-      else if (g.b_kmajor) SLT_DL_GO(false, true);
-      else SLT_DL_GO(false, false);
+      // Larger block tiles stage fewer bytes per FLOP (the copies feeding LDS
+      // are the limit at 128 x 128): 256 x 128 (or 128 x 256) when the grid
+      // holds at least 1.5 rounds of two such blocks per CU and K is not split
+      // (at fewer tiles the last round leaves CUs idle and 128 x 128 is faster).
+      int fm = 4, fn = 4;
+      if (!split && g.a_kmajor && SLT_GEMM_BIG) {
+        auto ntiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
+        if (g.M >= g.N && ntiles(256, 128) >= 768) fm = 8;
+        else if (g.b_kmajor && ntiles(128, 256) >= 768) fn = 8;
+      }
+      if (fm != 4 || fn != 4) {
+        ka.tiles_n = (g.N + 32 * fn - 1) / (32 * fn);
+        ka.tiles = ((g.M + 32 * fm - 1) / (32 * fm)) * ka.tiles_n;
+        grid = dim3(ka.tiles, 1, 1);
+      }
+      if (g.a_kmajor && g.b_kmajor) {
+        if (fm == 8) SLT_DL_GO(true, true, 8, 4);
+        else if (fn == 8) SLT_DL_GO(true, true, 4, 8);
+        else SLT_DL_GO(true, true, 4, 4);
+      } else if (g.a_kmajor) {
+        if (fm == 8) SLT_DL_GO(true, false, 8, 4);
+        else SLT_DL_GO(true, false, 4, 4);
+      } else if (g.b_kmajor) {
+        SLT_DL_GO(false, true, 4, 4);
+      } else {
+        SLT_DL_GO(false, false, 4, 4);
+      }
 #undef SLT_DL_GO
       return finish<TO>(g, split, splits, s);
     }

@@ -108,6 +108,17 @@ def test_gemm_direct_lds_path(B, a_k, b_k, outd):
     gemm_case(B, rng, 264, 136, 4096, a_k, b_k, BF16, outd, ws=True, resid=True)
 
 
+@pytest.mark.parametrize("a_k,b_k,M,N", [(1, 1, 12296, 4000), (1, 1, 4000, 12296), (1, 0, 12296, 4000)])
+def test_gemm_big_tiles(B, a_k, b_k, M, N):
+    # grids with enough 256 x 128 (128 x 256) tiles take the larger block
+    # tile; ragged M and N, 1..5 k-steps, residual; sampled rows
+    rng = np.random.default_rng(6)
+    for K in (32, 96, 160):
+        gemm_case(B, rng, M, N, K, a_k, b_k, BF16, BF16, sample=40)
+    gemm_case(B, rng, M, N, 64, a_k, b_k, BF16, BF16, resid=True, sample=40)
+    gemm_case(B, rng, M, N, 64, a_k, b_k, BF16, F32, sample=40)
+
+
 def test_gemm_zero_k_gives_residual_or_zero(B):
     rng = np.random.default_rng(2)
     gemm_case(B, rng, 17, 9, 0, 1, 1, F32, F32)
