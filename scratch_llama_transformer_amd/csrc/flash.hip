@@ -7,7 +7,9 @@
 // Work split:
 //  * fl_prep_k rotates q and k once (RoPE, fp32) and stores each rotated
 //    value as a bf16 pair hi + lo (lo = bf16(x - hi)) in head-major copies
-//    [B][heads][T][64], zero-padded to 64 dims.  The attention kernels then
+//    [B][heads][T][64], zero-padded to 64 dims; the query copy also carries
+//    the factor log2(e)/sqrt(d), so that q.k comes out as the score in base-2
+//    units the softmax exponentiates.  The attention kernels then
 //    only copy tiles: every tile (64 rows x 64 dims, 8 KiB) goes HBM -> LDS
 //    with global_load_lds_dwordx4, double-buffered, no register staging.
 //  * MFMA v_mfma_f32_16x16x32_bf16: operand A lane (g = l/16, i = l%16)
@@ -62,6 +64,15 @@ __device__ __forceinline__ f32x4 mma(const u32x4& a, const u32x4& b, f32x4 c) {
 __device__ __forceinline__ u32x4 cat(const u32x2& lo, const u32x2& hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float bf_hi(float x) { return __uint_as_float((uint32_t)f32_to_bf16_bits(x) << 16); }
+
+// Work item of this block: consecutive block ids go round-robin to the 8
+// XCDs, so the id is remapped to give each XCD one contiguous range of work
+// items -- the tiles of one (batch, head) then share that XCD's L2.
+__device__ __forceinline__ int fl_work_item() {
+  const int n = gridDim.x, id = blockIdx.x;
+  const int q = n >> 3, r = n & 7, x = id & 7;
+  return x * q + min(x, r) + (id >> 3);
+}
 
 // chunk position of logical chunk c in row r of a tile
 __device__ __forceinline__ int fsw(int r) { return 2 * ((r >> 1) & 3); }
@@ -159,6 +170,13 @@ __device__ __forceinline__ void rd_cols(unsigned base, const FlOff& o, u32x4 (&f
   rd_cols16(base + o.col[0], base + o.col[1], base + o.col[2], base + o.col[3], f);
 }
 
+// (x, y) -> bf16 pairs hi = (bf16(x), bf16(y)) and lo = (bf16(x - hi.x),
+// bf16(y - hi.y)): two conversions, two subtractions.
+__device__ __forceinline__ void split2(float x, float y, uint32_t& hi, uint32_t& lo) {
+  hi = f32x2_to_bf16x2_bits(x, y);
+  lo = f32x2_to_bf16x2_bits(x - __uint_as_float(hi << 16), y - __uint_as_float(hi & 0xffff0000u));
+}
+
 // Four probabilities (or gradients) of two neighbouring 16-row results in
 // the k order the transposed reads use.
 __device__ __forceinline__ u32x4 pack_k(const float (&x)[4], const float (&y)[4]) {
@@ -166,14 +184,13 @@ __device__ __forceinline__ u32x4 pack_k(const float (&x)[4], const float (&y)[4]
                f32x2_to_bf16x2_bits(y[2], y[3])};
 }
 __device__ __forceinline__ void pack_k_hilo(const float (&x)[4], const float (&y)[4], u32x4& hi, u32x4& lo) {
-  float xl[4], yl[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    xl[r] = x[r] - bf_hi(x[r]);
-    yl[r] = y[r] - bf_hi(y[r]);
-  }
-  hi = pack_k(x, y);
-  lo = pack_k(xl, yl);
+  uint32_t h[4], l[4];
+  split2(x[0], x[1], h[0], l[0]);
+  split2(x[2], x[3], h[1], l[1]);
+  split2(y[0], y[1], h[2], l[2]);
+  split2(y[2], y[3], h[3], l[3]);
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
 struct FlArgs {
@@ -198,17 +215,18 @@ struct FlArgs {
 // 16-byte stores; otherwise element by element.
 // ---------------------------------------------------------------------------
 template <bool VEC>
-__global__ __launch_bounds__(256) void fl_prep_k(const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ k,
+__global__ __launch_bounds__(128) void fl_prep_k(const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ k,
                                                  int64_t ldk, bf16* qh, bf16* ql, bf16* kh, bf16* kl, int B, int T,
-                                                 int H, int Hkv, int d, int R, int mode, const float* cs) {
+                                                 int H, int Hkv, int d, int R, int mode, const float* cs,
+                                                 float qscale) {
+  // grid (B T, ceil(8 (H + Hkv) / 128)): one token per block row, one
+  // (head slot, 8-dim chunk) per thread
   const int slots = H + Hkv;
-  const int64_t total = (int64_t)B * T * slots * 8;
-  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int c = idx & 7;
-    const int64_t rest = idx >> 3;
-    const int slot = (int)(rest % slots);
-    const int64_t bt = rest / slots;
+  const int j = blockIdx.y * blockDim.x + threadIdx.x;
+  if (j < slots * 8) {
+    const int c = j & 7;
+    const int slot = j >> 3;
+    const int64_t bt = blockIdx.x;
     const int t = (int)(bt % T), b = (int)(bt / T);
     const bool isq = slot < H;
     const int hd = isq ? slot : slot - H;
@@ -283,11 +301,12 @@ __global__ __launch_bounds__(256) void fl_prep_k(const bf16* __restrict__ q, int
           x[e] = v;
         }
       }
+      if (isq) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hw[e] = f32x2_to_bf16x2_bits(x[2 * e], x[2 * e + 1]);
-        lw[e] = f32x2_to_bf16x2_bits(x[2 * e] - bf_hi(x[2 * e]), x[2 * e + 1] - bf_hi(x[2 * e + 1]));
+        for (int e = 0; e < 8; ++e) x[e] *= qscale;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split2(x[2 * e], x[2 * e + 1], hw[e], lw[e]);
     }
     *reinterpret_cast<uint4*>(dh) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     *reinterpret_cast<uint4*>(dl) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
@@ -295,20 +314,21 @@ __global__ __launch_bounds__(256) void fl_prep_k(const bf16* __restrict__ q, int
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  grid (ceil(T/64), H, B).  Wave w owns queries q0 + 16w + i; per
+// Forward.  ceil(T/64) H B workgroups, one per (query tile, head, batch).  Wave w owns queries q0 + 16w + i; per
 // key tile: S^T = K Q^T (hi/lo), online softmax in base 2, O^T += V^T P^T.
 // LDS stage: [K hi | K lo | V], two stages.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fl_fwd_k(FlArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][3 * FTB];
-  const int b = blockIdx.z, h = blockIdx.y, qt = blockIdx.x, q0 = qt * FR;
-  const int T = a.T, kvh = h / (a.H / a.Hkv);
+  const int T = a.T, ntq = (T + FR - 1) / FR;
+  const int w = fl_work_item();
+  const int qt = ntq - 1 - w % ntq, h = (w / ntq) % a.H, b = w / (ntq * a.H);  // longest rows first
+  const int q0 = qt * FR, kvh = h / (a.H / a.Hkv);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int qi = q0 + wave * 16 + (lane & 15);
   const int qc = min(qi, T - 1);
   const int nch = a.d / 8;
-  const float sc = kLog2e / sqrtf((float)a.d);
   const FlOff off(lane);
 
   const int64_t qrow = ((int64_t)(b * a.H + h) * T + qc) * FD;
@@ -358,12 +378,14 @@ __global__ __launch_bounds__(256) void fl_fwd_k(FlArgs a) {
         st = mma(kf[1][t][s], qh[s], st);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = st[r] * sc;
-        if (kt == qt && k0 + 16 * t + 4 * g + r > qi) v = -INFINITY;
-        sv[t][r] = v;
-        tmax = fmaxf(tmax, v);
+      for (int r = 0; r < 4; ++r) sv[t][r] = st[r];
+      if (kt == qt) {  // the diagonal tile: keys after the query are masked
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (k0 + 16 * t + 4 * g + r > qi) sv[t][r] = -INFINITY;
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sv[t][r]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
@@ -464,21 +486,22 @@ __device__ __forceinline__ void fl_stage_acc(float* F, int row, int g, const f32
 }
 
 // ---------------------------------------------------------------------------
-// dQ (and D).  grid (ceil(T/64), H, B).  Wave w owns queries q0 + 16w + i:
+// dQ (and D).  One workgroup per (query tile, head, batch).  Wave w owns queries q0 + 16w + i:
 // D = dO.(O + ores); per key tile: S^T = K Q^T, P^T = exp2(S^T - lse),
 // dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (hi/lo).
 // LDS stage: [K hi | K lo | V], two stages.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][3 * FTB];
-  const int b = blockIdx.z, h = blockIdx.y, qt = blockIdx.x, q0 = qt * FR;
-  const int T = a.T, kvh = h / (a.H / a.Hkv);
+  const int T = a.T, ntq = (T + FR - 1) / FR;
+  const int w = fl_work_item();
+  const int qt = ntq - 1 - w % ntq, h = (w / ntq) % a.H, b = w / (ntq * a.H);
+  const int q0 = qt * FR, kvh = h / (a.H / a.Hkv);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int qi = q0 + wave * 16 + (lane & 15);
   const int qc = min(qi, T - 1);
   const int nch = a.d / 8;
-  const float sc = kLog2e / sqrtf((float)a.d);
   const FlOff off(lane);
 
   const int64_t qrow = ((int64_t)(b * a.H + h) * T + qc) * FD;
@@ -550,9 +573,11 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
           st = mma(kf[1][t][s], qh[s], st);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool live = !(kt == qt && k0 + 16 * t + 4 * g + r > qi);
-          p[t][r] = live ? ex2(st[r] * sc - lse2) : 0.f;
+        for (int r = 0; r < 4; ++r) p[t][r] = ex2(st[r] - lse2);
+        if (kt == qt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (k0 + 16 * t + 4 * g + r > qi) p[t][r] = 0.f;
         }
       }
     }
@@ -600,7 +625,7 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  grid (ceil(T/64), Hkv, B).  Wave w owns keys k0 + 16w + i and
+// dK, dV.  One workgroup per (key tile, KV head, batch).  Wave w owns keys k0 + 16w + i and
 // loops over the query heads of its KV head and the query tiles at or after
 // its key tile: S = Q K^T (hi/lo), P = exp2(S - lse), dP = dO V^T,
 // dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS (hi/lo).
@@ -608,14 +633,15 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][3 * FTB];
-  const int b = blockIdx.z, kvh = blockIdx.y, kt = blockIdx.x, k0 = kt * FR;
-  const int T = a.T, G = a.H / a.Hkv;
+  const int T = a.T, G = a.H / a.Hkv, ntk = (T + FR - 1) / FR;
+  const int w = fl_work_item();
+  const int kt = w % ntk, kvh = (w / ntk) % a.Hkv, b = w / (ntk * a.Hkv);  // earliest keys (most queries) first
+  const int k0 = kt * FR;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int ki = k0 + wave * 16 + (lane & 15);
   const int kc = min(ki, T - 1);
   const int nch = a.d / 8;
-  const float sc = kLog2e / sqrtf((float)a.d);
   const FlOff off(lane);
 
   const int64_t krow = ((int64_t)(b * a.Hkv + kvh) * T + kc) * FD;
@@ -651,17 +677,29 @@ __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
   // needs, loaded one step ahead (before that step's tile copies, so that
   // waiting for them never waits for the copies issued after them)
   float ln[4][4], dn[4][4];
+  // rows (b, h) of lse and D start 16-byte aligned when T % 4 == 0
+  const bool vec4 = (T & 3) == 0 && (reinterpret_cast<uintptr_t>(a.lse_in) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(a.delta) & 15) == 0;
   auto rows_of = [&](int n) {
     const int hh = kvh * G + n / per, qt = kt + n % per;
     const int64_t sb = ((int64_t)b * a.H + hh) * T;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      const int q4 = qt * FR + 16 * t + 4 * g;
+      if (vec4 && q4 + 3 < T) {
+        const float4 l4 = *reinterpret_cast<const float4*>(a.lse_in + sb + q4);
+        const float4 d4 = *reinterpret_cast<const float4*>(a.delta + sb + q4);
+        ln[t][0] = l4.x * kLog2e; ln[t][1] = l4.y * kLog2e; ln[t][2] = l4.z * kLog2e; ln[t][3] = l4.w * kLog2e;
+        dn[t][0] = d4.x; dn[t][1] = d4.y; dn[t][2] = d4.z; dn[t][3] = d4.w;
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = min(qt * FR + 16 * t + 4 * g + r, T - 1);
-        ln[t][r] = a.lse_in[sb + qq] * kLog2e;
-        dn[t][r] = a.delta[sb + qq];
+        for (int r = 0; r < 4; ++r) {
+          const int qq = min(q4 + r, T - 1);
+          ln[t][r] = a.lse_in[sb + qq] * kLog2e;
+          dn[t][r] = a.delta[sb + qq];
+        }
       }
+    }
   };
   rows_of(0);
   issue(0, lds[0]);
@@ -699,10 +737,13 @@ __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
           st = mma(qf[1][t][s], kh[s], st);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qq = q0 + 16 * t + 4 * g + r;
-          const bool live = qq < T && !(qt == kt && ki > qq);
-          p[t][r] = live ? ex2(st[r] * sc - lc[t][r]) : 0.f;
+        for (int r = 0; r < 4; ++r) p[t][r] = ex2(st[r] - lc[t][r]);
+        if (qt == kt || q0 + FR > T) {  // the diagonal tile, or rows past T
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int qq = q0 + 16 * t + 4 * g + r;
+            if (qq >= T || ki > qq) p[t][r] = 0.f;
+          }
         }
       }
     }
@@ -762,8 +803,9 @@ __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
   fl_stage_acc(F, row, g, dka);
   fl_stage_acc(F2, row, g, dva);
   lds_barrier();
-  fl_store_rows(F, 1.0f / sqrtf((float)a.d), a.dk + (int64_t)b * T * a.lddk + (int64_t)kvh * a.d, a.lddk, k0, T, a.d,
-                a.R, a.rope_mode, a.cs);
+  // the query copy carries log2(e) / sqrt(d): dK = dS^T Q / sqrt(d) = ln(2) dS^T Q'
+  fl_store_rows(F, kLn2, a.dk + (int64_t)b * T * a.lddk + (int64_t)kvh * a.d, a.lddk, k0, T, a.d, a.R, a.rope_mode,
+                a.cs);
   fl_store_rows(F2, 1.0f, a.dv + (int64_t)b * T * a.lddv + (int64_t)kvh * a.d, a.lddv, k0, T, a.d, 0, 0, nullptr);
 }
 
@@ -808,14 +850,14 @@ FlArgs to_fl(const AttnArgs& a) {
 }
 
 slt_status prep(const AttnArgs& a, const FlArgs& f, hipStream_t s) {
-  const int64_t items = (int64_t)a.B * a.T * (a.H + a.Hkv) * 8;
-  const int blocks = (int)std::min<int64_t>((items + 255) / 256, 16384);
+  const dim3 grid((unsigned)((int64_t)a.B * a.T), (unsigned)(((a.H + a.Hkv) * 8 + 127) / 128));
   const bool vec = al(a.q, 16) && al(a.k, 16) && a.ldq % 8 == 0 && a.ldk % 8 == 0 && (a.R == 0 || a.cs != nullptr) &&
                    (a.R == 0 || (a.rope_mode == SLT_ROPE_HALF ? (a.R / 2) % 8 == 0 : a.R % 8 == 0));
   auto* kern = vec ? fl_prep_k<true> : fl_prep_k<false>;
-  kern<<<blocks, 256, 0, s>>>(static_cast<const bf16*>(a.q), a.ldq, static_cast<const bf16*>(a.k), a.ldk,
+  kern<<<grid, 128, 0, s>>>(static_cast<const bf16*>(a.q), a.ldq, static_cast<const bf16*>(a.k), a.ldk,
                                    const_cast<bf16*>(f.qh), const_cast<bf16*>(f.ql), const_cast<bf16*>(f.kh),
-                                   const_cast<bf16*>(f.kl), a.B, a.T, a.H, a.Hkv, a.d, a.R, a.rope_mode, a.cs);
+                                   const_cast<bf16*>(f.kl), a.B, a.T, a.H, a.Hkv, a.d, a.R, a.rope_mode, a.cs,
+                                   kLog2e / sqrtf((float)a.d));
   return check_launch("attention rope prep");
 }
 
@@ -840,8 +882,8 @@ slt_status flash_fwd(const AttnArgs& a, hipStream_t s) {
     const slt_status st = prep(a, f, s);
     if (st != SLT_OK) return st;
   }
-  dim3 grid((a.T + FR - 1) / FR, a.H, a.B);
-  fl_fwd_k<<<grid, 256, 0, s>>>(f);
+  const int ntq = (a.T + FR - 1) / FR;
+  fl_fwd_k<<<ntq * a.H * a.B, 256, 0, s>>>(f);
   return check_launch("attention forward");
 }
 
@@ -851,12 +893,11 @@ slt_status flash_bwd(const AttnArgs& a, hipStream_t s) {
     const slt_status st = prep(a, f, s);
     if (st != SLT_OK) return st;
   }
-  dim3 gq((a.T + FR - 1) / FR, a.H, a.B);
-  fl_dq_k<<<gq, 256, 0, s>>>(f);
+  const int nt = (a.T + FR - 1) / FR;
+  fl_dq_k<<<nt * a.H * a.B, 256, 0, s>>>(f);
   slt_status st = check_launch("attention backward (dq)");
   if (st != SLT_OK) return st;
-  dim3 gk((a.T + FR - 1) / FR, a.Hkv, a.B);
-  fl_dkdv_k<<<gk, 256, 0, s>>>(f);
+  fl_dkdv_k<<<nt * a.Hkv * a.B, 256, 0, s>>>(f);
   return check_launch("attention backward (dk, dv)");
 }
 
