@@ -45,7 +45,7 @@ __all__ = [
     "rope_tables", "rope_apply",
     "attention_fwd", "attention_bwd",
     "swiglu_fwd", "swiglu_bwd", "gelu_fwd", "gelu_bwd",
-    "cross_entropy", "adamw",
+    "cross_entropy", "adamw", "grad_norm", "clip_scale",
     "forward", "backward", "train_step", "decay_mask_like",
 ]
 
@@ -356,6 +356,29 @@ def adamw(theta, g, m, v, t, lr, beta1, beta2, eps, wd, decay=None):
     return theta, m, v
 
 
+def grad_norm(grads, kind="l2"):
+    """Global norm over every gradient element of every tensor: the L2 norm
+    (MicroGPT in Rust, "Gradient Clipping"; Transformer in Rust, "Features":
+    clipping by global norm) or the L-infinity norm max |g| (randyGPT,
+    "Training (Metal GPU path)")."""
+    flat = np.concatenate([np.asarray(g, np.float64).ravel() for g in grads.values()])
+    if flat.size == 0:
+        return 0.0
+    if kind == "l2":
+        return float(np.sqrt(np.sum(flat * flat)))
+    if kind == "linf":
+        return float(np.max(np.abs(flat)))
+    raise ValueError(kind)
+
+
+def clip_scale(norm, max_norm):
+    """MicroGPT in Rust, "Gradient Clipping": max_norm / norm when the norm
+    exceeds max_norm, else 1.  Reading: randyGPT's "L-infinity norm clipped
+    at 1.0" is the same rule with the L-infinity norm (a scale, not an
+    element-wise clamp)."""
+    return max_norm / norm if norm > max_norm else 1.0
+
+
 def decay_mask_like(params):
     """Reading: the pages exclude no tensor from weight decay, so every
     element decays."""
@@ -511,11 +534,18 @@ def backward(cfg, cache):
 
 
 def train_step(cfg, params, tokens, t=1, m=None, v=None, decay=None,
-               lr=None, beta1=None, beta2=None, adam_eps=None, wd=None, jitter=0.0, seed=0):
-    """forward -> backward -> AdamW on every tensor.  m and v default to zero
-    (first step).  Returns dict(loss, grads, params, m, v)."""
+               lr=None, beta1=None, beta2=None, adam_eps=None, wd=None, jitter=0.0, seed=0, clip=None):
+    """forward -> backward -> (optional clipping) -> AdamW on every tensor.
+    m and v default to zero (first step).  clip: None or (kind, max_norm):
+    every gradient is multiplied by clip_scale(grad_norm(grads, kind),
+    max_norm) before AdamW sees it.  Returns dict(loss, grads, params, m, v,
+    grad_norm, clip_scale); grads are the unclipped gradients."""
     loss, cache = forward(cfg, params, tokens, jitter, seed)
     grads = backward(cfg, cache)
+    gn, cscale = None, 1.0
+    if clip is not None:
+        gn = grad_norm(grads, clip[0])
+        cscale = clip_scale(gn, clip[1])
     lr = cfg.lr if lr is None else lr
     beta1 = cfg.beta1 if beta1 is None else beta1
     beta2 = cfg.beta2 if beta2 is None else beta2
@@ -527,5 +557,5 @@ def train_step(cfg, params, tokens, t=1, m=None, v=None, decay=None,
         v0 = np.zeros_like(np.asarray(th, np.float64)) if v is None else v[name]
         dm = None if decay is None else decay[name]
         new_p[name], new_m[name], new_v[name] = adamw(
-            th, grads[name], m0, v0, t, lr, beta1, beta2, adam_eps, wd, dm)
-    return dict(loss=loss, grads=grads, params=new_p, m=new_m, v=new_v)
+            th, cscale * np.asarray(grads[name], np.float64), m0, v0, t, lr, beta1, beta2, adam_eps, wd, dm)
+    return dict(loss=loss, grads=grads, params=new_p, m=new_m, v=new_v, grad_norm=gn, clip_scale=cscale)

@@ -611,3 +611,46 @@ def test_bf16_forward_close_to_exact():
     gb, gf = O.backward(cfg, cb), O.backward(cfg.with_(act="f32"), cf)
     for k in gf:
         assert np.linalg.norm(gb[k] - gf[k]) <= 0.05 * np.linalg.norm(gf[k]) + 1e-12, k
+
+
+# ---------------------------------------------------------------------------
+# Global-norm gradient clipping (MicroGPT in Rust, "Gradient Clipping";
+# Transformer in Rust, "Features"; randyGPT, "Training (Metal GPU path)")
+# ---------------------------------------------------------------------------
+def test_grad_norm_closed_forms():
+    g = {"a": np.array([[3.0, 0.0]]), "b": np.array([-4.0]), "c": np.zeros((2, 2))}
+    assert O.grad_norm(g, "l2") == 5.0            # 3-4-5 across tensors: the norm is global
+    assert O.grad_norm(g, "linf") == 4.0          # largest magnitude, sign ignored
+    assert O.grad_norm({"z": np.zeros(3)}, "l2") == 0.0
+    assert O.clip_scale(5.0, 1.0) == 0.2
+    assert O.clip_scale(0.5, 1.0) == 1.0          # below the threshold: untouched
+    assert O.clip_scale(1.0, 1.0) == 1.0          # at the threshold: untouched
+    rng = np.random.default_rng(40)
+    g = {k: rng.standard_normal(s) * 3 for k, s in [("x", (7, 5)), ("y", (11,))]}
+    for kind in ("l2", "linf"):
+        s_ = O.clip_scale(O.grad_norm(g, kind), 0.75)
+        clipped = {k: s_ * v for k, v in g.items()}
+        assert abs(O.grad_norm(clipped, kind) - 0.75) < 1e-15   # clipped to exactly max_norm
+
+
+def test_train_step_clipping_scales_first_moments():
+    w = W.get_config(1)
+    params = W.make_params(w, 41)
+    tokens = W.make_tokens(w, 41)
+    base = O.train_step(w, params, tokens)
+    n2 = O.grad_norm(base["grads"], "l2")
+    # a threshold above the norm changes nothing
+    same = O.train_step(w, params, tokens, clip=("l2", 2.0 * n2))
+    assert same["clip_scale"] == 1.0
+    for k in params:
+        assert np.array_equal(same["params"][k], base["params"][k])
+    # below it, AdamW sees s g: m1 = 0.1 s g, v1 = 0.001 s^2 g^2 (t = 1)
+    for kind in ("l2", "linf"):
+        nrm = O.grad_norm(base["grads"], kind)
+        out = O.train_step(w, params, tokens, clip=(kind, 0.25 * nrm))
+        s_ = out["clip_scale"]
+        assert abs(s_ - 0.25) < 1e-15 and out["grad_norm"] == nrm
+        for k in params:
+            g = base["grads"][k]
+            np.testing.assert_allclose(out["m"][k], 0.1 * s_ * g, rtol=1e-14, atol=1e-300)
+            np.testing.assert_allclose(out["v"][k], 0.001 * s_ * s_ * g * g, rtol=1e-14, atol=1e-300)
