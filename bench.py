@@ -158,6 +158,28 @@ def kernel_classes(w, ts, torch, reps):
         out[name] = {"ms_per_step": sec * 1e3, "launches": nl, "tflops": fl / sec / 1e12,
                      "frac_of_peak": fl / sec / 1e12 / peak, "flops": fl, "avg_launch_us": sec * 1e6 / nl,
                      "bound": "mfma", "peak": peak}
+    del qkv, o, ores, g, dqkv, aws
+    # HBM-bound optimizer-side kernels over the flat parameter buffer: AdamW
+    # (theta, g, m, v read; theta, m, v written; the bf16 copy written) and
+    # the global gradient norm used for clipping (g read once)
+    _, n = B.slt_param_layout(B.make_config(w))
+    th = torch.empty(n, device="cuda").normal_(0, 0.02)
+    gr = torch.empty(n, device="cuda").normal_(0, 1e-3)
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    sh = torch.empty(n, dtype=torch.int16, device="cuda") if dt == B.BF16 else None
+    cws = torch.empty(B.slt_clip_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    nrm = torch.empty(2, device="cuda")
+    byt_adamw = n * (30 if sh is not None else 28)
+    hbm = PEAK["hbm"]
+    for name, fn, byt, nl in [
+        ("adamw", lambda: B.slt_adamw_step(n, th, sh, gr, m, v, 1, 1e-3, 0.9, 0.999, 1e-8, 0.1), byt_adamw, 1),
+        ("grad_norm", lambda: B.slt_clip_grad_norm(n, gr, B.NORM_L2, 1.0, nrm, nrm.data_ptr() + 4, cws), 4 * n, 1),
+    ]:
+        sec = time_block(fn, reps, torch)
+        gbs = byt / sec / 1e9
+        out[name] = {"ms_per_step": sec * 1e3, "launches": nl, "gbps": gbs, "frac_of_peak": gbs / hbm,
+                     "bytes": byt, "avg_launch_us": sec * 1e6 / nl, "bound": "hbm", "peak": hbm}
     return out
 
 
@@ -280,7 +302,7 @@ def main():
     if not args.no_breakdown:
         cl = kernel_classes(w, None, torch, args.kernel_reps)
         out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
-                              if kk in ("ms_per_step", "launches", "tflops", "frac_of_peak", "avg_launch_us")}
+                              if kk in ("ms_per_step", "launches", "tflops", "gbps", "frac_of_peak", "avg_launch_us")}
                           for k, v in cl.items()}
         # the dominant kernel of the step (largest total time in the kernel
         # trace): the forward-projection GEMM, every launch of which is

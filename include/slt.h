@@ -59,6 +59,7 @@ typedef enum {
 typedef enum { SLT_F32 = 0, SLT_BF16 = 1 } slt_dtype;
 typedef enum { SLT_ROPE_HALF = 0, SLT_ROPE_PAIRS = 1 } slt_rope_mode;
 typedef enum { SLT_BLOCK_LLAMA = 0, SLT_BLOCK_PARALLEL = 1 } slt_block;
+typedef enum { SLT_NORM_L2 = 0, SLT_NORM_LINF = 1 } slt_norm_kind;
 
 /* Model and workload shape.  d = C / H is the head dimension. */
 typedef struct {
@@ -150,14 +151,31 @@ slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t
 
 /* AdamW on n flat fp32 elements at step t >= 1 (Hephaistos, "Architecture at a
  * glance"; strata, "AdamW (decoupled decay, bias-corrected)"):
- *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   g = s grads;  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
  *   theta -= lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd theta)
  * with wd applied where decay_mask[i] != 0 (all elements when decay_mask is
- * NULL).  When shadow is not NULL it receives bf16(theta).  master, m, v are
- * updated in place. */
+ * NULL).  s = *grad_scale, a device fp32 scalar such as the factor written by
+ * slt_clip_grad_norm, or 1 when grad_scale is NULL.  When shadow is not NULL
+ * it receives bf16(theta).  master, m, v are updated in place; grads is not
+ * modified.  Buffers 16-byte aligned (shadow 8, decay_mask 4). */
 slt_status slt_adamw_step(int64_t n, float* master, uint16_t* shadow, const float* grads,
                           float* m, float* v, int64_t t, float lr, float beta1, float beta2,
-                          float eps, float wd, const uint8_t* decay_mask, void* stream);
+                          float eps, float wd, const uint8_t* decay_mask, const float* grad_scale,
+                          void* stream);
+
+/* Global gradient norm and clipping factor (MicroGPT in Rust, "Gradient
+ * Clipping"; Transformer in Rust, "Features": clipping by global norm;
+ * randyGPT, "Training (Metal GPU path)": the L-infinity variant).  Over the n
+ * fp32 values of grads (the flat gradient buffer): kind SLT_NORM_L2 gives
+ * sqrt(sum g^2), SLT_NORM_LINF gives max |g|; the sums are formed in float64
+ * in a fixed order (bitwise reproducible).  Writes, to device memory, *norm
+ * (if not NULL) and *scale = max_norm / norm when norm > max_norm, else 1
+ * (if not NULL) -- the factor slt_adamw_step's grad_scale applies.  No host
+ * synchronisation.  workspace: slt_clip_workspace_bytes() bytes of device
+ * memory, 16-byte aligned, scratch for the call.  grads 16-byte aligned. */
+int64_t slt_clip_workspace_bytes(void);
+slt_status slt_clip_grad_norm(int64_t n, const float* grads, int32_t kind, float max_norm, float* norm,
+                              float* scale, void* workspace, void* stream);
 
 /* ------------------------------------------------------------------------
  * Per-op calls.  dtype is the storage type of the activation operands

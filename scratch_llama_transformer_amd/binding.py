@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libslt.so")
 F32, BF16 = 0, 1
 ROPE_HALF, ROPE_PAIRS = 0, 1
 BLOCK_LLAMA, BLOCK_PARALLEL = 0, 1
+NORM_L2, NORM_LINF = 0, 1
 STATUS = {0: "SLT_OK", 1: "SLT_EINVAL", 2: "SLT_EUNSUPPORTED", 3: "SLT_EHIP"}
 
 
@@ -53,7 +54,9 @@ SIGNATURES = {
     "slt_cast_bf16": (_I32, [_P, _P, _I64, _P]),
     "slt_forward_loss": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _P]),
     "slt_backward": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _P]),
-    "slt_adamw_step": (_I32, [_I64, _P, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P]),
+    "slt_adamw_step": (_I32, [_I64, _P, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P, _P]),
+    "slt_clip_workspace_bytes": (_I64, []),
+    "slt_clip_grad_norm": (_I32, [_I64, _P, _I32, _F, _P, _P, _P, _P]),
     "slt_gemm": (_I32, [_I32, _I32, _I32, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _P, _I64,
                         _I32, _I32, _P, _I64, _P]),
     "slt_embedding_fwd": (_I32, [_P, _I32, _I32, _I64, _P, _P, _I32, _I32, _I32, _P]),
@@ -196,10 +199,20 @@ def slt_backward(cfg, params, tokens, acts, scratch, grads, stream=None):
                                                _ptr(scratch), _ptr(grads), _stream(stream)))
 
 
-def slt_adamw_step(n, master, shadow, grads, m, v, t, lr, beta1, beta2, eps, wd, decay_mask=None, stream=None):
+def slt_adamw_step(n, master, shadow, grads, m, v, t, lr, beta1, beta2, eps, wd, decay_mask=None, grad_scale=None,
+                   stream=None):
     _check("slt_adamw_step", load().slt_adamw_step(n, _ptr(master), _ptr(shadow), _ptr(grads), _ptr(m), _ptr(v),
-                                                   t, lr, beta1, beta2, eps, wd, _ptr(decay_mask),
+                                                   t, lr, beta1, beta2, eps, wd, _ptr(decay_mask), _ptr(grad_scale),
                                                    _stream(stream)))
+
+
+def slt_clip_workspace_bytes() -> int:
+    return int(load().slt_clip_workspace_bytes())
+
+
+def slt_clip_grad_norm(n, grads, kind, max_norm, norm, scale, workspace, stream=None):
+    _check("slt_clip_grad_norm", load().slt_clip_grad_norm(n, _ptr(grads), kind, max_norm, _ptr(norm), _ptr(scale),
+                                                           _ptr(workspace), _stream(stream)))
 
 
 def slt_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, ldc, R, ldr, in_dtype, out_dtype,

@@ -492,7 +492,7 @@ slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t
 
 slt_status slt_adamw_step(int64_t n, float* master, uint16_t* shadow, const float* grads, float* m, float* v,
                           int64_t t, float lr, float beta1, float beta2, float eps, float wd,
-                          const uint8_t* decay_mask, void* stream) {
+                          const uint8_t* decay_mask, const float* grad_scale, void* stream) {
   if (n < 0) return fail(SLT_EINVAL, "adamw: n < 0");
   if (n == 0) return SLT_OK;
   if (!master || !grads || !m || !v) return fail(SLT_EINVAL, "adamw: NULL pointer");
@@ -503,7 +503,22 @@ slt_status slt_adamw_step(int64_t n, float* master, uint16_t* shadow, const floa
   if (!al16(master) || !al16(grads) || !al16(m) || !al16(v) || (shadow && reinterpret_cast<uintptr_t>(shadow) % 8) ||
       (decay_mask && reinterpret_cast<uintptr_t>(decay_mask) % 4))
     return fail(SLT_EINVAL, "adamw: buffers must be 16-byte aligned (shadow 8, mask 4)");
-  return launch_adamw(n, master, shadow, grads, m, v, t, lr, beta1, beta2, eps, wd, decay_mask, as_stream(stream));
+  if (grad_scale && reinterpret_cast<uintptr_t>(grad_scale) % 4) return fail(SLT_EINVAL, "adamw: misaligned grad_scale");
+  return launch_adamw(n, master, shadow, grads, m, v, t, lr, beta1, beta2, eps, wd, decay_mask, grad_scale,
+                      as_stream(stream));
+}
+
+int64_t slt_clip_workspace_bytes(void) { return grad_norm_ws(); }
+
+slt_status slt_clip_grad_norm(int64_t n, const float* grads, int32_t kind, float max_norm, float* norm, float* scale,
+                              void* workspace, void* stream) {
+  if (n < 0) return fail(SLT_EINVAL, "clip_grad_norm: n < 0");
+  if (kind != SLT_NORM_L2 && kind != SLT_NORM_LINF) return fail(SLT_EINVAL, "clip_grad_norm: bad kind");
+  if (!(max_norm > 0.f)) return fail(SLT_EINVAL, "clip_grad_norm: max_norm must be > 0");
+  if ((n > 0 && !grads) || !workspace) return fail(SLT_EINVAL, "clip_grad_norm: NULL pointer");
+  if (reinterpret_cast<uintptr_t>(grads) % 16 || reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(SLT_EINVAL, "clip_grad_norm: grads and workspace must be 16-byte aligned");
+  return launch_grad_norm(n, grads, kind, max_norm, norm, scale, workspace, as_stream(stream));
 }
 
 slt_status slt_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_kmajor, const void* B,

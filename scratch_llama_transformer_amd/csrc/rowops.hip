@@ -694,11 +694,14 @@ __device__ __forceinline__ void adamw_one(float& th, float g, float& m, float& v
 __global__ __launch_bounds__(256) void adamw_k(int64_t n, float* __restrict__ th, uint16_t* __restrict__ shadow,
                                                const float* __restrict__ g, float* __restrict__ m,
                                                float* __restrict__ v, float b1, float b2, float ib1, float ib2,
-                                               float lr, float eps, float wd, const uint8_t* __restrict__ mask) {
+                                               float lr, float eps, float wd, const uint8_t* __restrict__ mask,
+                                               const float* __restrict__ gscale) {
+  const float gs = gscale ? *gscale : 1.0f;  // gradient clipping factor (1: none)
   const int64_t n4 = n / 4;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
     float4 t4 = reinterpret_cast<float4*>(th)[i];
-    const float4 g4 = reinterpret_cast<const float4*>(g)[i];
+    float4 g4 = reinterpret_cast<const float4*>(g)[i];
+    g4.x *= gs; g4.y *= gs; g4.z *= gs; g4.w *= gs;
     float4 m4 = reinterpret_cast<float4*>(m)[i];
     float4 v4 = reinterpret_cast<float4*>(v)[i];
     float w[4] = {wd, wd, wd, wd};
@@ -724,9 +727,64 @@ __global__ __launch_bounds__(256) void adamw_k(int64_t n, float* __restrict__ th
   const int64_t i = n4 * 4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (blockIdx.x == 0 && i < n) {
     float t1 = th[i], m1 = m[i], v1 = v[i];
-    adamw_one(t1, g[i], m1, v1, b1, b2, ib1, ib2, lr, eps, (mask && !mask[i]) ? 0.f : wd);
+    adamw_one(t1, g[i] * gs, m1, v1, b1, b2, ib1, ib2, lr, eps, (mask && !mask[i]) ? 0.f : wd);
     th[i] = t1; m[i] = m1; v[i] = v1;
     if (shadow) shadow[i] = f32_to_bf16_bits(t1);
+  }
+}
+
+// Global gradient norm, two deterministic stages: a fixed grid of
+// kGnBlocks blocks each reduces a fixed strided share in double precision
+// (sum of squares, or max |g|) and writes one partial; one block reduces the
+// partials in a fixed tree and writes the norm and the clipping factor
+// (MicroGPT in Rust, "Gradient Clipping": max_norm / norm above max_norm,
+// else 1).
+constexpr int kGnBlocks = 1024;
+
+template <bool LINF>
+__global__ __launch_bounds__(256) void gnorm_partial_k(int64_t n, const float* __restrict__ g,
+                                                       double* __restrict__ part) {
+  double acc = 0.0;
+  const int64_t n4 = n / 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 x = reinterpret_cast<const float4*>(g)[i];
+    if (LINF) {
+      acc = fmax(acc, (double)fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    } else {
+      acc += (double)x.x * x.x + (double)x.y * x.y + (double)x.z * x.z + (double)x.w * x.w;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (int)(n - n4 * 4)) {
+    const double x = g[n4 * 4 + threadIdx.x];
+    acc = LINF ? fmax(acc, fabs(x)) : acc + x * x;
+  }
+  __shared__ double red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] = LINF ? fmax(red[threadIdx.x], red[threadIdx.x + w])
+                                                 : red[threadIdx.x] + red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+template <bool LINF>
+__global__ __launch_bounds__(1024) void gnorm_final_k(const double* __restrict__ part, float max_norm,
+                                                      float* norm_out, float* scale_out) {
+  __shared__ double red[1024];
+  red[threadIdx.x] = part[threadIdx.x];
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] = LINF ? fmax(red[threadIdx.x], red[threadIdx.x + w])
+                                                 : red[threadIdx.x] + red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double nrm = LINF ? red[0] : sqrt(red[0]);
+    if (norm_out) *norm_out = (float)nrm;
+    if (scale_out) *scale_out = nrm > (double)max_norm ? (float)((double)max_norm / nrm) : 1.0f;
   }
 }
 
@@ -1053,12 +1111,28 @@ slt_status launch_softmax_xent(void* z, int64_t ldz, const int32_t* tok, int B, 
 }
 
 slt_status launch_adamw(int64_t n, float* master, uint16_t* shadow, const float* g, float* m, float* v, int64_t t,
-                        float lr, float b1, float b2, float eps, float wd, const uint8_t* mask, hipStream_t s) {
+                        float lr, float b1, float b2, float eps, float wd, const uint8_t* mask, const float* gscale,
+                        hipStream_t s) {
   const double bc1 = 1.0 - pow((double)b1, (double)t);
   const double bc2 = 1.0 - pow((double)b2, (double)t);
   adamw_k<<<grid_for(n / 4 + 1, 256, 8192), 256, 0, s>>>(n, master, shadow, g, m, v, b1, b2, (float)(1.0 / bc1),
-                                                           (float)(1.0 / bc2), lr, eps, wd, mask);
+                                                           (float)(1.0 / bc2), lr, eps, wd, mask, gscale);
   return check_launch("adamw");
+}
+
+int64_t grad_norm_ws() { return kGnBlocks * (int64_t)sizeof(double); }
+
+slt_status launch_grad_norm(int64_t n, const float* g, int kind, float max_norm, float* norm, float* scale, void* ws,
+                            hipStream_t s) {
+  double* part = static_cast<double*>(ws);
+  if (kind == SLT_NORM_LINF) {
+    gnorm_partial_k<true><<<kGnBlocks, 256, 0, s>>>(n, g, part);
+    gnorm_final_k<true><<<1, 1024, 0, s>>>(part, max_norm, norm, scale);
+  } else {
+    gnorm_partial_k<false><<<kGnBlocks, 256, 0, s>>>(n, g, part);
+    gnorm_final_k<false><<<1, 1024, 0, s>>>(part, max_norm, norm, scale);
+  }
+  return check_launch("grad_norm");
 }
 
 slt_status launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s) {

@@ -116,7 +116,10 @@ slt_status launch_softmax_xent(void* z, int64_t ldz, const int32_t* tok, int B, 
                                int V, float* loss, float* lse, int dtype, void* ws, hipStream_t s);
 slt_status launch_adamw(int64_t n, float* master, uint16_t* shadow, const float* g, float* m,
                         float* v, int64_t t, float lr, float b1, float b2, float eps, float wd,
-                        const uint8_t* mask, hipStream_t s);
+                        const uint8_t* mask, const float* gscale, hipStream_t s);
+int64_t grad_norm_ws();
+slt_status launch_grad_norm(int64_t n, const float* g, int kind, float max_norm, float* norm, float* scale,
+                            void* ws, hipStream_t s);
 slt_status launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 slt_status launch_fill_f32(float* dst, float value, int64_t n, hipStream_t s);
 slt_status launch_model_init_range(float* dst, int64_t n, int64_t index0, uint64_t seed, float std,

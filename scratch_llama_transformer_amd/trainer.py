@@ -14,8 +14,11 @@ from . import binding as B
 
 
 class TrainStep:
-    def __init__(self, wcfg, params: dict | None = None, seed: int = 0, device: str = "cuda"):
+    def __init__(self, wcfg, params: dict | None = None, seed: int = 0, device: str = "cuda", clip=None):
+        """clip: None, or (kind, max_norm) with kind "l2" or "linf": the
+        gradient is scaled by the global-norm clipping factor before AdamW."""
         self.w = wcfg
+        self.clip = clip
         self.cfg = B.make_config(wcfg)
         B.slt_validate(self.cfg)
         self.layout, self.n = B.slt_param_layout(self.cfg)
@@ -36,6 +39,8 @@ class TrainStep:
         self.acts = torch.empty(act, dtype=torch.uint8, device=self.device)
         self.scratch = torch.empty(scr, dtype=torch.uint8, device=self.device)
         self.loss = torch.zeros(1, **f32)
+        self.gnorm = torch.zeros(2, **f32)  # [norm, clipping factor]
+        self.clip_ws = torch.empty(B.slt_clip_workspace_bytes(), dtype=torch.uint8, device=self.device)
         self.t = 0
         self.refresh_shadow()
 
@@ -69,11 +74,21 @@ class TrainStep:
     def backward(self, tokens: torch.Tensor) -> None:
         B.slt_backward(self.cfg, self.compute_params, tokens, self.acts, self.scratch, self.grads)
 
+    def clip_grads(self) -> None:
+        kind, max_norm = self.clip
+        B.slt_clip_grad_norm(self.n, self.grads, B.NORM_L2 if kind == "l2" else B.NORM_LINF, float(max_norm),
+                             self.gnorm, self.gnorm.data_ptr() + 4, self.clip_ws)
+
     def adamw(self, lr=None, wd=None) -> None:
         self.t += 1
         w = self.w
+        scale = None
+        if self.clip is not None:
+            self.clip_grads()
+            scale = self.gnorm.data_ptr() + 4
         B.slt_adamw_step(self.n, self.master, self.shadow, self.grads, self.m, self.v, self.t,
-                         w.lr if lr is None else lr, w.beta1, w.beta2, w.adam_eps, w.wd if wd is None else wd)
+                         w.lr if lr is None else lr, w.beta1, w.beta2, w.adam_eps, w.wd if wd is None else wd,
+                         grad_scale=scale)
 
     def step(self, tokens: torch.Tensor) -> None:
         self.forward(tokens)

@@ -110,7 +110,11 @@ def test_host_calls_reject_bad_arguments_before_launch():
     # negative sizes and NULL operands are caught on the host; stream NULL is fine
     assert lib.slt_gemm(-1, 4, 4, None, 4, 1, None, 4, 1, None, 4, None, 0, 1, 1, None, 0, None) == 1
     assert lib.slt_gemm(4, 4, 4, None, 4, 1, None, 4, 1, None, 4, None, 0, 1, 1, None, 0, None) == 1
-    assert lib.slt_adamw_step(10, None, None, None, None, None, 1, 1e-3, 0.9, 0.999, 1e-8, 0.1, None, None) == 1
+    assert lib.slt_adamw_step(10, None, None, None, None, None, 1, 1e-3, 0.9, 0.999, 1e-8, 0.1, None, None, None) == 1
+    assert lib.slt_clip_grad_norm(-1, None, 0, 1.0, None, None, None, None) == 1
+    assert lib.slt_clip_grad_norm(8, None, 2, 1.0, None, None, None, None) == 1      # bad kind
+    assert lib.slt_clip_grad_norm(8, None, 0, 0.0, None, None, None, None) == 1      # max_norm <= 0
+    assert B.slt_clip_workspace_bytes() > 0
     assert lib.slt_attention_fwd(None, None, None, None, None, None, 8, 8, 8, 8, 1, 4, 2, 1, 128, 0, 0, None, 1,
                                  None, None) == 2
     # a bf16 head dim the rotated-copy path takes needs its workspace

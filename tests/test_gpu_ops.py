@@ -410,6 +410,47 @@ def test_adamw_flat(B, n):
     np.testing.assert_array_equal(shadow, O.bf16_round(got))
 
 
+@pytest.mark.parametrize("n", [0, 5, 1000003])
+def test_clip_grad_norm_and_scaled_adamw(B, n):
+    say("clip", n)
+    rng = np.random.default_rng(13)
+    g = (rng.standard_normal(n) * 3.0).astype(np.float32)
+    tg = torch.from_numpy(g).cuda() if n else torch.empty(4, device="cuda")
+    ws = torch.empty(B.slt_clip_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    out = torch.full((2,), float("nan"), device="cuda")
+    gd = {"g": g.astype(np.float64)}
+    for kind, name in [(B.NORM_L2, "l2"), (B.NORM_LINF, "linf")]:
+        ref = O.grad_norm(gd, name) if n else 0.0
+        for max_norm in ([0.5 * ref, 2.0 * ref] if n else [1.0]):
+            B.slt_clip_grad_norm(n, tg, kind, max_norm, out, out.data_ptr() + 4, ws)
+            nrm, sc = host(out)
+            assert abs(nrm - ref) <= 1e-6 * ref, (name, nrm, ref)
+            want = O.clip_scale(ref, max_norm)
+            assert abs(sc - want) <= 1e-6 * want, (name, max_norm, sc, want)
+            again = out.clone()
+            B.slt_clip_grad_norm(n, tg, kind, max_norm, out, out.data_ptr() + 4, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out, again)          # fixed reduction order: bitwise reproducible
+    if n:
+        # AdamW applies the factor to the gradient it reads
+        th = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+        v = (np.abs(rng.standard_normal(n)) * 1e-7).astype(np.float32)
+        t_th, t_m, t_v = (torch.from_numpy(a.copy()).cuda() for a in (th, m, v))
+        B.slt_clip_grad_norm(n, tg, B.NORM_L2, 0.25 * O.grad_norm(gd, "l2"), None, out.data_ptr() + 4, ws)
+        s_ = float(host(out)[1])
+        B.slt_adamw_step(n, t_th, None, tg, t_m, t_v, 3, 1e-3, 0.9, 0.999, 1e-8, 0.1, None, out.data_ptr() + 4)
+        # the ABI takes fp32 hyperparameters: the reference uses the same values
+        # (0.999 as fp32 moves 1 - beta2 by 1.3e-5, which a v dominated by the
+        # new g^2 term shows)
+        f = lambda x: float(np.float32(x))
+        rth, rm, rv = O.adamw(th, s_ * g.astype(np.float64), m, v, 3, f(1e-3), f(0.9), f(0.999), f(1e-8), f(0.1))
+        check(host(t_m), rm, "f32", "clipped adamw m", tol=1e-6)
+        check(host(t_v), rv, "f32", "clipped adamw v", tol=1e-6)
+        got = host(t_th)
+        assert np.max(np.abs(got - rth) / (np.abs(rth) + rms(rth))) < 1e-5
+
+
 def test_cast_bf16_matches_oracle_rounding(B):
     rng = np.random.default_rng(12)
     x = (rng.standard_normal(100003) * 10.0 ** rng.integers(-30, 30, 100003)).astype(np.float32)

@@ -79,6 +79,42 @@ def test_full_step_parity(TS, ci, Bn, L):
     print(f"[result] {w.name} loss gpu {loss:.7f} oracle {ref['loss']:.7f}; tie-exempt weights {ties}")
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ci,Bn,kind", [(1, None, "l2"), (2, 8, "linf"), (3, 8, "l2")])
+def test_full_step_with_gradient_clipping(TS, ci, Bn, kind):
+    """Global-norm clipping between the backward and AdamW: the GPU's norm and
+    factor against the oracle's, and the clipped step's weights."""
+    w = W.get_config(ci)
+    w = w.with_(B=Bn or w.B)
+    say("clipped step", w, kind)
+    params = W.make_params(w, 2000 + ci)
+    tokens = W.make_tokens(w, 2000 + ci)
+    plain = O.train_step(w, params, tokens)
+    max_norm = 0.3 * O.grad_norm(plain["grads"], kind)        # clipping active
+    ref = O.train_step(w, params, tokens, clip=(kind, max_norm))
+    ts = TS(w, params=params, clip=(kind, max_norm))
+    tok = torch.from_numpy(tokens).cuda()
+    ts.forward(tok)
+    ts.backward(tok)
+    ts.adamw()
+    torch.cuda.synchronize()
+    nrm, sc = (float(x) for x in ts.gnorm.cpu().numpy())
+    tol = 1e-5 if w.act == "f32" else 2e-2
+    assert abs(nrm - ref["grad_norm"]) <= tol * ref["grad_norm"], (nrm, ref["grad_norm"])
+    assert abs(sc - ref["clip_scale"]) <= tol * ref["clip_scale"], (sc, ref["clip_scale"])
+    grads = ts.unpack(ts.grads)
+    new = ts.unpack(ts.master)
+    for name in params:
+        if w.act == "f32":
+            check_weights(new[name], ref["params"][name], ref["grads"][name], w.act, f"weight {name}")
+        else:
+            check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
+                                    f"weight {name}", w.adam_eps)
+        # every element: the oracle's AdamW on the GPU's gradient times the GPU's factor
+        own, _, _ = O.adamw(params[name], sc * grads[name], 0.0, 0.0, 1, w.lr, w.beta1, w.beta2, w.adam_eps, w.wd)
+        check(new[name], own, "f32", f"weight {name} from the GPU gradient")
+
+
 def test_step_is_deterministic(TS):
     w = W.get_config(3).with_(B=4, L=2)
     say("determinism", w)
