@@ -46,7 +46,7 @@ __all__ = [
     "attention_fwd", "attention_bwd",
     "swiglu_fwd", "swiglu_bwd", "gelu_fwd", "gelu_bwd",
     "cross_entropy", "adamw", "grad_norm", "clip_scale",
-    "forward", "backward", "train_step", "decay_mask_like",
+    "forward", "backward", "train_step", "decay_mask_like", "accumulated_grads",
 ]
 
 
@@ -531,6 +531,22 @@ def backward(cfg, cache):
         dx = S(dx + dxn)
     grads["wte"] = embedding_bwd(dx, cache["X"], cfg.V)
     return grads
+
+
+def accumulated_grads(cfg, params, micro_tokens):
+    """Gradient accumulation (Transformer in Rust, "Configuration": several
+    forward passes per optimizer step; "Features": gradient accumulation):
+    the mean over S equal micro-batches of each micro-batch's gradient (of its
+    own mean loss) -- the gradient of the mean loss over all of them.
+    Returns (mean loss, grads)."""
+    S = len(micro_tokens)
+    total, acc = 0.0, None
+    for tok in micro_tokens:
+        loss, cache = forward(cfg, params, tok)
+        g = backward(cfg, cache)
+        total += loss
+        acc = {k: v / S for k, v in g.items()} if acc is None else {k: acc[k] + g[k] / S for k in acc}
+    return total / S, acc
 
 
 def train_step(cfg, params, tokens, t=1, m=None, v=None, decay=None,

@@ -654,3 +654,27 @@ def test_train_step_clipping_scales_first_moments():
             g = base["grads"][k]
             np.testing.assert_allclose(out["m"][k], 0.1 * s_ * g, rtol=1e-14, atol=1e-300)
             np.testing.assert_allclose(out["v"][k], 0.001 * s_ * s_ * g * g, rtol=1e-14, atol=1e-300)
+
+
+# ---------------------------------------------------------------------------
+# Gradient accumulation (Transformer in Rust, "Configuration", "Features")
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("ci,S", [(1, 2), (1, 4), (3, 2)])
+def test_accumulation_over_micro_batches_equals_full_batch(ci, S):
+    # sequences are independent, so the mean of the micro-batch gradients is
+    # the full batch's gradient; for bf16 storage the micro-batch dz is S times
+    # the full batch's, an exact power-of-two scaling, so even the rounding
+    # points agree
+    w = W.get_config(ci)
+    w = w.with_(B=4, L=1, T=16) if ci == 3 else w.with_(B=4)
+    params = W.make_params(w, 42)
+    tokens = W.make_tokens(w, 42)
+    loss_full, cache = O.forward(w, params, tokens)
+    full = O.backward(w, cache)
+    micro = np.split(tokens, S, axis=0)
+    wm = w.with_(B=w.B // S)
+    loss_acc, acc = O.accumulated_grads(wm, params, micro)
+    assert abs(loss_acc - loss_full) <= 1e-13 * abs(loss_full)
+    for k in full:
+        den = np.linalg.norm(full[k])
+        assert np.linalg.norm(acc[k] - full[k]) <= 1e-12 * max(den, 1e-300), k
