@@ -149,6 +149,17 @@ slt_status slt_forward_loss(const slt_config* cfg, const void* params, const int
 slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t* tokens,
                         void* acts, void* scratch, float* grads, void* stream);
 
+/* Gradient accumulation over micro-batches (Transformer in Rust,
+ * "Configuration" and "Features": forward passes per optimizer step): the
+ * same backward, but grads += scale * (gradient of this micro-batch's mean
+ * loss) instead of overwriting.  With S micro-batches of equal size and
+ * scale = 1/S, starting from zeroed grads, the result is the gradient of the
+ * mean loss over all S micro-batches -- the full batch's gradient, up to the
+ * summation order.  Activation gradients are not scaled; only the writes of
+ * parameter gradients are. */
+slt_status slt_backward_accumulate(const slt_config* cfg, const void* params, const int32_t* tokens,
+                                   void* acts, void* scratch, float* grads, float scale, void* stream);
+
 /* AdamW on n flat fp32 elements at step t >= 1 (Hephaistos, "Architecture at a
  * glance"; strata, "AdamW (decoupled decay, bias-corrected)"):
  *   g = s grads;  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;

@@ -54,6 +54,7 @@ SIGNATURES = {
     "slt_cast_bf16": (_I32, [_P, _P, _I64, _P]),
     "slt_forward_loss": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _P]),
     "slt_backward": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _P]),
+    "slt_backward_accumulate": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _F, _P]),
     "slt_adamw_step": (_I32, [_I64, _P, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P, _P]),
     "slt_clip_workspace_bytes": (_I64, []),
     "slt_clip_grad_norm": (_I32, [_I64, _P, _I32, _F, _P, _P, _P, _P]),
@@ -197,6 +198,12 @@ def slt_forward_loss(cfg, params, tokens, acts, scratch, loss, stream=None):
 def slt_backward(cfg, params, tokens, acts, scratch, grads, stream=None):
     _check("slt_backward", load().slt_backward(ct.byref(cfg), _ptr(params), _ptr(tokens), _ptr(acts),
                                                _ptr(scratch), _ptr(grads), _stream(stream)))
+
+
+def slt_backward_accumulate(cfg, params, tokens, acts, scratch, grads, scale, stream=None):
+    _check("slt_backward_accumulate", load().slt_backward_accumulate(
+        ct.byref(cfg), _ptr(params), _ptr(tokens), _ptr(acts), _ptr(scratch), _ptr(grads), scale,
+        _stream(stream)))
 
 
 def slt_adamw_step(n, master, shadow, grads, m, v, t, lr, beta1, beta2, eps, wd, decay_mask=None, grad_scale=None,

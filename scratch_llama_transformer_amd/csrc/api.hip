@@ -226,6 +226,7 @@ struct Ctx {
   char* scr;
   const char* params;
   int dt;  // activation dtype
+  GradW gw{};  // how parameter gradients are written (scale, accumulate)
   void* A(int64_t off) const { return acts + off; }
   void* S(int64_t off) const { return scr + off; }
   const void* P(int64_t off) const { return params + off * p.es; }
@@ -245,11 +246,12 @@ static slt_status proj_dx(const Ctx& x, int M, int N, int K, const void* dY, int
   return launch_gemm(g, x.s);
 }
 
-// dW[N, K] = dY[M, N]^T X[M, K]  (fp32 out, row stride ldw)
+// dW[N, K] = alpha dY[M, N]^T X[M, K] (+ dW when accumulating)  (fp32 out, row stride ldw)
 static slt_status proj_dw(const Ctx& x, int M, int N, int K, const void* dY, int64_t lddy, const void* X,
                           int64_t ldx, float* dW, int64_t ldw) {
-  GemmArgs g{N, K, M, dY, lddy, false, X, ldx, false, dW, ldw, nullptr, 0, x.dt, SLT_F32,
+  GemmArgs g{N, K, M, dY, lddy, false, X, ldx, false, dW, ldw, x.gw.accumulate ? dW : nullptr, ldw, x.dt, SLT_F32,
              reinterpret_cast<float*>(x.S(x.p.gemmws)), x.p.gemmws_bytes};
+  g.alpha = x.gw.alpha;
   return launch_gemm(g, x.s);
 }
 
@@ -333,11 +335,11 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
   SLT_TRY(proj_dx(x, N, c.V, C, x.A(p.z), c.V, x.P(p.head), C, dn, C));
   if (p.llama)
     SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.rf), dn, nullptr, dx,
-                               grads + p.normf, N, C, x.dt, nws, x.s));
+                               grads + p.normf, N, C, x.dt, nws, x.s, x.gw));
   else
     SLT_TRY(launch_layernorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.muf),
                                  (const float*)x.A(p.rf), dn, nullptr, dx, grads + p.normf, grads + p.normfb, N, C,
-                                 x.dt, nws, x.s));
+                                 x.dt, nws, x.s, x.gw));
 
   for (int l = c.L - 1; l >= 0; --l) {
     const LayerP& W = p.lp[l];
@@ -361,7 +363,7 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(proj_dw(x, N, 2 * c.F, C, dbig, 2 * c.F, x.A(A.n2), C, grads + W.w1, C));
       SLT_TRY(proj_dx(x, N, 2 * c.F, C, dbig, 2 * c.F, x.P(W.w1), C, dn, C));
       SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l + 1]), x.P(W.norm2), (const float*)x.A(A.r2), dn, dx, dx,
-                                 grads + W.norm2, N, C, x.dt, nws, x.s));
+                                 grads + W.norm2, N, C, x.dt, nws, x.s, x.gw));
       // x_mid = x_in + o W_o^T
       SLT_TRY(proj_dw(x, N, C, p.qd, dx, C, x.A(A.o), p.qd, grads + W.wo, p.qd));
       SLT_TRY(proj_dx(x, N, C, p.qd, dx, C, x.P(W.wo), p.qd, dmid, p.qd));
@@ -375,7 +377,7 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(proj_dw(x, N, p.qkv_w, C, dbig, p.qkv_w, x.A(A.n1), C, grads + W.qkvw, C));
       SLT_TRY(proj_dx(x, N, p.qkv_w, C, dbig, p.qkv_w, x.P(W.qkvw), C, dn, C));
       SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l]), x.P(W.norm1), (const float*)x.A(A.r1), dn, dx, dx,
-                                 grads + W.norm1, N, C, x.dt, nws, x.s));
+                                 grads + W.norm1, N, C, x.dt, nws, x.s, x.gw));
     } else {
       char* ou = (char*)x.A(A.o);
       // x_out = x_in + [o | u] W_out^T
@@ -393,10 +395,10 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(proj_dw(x, N, p.in_w, C, dbig, p.in_w, x.A(A.n1), C, grads + W.qkvw, C));
       SLT_TRY(proj_dx(x, N, p.in_w, C, dbig, p.in_w, x.P(W.qkvw), C, dn, C));
       SLT_TRY(launch_layernorm_bwd(x.A(p.xs[l]), x.P(W.norm1), (const float*)x.A(A.mu1), (const float*)x.A(A.r1),
-                                   dn, dx, dx, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws, x.s));
+                                   dn, dx, dx, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws, x.s, x.gw));
     }
   }
-  SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, dx, grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s));
+  SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, dx, grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s, x.gw));
   return SLT_OK;
 }
 
@@ -487,6 +489,18 @@ slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t
   SLT_TRY(make_plan(cfg, p));
   if (!params || !tokens || !acts || !scratch || !grads) return fail(SLT_EINVAL, "backward: NULL pointer");
   Ctx x{p, as_stream(stream), (char*)acts, (char*)scratch, (const char*)params, cfg->act};
+  return backward(p, x, tokens, grads);
+}
+
+slt_status slt_backward_accumulate(const slt_config* cfg, const void* params, const int32_t* tokens, void* acts,
+                                   void* scratch, float* grads, float scale, void* stream) {
+  Plan p;
+  SLT_TRY(make_plan(cfg, p));
+  if (!params || !tokens || !acts || !scratch || !grads) return fail(SLT_EINVAL, "backward_accumulate: NULL pointer");
+  if (!(scale == scale)) return fail(SLT_EINVAL, "backward_accumulate: scale is NaN");
+  Ctx x{p, as_stream(stream), (char*)acts, (char*)scratch, (const char*)params, cfg->act};
+  x.gw.alpha = scale;
+  x.gw.accumulate = true;
   return backward(p, x, tokens, grads);
 }
 

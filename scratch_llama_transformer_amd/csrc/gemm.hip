@@ -175,6 +175,7 @@ struct KArgs {
   int kchunk;         // k range per split (multiple of BK)
   int tiles_n, tiles;
   bool evec;          // 4-wide epilogue stores allowed
+  float alpha;        // C = alpha A B (+ R)
 };
 
 template <typename TO>
@@ -281,6 +282,8 @@ __global__ __launch_bounds__(NT) void gemm_k(KArgs a) {
       } else {
         TO* dst = static_cast<TO*>(a.C) + (int64_t)m * a.ldc + n;
         const TO* res = a.R ? static_cast<const TO*>(a.R) + (int64_t)m * a.ldr + n : nullptr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] *= a.alpha;
         if (a.evec && n + 3 < a.N) {
           if (res) {
             float rv[4];
@@ -304,13 +307,14 @@ __global__ __launch_bounds__(NT) void gemm_k(KArgs a) {
 // out[m, n] = sum_z ws[z][m][n] (+ R[m, n]), z in increasing order.
 template <typename TO>
 __global__ __launch_bounds__(256) void splitk_reduce_k(const float* __restrict__ ws, int splits, int M, int N,
-                                                       TO* C, int64_t ldc, const TO* R, int64_t ldr) {
+                                                       TO* C, int64_t ldc, const TO* R, int64_t ldr, float alpha) {
   const int64_t total = (int64_t)M * N;
   for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = idx / N, n = idx % N;
     float s = 0.f;
     for (int z = 0; z < splits; ++z) s += ws[(int64_t)z * total + idx];
+    s *= alpha;
     if (R) s += to_f32(R[m * ldr + n]);
     C[m * ldc + n] = from_f32<TO>(s);
   }
@@ -593,6 +597,8 @@ __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a)
       }
       TO* dst = static_cast<TO*>(a.C) + (int64_t)m * a.ldc + n;
       const TO* res = a.R ? static_cast<const TO*>(a.R) + (int64_t)m * a.ldr + n : nullptr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] *= a.alpha;
       if (a.evec && n + 3 < a.N) {
         if (res) {
           float rv[4];
@@ -627,7 +633,7 @@ slt_status finish(const GemmArgs& g, bool split, int splits, hipStream_t s) {
     const int64_t total = (int64_t)g.M * g.N;
     int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
     splitk_reduce_k<TO><<<blocks, 256, 0, s>>>(g.workspace, splits, g.M, g.N, static_cast<TO*>(g.C), g.ldc,
-                                               static_cast<const TO*>(g.R), g.ldr);
+                                               static_cast<const TO*>(g.R), g.ldr, g.alpha);
   }
   return check_launch("gemm split-K reduction");
 }
@@ -639,6 +645,7 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
   ka.M = g.M; ka.N = g.N; ka.K = g.K;
   ka.A = g.A; ka.lda = g.lda; ka.B = g.B; ka.ldb = g.ldb;
   ka.C = g.C; ka.ldc = g.ldc; ka.R = g.R; ka.ldr = g.ldr;
+  ka.alpha = g.alpha;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   ka.tiles_n = tiles_n;
   const int tiles = tiles_m * tiles_n;

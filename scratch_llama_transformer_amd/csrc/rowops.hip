@@ -215,7 +215,7 @@ __global__ void emb_scatter_k(const int32_t* __restrict__ tok, int T_, int64_t l
 template <typename T, int VEC>
 __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict__ tok, int T_, int64_t ld,
                                                       const T* __restrict__ dx, float* __restrict__ dwte,
-                                                      int N, int V_, int C, EmbWs w) {
+                                                      int N, int V_, int C, EmbWs w, GradW gw) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int tile = blockIdx.x * 4 + wave;
   const int s = tile * kEmbTile;
@@ -244,12 +244,16 @@ __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict_
           const int id = ids[k];
           const int rs = w.start[id], re = w.start[id + 1];
           float* dst;
+          bool final_row = false;
           if (rs < s) dst = w.head + (int64_t)tile * C;          // continues from an earlier tile
           else if (re > e) dst = w.tail + (int64_t)tile * C;     // continues into a later tile
-          else dst = dwte + (int64_t)id * C;                     // complete inside this tile
+          else {                                                 // complete inside this tile
+            dst = dwte + (int64_t)id * C;
+            final_row = true;
+          }
 #pragma unroll
           for (int q = 0; q < VEC; ++q) {
-            dst[c0 + q] = acc[q];
+            dst[c0 + q] = final_row ? gw.alpha * acc[q] + (gw.accumulate ? dst[c0 + q] : 0.f) : acc[q];
             acc[q] = 0.f;
           }
         }
@@ -262,14 +266,16 @@ __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict_
 // several tiles.  For the latter the 4 waves take contiguous quarters of the
 // tiles (tail of the first tile, then heads in tile order), each summing with
 // 4 interleaved accumulators; the quarters are added in order.
-__global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte, int V, int C, EmbWs w) {
+__global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte, int V, int C, EmbWs w,
+                                                        GradW gw) {
   __shared__ float part[4][256];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int v = blockIdx.x;
   const int rs = w.start[v], re = w.start[v + 1];
   float* row = dwte + (int64_t)v * C;
-  if (re == rs) {
-    for (int c = threadIdx.x; c < C; c += blockDim.x) row[c] = 0.f;
+  if (re == rs) {  // unseen id: exactly zero (or unchanged when accumulating)
+    if (!gw.accumulate)
+      for (int c = threadIdx.x; c < C; c += blockDim.x) row[c] = 0.f;
     return;
   }
   const int t0 = rs / kEmbTile, t1 = (re - 1) / kEmbTile;
@@ -302,7 +308,10 @@ __global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte
     for (int q = 0; q < 4; ++q) part[wave][q * kWave + lane] = (acc[0][q] + acc[1][q]) + (acc[2][q] + acc[3][q]);
     __syncthreads();
     for (int c = threadIdx.x; c < kWave * 4; c += blockDim.x)
-      if (c0 + c < C) row[c0 + c] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+      if (c0 + c < C) {
+        const float sum = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+        row[c0 + c] = gw.alpha * sum + (gw.accumulate ? row[c0 + c] : 0.f);
+      }
     __syncthreads();
   }
 }
@@ -488,7 +497,7 @@ __global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const
 // (g, c) adds partials g, g+32, ... in order, then the 32 group sums are added
 // in a fixed tree.
 __global__ __launch_bounds__(1024) void norm_colsum_k(const float* __restrict__ part, int nb, int C,
-                                                       float* __restrict__ out) {
+                                                       float* __restrict__ out, GradW gw) {
   __shared__ float red[32][33];
   const int tc = threadIdx.x & 31, g = threadIdx.x >> 5;
   const int c = blockIdx.x * 32 + tc;
@@ -503,7 +512,7 @@ __global__ __launch_bounds__(1024) void norm_colsum_k(const float* __restrict__ 
     if (g < off) red[g][tc] += red[g + off][tc];
     __syncthreads();
   }
-  if (g == 0 && c < C) out[c] = red[0][tc];
+  if (g == 0 && c < C) out[c] = gw.alpha * red[0][tc] + (gw.accumulate ? out[c] : 0.f);
 }
 
 constexpr int kNormBwdBlocks = 512;
@@ -902,7 +911,7 @@ int64_t embedding_bwd_ws(int64_t N, int V) {
 }
 
 slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, const void* dx, float* dwte, int V,
-                                int C, int dtype, void* ws, hipStream_t s) {
+                                int C, int dtype, void* ws, hipStream_t s, GradW gw) {
   const int N = B * T_;
   EmbWs w = emb_ws_layout(ws, N, V, 4096);
   const int nchunk = cdiv(N, kEmbChunk);
@@ -916,12 +925,12 @@ slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, c
     using T = decltype(tag);
     constexpr int VEC = full_vec<T>();
     if (C % VEC == 0 && aligned(dx, 16))
-      emb_tile_sum_k<T, VEC><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w);
+      emb_tile_sum_k<T, VEC><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w, gw);
     else
-      emb_tile_sum_k<T, 1><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w);
+      emb_tile_sum_k<T, 1><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w, gw);
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
-  emb_row_finish_k<<<V, 256, 0, s>>>(dwte, V, C, w);
+  emb_row_finish_k<<<V, 256, 0, s>>>(dwte, V, C, w, gw);
   return check_launch("embedding_bwd");
 }
 
@@ -981,7 +990,7 @@ int64_t norm_bwd_ws(int rows, int C) {
 template <bool LN>
 static slt_status norm_bwd_common(const void* x, const void* g, const float* mean, const float* rstd,
                                   const void* dy, const void* dres, void* dx, float* dg, float* db, int rows,
-                                  int C, int dtype, void* ws, hipStream_t s) {
+                                  int C, int dtype, void* ws, hipStream_t s, GradW gw) {
   const int nb = std::max(1, std::min(kNormBwdBlocks, cdiv(rows, 4)));
   float* part = static_cast<float*>(ws);
   const size_t smem = (size_t)(LN ? 2 : 1) * C * sizeof(float);
@@ -996,20 +1005,20 @@ static slt_status norm_bwd_common(const void* x, const void* g, const float* mea
   };
   slt_status st = dtype == SLT_BF16 ? go(bf16{}) : go(float{});
   if (st != SLT_OK) return st;
-  norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part, nb, C, dg);
-  if (LN) norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part + (int64_t)nb * C, nb, C, db);
+  norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part, nb, C, dg, gw);
+  if (LN) norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part + (int64_t)nb * C, nb, C, db, gw);
   return check_launch("norm_colsum");
 }
 
 slt_status launch_rmsnorm_bwd(const void* x, const void* g, const float* rstd, const void* dy, const void* dres,
-                              void* dx, float* dg, int rows, int C, int dtype, void* ws, hipStream_t s) {
-  return norm_bwd_common<false>(x, g, nullptr, rstd, dy, dres, dx, dg, nullptr, rows, C, dtype, ws, s);
+                              void* dx, float* dg, int rows, int C, int dtype, void* ws, hipStream_t s, GradW gw) {
+  return norm_bwd_common<false>(x, g, nullptr, rstd, dy, dres, dx, dg, nullptr, rows, C, dtype, ws, s, gw);
 }
 
 slt_status launch_layernorm_bwd(const void* x, const void* gm, const float* mean, const float* rstd,
                                 const void* dy, const void* dres, void* dx, float* dgm, float* dbt, int rows,
-                                int C, int dtype, void* ws, hipStream_t s) {
-  return norm_bwd_common<true>(x, gm, mean, rstd, dy, dres, dx, dgm, dbt, rows, C, dtype, ws, s);
+                                int C, int dtype, void* ws, hipStream_t s, GradW gw) {
+  return norm_bwd_common<true>(x, gm, mean, rstd, dy, dres, dx, dgm, dbt, rows, C, dtype, ws, s, gw);
 }
 
 slt_status launch_rope_table(int T_, int R, float base, float* cs, hipStream_t s) {

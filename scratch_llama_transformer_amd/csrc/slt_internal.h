@@ -83,6 +83,14 @@ struct GemmArgs {
   const void* R; int64_t ldr;
   int in_dtype, out_dtype;
   float* workspace; int64_t workspace_bytes;
+  float alpha = 1.0f;  // C = alpha A B (+ R)
+};
+
+// How a parameter-gradient kernel writes its result g: out = alpha g, or
+// out += alpha g when accumulating over micro-batches.
+struct GradW {
+  float alpha = 1.0f;
+  bool accumulate = false;
 };
 slt_status launch_gemm(const GemmArgs& g, hipStream_t s);
 
@@ -90,18 +98,18 @@ slt_status launch_embedding_fwd(const int32_t* tok, int B, int T, int64_t ld, co
                                 void* x, int V, int C, int dtype, hipStream_t s);
 int64_t embedding_bwd_ws(int64_t N, int V);
 slt_status launch_embedding_bwd(const int32_t* tok, int B, int T, int64_t ld, const void* dx,
-                                float* dwte, int V, int C, int dtype, void* ws, hipStream_t s);
+                                float* dwte, int V, int C, int dtype, void* ws, hipStream_t s, GradW gw = {});
 int64_t norm_bwd_ws(int rows, int C);
 slt_status launch_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd, int rows, int C,
                               float eps, int dtype, hipStream_t s);
 slt_status launch_rmsnorm_bwd(const void* x, const void* g, const float* rstd, const void* dy,
                               const void* dres, void* dx, float* dg, int rows, int C, int dtype,
-                              void* ws, hipStream_t s);
+                              void* ws, hipStream_t s, GradW gw = {});
 slt_status launch_layernorm_fwd(const void* x, const void* gm, const void* bt, void* y, float* mean,
                                 float* rstd, int rows, int C, float eps, int dtype, hipStream_t s);
 slt_status launch_layernorm_bwd(const void* x, const void* gm, const float* mean, const float* rstd,
                                 const void* dy, const void* dres, void* dx, float* dgm, float* dbt,
-                                int rows, int C, int dtype, void* ws, hipStream_t s);
+                                int rows, int C, int dtype, void* ws, hipStream_t s, GradW gw = {});
 slt_status launch_rope_table(int T, int R, float base, float* cs, hipStream_t s);
 slt_status launch_swiglu_fwd(const void* a, const void* b, void* h, int rows, int F, int64_t lda,
                              int64_t ldb, int64_t ldh, int dtype, hipStream_t s);

@@ -115,6 +115,39 @@ def test_full_step_with_gradient_clipping(TS, ci, Bn, kind):
         check(new[name], own, "f32", f"weight {name} from the GPU gradient")
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ci,Bn,S", [(1, 4, 2), (2, 8, 2), (3, 8, 4)])
+def test_gradient_accumulation(TS, ci, Bn, S):
+    """S micro-batches through slt_backward_accumulate (scale 1/S) give the
+    full batch's gradient: against the GPU's own full-batch step (same
+    rounding points for power-of-two S, so only summation order differs) and
+    against the oracle's accumulation."""
+    w = W.get_config(ci).with_(B=Bn)
+    say("accumulation", w, S)
+    params = W.make_params(w, 3000 + ci)
+    tokens = W.make_tokens(w, 3000 + ci)
+    full = TS(w, params=params)
+    tok = torch.from_numpy(tokens).cuda()
+    full.forward(tok)
+    full.backward(tok)
+    torch.cuda.synchronize()
+    full_loss = float(full.loss.item())
+    gfull = full.unpack(full.grads)
+    wm = w.with_(B=Bn // S)
+    ts = TS(wm, params=params)
+    micro = [torch.from_numpy(np.ascontiguousarray(t)).cuda() for t in np.split(tokens, S, axis=0)]
+    loss = ts.accumulate(micro)
+    gacc = ts.unpack(ts.grads)
+    assert abs(loss - full_loss) <= 1e-5 * abs(full_loss), (loss, full_loss)
+    for name in gfull:
+        check(gacc[name], gfull[name], "f32", f"accumulated vs full-batch {name}")
+    ref_loss, ref = O.accumulated_grads(wm, params, np.split(tokens, S, axis=0))
+    assert abs(loss - ref_loss) <= LOSS_TOL[w.act] * abs(ref_loss)
+    if w.act == "f32":
+        for name in ref:
+            check(gacc[name], ref[name], "f32", f"accumulated vs oracle {name}")
+
+
 def test_step_is_deterministic(TS):
     w = W.get_config(3).with_(B=4, L=2)
     say("determinism", w)
