@@ -31,6 +31,12 @@
 #ifndef SLT_GEMM_BKX
 #define SLT_GEMM_BKX 2
 #endif
+#ifndef SLT_SPLIT_TARGET
+#define SLT_SPLIT_TARGET 384  // blocks a split-K grid aims for
+#endif
+#ifndef SLT_SPLIT_MINK
+#define SLT_SPLIT_MINK 8  // fewest k-steps per split
+#endif
 #ifndef SLT_GEMM_BIG
 #define SLT_GEMM_BIG 1
 #endif
@@ -663,7 +669,7 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
   int splits = 1;
   if (g.workspace && tiles < 256) {
     const int kt = (g.K + BK - 1) / BK;
-    int want = std::min((512 + tiles - 1) / tiles, kt / 8);
+    int want = std::min((SLT_SPLIT_TARGET + tiles - 1) / tiles, kt / SLT_SPLIT_MINK);
     const int64_t per = (int64_t)g.M * g.N * 4;
     while (want > 1 && per * want > g.workspace_bytes) --want;
     splits = std::max(1, want);
