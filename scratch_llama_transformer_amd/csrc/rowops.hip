@@ -328,13 +328,20 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const T* __restrict__ x, co
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;
   const T* xr = x + (int64_t)row * C;
-  float xv[NCH][VEC];
+  float xv[NCH][VEC], gv[NCH][VEC];
   float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {  // the gain is loaded with x, not after the reduction
+    const int c = (lane + j * kWave) * VEC;
+    if (c < C) {
+      load_f<T, VEC>(xr + c, xv[j]);
+      load_f<T, VEC>(g + c, gv[j]);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = (lane + j * kWave) * VEC;
     if (c < C) {
-      load_f<T, VEC>(xr + c, xv[j]);
 #pragma unroll
       for (int q = 0; q < VEC; ++q) ss += xv[j][q] * xv[j][q];
     }
@@ -346,10 +353,9 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_k(const T* __restrict__ x, co
   for (int j = 0; j < NCH; ++j) {
     const int c = (lane + j * kWave) * VEC;
     if (c < C) {
-      float gv[VEC], out[VEC];
-      load_f<T, VEC>(g + c, gv);
+      float out[VEC];
 #pragma unroll
-      for (int q = 0; q < VEC; ++q) out[q] = xv[j][q] * r * gv[q];
+      for (int q = 0; q < VEC; ++q) out[q] = xv[j][q] * r * gv[j][q];
       store_f<T, VEC>(y + (int64_t)row * C + c, out);
     }
   }
@@ -418,54 +424,79 @@ __global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const
                                                   float* __restrict__ part, int rows, int C) {
   extern __shared__ float red[];  // [C] (x2 for LayerNorm)
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  float pg[NCH][VEC], pb[NCH][VEC];
+  float pg[NCH][VEC], pb[NCH][VEC], gv[NCH][VEC];
 #pragma unroll
-  for (int j = 0; j < NCH; ++j)
+  for (int j = 0; j < NCH; ++j) {
+    const int c = (lane + j * kWave) * VEC;
 #pragma unroll
-    for (int q = 0; q < VEC; ++q) pg[j][q] = pb[j][q] = 0.f;
+    for (int q = 0; q < VEC; ++q) pg[j][q] = pb[j][q] = gv[j][q] = 0.f;
+    if (c < C) load_f<T, VEC>(g + c, gv[j]);
+  }
 
-  for (int row = blockIdx.x * 4 + wave; row < rows; row += gridDim.x * 4) {
-    const int64_t base = (int64_t)row * C;
-    const float r = rstd[row];
-    const float mu = LN ? mean[row] : 0.f;
-    float xh[NCH][VEC], dxh[NCH][VEC];
-    float s1 = 0.f, s2 = 0.f;  // sum dxh, sum dxh*xh
+  // Four rows per iteration, every load of them issued before any use, so
+  // that each wave keeps four rows of x, dy and the incoming gradient in
+  // flight (the grid is small: its block count sets the number of dg partials).
+  constexpr int RP = 4;
+  const int step = gridDim.x * 4;
+  for (int row0 = blockIdx.x * 4 + wave; row0 < rows; row0 += RP * step) {
+    float xv[RP][NCH][VEC], dv[RP][NCH][VEC], rv[RP][NCH][VEC], r[RP], mu[RP];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = (lane + j * kWave) * VEC;
-      if (c < C) {
-        float xv[VEC], dv[VEC], gv[VEC];
-        load_f<T, VEC>(x + base + c, xv);
-        load_f<T, VEC>(dy + base + c, dv);
-        load_f<T, VEC>(g + c, gv);
+    for (int k = 0; k < RP; ++k) {
+      const int row = row0 + k * step;
+      const bool ok = row < rows;
+      const int64_t base = (int64_t)(ok ? row : row0) * C;
+      r[k] = ok ? rstd[row] : 0.f;
+      mu[k] = (LN && ok) ? mean[row] : 0.f;
 #pragma unroll
-        for (int q = 0; q < VEC; ++q) {
-          xh[j][q] = (xv[q] - mu) * r;
-          dxh[j][q] = dv[q] * gv[q];
-          s1 += dxh[j][q];
-          s2 += dxh[j][q] * xh[j][q];
-          pg[j][q] += dv[q] * xh[j][q];
-          pb[j][q] += dv[q];
+      for (int j = 0; j < NCH; ++j) {
+        const int c = (lane + j * kWave) * VEC;
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) xv[k][j][q] = dv[k][j][q] = rv[k][j][q] = 0.f;
+        if (c < C && ok) {
+          load_f<T, VEC>(x + base + c, xv[k][j]);
+          load_f<T, VEC>(dy + base + c, dv[k][j]);
+          if (dres != nullptr) load_f<T, VEC>(dres + base + c, rv[k][j]);
         }
       }
     }
-    const float m2 = wave_sum(s2) / (float)C;
-    const float m1 = LN ? wave_sum(s1) / (float)C : 0.f;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = (lane + j * kWave) * VEC;
-      if (c < C) {
-        float out[VEC];
-        float rv[VEC];
-        if (dres != nullptr) {
-          load_f<T, VEC>(dres + base + c, rv);
-        } else {
+    for (int k = 0; k < RP; ++k) {
+      const int row = row0 + k * step;
+      if (row >= rows) break;
+      const int64_t base = (int64_t)row * C;
+      float s1 = 0.f, s2 = 0.f;  // sum dxh, sum dxh*xh
 #pragma unroll
-          for (int q = 0; q < VEC; ++q) rv[q] = 0.f;
+      for (int j = 0; j < NCH; ++j) {
+        const int c = (lane + j * kWave) * VEC;
+        if (c < C) {
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) {
+            const float xh = (xv[k][j][q] - mu[k]) * r[k];
+            const float dyv = dv[k][j][q];
+            const float dxh = dyv * gv[j][q];
+            pg[j][q] += dyv * xh;
+            pb[j][q] += dyv;
+            xv[k][j][q] = xh;
+            dv[k][j][q] = dxh;
+            s1 += dxh;
+            s2 += dxh * xh;
+          }
         }
+      }
+      const float m2 = wave_sum(s2) / (float)C;
+      const float m1 = LN ? wave_sum(s1) / (float)C : 0.f;
 #pragma unroll
-        for (int q = 0; q < VEC; ++q) out[q] = rv[q] + r * (dxh[j][q] - m1 - xh[j][q] * m2);
-        store_f<T, VEC>(dx + base + c, out);
+      for (int j = 0; j < NCH; ++j) {
+        const int c = (lane + j * kWave) * VEC;
+        if (c < C) {
+          float out[VEC];
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) {
+            const float xh = xv[k][j][q], dxh = dv[k][j][q];
+            out[q] = rv[k][j][q] + r[k] * (dxh - m1 - xh * m2);
+          }
+          store_f<T, VEC>(dx + base + c, out);
+        }
       }
     }
   }
@@ -515,7 +546,10 @@ __global__ __launch_bounds__(1024) void norm_colsum_k(const float* __restrict__ 
   if (g == 0 && c < C) out[c] = gw.alpha * red[0][tc] + (gw.accumulate ? out[c] : 0.f);
 }
 
-constexpr int kNormBwdBlocks = 512;
+#ifndef SLT_NORM_BLOCKS
+#define SLT_NORM_BLOCKS 512
+#endif
+constexpr int kNormBwdBlocks = SLT_NORM_BLOCKS;
 
 // ---------------------------------------------------------------------------
 // SwiGLU and GELU on [rows, F] with row strides.
