@@ -37,6 +37,9 @@
 #ifndef SLT_SPLIT_MINK
 #define SLT_SPLIT_MINK 8  // fewest k-steps per split
 #endif
+#ifndef SLT_GEMM_D64
+#define SLT_GEMM_D64 1  // 64-deep two-stage kernel for k-major x k-major 128 x 128 tiles
+#endif
 #ifndef SLT_GEMM_BIG
 #define SLT_GEMM_BIG 1
 #endif
@@ -529,6 +532,52 @@ __device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK,
                                                           __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
 }
 
+// Block epilogue: lane holds C[m][n .. n+3] of each 16 x 16 fragment; split-K
+// blocks write fp32 partials, the others alpha C (+ R) in the output type.
+template <typename TO, bool SPLIT, int FM, int FN>
+__device__ __forceinline__ void dl_epilogue(const KArgs& a, const f32x4 (&acc)[FM][FN], int m0, int n0, int wm, int wn,
+                                            int lane) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * 16 * FM + i * 16 + (lane & 15);
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * 16 * FN + j * 16 + 4 * (lane >> 4);
+      if (n >= a.N) continue;
+      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      if (SPLIT) {
+        float* dst = a.ws + ((int64_t)blockIdx.z * a.M + m) * a.N + n;
+        if (a.evec && n + 3 < a.N) {
+          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          for (int r = 0; r < 4 && n + r < a.N; ++r) dst[r] = v[r];
+        }
+        continue;
+      }
+      TO* dst = static_cast<TO*>(a.C) + (int64_t)m * a.ldc + n;
+      const TO* res = a.R ? static_cast<const TO*>(a.R) + (int64_t)m * a.ldr + n : nullptr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] *= a.alpha;
+      if (a.evec && n + 3 < a.N) {
+        if (res) {
+          float rv[4];
+          load4<TO>(res, rv);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] += rv[r];
+        }
+        store4<TO>(dst, v);
+      } else {
+        for (int r = 0; r < 4 && n + r < a.N; ++r) {
+          float x = v[r];
+          if (res) x += to_f32(res[r]);
+          dst[r] = from_f32<TO>(x);
+        }
+      }
+    }
+  }
+}
+
 // Block tile (32 FM) x (32 FN): 2 x 2 waves, each 16 FM x 16 FN.
 template <typename TO, bool AK, bool BK, bool SPLIT, int FM, int FN>
 __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a) {
@@ -581,47 +630,113 @@ __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a)
     if (it + 2 < c.nk) dl_step<AK, BK, FM, FN>(c, it + 2, da, db, a2, b2, A1, B1, acc);
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+  dl_epilogue<TO, SPLIT, FM, FN>(a, acc, c.m0, c.n0, wm, wn, lane);
+}
 
-  const int m0 = c.m0, n0 = c.n0;
+
+// ---------------------------------------------------------------------------
+// Both operands k-major, 128 x 128 block tile: 64-deep k-steps in two stages.
+// A tile row is then a whole 128-byte line (8 chunks of 16 bytes at position
+// chunk XOR 2 ((row >> 1) & 3), conflict-free for the 16-row fragment reads),
+// so each copy instruction fetches 8 full lines where the 32-deep ring's
+// fetches 16 half lines.  Per k-step: one wait and barrier, the next tile's
+// copies, then two 32-deep halves of reads and MFMAs.  Measured on gfx950 it
+// beats the 32-deep ring on the forward projections with 384 to 1152 output
+// columns; it loses on the m/n-major layouts and, as a 256 x 128 tile, on the
+// wider forward projections, where it is not used.
+// ---------------------------------------------------------------------------
+constexpr int D64_TILE = 128 * 64;  // elements per 128-row operand tile (16 KiB)
+
+__device__ __forceinline__ int d64_swz(int r) { return 2 * ((r >> 1) & 3); }
+
+// Copy the (32 F) x 64 tile at (row0, k0): F copies per lane.
+template <int F>
+__device__ __forceinline__ void d64_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
+                                          int lane) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * 16 * FM + i * 16 + (lane & 15);
-    if (m >= a.M) continue;
+  for (int i = 0; i < F; ++i) {
+    const int p = (wave * F + i) * 64 + lane;  // 16-byte chunk position in the tile
+    const int r = p >> 3;
+    const int lc = (p & 7) ^ d64_swz(r);
+    lds_copy16(g + (int64_t)min(row0 + r, rows - 1) * ld + k0 + lc * 8, tile + (wave * F + i) * 512);
+  }
+}
+
+#define D64_R128(X, f, off) "ds_read_b128 %[" #X #f "], %[" #X "p] offset:" #off "\n\t"
+#define D64_KM4(X) D64_R128(X, 0, 0) D64_R128(X, 1, 2048) D64_R128(X, 2, 4096) D64_R128(X, 3, 6144)
+#define D64_OKM(X, f, v) [X##f] "=&v"(v[f])
+#define D64_OUT_KM4(X, v) D64_OKM(X, 0, v), D64_OKM(X, 1, v), D64_OKM(X, 2, v), D64_OKM(X, 3, v)
+
+// Fragments f = 0..3 of both operands (16 rows of 128 bytes each, 2 KiB
+// apart) from LDS byte addresses pa and pb.
+__device__ __forceinline__ void d64_read(unsigned pa, unsigned pb, u32x4 (&af)[4], u32x4 (&bf)[4]) {
+  asm volatile(D64_KM4(a) D64_KM4(b) "s_waitcnt lgkmcnt(0)"
+               : D64_OUT_KM4(a, af), D64_OUT_KM4(b, bf) : [ap] "v"(pa), [bp] "v"(pb) : "memory");
+}
+#undef D64_R128
+#undef D64_KM4
+#undef D64_OKM
+#undef D64_OUT_KM4
+
+template <typename TO, bool SPLIT>
+__global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
+  constexpr int FM = 4;
+  __shared__ __attribute__((aligned(16))) bf16 A0[D64_TILE], A1[D64_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 B0[D64_TILE], B1[D64_TILE];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tile = blockIdx.x;
+  if (SLT_GEMM_XCD) {
+    const int q = a.tiles >> 3, r = a.tiles & 7, x = tile & 7;
+    tile = x * q + min(x, r) + (tile >> 3);
+  }
+  const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
+  const bf16* A = static_cast<const bf16*>(a.A);
+  const bf16* B = static_cast<const bf16*>(a.B);
+  const int m0 = tm * 32 * FM, n0 = tn * 128;
+  const int kbeg = SPLIT ? blockIdx.z * a.kchunk : 0;
+  const int nk = (min(a.K, kbeg + a.kchunk) - kbeg) / 64;
+  // lane (g, i) reads row i of a fragment, k chunk 4 s + g of half s
+  const int i = lane & 15, g = lane >> 4;
+  unsigned ra[2], rb[2];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * 16 * FN + j * 16 + 4 * (lane >> 4);
-      if (n >= a.N) continue;
-      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      if (SPLIT) {
-        float* dst = a.ws + ((int64_t)blockIdx.z * a.M + m) * a.N + n;
-        if (a.evec && n + 3 < a.N) {
-          *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-          for (int r = 0; r < 4 && n + r < a.N; ++r) dst[r] = v[r];
-        }
-        continue;
-      }
-      TO* dst = static_cast<TO*>(a.C) + (int64_t)m * a.ldc + n;
-      const TO* res = a.R ? static_cast<const TO*>(a.R) + (int64_t)m * a.ldr + n : nullptr;
+  for (int s = 0; s < 2; ++s) {
+    ra[s] = (wm * 16 * FM + i) * 128 + ((4 * s + g) ^ d64_swz(i)) * 16;
+    rb[s] = (wn * 64 + i) * 128 + ((4 * s + g) ^ d64_swz(i)) * 16;
+  }
+
+  f32x4 acc[FM][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] *= a.alpha;
-      if (a.evec && n + 3 < a.N) {
-        if (res) {
-          float rv[4];
-          load4<TO>(res, rv);
+  for (int x = 0; x < FM; ++x)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] += rv[r];
-        }
-        store4<TO>(dst, v);
-      } else {
-        for (int r = 0; r < 4 && n + r < a.N; ++r) {
-          float x = v[r];
-          if (res) x += to_f32(res[r]);
-          dst[r] = from_f32<TO>(x);
-        }
-      }
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  d64_issue<FM>(A, a.lda, a.M, m0, kbeg, A0, wave, lane);
+  d64_issue<4>(B, a.ldb, a.N, n0, kbeg, B0, wave, lane);
+  for (int it = 0; it < nk; ++it) {
+    SLT_WAIT_VMCNT(0);  // this wave's copies of tile it have landed
+    lds_barrier();      // ... everyone's have, and the other stage is free
+    if (it + 1 < nk) {
+      const int kn = kbeg + (it + 1) * 64;
+      d64_issue<FM>(A, a.lda, a.M, m0, kn, (it & 1) ? A0 : A1, wave, lane);
+      d64_issue<4>(B, a.ldb, a.N, n0, kn, (it & 1) ? B0 : B1, wave, lane);
+    }
+    const unsigned as = lds_off((it & 1) ? A1 : A0), bs = lds_off((it & 1) ? B1 : B0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 af[FM], bfr[4];
+      d64_read(as + ra[s], bs + rb[s], af, bfr);
+#pragma unroll
+      for (int x = 0; x < FM; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[y]),
+                                                              __builtin_bit_cast(bf16x8_t, af[x]), acc[x][y], 0, 0, 0);
     }
   }
+  SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+  dl_epilogue<TO, SPLIT, FM, 4>(a, acc, m0, n0, wm, wn, lane);
 }
 
 inline bool al(const void* p, int b) { return (reinterpret_cast<uintptr_t>(p) % b) == 0; }
@@ -718,7 +833,10 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
         ka.tiles = ((g.M + 32 * fm - 1) / (32 * fm)) * ka.tiles_n;
         grid = dim3(ka.tiles, 1, 1);
       }
-      if (g.a_kmajor && g.b_kmajor) {
+      if (SLT_GEMM_D64 && g.a_kmajor && g.b_kmajor && fm == 4 && fn == 4 && g.K % 64 == 0 && ka.kchunk % 64 == 0) {
+        if (split) gemm_d64_k<float, true><<<grid, NT, 0, s>>>(ka);
+        else gemm_d64_k<TO, false><<<grid, NT, 0, s>>>(ka);
+      } else if (g.a_kmajor && g.b_kmajor) {
         if (fm == 8) SLT_DL_GO(true, true, 8, 4);
         else if (fn == 8) SLT_DL_GO(true, true, 4, 8);
         else SLT_DL_GO(true, true, 4, 4);

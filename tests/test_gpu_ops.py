@@ -101,7 +101,7 @@ def test_gemm_direct_lds_path(B, a_k, b_k, outd):
     # residual, and split K through the workspace
     rng = np.random.default_rng(5)
     for (M, N, K) in [(40, 56, 32), (136, 264, 64), (128, 256, 96), (200, 136, 128), (256, 384, 160),
-                      (8, 296, 32), (37, 56, 64)]:
+                      (8, 296, 32), (37, 56, 64), (136, 264, 192), (72, 200, 320)]:
         gemm_case(B, rng, M, N, K, a_k, b_k, BF16, outd)
         gemm_case(B, rng, M, N, K, a_k, b_k, BF16, outd, resid=True)
     gemm_case(B, rng, 96, 72, 3008, a_k, b_k, BF16, outd, ws=True)
@@ -111,9 +111,10 @@ def test_gemm_direct_lds_path(B, a_k, b_k, outd):
 @pytest.mark.parametrize("a_k,b_k,M,N", [(1, 1, 12296, 4000), (1, 1, 4000, 12296), (1, 0, 12296, 4000)])
 def test_gemm_big_tiles(B, a_k, b_k, M, N):
     # grids with enough 256 x 128 (128 x 256) tiles take the larger block
-    # tile; ragged M and N, 1..5 k-steps, residual; sampled rows
+    # tile; ragged M and N, 1..6 k-steps of 32 (1..3 of 64), residual;
+    # sampled rows
     rng = np.random.default_rng(6)
-    for K in (32, 96, 160):
+    for K in (32, 96, 128, 160, 192):
         gemm_case(B, rng, M, N, K, a_k, b_k, BF16, BF16, sample=40)
     gemm_case(B, rng, M, N, 64, a_k, b_k, BF16, BF16, resid=True, sample=40)
     gemm_case(B, rng, M, N, 64, a_k, b_k, BF16, F32, sample=40)
