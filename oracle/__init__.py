@@ -9,3 +9,6 @@ other step is written out from its definition.  See ``oracle/model.py``.
 """
 from .model import *  # noqa: F401,F403
 from .model import __all__  # noqa: F401
+from .kvcache import kv_cache_new, forward_cached  # noqa: F401
+
+__all__ = list(__all__) + ["kv_cache_new", "forward_cached"]

@@ -678,3 +678,80 @@ def test_accumulation_over_micro_batches_equals_full_batch(ci, S):
     for k in full:
         den = np.linalg.norm(full[k])
         assert np.linalg.norm(acc[k] - full[k]) <= 1e-12 * max(den, 1e-300), k
+
+
+# --------------------------------------------------------------------------
+# Key/value-cache forward (randyGPT, "Features": prefill once, then one
+# single-token forward per new token; strata, "rules": the cached decoder
+# equals the full forward to about 1e-9 at float64, with pre-rotated keys)
+# --------------------------------------------------------------------------
+KV_CASES = [("llama", 4, 4, {}), ("llama", 4, 2, {}), ("llama", 4, 1, {}), ("llama", 4, 4, {"R": 0}),
+            ("parallel", 4, 4, {}), ("llama", 2, 2, {"rope_mode": "pairs", "R": 8})]
+
+
+@pytest.mark.parametrize("block,H,Hkv,kw", KV_CASES)
+def test_cached_decode_equals_full_forward(block, H, Hkv, kw):
+    """Prefill a 3-token prompt, then decode one token at a time: the logits
+    of every position equal that row of the full causal forward, and no
+    sequence sees another's keys."""
+    cfg = tiny(block=block, H=H, Hkv=Hkv, T=9, B=2, **kw)
+    params = rand_params(cfg, seed=41)
+    tokens = np.random.default_rng(42).integers(0, cfg.V, size=(2, cfg.T + 1))
+    _, full = O.forward(cfg, params, tokens)
+    zfull = full["z"].reshape(2, cfg.T, cfg.V)
+    cache = O.kv_cache_new(cfg, 2, cfg.T + 3)
+    got = [O.forward_cached(cfg, params, cache, tokens[:, :3])]
+    for t in range(3, cfg.T):
+        got.append(O.forward_cached(cfg, params, cache, tokens[:, t:t + 1]))
+    got = np.concatenate(got, axis=1)
+    assert cache["len"] == cfg.T
+    assert np.max(np.abs(got - zfull)) <= 1e-9 * max(1.0, np.max(np.abs(zfull)))
+    np.testing.assert_allclose(got, zfull, rtol=1e-11, atol=1e-12)
+
+
+def test_chunked_prefill_equals_full_forward():
+    """Chunks of 2, 4, 1 and 2 tokens: each query attends to every earlier
+    cached position and to the earlier queries of its own chunk only."""
+    cfg = tiny(H=4, Hkv=2, T=9, B=2)
+    params = rand_params(cfg, seed=43)
+    tokens = np.random.default_rng(44).integers(0, cfg.V, size=(2, cfg.T + 1))
+    _, full = O.forward(cfg, params, tokens)
+    cache = O.kv_cache_new(cfg, 2, cfg.T)
+    got, t = [], 0
+    for n in (2, 4, 1, 2):
+        got.append(O.forward_cached(cfg, params, cache, tokens[:, t:t + n]))
+        t += n
+    np.testing.assert_allclose(np.concatenate(got, axis=1), full["z"].reshape(2, cfg.T, cfg.V),
+                               rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("block,H,Hkv,kw", KV_CASES[:2] + KV_CASES[4:5])
+def test_cache_holds_rotated_keys_and_values(block, H, Hkv, kw):
+    """The cache rows of positions 0..T-1 are the full forward's rotated keys
+    and its values, layer by layer; rows past the written length stay 0."""
+    cfg = tiny(block=block, H=H, Hkv=Hkv, T=8, B=2, **kw)
+    params = rand_params(cfg, seed=45)
+    tokens = np.random.default_rng(46).integers(0, cfg.V, size=(2, cfg.T + 1))
+    _, full = O.forward(cfg, params, tokens)
+    cache = O.kv_cache_new(cfg, 2, cfg.T + 2)
+    O.forward_cached(cfg, params, cache, tokens[:, :5])
+    O.forward_cached(cfg, params, cache, tokens[:, 5:cfg.T])
+    for l in range(cfg.L):
+        np.testing.assert_allclose(cache["k"][l][:, :, :cfg.T], full["layers"][l]["k"], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(cache["v"][l][:, :, :cfg.T], full["layers"][l]["v"], rtol=1e-12, atol=1e-13)
+        assert not np.any(cache["k"][l][:, :, cfg.T:]) and not np.any(cache["v"][l][:, :, cfg.T:])
+    # the first head's keys at position 0 are the unrotated projection (angle 0)
+    n1 = full["layers"][0]["n1"]
+    qd = cfg.H * (cfg.C // cfg.H)
+    d = cfg.C // cfg.H
+    k0 = (n1 @ np.asarray(params["h0.qkvw"]).T)[0, qd:qd + d]
+    np.testing.assert_allclose(cache["k"][0][0, 0, 0], k0, rtol=1e-12, atol=1e-13)
+
+
+def test_cached_forward_rejects_overflowing_cache():
+    cfg = tiny(T=4, B=1)
+    params = rand_params(cfg, seed=47)
+    cache = O.kv_cache_new(cfg, 1, 4)
+    O.forward_cached(cfg, params, cache, np.zeros((1, 3), int))
+    with pytest.raises(ValueError):
+        O.forward_cached(cfg, params, cache, np.zeros((1, 2), int))
