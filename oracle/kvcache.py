@@ -62,16 +62,22 @@ def _cached_attention(q, kc, vc, pos0):
     return np.matmul(p, _expand_kv(vc, H))
 
 
-def forward_cached(cfg, params, cache, ids):
+def forward_cached(cfg, params, cache, ids, jitter=0.0, seed=0):
     """Run the next Tq tokens of each sequence through the model.
 
     ids: int [B, Tq].  Their positions are cache["len"] .. cache["len"]+Tq-1.
     Each layer rotates q and k at those absolute positions, writes the rotated
     keys and the values into the cache, and attends over every cached
     position up to the query's own.  Returns the logits [B, Tq, V] (rounded
-    like the full forward's) and advances cache["len"] by Tq."""
-    S = store_fn(cfg.act)
-    W = {k: S(np.asarray(v, np.float64)) for k, v in params.items()}
+    like the full forward's) and advances cache["len"] by Tq.
+
+    jitter/seed: as for the full forward (see store_fn), applied to the stored
+    activations only; the bf16 copy of the weights is the plain rounding.
+    With jitter = 2^-24 this is another valid bf16 computation of the same
+    call, whose distance from the plain one measures the spread that
+    storage-rounding flips cause."""
+    S = store_fn(cfg.act, jitter, seed)
+    W = {k: store_fn(cfg.act)(np.asarray(v, np.float64)) for k, v in params.items()}
     ids = np.asarray(ids)
     B, Tq = ids.shape
     pos0 = cache["len"]
