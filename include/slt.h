@@ -160,6 +160,39 @@ slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t
 slt_status slt_backward_accumulate(const slt_config* cfg, const void* params, const int32_t* tokens,
                                    void* acts, void* scratch, float* grads, float scale, void* stream);
 
+/* Key/value-cache forward (randyGPT, "Features": the prompt is run once and
+ * each further token costs one single-token forward; Transformer in Rust,
+ * "CodeGen Inference Pipeline": prefill fills the cache and every generated
+ * token appends its keys and values; strata, model table: the cache holds
+ * pre-rotated keys, and the cached decoder equals the full forward).
+ *
+ * slt_kv_cache_bytes: bytes of the cache for B sequences of up to Tmax
+ * positions, and of the workspace one slt_forward_cached call of Tq new
+ * tokens per sequence needs (a workspace sized for (B, Tq) serves every call
+ * with smaller B or Tq).  Host only; cfg->T and cfg->B are not used.
+ *
+ * slt_forward_cached: runs tokens [B, Tq] (row stride ld_tokens, ids in
+ * [0, V)) at positions pos0 .. pos0+Tq-1 of each sequence, pos0 being the
+ * number of positions already in the cache (pos0 = 0 starts a sequence and
+ * fills the RoPE table kept in the cache; the caller supplies pos0, the
+ * library keeps no length).  Each layer writes the new rows' rotated keys and
+ * values into the cache and attends each query to cached positions
+ * 0 .. its own; prompts of 16 or more tokens at pos0 = 0 use the training
+ * forward's attention kernel.  Logits: [B*Tq, V] (row stride ld_logits) of
+ * every new row, or [B, V] of the last row of each sequence when last_only
+ * != 0, in cfg->act.  params: compute copy as for slt_forward_loss.
+ * cache: caller-owned device memory of slt_kv_cache_bytes(Tmax) bytes, per
+ * layer K then V [B, Hkv, Tmax, d] in cfg->act, then the RoPE table;
+ * positions >= pos0+Tq are neither read nor written.  workspace: 256-byte
+ * aligned, contents not kept.  SLT_EINVAL when pos0 + Tq > Tmax or a size is
+ * non-positive; SLT_EUNSUPPORTED for head dimensions above 64. */
+slt_status slt_kv_cache_bytes(const slt_config* cfg, int32_t B, int32_t Tq, int32_t Tmax,
+                              int64_t* cache_bytes, int64_t* workspace_bytes);
+slt_status slt_forward_cached(const slt_config* cfg, const void* params, const int32_t* tokens, int32_t B,
+                              int32_t Tq, int64_t ld_tokens, int32_t pos0, void* cache, int32_t Tmax,
+                              void* workspace, int32_t last_only, void* logits, int64_t ld_logits,
+                              void* stream);
+
 /* AdamW on n flat fp32 elements at step t >= 1 (Hephaistos, "Architecture at a
  * glance"; strata, "AdamW (decoupled decay, bias-corrected)"):
  *   g = s grads;  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;

@@ -55,6 +55,9 @@ SIGNATURES = {
     "slt_forward_loss": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _P]),
     "slt_backward": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _P]),
     "slt_backward_accumulate": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _F, _P]),
+    "slt_kv_cache_bytes": (_I32, [ct.POINTER(slt_config), _I32, _I32, _I32, ct.POINTER(_I64), ct.POINTER(_I64)]),
+    "slt_forward_cached": (_I32, [ct.POINTER(slt_config), _P, _P, _I32, _I32, _I64, _I32, _P, _I32, _P, _I32,
+                                  _P, _I64, _P]),
     "slt_adamw_step": (_I32, [_I64, _P, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P, _P]),
     "slt_clip_workspace_bytes": (_I64, []),
     "slt_clip_grad_norm": (_I32, [_I64, _P, _I32, _F, _P, _P, _P, _P]),
@@ -204,6 +207,20 @@ def slt_backward_accumulate(cfg, params, tokens, acts, scratch, grads, scale, st
     _check("slt_backward_accumulate", load().slt_backward_accumulate(
         ct.byref(cfg), _ptr(params), _ptr(tokens), _ptr(acts), _ptr(scratch), _ptr(grads), scale,
         _stream(stream)))
+
+
+def slt_kv_cache_bytes(cfg, B, Tq, Tmax):
+    """(cache bytes, workspace bytes) of the key/value-cache forward."""
+    cb, wb = ct.c_int64(0), ct.c_int64(0)
+    _check("slt_kv_cache_bytes", load().slt_kv_cache_bytes(ct.byref(cfg), B, Tq, Tmax, ct.byref(cb), ct.byref(wb)))
+    return cb.value, wb.value
+
+
+def slt_forward_cached(cfg, params, tokens, B, Tq, ld_tokens, pos0, cache, Tmax, workspace, last_only, logits,
+                       ld_logits, stream=None):
+    _check("slt_forward_cached", load().slt_forward_cached(
+        ct.byref(cfg), _ptr(params), _ptr(tokens), B, Tq, ld_tokens, pos0, _ptr(cache), Tmax, _ptr(workspace),
+        int(last_only), _ptr(logits), ld_logits, _stream(stream)))
 
 
 def slt_adamw_step(n, master, shadow, grads, m, v, t, lr, beta1, beta2, eps, wd, decay_mask=None, grad_scale=None,

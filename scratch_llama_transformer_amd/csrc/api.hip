@@ -404,6 +404,114 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
 
 static bool is_dtype(int32_t d) { return d == SLT_F32 || d == SLT_BF16; }
 
+// ---------------------------------------------------------------------------
+// Key/value-cache forward: buffers for B sequences, Tq new rows each, and a
+// cache of Tmax positions.  The cache holds per layer K then V
+// ([B, Hkv, Tmax, d] each, activation type), then the RoPE table of Tmax
+// positions (fp32).
+// ---------------------------------------------------------------------------
+struct CachePlan {
+  int64_t kv, table, bytes;  // one K or V block, table offset, total cache bytes
+  int64_t x0, x1, n, r, mu, qkv, qrot, o, ab, h, lse, rot, part, ws_bytes;
+};
+
+static CachePlan cache_plan(const Plan& p, int B, int Tq, int Tmax) {
+  const slt_config& c = p.c;
+  CachePlan q;
+  q.kv = a256((int64_t)B * c.Hkv * Tmax * p.d * p.es);
+  q.table = 2 * c.L * q.kv;
+  q.bytes = q.table + a256((int64_t)Tmax * std::max(c.R, 2) * 4);
+  const int64_t M = (int64_t)B * Tq, es = p.es, C = c.C;
+  int64_t a = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = a;
+    a += a256(bytes);
+    return o;
+  };
+  q.x0 = take(M * C * es);
+  q.x1 = take(M * C * es);
+  q.n = take(M * C * es);
+  q.r = take(M * 4);
+  q.mu = take(M * 4);
+  q.qkv = take(M * (p.llama ? p.qkv_w : p.in_w) * es);
+  q.qrot = take(M * p.qd * 4);
+  q.o = take(M * (p.llama ? p.qd : p.ou_w) * es);
+  q.ab = p.llama ? take(M * 2 * c.F * es) : -1;
+  q.h = p.llama ? take(M * c.F * es) : -1;
+  q.lse = take((int64_t)B * c.H * Tq * 4);
+  q.rot = flash_eligible(c.act, p.d) ? take(flash_rot_elems(B, Tq, c.H, c.Hkv) * 2) : -1;
+  q.part = take(decode_attention_ws(B, Tq, c.H, c.Hkv, p.d, Tmax));
+  q.ws_bytes = a;
+  return q;
+}
+
+// Tq new tokens per sequence at positions pos0 .. pos0 + Tq - 1.  A prompt
+// of 16 or more tokens at pos0 = 0 runs the training forward's attention on
+// the projections; every other call attends over the cache.
+static slt_status forward_cached(const Plan& p, const Ctx& x, const CachePlan& q, const int32_t* tok, int B, int Tq,
+                                 int64_t ldt, int pos0, char* cache, int Tmax, bool last_only, void* logits,
+                                 int64_t ldz) {
+  const slt_config& c = p.c;
+  const int M = B * Tq, C = c.C;
+  float* cs = reinterpret_cast<float*>(cache + q.table);
+  if (c.R > 0 && pos0 == 0) SLT_TRY(launch_rope_table(Tmax, c.R, c.rope_base, cs, x.s));
+  const bool prefill = pos0 == 0 && Tq >= 16;
+  void* xa = x.A(q.x0);
+  void* xb = x.A(q.x1);
+  SLT_TRY(launch_embedding_fwd(tok, B, Tq, ldt, x.P(p.wte), xa, c.V, C, x.dt, x.s));
+  for (int l = 0; l < c.L; ++l) {
+    const LayerP& W = p.lp[l];
+    char* Kc = cache + 2 * l * q.kv;
+    char* Vc = Kc + q.kv;
+    char* qkv = (char*)x.A(q.qkv);
+    char* ou = (char*)x.A(q.o);
+    const int64_t ldqkv = p.llama ? p.qkv_w : p.in_w, ldo = p.llama ? p.qd : p.ou_w;
+    if (p.llama)
+      SLT_TRY(launch_rmsnorm_fwd(xa, x.P(W.norm1), x.A(q.n), (float*)x.A(q.r), M, C, c.eps, x.dt, x.s));
+    else
+      SLT_TRY(launch_layernorm_fwd(xa, x.P(W.norm1), x.P(W.norm1b), x.A(q.n), (float*)x.A(q.mu), (float*)x.A(q.r),
+                                   M, C, c.eps, x.dt, x.s));
+    SLT_TRY(proj(x, M, (int)ldqkv, C, x.A(q.n), C, x.P(W.qkvw), qkv, ldqkv, nullptr, 0));
+    SLT_TRY(launch_kv_append(qkv, ldqkv, (float*)x.A(q.qrot), B, Tq, pos0, c.H, c.Hkv, p.d, c.R, c.rope_mode, cs, Kc,
+                             Vc, Tmax, x.dt, x.s));
+    if (prefill) {
+      AttnArgs at{};
+      at.B = B; at.T = Tq; at.H = c.H; at.Hkv = c.Hkv; at.d = p.d; at.R = c.R; at.rope_mode = c.rope_mode;
+      at.dtype = x.dt; at.cs = cs;
+      at.lse = (float*)x.A(q.lse);
+      at.rot = q.rot >= 0 ? x.A(q.rot) : nullptr;
+      at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
+      at.ldq = at.ldk = at.ldv = ldqkv;
+      at.out = ou; at.ldo = ldo;
+      SLT_TRY(launch_attention_fwd(at, x.s));
+    } else {
+      SLT_TRY(launch_attention_decode((const float*)x.A(q.qrot), Kc, Vc, ou, ldo, B, Tq, pos0, c.H, c.Hkv, p.d, Tmax,
+                                      x.dt, (float*)x.A(q.part), x.s));
+    }
+    if (p.llama) {
+      SLT_TRY(proj(x, M, C, p.qd, ou, p.qd, x.P(W.wo), xb, C, xa, C));
+      SLT_TRY(launch_rmsnorm_fwd(xb, x.P(W.norm2), x.A(q.n), (float*)x.A(q.r), M, C, c.eps, x.dt, x.s));
+      char* ab = (char*)x.A(q.ab);
+      SLT_TRY(proj(x, M, 2 * c.F, C, x.A(q.n), C, x.P(W.w1), ab, 2 * c.F, nullptr, 0));
+      SLT_TRY(launch_swiglu_fwd(ab, ab + c.F * p.es, x.A(q.h), M, c.F, 2 * c.F, 2 * c.F, c.F, x.dt, x.s));
+      SLT_TRY(proj(x, M, C, c.F, x.A(q.h), c.F, x.P(W.w2), xa, C, xb, C));
+    } else {
+      SLT_TRY(launch_gelu_fwd(qkv + p.qkv_w * p.es, ou + p.qd * p.es, M, c.F, p.in_w, p.ou_w, x.dt, x.s));
+      SLT_TRY(proj(x, M, C, p.ou_w, ou, p.ou_w, x.P(W.wout), xb, C, xa, C));
+      std::swap(xa, xb);
+    }
+  }
+  if (p.llama)
+    SLT_TRY(launch_rmsnorm_fwd(xa, x.P(p.normf), x.A(q.n), (float*)x.A(q.r), M, C, c.eps, x.dt, x.s));
+  else
+    SLT_TRY(launch_layernorm_fwd(xa, x.P(p.normf), x.P(p.normfb), x.A(q.n), (float*)x.A(q.mu), (float*)x.A(q.r), M,
+                                 C, c.eps, x.dt, x.s));
+  if (last_only)
+    return proj(x, B, c.V, C, (char*)x.A(q.n) + (int64_t)(Tq - 1) * C * p.es, (int64_t)Tq * C, x.P(p.head), logits,
+                ldz, nullptr, 0);
+  return proj(x, M, c.V, C, x.A(q.n), C, x.P(p.head), logits, ldz, nullptr, 0);
+}
+
 }  // namespace slt
 
 using namespace slt;
@@ -736,6 +844,33 @@ slt_status slt_softmax_xent(void* z, int64_t ldz, const int32_t* tokens, int32_t
     return fail(SLT_EINVAL, "softmax_xent: bad sizes");
   if (!z || !tokens || !loss || !workspace) return fail(SLT_EINVAL, "softmax_xent: NULL pointer");
   return launch_softmax_xent(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtype, workspace, as_stream(stream));
+}
+
+slt_status slt_kv_cache_bytes(const slt_config* cfg, int32_t B, int32_t Tq, int32_t Tmax, int64_t* cache_bytes,
+                              int64_t* workspace_bytes) {
+  Plan p;
+  SLT_TRY(make_plan(cfg, p));
+  if (B <= 0 || Tq <= 0 || Tmax <= 0 || Tq > Tmax) return fail(SLT_EINVAL, "kv cache: need B, Tq > 0 and Tq <= Tmax");
+  if (!cache_bytes || !workspace_bytes) return fail(SLT_EINVAL, "kv cache: output pointers must not be NULL");
+  const CachePlan q = cache_plan(p, B, Tq, Tmax);
+  *cache_bytes = q.bytes;
+  *workspace_bytes = q.ws_bytes;
+  return SLT_OK;
+}
+
+slt_status slt_forward_cached(const slt_config* cfg, const void* params, const int32_t* tokens, int32_t B, int32_t Tq,
+                              int64_t ld_tokens, int32_t pos0, void* cache, int32_t Tmax, void* workspace,
+                              int32_t last_only, void* logits, int64_t ld_logits, void* stream) {
+  Plan p;
+  SLT_TRY(make_plan(cfg, p));
+  if (B <= 0 || Tq <= 0 || pos0 < 0 || Tmax <= 0 || (int64_t)pos0 + Tq > Tmax)
+    return fail(SLT_EINVAL, "forward_cached: need B, Tq > 0, pos0 >= 0 and pos0 + Tq <= Tmax");
+  if (ld_tokens < Tq || ld_logits < cfg->V) return fail(SLT_EINVAL, "forward_cached: ld_tokens < Tq or ld_logits < V");
+  if ((int64_t)B * Tq > (1 << 30)) return fail(SLT_EUNSUPPORTED, "forward_cached: too many rows");
+  if (!params || !tokens || !cache || !workspace || !logits) return fail(SLT_EINVAL, "forward_cached: NULL pointer");
+  Ctx x{p, as_stream(stream), (char*)workspace, nullptr, (const char*)params, cfg->act};
+  return forward_cached(p, x, cache_plan(p, B, Tq, Tmax), tokens, B, Tq, ld_tokens, pos0, (char*)cache, Tmax,
+                        last_only != 0, logits, ld_logits);
 }
 
 }  // extern "C"

@@ -158,4 +158,13 @@ bool flash_ok(const AttnArgs& a, bool bwd);
 slt_status flash_fwd(const AttnArgs& a, hipStream_t s);
 slt_status flash_bwd(const AttnArgs& a, hipStream_t s);
 
+// Key/value cache (decode.hip): append rotated keys and values of Tq new rows
+// per sequence at positions pos0.., and attend those rows over the cache.
+slt_status launch_kv_append(const void* qkv, int64_t ld, float* qrot, int B, int Tq, int pos0, int H, int Hkv, int d,
+                            int R, int mode, const float* cs, void* Kc, void* Vc, int Tmax, int dtype, hipStream_t s);
+int64_t decode_attention_ws(int B, int Tq, int H, int Hkv, int d, int Tmax);
+slt_status launch_attention_decode(const float* qrot, const void* Kc, const void* Vc, void* out, int64_t ldo, int B,
+                                   int Tq, int pos0, int H, int Hkv, int d, int Tmax, int dtype, float* ws,
+                                   hipStream_t s);
+
 }  // namespace slt

@@ -109,3 +109,36 @@ class TrainStep:
             B.slt_backward_accumulate(self.cfg, self.compute_params, tok, self.acts, self.scratch, self.grads,
                                       1.0 / S)
         return float(total.item()) / S
+
+
+class CachedForward:
+    """Key/value cache and workspace for incremental forwards of one model:
+    ``run(tokens)`` feeds the next Tq tokens of each of the B sequences
+    (prefill when the cache is empty, then single tokens) through
+    slt_forward_cached and returns their logits.  ``params`` is the compute
+    copy of the flat parameters (a TrainStep's ``compute_params``)."""
+
+    def __init__(self, wcfg, params: torch.Tensor, batch: int, Tmax: int, Tq_max: int, device: str = "cuda"):
+        self.w = wcfg
+        self.cfg = B.make_config(wcfg)
+        B.slt_validate(self.cfg)
+        self.params = params
+        self.B, self.Tmax, self.Tq_max = batch, Tmax, Tq_max
+        cache_bytes, ws_bytes = B.slt_kv_cache_bytes(self.cfg, batch, Tq_max, Tmax)
+        self.cache = torch.empty(cache_bytes, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.dtype = torch.bfloat16 if wcfg.act == "bf16" else torch.float32
+        self.pos = 0
+
+    def run(self, tokens: torch.Tensor, last_only: bool = False) -> torch.Tensor:
+        """tokens: int32 [B, Tq] on the device.  Returns logits [B, Tq, V]
+        (or [B, V] with last_only) in the activation dtype."""
+        Bn, Tq = tokens.shape
+        if Bn != self.B or Tq > self.Tq_max:
+            raise ValueError("batch or chunk length does not fit this cache")
+        rows = Bn if last_only else Bn * Tq
+        z = torch.empty(rows, self.w.V, dtype=self.dtype, device=self.cache.device)
+        B.slt_forward_cached(self.cfg, self.params, tokens, Bn, Tq, tokens.stride(0), self.pos, self.cache,
+                             self.Tmax, self.ws, last_only, z, self.w.V)
+        self.pos += Tq
+        return z if last_only else z.view(Bn, Tq, self.w.V)

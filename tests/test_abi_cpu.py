@@ -123,3 +123,21 @@ def test_host_calls_reject_bad_arguments_before_launch():
     assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 24, 1) == 0
     assert B.slt_attention_bwd_workspace(2, 64, 4, 2, 24, 1) == 2 * 4 * 64 * 4
     assert lib.slt_softmax_xent(None, 10, None, 1, 4, 5, 10, None, None, 1, None, None) == 1
+
+
+def test_kv_cache_sizes():
+    """Cache = per layer K and V [B, Hkv, Tmax, d] (256-byte aligned each),
+    then the RoPE table [Tmax, R] fp32; bad sizes are rejected on the host."""
+    from scratch_llama_transformer_amd import binding as B
+    a256 = lambda n: (n + 255) // 256 * 256
+    for i in (1, 3, 4, 5):
+        w = W.get_config(i)
+        cfg = B.make_config(w)
+        d, es = w.C // w.H, (2 if w.act == "bf16" else 4)
+        for Bn, Tq, Tmax in ((1, 1, 16), (3, 5, 300)):
+            cb, wb = B.slt_kv_cache_bytes(cfg, Bn, Tq, Tmax)
+            assert cb == 2 * w.L * a256(Bn * w.Hkv * Tmax * d * es) + a256(Tmax * max(w.R, 2) * 4)
+            assert wb > 0
+        for bad in ((0, 1, 16), (1, 0, 16), (1, 17, 16), (1, 1, 0)):
+            with pytest.raises(B.SltError):
+                B.slt_kv_cache_bytes(cfg, *bad)
