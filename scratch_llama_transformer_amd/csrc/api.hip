@@ -65,7 +65,7 @@ struct Plan {
   std::vector<LayerA> la;
   int64_t nf, rf, muf, z, cs, act_bytes;
   // scratch
-  int64_t rowloss, dx, dbig, dmid, dn, delta, normws, embws, gemmws, gemmws_bytes, scratch_bytes;
+  int64_t rowloss, dx, dx2, dbig, dqkv, dmid, dn, delta, normws, embws, gemmws, gemmws_bytes, scratch_bytes;
   int dbig_w, dmid_w;
 };
 
@@ -203,7 +203,9 @@ static slt_status make_plan(const slt_config* cfg, Plan& p) {
   };
   p.rowloss = takes(N * 4);
   p.dx = takes(N * C * es);
+  p.dx2 = takes(N * C * es);  // residual-stream gradient between the two sub-blocks of a layer
   p.dbig = takes(N * p.dbig_w * es);
+  p.dqkv = p.llama ? takes(N * p.qkv_w * es) : -1;  // kept apart from dbig until the layer's dW launch
   p.dmid = takes(N * p.dmid_w * es);
   p.dn = takes(N * C * es);
   p.delta = takes(attention_bwd_ws(c.B, c.H, c.T));
@@ -253,6 +255,47 @@ static slt_status proj_dw(const Ctx& x, int M, int N, int K, const void* dY, int
              reinterpret_cast<float*>(x.S(x.p.gemmws)), x.p.gemmws_bytes};
   g.alpha = x.gw.alpha;
   return launch_gemm(g, x.s);
+}
+
+// Weight gradients deferred to the end of a layer's backward walk, so that
+// they run as one grouped launch (every product fits the grouped kernel) or
+// else one GEMM each, in the order they were added.
+struct DwList {
+  struct Item {
+    int M, N, K;
+    const void* dY;
+    int64_t lddy;
+    const void* X;
+    int64_t ldx;
+    float* dW;
+    int64_t ldw;
+  };
+  Item it[6];
+  int n = 0;
+  // dW[N, K] = dY[M, N]^T X[M, K]
+  void add(int M, int N, int K, const void* dY, int64_t lddy, const void* X, int64_t ldx, float* dW, int64_t ldw) {
+    it[n++] = Item{M, N, K, dY, lddy, X, ldx, dW, ldw};
+  }
+};
+
+static slt_status flush_dw(const Ctx& x, DwList& L) {
+  bool group = x.dt == SLT_BF16 && L.n > 1;
+  GroupItem g[6];
+  for (int i = 0; i < L.n && group; ++i) {
+    const DwList::Item& t = L.it[i];
+    g[i] = GroupItem{t.N, t.K, t.dY, t.lddy, t.X, t.ldx, t.dW, t.ldw, x.gw.alpha, x.gw.accumulate};
+    group = t.M == L.it[0].M && gemm_group_ok(g[i], t.M);
+  }
+  if (group) {
+    SLT_TRY(launch_gemm_group(g, L.n, L.it[0].M, reinterpret_cast<float*>(x.S(x.p.gemmws)), x.p.gemmws_bytes, x.s));
+  } else {
+    for (int i = 0; i < L.n; ++i) {
+      const DwList::Item& t = L.it[i];
+      SLT_TRY(proj_dw(x, t.M, t.N, t.K, t.dY, t.lddy, t.X, t.ldx, t.dW, t.ldw));
+    }
+  }
+  L.n = 0;
+  return SLT_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -330,8 +373,11 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
   char* dmid = (char*)x.S(p.dmid);
   void* nws = x.S(p.normws);
 
-  // lm_head and final norm
-  SLT_TRY(proj_dw(x, N, c.V, C, x.A(p.z), c.V, x.A(p.nf), C, grads + p.head, C));
+  void* dx2 = x.S(p.dx2);
+  DwList dws;
+
+  // lm_head and final norm (its weight gradient joins the last layer's launch)
+  dws.add(N, c.V, C, x.A(p.z), c.V, x.A(p.nf), C, grads + p.head, C);
   SLT_TRY(proj_dx(x, N, c.V, C, x.A(p.z), c.V, x.P(p.head), C, dn, C));
   if (p.llama)
     SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.rf), dn, nullptr, dx,
@@ -354,34 +400,38 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     at.rot_ready = true;
     char* qkv = (char*)x.A(A.qkv);
     if (p.llama) {
+      // dx: gradient at x_out, kept until the layer's weight gradients;
+      // dx2: gradient at x_mid; dbig: [da | db]; dqkv: [dq | dk | dv].
+      char* dqkv = (char*)x.S(p.dqkv);
       // x_out = x_mid + h W2^T
-      SLT_TRY(proj_dw(x, N, C, c.F, dx, C, x.A(A.h), c.F, grads + W.w2, c.F));
+      dws.add(N, C, c.F, dx, C, x.A(A.h), c.F, grads + W.w2, c.F);
       SLT_TRY(proj_dx(x, N, C, c.F, dx, C, x.P(W.w2), c.F, dmid, c.F));
       char* ab = (char*)x.A(A.ab);
       SLT_TRY(launch_swiglu_bwd(ab, ab + c.F * p.es, dmid, dbig, dbig + c.F * p.es, N, c.F, 2 * c.F, 2 * c.F, c.F,
                                 2 * c.F, 2 * c.F, x.dt, x.s));
-      SLT_TRY(proj_dw(x, N, 2 * c.F, C, dbig, 2 * c.F, x.A(A.n2), C, grads + W.w1, C));
+      dws.add(N, 2 * c.F, C, dbig, 2 * c.F, x.A(A.n2), C, grads + W.w1, C);
       SLT_TRY(proj_dx(x, N, 2 * c.F, C, dbig, 2 * c.F, x.P(W.w1), C, dn, C));
-      SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l + 1]), x.P(W.norm2), (const float*)x.A(A.r2), dn, dx, dx,
+      SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l + 1]), x.P(W.norm2), (const float*)x.A(A.r2), dn, dx, dx2,
                                  grads + W.norm2, N, C, x.dt, nws, x.s, x.gw));
       // x_mid = x_in + o W_o^T
-      SLT_TRY(proj_dw(x, N, C, p.qd, dx, C, x.A(A.o), p.qd, grads + W.wo, p.qd));
-      SLT_TRY(proj_dx(x, N, C, p.qd, dx, C, x.P(W.wo), p.qd, dmid, p.qd));
+      dws.add(N, C, p.qd, dx2, C, x.A(A.o), p.qd, grads + W.wo, p.qd);
+      SLT_TRY(proj_dx(x, N, C, p.qd, dx2, C, x.P(W.wo), p.qd, dmid, p.qd));
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
       at.ldq = at.ldk = at.ldv = p.qkv_w;
       at.o = x.A(A.o); at.ldo = p.qd;
       at.dout = dmid; at.lddo = p.qd;
-      at.dq = dbig; at.dk = dbig + p.qd * p.es; at.dv = dbig + (p.qd + p.kd) * p.es;
+      at.dq = dqkv; at.dk = dqkv + p.qd * p.es; at.dv = dqkv + (p.qd + p.kd) * p.es;
       at.lddq = at.lddk = at.lddv = p.qkv_w;
       SLT_TRY(launch_attention_bwd(at, x.s));
-      SLT_TRY(proj_dw(x, N, p.qkv_w, C, dbig, p.qkv_w, x.A(A.n1), C, grads + W.qkvw, C));
-      SLT_TRY(proj_dx(x, N, p.qkv_w, C, dbig, p.qkv_w, x.P(W.qkvw), C, dn, C));
-      SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l]), x.P(W.norm1), (const float*)x.A(A.r1), dn, dx, dx,
+      dws.add(N, p.qkv_w, C, dqkv, p.qkv_w, x.A(A.n1), C, grads + W.qkvw, C);
+      SLT_TRY(flush_dw(x, dws));
+      SLT_TRY(proj_dx(x, N, p.qkv_w, C, dqkv, p.qkv_w, x.P(W.qkvw), C, dn, C));
+      SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l]), x.P(W.norm1), (const float*)x.A(A.r1), dn, dx2, dx,
                                  grads + W.norm1, N, C, x.dt, nws, x.s, x.gw));
     } else {
       char* ou = (char*)x.A(A.o);
       // x_out = x_in + [o | u] W_out^T
-      SLT_TRY(proj_dw(x, N, C, p.ou_w, dx, C, ou, p.ou_w, grads + W.wout, p.ou_w));
+      dws.add(N, C, p.ou_w, dx, C, ou, p.ou_w, grads + W.wout, p.ou_w);
       SLT_TRY(proj_dx(x, N, C, p.ou_w, dx, C, x.P(W.wout), p.ou_w, dmid, p.ou_w));
       SLT_TRY(launch_gelu_bwd(qkv + p.qkv_w * p.es, dmid + p.qd * p.es, dbig + p.qkv_w * p.es, N, c.F, p.in_w,
                               p.ou_w, p.in_w, x.dt, x.s));
@@ -392,7 +442,8 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       at.dq = dbig; at.dk = dbig + p.qd * p.es; at.dv = dbig + (p.qd + p.kd) * p.es;
       at.lddq = at.lddk = at.lddv = p.in_w;
       SLT_TRY(launch_attention_bwd(at, x.s));
-      SLT_TRY(proj_dw(x, N, p.in_w, C, dbig, p.in_w, x.A(A.n1), C, grads + W.qkvw, C));
+      dws.add(N, p.in_w, C, dbig, p.in_w, x.A(A.n1), C, grads + W.qkvw, C);
+      SLT_TRY(flush_dw(x, dws));
       SLT_TRY(proj_dx(x, N, p.in_w, C, dbig, p.in_w, x.P(W.qkvw), C, dn, C));
       SLT_TRY(launch_layernorm_bwd(x.A(p.xs[l]), x.P(W.norm1), (const float*)x.A(A.mu1), (const float*)x.A(A.r1),
                                    dn, dx, dx, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws, x.s, x.gw));

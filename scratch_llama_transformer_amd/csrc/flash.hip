@@ -65,6 +65,23 @@ __device__ __forceinline__ u32x4 cat(const u32x2& lo, const u32x2& hi) { return 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float bf_hi(float x) { return __uint_as_float((uint32_t)f32_to_bf16_bits(x) << 16); }
 
+// Maximum and sum over the four lanes l, l^16, l^32, l^48 (the lanes holding
+// one query's keys) with gfx950's v_permlane32_swap / v_permlane16_swap: with
+// both operands equal, the swap leaves each lane its own value in one result
+// and its partner's in the other, so no LDS round trip is needed.
+__device__ __forceinline__ float max4lanes(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float sum4lanes(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Work item of this block: consecutive block ids go round-robin to the 8
 // XCDs, so the id is remapped to give each XCD one contiguous range of work
 // items -- the tiles of one (batch, head) then share that XCD's L2.
@@ -161,6 +178,34 @@ __device__ __forceinline__ void rd_cols16(unsigned c0, unsigned c1, unsigned c2,
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int c = 0; c < 2; ++c) f[dt][c] = cat(x[dt][c][0], x[dt][c][1]);
+}
+// K row fragments of one 32-key half (16-key groups tt = 0, 1) of a hi tile
+// and of the lo tile 8 KiB after it: f[hl][tt][s].  a0 / a1 = tile address
+// plus the lane's row[0] / row[1] plus 4096 per half.
+__device__ __forceinline__ void rd_khalf(unsigned a0, unsigned a1, u32x4 (&f)[2][2][2]) {
+  asm volatile(FL_R128(h00, a0, 0) FL_R128(h01, a1, 0) FL_R128(h10, a0, 2048) FL_R128(h11, a1, 2048)
+                   FL_R128(l00, a0, 8192) FL_R128(l01, a1, 8192) FL_R128(l10, a0, 10240)
+                       FL_R128(l11, a1, 10240) "s_waitcnt lgkmcnt(0)"
+               : FL_O(h00, f[0][0][0]), FL_O(h01, f[0][0][1]), FL_O(h10, f[0][1][0]), FL_O(h11, f[0][1][1]),
+                 FL_O(l00, f[1][0][0]), FL_O(l01, f[1][0][1]), FL_O(l10, f[1][1][0]), FL_O(l11, f[1][1][1])
+               : [a0] "v"(a0), [a1] "v"(a1)
+               : "memory");
+}
+
+// Column fragments of one 32-row half of a tile: f[dt] = rows 32 hf +
+// (4g..4g+3, then 16 + 4g..4g+3) at dims 16 dt + i.  cK = tile address plus
+// the lane's col[dt] plus 4096 hf.
+__device__ __forceinline__ void rd_chalf(unsigned c0, unsigned c1, unsigned c2, unsigned c3, u32x4 (&f)[4]) {
+  u32x2 x[4][2];
+  asm volatile(FL_RTR(x00, c0, 0) FL_RTR(x01, c0, 2048) FL_RTR(x10, c1, 0) FL_RTR(x11, c1, 2048)
+                   FL_RTR(x20, c2, 0) FL_RTR(x21, c2, 2048) FL_RTR(x30, c3, 0) FL_RTR(x31, c3, 2048)
+                       "s_waitcnt lgkmcnt(0)"
+               : FL_O(x00, x[0][0]), FL_O(x01, x[0][1]), FL_O(x10, x[1][0]), FL_O(x11, x[1][1]),
+                 FL_O(x20, x[2][0]), FL_O(x21, x[2][1]), FL_O(x30, x[3][0]), FL_O(x31, x[3][1])
+               : [c0] "v"(c0), [c1] "v"(c1), [c2] "v"(c2), [c3] "v"(c3)
+               : "memory");
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) f[dt] = cat(x[dt][0], x[dt][1]);
 }
 #undef FL_R128
 #undef FL_RTR
@@ -314,108 +359,137 @@ __global__ __launch_bounds__(128) void fl_prep_k(const bf16* __restrict__ q, int
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  ceil(T/64) H B workgroups, one per (query tile, head, batch).  Wave w owns queries q0 + 16w + i; per
-// key tile: S^T = K Q^T (hi/lo), online softmax in base 2, O^T += V^T P^T.
-// LDS stage: [K hi | K lo | V], two stages.
+// Forward, one workgroup per (256-query chunk, head, batch), longest chunks
+// first.  Wave w owns the 16-query subtiles u = w, w+4, w+8, w+12 of the
+// chunk, their rotated queries held as MFMA fragments in registers.  Key /
+// value tiles of 64 rows stream through a three-stage LDS ring ([K hi | K lo
+// | V] per stage, two tiles in flight while one is used); each 32-key half
+// is read from LDS once per wave and applied to all of the wave's subtiles
+// that reach it, so a tile is fetched once per chunk and its fragments once
+// per wave.  Per subtile and half: S^T = K Q^T (hi/lo), online softmax in
+// base 2, O^T += V^T P^T.  Subtile u needs key tile j iff 64 j <= 16 u + 15
+// (chunk-relative), i.e. subtile i = 0..3 of a wave from tile i on, so every
+// wave does the same work.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void fl_fwd_k(FlArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2][3 * FTB];
-  const int T = a.T, ntq = (T + FR - 1) / FR;
+constexpr int FC = 256;  // queries per chunk
+
+__global__ __launch_bounds__(256, 2) void fl_fwd2_k(FlArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[3][3 * FTB];
+  const int T = a.T, nck = (T + FC - 1) / FC;
   const int w = fl_work_item();
-  const int qt = ntq - 1 - w % ntq, h = (w / ntq) % a.H, b = w / (ntq * a.H);  // longest rows first
-  const int q0 = qt * FR, kvh = h / (a.H / a.Hkv);
+  const int ck = nck - 1 - w % nck, h = (w / nck) % a.H, b = w / (nck * a.H);
+  const int c0 = ck * FC, kvh = h / (a.H / a.Hkv);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4;
-  const int qi = q0 + wave * 16 + (lane & 15);
-  const int qc = min(qi, T - 1);
+  const int g = lane >> 4, li = lane & 15;
   const int nch = a.d / 8;
   const FlOff off(lane);
 
-  const int64_t qrow = ((int64_t)(b * a.H + h) * T + qc) * FD;
-  u32x4 qh[2], ql[2];
+  // subtile i of this wave: queries c0 + 16 (wave + 4 i) + li
+  u32x4 qh[4][2], ql[4][2];
+  const int64_t qb = (int64_t)(b * a.H + h) * T;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    qh[s] = *reinterpret_cast<const u32x4*>(a.qh + qrow + 32 * s + 8 * g);
-    ql[s] = *reinterpret_cast<const u32x4*>(a.ql + qrow + 32 * s + 8 * g);
+  for (int i = 0; i < 4; ++i) {
+    const int qc = min(c0 + 16 * (wave + 4 * i) + li, T - 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      qh[i][s] = *reinterpret_cast<const u32x4*>(a.qh + (qb + qc) * FD + 32 * s + 8 * g);
+      ql[i][s] = *reinterpret_cast<const u32x4*>(a.ql + (qb + qc) * FD + 32 * s + 8 * g);
+    }
   }
   const int64_t kbase = (int64_t)(b * a.Hkv + kvh) * T * FD;
   const bf16* kh = a.kh + kbase;
   const bf16* kl = a.kl + kbase;
   const bf16* vb = a.v + (int64_t)b * T * a.ldv + (int64_t)kvh * a.d;
 
-  f32x4 oacc[4];
+  f32x4 oacc[4][4];
+  float m[4], l[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
-
-  const int nt = qt + 1;
-  fl_issue(kh, FD, 0, T, 8, lds[0], wave, lane);
-  fl_issue(kl, FD, 0, T, 8, lds[0] + FTB, wave, lane);
-  fl_issue(vb, a.ldv, 0, T, nch, lds[0] + 2 * FTB, wave, lane);
-  for (int kt = 0; kt < nt; ++kt) {
-    SLT_WAIT_VMCNT(0);
-    lds_barrier();
-    if (kt + 1 < nt) {
-      char* nx = lds[(kt + 1) & 1];
-      const int r0 = (kt + 1) * FR;
-      fl_issue(kh, FD, r0, T, 8, nx, wave, lane);
-      fl_issue(kl, FD, r0, T, 8, nx + FTB, wave, lane);
-      fl_issue(vb, a.ldv, r0, T, nch, nx + 2 * FTB, wave, lane);
-    }
-    const unsigned base = lds_off(lds[kt & 1]);
-    u32x4 kf[2][4][2];
-    rd_rows16(base + off.row[0], base + off.row[1], kf);
-    float sv[4][4];
-    float tmax = -INFINITY;
-    const int k0 = kt * FR;
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        st = mma(kf[0][t][s], qh[s], st);
-        st = mma(kf[0][t][s], ql[s], st);
-        st = mma(kf[1][t][s], qh[s], st);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[t][r] = st[r];
-      if (kt == qt) {  // the diagonal tile: keys after the query are masked
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (k0 + 16 * t + 4 * g + r > qi) sv[t][r] = -INFINITY;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sv[t][r]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = ex2(m - mn);
-    float rs = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[t][r] = ex2(sv[t][r] - mn);
-        rs += sv[t][r];
-      }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-    l = l * alpha + rs;
-    m = mn;
-    const u32x4 pb[2] = {pack_k(sv[0], sv[1]), pack_k(sv[2], sv[3])};
-    u32x4 vf[4][2];
-    rd_cols(base + 2 * FTB, off, vf);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      oacc[dt] *= alpha;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) oacc[dt] = mma(vf[dt][c], pb[c], oacc[dt]);
-    }
+    for (int dt = 0; dt < 4; ++dt) oacc[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (qi < T) {
-    const float inv = 1.0f / l;
+  // key tiles 0 .. nt-1 cover keys up to the chunk's last query
+  const int nt = (min(T, c0 + FC) + FR - 1) / FR;
+  auto issue = [&](int j, char* st) {
+    fl_issue(kh, FD, j * FR, T, 8, st, wave, lane);
+    fl_issue(kl, FD, j * FR, T, 8, st + FTB, wave, lane);
+    fl_issue(vb, a.ldv, j * FR, T, nch, st + 2 * FTB, wave, lane);
+  };
+  issue(0, lds[0]);
+  issue(min(1, nt - 1), lds[1]);  // past the end: tile 0 again, into a stage nobody reads
+  for (int j = 0; j < nt; ++j) {
+    SLT_WAIT_VMCNT(6);  // only the copies of tile j+1 may still fly
+    lds_barrier();
+    issue(min(j + 2, nt - 1), lds[(j + 2) % 3]);
+    const unsigned base = lds_off(lds[j % 3]);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int k0 = j * FR + 32 * hf;  // first key of this half
+      // subtiles whose last query reaches this half (uniform over the wave)
+      if (k0 > c0 + 16 * (wave + 12) + 15 || k0 >= T) break;
+      u32x4 kf[2][2][2], vf[4];
+      rd_khalf(base + off.row[0] + 4096 * hf, base + off.row[1] + 4096 * hf, kf);
+      rd_chalf(base + 2 * FTB + off.col[0] + 4096 * hf, base + 2 * FTB + off.col[1] + 4096 * hf,
+               base + 2 * FTB + off.col[2] + 4096 * hf, base + 2 * FTB + off.col[3] + 4096 * hf, vf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int u0 = c0 + 16 * (wave + 4 * i);  // first query of subtile i
+        if (k0 > u0 + 15 || u0 >= T) continue;
+        const int qi = u0 + li;
+        float sv[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            st = mma(kf[0][tt][s], qh[i][s], st);
+            st = mma(kf[0][tt][s], ql[i][s], st);
+            st = mma(kf[1][tt][s], qh[i][s], st);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sv[tt][r] = st[r];
+          if (k0 + 31 > u0) {  // keys after a query of the subtile are masked
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (k0 + 16 * tt + 4 * g + r > qi) sv[tt][r] = -INFINITY;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sv[tt][r]);
+        }
+        const float mn = fmaxf(m[i], max4lanes(tmax));
+        const float alpha = ex2(m[i] - mn);
+        float rs = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sv[tt][r] = ex2(sv[tt][r] - mn);
+            rs += sv[tt][r];
+          }
+        l[i] = l[i] * alpha + rs;  // this lane's keys only; the four lanes are summed at the end
+        m[i] = mn;
+        const u32x4 pb = pack_k(sv[0], sv[1]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          oacc[i][dt] *= alpha;
+          oacc[i][dt] = mma(vf[dt], pb, oacc[i][dt]);
+        }
+      }
+    }
+  }
+  SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l[i] = sum4lanes(l[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = c0 + 16 * (wave + 4 * i) + li;
+    if (qi >= T) continue;
+    const float inv = 1.0f / l[i];
     bf16* ob = a.out + ((int64_t)b * T + qi) * a.ldo + (int64_t)h * a.d;
     bf16* rb = a.ores_out ? a.ores_out + ((int64_t)b * T + qi) * a.ldores + (int64_t)h * a.d : nullptr;
 #pragma unroll
@@ -425,7 +499,7 @@ __global__ __launch_bounds__(256) void fl_fwd_k(FlArgs a) {
       float v[4], lo[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] = oacc[dt][r] * inv;
+        v[r] = oacc[i][dt][r] * inv;
         lo[r] = v[r] - bf_hi(v[r]);
       }
       *reinterpret_cast<u32x2*>(ob + j0) = u32x2{f32x2_to_bf16x2_bits(v[0], v[1]), f32x2_to_bf16x2_bits(v[2], v[3])};
@@ -433,7 +507,7 @@ __global__ __launch_bounds__(256) void fl_fwd_k(FlArgs a) {
         *reinterpret_cast<u32x2*>(rb + j0) =
             u32x2{f32x2_to_bf16x2_bits(lo[0], lo[1]), f32x2_to_bf16x2_bits(lo[2], lo[3])};
     }
-    if (g == 0) a.lse[((int64_t)b * a.H + h) * T + qi] = (m + log2f(l)) * kLn2;
+    if (g == 0) a.lse[((int64_t)b * a.H + h) * T + qi] = (m[i] + log2f(l[i])) * kLn2;
   }
 }
 
@@ -529,8 +603,7 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
       }
     }
   }
-  D += __shfl_xor(D, 16, 64);
-  D += __shfl_xor(D, 32, 64);
+  D = sum4lanes(D);
   const float lse2 = a.lse_in[((int64_t)b * a.H + h) * T + qc] * kLog2e;
   if (g == 0 && qi < T) a.delta[((int64_t)b * a.H + h) * T + qi] = D;
 
@@ -882,8 +955,8 @@ slt_status flash_fwd(const AttnArgs& a, hipStream_t s) {
     const slt_status st = prep(a, f, s);
     if (st != SLT_OK) return st;
   }
-  const int ntq = (a.T + FR - 1) / FR;
-  fl_fwd_k<<<ntq * a.H * a.B, 256, 0, s>>>(f);
+  const int nck = (a.T + FC - 1) / FC;
+  fl_fwd2_k<<<nck * a.H * a.B, 256, 0, s>>>(f);
   return check_launch("attention forward");
 }
 

@@ -34,6 +34,9 @@
 #ifndef SLT_SPLIT_TARGET
 #define SLT_SPLIT_TARGET 384  // blocks a split-K grid aims for
 #endif
+#ifndef SLT_GROUP_TARGET
+#define SLT_GROUP_TARGET 512  // blocks a grouped weight-gradient grid aims for
+#endif
 #ifndef SLT_SPLIT_MINK
 #define SLT_SPLIT_MINK 8  // fewest k-steps per split
 #endif
@@ -739,6 +742,148 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
   dl_epilogue<TO, SPLIT, FM, 4>(a, acc, m0, n0, wm, wn, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Grouped weight gradients: several products dW_i = alpha_i A_i^T B_i with
+// the same K (the token count) and both operands m/n-major (rows of tokens),
+// in one launch.  The tiles of all products form one list, so a layer's
+// weight gradients together fill the chip with few K splits (long k-ranges
+// per block, few partials) where each alone needs many.  Blocks run the
+// direct-to-LDS main loop of gemm_dl_k; with splits, partial tiles go to
+// ws[split][tile][128 x 128] and gemm_group_reduce_k adds them in split
+// order (deterministic); without, the block writes alpha C (+ C).
+// ---------------------------------------------------------------------------
+constexpr int kGroupMax = 6;
+
+struct GProb {
+  const bf16* A;  // A(m, k) = A[k lda + m]
+  const bf16* B;  // B(n, k) = B[k ldb + n]
+  float* C;
+  int64_t lda, ldb, ldc;
+  int M, N, tiles_n, tile0;  // first tile of this product in the group's list
+  float alpha;
+  int accumulate;  // C = alpha A B + C
+};
+
+struct GArgs {
+  GProb p[kGroupMax];
+  int np, tiles, kchunk;
+  float* ws;
+};
+
+__device__ __forceinline__ int group_find(const GArgs& a, int tile) {
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < kGroupMax; ++j)
+    if (j < a.np && tile >= a.p[j].tile0) i = j;
+  return i;
+}
+
+template <bool SPLIT>
+__global__ __launch_bounds__(NT) void gemm_group_k(GArgs a) {
+  constexpr int FM = 4, FN = 4;
+  __shared__ __attribute__((aligned(16))) bf16 A0[DL_TILE], A1[DL_TILE], A2[DL_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 B0[DL_TILE], B1[DL_TILE], B2[DL_TILE];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  int tile = blockIdx.x;
+  if (SLT_GEMM_XCD) {
+    const int q = a.tiles >> 3, r = a.tiles & 7, x = tile & 7;
+    tile = x * q + min(x, r) + (tile >> 3);
+  }
+  const GProb& P = a.p[group_find(a, tile)];
+  const int lt = tile - P.tile0;
+  const int tm = lt / P.tiles_n, tn = lt % P.tiles_n;
+  DlCtx c;
+  c.A = P.A;
+  c.B = P.B;
+  c.lda = P.lda;
+  c.ldb = P.ldb;
+  c.M = P.M;
+  c.N = P.N;
+  c.m0 = tm * 128;
+  c.n0 = tn * 128;
+  c.kbeg = SPLIT ? blockIdx.z * a.kchunk : 0;
+  c.nk = a.kchunk / DL_BK;
+  c.wave = wave;
+  c.lane = lane;
+  const DlAddr<false, FM> da(wm * 64, lane);
+  const DlAddr<false, FN> db(wn * 64, lane);
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  dl_issue_tile<false, 1>(c.A, c.lda, c.M, c.m0, c.kbeg, A0, wave, lane);
+  dl_issue_tile<false, 1>(c.B, c.ldb, c.N, c.n0, c.kbeg, B0, wave, lane);
+  dl_issue_tile<false, 1>(c.A, c.lda, c.M, c.m0, c.kbeg + min(1, c.nk - 1) * DL_BK, A1, wave, lane);
+  dl_issue_tile<false, 1>(c.B, c.ldb, c.N, c.n0, c.kbeg + min(1, c.nk - 1) * DL_BK, B1, wave, lane);
+  const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
+  const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
+  for (int it = 0; it < c.nk; it += 3) {
+    dl_step<false, false, FM, FN>(c, it, da, db, a0, b0, A2, B2, acc);
+    if (it + 1 < c.nk) dl_step<false, false, FM, FN>(c, it + 1, da, db, a1, b1, A0, B0, acc);
+    if (it + 2 < c.nk) dl_step<false, false, FM, FN>(c, it + 2, da, db, a2, b2, A1, B1, acc);
+  }
+  SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+
+  // lane holds C[m][n .. n+3] of each 16 x 16 fragment
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int ml = wm * 64 + i * 16 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int nl = wn * 64 + j * 16 + 4 * (lane >> 4);
+      const f32x4 v = acc[i][j];
+      if (SPLIT) {
+        float* dst = a.ws + ((int64_t)blockIdx.z * a.tiles + tile) * (128 * 128) + ml * 128 + nl;
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        const int m = c.m0 + ml, n = c.n0 + nl;
+        if (m >= P.M || n >= P.N) continue;  // N % 8 == 0: the 4 columns are all inside
+        float* dst = P.C + (int64_t)m * P.ldc + n;
+        float4 o = make_float4(P.alpha * v[0], P.alpha * v[1], P.alpha * v[2], P.alpha * v[3]);
+        if (P.accumulate) {
+          const float4 r = *reinterpret_cast<const float4*>(dst);
+          o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+        }
+        *reinterpret_cast<float4*>(dst) = o;
+      }
+    }
+  }
+}
+
+// C[m, n] = alpha sum_z ws[z][tile][m, n] (+ C) over the group's tiles; four
+// consecutive columns per thread, splits added in increasing order.
+__global__ __launch_bounds__(256) void gemm_group_reduce_k(GArgs a, int splits) {
+  const int64_t total = (int64_t)a.tiles * (128 * 128 / 4);
+  const int64_t tstride = (int64_t)a.tiles * (128 * 128);
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int tile = (int)(idx >> 12);
+    const int e = (int)(idx & 4095) * 4;
+    const GProb& P = a.p[group_find(a, tile)];
+    const int lt = tile - P.tile0;
+    const int m = (lt / P.tiles_n) * 128 + (e >> 7), n = (lt % P.tiles_n) * 128 + (e & 127);
+    if (m >= P.M || n >= P.N) continue;
+    const float* src = a.ws + (int64_t)tile * (128 * 128) + e;
+    float4 s = *reinterpret_cast<const float4*>(src);
+    for (int z = 1; z < splits; ++z) {
+      const float4 t = *reinterpret_cast<const float4*>(src + z * tstride);
+      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    }
+    float* dst = P.C + (int64_t)m * P.ldc + n;
+    float4 o = make_float4(P.alpha * s.x, P.alpha * s.y, P.alpha * s.z, P.alpha * s.w);
+    if (P.accumulate) {
+      const float4 r = *reinterpret_cast<const float4*>(dst);
+      o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+    }
+    *reinterpret_cast<float4*>(dst) = o;
+  }
+}
+
 inline bool al(const void* p, int b) { return (reinterpret_cast<uintptr_t>(p) % b) == 0; }
 
 template <typename T, typename TO, bool AK, bool BKM, bool VEC, bool SPLIT>
@@ -873,6 +1018,58 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
 }
 
 }  // namespace
+
+bool gemm_group_ok(const GroupItem& it, int K) {
+  auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  return K > 0 && K % DL_BK == 0 && it.M >= 8 && it.N >= 8 && it.M % 8 == 0 && it.N % 8 == 0 && it.lda % 8 == 0 &&
+         it.ldb % 8 == 0 && it.ldc % 4 == 0 && al16(it.A) && al16(it.B) && al16(it.C);
+}
+
+slt_status launch_gemm_group(const GroupItem* items, int n, int K, float* ws, int64_t ws_bytes, hipStream_t s) {
+  if (n <= 0) return SLT_OK;
+  if (n > kGroupMax) return fail(SLT_EUNSUPPORTED, "gemm group: too many products");
+  GArgs a{};
+  a.np = n;
+  int tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const GroupItem& it = items[i];
+    if (!gemm_group_ok(it, K)) return fail(SLT_EUNSUPPORTED, "gemm group: shape or alignment");
+    GProb& P = a.p[i];
+    P.A = static_cast<const bf16*>(it.A);
+    P.B = static_cast<const bf16*>(it.B);
+    P.C = it.C;
+    P.lda = it.lda;
+    P.ldb = it.ldb;
+    P.ldc = it.ldc;
+    P.M = it.M;
+    P.N = it.N;
+    P.tiles_n = (it.N + 127) / 128;
+    P.tile0 = tiles;
+    P.alpha = it.alpha;
+    P.accumulate = it.accumulate ? 1 : 0;
+    tiles += ((it.M + 127) / 128) * P.tiles_n;
+  }
+  a.tiles = tiles;
+  // splits: aim for SLT_GROUP_TARGET blocks, at least SLT_SPLIT_MINK k-steps
+  // each, K divided evenly in whole k-steps, partials inside the workspace
+  const int kt = K / DL_BK;
+  int splits = std::max(1, std::min((SLT_GROUP_TARGET + tiles - 1) / tiles, kt / SLT_SPLIT_MINK));
+  const int64_t per = (int64_t)tiles * 128 * 128 * 4;
+  while (splits > 1 && (kt % splits || !ws || per * splits > ws_bytes)) --splits;
+  a.kchunk = (kt / splits) * DL_BK;
+  a.ws = ws;
+  const dim3 grid(tiles, 1, splits);
+  if (splits > 1) {
+    gemm_group_k<true><<<grid, NT, 0, s>>>(a);
+    if (slt_status st = check_launch("gemm group"); st != SLT_OK) return st;
+    const int64_t total = (int64_t)tiles * 4096;
+    const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
+    gemm_group_reduce_k<<<blocks, 256, 0, s>>>(a, splits);
+    return check_launch("gemm group reduction");
+  }
+  gemm_group_k<false><<<grid, NT, 0, s>>>(a);
+  return check_launch("gemm group");
+}
 
 slt_status launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return SLT_OK;

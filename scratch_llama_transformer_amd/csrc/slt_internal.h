@@ -94,6 +94,20 @@ struct GradW {
 };
 slt_status launch_gemm(const GemmArgs& g, hipStream_t s);
 
+// One product of a grouped weight-gradient launch: C[M, N] (fp32, row stride
+// ldc) = alpha sum_k A[k lda + m] B[k ldb + n] (+ C when accumulate), bf16
+// operands with rows of tokens.  All products of a group share K.
+struct GroupItem {
+  int M, N;
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  float* C; int64_t ldc;
+  float alpha;
+  bool accumulate;
+};
+bool gemm_group_ok(const GroupItem& it, int K);
+slt_status launch_gemm_group(const GroupItem* items, int n, int K, float* ws, int64_t ws_bytes, hipStream_t s);
+
 slt_status launch_embedding_fwd(const int32_t* tok, int B, int T, int64_t ld, const void* wte,
                                 void* x, int V, int C, int dtype, hipStream_t s);
 int64_t embedding_bwd_ws(int64_t N, int V);
