@@ -46,6 +46,15 @@
 #ifndef SLT_GEMM_BIG
 #define SLT_GEMM_BIG 1
 #endif
+#ifndef SLT_GEMM_W8
+#define SLT_GEMM_W8 1
+#endif
+#ifndef SLT_W8_MIN
+#define SLT_W8_MIN 256  // fewest 256 x 256 tiles for the 8-wave kernel
+#endif
+#ifndef SLT_GEMM_BAND
+#define SLT_GEMM_BAND 8  // tile rows per band of the 256 x 256 tile order
+#endif
 #ifndef SLT_GEMM_XCD
 #define SLT_GEMM_XCD 1
 #endif
@@ -367,6 +376,18 @@ __device__ __forceinline__ int dl_swz(int r) { return (r >> 1) & 3; }
 __device__ __forceinline__ int dl_swz_mn(int kr) { return 2 * ((kr & 3) | (((kr >> 3) & 1) << 2)); }
 
 
+// Tile coordinates of list position `idx` in bands of G tile rows, each band
+// walked column by column: the tiles an XCD runs together (a contiguous range
+// of positions) then share both A row-blocks and B column-blocks in its L2,
+// where a row-major walk shares only A and streams B from memory.
+__device__ __forceinline__ void band_coords(int idx, int tiles, int tiles_n, int G, int& tm, int& tn) {
+  const int tiles_m = tiles / tiles_n;
+  const int band = idx / (G * tiles_n), within = idx - band * G * tiles_n;
+  const int gm = min(G, tiles_m - band * G);
+  tm = band * G + within % gm;
+  tn = within / gm;
+}
+
 // Copy the 128 x 32 tile at (row0, k0) of an operand into `tile`: 2 copies per
 // wave (512 chunks of 16 bytes over 4 waves).
 template <bool KM>
@@ -636,6 +657,109 @@ __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a)
   dl_epilogue<TO, SPLIT, FM, FN>(a, acc, c.m0, c.n0, wm, wn, lane);
 }
 
+
+// ---------------------------------------------------------------------------
+// 256 x 256 block tile, 8 waves (512 threads) as 2 x 4, each wave 128 x 64
+// (8 x 4 MFMA tiles).  Per 32-deep k-step a block copies 32 KiB for 4 MFLOP
+// -- half the bytes per FLOP of the 128 x 128 tile, whose copy path is the
+// limit -- and two waves per SIMD let one wave's LDS reads overlap the
+// other's MFMAs.  Three-stage LDS ring of 32 KiB stages (one block per CU).
+// Each 128-row operand sub-tile takes one copy per lane.  Tiles are taken in
+// bands of SLT_GEMM_BAND tile rows (band_coords).  Measured on gfx950 against
+// a persistent form (one block per CU walking its XCD's tiles as one stream
+// of k-steps) and a 64-deep two-stage form, this one was fastest.
+// ---------------------------------------------------------------------------
+constexpr int W8_NT = 512;
+
+template <bool KM>
+__device__ __forceinline__ void w8_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
+                                         int lane) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int p = wave * 64 + lane;  // 16-byte chunk position in the 128 x 32 sub-tile
+    const int r0 = row0 + 128 * s;
+    const bf16* src;
+    if constexpr (KM) {
+      const int r = p >> 2;
+      const int lc = (p & 3) ^ dl_swz(r);
+      src = g + (int64_t)min(r0 + r, rows - 1) * ld + k0 + lc * 8;
+    } else {
+      const int kr = p >> 4;
+      const int c = (p & 15) ^ dl_swz_mn(kr);
+      src = g + (int64_t)(k0 + kr) * ld + min(r0 + c * 8, rows - 8);
+    }
+    lds_copy16(src, tile + s * DL_TILE + wave * 512);
+  }
+}
+
+template <bool AK, bool BK>
+__device__ __forceinline__ void w8_step(const DlCtx& c, int it, const DlAddr<AK, 8>& da, const DlAddr<BK, 4>& db,
+                                        unsigned as, unsigned bs, bf16* An, bf16* Bn, f32x4 (&acc)[8][4]) {
+  SLT_WAIT_VMCNT(4);  // only the copies of tile it+1 may still fly
+  lds_barrier();
+  u32x4 af[8], bfr[4];
+  dl_read<AK, BK, 8, 4>(da.at(as), db.at(bs), af, bfr);
+  const int kn = c.kbeg + min(it + 2, c.nk - 1) * DL_BK;
+  w8_issue<AK>(c.A, c.lda, c.M, c.m0, kn, An, c.wave, c.lane);
+  w8_issue<BK>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[j]),
+                                                          __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
+}
+
+template <typename TO, bool AK, bool BK>
+__global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 A0[2 * DL_TILE], A1[2 * DL_TILE], A2[2 * DL_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 B0[2 * DL_TILE], B1[2 * DL_TILE], B2[2 * DL_TILE];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  int tile = blockIdx.x;
+  if (SLT_GEMM_XCD) {
+    const int q = a.tiles >> 3, r = a.tiles & 7, x = tile & 7;
+    tile = x * q + min(x, r) + (tile >> 3);
+  }
+  int tm, tn;
+  band_coords(tile, a.tiles, a.tiles_n, SLT_GEMM_BAND, tm, tn);
+  DlCtx c;
+  c.A = static_cast<const bf16*>(a.A);
+  c.B = static_cast<const bf16*>(a.B);
+  c.lda = a.lda;
+  c.ldb = a.ldb;
+  c.M = a.M;
+  c.N = a.N;
+  c.m0 = tm * 256;
+  c.n0 = tn * 256;
+  c.kbeg = 0;
+  c.nk = a.K / DL_BK;
+  c.wave = wave;
+  c.lane = lane;
+  const DlAddr<AK, 8> da(wm * 128, lane);
+  const DlAddr<BK, 4> db(wn * 64, lane);
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  w8_issue<AK>(c.A, c.lda, c.M, c.m0, 0, A0, wave, lane);
+  w8_issue<BK>(c.B, c.ldb, c.N, c.n0, 0, B0, wave, lane);
+  w8_issue<AK>(c.A, c.lda, c.M, c.m0, min(1, c.nk - 1) * DL_BK, A1, wave, lane);
+  w8_issue<BK>(c.B, c.ldb, c.N, c.n0, min(1, c.nk - 1) * DL_BK, B1, wave, lane);
+  const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
+  const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
+  for (int it = 0; it < c.nk; it += 3) {
+    w8_step<AK, BK>(c, it, da, db, a0, b0, A2, B2, acc);
+    if (it + 1 < c.nk) w8_step<AK, BK>(c, it + 1, da, db, a1, b1, A0, B0, acc);
+    if (it + 2 < c.nk) w8_step<AK, BK>(c, it + 2, da, db, a2, b2, A1, B1, acc);
+  }
+  SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+  dl_epilogue<TO, false, 8, 4>(a, acc, c.m0, c.n0, wm, wn, lane);
+}
 
 // ---------------------------------------------------------------------------
 // Both operands k-major, 128 x 128 block tile: 64-deep k-steps in two stages.
@@ -967,6 +1091,22 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
       // are the limit at 128 x 128): 256 x 128 (or 128 x 256) when the grid
       // holds at least 1.5 rounds of two such blocks per CU and K is not split
       // (at fewer tiles the last round leaves CUs idle and 128 x 128 is faster).
+      // 256 x 256 tiles (one 8-wave block per CU) for grids of at least
+      // SLT_W8_MIN such tiles whose edges waste little and whose last round
+      // of 256 blocks is mostly full (measured: 1.25 or 1.5 rounds lose to
+      // the smaller tiles)
+      if (!split && g.a_kmajor && SLT_GEMM_W8) {
+        const int t8m = (g.M + 255) / 256, t8n = (g.N + 255) / 256, t8 = t8m * t8n;
+        const bool edges = (int64_t)t8 * 256 * 256 <= (int64_t)g.M * g.N * 9 / 8;
+        const bool rounds = t8 * 20 >= ((t8 + 255) / 256) * 256 * 17;
+        if (t8 >= SLT_W8_MIN && edges && rounds) {
+          ka.tiles_n = t8n;
+          ka.tiles = t8m * t8n;
+          if (g.b_kmajor) gemm_w8_k<TO, true, true><<<ka.tiles, W8_NT, 0, s>>>(ka);
+          else gemm_w8_k<TO, true, false><<<ka.tiles, W8_NT, 0, s>>>(ka);
+          return finish<TO>(g, false, 1, s);
+        }
+      }
       int fm = 4, fn = 4;
       if (!split && g.a_kmajor && SLT_GEMM_BIG) {
         auto ntiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };

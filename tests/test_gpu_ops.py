@@ -108,11 +108,13 @@ def test_gemm_direct_lds_path(B, a_k, b_k, outd):
     gemm_case(B, rng, 264, 136, 4096, a_k, b_k, BF16, outd, ws=True, resid=True)
 
 
-@pytest.mark.parametrize("a_k,b_k,M,N", [(1, 1, 12296, 4000), (1, 1, 4000, 12296), (1, 0, 12296, 4000)])
+@pytest.mark.parametrize("a_k,b_k,M,N", [(1, 1, 12296, 4000), (1, 1, 4000, 12296), (1, 0, 12296, 4000),
+                                         (1, 1, 65560, 296), (1, 0, 65560, 296)])
 def test_gemm_big_tiles(B, a_k, b_k, M, N):
-    # grids with enough 256 x 128 (128 x 256) tiles take the larger block
-    # tile; ragged M and N, 1..6 k-steps of 32 (1..3 of 64), residual;
-    # sampled rows
+    # grids of at least 256 tiles of 256 x 256 with little edge waste take the
+    # 8-wave 256 x 256 kernel (12296 x 4000, 4000 x 12296); narrow grids with
+    # enough 256 x 128 tiles take that block tile (65560 x 296); ragged M and
+    # N, 1..6 k-steps of 32 (1..3 of 64), residual; sampled rows
     rng = np.random.default_rng(6)
     for K in (32, 96, 128, 160, 192):
         gemm_case(B, rng, M, N, K, a_k, b_k, BF16, BF16, sample=40)
