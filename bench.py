@@ -67,6 +67,15 @@ def step_flops(w):
     return g + fa + ba
 
 
+def describe(w):
+    if w.block == "llama":
+        heads = f"H={w.H}" + (f"/Hkv={w.Hkv} (GQA)" if w.Hkv != w.H else "")
+        return (f"{w.name}: Llama-style decoder V={w.V} C={w.C} {heads} L={w.L} T={w.T} B={w.B} F={w.F}, "
+                f"RMSNorm, rotate-half RoPE, SwiGLU, untied head")
+    return (f"{w.name}: parallel-block (GPT-J style) decoder V={w.V} C={w.C} H={w.H} L={w.L} T={w.T} B={w.B} "
+            f"F={w.F}, LayerNorm, even-odd RoPE on {w.R} of {w.C // w.H} dims, GELU MLP, untied head")
+
+
 def time_block(fn, reps, torch):
     """Average seconds of fn() (which enqueues on the current stream), HIP
     events on that stream."""
@@ -113,9 +122,21 @@ def kernel_classes(w, ts, torch, reps):
                 Cm = torch.empty((M, N), dtype=torch.float32, device="cuda")
                 bufs.append((M, N, K, A, M, 0, Bm, N, 0, Cm, N, None, 0, dt, B.F32, ws, ws.numel()))
 
-        def run(bufs=bufs):
-            for args in bufs:
-                B.slt_gemm(*args)
+        if cls == "gemm_dw" and dt == B.BF16:
+            # as the step runs them: one grouped launch per layer (the head's
+            # product joins the last layer's group)
+            per = 4 if w.block == "llama" else 2
+            items = [(a[0], a[1], a[3], a[4], a[6], a[7], a[9], a[10], 1.0, 0) for a in bufs]
+            groups = [items[i:i + per] for i in range(0, len(items) - 1, per)]
+            groups[-1] = groups[-1] + [items[-1]]
+
+            def run(groups=groups, K=launches[0][2]):
+                for grp in groups:
+                    B.slt_gemm_dw_group(grp, K, ws, ws.numel())
+        else:
+            def run(bufs=bufs):
+                for args in bufs:
+                    B.slt_gemm(*args)
 
         sec = time_block(run, reps, torch)
         flops = sum(2.0 * M * N * K for (M, N, K, _) in launches)
@@ -289,9 +310,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.act == "bf16" else "f32",
-        "data": "synthetic (seeded Zipf(1.1) token ids, device-initialised N(0, 0.02) weights)",
-        "config": {"workload": f"{w.name}: Llama-style decoder V={w.V} C={w.C} H={w.H} L={w.L} "
-                               f"T={w.T} B={w.B} F={w.F}, RoPE, SwiGLU, untied head",
+        "data": f"synthetic (seeded {'Zipf(1.1)' if w.tokens == 'zipf' else 'uniform'} token ids, "
+                "device-initialised N(0, 0.02) weights)",
+        "config": {"workload": describe(w),
                    "global_batch": w.B, "seq_len": w.T, "tokens_per_step": w.N},
         "mfma_util_pct": round(100.0 * flops / (ms / 1e3) / 1e12 / peak, 2),
         "step_tflops": round(flops / (ms / 1e3) / 1e12, 2),

@@ -241,6 +241,29 @@ slt_status slt_gemm(int32_t M, int32_t N, int32_t K,
                     int32_t in_dtype, int32_t out_dtype,
                     void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Grouped weight gradients (the matmul family's A^T.B form, several
+ * products in one launch; Hephaistos, "Design notes": the backward walk
+ * produces each layer's weight gradients from cached activations).  Product
+ * i computes, in fp32,
+ *   C_i[m, n] = alpha_i sum_k A_i[k*lda_i + m] B_i[k*ldb_i + n]  (+ C_i when accumulate_i)
+ * with bf16 operands whose rows are the K tokens (dW = dY^T X).  All products
+ * share K.  Requirements (else SLT_EUNSUPPORTED, nothing enqueued): bf16
+ * operands, K a positive multiple of 32, M_i and N_i multiples of 8 (>= 8),
+ * lda/ldb multiples of 8, ldc a multiple of 4, A/B/C 16-byte aligned,
+ * 1 <= n <= 6.  workspace (fp32 partials, may be NULL) lets the library split
+ * K over the products' tiles with a fixed-order reduction (deterministic).
+ * items is host memory, read before the call returns. */
+typedef struct {
+  int32_t M, N;
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  float* C; int64_t ldc;
+  float alpha;
+  int32_t accumulate;
+} slt_gemm_group_item;
+slt_status slt_gemm_dw_group(const slt_gemm_group_item* items, int32_t n, int32_t K, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+
 /* x[b*T + t, :] = wte[tokens[b*ld_tokens + t], :] for t < T. */
 slt_status slt_embedding_fwd(const int32_t* tokens, int32_t B, int32_t T, int64_t ld_tokens,
                              const void* wte, void* x, int32_t V, int32_t C, int32_t dtype,

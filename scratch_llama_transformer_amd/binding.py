@@ -42,6 +42,11 @@ class slt_tensor(ct.Structure):
 _P = ct.c_void_p
 _I32, _I64, _F = ct.c_int32, ct.c_int64, ct.c_float
 
+
+class slt_gemm_group_item(ct.Structure):
+    _fields_ = [("M", _I32), ("N", _I32), ("A", _P), ("lda", _I64), ("B", _P), ("ldb", _I64), ("C", _P),
+                ("ldc", _I64), ("alpha", _F), ("accumulate", _I32)]
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "slt_last_error": (ct.c_char_p, []),
@@ -63,6 +68,7 @@ SIGNATURES = {
     "slt_clip_grad_norm": (_I32, [_I64, _P, _I32, _F, _P, _P, _P, _P]),
     "slt_gemm": (_I32, [_I32, _I32, _I32, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _P, _I64,
                         _I32, _I32, _P, _I64, _P]),
+    "slt_gemm_dw_group": (_I32, [ct.POINTER(slt_gemm_group_item), _I32, _I32, _P, _I64, _P]),
     "slt_embedding_fwd": (_I32, [_P, _I32, _I32, _I64, _P, _P, _I32, _I32, _I32, _P]),
     "slt_embedding_bwd_workspace": (_I64, [_I64, _I32]),
     "slt_embedding_bwd": (_I32, [_P, _I32, _I32, _I64, _P, _P, _I32, _I32, _I32, _P, _P]),
@@ -244,6 +250,15 @@ def slt_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, ldc, R, ldr, in_dty
     _check("slt_gemm", load().slt_gemm(M, N, K, _ptr(A), lda, int(a_kmajor), _ptr(B), ldb, int(b_kmajor), _ptr(C),
                                        ldc, _ptr(R), ldr, in_dtype, out_dtype, _ptr(workspace), workspace_bytes,
                                        _stream(stream)))
+
+
+def slt_gemm_dw_group(items, K, workspace=None, workspace_bytes=0, stream=None):
+    """items: sequence of (M, N, A, lda, B, ldb, C, ldc, alpha, accumulate)."""
+    arr = (slt_gemm_group_item * len(items))()
+    for i, (M, N, A, lda, Bm, ldb, C, ldc, alpha, acc) in enumerate(items):
+        arr[i] = slt_gemm_group_item(M, N, _ptr(A), lda, _ptr(Bm), ldb, _ptr(C), ldc, alpha, int(acc))
+    _check("slt_gemm_dw_group", load().slt_gemm_dw_group(arr, len(items), K, _ptr(workspace), workspace_bytes,
+                                                         _stream(stream)))
 
 
 def slt_embedding_fwd(tokens, B, T, ld_tokens, wte, x, V, C, dtype, stream=None):

@@ -897,6 +897,23 @@ slt_status slt_softmax_xent(void* z, int64_t ldz, const int32_t* tokens, int32_t
   return launch_softmax_xent(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtype, workspace, as_stream(stream));
 }
 
+slt_status slt_gemm_dw_group(const slt_gemm_group_item* items, int32_t n, int32_t K, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  if (!items || n < 1 || n > 6) return fail(SLT_EINVAL, "gemm group: 1 to 6 items required");
+  if (K <= 0) return fail(SLT_EINVAL, "gemm group: K must be positive");
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace))
+    return fail(SLT_EINVAL, "gemm group: bad workspace");
+  GroupItem g[6];
+  for (int i = 0; i < n; ++i) {
+    const slt_gemm_group_item& t = items[i];
+    if (!t.A || !t.B || !t.C) return fail(SLT_EINVAL, "gemm group: NULL operand");
+    g[i] = GroupItem{t.M, t.N, t.A, t.lda, t.B, t.ldb, t.C, t.ldc, t.alpha, t.accumulate != 0};
+    if (!gemm_group_ok(g[i], K)) return fail(SLT_EUNSUPPORTED, "gemm group: shape or alignment");
+  }
+  return launch_gemm_group(g, n, K, static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
+                           as_stream(stream));
+}
+
 slt_status slt_kv_cache_bytes(const slt_config* cfg, int32_t B, int32_t Tq, int32_t Tmax, int64_t* cache_bytes,
                               int64_t* workspace_bytes) {
   Plan p;

@@ -192,6 +192,16 @@ __device__ __forceinline__ void rd_khalf(unsigned a0, unsigned a1, u32x4 (&f)[2]
                : "memory");
 }
 
+// Row fragments of one 32-row half of one tile: f[tt][s] (a0 / a1 as for
+// rd_khalf).
+__device__ __forceinline__ void rd_rows4(unsigned a0, unsigned a1, u32x4 (&f)[2][2]) {
+  asm volatile(FL_R128(f00, a0, 0) FL_R128(f01, a1, 0) FL_R128(f10, a0, 2048) FL_R128(f11, a1, 2048)
+               "s_waitcnt lgkmcnt(0)"
+               : FL_O(f00, f[0][0]), FL_O(f01, f[0][1]), FL_O(f10, f[1][0]), FL_O(f11, f[1][1])
+               : [a0] "v"(a0), [a1] "v"(a1)
+               : "memory");
+}
+
 // Column fragments of one 32-row half of a tile: f[dt] = rows 32 hf +
 // (4g..4g+3, then 16 + 4g..4g+3) at dims 16 dt + i.  cK = tile address plus
 // the lane's col[dt] plus 4096 hf.
@@ -515,9 +525,9 @@ __global__ __launch_bounds__(256, 2) void fl_fwd2_k(FlArgs a) {
 // scaled, rotated back by RoPE when R > 0 (the transpose of the forward
 // rotation: the gradient of the rotated copy is the rotated-back gradient).
 __device__ __forceinline__ void fl_store_rows(const float* F, float scale, bf16* out, int64_t ld, int row0, int T,
-                                              int d, int R, int mode, const float* cs) {
+                                              int d, int R, int mode, const float* cs, int nrows = FR) {
   const int ng = d / 4;
-  for (int idx = threadIdx.x; idx < FR * ng; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < nrows * ng; idx += blockDim.x) {
     const int r = idx / ng, j0 = (idx % ng) * 4;
     const int t = row0 + r;
     if (t >= T) continue;
@@ -882,6 +892,200 @@ __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
   fl_store_rows(F2, 1.0f, a.dv + (int64_t)b * T * a.lddv + (int64_t)kvh * a.d, a.lddv, k0, T, a.d, 0, 0, nullptr);
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV over 256-key chunks.  One 8-wave workgroup per (key chunk, KV head,
+// batch), chunks with the most queries first; wave w owns the key subtiles
+// u = w and w + 8 (16 keys each) of the chunk, their rotated keys, values and
+// dK / dV accumulators held in registers.  Query tiles of 64 rows of every
+// query head of the group stream through a three-stage LDS ring ([Q hi | Q lo
+// | dO | lse, D] per stage); each 32-query half is read from LDS once per
+// wave and applied to both subtiles: S = Q K^T (hi/lo), P = exp2(S - lse),
+// dP = dO V^T, dS = P (dP - D), then dV^T += dO^T P (P as hi/lo) and
+// dK^T += Q^T dS (hi/lo).  Needs T % 4 == 0 (16-byte lse / D rows).
+// ---------------------------------------------------------------------------
+constexpr int KC = 256;                 // keys per chunk
+constexpr int STB = 3 * FTB + 1024;     // stage bytes: Q hi, Q lo, dO, then lse (256 B), D (256 B), pad
+
+// Copy rows row0..row0+63 of a bf16 array into an LDS tile with 512 threads:
+// one copy per lane (as fl_issue).
+__device__ __forceinline__ void fl_issue8(const bf16* g, int64_t ld, int row0, int nrows, int nch, char* tile,
+                                          int wave, int lane) {
+  const int p = wave * 64 + lane;
+  const int r = p >> 3;
+  const int c = (p & 7) ^ fsw(r);
+  const void* src = c < nch ? static_cast<const void*>(g + (int64_t)min(row0 + r, nrows - 1) * ld + c * 8)
+                            : static_cast<const void*>(g_zero16);
+  lds_copy16(src, tile + wave * 1024);
+}
+
+__global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[3][STB];
+  const int T = a.T, G = a.H / a.Hkv, nkc = (T + KC - 1) / KC;
+  const int w = fl_work_item();
+  const int kc = w % nkc, kvh = (w / nkc) % a.Hkv, b = w / (nkc * a.Hkv);  // earliest keys (most queries) first
+  const int k0 = kc * KC;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, li = lane & 15;
+  const int nch = a.d / 8;
+  const FlOff off(lane);
+
+  // subtile i: keys k0 + 16 (wave + 8 i) + li
+  u32x4 kh[2][2], kl[2][2], vf[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int kc_ = min(k0 + 16 * (wave + 8 * i) + li, T - 1);
+    const int64_t krow = ((int64_t)(b * a.Hkv + kvh) * T + kc_) * FD;
+    const bf16* vrow = a.v + ((int64_t)b * T + kc_) * a.ldv + (int64_t)kvh * a.d;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      kh[i][s] = *reinterpret_cast<const u32x4*>(a.kh + krow + 32 * s + 8 * g);
+      kl[i][s] = *reinterpret_cast<const u32x4*>(a.kl + krow + 32 * s + 8 * g);
+      const int j0 = 32 * s + 8 * g;
+      vf[i][s] = j0 < a.d ? *reinterpret_cast<const u32x4*>(vrow + j0) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  f32x4 dva[2][4], dka[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      dva[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dka[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int ntq = (T + FR - 1) / FR;
+  const int qt0 = k0 / FR;         // first query tile a key of the chunk needs
+  const int per = ntq - qt0;       // query tiles per head
+  const int nsteps = G * per;
+  auto issue = [&](int n, char* st) {
+    const int hh = kvh * G + n / per, qt = qt0 + n % per;
+    const int64_t hb = (int64_t)(b * a.H + hh) * T;
+    fl_issue8(a.qh + hb * FD, FD, qt * FR, T, 8, st, wave, lane);
+    fl_issue8(a.ql + hb * FD, FD, qt * FR, T, 8, st + FTB, wave, lane);
+    fl_issue8(a.dout + (int64_t)b * T * a.lddo + (int64_t)hh * a.d, a.lddo, qt * FR, T, nch, st + 2 * FTB, wave,
+              lane);
+    if (wave == 0) {  // lse then D of the 64 rows: 16 + 16 chunks (lanes 32..63 repeat into the pad)
+      const int c = lane & 15;
+      const int q = min(qt * FR + 4 * c, T - 4);
+      const float* src = (lane & 16) ? a.delta + hb + q : a.lse_in + hb + q;
+      lds_copy16(src, st + 3 * FTB);
+    }
+  };
+  issue(0, lds[0]);
+  issue(min(1, nsteps - 1), lds[1]);
+  for (int n = 0; n < nsteps; ++n) {
+    SLT_WAIT_VMCNT(3);  // only the next step's copies may still fly (wave 0 waits for one more)
+    lds_barrier();
+    issue(min(n + 2, nsteps - 1), lds[(n + 2) % 3]);
+    const int qt = qt0 + n % per;
+    const int q0 = qt * FR;
+    char* stg = lds[n % 3];
+    const unsigned base = lds_off(stg);
+    const float* lsd = reinterpret_cast<const float*>(stg + 3 * FTB);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int qh0 = q0 + 32 * hf;  // first query of this half
+      if (qh0 >= T || qh0 + 31 < k0 + 16 * wave) continue;  // past T, or before every key of the wave
+      u32x4 qf[2][2][2], gr[2][2];
+      rd_khalf(base + off.row[0] + 4096 * hf, base + off.row[1] + 4096 * hf, qf);
+      rd_rows4(base + 2 * FTB + off.row[0] + 4096 * hf, base + 2 * FTB + off.row[1] + 4096 * hf, gr);
+      u32x4 ph[2], pl[2], dh[2], dl[2];
+      bool act[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int kf = k0 + 16 * (wave + 8 * i);  // first key of subtile i
+        act[i] = qh0 + 31 >= kf;
+        if (!act[i]) continue;
+        const int ki = kf + li;
+        float p[2][4], ds[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            st = mma(qf[0][tt][s], kh[i][s], st);
+            st = mma(qf[0][tt][s], kl[i][s], st);
+            st = mma(qf[1][tt][s], kh[i][s], st);
+            dp = mma(gr[tt][s], vf[i][s], dp);
+          }
+          // lse (to base 2) and D of the lane's 4 query rows, read where used
+          const float4 l4 = *reinterpret_cast<const float4*>(lsd + 32 * hf + 16 * tt + 4 * g);
+          const float4 d4 = *reinterpret_cast<const float4*>(lsd + 64 + 32 * hf + 16 * tt + 4 * g);
+          p[tt][0] = ex2(st[0] - l4.x * kLog2e);
+          p[tt][1] = ex2(st[1] - l4.y * kLog2e);
+          p[tt][2] = ex2(st[2] - l4.z * kLog2e);
+          p[tt][3] = ex2(st[3] - l4.w * kLog2e);
+          const float dn[4] = {d4.x, d4.y, d4.z, d4.w};
+          if (qh0 < kf + 15 || qh0 + 31 >= T) {  // the diagonal, or rows past T
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int qq = qh0 + 16 * tt + 4 * g + r;
+              if (qq >= T || ki > qq) p[tt][r] = 0.f;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ds[tt][r] = p[tt][r] * (dp[r] - dn[r]);
+        }
+        pack_k_hilo(p[0], p[1], ph[i], pl[i]);
+        pack_k_hilo(ds[0], ds[1], dh[i], dl[i]);
+      }
+      {
+        u32x4 gt[4];
+        rd_chalf(base + 2 * FTB + off.col[0] + 4096 * hf, base + 2 * FTB + off.col[1] + 4096 * hf,
+                 base + 2 * FTB + off.col[2] + 4096 * hf, base + 2 * FTB + off.col[3] + 4096 * hf, gt);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (!act[i]) continue;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            dva[i][dt] = mma(gt[dt], ph[i], dva[i][dt]);
+            dva[i][dt] = mma(gt[dt], pl[i], dva[i][dt]);
+          }
+        }
+      }
+      {
+        u32x4 qc[4];
+        rd_chalf(base + off.col[0] + 4096 * hf, base + off.col[1] + 4096 * hf, base + off.col[2] + 4096 * hf,
+                 base + off.col[3] + 4096 * hf, qc);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (!act[i]) continue;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            dka[i][dt] = mma(qc[dt], dh[i], dka[i][dt]);
+            dka[i][dt] = mma(qc[dt], dl[i], dka[i][dt]);
+          }
+        }
+        rd_chalf(base + FTB + off.col[0] + 4096 * hf, base + FTB + off.col[1] + 4096 * hf,
+                 base + FTB + off.col[2] + 4096 * hf, base + FTB + off.col[3] + 4096 * hf, qc);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (!act[i]) continue;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) dka[i][dt] = mma(qc[dt], dh[i], dka[i][dt]);
+        }
+      }
+    }
+  }
+  SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+
+  // stage the chunk's 256 rows of dK (then dV) as fp32 and store them
+  lds_barrier();
+  float* F = reinterpret_cast<float*>(&lds[0][0]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) fl_stage_acc(F, 16 * (wave + 8 * i) + li, g, dka[i]);
+  lds_barrier();
+  // the query copy carries log2(e) / sqrt(d): dK = dS^T Q / sqrt(d) = ln(2) dS^T Q'
+  fl_store_rows(F, kLn2, a.dk + (int64_t)b * T * a.lddk + (int64_t)kvh * a.d, a.lddk, k0, T, a.d, a.R, a.rope_mode,
+                a.cs, KC);
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) fl_stage_acc(F, 16 * (wave + 8 * i) + li, g, dva[i]);
+  lds_barrier();
+  fl_store_rows(F, 1.0f, a.dv + (int64_t)b * T * a.lddv + (int64_t)kvh * a.d, a.lddv, k0, T, a.d, 0, 0, nullptr, KC);
+}
+
 inline bool al(const void* p, int n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
 
 FlArgs to_fl(const AttnArgs& a) {
@@ -970,7 +1174,12 @@ slt_status flash_bwd(const AttnArgs& a, hipStream_t s) {
   fl_dq_k<<<nt * a.H * a.B, 256, 0, s>>>(f);
   slt_status st = check_launch("attention backward (dq)");
   if (st != SLT_OK) return st;
-  fl_dkdv_k<<<nt * a.Hkv * a.B, 256, 0, s>>>(f);
+  if (a.T % 4 == 0 && al(a.lse_in, 16) && al(a.delta, 16)) {
+    const int nkc = (a.T + KC - 1) / KC;
+    fl_dkdv2_k<<<nkc * a.Hkv * a.B, 512, 0, s>>>(f);
+  } else {
+    fl_dkdv_k<<<nt * a.Hkv * a.B, 256, 0, s>>>(f);
+  }
   return check_launch("attention backward (dk, dv)");
 }
 

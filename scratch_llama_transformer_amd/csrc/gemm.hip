@@ -37,6 +37,9 @@
 #ifndef SLT_GROUP_TARGET
 #define SLT_GROUP_TARGET 512  // blocks a grouped weight-gradient grid aims for
 #endif
+#ifndef SLT_GROUP_W8_MIN
+#define SLT_GROUP_W8_MIN 160  // fewest 256 x 256 tiles for the 8-wave grouped kernel
+#endif
 #ifndef SLT_SPLIT_MINK
 #define SLT_SPLIT_MINK 8  // fewest k-steps per split
 #endif
@@ -490,6 +493,16 @@ __device__ __forceinline__ void dl_read(const DlAddr<AK, FA>& da, const DlAddr<B
   } else if constexpr (!AK && BK && FA == 4 && FB == 4) {
     asm volatile(DL_MN4(a) DL_KM4(b) "s_waitcnt lgkmcnt(0)"
                  : DL_OUT_MN4(a, al, ah), DL_OUT_KM4(b, bf) : DL_IN_MN4(a, da), DL_IN_KM(b, db) : "memory");
+  } else if constexpr (!AK && !BK && FA == 8 && FB == 4) {
+    // two blocks (operand count): A fragments 0..3 with B, then A 4..7
+    asm volatile(DL_MN4(a) DL_MN4(b) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_MN4(a, al, ah), DL_OUT_MN4(b, bl, bh) : DL_IN_MN4(a, da), DL_IN_MN4(b, db) : "memory");
+    u32x2* al4 = al + 4;
+    u32x2* ah4 = ah + 4;
+    asm volatile(DL_MN4(c) "s_waitcnt lgkmcnt(0)"
+                 : DL_OUT_MN4(c, al4, ah4)
+                 : [cp0] "v"(da.a[4]), [cp1] "v"(da.a[5]), [cp2] "v"(da.a[6]), [cp3] "v"(da.a[7])
+                 : "memory");
   } else if constexpr (!AK && !BK && FA == 4 && FB == 4) {
     asm volatile(DL_MN4(a) DL_MN4(b) "s_waitcnt lgkmcnt(0)"
                  : DL_OUT_MN4(a, al, ah), DL_OUT_MN4(b, bl, bh) : DL_IN_MN4(a, da), DL_IN_MN4(b, db) : "memory");
@@ -979,6 +992,75 @@ __global__ __launch_bounds__(NT) void gemm_group_k(GArgs a) {
   }
 }
 
+// Large groups: 256 x 256 tiles, 8 waves of 128 x 64 (the gemm_w8_k main
+// loop), whole K per block, alpha C (+ C) written directly.
+__global__ __launch_bounds__(W8_NT, 1) void gemm_group_w8_k(GArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 A0[2 * DL_TILE], A1[2 * DL_TILE], A2[2 * DL_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 B0[2 * DL_TILE], B1[2 * DL_TILE], B2[2 * DL_TILE];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  int tile = blockIdx.x;
+  if (SLT_GEMM_XCD) {
+    const int q = a.tiles >> 3, r = a.tiles & 7, x = tile & 7;
+    tile = x * q + min(x, r) + (tile >> 3);
+  }
+  const GProb& P = a.p[group_find(a, tile)];
+  const int lt = tile - P.tile0;
+  DlCtx c;
+  c.A = P.A;
+  c.B = P.B;
+  c.lda = P.lda;
+  c.ldb = P.ldb;
+  c.M = P.M;
+  c.N = P.N;
+  c.m0 = (lt / P.tiles_n) * 256;
+  c.n0 = (lt % P.tiles_n) * 256;
+  c.kbeg = 0;
+  c.nk = a.kchunk / DL_BK;
+  c.wave = wave;
+  c.lane = lane;
+  const DlAddr<false, 8> da(wm * 128, lane);
+  const DlAddr<false, 4> db(wn * 64, lane);
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  w8_issue<false>(c.A, c.lda, c.M, c.m0, 0, A0, wave, lane);
+  w8_issue<false>(c.B, c.ldb, c.N, c.n0, 0, B0, wave, lane);
+  w8_issue<false>(c.A, c.lda, c.M, c.m0, min(1, c.nk - 1) * DL_BK, A1, wave, lane);
+  w8_issue<false>(c.B, c.ldb, c.N, c.n0, min(1, c.nk - 1) * DL_BK, B1, wave, lane);
+  const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
+  const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
+  for (int it = 0; it < c.nk; it += 3) {
+    w8_step<false, false>(c, it, da, db, a0, b0, A2, B2, acc);
+    if (it + 1 < c.nk) w8_step<false, false>(c, it + 1, da, db, a1, b1, A0, B0, acc);
+    if (it + 2 < c.nk) w8_step<false, false>(c, it + 2, da, db, a2, b2, A1, B1, acc);
+  }
+  SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = c.m0 + wm * 128 + i * 16 + (lane & 15);
+    if (m >= P.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = c.n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+      if (n >= P.N) continue;  // N % 8 == 0: the 4 columns are all inside
+      const f32x4 v = acc[i][j];
+      float* dst = P.C + (int64_t)m * P.ldc + n;
+      float4 o = make_float4(P.alpha * v[0], P.alpha * v[1], P.alpha * v[2], P.alpha * v[3]);
+      if (P.accumulate) {
+        const float4 r = *reinterpret_cast<const float4*>(dst);
+        o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+      }
+      *reinterpret_cast<float4*>(dst) = o;
+    }
+  }
+}
+
 // C[m, n] = alpha sum_z ws[z][tile][m, n] (+ C) over the group's tiles; four
 // consecutive columns per thread, splits added in increasing order.
 __global__ __launch_bounds__(256) void gemm_group_reduce_k(GArgs a, int splits) {
@@ -1190,6 +1272,28 @@ slt_status launch_gemm_group(const GroupItem* items, int n, int K, float* ws, in
     tiles += ((it.M + 127) / 128) * P.tiles_n;
   }
   a.tiles = tiles;
+  // 256 x 256 tiles when the group has at least SLT_GROUP_W8_MIN of them and
+  // their edges waste little
+  {
+    int64_t t8 = 0, area = 0;
+    for (int i = 0; i < n; ++i) {
+      t8 += (int64_t)((items[i].M + 255) / 256) * ((items[i].N + 255) / 256);
+      area += (int64_t)items[i].M * items[i].N;
+    }
+    if (SLT_GEMM_W8 && t8 >= SLT_GROUP_W8_MIN && t8 * 256 * 256 <= area * 9 / 8) {
+      GArgs b = a;
+      int t = 0;
+      for (int i = 0; i < n; ++i) {
+        b.p[i].tiles_n = (items[i].N + 255) / 256;
+        b.p[i].tile0 = t;
+        t += ((items[i].M + 255) / 256) * b.p[i].tiles_n;
+      }
+      b.tiles = t;
+      b.kchunk = K;
+      gemm_group_w8_k<<<t, W8_NT, 0, s>>>(b);
+      return check_launch("gemm group (256 x 256)");
+    }
+  }
   // splits: aim for SLT_GROUP_TARGET blocks, at least SLT_SPLIT_MINK k-steps
   // each, K divided evenly in whole k-steps, partials inside the workspace
   const int kt = K / DL_BK;

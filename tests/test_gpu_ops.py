@@ -122,6 +122,50 @@ def test_gemm_big_tiles(B, a_k, b_k, M, N):
     gemm_case(B, rng, M, N, 64, a_k, b_k, BF16, F32, sample=40)
 
 
+def test_gemm_dw_group(B):
+    """Several weight-gradient products in one launch: C_i = alpha_i A_i^T B_i
+    (+ C_i), bf16 operands with rows of tokens, fp32 out; with the workspace
+    (K split over the group's tiles, fixed-order reduction) and without;
+    ragged tiles; one product accumulating into its old value."""
+    rng = np.random.default_rng(8)
+    shapes = [(384, 1024), (2048, 384), (136, 200), (1152, 384)]
+    for K, ws in ((2048, True), (2048, False), (32, True), (96, True)):
+        say("gemm group", K, ws)
+        items, refs = [], []
+        for i, (M, N) in enumerate(shapes):
+            A = rnd(rng, (K, M), BF16)
+            Bm = rnd(rng, (K, N), BF16)
+            old = rng.standard_normal((M, N)).astype(np.float32)
+            C = torch.from_numpy(old).cuda()
+            alpha = 0.5 if i == 1 else 1.0
+            acc = i == 2
+            items.append((M, N, dev(A, BF16), M, dev(Bm, BF16), N, C, N, alpha, acc))
+            refs.append(alpha * (A.T @ Bm) + (old if acc else 0.0))
+        W = torch.empty(64 << 20, dtype=torch.uint8, device="cuda") if ws else None
+        B.slt_gemm_dw_group(items, K, W, W.numel() if ws else 0)
+        for it, ref in zip(items, refs):
+            check(host(it[6]), ref, "bf16", f"group product {it[0]}x{it[1]} K={K}")
+    # a group with at least 160 tiles of 256 x 256 takes the 8-wave kernel
+    # (whole K per block): ragged M and N, 1, 3 and 5 k-steps
+    for K in (32, 96, 160):
+        say("gemm group, 256 x 256 tiles", K)
+        items, refs = [], []
+        for i, (M, N) in enumerate([(4104, 4000), (1024, 2048)]):
+            A = rnd(rng, (K, M), BF16)
+            Bm = rnd(rng, (K, N), BF16)
+            old = rng.standard_normal((M, N)).astype(np.float32)
+            C = torch.from_numpy(old).cuda()
+            items.append((M, N, dev(A, BF16), M, dev(Bm, BF16), N, C, N, 0.25 if i else 1.0, i == 0))
+            refs.append((0.25 if i else 1.0) * (A.T @ Bm) + (old if i == 0 else 0.0))
+        B.slt_gemm_dw_group(items, K)
+        for it, ref in zip(items, refs):
+            check(host(it[6]), ref, "bf16", f"group product {it[0]}x{it[1]} K={K}")
+    A = torch.zeros(32, 12, dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros(12, 12, device="cuda")
+    with pytest.raises(B.SltError):  # M and N not multiples of 8
+        B.slt_gemm_dw_group([(12, 12, A, 12, A, 12, C, 12, 1.0, 0)], 32)
+
+
 def test_gemm_zero_k_gives_residual_or_zero(B):
     rng = np.random.default_rng(2)
     gemm_case(B, rng, 17, 9, 0, 1, 1, F32, F32)
