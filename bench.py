@@ -325,11 +325,13 @@ def main():
         out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
                               if kk in ("ms_per_step", "launches", "tflops", "gbps", "frac_of_peak", "avg_launch_us")}
                           for k, v in cl.items()}
-        # the dominant kernel of the step (largest total time in the kernel
-        # trace): the forward-projection GEMM, every launch of which is
-        # gemm_dl_k with both operands k-major
+        # the dominant kernel class of the step (largest time in the
+        # breakdown): the forward-projection GEMMs, both operands k-major
+        # (gemm_d64_k for 384 to 1152 output columns, gemm_w8_k's 256 x 256
+        # tiles for the wide ones at this workload)
         c = cl["gemm_fwd"]
-        out["roofline"] = {"kernel": "gemm_dl_k (forward projections, k-major x k-major)", "bound": c["bound"],
+        out["roofline"] = {"kernel": "forward-projection GEMMs (gemm_d64_k, gemm_w8_k; k-major x k-major)",
+                           "bound": c["bound"],
                            "achieved": round(c["tflops"], 2), "peak": c["peak"], "unit": "TFLOP/s",
                            "frac": round(c["tflops"] / c["peak"], 4), "traffic": measured_traffic(w),
                            "avg_launch_us": round(c["avg_launch_us"], 2), "launches_per_step": c["launches"]}

@@ -892,6 +892,18 @@ __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
   fl_store_rows(F2, 1.0f, a.dv + (int64_t)b * T * a.lddv + (int64_t)kvh * a.d, a.lddv, k0, T, a.d, 0, 0, nullptr);
 }
 
+// Copy rows row0..row0+63 of a bf16 array into an LDS tile with 512 threads:
+// one copy per lane (as fl_issue).
+__device__ __forceinline__ void fl_issue8(const bf16* g, int64_t ld, int row0, int nrows, int nch, char* tile,
+                                          int wave, int lane) {
+  const int p = wave * 64 + lane;
+  const int r = p >> 3;
+  const int c = (p & 7) ^ fsw(r);
+  const void* src = c < nch ? static_cast<const void*>(g + (int64_t)min(row0 + r, nrows - 1) * ld + c * 8)
+                            : static_cast<const void*>(g_zero16);
+  lds_copy16(src, tile + wave * 1024);
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV over 256-key chunks.  One 8-wave workgroup per (key chunk, KV head,
 // batch), chunks with the most queries first; wave w owns the key subtiles
@@ -906,17 +918,6 @@ __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
 constexpr int KC = 256;                 // keys per chunk
 constexpr int STB = 3 * FTB + 1024;     // stage bytes: Q hi, Q lo, dO, then lse (256 B), D (256 B), pad
 
-// Copy rows row0..row0+63 of a bf16 array into an LDS tile with 512 threads:
-// one copy per lane (as fl_issue).
-__device__ __forceinline__ void fl_issue8(const bf16* g, int64_t ld, int row0, int nrows, int nch, char* tile,
-                                          int wave, int lane) {
-  const int p = wave * 64 + lane;
-  const int r = p >> 3;
-  const int c = (p & 7) ^ fsw(r);
-  const void* src = c < nch ? static_cast<const void*>(g + (int64_t)min(row0 + r, nrows - 1) * ld + c * 8)
-                            : static_cast<const void*>(g_zero16);
-  lds_copy16(src, tile + wave * 1024);
-}
 
 __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[3][STB];
