@@ -264,6 +264,27 @@ typedef struct {
 slt_status slt_gemm_dw_group(const slt_gemm_group_item* items, int32_t n, int32_t K, void* workspace,
                              int64_t workspace_bytes, void* stream);
 
+/* MLP input projection with SwiGLU (Hephaistos, "Architecture at a glance":
+ * (silu(x W1) * x W3) W2):
+ *   ab[M, 2F] = x[M, C] [W1; W3]^T   (a in columns 0..F-1, b in F..2F-1)
+ *   h[M, F]   = silu(a) * b          (from a and b as stored, i.e. rounded)
+ * w13: [2F, C] (w1 then w3, as in the parameter layout); row strides C, 2F,
+ * F.  Large bf16 shapes run as one launch (the GEMM epilogue writes a, b and
+ * h), others as the GEMM and the element kernel; the results are the same
+ * either way. */
+slt_status slt_mlp_swiglu_fwd(int32_t M, int32_t F, int32_t C, const void* x, const void* w13, void* ab, void* h,
+                              int32_t dtype, void* stream);
+
+/* Its backward into the projection outputs:
+ *   dh = dy[M, C] W2[C, F]  (rounded to the activation type, as a stored
+ *                            activation gradient)
+ *   da, db from a, b (ab, row stride 2F) and dh  ->  dab[M, 2F] = [da | db]
+ * w2: [C, F].  dh_workspace: [M, F] in dtype, written where the fused
+ * single-launch form does not apply (large bf16 shapes never touch it); NULL
+ * is allowed only for shapes that run fused (else SLT_EINVAL). */
+slt_status slt_mlp_swiglu_bwd(int32_t M, int32_t F, int32_t C, const void* dy, const void* w2, const void* ab,
+                              void* dab, void* dh_workspace, int32_t dtype, void* stream);
+
 /* x[b*T + t, :] = wte[tokens[b*ld_tokens + t], :] for t < T. */
 slt_status slt_embedding_fwd(const int32_t* tokens, int32_t B, int32_t T, int64_t ld_tokens,
                              const void* wte, void* x, int32_t V, int32_t C, int32_t dtype,

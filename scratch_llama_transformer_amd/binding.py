@@ -68,6 +68,8 @@ SIGNATURES = {
     "slt_clip_grad_norm": (_I32, [_I64, _P, _I32, _F, _P, _P, _P, _P]),
     "slt_gemm": (_I32, [_I32, _I32, _I32, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _P, _I64,
                         _I32, _I32, _P, _I64, _P]),
+    "slt_mlp_swiglu_fwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _I32, _P]),
+    "slt_mlp_swiglu_bwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P]),
     "slt_gemm_dw_group": (_I32, [ct.POINTER(slt_gemm_group_item), _I32, _I32, _P, _I64, _P]),
     "slt_embedding_fwd": (_I32, [_P, _I32, _I32, _I64, _P, _P, _I32, _I32, _I32, _P]),
     "slt_embedding_bwd_workspace": (_I64, [_I64, _I32]),
@@ -250,6 +252,16 @@ def slt_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, ldc, R, ldr, in_dty
     _check("slt_gemm", load().slt_gemm(M, N, K, _ptr(A), lda, int(a_kmajor), _ptr(B), ldb, int(b_kmajor), _ptr(C),
                                        ldc, _ptr(R), ldr, in_dtype, out_dtype, _ptr(workspace), workspace_bytes,
                                        _stream(stream)))
+
+
+def slt_mlp_swiglu_fwd(M, F, C, x, w13, ab, h, dtype, stream=None):
+    _check("slt_mlp_swiglu_fwd", load().slt_mlp_swiglu_fwd(M, F, C, _ptr(x), _ptr(w13), _ptr(ab), _ptr(h), dtype,
+                                                           _stream(stream)))
+
+
+def slt_mlp_swiglu_bwd(M, F, C, dy, w2, ab, dab, dh_workspace, dtype, stream=None):
+    _check("slt_mlp_swiglu_bwd", load().slt_mlp_swiglu_bwd(M, F, C, _ptr(dy), _ptr(w2), _ptr(ab), _ptr(dab),
+                                                           _ptr(dh_workspace), dtype, _stream(stream)))
 
 
 def slt_gemm_dw_group(items, K, workspace=None, workspace_bytes=0, stream=None):

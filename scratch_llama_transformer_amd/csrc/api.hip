@@ -257,6 +257,37 @@ static slt_status proj_dw(const Ctx& x, int M, int N, int K, const void* dY, int
   return launch_gemm(g, x.s);
 }
 
+// [a | b] = n [W1; W3]^T and h = swiglu(a, b): one fused launch where the
+// fused kernel applies (bf16, wide enough grids), else the projection and the
+// element kernel.
+static slt_status mlp_in(int M, int F, int C, const void* n, const void* w13, char* ab, void* h, int dt,
+                         hipStream_t s) {
+  if (dt == SLT_BF16) {
+    const slt_status st = launch_gemm_swiglu_fwd(M, F, C, n, C, w13, ab, 2 * F, h, F, s);
+    if (st != SLT_EUNSUPPORTED) return st;
+  }
+  GemmArgs g{M, 2 * F, C, n, C, true, w13, C, true, ab, 2 * F, nullptr, 0, dt, dt, nullptr, 0};
+  SLT_TRY(launch_gemm(g, s));
+  const int64_t es = dt == SLT_BF16 ? 2 : 4;
+  return launch_swiglu_fwd(ab, ab + F * es, h, M, F, 2 * F, 2 * F, F, dt, s);
+}
+
+// [da | db] from dh = dY W2 and the cached [a | b]: one fused launch where it
+// applies (dh never stored), else the product into dh_buf and the element
+// kernel.
+static slt_status mlp_in_bwd(int M, int F, int C, const void* dy, const void* w2, const char* ab, char* dab,
+                             void* dh_buf, int dt, hipStream_t s) {
+  if (dt == SLT_BF16) {
+    const slt_status st = launch_gemm_swiglu_bwd(M, F, C, dy, C, w2, ab, 2 * F, dab, 2 * F, s);
+    if (st != SLT_EUNSUPPORTED) return st;
+  }
+  if (!dh_buf) return fail(SLT_EINVAL, "SwiGLU backward: this shape needs the dh workspace");
+  GemmArgs g{M, F, C, dy, C, true, w2, F, false, dh_buf, F, nullptr, 0, dt, dt, nullptr, 0};
+  SLT_TRY(launch_gemm(g, s));
+  const int64_t es = dt == SLT_BF16 ? 2 : 4;
+  return launch_swiglu_bwd(ab, ab + F * es, dh_buf, dab, dab + F * es, M, F, 2 * F, 2 * F, F, 2 * F, 2 * F, dt, s);
+}
+
 // Weight gradients deferred to the end of a layer's backward walk, so that
 // they run as one grouped launch (every product fits the grouped kernel) or
 // else one GEMM each, in the order they were added.
@@ -331,9 +362,7 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
       SLT_TRY(launch_attention_fwd(at, x.s));
       SLT_TRY(proj(x, N, C, p.qd, x.A(A.o), p.qd, x.P(W.wo), xmid, C, xin, C));
       SLT_TRY(launch_rmsnorm_fwd(xmid, x.P(W.norm2), x.A(A.n2), (float*)x.A(A.r2), N, C, c.eps, x.dt, x.s));
-      SLT_TRY(proj(x, N, 2 * c.F, C, x.A(A.n2), C, x.P(W.w1), x.A(A.ab), 2 * c.F, nullptr, 0));
-      char* ab = (char*)x.A(A.ab);
-      SLT_TRY(launch_swiglu_fwd(ab, ab + c.F * p.es, x.A(A.h), N, c.F, 2 * c.F, 2 * c.F, c.F, x.dt, x.s));
+      SLT_TRY(mlp_in(N, c.F, C, x.A(A.n2), x.P(W.w1), (char*)x.A(A.ab), x.A(A.h), x.dt, x.s));
       SLT_TRY(proj(x, N, C, c.F, x.A(A.h), c.F, x.P(W.w2), xout, C, xmid, C));
     } else {
       void* xin = x.A(p.xs[l]);
@@ -405,10 +434,7 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       char* dqkv = (char*)x.S(p.dqkv);
       // x_out = x_mid + h W2^T
       dws.add(N, C, c.F, dx, C, x.A(A.h), c.F, grads + W.w2, c.F);
-      SLT_TRY(proj_dx(x, N, C, c.F, dx, C, x.P(W.w2), c.F, dmid, c.F));
-      char* ab = (char*)x.A(A.ab);
-      SLT_TRY(launch_swiglu_bwd(ab, ab + c.F * p.es, dmid, dbig, dbig + c.F * p.es, N, c.F, 2 * c.F, 2 * c.F, c.F,
-                                2 * c.F, 2 * c.F, x.dt, x.s));
+      SLT_TRY(mlp_in_bwd(N, c.F, C, dx, x.P(W.w2), (const char*)x.A(A.ab), dbig, dmid, x.dt, x.s));
       dws.add(N, 2 * c.F, C, dbig, 2 * c.F, x.A(A.n2), C, grads + W.w1, C);
       SLT_TRY(proj_dx(x, N, 2 * c.F, C, dbig, 2 * c.F, x.P(W.w1), C, dn, C));
       SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l + 1]), x.P(W.norm2), (const float*)x.A(A.r2), dn, dx, dx2,
@@ -542,9 +568,7 @@ static slt_status forward_cached(const Plan& p, const Ctx& x, const CachePlan& q
     if (p.llama) {
       SLT_TRY(proj(x, M, C, p.qd, ou, p.qd, x.P(W.wo), xb, C, xa, C));
       SLT_TRY(launch_rmsnorm_fwd(xb, x.P(W.norm2), x.A(q.n), (float*)x.A(q.r), M, C, c.eps, x.dt, x.s));
-      char* ab = (char*)x.A(q.ab);
-      SLT_TRY(proj(x, M, 2 * c.F, C, x.A(q.n), C, x.P(W.w1), ab, 2 * c.F, nullptr, 0));
-      SLT_TRY(launch_swiglu_fwd(ab, ab + c.F * p.es, x.A(q.h), M, c.F, 2 * c.F, 2 * c.F, c.F, x.dt, x.s));
+      SLT_TRY(mlp_in(M, c.F, C, x.A(q.n), x.P(W.w1), (char*)x.A(q.ab), x.A(q.h), x.dt, x.s));
       SLT_TRY(proj(x, M, C, c.F, x.A(q.h), c.F, x.P(W.w2), xa, C, xb, C));
     } else {
       SLT_TRY(launch_gelu_fwd(qkv + p.qkv_w * p.es, ou + p.qd * p.es, M, c.F, p.in_w, p.ou_w, x.dt, x.s));
@@ -895,6 +919,25 @@ slt_status slt_softmax_xent(void* z, int64_t ldz, const int32_t* tokens, int32_t
     return fail(SLT_EINVAL, "softmax_xent: bad sizes");
   if (!z || !tokens || !loss || !workspace) return fail(SLT_EINVAL, "softmax_xent: NULL pointer");
   return launch_softmax_xent(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtype, workspace, as_stream(stream));
+}
+
+slt_status slt_mlp_swiglu_fwd(int32_t M, int32_t F, int32_t C, const void* x, const void* w13, void* ab, void* h,
+                              int32_t dtype, void* stream) {
+  if (M < 0 || F <= 0 || C <= 0) return fail(SLT_EINVAL, "mlp_swiglu_fwd: bad sizes");
+  if (!is_dtype(dtype)) return fail(SLT_EINVAL, "mlp_swiglu_fwd: bad dtype");
+  if (M == 0) return SLT_OK;
+  if (!x || !w13 || !ab || !h) return fail(SLT_EINVAL, "mlp_swiglu_fwd: NULL pointer");
+  return mlp_in(M, F, C, x, w13, static_cast<char*>(ab), h, dtype, as_stream(stream));
+}
+
+slt_status slt_mlp_swiglu_bwd(int32_t M, int32_t F, int32_t C, const void* dy, const void* w2, const void* ab,
+                              void* dab, void* dh_workspace, int32_t dtype, void* stream) {
+  if (M < 0 || F <= 0 || C <= 0) return fail(SLT_EINVAL, "mlp_swiglu_bwd: bad sizes");
+  if (!is_dtype(dtype)) return fail(SLT_EINVAL, "mlp_swiglu_bwd: bad dtype");
+  if (M == 0) return SLT_OK;
+  if (!dy || !w2 || !ab || !dab) return fail(SLT_EINVAL, "mlp_swiglu_bwd: NULL pointer");
+  return mlp_in_bwd(M, F, C, dy, w2, static_cast<const char*>(ab), static_cast<char*>(dab), dh_workspace, dtype,
+                    as_stream(stream));
 }
 
 slt_status slt_gemm_dw_group(const slt_gemm_group_item* items, int32_t n, int32_t K, void* workspace,

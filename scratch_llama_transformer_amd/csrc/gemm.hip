@@ -55,6 +55,9 @@
 #ifndef SLT_W8_MIN
 #define SLT_W8_MIN 256  // fewest 256 x 256 tiles for the 8-wave kernel
 #endif
+#ifndef SLT_FUSED_SWIGLU
+#define SLT_FUSED_SWIGLU 1  // SwiGLU in the epilogues of the 256 x 256 kernel
+#endif
 #ifndef SLT_GEMM_BAND
 #define SLT_GEMM_BAND 8  // tile rows per band of the 256 x 256 tile order
 #endif
@@ -200,6 +203,9 @@ struct KArgs {
   int tiles_n, tiles;
   bool evec;          // 4-wide epilogue stores allowed
   float alpha;        // C = alpha A B (+ R)
+  void* C2;           // fused SwiGLU epilogues: h (forward)
+  int64_t ldc2;
+  int F;              // fused SwiGLU epilogues: MLP width (b at column F + f)
 };
 
 template <typename TO>
@@ -705,7 +711,24 @@ __device__ __forceinline__ void w8_issue(const bf16* g, int64_t ld, int rows, in
   }
 }
 
-template <bool AK, bool BK>
+// B sub-tiles of the fused [W1; W3] projection: tile rows 64 w .. 64 w + 31
+// are W1 rows f0 + 32 w + (0..31) and rows 64 w + 32 .. 64 w + 63 the W3 rows
+// F + f0 + 32 w + (0..31), so that wave w's fragments 0, 1 (a) and 2, 3 (b)
+// hold the same 32 output columns f.  F % 128 == 0.
+__device__ __forceinline__ void w8_issue_pair(const bf16* g, int64_t ld, int F, int f0, int k0, bf16* tile, int wave,
+                                              int lane) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int p = wave * 64 + lane;
+    const int r = p >> 2;
+    const int lc = (p & 3) ^ dl_swz(r);
+    const int n = 128 * s + r, w = n & 63;
+    const int grow = (w < 32 ? f0 : F + f0 - 32) + 32 * (n >> 6) + w;
+    lds_copy16(g + (int64_t)grow * ld + k0 + lc * 8, tile + s * DL_TILE + wave * 512);
+  }
+}
+
+template <bool AK, bool BK, int EPI = 0>
 __device__ __forceinline__ void w8_step(const DlCtx& c, int it, const DlAddr<AK, 8>& da, const DlAddr<BK, 4>& db,
                                         unsigned as, unsigned bs, bf16* An, bf16* Bn, f32x4 (&acc)[8][4]) {
   SLT_WAIT_VMCNT(4);  // only the copies of tile it+1 may still fly
@@ -714,7 +737,8 @@ __device__ __forceinline__ void w8_step(const DlCtx& c, int it, const DlAddr<AK,
   dl_read<AK, BK, 8, 4>(da.at(as), db.at(bs), af, bfr);
   const int kn = c.kbeg + min(it + 2, c.nk - 1) * DL_BK;
   w8_issue<AK>(c.A, c.lda, c.M, c.m0, kn, An, c.wave, c.lane);
-  w8_issue<BK>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
+  if constexpr (EPI == 1) w8_issue_pair(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
+  else w8_issue<BK>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -723,7 +747,59 @@ __device__ __forceinline__ void w8_step(const DlCtx& c, int it, const DlAddr<AK,
                                                           __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
 }
 
-template <typename TO, bool AK, bool BK>
+// Fused SwiGLU epilogues of the 256 x 256 kernel (bf16).  EPI 1: the tile
+// covers f0 .. f0 + 127 of a and of b (w8_issue_pair); writes a, b and h.
+// EPI 2: the product is dh (columns f); dh is rounded to bf16 as a stored
+// activation gradient would be, a and b are read from R, da and db written.
+__device__ __forceinline__ void w8_epilogue_swiglu_fwd(const KArgs& a, const f32x4 (&acc)[8][4], int m0, int f0,
+                                                       int wm, int wn, int lane) {
+  bf16* ab = static_cast<bf16*>(a.C);
+  bf16* hb = static_cast<bf16*>(a.C2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int f = f0 + wn * 32 + j * 16 + 4 * (lane >> 4);
+      float av[4], bv[4], hv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        av[r] = to_f32(from_f32<bf16>(acc[i][j][r]));
+        bv[r] = to_f32(from_f32<bf16>(acc[i][j + 2][r]));
+        hv[r] = swiglu_h(av[r], bv[r]);
+      }
+      store4<bf16>(ab + (int64_t)m * a.ldc + f, av);
+      store4<bf16>(ab + (int64_t)m * a.ldc + a.F + f, bv);
+      store4<bf16>(hb + (int64_t)m * a.ldc2 + f, hv);
+    }
+  }
+}
+
+__device__ __forceinline__ void w8_epilogue_swiglu_bwd(const KArgs& a, const f32x4 (&acc)[8][4], int m0, int n0,
+                                                       int wm, int wn, int lane) {
+  const bf16* ab = static_cast<const bf16*>(a.R);
+  bf16* dab = static_cast<bf16*>(a.C);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+      if (f >= a.N) continue;  // F % 4 == 0: the 4 columns are all inside
+      float av[4], bv[4], da[4], db[4];
+      load4<bf16>(ab + (int64_t)m * a.ldr + f, av);
+      load4<bf16>(ab + (int64_t)m * a.ldr + a.F + f, bv);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) swiglu_grad(av[r], bv[r], to_f32(from_f32<bf16>(acc[i][j][r])), da[r], db[r]);
+      store4<bf16>(dab + (int64_t)m * a.ldc + f, da);
+      store4<bf16>(dab + (int64_t)m * a.ldc + a.F + f, db);
+    }
+  }
+}
+
+template <typename TO, bool AK, bool BK, int EPI = 0>
 __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 A0[2 * DL_TILE], A1[2 * DL_TILE], A2[2 * DL_TILE];
   __shared__ __attribute__((aligned(16))) bf16 B0[2 * DL_TILE], B1[2 * DL_TILE], B2[2 * DL_TILE];
@@ -745,7 +821,8 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
   c.M = a.M;
   c.N = a.N;
   c.m0 = tm * 256;
-  c.n0 = tn * 256;
+  c.n0 = EPI == 1 ? tn * 128 : tn * 256;  // EPI 1: first f of the tile (B rows gathered by w8_issue_pair)
+  if (EPI == 1) c.N = a.F;
   c.kbeg = 0;
   c.nk = a.K / DL_BK;
   c.wave = wave;
@@ -759,19 +836,26 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  w8_issue<AK>(c.A, c.lda, c.M, c.m0, 0, A0, wave, lane);
-  w8_issue<BK>(c.B, c.ldb, c.N, c.n0, 0, B0, wave, lane);
-  w8_issue<AK>(c.A, c.lda, c.M, c.m0, min(1, c.nk - 1) * DL_BK, A1, wave, lane);
-  w8_issue<BK>(c.B, c.ldb, c.N, c.n0, min(1, c.nk - 1) * DL_BK, B1, wave, lane);
+  // tile 0's copies (A then B), then tile 1's: the first step's vmcnt wait
+  // counts on that order
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int k0 = min(t, c.nk - 1) * DL_BK;
+    w8_issue<AK>(c.A, c.lda, c.M, c.m0, k0, t ? A1 : A0, wave, lane);
+    if constexpr (EPI == 1) w8_issue_pair(c.B, c.ldb, c.N, c.n0, k0, t ? B1 : B0, wave, lane);
+    else w8_issue<BK>(c.B, c.ldb, c.N, c.n0, k0, t ? B1 : B0, wave, lane);
+  }
   const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
   const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
   for (int it = 0; it < c.nk; it += 3) {
-    w8_step<AK, BK>(c, it, da, db, a0, b0, A2, B2, acc);
-    if (it + 1 < c.nk) w8_step<AK, BK>(c, it + 1, da, db, a1, b1, A0, B0, acc);
-    if (it + 2 < c.nk) w8_step<AK, BK>(c, it + 2, da, db, a2, b2, A1, B1, acc);
+    w8_step<AK, BK, EPI>(c, it, da, db, a0, b0, A2, B2, acc);
+    if (it + 1 < c.nk) w8_step<AK, BK, EPI>(c, it + 1, da, db, a1, b1, A0, B0, acc);
+    if (it + 2 < c.nk) w8_step<AK, BK, EPI>(c, it + 2, da, db, a2, b2, A1, B1, acc);
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
-  dl_epilogue<TO, false, 8, 4>(a, acc, c.m0, c.n0, wm, wn, lane);
+  if constexpr (EPI == 1) w8_epilogue_swiglu_fwd(a, acc, c.m0, c.n0, wm, wn, lane);
+  else if constexpr (EPI == 2) w8_epilogue_swiglu_bwd(a, acc, c.m0, c.n0, wm, wn, lane);
+  else dl_epilogue<TO, false, 8, 4>(a, acc, c.m0, c.n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1240,6 +1324,46 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
 }
 
 }  // namespace
+
+// The 256 x 256 kernel's selection rule (see run()) for an M x N grid.
+static bool w8_fits(int M, int N) {
+  const int t8m = (M + 255) / 256, t8n = (N + 255) / 256, t8 = t8m * t8n;
+  const bool edges = (int64_t)t8 * 256 * 256 <= (int64_t)M * N * 9 / 8;
+  const bool rounds = t8 * 20 >= ((t8 + 255) / 256) * 256 * 17;
+  return SLT_GEMM_W8 && t8 >= SLT_W8_MIN && edges && rounds;
+}
+
+slt_status launch_gemm_swiglu_fwd(int M, int F, int K, const void* X, int64_t ldx, const void* W13, void* ab,
+                                  int64_t ldab, void* h, int64_t ldh, hipStream_t s) {
+  if (!(SLT_FUSED_SWIGLU && M > 0 && F > 0 && F % 128 == 0 && K > 0 && K % DL_BK == 0 && al(X, 16) && ldx % 8 == 0 && al(W13, 16) &&
+        al(ab, 8) && ldab % 4 == 0 && al(h, 8) && ldh % 4 == 0 && w8_fits(M, 2 * F)))
+    return fail(SLT_EUNSUPPORTED, "fused SwiGLU projection: shape or alignment");
+  KArgs ka{};
+  ka.M = M; ka.N = 2 * F; ka.K = K;
+  ka.A = X; ka.lda = ldx; ka.B = W13; ka.ldb = K;
+  ka.C = ab; ka.ldc = ldab; ka.C2 = h; ka.ldc2 = ldh; ka.F = F;
+  ka.alpha = 1.f;
+  ka.tiles_n = F / 128;
+  ka.tiles = ((M + 255) / 256) * ka.tiles_n;
+  gemm_w8_k<bf16, true, true, 1><<<ka.tiles, W8_NT, 0, s>>>(ka);
+  return check_launch("fused SwiGLU projection");
+}
+
+slt_status launch_gemm_swiglu_bwd(int M, int F, int K, const void* dY, int64_t lddy, const void* W2,
+                                  const void* ab, int64_t ldab, void* dab, int64_t lddab, hipStream_t s) {
+  if (!(SLT_FUSED_SWIGLU && M > 0 && F >= 8 && F % 8 == 0 && K > 0 && K % DL_BK == 0 && al(dY, 16) && lddy % 8 == 0 && al(W2, 16) &&
+        al(ab, 8) && ldab % 4 == 0 && al(dab, 8) && lddab % 4 == 0 && w8_fits(M, F)))
+    return fail(SLT_EUNSUPPORTED, "fused SwiGLU backward: shape or alignment");
+  KArgs ka{};
+  ka.M = M; ka.N = F; ka.K = K;
+  ka.A = dY; ka.lda = lddy; ka.B = W2; ka.ldb = F;
+  ka.C = dab; ka.ldc = lddab; ka.R = ab; ka.ldr = ldab; ka.F = F;
+  ka.alpha = 1.f;
+  ka.tiles_n = (F + 255) / 256;
+  ka.tiles = ((M + 255) / 256) * ka.tiles_n;
+  gemm_w8_k<bf16, true, false, 2><<<ka.tiles, W8_NT, 0, s>>>(ka);
+  return check_launch("fused SwiGLU backward");
+}
 
 bool gemm_group_ok(const GroupItem& it, int K) {
   auto al16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };

@@ -554,7 +554,6 @@ constexpr int kNormBwdBlocks = SLT_NORM_BLOCKS;
 // ---------------------------------------------------------------------------
 // SwiGLU and GELU on [rows, F] with row strides.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
 template <typename T, int VEC>
 __global__ __launch_bounds__(256) void swiglu_fwd_k(const T* __restrict__ a, const T* __restrict__ b,
@@ -570,7 +569,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd_k(const T* __restrict__ a, con
     load_f<T, VEC>(a + r * lda + c, av);
     load_f<T, VEC>(b + r * ldb + c, bv);
 #pragma unroll
-    for (int q = 0; q < VEC; ++q) out[q] = av[q] * sigmoidf_(av[q]) * bv[q];
+    for (int q = 0; q < VEC; ++q) out[q] = swiglu_h(av[q], bv[q]);
     store_f<T, VEC>(h + r * ldh + c, out);
   }
 }
@@ -591,11 +590,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_k(const T* __restrict__ a, con
     load_f<T, VEC>(b + r * ldb + c, bv);
     load_f<T, VEC>(dh + r * lddh + c, hv);
 #pragma unroll
-    for (int q = 0; q < VEC; ++q) {
-      const float sg = sigmoidf_(av[q]);
-      ob[q] = hv[q] * av[q] * sg;
-      oa[q] = hv[q] * bv[q] * sg * (1.0f + av[q] * (1.0f - sg));
-    }
+    for (int q = 0; q < VEC; ++q) swiglu_grad(av[q], bv[q], hv[q], oa[q], ob[q]);
     store_f<T, VEC>(da + r * ldda + c, oa);
     store_f<T, VEC>(db + r * lddb + c, ob);
   }

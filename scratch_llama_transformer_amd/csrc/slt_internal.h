@@ -31,6 +31,18 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(slt_f32x2{a, b}, slt_bf16x2));
 }
 
+// SwiGLU (Hephaistos, "Architecture at a glance": silu(x W1) * (x W3)), shared
+// by the element kernels and the fused GEMM epilogues so both compute the
+// same expression: h = a sigmoid(a) b; db = dh a sigmoid(a),
+// da = dh b sigmoid(a) (1 + a (1 - sigmoid(a))).
+__device__ __forceinline__ float slt_sigmoid(float a) { return 1.0f / (1.0f + __expf(-a)); }
+__device__ __forceinline__ float swiglu_h(float a, float b) { return a * slt_sigmoid(a) * b; }
+__device__ __forceinline__ void swiglu_grad(float a, float b, float dh, float& da, float& db) {
+  const float sg = slt_sigmoid(a);
+  db = dh * a * sg;
+  da = dh * b * sg * (1.0f + a * (1.0f - sg));
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return bf16{f32_to_bf16_bits(x)}; }
@@ -93,6 +105,17 @@ struct GradW {
   bool accumulate = false;
 };
 slt_status launch_gemm(const GemmArgs& g, hipStream_t s);
+
+// [W1; W3] projection fused with SwiGLU: ab[M, 2F] = X[M, K] W13[2F, K]^T
+// (a | b, bf16, row stride ldab) and h[M, F] = swiglu(bf16(a), bf16(b)).
+// SLT_EUNSUPPORTED (nothing enqueued) where the fused kernel does not apply.
+slt_status launch_gemm_swiglu_fwd(int M, int F, int K, const void* X, int64_t ldx, const void* W13, void* ab,
+                                  int64_t ldab, void* h, int64_t ldh, hipStream_t s);
+// W2 activation gradient fused with the SwiGLU backward: dh = dY[M, K] W2[K, F]
+// rounded to bf16, then [da | db] (row stride lddab) from ab (row stride ldab).
+// SLT_EUNSUPPORTED (nothing enqueued) where the fused kernel does not apply.
+slt_status launch_gemm_swiglu_bwd(int M, int F, int K, const void* dY, int64_t lddy, const void* W2,
+                                  const void* ab, int64_t ldab, void* dab, int64_t lddab, hipStream_t s);
 
 // One product of a grouped weight-gradient launch: C[M, N] (fp32, row stride
 // ldc) = alpha sum_k A[k lda + m] B[k ldb + n] (+ C when accumulate), bf16

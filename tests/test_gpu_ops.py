@@ -188,6 +188,49 @@ def test_gemm_full_size_sampled_rows(B, shape):
     gemm_case(B, rng, M, N, K, a_k, b_k, ind, outd, resid, ws, sample=48)
 
 
+@pytest.mark.parametrize("M,F,C,dtype", [
+    (16384, 1024, 384, BF16),   # the d=384 MLP: one fused launch each way
+    (12296, 1152, 256, BF16),   # fused, ragged M
+    (1000, 512, 256, BF16),     # too small a grid: GEMM and element kernel
+    (300, 96, 64, F32),         # fp32: GEMM and element kernel
+])
+def test_mlp_swiglu_projection_fwd_bwd(B, M, F, C, dtype):
+    """[a | b] = x [W1; W3]^T with h = swiglu(a, b), and the backward
+    dh = dy W2 -> [da | db], whether they run as one fused launch (large bf16
+    grids) or as the GEMM plus the element kernel; sampled rows."""
+    say("mlp swiglu", M, F, C, dtype)
+    rng = np.random.default_rng(11)
+    x = rnd(rng, (M, C), dtype)
+    w13 = rnd(rng, (2 * F, C), dtype, 0.05)
+    ab = torch.full((M, 2 * F), float("nan"), dtype=torch.bfloat16 if dtype == BF16 else torch.float32,
+                    device="cuda")
+    h = torch.full((M, F), float("nan"), dtype=ab.dtype, device="cuda")
+    B.slt_mlp_swiglu_fwd(M, F, C, dev(x, dtype), dev(w13, dtype), ab, h, dtype)
+    rows = np.unique(rng.integers(0, M, 64))
+    rows = np.union1d(rows, [0, M - 1])
+    a_ref = ref_round(x[rows] @ w13[:F].T, dtype)
+    b_ref = ref_round(x[rows] @ w13[F:].T, dtype)
+    got_ab = host(ab)[rows]
+    check(got_ab[:, :F], a_ref, act(dtype), "a")
+    check(got_ab[:, F:], b_ref, act(dtype), "b")
+    check(host(h)[rows], ref_round(O.swiglu_fwd(a_ref, b_ref), dtype), act(dtype), "h")
+    # backward from a fixed (a | b) input
+    abin = rnd(rng, (M, 2 * F), dtype)
+    dy = rnd(rng, (M, C), dtype)
+    w2 = rnd(rng, (C, F), dtype, 0.05)
+    dab = torch.full((M, 2 * F), float("nan"), dtype=ab.dtype, device="cuda")
+    dhws = torch.empty((M, F), dtype=ab.dtype, device="cuda")
+    B.slt_mlp_swiglu_bwd(M, F, C, dev(dy, dtype), dev(w2, dtype), dev(abin, dtype), dab, dhws, dtype)
+    dh = ref_round(dy[rows] @ w2, dtype)
+    da, db = O.swiglu_bwd(abin[rows, :F], abin[rows, F:], dh)
+    got = host(dab)[rows]
+    check(got[:, :F], ref_round(da, dtype), act(dtype), "da")
+    check(got[:, F:], ref_round(db, dtype), act(dtype), "db")
+    if M == 1000:  # an unfused shape needs the dh workspace
+        with pytest.raises(B.SltError):
+            B.slt_mlp_swiglu_bwd(M, F, C, dev(dy, dtype), dev(w2, dtype), dev(abin, dtype), dab, None, dtype)
+
+
 # ---------------------------------------------------------------------------
 # Embedding
 # ---------------------------------------------------------------------------

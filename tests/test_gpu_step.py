@@ -9,7 +9,7 @@ import pytest
 
 import oracle as O
 import slt_workloads as W
-from parity import LOSS_TOL, check, check_bf16_step_tensor, check_bf16_step_weights, check_weights
+from parity import LOSS_TOL, band_stats, check, check_bf16_step_tensor, check_bf16_step_weights, check_weights
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -77,6 +77,40 @@ def test_full_step_parity(TS, ci, Bn, L):
         print(f"[result] worst over gradients: normwise {worst[0]:.2e}, 99.9% quantile {worst[1]:.2f}x band, "
               f"worst element {worst[2]:.2f}x band")
     print(f"[result] {w.name} loss gpu {loss:.7f} oracle {ref['loss']:.7f}; tie-exempt weights {ties}")
+
+
+@pytest.mark.timeout(900)
+def test_full_batch_step_one_layer(TS):
+    """The d=384 workload's whole 64-sequence batch (16384 tokens) through one
+    layer: every product at its full token count (the fused SwiGLU launches,
+    the grouped weight gradients with split K, the 256 x 256 tiles).  Loss,
+    every gradient and every post-AdamW weight against the oracle.  Gradients:
+    normwise and 99.9th-percentile rules as for the reduced cases; the worst
+    element is held to 3 bands instead of 3x the companion's worst, because
+    16384-token weight-gradient sums also carry the GPU's in-register
+    roundings (P in the forward's P V feeds n2), which the storage-rounding
+    companion does not model -- measured ~2-2.5 bands on w1/w2/w3 for both the
+    fused and the unfused MLP kernels (bitwise equal)."""
+    w = W.get_config(3).with_(B=64, L=1)
+    say("full-batch step", w)
+    params, tokens, ts, loss = run_step(TS, w, 1003)
+    ref = O.train_step(w, params, tokens)
+    assert abs(loss - ref["loss"]) <= LOSS_TOL[w.act] * abs(ref["loss"]), (loss, ref["loss"])
+    grads = ts.unpack(ts.grads)
+    new = ts.unpack(ts.master)
+    _, ccache = O.forward(w, params, tokens, jitter=2.0 ** -24, seed=1)
+    comp = O.backward(w, ccache)
+    for name in params:
+        g = np.asarray(grads[name], np.float64)
+        assert np.all(np.isfinite(g)), name
+        nw, q, worst = band_stats(g, ref["grads"][name])
+        cnw, cq, _ = band_stats(comp[name], ref["grads"][name])
+        print(f"[result] {name}: normwise {nw:.2e} (companion {cnw:.2e}), 99.9% {q:.2f}, worst {worst:.2f} bands")
+        assert nw <= min(2e-2, max(3 * cnw, 2e-3)), (name, nw, cnw)
+        assert q <= max(3 * cq, 1.0), (name, q, cq)
+        assert worst <= 3.0, (name, worst)
+        check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
+                                f"weight {name}", w.adam_eps)
 
 
 @pytest.mark.timeout(900)
