@@ -275,13 +275,19 @@ slt_status slt_gemm_dw_group(const slt_gemm_group_item* items, int32_t n, int32_
 slt_status slt_mlp_swiglu_fwd(int32_t M, int32_t F, int32_t C, const void* x, const void* w13, void* ab, void* h,
                               int32_t dtype, void* stream);
 
+/* Projection whose trailing columns feed GELU (Transformer in Rust, "CodeGen:
+ * Parallel Sub-Block Design": one LayerNorm output feeds attention and the
+ * GELU MLP, so [q | k | v | fc_in] is one product):
+ *   y[M, N] = x[M, K] w[N, K]^T        (row stride ldy)
+ *   u[M, N - col0] = gelu(y[:, col0:])  (tanh form, from y as stored; row
+ *                                        stride ldu) */
+slt_status slt_proj_gelu_fwd(int32_t M, int32_t N, int32_t K, const void* x, const void* w, void* y, int64_t ldy,
+                             int32_t col0, void* u, int64_t ldu, int32_t dtype, void* stream);
+
 /* Its backward into the projection outputs:
- *   dh = dy[M, C] W2[C, F]  (rounded to the activation type, as a stored
- *                            activation gradient)
+ *   dh = dy[M, C] W2[C, F]  -> dh_workspace [M, F] in dtype (row stride F)
  *   da, db from a, b (ab, row stride 2F) and dh  ->  dab[M, 2F] = [da | db]
- * w2: [C, F].  dh_workspace: [M, F] in dtype, written where the fused
- * single-launch form does not apply (large bf16 shapes never touch it); NULL
- * is allowed only for shapes that run fused (else SLT_EINVAL). */
+ * w2: [C, F].  All pointers non-NULL. */
 slt_status slt_mlp_swiglu_bwd(int32_t M, int32_t F, int32_t C, const void* dy, const void* w2, const void* ab,
                               void* dab, void* dh_workspace, int32_t dtype, void* stream);
 

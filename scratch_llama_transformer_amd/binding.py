@@ -69,6 +69,7 @@ SIGNATURES = {
     "slt_gemm": (_I32, [_I32, _I32, _I32, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _P, _I64,
                         _I32, _I32, _P, _I64, _P]),
     "slt_mlp_swiglu_fwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _I32, _P]),
+    "slt_proj_gelu_fwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I64, _I32, _P]),
     "slt_mlp_swiglu_bwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P]),
     "slt_gemm_dw_group": (_I32, [ct.POINTER(slt_gemm_group_item), _I32, _I32, _P, _I64, _P]),
     "slt_embedding_fwd": (_I32, [_P, _I32, _I32, _I64, _P, _P, _I32, _I32, _I32, _P]),
@@ -257,6 +258,11 @@ def slt_gemm(M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, C, ldc, R, ldr, in_dty
 def slt_mlp_swiglu_fwd(M, F, C, x, w13, ab, h, dtype, stream=None):
     _check("slt_mlp_swiglu_fwd", load().slt_mlp_swiglu_fwd(M, F, C, _ptr(x), _ptr(w13), _ptr(ab), _ptr(h), dtype,
                                                            _stream(stream)))
+
+
+def slt_proj_gelu_fwd(M, N, K, x, w, y, ldy, col0, u, ldu, dtype, stream=None):
+    _check("slt_proj_gelu_fwd", load().slt_proj_gelu_fwd(M, N, K, _ptr(x), _ptr(w), _ptr(y), ldy, col0, _ptr(u), ldu,
+                                                         dtype, _stream(stream)))
 
 
 def slt_mlp_swiglu_bwd(M, F, C, dy, w2, ab, dab, dh_workspace, dtype, stream=None):

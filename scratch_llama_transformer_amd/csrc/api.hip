@@ -272,16 +272,18 @@ static slt_status mlp_in(int M, int F, int C, const void* n, const void* w13, ch
   return launch_swiglu_fwd(ab, ab + F * es, h, M, F, 2 * F, 2 * F, F, dt, s);
 }
 
-// [da | db] from dh = dY W2 and the cached [a | b]: one fused launch where it
-// applies (dh never stored), else the product into dh_buf and the element
-// kernel.
+// y = n W^T over N columns and u = gelu(y[:, col0:]).
+static slt_status proj_gelu(int M, int N, int K, const void* n, const void* w, char* y, int64_t ldy, int col0,
+                            char* u, int64_t ldu, int dt, hipStream_t s) {
+  GemmArgs g{M, N, K, n, K, true, w, K, true, y, ldy, nullptr, 0, dt, dt, nullptr, 0};
+  SLT_TRY(launch_gemm(g, s));
+  const int64_t es = dt == SLT_BF16 ? 2 : 4;
+  return launch_gelu_fwd(y + col0 * es, u, M, N - col0, ldy, ldu, dt, s);
+}
+
+// [da | db] from dh = dY W2 (stored in dh_buf) and the cached [a | b].
 static slt_status mlp_in_bwd(int M, int F, int C, const void* dy, const void* w2, const char* ab, char* dab,
                              void* dh_buf, int dt, hipStream_t s) {
-  if (dt == SLT_BF16) {
-    const slt_status st = launch_gemm_swiglu_bwd(M, F, C, dy, C, w2, ab, 2 * F, dab, 2 * F, s);
-    if (st != SLT_EUNSUPPORTED) return st;
-  }
-  if (!dh_buf) return fail(SLT_EINVAL, "SwiGLU backward: this shape needs the dh workspace");
   GemmArgs g{M, F, C, dy, C, true, w2, F, false, dh_buf, F, nullptr, 0, dt, dt, nullptr, 0};
   SLT_TRY(launch_gemm(g, s));
   const int64_t es = dt == SLT_BF16 ? 2 : 4;
@@ -369,14 +371,15 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
       void* xout = x.A(p.xs[l + 1]);
       SLT_TRY(launch_layernorm_fwd(xin, x.P(W.norm1), x.P(W.norm1b), x.A(A.n1), (float*)x.A(A.mu1),
                                    (float*)x.A(A.r1), N, C, c.eps, x.dt, x.s));
-      SLT_TRY(proj(x, N, p.in_w, C, x.A(A.n1), C, x.P(W.qkvw), x.A(A.qkv), p.in_w, nullptr, 0));
       char* qkv = (char*)x.A(A.qkv);
       char* ou = (char*)x.A(A.o);
+      // [q | k | v | a] = n W^T and u = gelu(a) into [o | u]
+      SLT_TRY(proj_gelu(N, p.in_w, C, x.A(A.n1), x.P(W.qkvw), qkv, p.in_w, p.qkv_w, ou + p.qd * p.es, p.ou_w, x.dt,
+                        x.s));
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
       at.ldq = at.ldk = at.ldv = p.in_w;
       at.out = ou; at.ldo = p.ou_w;
       SLT_TRY(launch_attention_fwd(at, x.s));
-      SLT_TRY(launch_gelu_fwd(qkv + p.qkv_w * p.es, ou + p.qd * p.es, N, c.F, p.in_w, p.ou_w, x.dt, x.s));
       SLT_TRY(proj(x, N, C, p.ou_w, ou, p.ou_w, x.P(W.wout), xout, C, xin, C));
     }
   }
@@ -548,7 +551,11 @@ static slt_status forward_cached(const Plan& p, const Ctx& x, const CachePlan& q
     else
       SLT_TRY(launch_layernorm_fwd(xa, x.P(W.norm1), x.P(W.norm1b), x.A(q.n), (float*)x.A(q.mu), (float*)x.A(q.r),
                                    M, C, c.eps, x.dt, x.s));
-    SLT_TRY(proj(x, M, (int)ldqkv, C, x.A(q.n), C, x.P(W.qkvw), qkv, ldqkv, nullptr, 0));
+    if (p.llama)
+      SLT_TRY(proj(x, M, (int)ldqkv, C, x.A(q.n), C, x.P(W.qkvw), qkv, ldqkv, nullptr, 0));
+    else  // [q | k | v | a] and u = gelu(a) into [o | u]
+      SLT_TRY(proj_gelu(M, (int)ldqkv, C, x.A(q.n), x.P(W.qkvw), qkv, ldqkv, p.qkv_w, ou + p.qd * p.es, ldo, x.dt,
+                        x.s));
     SLT_TRY(launch_kv_append(qkv, ldqkv, (float*)x.A(q.qrot), B, Tq, pos0, c.H, c.Hkv, p.d, c.R, c.rope_mode, cs, Kc,
                              Vc, Tmax, x.dt, x.s));
     if (prefill) {
@@ -571,7 +578,6 @@ static slt_status forward_cached(const Plan& p, const Ctx& x, const CachePlan& q
       SLT_TRY(mlp_in(M, c.F, C, x.A(q.n), x.P(W.w1), (char*)x.A(q.ab), x.A(q.h), x.dt, x.s));
       SLT_TRY(proj(x, M, C, c.F, x.A(q.h), c.F, x.P(W.w2), xa, C, xb, C));
     } else {
-      SLT_TRY(launch_gelu_fwd(qkv + p.qkv_w * p.es, ou + p.qd * p.es, M, c.F, p.in_w, p.ou_w, x.dt, x.s));
       SLT_TRY(proj(x, M, C, p.ou_w, ou, p.ou_w, x.P(W.wout), xb, C, xa, C));
       std::swap(xa, xb);
     }
@@ -930,12 +936,23 @@ slt_status slt_mlp_swiglu_fwd(int32_t M, int32_t F, int32_t C, const void* x, co
   return mlp_in(M, F, C, x, w13, static_cast<char*>(ab), h, dtype, as_stream(stream));
 }
 
+slt_status slt_proj_gelu_fwd(int32_t M, int32_t N, int32_t K, const void* x, const void* w, void* y, int64_t ldy,
+                             int32_t col0, void* u, int64_t ldu, int32_t dtype, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0 || col0 < 0 || col0 >= N || ldy < N || ldu < N - col0)
+    return fail(SLT_EINVAL, "proj_gelu_fwd: bad sizes");
+  if (!is_dtype(dtype)) return fail(SLT_EINVAL, "proj_gelu_fwd: bad dtype");
+  if (M == 0) return SLT_OK;
+  if (!x || !w || !y || !u) return fail(SLT_EINVAL, "proj_gelu_fwd: NULL pointer");
+  return proj_gelu(M, N, K, x, w, static_cast<char*>(y), ldy, col0, static_cast<char*>(u), ldu, dtype,
+                   as_stream(stream));
+}
+
 slt_status slt_mlp_swiglu_bwd(int32_t M, int32_t F, int32_t C, const void* dy, const void* w2, const void* ab,
                               void* dab, void* dh_workspace, int32_t dtype, void* stream) {
   if (M < 0 || F <= 0 || C <= 0) return fail(SLT_EINVAL, "mlp_swiglu_bwd: bad sizes");
   if (!is_dtype(dtype)) return fail(SLT_EINVAL, "mlp_swiglu_bwd: bad dtype");
   if (M == 0) return SLT_OK;
-  if (!dy || !w2 || !ab || !dab) return fail(SLT_EINVAL, "mlp_swiglu_bwd: NULL pointer");
+  if (!dy || !w2 || !ab || !dab || !dh_workspace) return fail(SLT_EINVAL, "mlp_swiglu_bwd: NULL pointer");
   return mlp_in_bwd(M, F, C, dy, w2, static_cast<const char*>(ab), static_cast<char*>(dab), dh_workspace, dtype,
                     as_stream(stream));
 }

@@ -56,7 +56,7 @@
 #define SLT_W8_MIN 256  // fewest 256 x 256 tiles for the 8-wave kernel
 #endif
 #ifndef SLT_FUSED_SWIGLU
-#define SLT_FUSED_SWIGLU 1  // SwiGLU in the epilogues of the 256 x 256 kernel
+#define SLT_FUSED_SWIGLU 1  // SwiGLU in the epilogue of the 256 x 256 kernel
 #endif
 #ifndef SLT_GEMM_BAND
 #define SLT_GEMM_BAND 8  // tile rows per band of the 256 x 256 tile order
@@ -747,10 +747,14 @@ __device__ __forceinline__ void w8_step(const DlCtx& c, int it, const DlAddr<AK,
                                                           __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
 }
 
-// Fused SwiGLU epilogues of the 256 x 256 kernel (bf16).  EPI 1: the tile
+// Fused SwiGLU epilogue of the 256 x 256 kernel (bf16, EPI 1): the tile
 // covers f0 .. f0 + 127 of a and of b (w8_issue_pair); writes a, b and h.
-// EPI 2: the product is dh (columns f); dh is rounded to bf16 as a stored
-// activation gradient would be, a and b are read from R, da and db written.
+// Measured alternatives that were not kept: the backward counterpart (dh's
+// product with SwiGLU's backward in the epilogue) was slower than the GEMM
+// plus the element kernel -- with one block per CU its 256 KiB of a/b reads
+// per tile are not overlapped -- and GELU in the parallel block's projection
+// epilogue was no faster than the separate element kernel (its extra stores
+// cost what the saved read gained).
 __device__ __forceinline__ void w8_epilogue_swiglu_fwd(const KArgs& a, const f32x4 (&acc)[8][4], int m0, int f0,
                                                        int wm, int wn, int lane) {
   bf16* ab = static_cast<bf16*>(a.C);
@@ -772,29 +776,6 @@ __device__ __forceinline__ void w8_epilogue_swiglu_fwd(const KArgs& a, const f32
       store4<bf16>(ab + (int64_t)m * a.ldc + f, av);
       store4<bf16>(ab + (int64_t)m * a.ldc + a.F + f, bv);
       store4<bf16>(hb + (int64_t)m * a.ldc2 + f, hv);
-    }
-  }
-}
-
-__device__ __forceinline__ void w8_epilogue_swiglu_bwd(const KArgs& a, const f32x4 (&acc)[8][4], int m0, int n0,
-                                                       int wm, int wn, int lane) {
-  const bf16* ab = static_cast<const bf16*>(a.R);
-  bf16* dab = static_cast<bf16*>(a.C);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m0 + wm * 128 + i * 16 + (lane & 15);
-    if (m >= a.M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int f = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
-      if (f >= a.N) continue;  // F % 4 == 0: the 4 columns are all inside
-      float av[4], bv[4], da[4], db[4];
-      load4<bf16>(ab + (int64_t)m * a.ldr + f, av);
-      load4<bf16>(ab + (int64_t)m * a.ldr + a.F + f, bv);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) swiglu_grad(av[r], bv[r], to_f32(from_f32<bf16>(acc[i][j][r])), da[r], db[r]);
-      store4<bf16>(dab + (int64_t)m * a.ldc + f, da);
-      store4<bf16>(dab + (int64_t)m * a.ldc + a.F + f, db);
     }
   }
 }
@@ -854,7 +835,6 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
   if constexpr (EPI == 1) w8_epilogue_swiglu_fwd(a, acc, c.m0, c.n0, wm, wn, lane);
-  else if constexpr (EPI == 2) w8_epilogue_swiglu_bwd(a, acc, c.m0, c.n0, wm, wn, lane);
   else dl_epilogue<TO, false, 8, 4>(a, acc, c.m0, c.n0, wm, wn, lane);
 }
 
@@ -1347,22 +1327,6 @@ slt_status launch_gemm_swiglu_fwd(int M, int F, int K, const void* X, int64_t ld
   ka.tiles = ((M + 255) / 256) * ka.tiles_n;
   gemm_w8_k<bf16, true, true, 1><<<ka.tiles, W8_NT, 0, s>>>(ka);
   return check_launch("fused SwiGLU projection");
-}
-
-slt_status launch_gemm_swiglu_bwd(int M, int F, int K, const void* dY, int64_t lddy, const void* W2,
-                                  const void* ab, int64_t ldab, void* dab, int64_t lddab, hipStream_t s) {
-  if (!(SLT_FUSED_SWIGLU && M > 0 && F >= 8 && F % 8 == 0 && K > 0 && K % DL_BK == 0 && al(dY, 16) && lddy % 8 == 0 && al(W2, 16) &&
-        al(ab, 8) && ldab % 4 == 0 && al(dab, 8) && lddab % 4 == 0 && w8_fits(M, F)))
-    return fail(SLT_EUNSUPPORTED, "fused SwiGLU backward: shape or alignment");
-  KArgs ka{};
-  ka.M = M; ka.N = F; ka.K = K;
-  ka.A = dY; ka.lda = lddy; ka.B = W2; ka.ldb = F;
-  ka.C = dab; ka.ldc = lddab; ka.R = ab; ka.ldr = ldab; ka.F = F;
-  ka.alpha = 1.f;
-  ka.tiles_n = (F + 255) / 256;
-  ka.tiles = ((M + 255) / 256) * ka.tiles_n;
-  gemm_w8_k<bf16, true, false, 2><<<ka.tiles, W8_NT, 0, s>>>(ka);
-  return check_launch("fused SwiGLU backward");
 }
 
 bool gemm_group_ok(const GroupItem& it, int K) {

@@ -611,10 +611,7 @@ __global__ __launch_bounds__(256) void gelu_fwd_k(const T* __restrict__ a, T* __
     float av[VEC], out[VEC];
     load_f<T, VEC>(a + r * lda + c, av);
 #pragma unroll
-    for (int q = 0; q < VEC; ++q) {
-      const float x = av[q];
-      out[q] = 0.5f * x * (1.0f + tanhf(kGeluK * (x + kGeluC * x * x * x)));
-    }
+    for (int q = 0; q < VEC; ++q) out[q] = gelu_tanh(av[q]);
     store_f<T, VEC>(u + r * ldu + c, out);
   }
 }

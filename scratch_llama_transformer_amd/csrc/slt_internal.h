@@ -43,6 +43,11 @@ __device__ __forceinline__ void swiglu_grad(float a, float b, float dh, float& d
   da = dh * b * sg * (1.0f + a * (1.0f - sg));
 }
 
+// GELU, tanh form (the GPT-2 / CodeGen family's).
+__device__ __forceinline__ float gelu_tanh(float x) {
+  return 0.5f * x * (1.0f + tanhf(0.7978845608028654f * (x + 0.044715f * x * x * x)));
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return bf16{f32_to_bf16_bits(x)}; }
@@ -111,11 +116,6 @@ slt_status launch_gemm(const GemmArgs& g, hipStream_t s);
 // SLT_EUNSUPPORTED (nothing enqueued) where the fused kernel does not apply.
 slt_status launch_gemm_swiglu_fwd(int M, int F, int K, const void* X, int64_t ldx, const void* W13, void* ab,
                                   int64_t ldab, void* h, int64_t ldh, hipStream_t s);
-// W2 activation gradient fused with the SwiGLU backward: dh = dY[M, K] W2[K, F]
-// rounded to bf16, then [da | db] (row stride lddab) from ab (row stride ldab).
-// SLT_EUNSUPPORTED (nothing enqueued) where the fused kernel does not apply.
-slt_status launch_gemm_swiglu_bwd(int M, int F, int K, const void* dY, int64_t lddy, const void* W2,
-                                  const void* ab, int64_t ldab, void* dab, int64_t lddab, hipStream_t s);
 
 // One product of a grouped weight-gradient launch: C[M, N] (fp32, row stride
 // ldc) = alpha sum_k A[k lda + m] B[k ldb + n] (+ C when accumulate), bf16

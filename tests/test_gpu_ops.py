@@ -189,15 +189,15 @@ def test_gemm_full_size_sampled_rows(B, shape):
 
 
 @pytest.mark.parametrize("M,F,C,dtype", [
-    (16384, 1024, 384, BF16),   # the d=384 MLP: one fused launch each way
+    (16384, 1024, 384, BF16),   # the d=384 MLP: the forward as one fused launch
     (12296, 1152, 256, BF16),   # fused, ragged M
     (1000, 512, 256, BF16),     # too small a grid: GEMM and element kernel
     (300, 96, 64, F32),         # fp32: GEMM and element kernel
 ])
 def test_mlp_swiglu_projection_fwd_bwd(B, M, F, C, dtype):
-    """[a | b] = x [W1; W3]^T with h = swiglu(a, b), and the backward
-    dh = dy W2 -> [da | db], whether they run as one fused launch (large bf16
-    grids) or as the GEMM plus the element kernel; sampled rows."""
+    """[a | b] = x [W1; W3]^T with h = swiglu(a, b), whether it runs as one
+    fused launch (large bf16 grids) or as the GEMM plus the element kernel,
+    and the backward dh = dy W2 -> [da | db]; sampled rows."""
     say("mlp swiglu", M, F, C, dtype)
     rng = np.random.default_rng(11)
     x = rnd(rng, (M, C), dtype)
@@ -226,9 +226,31 @@ def test_mlp_swiglu_projection_fwd_bwd(B, M, F, C, dtype):
     got = host(dab)[rows]
     check(got[:, :F], ref_round(da, dtype), act(dtype), "da")
     check(got[:, F:], ref_round(db, dtype), act(dtype), "db")
-    if M == 1000:  # an unfused shape needs the dh workspace
+    if M == 1000:  # the dh workspace is required
         with pytest.raises(B.SltError):
             B.slt_mlp_swiglu_bwd(M, F, C, dev(dy, dtype), dev(w2, dtype), dev(abin, dtype), dab, None, dtype)
+
+
+@pytest.mark.parametrize("M,N,K,col0,dtype", [
+    (16384, 7168, 1024, 3072, BF16),  # the parallel block's [q|k|v|fc_in]
+    (16380, 4100, 512, 1028, BF16),   # ragged M and N
+    (1000, 704, 256, 192, BF16),
+    (300, 160, 64, 48, F32),
+])
+def test_proj_gelu_fwd(B, M, N, K, col0, dtype):
+    """y = x W^T and u = gelu(y[:, col0:]); sampled rows."""
+    say("proj gelu", M, N, K, col0, dtype)
+    rng = np.random.default_rng(12)
+    x = rnd(rng, (M, K), dtype)
+    w = rnd(rng, (N, K), dtype, 0.05)
+    tdt = torch.bfloat16 if dtype == BF16 else torch.float32
+    y = torch.full((M, N), float("nan"), dtype=tdt, device="cuda")
+    u = torch.full((M, N - col0), float("nan"), dtype=tdt, device="cuda")
+    B.slt_proj_gelu_fwd(M, N, K, dev(x, dtype), dev(w, dtype), y, N, col0, u, N - col0, dtype)
+    rows = np.union1d(np.unique(rng.integers(0, M, 64)), [0, M - 1])
+    yr = ref_round(x[rows] @ w.T, dtype)
+    check(host(y)[rows], yr, act(dtype), "y")
+    check(host(u)[rows], ref_round(O.gelu_fwd(yr[:, col0:]), dtype), act(dtype), "u")
 
 
 # ---------------------------------------------------------------------------
