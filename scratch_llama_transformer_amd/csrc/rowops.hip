@@ -42,17 +42,6 @@ __device__ __forceinline__ void store_f(T* p, const float (&f)[VEC]) {
   *reinterpret_cast<Pack<T, VEC>*>(p) = pk;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
 
 inline bool aligned(const void* p, int bytes) {
   return p == nullptr || (reinterpret_cast<uintptr_t>(p) % bytes) == 0;

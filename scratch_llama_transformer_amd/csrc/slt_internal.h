@@ -31,6 +31,39 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(slt_f32x2{a, b}, slt_bf16x2));
 }
 
+// ---------------------------------------------------------------------------
+// Wavefront reductions (64 lanes) without LDS: DPP row_mirror, row_half_mirror
+// and two quad permutations sum each 16-lane row, v_permlane16_swap and
+// v_permlane32_swap (gfx950) then combine the four rows.  Every step adds a
+// value to its partner's with both orders giving the same float, so all 64
+// lanes end with bitwise the same result.  (A __shfl_xor ladder compiles to
+// six ds_bpermute LDS round trips.)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0x140>(v);  // row_mirror: lane i with 15 - i
+  v += dpp_mov<0x141>(v);  // row_half_mirror: lane i with 7 - i in each half row
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // SwiGLU (Hephaistos, "Architecture at a glance": silu(x W1) * (x W3)), shared
 // by the element kernels and the fused GEMM epilogues so both compute the
 // same expression: h = a sigmoid(a) b; db = dh a sigmoid(a),
