@@ -38,6 +38,8 @@ from __future__ import annotations
 import math
 import numpy as np
 
+from .dropout import dropout_multiplier
+
 __all__ = [
     "bf16_round", "store_fn",
     "embedding_fwd", "embedding_bwd",
@@ -422,7 +424,20 @@ def forward(cfg, params, tokens, jitter=0.0, seed=0):
     cos, sin = rope_tables(T, R, cfg.base)
     qd, kd = H * d, Hkv * d
 
+    # inverted dropout (training forward; Hephaistos, "Architecture at a
+    # glance"; randyGPT, "Architecture Details"): multipliers of sites 0
+    # (embedding output), 1 (attention projection / parallel block output) and
+    # 2 (MLP output), cached for the backward
+    p_drop = getattr(cfg, "dropout", 0.0)
+    seed_drop = getattr(cfg, "dropout_seed", 0)
+
+    def dmask(site, layer):
+        return dropout_multiplier(p_drop, seed_drop, site, layer, B * T, C) if p_drop > 0 else None
+
     x = embedding_fwd(W["wte"], X)
+    m_emb = dmask(0, 0)
+    if m_emb is not None:
+        x = S(x * m_emb)
     layers = []
     for l in range(cfg.L):
         p = f"h{l}."
@@ -443,19 +458,24 @@ def forward(cfg, params, tokens, jitter=0.0, seed=0):
         o4, lse = attention_fwd(q, k, v)
         o = S(_unheads(o4))
         c.update(n1=n1, r1=r1, q=q, k=k, v=v, o=o)
+        m1 = dmask(1, l)
+        c["m1"] = m1
+        drop1 = (lambda y: y) if m1 is None else (lambda y: y * m1)
         if cfg.block == "llama":
-            x = S(x + o @ W[p + "w_o"].T)
+            x = S(x + drop1(o @ W[p + "w_o"].T))
             c["x_mid"] = x
             n2, r2 = rmsnorm_fwd(x, W[p + "mlp_norm"], cfg.eps)
             n2 = S(n2)
             a = S(n2 @ W[p + "w1"].T)
             b = S(n2 @ W[p + "w3"].T)
             h = S(swiglu_fwd(a, b))
-            x = S(x + h @ W[p + "w2"].T)
-            c.update(n2=n2, r2=r2, a=a, b=b, h=h)
+            m2 = dmask(2, l)
+            y2 = h @ W[p + "w2"].T
+            x = S(x + (y2 if m2 is None else y2 * m2))
+            c.update(n2=n2, r2=r2, a=a, b=b, h=h, m2=m2)
         else:
             u = S(gelu_fwd(c["a"]))
-            x = S(x + np.concatenate([o, u], axis=1) @ W[p + "w_out"].T)
+            x = S(x + drop1(np.concatenate([o, u], axis=1) @ W[p + "w_out"].T))
             c["u"] = u
         layers.append(c)
     x_f = x
@@ -468,7 +488,7 @@ def forward(cfg, params, tokens, jitter=0.0, seed=0):
     z = S(nf @ W["lm_head"].T)
     loss, dz, lse_z = cross_entropy(z, Y)
     cache = dict(store=S, W=W, X=X, Y=Y, B=B, T=T, cos=cos, sin=sin, layers=layers,
-                 x_f=x_f, nf=nf, rf=rf, muf=muf, z=z, dz=dz, lse_z=lse_z)
+                 x_f=x_f, nf=nf, rf=rf, muf=muf, z=z, dz=dz, lse_z=lse_z, m_emb=m_emb)
     return loss, cache
 
 
@@ -497,9 +517,12 @@ def backward(cfg, cache):
     for l in reversed(range(cfg.L)):
         p = f"h{l}."
         c = cache["layers"][l]
+        # through dropout: the projection's output gradient is the incoming
+        # one times the mask (stored like any activation gradient)
         if cfg.block == "llama":
-            grads[p + "w2"] = dx.T @ c["h"]
-            dh = S(dx @ W[p + "w2"])
+            dy2 = dx if c.get("m2") is None else S(dx * c["m2"])
+            grads[p + "w2"] = dy2.T @ c["h"]
+            dh = S(dy2 @ W[p + "w2"])
             da, db = swiglu_bwd(c["a"], c["b"], dh)
             da, db = S(da), S(db)
             grads[p + "w1"] = da.T @ c["n2"]
@@ -507,12 +530,14 @@ def backward(cfg, cache):
             dn2 = S(da @ W[p + "w1"] + db @ W[p + "w3"])
             dxn, grads[p + "mlp_norm"] = rmsnorm_bwd(c["x_mid"], W[p + "mlp_norm"], c["r2"], dn2)
             dx = S(dx + dxn)
-            grads[p + "w_o"] = dx.T @ c["o"]
-            do = S(dx @ W[p + "w_o"])
+            dy1 = dx if c.get("m1") is None else S(dx * c["m1"])
+            grads[p + "w_o"] = dy1.T @ c["o"]
+            do = S(dy1 @ W[p + "w_o"])
         else:
             ou = np.concatenate([c["o"], c["u"]], axis=1)
-            grads[p + "w_out"] = dx.T @ ou
-            dou = S(dx @ W[p + "w_out"])
+            dy1 = dx if c.get("m1") is None else S(dx * c["m1"])
+            grads[p + "w_out"] = dy1.T @ ou
+            dou = S(dy1 @ W[p + "w_out"])
             do, du = dou[:, :C], dou[:, C:]
             da = S(gelu_bwd(c["a"], du))
         dq, dk, dv = attention_bwd(c["q"], c["k"], c["v"], _heads(do, B, T, H, d))
@@ -529,7 +554,8 @@ def backward(cfg, cache):
             dxn, grads[p + "ln_g"], grads[p + "ln_b"] = layernorm_bwd(
                 c["x_in"], W[p + "ln_g"], c["mu1"], c["r1"], dn1)
         dx = S(dx + dxn)
-    grads["wte"] = embedding_bwd(dx, cache["X"], cfg.V)
+    m_emb = cache.get("m_emb")
+    grads["wte"] = embedding_bwd(dx if m_emb is None else dx * m_emb, cache["X"], cfg.V)
     return grads
 
 

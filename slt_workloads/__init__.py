@@ -44,6 +44,8 @@ class Config:
     adam_eps: float = 1e-8
     wd: float = 0.1
     init_std: float = 0.02
+    dropout: float = 0.0      # inverted-dropout probability (training forward only); 0 = off
+    dropout_seed: int = 0     # key of the counter-based generator that draws the masks
 
     @property
     def d(self) -> int:

@@ -755,3 +755,82 @@ def test_cached_forward_rejects_overflowing_cache():
     O.forward_cached(cfg, params, cache, np.zeros((1, 3), int))
     with pytest.raises(ValueError):
         O.forward_cached(cfg, params, cache, np.zeros((1, 2), int))
+
+
+# --------------------------------------------------------------------------
+# Inverted dropout (Hephaistos, "Architecture at a glance", "Design notes";
+# randyGPT, "Architecture Details" and its default rate 0.1)
+# --------------------------------------------------------------------------
+def test_oracle_philox_published_vectors():
+    """The oracle's own Philox-4x32-10 against the known-answer vectors its
+    authors distribute with the generator."""
+    from oracle.dropout import philox4x32_10
+    cases = [
+        ((0, 0, 0, 0), (0, 0), (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+        ((0xffffffff,) * 4, (0xffffffff,) * 2, (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+        ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+         (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1)),
+    ]
+    for ctr, key, want in cases:
+        assert tuple(int(x) for x in philox4x32_10(ctr, key)) == want
+
+
+def test_dropout_masks_rate_scale_and_independence():
+    from oracle.dropout import dropout_multiplier
+    p, rows, C = 0.1, 512, 384
+    m = dropout_multiplier(p, 77, 1, 3, rows, C)
+    kept = m > 0
+    n = m.size
+    # keep rate within 5 sigma of 1 - p; kept elements carry float32(1/(1-p))
+    assert abs(kept.mean() - (1 - p)) < 5 * math.sqrt(p * (1 - p) / n)
+    assert np.all(m[kept] == float(np.float32(1 / 0.9)))
+    # inverted dropout preserves the mean: E[m] = (1-p) / (1-p)
+    assert abs(m.mean() - 1.0) < 5 * math.sqrt(p * (1 - p) / n) / (1 - p) + 1e-7
+    # other sites, layers and seeds draw other masks (agreement ~ p^2 + (1-p)^2)
+    for other in (dropout_multiplier(p, 77, 2, 3, rows, C), dropout_multiplier(p, 77, 1, 4, rows, C),
+                  dropout_multiplier(p, 78, 1, 3, rows, C)):
+        agree = ((other > 0) == kept).mean()
+        assert abs(agree - (p * p + (1 - p) ** 2)) < 0.01
+    # no rate: every element kept with factor 1
+    assert np.all(dropout_multiplier(0.0, 77, 1, 3, rows, C) == 1.0)
+
+
+def test_dropout_rate_zero_is_the_plain_step():
+    cfg = tiny()
+    params = rand_params(cfg, seed=3)
+    tokens = np.random.default_rng(4).integers(0, cfg.V, size=(cfg.B, cfg.T + 1))
+    l0, c0 = O.forward(cfg, params, tokens)
+    l1, c1 = O.forward(cfg.with_(dropout=0.0, dropout_seed=9), params, tokens)
+    assert l0 == l1
+    g0, g1 = O.backward(cfg, c0), O.backward(cfg, c1)
+    assert all(np.array_equal(g0[k], g1[k]) for k in g0)
+
+
+@pytest.mark.parametrize("block", ["llama", "parallel"])
+def test_dropout_gradcheck_every_tensor(block):
+    """With the masks fixed by the seed the loss is a smooth function of the
+    weights: the backward through every dropout site against f64 central
+    differences; a heavy rate so that every site drops elements."""
+    cfg = tiny(block=block).with_(dropout=0.3, dropout_seed=12345)
+    params = rand_params(cfg, seed=3)
+    tokens = np.random.default_rng(4).integers(0, cfg.V, size=(cfg.B, cfg.T + 1))
+    loss, cache = O.forward(cfg, params, tokens)
+    assert loss != O.forward(cfg.with_(dropout=0.0), params, tokens)[0]
+    grads = O.backward(cfg, cache)
+    rng = np.random.default_rng(5)
+    h = 1e-6
+    for name, p in params.items():
+        flat = p.reshape(-1)
+        idx = rng.choice(flat.size, size=min(5, flat.size), replace=False)
+        if name == "wte":
+            idx = np.concatenate([idx, tokens[0, :3] * cfg.C])
+        for i in idx:
+            old = flat[i]
+            flat[i] = old + h
+            lp, _ = O.forward(cfg, params, tokens)
+            flat[i] = old - h
+            lm, _ = O.forward(cfg, params, tokens)
+            flat[i] = old
+            num = (lp - lm) / (2 * h)
+            ana = grads[name].reshape(-1)[i]
+            assert abs(ana - num) / max(abs(ana), abs(num), 1e-4) < 1e-5, (name, i, ana, num)
