@@ -70,6 +70,18 @@ typedef struct {
   int32_t act;        /* slt_dtype of activations and of the compute copy of weights */
   float eps;          /* norm epsilon, added inside the square root (1e-5)          */
   float rope_base;    /* RoPE base (10000)                                           */
+  float dropout;      /* inverted-dropout probability p, 0 <= p < 1 (0: off); applied by
+                         the training forward (slt_forward_loss) to the embedding output
+                         and to each block's attention-projection and MLP outputs (the
+                         parallel block's one combined output) before the residual add,
+                         kept values scaled by float(1/(1-p)) (Hephaistos, "Architecture
+                         at a glance"; randyGPT, "Architecture Details").  Element e =
+                         row*C + column of a site's [B*T, C] tensor is kept iff word
+                         e mod 4 of Philox-4x32-10(counter (e/4 mod 2^32, e/4 div 2^32,
+                         site, layer), key (seed mod 2^32, seed div 2^32)) is at least
+                         floor(p 2^32); sites 0 = embedding, 1 = attention projection,
+                         2 = MLP.  slt_backward regenerates the same masks. */
+  uint64_t dropout_seed; /* key of the mask generator; change it per step for fresh masks */
 } slt_config;
 
 /* One tensor of the flat parameter buffer.  rows/cols describe a matrix
@@ -94,8 +106,8 @@ const char* slt_version(void);
  * ---------------------------------------------------------------------- */
 
 /* Checks a configuration: all sizes positive, C = H*d, H a multiple of Hkv,
- * R even and R <= d, rope_mode/block/act valid, C <= 4096.  SLT_EINVAL with a
- * message otherwise. */
+ * R even and R <= d, rope_mode/block/act valid, C <= 4096, 0 <= dropout < 1.
+ * SLT_EINVAL with a message otherwise. */
 slt_status slt_validate(const slt_config* cfg);
 
 /* Parameter layout (Hephaistos, "Design notes": flat buffer, (offset, len)).

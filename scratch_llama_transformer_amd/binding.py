@@ -31,7 +31,8 @@ class slt_config(ct.Structure):
     _fields_ = [("V", ct.c_int32), ("C", ct.c_int32), ("H", ct.c_int32), ("Hkv", ct.c_int32),
                 ("L", ct.c_int32), ("T", ct.c_int32), ("B", ct.c_int32), ("F", ct.c_int32),
                 ("R", ct.c_int32), ("rope_mode", ct.c_int32), ("block", ct.c_int32), ("act", ct.c_int32),
-                ("eps", ct.c_float), ("rope_base", ct.c_float)]
+                ("eps", ct.c_float), ("rope_base", ct.c_float), ("dropout", ct.c_float),
+                ("dropout_seed", ct.c_uint64)]
 
 
 class slt_tensor(ct.Structure):
@@ -144,7 +145,8 @@ def make_config(w) -> slt_config:
     return slt_config(V=w.V, C=w.C, H=w.H, Hkv=w.Hkv, L=w.L, T=w.T, B=w.B, F=w.F, R=w.R,
                       rope_mode=ROPE_HALF if w.rope_mode == "half" else ROPE_PAIRS,
                       block=BLOCK_LLAMA if w.block == "llama" else BLOCK_PARALLEL,
-                      act=BF16 if w.act == "bf16" else F32, eps=w.eps, rope_base=w.base)
+                      act=BF16 if w.act == "bf16" else F32, eps=w.eps, rope_base=w.base,
+                dropout=getattr(w, "dropout", 0.0), dropout_seed=getattr(w, "dropout_seed", 0))
 
 
 # ---------------------------------------------------------------------------

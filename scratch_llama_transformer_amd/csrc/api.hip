@@ -66,6 +66,7 @@ struct Plan {
   int64_t nf, rf, muf, z, cs, act_bytes;
   // scratch
   int64_t rowloss, dx, dx2, dbig, dqkv, dmid, dn, delta, normws, embws, gemmws, gemmws_bytes, scratch_bytes;
+  int64_t dy1 = -1, dy2 = -1;  // masked output gradients of the dropped projections (dropout on)
   int dbig_w, dmid_w;
 };
 
@@ -83,6 +84,7 @@ static slt_status validate(const slt_config* c) {
   if (c->act != SLT_F32 && c->act != SLT_BF16) return fail(SLT_EINVAL, "bad act dtype");
   if (c->C > 4096 || (c->C % 8 && c->C > 512)) return fail(SLT_EUNSUPPORTED, "C above 4096 (or above 512 unaligned)");
   if (!(c->eps >= 0.f) || !(c->rope_base > 0.f)) return fail(SLT_EINVAL, "eps must be >= 0 and rope_base > 0");
+  if (!(c->dropout >= 0.f && c->dropout < 1.f)) return fail(SLT_EINVAL, "dropout must satisfy 0 <= p < 1");
   const int64_t N = (int64_t)c->B * c->T;
   if (N > (1 << 30) || (int64_t)c->V * c->C > ((int64_t)1 << 40)) return fail(SLT_EUNSUPPORTED, "sizes too large");
   return SLT_OK;
@@ -211,6 +213,10 @@ static slt_status make_plan(const slt_config* cfg, Plan& p) {
   p.delta = takes(attention_bwd_ws(c.B, c.H, c.T));
   p.normws = takes(norm_bwd_ws(p.N, c.C));
   p.embws = takes(embedding_bwd_ws(N, c.V));
+  if (c.dropout > 0.f) {
+    p.dy1 = takes(N * C * es);
+    p.dy2 = p.llama ? takes(N * C * es) : -1;
+  }
   // split-K partials of the weight gradients
   p.gemmws_bytes = 64ll << 20;
   p.gemmws = takes(p.gemmws_bytes);
@@ -234,10 +240,28 @@ struct Ctx {
   const void* P(int64_t off) const { return params + off * p.es; }
 };
 
-// y[M, N] = x[M, K] W[N, K]^T (+ R)
+// Inverted dropout of one site of one layer (0: embedding output, 1:
+// attention projection output, 2: MLP output); off when p = 0.  A kept
+// element is scaled by 1/(1-p) rounded to fp32; the mask bit of element e
+// compares one Philox-4x32-10 word with floor(p 2^32) (drop_mult).
+static Drop make_drop(const slt_config& c, int site, int layer) {
+  Drop d;
+  if (!(c.dropout > 0.f)) return d;
+  d.on = true;
+  d.thr = (uint32_t)floor((double)c.dropout * 4294967296.0);
+  d.scale = (float)(1.0 / (1.0 - (double)c.dropout));
+  d.k0 = (uint32_t)c.dropout_seed;
+  d.k1 = (uint32_t)(c.dropout_seed >> 32);
+  d.site = site;
+  d.layer = layer;
+  return d;
+}
+
+// y[M, N] = drop(x[M, K] W[N, K]^T) (+ R)
 static slt_status proj(const Ctx& x, int M, int N, int K, const void* X, int64_t ldx, const void* W, void* Y,
-                       int64_t ldy, const void* R, int64_t ldr) {
+                       int64_t ldy, const void* R, int64_t ldr, Drop drop = {}) {
   GemmArgs g{M, N, K, X, ldx, true, W, (int64_t)K, true, Y, ldy, R, ldr, x.dt, x.dt, nullptr, 0};
+  g.drop = drop;
   return launch_gemm(g, x.s);
 }
 
@@ -340,7 +364,7 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
   const int64_t ldt = c.T + 1;
   float* cs = reinterpret_cast<float*>(x.A(p.cs));
   if (c.R > 0) SLT_TRY(launch_rope_table(c.T, c.R, c.rope_base, cs, x.s));
-  SLT_TRY(launch_embedding_fwd(tok, c.B, c.T, ldt, x.P(p.wte), x.A(p.xs[0]), c.V, C, x.dt, x.s));
+  SLT_TRY(launch_embedding_fwd(tok, c.B, c.T, ldt, x.P(p.wte), x.A(p.xs[0]), c.V, C, x.dt, x.s, make_drop(c, 0, 0)));
   for (int l = 0; l < c.L; ++l) {
     const LayerP& W = p.lp[l];
     const LayerA& A = p.la[l];
@@ -362,10 +386,10 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
       at.ldq = at.ldk = at.ldv = p.qkv_w;
       at.out = x.A(A.o); at.ldo = p.qd;
       SLT_TRY(launch_attention_fwd(at, x.s));
-      SLT_TRY(proj(x, N, C, p.qd, x.A(A.o), p.qd, x.P(W.wo), xmid, C, xin, C));
+      SLT_TRY(proj(x, N, C, p.qd, x.A(A.o), p.qd, x.P(W.wo), xmid, C, xin, C, make_drop(c, 1, l)));
       SLT_TRY(launch_rmsnorm_fwd(xmid, x.P(W.norm2), x.A(A.n2), (float*)x.A(A.r2), N, C, c.eps, x.dt, x.s));
       SLT_TRY(mlp_in(N, c.F, C, x.A(A.n2), x.P(W.w1), (char*)x.A(A.ab), x.A(A.h), x.dt, x.s));
-      SLT_TRY(proj(x, N, C, c.F, x.A(A.h), c.F, x.P(W.w2), xout, C, xmid, C));
+      SLT_TRY(proj(x, N, C, c.F, x.A(A.h), c.F, x.P(W.w2), xout, C, xmid, C, make_drop(c, 2, l)));
     } else {
       void* xin = x.A(p.xs[l]);
       void* xout = x.A(p.xs[l + 1]);
@@ -380,7 +404,7 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
       at.ldq = at.ldk = at.ldv = p.in_w;
       at.out = ou; at.ldo = p.ou_w;
       SLT_TRY(launch_attention_fwd(at, x.s));
-      SLT_TRY(proj(x, N, C, p.ou_w, ou, p.ou_w, x.P(W.wout), xout, C, xin, C));
+      SLT_TRY(proj(x, N, C, p.ou_w, ou, p.ou_w, x.P(W.wout), xout, C, xin, C, make_drop(c, 1, l)));
     }
   }
   void* xf = x.A(p.xs.back());
@@ -435,16 +459,26 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       // dx: gradient at x_out, kept until the layer's weight gradients;
       // dx2: gradient at x_mid; dbig: [da | db]; dqkv: [dq | dk | dv].
       char* dqkv = (char*)x.S(p.dqkv);
-      // x_out = x_mid + h W2^T
-      dws.add(N, C, c.F, dx, C, x.A(A.h), c.F, grads + W.w2, c.F);
-      SLT_TRY(mlp_in_bwd(N, c.F, C, dx, x.P(W.w2), (const char*)x.A(A.ab), dbig, dmid, x.dt, x.s));
+      // x_out = x_mid + drop(h W2^T): the product's gradient is dx times the mask
+      const void* dy2 = dx;
+      if (p.dy2 >= 0) {
+        SLT_TRY(launch_drop_apply(dx, x.S(p.dy2), N, C, x.dt, make_drop(c, 2, l), x.s));
+        dy2 = x.S(p.dy2);
+      }
+      dws.add(N, C, c.F, dy2, C, x.A(A.h), c.F, grads + W.w2, c.F);
+      SLT_TRY(mlp_in_bwd(N, c.F, C, dy2, x.P(W.w2), (const char*)x.A(A.ab), dbig, dmid, x.dt, x.s));
       dws.add(N, 2 * c.F, C, dbig, 2 * c.F, x.A(A.n2), C, grads + W.w1, C);
       SLT_TRY(proj_dx(x, N, 2 * c.F, C, dbig, 2 * c.F, x.P(W.w1), C, dn, C));
       SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l + 1]), x.P(W.norm2), (const float*)x.A(A.r2), dn, dx, dx2,
                                  grads + W.norm2, N, C, x.dt, nws, x.s, x.gw));
-      // x_mid = x_in + o W_o^T
-      dws.add(N, C, p.qd, dx2, C, x.A(A.o), p.qd, grads + W.wo, p.qd);
-      SLT_TRY(proj_dx(x, N, C, p.qd, dx2, C, x.P(W.wo), p.qd, dmid, p.qd));
+      // x_mid = x_in + drop(o W_o^T)
+      const void* dy1 = dx2;
+      if (p.dy1 >= 0) {
+        SLT_TRY(launch_drop_apply(dx2, x.S(p.dy1), N, C, x.dt, make_drop(c, 1, l), x.s));
+        dy1 = x.S(p.dy1);
+      }
+      dws.add(N, C, p.qd, dy1, C, x.A(A.o), p.qd, grads + W.wo, p.qd);
+      SLT_TRY(proj_dx(x, N, C, p.qd, dy1, C, x.P(W.wo), p.qd, dmid, p.qd));
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
       at.ldq = at.ldk = at.ldv = p.qkv_w;
       at.o = x.A(A.o); at.ldo = p.qd;
@@ -459,9 +493,14 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
                                  grads + W.norm1, N, C, x.dt, nws, x.s, x.gw));
     } else {
       char* ou = (char*)x.A(A.o);
-      // x_out = x_in + [o | u] W_out^T
-      dws.add(N, C, p.ou_w, dx, C, ou, p.ou_w, grads + W.wout, p.ou_w);
-      SLT_TRY(proj_dx(x, N, C, p.ou_w, dx, C, x.P(W.wout), p.ou_w, dmid, p.ou_w));
+      // x_out = x_in + drop([o | u] W_out^T)
+      const void* dy1 = dx;
+      if (p.dy1 >= 0) {
+        SLT_TRY(launch_drop_apply(dx, x.S(p.dy1), N, C, x.dt, make_drop(c, 1, l), x.s));
+        dy1 = x.S(p.dy1);
+      }
+      dws.add(N, C, p.ou_w, dy1, C, ou, p.ou_w, grads + W.wout, p.ou_w);
+      SLT_TRY(proj_dx(x, N, C, p.ou_w, dy1, C, x.P(W.wout), p.ou_w, dmid, p.ou_w));
       SLT_TRY(launch_gelu_bwd(qkv + p.qkv_w * p.es, dmid + p.qd * p.es, dbig + p.qkv_w * p.es, N, c.F, p.in_w,
                               p.ou_w, p.in_w, x.dt, x.s));
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
@@ -478,7 +517,8 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
                                    dn, dx, dx, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws, x.s, x.gw));
     }
   }
-  SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, dx, grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s, x.gw));
+  SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, dx, grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s, x.gw,
+                               make_drop(c, 0, 0)));
   return SLT_OK;
 }
 

@@ -206,6 +206,7 @@ struct KArgs {
   void* C2;           // fused SwiGLU epilogues: h (forward)
   int64_t ldc2;
   int F;              // fused SwiGLU epilogues: MLP width (b at column F + f)
+  Drop drop;          // C = drop(alpha A B) + R, element (m, n) = e m N + n
 };
 
 template <typename TO>
@@ -314,6 +315,12 @@ __global__ __launch_bounds__(NT) void gemm_k(KArgs a) {
         const TO* res = a.R ? static_cast<const TO*>(a.R) + (int64_t)m * a.ldr + n : nullptr;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] *= a.alpha;
+        if (a.drop.on) {
+          float dm[4];
+          drop_mults<4>(a.drop, (uint64_t)m * a.N + n, dm);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] *= dm[r];
+        }
         if (a.evec && n + 3 < a.N) {
           if (res) {
             float rv[4];
@@ -602,6 +609,12 @@ __device__ __forceinline__ void dl_epilogue(const KArgs& a, const f32x4 (&acc)[F
       const TO* res = a.R ? static_cast<const TO*>(a.R) + (int64_t)m * a.ldr + n : nullptr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] *= a.alpha;
+      if (a.drop.on) {
+        float dm[4];
+        drop_mults<4>(a.drop, (uint64_t)m * a.N + n, dm);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] *= dm[r];
+      }
       if (a.evec && n + 3 < a.N) {
         if (res) {
           float rv[4];
@@ -1182,6 +1195,7 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
   ka.A = g.A; ka.lda = g.lda; ka.B = g.B; ka.ldb = g.ldb;
   ka.C = g.C; ka.ldc = g.ldc; ka.R = g.R; ka.ldr = g.ldr;
   ka.alpha = g.alpha;
+  ka.drop = g.drop;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   ka.tiles_n = tiles_n;
   const int tiles = tiles_m * tiles_n;
@@ -1197,7 +1211,7 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
   // Split K when the output grid cannot fill the 256 compute units and K is
   // long; the partials must fit the workspace.
   int splits = 1;
-  if (g.workspace && tiles < 256) {
+  if (g.workspace && tiles < 256 && !g.drop.on) {
     const int kt = (g.K + BK - 1) / BK;
     int want = std::min((SLT_SPLIT_TARGET + tiles - 1) / tiles, kt / SLT_SPLIT_MINK);
     const int64_t per = (int64_t)g.M * g.N * 4;

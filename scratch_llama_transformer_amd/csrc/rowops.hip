@@ -56,7 +56,7 @@ inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 template <typename T, int VEC>
 __global__ __launch_bounds__(256) void embedding_fwd_k(const int32_t* __restrict__ tok, int T_, int64_t ld,
                                                        const T* __restrict__ wte, T* __restrict__ x, int N,
-                                                       int V, int C) {
+                                                       int V, int C, Drop drop) {
   const int cv = C / VEC;
   const int64_t total = (int64_t)N * cv;
   for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
@@ -70,6 +70,12 @@ __global__ __launch_bounds__(256) void embedding_fwd_k(const int32_t* __restrict
     } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) f[e] = __builtin_nanf("");
+    }
+    if (drop.on) {  // inverted dropout of the embedding output (site 0)
+      float m[VEC];
+      drop_mults<VEC>(drop, (uint64_t)i * C + c, m);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) f[e] *= m[e];
     }
     store_f<T, VEC>(x + (int64_t)i * C + c, f);
   }
@@ -204,7 +210,7 @@ __global__ void emb_scatter_k(const int32_t* __restrict__ tok, int T_, int64_t l
 template <typename T, int VEC>
 __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict__ tok, int T_, int64_t ld,
                                                       const T* __restrict__ dx, float* __restrict__ dwte,
-                                                      int N, int V_, int C, EmbWs w, GradW gw) {
+                                                      int N, int V_, int C, EmbWs w, GradW gw, Drop drop) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int tile = blockIdx.x * 4 + wave;
   const int s = tile * kEmbTile;
@@ -226,6 +232,12 @@ __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict_
       if (s + k < e) {
         float f[VEC];
         load_f<T, VEC>(dx + (int64_t)pos[k] * C + c0, f);
+        if (drop.on) {  // the embedding output's dropout mask (site 0), regenerated
+          float m[VEC];
+          drop_mults<VEC>(drop, (uint64_t)pos[k] * C + c0, m);
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) f[q] *= m[q];
+        }
 #pragma unroll
         for (int q = 0; q < VEC; ++q) acc[q] += f[q];
         const bool last = (k == kEmbTile - 1) || (s + k + 1 >= e) || (ids[k + 1] != ids[k]);
@@ -845,29 +857,6 @@ __global__ void rope_table_k(int T_, int R, double base, float* cs) {
 
 }  // namespace
 
-// ---------------------------------------------------------------------------
-// Philox-4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
-// easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64 multiplies with the
-// key bumped by the Weyl constants between rounds.
-// ---------------------------------------------------------------------------
-__host__ __device__ inline void philox4x32_10(const uint32_t in[4], const uint32_t key_in[2], uint32_t out[4]) {
-  uint32_t c0 = in[0], c1 = in[1], c2 = in[2], c3 = in[3];
-  uint32_t k0 = key_in[0], k1 = key_in[1];
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
-    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
-    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    c0 = hi1 ^ c1 ^ k0;
-    c1 = lo1;
-    c2 = hi0 ^ c3 ^ k1;
-    c3 = lo0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
-  }
-  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
-}
-
 namespace {
 // kind 0: N(0, std^2) by Box-Muller on the first two Philox outputs of
 // counter (index, 0, 0, 0); kind 1: constant std (used for ones and zeros).
@@ -905,16 +894,17 @@ template <typename T>
 static constexpr int full_vec() { return 16 / (int)sizeof(T); }
 
 slt_status launch_embedding_fwd(const int32_t* tok, int B, int T_, int64_t ld, const void* wte, void* x, int V,
-                                int C, int dtype, hipStream_t s) {
+                                int C, int dtype, hipStream_t s, Drop drop) {
   const int N = B * T_;
   auto go = [&](auto tag) {
     using T = decltype(tag);
     constexpr int VEC = full_vec<T>();
     if (C % VEC == 0 && aligned(wte, 16) && aligned(x, 16))
       embedding_fwd_k<T, VEC><<<grid_for((int64_t)N * C / VEC), 256, 0, s>>>(
-          tok, T_, ld, (const T*)wte, (T*)x, N, V, C);
+          tok, T_, ld, (const T*)wte, (T*)x, N, V, C, drop);
     else
-      embedding_fwd_k<T, 1><<<grid_for((int64_t)N * C), 256, 0, s>>>(tok, T_, ld, (const T*)wte, (T*)x, N, V, C);
+      embedding_fwd_k<T, 1><<<grid_for((int64_t)N * C), 256, 0, s>>>(tok, T_, ld, (const T*)wte, (T*)x, N, V, C,
+                                                                     drop);
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
   return check_launch("embedding_fwd");
@@ -926,7 +916,7 @@ int64_t embedding_bwd_ws(int64_t N, int V) {
 }
 
 slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, const void* dx, float* dwte, int V,
-                                int C, int dtype, void* ws, hipStream_t s, GradW gw) {
+                                int C, int dtype, void* ws, hipStream_t s, GradW gw, Drop drop) {
   const int N = B * T_;
   EmbWs w = emb_ws_layout(ws, N, V, 4096);
   const int nchunk = cdiv(N, kEmbChunk);
@@ -940,13 +930,47 @@ slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, c
     using T = decltype(tag);
     constexpr int VEC = full_vec<T>();
     if (C % VEC == 0 && aligned(dx, 16))
-      emb_tile_sum_k<T, VEC><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w, gw);
+      emb_tile_sum_k<T, VEC><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w, gw, drop);
     else
-      emb_tile_sum_k<T, 1><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w, gw);
+      emb_tile_sum_k<T, 1><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w, gw, drop);
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
   emb_row_finish_k<<<V, 256, 0, s>>>(dwte, V, C, w, gw);
   return check_launch("embedding_bwd");
+}
+
+// out[r, c] = g[r, c] * (dropout multiplier of element r C + c): the
+// gradient of a dropped site's pre-dropout value (stored in the activation
+// type, as the GEMMs that consume it read it).
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void drop_apply_k(const T* __restrict__ g, T* __restrict__ out, int rows, int C,
+                                                    Drop drop) {
+  const int cv = C / VEC;
+  const int64_t total = (int64_t)rows * cv;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / cv;
+    const int c = (int)(idx % cv) * VEC;
+    float f[VEC], m[VEC];
+    load_f<T, VEC>(g + r * C + c, f);
+    drop_mults<VEC>(drop, (uint64_t)r * C + c, m);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) f[q] *= m[q];
+    store_f<T, VEC>(out + r * C + c, f);
+  }
+}
+
+slt_status launch_drop_apply(const void* g, void* out, int rows, int C, int dtype, Drop drop, hipStream_t s) {
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    constexpr int VEC = full_vec<T>();
+    if (C % VEC == 0 && aligned(g, 16) && aligned(out, 16))
+      drop_apply_k<T, VEC><<<grid_for((int64_t)rows * C / VEC), 256, 0, s>>>((const T*)g, (T*)out, rows, C, drop);
+    else
+      drop_apply_k<T, 1><<<grid_for((int64_t)rows * C), 256, 0, s>>>((const T*)g, (T*)out, rows, C, drop);
+  };
+  if (dtype == SLT_BF16) go(bf16{}); else go(float{});
+  return check_launch("dropout (backward)");
 }
 
 // Picks VEC (16-byte groups when C allows) and NCH = groups per lane.

@@ -64,6 +64,74 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// ---------------------------------------------------------------------------
+// Philox-4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64 multiplies with the
+// key bumped by the Weyl constants between rounds.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline void philox4x32_10(const uint32_t in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  uint32_t c0 = in[0], c1 = in[1], c2 = in[2], c3 = in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+// Inverted dropout of one site (Hephaistos, "Architecture at a glance";
+// randyGPT, "Architecture Details"): element e of the site's [rows, C] tensor
+// (e = row C + column) is kept iff word e % 4 of Philox-4x32-10 at counter
+// (e / 4 low, e / 4 high, site, layer) under the seed is >= thr = floor(p
+// 2^32); a kept value is multiplied by scale = float(1 / (1 - p)).  The
+// backward regenerates the same words.
+struct Drop {
+  bool on = false;
+  uint32_t thr = 0, k0 = 0, k1 = 0;
+  int site = 0, layer = 0;
+  float scale = 1.f;
+};
+
+// Multiplier (0 or scale) of element e.
+__device__ __forceinline__ float drop_mult(const Drop& d, uint64_t e) {
+  const uint64_t q = e >> 2;
+  const uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), (uint32_t)d.site, (uint32_t)d.layer};
+  const uint32_t key[2] = {d.k0, d.k1};
+  uint32_t w[4];
+  philox4x32_10(ctr, key, w);
+  const uint32_t r = (e & 3) == 0 ? w[0] : (e & 3) == 1 ? w[1] : (e & 3) == 2 ? w[2] : w[3];
+  return r >= d.thr ? d.scale : 0.f;
+}
+
+// Multipliers of elements e0 .. e0 + N - 1 (one generator call per aligned
+// group of four).
+template <int N>
+__device__ __forceinline__ void drop_mults(const Drop& d, uint64_t e0, float (&m)[N]) {
+  if ((e0 & 3) == 0 && N % 4 == 0) {
+#pragma unroll
+    for (int g = 0; g < N / 4; ++g) {
+      const uint64_t q = (e0 >> 2) + g;
+      const uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), (uint32_t)d.site, (uint32_t)d.layer};
+      const uint32_t key[2] = {d.k0, d.k1};
+      uint32_t w[4];
+      philox4x32_10(ctr, key, w);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[4 * g + r] = w[r] >= d.thr ? d.scale : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < N; ++r) m[r] = drop_mult(d, e0 + r);
+  }
+}
+
 // SwiGLU (Hephaistos, "Architecture at a glance": silu(x W1) * (x W3)), shared
 // by the element kernels and the fused GEMM epilogues so both compute the
 // same expression: h = a sigmoid(a) b; db = dh a sigmoid(a),
@@ -134,6 +202,7 @@ struct GemmArgs {
   int in_dtype, out_dtype;
   float* workspace; int64_t workspace_bytes;
   float alpha = 1.0f;  // C = alpha A B (+ R)
+  Drop drop{};         // C = drop(alpha A B) + R: element (m, n) is e = m N + n of the site
 };
 
 // How a parameter-gradient kernel writes its result g: out = alpha g, or
@@ -165,10 +234,12 @@ bool gemm_group_ok(const GroupItem& it, int K);
 slt_status launch_gemm_group(const GroupItem* items, int n, int K, float* ws, int64_t ws_bytes, hipStream_t s);
 
 slt_status launch_embedding_fwd(const int32_t* tok, int B, int T, int64_t ld, const void* wte,
-                                void* x, int V, int C, int dtype, hipStream_t s);
+                                void* x, int V, int C, int dtype, hipStream_t s, Drop drop = {});
 int64_t embedding_bwd_ws(int64_t N, int V);
 slt_status launch_embedding_bwd(const int32_t* tok, int B, int T, int64_t ld, const void* dx,
-                                float* dwte, int V, int C, int dtype, void* ws, hipStream_t s, GradW gw = {});
+                                float* dwte, int V, int C, int dtype, void* ws, hipStream_t s, GradW gw = {},
+                                Drop drop = {});
+slt_status launch_drop_apply(const void* g, void* out, int rows, int C, int dtype, Drop drop, hipStream_t s);
 int64_t norm_bwd_ws(int rows, int C);
 slt_status launch_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd, int rows, int C,
                               float eps, int dtype, hipStream_t s);

@@ -90,10 +90,18 @@ class TrainStep:
                          w.lr if lr is None else lr, w.beta1, w.beta2, w.adam_eps, w.wd if wd is None else wd,
                          grad_scale=scale)
 
+    def next_masks(self) -> None:
+        """Moves the dropout key to the next value, so that the following
+        forward draws fresh masks (a forward and its backward must share one
+        key: the backward regenerates the forward's masks from it)."""
+        self.cfg.dropout_seed = (self.cfg.dropout_seed + 1) & 0xFFFFFFFFFFFFFFFF
+
     def step(self, tokens: torch.Tensor) -> None:
         self.forward(tokens)
         self.backward(tokens)
         self.adamw()
+        if self.cfg.dropout > 0:
+            self.next_masks()
 
     def accumulate(self, micro_tokens) -> float:
         """Gradient of the mean loss over several equal micro-batches, each run
@@ -108,6 +116,8 @@ class TrainStep:
             total += self.loss
             B.slt_backward_accumulate(self.cfg, self.compute_params, tok, self.acts, self.scratch, self.grads,
                                       1.0 / S)
+            if self.cfg.dropout > 0:
+                self.next_masks()
         return float(total.item()) / S
 
 

@@ -63,6 +63,7 @@ def test_layout_matches_workload_tensors(i):
 @pytest.mark.parametrize("bad,code", [
     (dict(H=3), 1), (dict(Hkv=3), 1), (dict(R=5), 1), (dict(R=64), 1), (dict(V=0), 1),
     (dict(rope_mode=7), 1), (dict(block=2), 1), (dict(act=5), 1), (dict(C=2048, H=16), 2),
+    (dict(dropout=1.0), 1), (dict(dropout=-0.25), 1), (dict(dropout=float("nan")), 1),
 ])
 def test_validation_rejects(bad, code):
     from scratch_llama_transformer_amd import binding as B

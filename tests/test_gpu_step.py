@@ -113,6 +113,68 @@ def test_full_batch_step_one_layer(TS):
                                 f"weight {name}", w.adam_eps)
 
 
+# (config index, batch, layers, dropout p): p exactly representable in binary32,
+# the library's type for it, so both sides draw the same threshold and scale.
+DROPOUT_CASES = [(1, None, None, 0.25), (2, 8, None, 0.125), (3, 8, None, 0.125), (5, 1, 2, 0.25)]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ci,Bn,L,pdrop", DROPOUT_CASES)
+def test_full_step_with_dropout(TS, ci, Bn, L, pdrop):
+    """Inverted dropout at the embedding output, the attention projection
+    (the parallel block's combined projection) and the MLP output: the GPU's
+    masks are regenerated from the same Philox counters as the oracle's, so
+    loss, gradients and post-AdamW weights meet the same bars as without
+    dropout."""
+    w = W.get_config(ci)
+    w = w.with_(B=Bn or w.B, L=L or w.L, dropout=pdrop, dropout_seed=0x1234_5678_9ABC + ci)
+    say("dropout step", w)
+    params, tokens, ts, loss = run_step(TS, w, 1500 + ci)
+    ref = O.train_step(w, params, tokens)
+    plain = O.train_step(w.with_(dropout=0.0), params, tokens)
+    gd = math.sqrt(sum(float(np.sum((ref["grads"][k] - plain["grads"][k]) ** 2)) for k in params))
+    gn = math.sqrt(sum(float(np.sum(plain["grads"][k] ** 2)) for k in params))
+    assert gd > 0.1 * gn, (gd, gn)      # the masks change the gradient
+    assert abs(loss - ref["loss"]) <= LOSS_TOL[w.act] * abs(ref["loss"]), (loss, ref["loss"])
+    grads = ts.unpack(ts.grads)
+    new = ts.unpack(ts.master)
+    if w.act == "f32":
+        for name in params:
+            check(grads[name], ref["grads"][name], w.act, f"grad {name}")
+            check_weights(new[name], ref["params"][name], ref["grads"][name], w.act, f"weight {name}")
+    else:
+        _, ccache = O.forward(w, params, tokens, jitter=2.0 ** -24, seed=1)
+        comp = O.backward(w, ccache)
+        for name in params:
+            check_bf16_step_tensor(grads[name], ref["grads"][name], comp[name], f"grad {name}")
+            check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
+                                    f"weight {name}", w.adam_eps)
+    print(f"[result] {w.name} p={pdrop} loss gpu {loss:.7f} oracle {ref['loss']:.7f} (no dropout "
+          f"{plain['loss']:.7f}); gradient change {gd / gn:.2f} of its norm")
+
+
+def test_dropout_key_advances_per_step(TS):
+    """step() moves to the next key after its backward: a second forward on
+    the same weights and tokens draws other masks (another loss), and going
+    back to the first key reproduces the first loss bit for bit."""
+    w = W.get_config(1).with_(dropout=0.25, dropout_seed=77)
+    params = W.make_params(w, 1600)
+    tok = torch.from_numpy(W.make_tokens(w, 1600)).cuda()
+    ts = TS(w, params=params)
+    ts.forward(tok)
+    first = float(ts.loss.item())
+    ts.next_masks()
+    assert ts.cfg.dropout_seed == 78
+    ts.forward(tok)
+    second = float(ts.loss.item())
+    ts.cfg.dropout_seed = 77
+    ts.forward(tok)
+    again = float(ts.loss.item())
+    assert second != first and again == first, (first, second, again)
+    ts.step(tok)
+    assert ts.cfg.dropout_seed == 78
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("ci,Bn,kind", [(1, None, "l2"), (2, 8, "linf"), (3, 8, "l2")])
 def test_full_step_with_gradient_clipping(TS, ci, Bn, kind):
