@@ -92,9 +92,9 @@ def time_block(fn, reps, torch):
     return a.elapsed_time(b) / 1e3 / reps
 
 
-def kernel_classes(w, ts, torch, reps):
+def kernel_classes(w, ts, torch, reps, only=None):
     """Per-class time of one step, each class re-run through the C ABI with
-    the step's shapes on fresh buffers."""
+    the step's shapes on fresh buffers (``only``: just that GEMM class)."""
     from scratch_llama_transformer_amd import binding as B
     dt = B.BF16 if w.act == "bf16" else B.F32
     tdt = torch.bfloat16 if dt == B.BF16 else torch.float32
@@ -103,6 +103,8 @@ def kernel_classes(w, ts, torch, reps):
     out = {}
     ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
     for cls, launches in shapes(w).items():
+        if only is not None and cls != only:
+            continue
         bufs = []
         for (M, N, K, res) in launches:
             if cls == "gemm_fwd":
@@ -144,6 +146,8 @@ def kernel_classes(w, ts, torch, reps):
                     "frac_of_peak": flops / sec / 1e12 / peak, "flops": flops, "avg_launch_us": sec * 1e6 / len(launches),
                     "bound": "mfma", "peak": peak}
         del bufs
+    if only is not None:
+        return out
     # attention: forward, and backward (dQ then dK/dV) on the step's strides
     d = w.C // w.H
     qd, kd = w.H * d, w.Hkv * d
@@ -255,6 +259,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--only-class", choices=["gemm_fwd", "gemm_dx", "gemm_dw"], default=None,
+                    help="only time one GEMM class of the breakdown (for hardware-counter runs) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (for scaling HBM byte counters) and exit")
     args = ap.parse_args()
@@ -279,6 +285,12 @@ def main():
         return
 
     w = W.get_config(args.config)
+    if args.only_class:
+        cl = kernel_classes(w, None, torch, args.kernel_reps, only=args.only_class)[args.only_class]
+        print(json.dumps({"workload": w.name, "class": args.only_class, "launches": cl["launches"],
+                          "avg_launch_us": round(cl["avg_launch_us"], 2), "tflops": round(cl["tflops"], 2)}),
+              flush=True)
+        return
     ts = TrainStep(w, seed=1000 + args.config)
     tok = torch.from_numpy(W.make_tokens(w, 1000 + args.config)).cuda()
     for _ in range(args.warmup):
