@@ -15,8 +15,11 @@ Sources (page title, section):
 Readings (the pages name the sites and the rate, nothing more):
   * Sites built: 0 = the embedding output, 1 = the attention projection's
     output (the parallel block: its one combined attention + MLP projection),
-    2 = the MLP output (Llama block), each before its residual add.  Dropout
-    on the attention weights is not part of this build.
+    2 = the MLP output (Llama block), each before its residual add, and 3 =
+    the attention weights: the softmax probabilities p_ij of head h of
+    sequence b are multiplied by the mask of element ((b H + h) T + i) T + j
+    of a [B H T, T] tensor before they weight the values (the softmax
+    normaliser is taken before dropout).
   * Inverted dropout: a kept element is multiplied by 1/(1-p) (that factor
     rounded once to float32, as the GPU applies it), a dropped one is 0.
   * Masks come from Philox-4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel

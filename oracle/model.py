@@ -232,10 +232,12 @@ def _causal_scores(q, k):
     return np.where(mask, s, -np.inf)
 
 
-def attention_fwd(q, k, v):
+def attention_fwd(q, k, v, drop=None):
     """q [B,H,T,d], k and v [B,Hkv,T,d] (already rotated).
     s_ij = q_i . k_j / sqrt(d) for j <= i; p_i = softmax(s_i) computed after
-    subtracting the row maximum; o_i = sum_j p_ij v_j.
+    subtracting the row maximum; o_i = sum_j p_ij m_ij v_j, where m is the
+    attention-weight dropout multiplier [B,H,T,T] (Hephaistos, "Architecture
+    at a glance": dropout on the attention weights; m = 1 without dropout).
     Returns (o [B,H,T,d], lse [B,H,T] = log sum_j exp(s_ij))."""
     q = np.asarray(q, np.float64)
     s = _causal_scores(q, np.asarray(k, np.float64))
@@ -243,15 +245,18 @@ def attention_fwd(q, k, v):
     e = np.exp(s - mx)
     den = np.sum(e, axis=-1, keepdims=True)
     p = e / den
+    if drop is not None:
+        p = p * drop
     o = np.matmul(p, _expand_kv(np.asarray(v, np.float64), q.shape[1]))
     return o, (mx + np.log(den))[..., 0]
 
 
-def attention_bwd(q, k, v, do):
-    """Backward of attention_fwd, recomputing p.  dp_ij = do_i . v_j;
+def attention_bwd(q, k, v, do, drop=None):
+    """Backward of attention_fwd, recomputing p.  With the dropout multiplier
+    m (ones without dropout): dp_ij = m_ij (do_i . v_j);
     ds_ij = p_ij (dp_ij - sum_l p_il dp_il); dq_i = sum_j ds_ij k_j / sqrt(d);
-    dk_j = sum_i ds_ij q_i / sqrt(d); dv_j = sum_i p_ij do_i.  dk and dv of a
-    KV head sum over the query heads that read it.  Returns (dq, dk, dv)."""
+    dk_j = sum_i ds_ij q_i / sqrt(d); dv_j = sum_i p_ij m_ij do_i.  dk and dv
+    of a KV head sum over the query heads that read it.  Returns (dq, dk, dv)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -264,11 +269,15 @@ def attention_bwd(q, k, v, do):
     p = e / np.sum(e, axis=-1, keepdims=True)
     ke, ve = _expand_kv(k, H), _expand_kv(v, H)
     dp = np.matmul(do, np.swapaxes(ve, -1, -2))
+    pm = p
+    if drop is not None:
+        dp = dp * drop
+        pm = p * drop
     ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
     scale = 1.0 / math.sqrt(d)
     dq = np.matmul(ds, ke) * scale
     dke = np.matmul(np.swapaxes(ds, -1, -2), q) * scale
-    dve = np.matmul(np.swapaxes(p, -1, -2), do)
+    dve = np.matmul(np.swapaxes(pm, -1, -2), do)
     rep = H // Hkv
     dk = dke.reshape(B, Hkv, rep, T, d).sum(axis=2)
     dv = dve.reshape(B, Hkv, rep, T, d).sum(axis=2)
@@ -426,8 +435,9 @@ def forward(cfg, params, tokens, jitter=0.0, seed=0):
 
     # inverted dropout (training forward; Hephaistos, "Architecture at a
     # glance"; randyGPT, "Architecture Details"): multipliers of sites 0
-    # (embedding output), 1 (attention projection / parallel block output) and
-    # 2 (MLP output), cached for the backward
+    # (embedding output), 1 (attention projection / parallel block output),
+    # 2 (MLP output) and 3 (attention weights, [B, H, T, T] with element
+    # ((b H + h) T + i) T + j), cached for the backward
     p_drop = getattr(cfg, "dropout", 0.0)
     seed_drop = getattr(cfg, "dropout_seed", 0)
 
@@ -455,9 +465,10 @@ def forward(cfg, params, tokens, jitter=0.0, seed=0):
         q = rope_apply(_heads(qkv[:, :qd], B, T, H, d), cos, sin, R, cfg.rope_mode)
         k = rope_apply(_heads(qkv[:, qd:qd + kd], B, T, Hkv, d), cos, sin, R, cfg.rope_mode)
         v = _heads(qkv[:, qd + kd:], B, T, Hkv, d)
-        o4, lse = attention_fwd(q, k, v)
+        ma = None if p_drop <= 0 else dropout_multiplier(p_drop, seed_drop, 3, l, B * H * T, T).reshape(B, H, T, T)
+        o4, lse = attention_fwd(q, k, v, ma)
         o = S(_unheads(o4))
-        c.update(n1=n1, r1=r1, q=q, k=k, v=v, o=o)
+        c.update(n1=n1, r1=r1, q=q, k=k, v=v, o=o, ma=ma)
         m1 = dmask(1, l)
         c["m1"] = m1
         drop1 = (lambda y: y) if m1 is None else (lambda y: y * m1)
@@ -540,7 +551,7 @@ def backward(cfg, cache):
             dou = S(dy1 @ W[p + "w_out"])
             do, du = dou[:, :C], dou[:, C:]
             da = S(gelu_bwd(c["a"], du))
-        dq, dk, dv = attention_bwd(c["q"], c["k"], c["v"], _heads(do, B, T, H, d))
+        dq, dk, dv = attention_bwd(c["q"], c["k"], c["v"], _heads(do, B, T, H, d), c.get("ma"))
         dq = rope_apply(dq, cos, sin, R, cfg.rope_mode, inverse=True)
         dk = rope_apply(dk, cos, sin, R, cfg.rope_mode, inverse=True)
         dqkv = S(np.concatenate([_unheads(dq), _unheads(dk), _unheads(dv)], axis=1))

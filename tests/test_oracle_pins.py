@@ -834,3 +834,40 @@ def test_dropout_gradcheck_every_tensor(block):
             num = (lp - lm) / (2 * h)
             ana = grads[name].reshape(-1)[i]
             assert abs(ana - num) / max(abs(ana), abs(num), 1e-4) < 1e-5, (name, i, ana, num)
+
+
+def test_attention_weight_dropout_gradcheck():
+    """Attention with a dropout mask on its weights (site 3): the backward's
+    dq, dk, dv (GQA: two query heads per KV head) against f64 central
+    differences of L = sum(o * g), and D_i = sum_j p_ij dp_ij equal to
+    do_i . o_i with the mask applied (the identity the kernels use)."""
+    from oracle.dropout import dropout_multiplier
+    rng = np.random.default_rng(21)
+    B, H, Hkv, T, d = 2, 4, 2, 7, 4
+    q = rng.standard_normal((B, H, T, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    g = rng.standard_normal((B, H, T, d))
+    m = dropout_multiplier(0.4, 99, 3, 1, B * H * T, T).reshape(B, H, T, T)
+    assert (m == 0).any() and (m > 0).any()
+    o, _ = O.attention_fwd(q, k, v, m)
+    assert not np.allclose(o, O.attention_fwd(q, k, v)[0])
+    dq, dk, dv = O.attention_bwd(q, k, v, g, m)
+    h = 1e-6
+    for x, dx in ((q, dq), (k, dk), (v, dv)):
+        for idx in [tuple(rng.integers(0, s) for s in x.shape) for _ in range(12)]:
+            old = x[idx]
+            x[idx] = old + h
+            lp = np.sum(O.attention_fwd(q, k, v, m)[0] * g)
+            x[idx] = old - h
+            lm = np.sum(O.attention_fwd(q, k, v, m)[0] * g)
+            x[idx] = old
+            num = (lp - lm) / (2 * h)
+            assert abs(dx[idx] - num) <= 1e-6 * max(1.0, abs(num)), (idx, dx[idx], num)
+    # D from the probabilities equals do . o (o already holds the mask)
+    s = np.einsum("bhid,bhjd->bhij", q, np.repeat(k, H // Hkv, axis=1)) / math.sqrt(d)
+    s = np.where(np.tril(np.ones((T, T), bool)), s, -np.inf)
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    dp = np.einsum("bhid,bhjd->bhij", g, np.repeat(v, H // Hkv, axis=1)) * m
+    assert np.allclose(np.sum(p * dp, -1), np.sum(g * o, -1), rtol=1e-12, atol=1e-12)
