@@ -71,16 +71,20 @@ typedef struct {
   float eps;          /* norm epsilon, added inside the square root (1e-5)          */
   float rope_base;    /* RoPE base (10000)                                           */
   float dropout;      /* inverted-dropout probability p, 0 <= p < 1 (0: off); applied by
-                         the training forward (slt_forward_loss) to the embedding output
-                         and to each block's attention-projection and MLP outputs (the
-                         parallel block's one combined output) before the residual add,
-                         kept values scaled by float(1/(1-p)) (Hephaistos, "Architecture
-                         at a glance"; randyGPT, "Architecture Details").  Element e =
-                         row*C + column of a site's [B*T, C] tensor is kept iff word
-                         e mod 4 of Philox-4x32-10(counter (e/4 mod 2^32, e/4 div 2^32,
-                         site, layer), key (seed mod 2^32, seed div 2^32)) is at least
-                         floor(p 2^32); sites 0 = embedding, 1 = attention projection,
-                         2 = MLP.  slt_backward regenerates the same masks. */
+                         the training forward (slt_forward_loss) to the embedding output,
+                         to each block's attention weights (after the softmax
+                         normalisation), and to its attention-projection and MLP outputs
+                         (the parallel block's one combined output) before the residual
+                         add, kept values scaled by float(1/(1-p)) (Hephaistos,
+                         "Architecture at a glance"; randyGPT, "Architecture Details").
+                         Element e of a site's tensor is kept iff word e mod 4 of
+                         Philox-4x32-10(counter (e/4 mod 2^32, e/4 div 2^32, site, layer),
+                         key (seed mod 2^32, seed div 2^32)) is at least floor(p 2^32);
+                         sites 0 = embedding, 1 = attention projection, 2 = MLP, with
+                         e = row*C + column of the [B*T, C] output, and 3 = attention
+                         weights, with e = ((b*H + h)*T + i)*T + j for query i, key j of
+                         head h of sequence b.  slt_backward regenerates the same masks;
+                         slt_forward_cached applies none. */
   uint64_t dropout_seed; /* key of the mask generator; change it per step for fresh masks */
 } slt_config;
 

@@ -241,7 +241,8 @@ struct Ctx {
 };
 
 // Inverted dropout of one site of one layer (0: embedding output, 1:
-// attention projection output, 2: MLP output); off when p = 0.  A kept
+// attention projection output, 2: MLP output, 3: attention weights); off
+// when p = 0.  A kept
 // element is scaled by 1/(1-p) rounded to fp32; the mask bit of element e
 // compares one Philox-4x32-10 word with floor(p 2^32) (drop_mult).
 static Drop make_drop(const slt_config& c, int site, int layer) {
@@ -375,6 +376,7 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
     at.ores_out = A.ores >= 0 ? x.A(A.ores) : nullptr;
     at.rot = A.rot >= 0 ? x.A(A.rot) : nullptr;
     at.rot_ready = false;
+    at.drop = make_drop(c, 3, l);
     if (p.llama) {
       void* xin = x.A(p.xs[2 * l]);
       void* xmid = x.A(p.xs[2 * l + 1]);
@@ -454,6 +456,7 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     at.ores_in = A.ores >= 0 ? x.A(A.ores) : nullptr;
     at.rot = A.rot >= 0 ? x.A(A.rot) : nullptr;
     at.rot_ready = true;
+    at.drop = make_drop(c, 3, l);
     char* qkv = (char*)x.A(A.qkv);
     if (p.llama) {
       // dx: gradient at x_out, kept until the layer's weight gradients;

@@ -318,7 +318,7 @@ struct Geo {
 // ---------------------------------------------------------------------------
 // Forward.  grid (ceil(T/64), H, B); wave w owns queries q0 + 16w + l%16.
 // ---------------------------------------------------------------------------
-template <typename T, int NC, bool VEC>
+template <typename T, int NC, bool VEC, bool DROP>
 __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
   using Gm = Geo<T, NC>;
   constexpr int DP = Gm::DP, XS = Gm::XS, TS = Gm::TS;
@@ -399,6 +399,12 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
         p[r] = exp2f(s[ks][r] - mn);
         rs += p[r];
       }
+      if (DROP) {  // the normaliser keeps every weight; the values see the dropped ones
+        float dm[4];
+        drop_mults<4>(a.drop, att_elem(b, a.H, h, T_, qi, k0 + ks * 16 + g4), dm);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] *= dm[r];
+      }
       pf[ks] = pack4<T>(p);
     }
     rs += __shfl_xor(rs, 16, 64);
@@ -449,7 +455,7 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
 //   S^T = K Q^T, P = exp(S/sqrt(d) - lse), dP^T = V dO^T,
 //   dS = P (dP - D), dQ^T += K^T dS^T, then dq = rotate^T(dQ) / sqrt(d).
 // ---------------------------------------------------------------------------
-template <typename T, int NC, bool VEC>
+template <typename T, int NC, bool VEC, bool DROP>
 __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
   using Gm = Geo<T, NC>;
   constexpr int DP = Gm::DP, XS = Gm::XS, TS = Gm::TS, FS = Gm::FS;
@@ -536,13 +542,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
         }
         pacc = mma16(lds4(&Vs[off]), gf[c], pacc);
       }
-      float ds[4];
+      float ds[4], dm[4] = {1.f, 1.f, 1.f, 1.f};
+      if (DROP) drop_mults<4>(a.drop, att_elem(b, a.H, h, T_, qi, k0 + ks * 16 + g4), dm);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = k0 + ks * 16 + g4 + r;
         const bool ok = key <= qi && key < T_ && qi < T_;
         const float p = ok ? exp2f(sacc[r] * scale2 - lse2) : 0.f;
-        ds[r] = p * (pacc[r] - Dq);
+        ds[r] = DROP ? p * (dm[r] * pacc[r] - Dq) : p * (pacc[r] - Dq);
       }
       const Pk<T, 4> dsf = pack4<T>(ds);
       const Pk<T, 4> dsl = low_part<T>(dsf, ds);
@@ -575,7 +582,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
 // its key tile:  S = Q K^T, P = exp(S/sqrt(d) - lse), dP = dO V^T,
 // dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
 // ---------------------------------------------------------------------------
-template <typename T, int NC, bool VEC>
+template <typename T, int NC, bool VEC, bool DROP>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
   using Gm = Geo<T, NC>;
   constexpr int DP = Gm::DP, XS = Gm::XS, TS = Gm::TS, FS = Gm::FS;
@@ -652,14 +659,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
           }
           pacc = mma16(lds4(&Gs[off]), vf[c], pacc);
         }
-        float p[4], ds[4];
+        float p[4], ds[4], dm[4] = {1.f, 1.f, 1.f, 1.f};
+        if (DROP) drop_mults_strided<4>(a.drop, att_elem(b, a.H, h, T_, q0 + qs * 16 + g4, ki), (uint64_t)T_, dm);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ql = qs * 16 + g4 + r;
           const int q = q0 + ql;
           const bool ok = ki <= q && q < T_ && ki < T_;
           p[r] = ok ? exp2f(sacc[r] * scale2 - lse2s[ql]) : 0.f;
-          ds[r] = p[r] * (pacc[r] - Ds[ql]);
+          if (DROP) {  // dS takes the dropped dP, dV the dropped weights
+            ds[r] = p[r] * (dm[r] * pacc[r] - Ds[ql]);
+            p[r] *= dm[r];
+          } else {
+            ds[r] = p[r] * (pacc[r] - Ds[ql]);
+          }
         }
         const Pk<T, 4> pf = pack4<T>(p);
         const Pk<T, 4> pfl = low_part<T>(pf, p);  // dV sums over the whole group: P as hi + lo
@@ -732,34 +745,44 @@ bool vec_path_ok(const AttnArgs& a, bool bwd) {
 
 int64_t attention_bwd_ws(int B, int H, int T) { return (int64_t)B * H * T * 4; }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool DROP>
 static slt_status attn_fwd_t(const AttnArgs& a, hipStream_t s) {
   dim3 grid((a.T + TQ - 1) / TQ, a.H, a.B);
   switch ((a.d + 15) / 16) {
-    case 1: attn_fwd_k<T, 1, VEC><<<grid, 256, 0, s>>>(a); break;
-    case 2: attn_fwd_k<T, 2, VEC><<<grid, 256, 0, s>>>(a); break;
-    case 3: attn_fwd_k<T, 3, VEC><<<grid, 256, 0, s>>>(a); break;
-    case 4: attn_fwd_k<T, 4, VEC><<<grid, 256, 0, s>>>(a); break;
+    case 1: attn_fwd_k<T, 1, VEC, DROP><<<grid, 256, 0, s>>>(a); break;
+    case 2: attn_fwd_k<T, 2, VEC, DROP><<<grid, 256, 0, s>>>(a); break;
+    case 3: attn_fwd_k<T, 3, VEC, DROP><<<grid, 256, 0, s>>>(a); break;
+    case 4: attn_fwd_k<T, 4, VEC, DROP><<<grid, 256, 0, s>>>(a); break;
     default: return fail(SLT_EUNSUPPORTED, "attention: head dim above 64");
   }
   return check_launch("attention_fwd");
 }
 
 template <typename T, bool VEC>
+static slt_status attn_fwd_t(const AttnArgs& a, hipStream_t s) {
+  return a.drop.on ? attn_fwd_t<T, VEC, true>(a, s) : attn_fwd_t<T, VEC, false>(a, s);
+}
+
+template <typename T, bool VEC, bool DROP>
 static slt_status attn_bwd_t(const AttnArgs& a, hipStream_t s) {
   dim3 gq((a.T + TQ - 1) / TQ, a.H, a.B);
   dim3 gk((a.T + TQ - 1) / TQ, a.Hkv, a.B);
   switch ((a.d + 15) / 16) {
-#define SLT_ATT_BWD(NCv)                                   \
-  case NCv:                                                \
-    attn_bwd_dq_k<T, NCv, VEC><<<gq, 256, 0, s>>>(a);      \
-    attn_bwd_dkdv_k<T, NCv, VEC><<<gk, 256, 0, s>>>(a);    \
+#define SLT_ATT_BWD(NCv)                                         \
+  case NCv:                                                      \
+    attn_bwd_dq_k<T, NCv, VEC, DROP><<<gq, 256, 0, s>>>(a);      \
+    attn_bwd_dkdv_k<T, NCv, VEC, DROP><<<gk, 256, 0, s>>>(a);    \
     break;
     SLT_ATT_BWD(1) SLT_ATT_BWD(2) SLT_ATT_BWD(3) SLT_ATT_BWD(4)
 #undef SLT_ATT_BWD
     default: return fail(SLT_EUNSUPPORTED, "attention: head dim above 64");
   }
   return check_launch("attention_bwd");
+}
+
+template <typename T, bool VEC>
+static slt_status attn_bwd_t(const AttnArgs& a, hipStream_t s) {
+  return a.drop.on ? attn_bwd_t<T, VEC, true>(a, s) : attn_bwd_t<T, VEC, false>(a, s);
 }
 
 slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s) {

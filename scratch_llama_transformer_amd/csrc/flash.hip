@@ -259,6 +259,7 @@ struct FlArgs {
   const float* cs;
   int64_t ldv, ldo, ldores, lddo, lddq, lddk, lddv;
   int B, T, H, Hkv, d, R, rope_mode;
+  Drop drop;                      // dropout of the attention weights (att_elem)
 };
 
 // ---------------------------------------------------------------------------
@@ -383,6 +384,7 @@ __global__ __launch_bounds__(128) void fl_prep_k(const bf16* __restrict__ q, int
 // ---------------------------------------------------------------------------
 constexpr int FC = 256;  // queries per chunk
 
+template <bool DROP>
 __global__ __launch_bounds__(256, 2) void fl_fwd2_k(FlArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[3][3 * FTB];
   const int T = a.T, nck = (T + FC - 1) / FC;
@@ -482,6 +484,15 @@ __global__ __launch_bounds__(256, 2) void fl_fwd2_k(FlArgs a) {
           }
         l[i] = l[i] * alpha + rs;  // this lane's keys only; the four lanes are summed at the end
         m[i] = mn;
+        if (DROP) {  // the normaliser keeps every weight; the values see the dropped ones
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            float dm[4];
+            drop_mults<4>(a.drop, att_elem(b, a.H, h, T, qi, k0 + 16 * tt + 4 * g), dm);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[tt][r] *= dm[r];
+          }
+        }
         const u32x4 pb = pack_k(sv[0], sv[1]);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
@@ -575,6 +586,7 @@ __device__ __forceinline__ void fl_stage_acc(float* F, int row, int g, const f32
 // dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (hi/lo).
 // LDS stage: [K hi | K lo | V], two stages.
 // ---------------------------------------------------------------------------
+template <bool DROP>
 __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][3 * FTB];
   const int T = a.T, ntq = (T + FR - 1) / FR;
@@ -673,6 +685,12 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
         f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 2; ++s) dp = mma(vf[t][s], gf[s], dp);
+        if (DROP) {  // dS takes the dropped dP
+          float dm[4];
+          drop_mults<4>(a.drop, att_elem(b, a.H, h, T, qi, k0 + 16 * t + 4 * g), dm);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dp[r] *= dm[r];
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) ds[t][r] = p[t][r] * (dp[r] - D);
       }
@@ -714,6 +732,7 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
 // dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS (hi/lo).
 // LDS stage: [Q hi | Q lo | dO], two stages.
 // ---------------------------------------------------------------------------
+template <bool DROP>
 __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[2][3 * FTB];
   const int T = a.T, G = a.H / a.Hkv, ntk = (T + FR - 1) / FR;
@@ -839,8 +858,19 @@ __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
         f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 2; ++s) dp = mma(gr[t][s], vf[s], dp);
+        if (DROP) {  // dS takes the dropped dP, dV the dropped weights
+          float dm[4];
+          drop_mults_strided<4>(a.drop, att_elem(b, a.H, kvh * G + n / per, T, q0 + 16 * t + 4 * g, ki),
+                                (uint64_t)T, dm);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ds[t][r] = p[t][r] * (dp[r] - dc[t][r]);
+          for (int r = 0; r < 4; ++r) {
+            ds[t][r] = p[t][r] * (dm[r] * dp[r] - dc[t][r]);
+            p[t][r] *= dm[r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ds[t][r] = p[t][r] * (dp[r] - dc[t][r]);
+        }
       }
     }
     {
@@ -919,6 +949,7 @@ constexpr int KC = 256;                 // keys per chunk
 constexpr int STB = 3 * FTB + 1024;     // stage bytes: Q hi, Q lo, dO, then lse (256 B), D (256 B), pad
 
 
+template <bool DROP>
 __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[3][STB];
   const int T = a.T, G = a.H / a.Hkv, nkc = (T + KC - 1) / KC;
@@ -1025,8 +1056,19 @@ __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
               if (qq >= T || ki > qq) p[tt][r] = 0.f;
             }
           }
+          if (DROP) {  // dS takes the dropped dP, dV the dropped weights
+            float dm[4];
+            drop_mults_strided<4>(a.drop, att_elem(b, a.H, kvh * G + n / per, T, qh0 + 16 * tt + 4 * g, ki),
+                                  (uint64_t)T, dm);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ds[tt][r] = p[tt][r] * (dp[r] - dn[r]);
+            for (int r = 0; r < 4; ++r) {
+              ds[tt][r] = p[tt][r] * (dm[r] * dp[r] - dn[r]);
+              p[tt][r] *= dm[r];
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ds[tt][r] = p[tt][r] * (dp[r] - dn[r]);
+          }
         }
         pack_k_hilo(p[0], p[1], ph[i], pl[i]);
         pack_k_hilo(ds[0], ds[1], dh[i], dl[i]);
@@ -1124,6 +1166,7 @@ FlArgs to_fl(const AttnArgs& a) {
   f.d = a.d;
   f.R = a.R;
   f.rope_mode = a.rope_mode;
+  f.drop = a.drop;
   return f;
 }
 
@@ -1161,7 +1204,8 @@ slt_status flash_fwd(const AttnArgs& a, hipStream_t s) {
     if (st != SLT_OK) return st;
   }
   const int nck = (a.T + FC - 1) / FC;
-  fl_fwd2_k<<<nck * a.H * a.B, 256, 0, s>>>(f);
+  if (a.drop.on) fl_fwd2_k<true><<<nck * a.H * a.B, 256, 0, s>>>(f);
+  else fl_fwd2_k<false><<<nck * a.H * a.B, 256, 0, s>>>(f);
   return check_launch("attention forward");
 }
 
@@ -1172,14 +1216,17 @@ slt_status flash_bwd(const AttnArgs& a, hipStream_t s) {
     if (st != SLT_OK) return st;
   }
   const int nt = (a.T + FR - 1) / FR;
-  fl_dq_k<<<nt * a.H * a.B, 256, 0, s>>>(f);
+  if (a.drop.on) fl_dq_k<true><<<nt * a.H * a.B, 256, 0, s>>>(f);
+  else fl_dq_k<false><<<nt * a.H * a.B, 256, 0, s>>>(f);
   slt_status st = check_launch("attention backward (dq)");
   if (st != SLT_OK) return st;
   if (a.T % 4 == 0 && al(a.lse_in, 16) && al(a.delta, 16)) {
     const int nkc = (a.T + KC - 1) / KC;
-    fl_dkdv2_k<<<nkc * a.Hkv * a.B, 512, 0, s>>>(f);
+    if (a.drop.on) fl_dkdv2_k<true><<<nkc * a.Hkv * a.B, 512, 0, s>>>(f);
+    else fl_dkdv2_k<false><<<nkc * a.Hkv * a.B, 512, 0, s>>>(f);
   } else {
-    fl_dkdv_k<<<nt * a.Hkv * a.B, 256, 0, s>>>(f);
+    if (a.drop.on) fl_dkdv_k<true><<<nt * a.Hkv * a.B, 256, 0, s>>>(f);
+    else fl_dkdv_k<false><<<nt * a.Hkv * a.B, 256, 0, s>>>(f);
   }
   return check_launch("attention backward (dk, dv)");
 }

@@ -132,6 +132,19 @@ __device__ __forceinline__ void drop_mults(const Drop& d, uint64_t e0, float (&m
   }
 }
 
+// Multipliers of elements e0, e0 + stride, ... (one generator call each).
+template <int N>
+__device__ __forceinline__ void drop_mults_strided(const Drop& d, uint64_t e0, uint64_t stride, float (&m)[N]) {
+#pragma unroll
+  for (int r = 0; r < N; ++r) m[r] = drop_mult(d, e0 + r * stride);
+}
+
+// Element of attention weight (query i, key j) of head h of sequence b: the
+// weights of one head form a T x T block, the blocks ordered by (b, h).
+__device__ __forceinline__ uint64_t att_elem(int b, int H, int h, int T, int i, int j) {
+  return (uint64_t)(((int64_t)b * H + h) * T + i) * (uint64_t)T + (uint64_t)j;
+}
+
 // SwiGLU (Hephaistos, "Architecture at a glance": silu(x W1) * (x W3)), shared
 // by the element kernels and the fused GEMM epilogues so both compute the
 // same expression: h = a sigmoid(a) b; db = dh a sigmoid(a),
@@ -287,6 +300,7 @@ struct AttnArgs {
   const void* ores_in; // backward: that residual (NULL: treat as 0)
   void* rot;           // bf16 path: rotated hi/lo copies of q and k (flash_rot_elems bf16 values)
   bool rot_ready;      // rot already holds them for these q, k (skip the RoPE pass)
+  Drop drop{};         // dropout of the attention weights: element ((b H + h) T + i) T + j
 };
 slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s);
 slt_status launch_attention_bwd(const AttnArgs& a, hipStream_t s);

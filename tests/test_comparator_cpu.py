@@ -57,8 +57,8 @@ def test_planted_mistakes_fail(base, monkeypatch, bug):
             x / np.sqrt(np.sum(x * x, -1, keepdims=True)) * g, 1.0 / np.sqrt(np.sum(x * x, -1))))
     elif bug == "attention_dv_dropped_group":
         orig = M.attention_bwd
-        monkeypatch.setattr(M, "attention_bwd", lambda q, k, v, do: (lambda r: (r[0], r[1], 0.9 * r[2]))(
-            orig(q, k, v, do)))
+        monkeypatch.setattr(M, "attention_bwd", lambda q, k, v, do, drop=None: (lambda r: (r[0], r[1], 0.9 * r[2]))(
+            orig(q, k, v, do, drop)))
     elif bug == "swiglu_missing_term":
         monkeypatch.setattr(M, "swiglu_bwd", lambda a, b, dh: (
             np.asarray(dh) * np.asarray(b) * M._sigmoid(np.asarray(a)), np.asarray(dh) * np.asarray(a) *

@@ -113,21 +113,25 @@ def test_full_batch_step_one_layer(TS):
                                 f"weight {name}", w.adam_eps)
 
 
-# (config index, batch, layers, dropout p): p exactly representable in binary32,
+# (config index, overrides, dropout p): p exactly representable in binary32,
 # the library's type for it, so both sides draw the same threshold and scale.
-DROPOUT_CASES = [(1, None, None, 0.25), (2, 8, None, 0.125), (3, 8, None, 0.125), (5, 1, 2, 0.25)]
+# The attention kernels covered: the generic fp32 ones (tiny, d=256), the
+# bf16 chunked ones (d=384; parallel block at T=2048) and the bf16 64-key
+# dK/dV kernel (T not a multiple of 4).
+DROPOUT_CASES = [(1, {}, 0.25), (2, dict(B=8), 0.125), (3, dict(B=8), 0.125), (3, dict(B=2, L=2, T=254), 0.25),
+                 (5, dict(B=1, L=2), 0.25)]
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("ci,Bn,L,pdrop", DROPOUT_CASES)
-def test_full_step_with_dropout(TS, ci, Bn, L, pdrop):
-    """Inverted dropout at the embedding output, the attention projection
-    (the parallel block's combined projection) and the MLP output: the GPU's
-    masks are regenerated from the same Philox counters as the oracle's, so
-    loss, gradients and post-AdamW weights meet the same bars as without
-    dropout."""
+@pytest.mark.parametrize("ci,over,pdrop", DROPOUT_CASES)
+def test_full_step_with_dropout(TS, ci, over, pdrop):
+    """Inverted dropout at the embedding output, the attention weights, the
+    attention projection (the parallel block's combined projection) and the
+    MLP output: the GPU's masks are regenerated from the same Philox counters
+    as the oracle's, so loss, gradients and post-AdamW weights meet the same
+    bars as without dropout."""
     w = W.get_config(ci)
-    w = w.with_(B=Bn or w.B, L=L or w.L, dropout=pdrop, dropout_seed=0x1234_5678_9ABC + ci)
+    w = w.with_(**over, dropout=pdrop, dropout_seed=0x1234_5678_9ABC + ci)
     say("dropout step", w)
     params, tokens, ts, loss = run_step(TS, w, 1500 + ci)
     ref = O.train_step(w, params, tokens)
