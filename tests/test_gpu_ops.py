@@ -372,6 +372,7 @@ ATTN_CASES = [
     (2, 100, 4, 2, 32, 8, "pairs", BF16),
     (1, 1024, 4, 1, 64, 64, "half", BF16),
     (1, 40, 2, 2, 24, 24, "half", BF16),      # head dim not a multiple of 16: register-staged kernels
+    (2, 50, 4, 2, 32, 12, "half", BF16),      # rotate-half pairs straddling 8-dim chunks: element-wise RoPE pass
 ]
 
 
