@@ -11,6 +11,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -65,8 +67,13 @@ struct Plan {
   std::vector<LayerA> la;
   int64_t nf, rf, muf, z, cs, act_bytes;
   // scratch
-  int64_t rowloss, dx, dx2, dbig, dqkv, dmid, dn, delta, normws, embws, gemmws, gemmws_bytes, scratch_bytes;
-  int64_t dy1 = -1, dy2 = -1;  // masked output gradients of the dropped projections (dropout on)
+  // Gradient buffers the layer weight gradients read run in three sets (set
+  // l % 3 for layer l; dx of set l % 3 holds the gradient at layer l's
+  // output), since those products run one layer behind the backward walk on
+  // a second stream.  dy1 / dy2: masked output gradients of the dropped
+  // projections (dropout on).
+  int64_t dx[3], dx2[3], dbig[3], dqkv[3], dy1[3], dy2[3];
+  int64_t rowloss, dmid, dn, delta, normws, embws, gemmws, gemmws_bytes, scratch_bytes;
   int dbig_w, dmid_w;
 };
 
@@ -204,19 +211,19 @@ static slt_status make_plan(const slt_config* cfg, Plan& p) {
     return o;
   };
   p.rowloss = takes(N * 4);
-  p.dx = takes(N * C * es);
-  p.dx2 = takes(N * C * es);  // residual-stream gradient between the two sub-blocks of a layer
-  p.dbig = takes(N * p.dbig_w * es);
-  p.dqkv = p.llama ? takes(N * p.qkv_w * es) : -1;  // kept apart from dbig until the layer's dW launch
+  for (int k = 0; k < 3; ++k) {
+    p.dx[k] = takes(N * C * es);
+    p.dx2[k] = takes(N * C * es);  // residual-stream gradient between the two sub-blocks of a layer
+    p.dbig[k] = takes(N * p.dbig_w * es);
+    p.dqkv[k] = p.llama ? takes(N * p.qkv_w * es) : -1;  // kept apart from dbig until the layer's dW launch
+    p.dy1[k] = c.dropout > 0.f ? takes(N * C * es) : -1;
+    p.dy2[k] = c.dropout > 0.f && p.llama ? takes(N * C * es) : -1;
+  }
   p.dmid = takes(N * p.dmid_w * es);
   p.dn = takes(N * C * es);
   p.delta = takes(attention_bwd_ws(c.B, c.H, c.T));
   p.normws = takes(norm_bwd_ws(p.N, c.C));
   p.embws = takes(embedding_bwd_ws(N, c.V));
-  if (c.dropout > 0.f) {
-    p.dy1 = takes(N * C * es);
-    p.dy2 = p.llama ? takes(N * C * es) : -1;
-  }
   // split-K partials of the weight gradients
   p.gemmws_bytes = 64ll << 20;
   p.gemmws = takes(p.gemmws_bytes);
@@ -420,34 +427,97 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
   return SLT_OK;
 }
 
+// A second stream per device for the layer weight gradients, and the events
+// that order it against the backward walk's stream: `ready` is recorded on
+// the walk's stream before each launch, done[k] after the launch that reads
+// buffer set k.  Created on first use (default priority, non-blocking);
+// host calls that enqueue backward walks on one device take turns (mutex),
+// so an event is never re-recorded before the waits on its last record are
+// enqueued.
+struct DwStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ready = nullptr, done[3] = {nullptr, nullptr, nullptr};
+};
+static std::mutex g_dw_mu;
+
+static DwStream* dw_stream() {
+  static std::map<int, DwStream> per_dev;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  auto it = per_dev.find(dev);
+  if (it == per_dev.end()) {
+    DwStream a;
+    bool ok = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&a.ready, hipEventDisableTiming) == hipSuccess;
+    for (int k = 0; k < 3 && ok; ++k) ok = hipEventCreateWithFlags(&a.done[k], hipEventDisableTiming) == hipSuccess;
+    if (!ok) a = DwStream{};  // fall back to the walk's stream (what was created stays until exit)
+    (void)hipGetLastError();
+    it = per_dev.emplace(dev, a).first;
+  }
+  return it->second.s ? &it->second : nullptr;
+}
+
+static slt_status hip_ok(hipError_t e, const char* what) {
+  return e == hipSuccess ? SLT_OK : fail(SLT_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
 static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, float* grads) {
   const slt_config& c = p.c;
   const int N = p.N, C = c.C;
   const int64_t ldt = c.T + 1;
   const float* cs = reinterpret_cast<const float*>(x.A(p.cs));
-  void* dx = x.S(p.dx);
   void* dn = x.S(p.dn);
-  char* dbig = (char*)x.S(p.dbig);
   char* dmid = (char*)x.S(p.dmid);
   void* nws = x.S(p.normws);
-
-  void* dx2 = x.S(p.dx2);
   DwList dws;
 
+  // The weight gradients of layer l run on the second stream while the walk
+  // goes on through layer l-1; before the walk writes a buffer set again it
+  // waits for the last launch that reads it.
+  std::lock_guard<std::mutex> lock(g_dw_mu);
+  DwStream* aux = dw_stream();
+  Ctx xw = x;
+  if (aux) xw.s = aux->s;
+  bool pending[3] = {false, false, false};
+  auto wait_set = [&](int k) -> slt_status {
+    if (!aux || !pending[k]) return SLT_OK;
+    pending[k] = false;
+    return hip_ok(hipStreamWaitEvent(x.s, aux->done[k], 0), "backward: stream wait");
+  };
+  auto launch_dw = [&](int k) -> slt_status {
+    if (aux) {
+      SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
+      SLT_TRY(hip_ok(hipStreamWaitEvent(aux->s, aux->ready, 0), "backward: stream wait"));
+    }
+    SLT_TRY(flush_dw(xw, dws));
+    if (aux) {
+      SLT_TRY(hip_ok(hipEventRecord(aux->done[k], aux->s), "backward: event record"));
+      pending[k] = true;
+    }
+    return SLT_OK;
+  };
+
   // lm_head and final norm (its weight gradient joins the last layer's launch)
+  void* dxL = x.S(p.dx[(c.L - 1) % 3]);
   dws.add(N, c.V, C, x.A(p.z), c.V, x.A(p.nf), C, grads + p.head, C);
   SLT_TRY(proj_dx(x, N, c.V, C, x.A(p.z), c.V, x.P(p.head), C, dn, C));
   if (p.llama)
-    SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.rf), dn, nullptr, dx,
+    SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.rf), dn, nullptr, dxL,
                                grads + p.normf, N, C, x.dt, nws, x.s, x.gw));
   else
     SLT_TRY(launch_layernorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.muf),
-                                 (const float*)x.A(p.rf), dn, nullptr, dx, grads + p.normf, grads + p.normfb, N, C,
+                                 (const float*)x.A(p.rf), dn, nullptr, dxL, grads + p.normf, grads + p.normfb, N, C,
                                  x.dt, nws, x.s, x.gw));
 
   for (int l = c.L - 1; l >= 0; --l) {
     const LayerP& W = p.lp[l];
     const LayerA& A = p.la[l];
+    const int sl = l % 3, si = (l + 2) % 3;  // this layer's set; the set of the gradient at its input
+    SLT_TRY(wait_set(sl));
+    void* dx = x.S(p.dx[sl]);          // gradient at the layer's output
+    void* dxi = x.S(p.dx[si]);         // gradient at its input (the next layer down's output)
+    void* dx2 = x.S(p.dx2[sl]);
+    char* dbig = (char*)x.S(p.dbig[sl]);
     AttnArgs at{};
     at.B = c.B; at.T = c.T; at.H = c.H; at.Hkv = c.Hkv; at.d = p.d; at.R = c.R; at.rope_mode = c.rope_mode;
     at.dtype = x.dt; at.cs = cs;
@@ -459,14 +529,14 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     at.drop = make_drop(c, 3, l);
     char* qkv = (char*)x.A(A.qkv);
     if (p.llama) {
-      // dx: gradient at x_out, kept until the layer's weight gradients;
+      // dx: gradient at x_out, read by the layer's weight gradients;
       // dx2: gradient at x_mid; dbig: [da | db]; dqkv: [dq | dk | dv].
-      char* dqkv = (char*)x.S(p.dqkv);
+      char* dqkv = (char*)x.S(p.dqkv[sl]);
       // x_out = x_mid + drop(h W2^T): the product's gradient is dx times the mask
       const void* dy2 = dx;
-      if (p.dy2 >= 0) {
-        SLT_TRY(launch_drop_apply(dx, x.S(p.dy2), N, C, x.dt, make_drop(c, 2, l), x.s));
-        dy2 = x.S(p.dy2);
+      if (p.dy2[sl] >= 0) {
+        SLT_TRY(launch_drop_apply(dx, x.S(p.dy2[sl]), N, C, x.dt, make_drop(c, 2, l), x.s));
+        dy2 = x.S(p.dy2[sl]);
       }
       dws.add(N, C, c.F, dy2, C, x.A(A.h), c.F, grads + W.w2, c.F);
       SLT_TRY(mlp_in_bwd(N, c.F, C, dy2, x.P(W.w2), (const char*)x.A(A.ab), dbig, dmid, x.dt, x.s));
@@ -476,9 +546,9 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
                                  grads + W.norm2, N, C, x.dt, nws, x.s, x.gw));
       // x_mid = x_in + drop(o W_o^T)
       const void* dy1 = dx2;
-      if (p.dy1 >= 0) {
-        SLT_TRY(launch_drop_apply(dx2, x.S(p.dy1), N, C, x.dt, make_drop(c, 1, l), x.s));
-        dy1 = x.S(p.dy1);
+      if (p.dy1[sl] >= 0) {
+        SLT_TRY(launch_drop_apply(dx2, x.S(p.dy1[sl]), N, C, x.dt, make_drop(c, 1, l), x.s));
+        dy1 = x.S(p.dy1[sl]);
       }
       dws.add(N, C, p.qd, dy1, C, x.A(A.o), p.qd, grads + W.wo, p.qd);
       SLT_TRY(proj_dx(x, N, C, p.qd, dy1, C, x.P(W.wo), p.qd, dmid, p.qd));
@@ -490,17 +560,18 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       at.lddq = at.lddk = at.lddv = p.qkv_w;
       SLT_TRY(launch_attention_bwd(at, x.s));
       dws.add(N, p.qkv_w, C, dqkv, p.qkv_w, x.A(A.n1), C, grads + W.qkvw, C);
-      SLT_TRY(flush_dw(x, dws));
+      SLT_TRY(launch_dw(sl));
       SLT_TRY(proj_dx(x, N, p.qkv_w, C, dqkv, p.qkv_w, x.P(W.qkvw), C, dn, C));
-      SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l]), x.P(W.norm1), (const float*)x.A(A.r1), dn, dx2, dx,
+      SLT_TRY(wait_set(si));
+      SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l]), x.P(W.norm1), (const float*)x.A(A.r1), dn, dx2, dxi,
                                  grads + W.norm1, N, C, x.dt, nws, x.s, x.gw));
     } else {
       char* ou = (char*)x.A(A.o);
       // x_out = x_in + drop([o | u] W_out^T)
       const void* dy1 = dx;
-      if (p.dy1 >= 0) {
-        SLT_TRY(launch_drop_apply(dx, x.S(p.dy1), N, C, x.dt, make_drop(c, 1, l), x.s));
-        dy1 = x.S(p.dy1);
+      if (p.dy1[sl] >= 0) {
+        SLT_TRY(launch_drop_apply(dx, x.S(p.dy1[sl]), N, C, x.dt, make_drop(c, 1, l), x.s));
+        dy1 = x.S(p.dy1[sl]);
       }
       dws.add(N, C, p.ou_w, dy1, C, ou, p.ou_w, grads + W.wout, p.ou_w);
       SLT_TRY(proj_dx(x, N, C, p.ou_w, dy1, C, x.P(W.wout), p.ou_w, dmid, p.ou_w));
@@ -514,14 +585,19 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       at.lddq = at.lddk = at.lddv = p.in_w;
       SLT_TRY(launch_attention_bwd(at, x.s));
       dws.add(N, p.in_w, C, dbig, p.in_w, x.A(A.n1), C, grads + W.qkvw, C);
-      SLT_TRY(flush_dw(x, dws));
+      SLT_TRY(launch_dw(sl));
       SLT_TRY(proj_dx(x, N, p.in_w, C, dbig, p.in_w, x.P(W.qkvw), C, dn, C));
+      SLT_TRY(wait_set(si));
       SLT_TRY(launch_layernorm_bwd(x.A(p.xs[l]), x.P(W.norm1), (const float*)x.A(A.mu1), (const float*)x.A(A.r1),
-                                   dn, dx, dx, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws, x.s, x.gw));
+                                   dn, dx, dxi, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws, x.s, x.gw));
     }
   }
-  SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, dx, grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s, x.gw,
-                               make_drop(c, 0, 0)));
+  SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, x.S(p.dx[2]), grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s,
+                               x.gw, make_drop(c, 0, 0)));
+  // the walk's stream ends after every weight gradient (launched in order on
+  // the second stream, so the last one's event covers them all)
+  SLT_TRY(wait_set(0));
+  for (int k = 0; k < 3; ++k) SLT_TRY(wait_set(k));
   return SLT_OK;
 }
 
