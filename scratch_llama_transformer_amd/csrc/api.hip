@@ -427,16 +427,17 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
   return SLT_OK;
 }
 
-// A second stream per device for the layer weight gradients, and the events
-// that order it against the backward walk's stream: `ready` is recorded on
-// the walk's stream before each launch, done[k] after the launch that reads
-// buffer set k.  Created on first use (default priority, non-blocking);
+// A second stream per device for the layer weight gradients (and the token
+// sort of the embedding gradient), and the events that order it against the
+// backward walk's stream: `ready` is recorded on the walk's stream before
+// each launch, done[k] after the launch that reads buffer set k, sort_done
+// after the sort.  Created on first use (default priority, non-blocking);
 // host calls that enqueue backward walks on one device take turns (mutex),
 // so an event is never re-recorded before the waits on its last record are
 // enqueued.
 struct DwStream {
   hipStream_t s = nullptr;
-  hipEvent_t ready = nullptr, done[3] = {nullptr, nullptr, nullptr};
+  hipEvent_t ready = nullptr, done[3] = {nullptr, nullptr, nullptr}, sort_done = nullptr;
 };
 static std::mutex g_dw_mu;
 
@@ -450,6 +451,7 @@ static DwStream* dw_stream() {
     bool ok = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) == hipSuccess &&
               hipEventCreateWithFlags(&a.ready, hipEventDisableTiming) == hipSuccess;
     for (int k = 0; k < 3 && ok; ++k) ok = hipEventCreateWithFlags(&a.done[k], hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&a.sort_done, hipEventDisableTiming) == hipSuccess;
     if (!ok) a = DwStream{};  // fall back to the walk's stream (what was created stays until exit)
     (void)hipGetLastError();
     it = per_dev.emplace(dev, a).first;
@@ -496,6 +498,17 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     }
     return SLT_OK;
   };
+
+  // the token sort of the embedding gradient (tokens only) runs on the second
+  // stream while the walk goes on; `sort_done` orders the final sums after it
+  bool sort_ahead = false;
+  if (aux) {
+    SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
+    SLT_TRY(hip_ok(hipStreamWaitEvent(aux->s, aux->ready, 0), "backward: stream wait"));
+    SLT_TRY(launch_embedding_sort(tok, c.B, c.T, ldt, c.V, x.S(p.embws), aux->s));
+    SLT_TRY(hip_ok(hipEventRecord(aux->sort_done, aux->s), "backward: event record"));
+    sort_ahead = true;
+  }
 
   // lm_head and final norm (its weight gradient joins the last layer's launch)
   void* dxL = x.S(p.dx[(c.L - 1) % 3]);
@@ -592,8 +605,9 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
                                    dn, dx, dxi, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws, x.s, x.gw));
     }
   }
+  if (sort_ahead) SLT_TRY(hip_ok(hipStreamWaitEvent(x.s, aux->sort_done, 0), "backward: stream wait"));
   SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, x.S(p.dx[2]), grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s,
-                               x.gw, make_drop(c, 0, 0)));
+                               x.gw, make_drop(c, 0, 0), sort_ahead));
   // the walk's stream ends after every weight gradient (launched in order on
   // the second stream, so the last one's event covers them all)
   SLT_TRY(wait_set(0));

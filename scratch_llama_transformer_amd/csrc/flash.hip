@@ -545,10 +545,32 @@ __device__ __forceinline__ void fl_store_rows(const float* F, float scale, bf16*
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = F[r * FS + j0 + e];
-    if (j0 < R) {
+    const int hr = R >> 1;
+    if (j0 < R && !(j0 + 4 <= R && (mode != SLT_ROPE_HALF || j0 + 4 <= hr || j0 >= hr))) {
+      // the group straddles R or (rotate-half) the middle of the rotated
+      // dims: one element at a time
+      const float* tb = cs + (int64_t)t * R;
+      float w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e;
+        w[e] = v[e];
+        if (j >= R) continue;
+        if (mode == SLT_ROPE_HALF) {
+          const bool first = j < hr;
+          const int i = first ? j : j - hr;
+          const float c = tb[2 * i], s = tb[2 * i + 1], y = F[r * FS + (first ? j + hr : j - hr)];
+          w[e] = first ? v[e] * c + y * s : v[e] * c - y * s;
+        } else {
+          const float c = tb[j & ~1], s = tb[(j & ~1) + 1];
+          w[e] = (j & 1) == 0 ? v[e] * c + F[r * FS + j + 1] * s : v[e] * c - F[r * FS + j - 1] * s;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = w[e];
+    } else if (j0 < R) {
       const float* tb = cs + (int64_t)t * R;
       if (mode == SLT_ROPE_HALF) {
-        const int hr = R >> 1;
         const bool first = j0 < hr;
         const int i0 = first ? j0 : j0 - hr, p0 = first ? j0 + hr : j0 - hr;
 #pragma unroll

@@ -163,12 +163,18 @@ __global__ __launch_bounds__(kEmbChunk) void emb_chunk_rank_k(const int32_t* __r
 __global__ void emb_col_prefix_k(int V, int nchunk, EmbWs w) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
   if (v >= V) return;
+  constexpr int G = 16;  // counts loaded per batch (independent loads in flight)
   int run = 0;
-  for (int c = 0; c < nchunk; ++c) {
-    const int64_t k = (int64_t)c * V + v;
-    const int x = w.cnt[k];
-    w.cnt[k] = run;
-    run += x;
+  for (int c0 = 0; c0 < nchunk; c0 += G) {
+    int x[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) x[j] = c0 + j < nchunk ? w.cnt[(int64_t)(c0 + j) * V + v] : 0;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (c0 + j < nchunk) {
+        w.cnt[(int64_t)(c0 + j) * V + v] = run;
+        run += x[j];
+      }
   }
   w.total[v] = run;
 }
@@ -227,11 +233,22 @@ __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict_
     float acc[VEC];
 #pragma unroll
     for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
+    // rows are loaded 8 at a time before the partials they end are stored (the
+    // stores could alias the rows as far as the compiler knows, which would
+    // otherwise serialise every load)
+    constexpr int KB = 8;
+    float fr[KB][VEC];
 #pragma unroll
     for (int k = 0; k < kEmbTile; ++k) {
+      if (k % KB == 0) {
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+          if (s + k + j < e) load_f<T, VEC>(dx + (int64_t)pos[k + j] * C + c0, fr[j]);
+      }
       if (s + k < e) {
         float f[VEC];
-        load_f<T, VEC>(dx + (int64_t)pos[k] * C + c0, f);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) f[q] = fr[k % KB][q];
         if (drop.on) {  // the embedding output's dropout mask (site 0), regenerated
           float m[VEC];
           drop_mults<VEC>(drop, (uint64_t)pos[k] * C + c0, m);
@@ -265,11 +282,14 @@ __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict_
 
 // One 256-thread block per vocabulary row: zero rows, and rows spanning
 // several tiles.  For the latter the 4 waves take contiguous quarters of the
-// tiles (tail of the first tile, then heads in tile order), each summing with
-// 4 interleaved accumulators; the quarters are added in order.
+// pieces (tail of the first tile, then heads in tile order); a lane owns 8
+// columns of a 512-column pass and sums 4 pieces per step into 4
+// interleaved accumulators, so that 32 loads are in flight per step; the
+// quarters are added in order.
 __global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte, int V, int C, EmbWs w,
                                                         GradW gw) {
-  __shared__ float part[4][256];
+  constexpr int QN = 8;  // columns per lane per pass
+  __shared__ float part[4][kWave * QN];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int v = blockIdx.x;
   const int rs = w.start[v], re = w.start[v + 1];
@@ -285,12 +305,12 @@ __global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte
   const int np = t1 - t0 + 1;
   const int per = (np + 3) / 4;
   const int pb = wave * per, pe = min(np, pb + per);
-  for (int c0 = 0; c0 < C; c0 += kWave * 4) {
-    float acc[4][4];
+  for (int c0 = 0; c0 < C; c0 += kWave * QN) {
+    float acc[4][QN];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[u][q] = 0.f;
+      for (int q = 0; q < QN; ++q) acc[u][q] = 0.f;
     for (int k = pb; k < pe; k += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -298,7 +318,7 @@ __global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte
         if (kk < pe) {
           const float* src = kk == 0 ? w.tail + (int64_t)t0 * C : w.head + (int64_t)(t0 + kk) * C;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < QN; ++q) {
             const int c = c0 + q * kWave + lane;
             if (c < C) acc[u][q] += src[c];
           }
@@ -306,9 +326,9 @@ __global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte
       }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) part[wave][q * kWave + lane] = (acc[0][q] + acc[1][q]) + (acc[2][q] + acc[3][q]);
+    for (int q = 0; q < QN; ++q) part[wave][q * kWave + lane] = (acc[0][q] + acc[1][q]) + (acc[2][q] + acc[3][q]);
     __syncthreads();
-    for (int c = threadIdx.x; c < kWave * 4; c += blockDim.x)
+    for (int c = threadIdx.x; c < kWave * QN; c += blockDim.x)
       if (c0 + c < C) {
         const float sum = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
         row[c0 + c] = gw.alpha * sum + (gw.accumulate ? row[c0 + c] : 0.f);
@@ -915,17 +935,27 @@ int64_t embedding_bwd_ws(int64_t N, int V) {
   return emb_ws_bytes(N, V, 4096);
 }
 
-slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, const void* dx, float* dwte, int V,
-                                int C, int dtype, void* ws, hipStream_t s, GradW gw, Drop drop) {
+slt_status launch_embedding_sort(const int32_t* tok, int B, int T_, int64_t ld, int V, void* ws, hipStream_t s) {
   const int N = B * T_;
   EmbWs w = emb_ws_layout(ws, N, V, 4096);
   const int nchunk = cdiv(N, kEmbChunk);
-  const int ntile = cdiv(N, kEmbTile);
   fill_i32_k<<<grid_for((int64_t)nchunk * V), 256, 0, s>>>(w.cnt, 0, (int64_t)nchunk * V);
   emb_chunk_rank_k<<<nchunk, kEmbChunk, 0, s>>>(tok, T_, ld, N, V, w);
   emb_col_prefix_k<<<cdiv(V, 256), 256, 0, s>>>(V, nchunk, w);
   emb_scan_k<<<1, 1024, 0, s>>>(V, w);
   emb_scatter_k<<<cdiv(N, 256), 256, 0, s>>>(tok, T_, ld, N, V, w);
+  return check_launch("embedding_bwd (sort)");
+}
+
+slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, const void* dx, float* dwte, int V,
+                                int C, int dtype, void* ws, hipStream_t s, GradW gw, Drop drop, bool sorted) {
+  const int N = B * T_;
+  EmbWs w = emb_ws_layout(ws, N, V, 4096);
+  const int ntile = cdiv(N, kEmbTile);
+  if (!sorted) {  // else launch_embedding_sort ran on this workspace, ordered before this call
+    const slt_status st = launch_embedding_sort(tok, B, T_, ld, V, ws, s);
+    if (st != SLT_OK) return st;
+  }
   auto go = [&](auto tag) {
     using T = decltype(tag);
     constexpr int VEC = full_vec<T>();

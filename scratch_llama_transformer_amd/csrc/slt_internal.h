@@ -249,9 +249,13 @@ slt_status launch_gemm_group(const GroupItem* items, int n, int K, float* ws, in
 slt_status launch_embedding_fwd(const int32_t* tok, int B, int T, int64_t ld, const void* wte,
                                 void* x, int V, int C, int dtype, hipStream_t s, Drop drop = {});
 int64_t embedding_bwd_ws(int64_t N, int V);
+// The embedding gradient in two phases: the stable sort of token positions
+// by id (tokens only), then the per-id sums of dx rows; launch_embedding_bwd
+// runs the sort itself unless `sorted` says it already ran on ws.
+slt_status launch_embedding_sort(const int32_t* tok, int B, int T, int64_t ld, int V, void* ws, hipStream_t s);
 slt_status launch_embedding_bwd(const int32_t* tok, int B, int T, int64_t ld, const void* dx,
                                 float* dwte, int V, int C, int dtype, void* ws, hipStream_t s, GradW gw = {},
-                                Drop drop = {});
+                                Drop drop = {}, bool sorted = false);
 slt_status launch_drop_apply(const void* g, void* out, int rows, int C, int dtype, Drop drop, hipStream_t s);
 int64_t norm_bwd_ws(int rows, int C);
 slt_status launch_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd, int rows, int C,

@@ -373,6 +373,7 @@ ATTN_CASES = [
     (1, 1024, 4, 1, 64, 64, "half", BF16),
     (1, 40, 2, 2, 24, 24, "half", BF16),      # head dim not a multiple of 16: register-staged kernels
     (2, 50, 4, 2, 32, 12, "half", BF16),      # rotate-half pairs straddling 8-dim chunks: element-wise RoPE pass
+    (1, 33, 2, 2, 16, 6, "pairs", BF16),      # R % 4 == 2: the rotated dims end inside a 4-dim group
 ]
 
 
