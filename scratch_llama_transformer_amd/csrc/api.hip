@@ -73,7 +73,7 @@ struct Plan {
   // a second stream.  dy1 / dy2: masked output gradients of the dropped
   // projections (dropout on).
   int64_t dx[3], dx2[3], dbig[3], dqkv[3], dy1[3], dy2[3];
-  int64_t rowloss, dmid, dn, delta, normws, embws, gemmws, gemmws_bytes, scratch_bytes;
+  int64_t rowloss, dmid, dn, delta, normws, normws_each, embws, gemmws, gemmws_bytes, scratch_bytes;
   int dbig_w, dmid_w;
 };
 
@@ -222,7 +222,10 @@ static slt_status make_plan(const slt_config* cfg, Plan& p) {
   p.dmid = takes(N * p.dmid_w * es);
   p.dn = takes(N * C * es);
   p.delta = takes(attention_bwd_ws(c.B, c.H, c.T));
-  p.normws = takes(norm_bwd_ws(p.N, c.C));
+  // one partial buffer per norm of the backward (final norm, then two per
+  // layer): their column sums run on the second stream, behind the walk
+  p.normws_each = a256(norm_bwd_ws(p.N, c.C));
+  p.normws = takes(p.normws_each * (2 * (int64_t)c.L + 1));
   p.embws = takes(embedding_bwd_ws(N, c.V));
   // split-K partials of the weight gradients
   p.gemmws_bytes = 64ll << 20;
@@ -431,13 +434,13 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
 // sort of the embedding gradient), and the events that order it against the
 // backward walk's stream: `ready` is recorded on the walk's stream before
 // each launch, done[k] after the launch that reads buffer set k, sort_done
-// after the sort.  Created on first use (default priority, non-blocking);
+// after the sort, fin after the last launch of a walk.  Created on first use (default priority, non-blocking);
 // host calls that enqueue backward walks on one device take turns (mutex),
 // so an event is never re-recorded before the waits on its last record are
 // enqueued.
 struct DwStream {
   hipStream_t s = nullptr;
-  hipEvent_t ready = nullptr, done[3] = {nullptr, nullptr, nullptr}, sort_done = nullptr;
+  hipEvent_t ready = nullptr, done[3] = {nullptr, nullptr, nullptr}, sort_done = nullptr, fin = nullptr;
 };
 static std::mutex g_dw_mu;
 
@@ -452,6 +455,7 @@ static DwStream* dw_stream() {
               hipEventCreateWithFlags(&a.ready, hipEventDisableTiming) == hipSuccess;
     for (int k = 0; k < 3 && ok; ++k) ok = hipEventCreateWithFlags(&a.done[k], hipEventDisableTiming) == hipSuccess;
     ok = ok && hipEventCreateWithFlags(&a.sort_done, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&a.fin, hipEventDisableTiming) == hipSuccess;
     if (!ok) a = DwStream{};  // fall back to the walk's stream (what was created stays until exit)
     (void)hipGetLastError();
     it = per_dev.emplace(dev, a).first;
@@ -470,7 +474,6 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
   const float* cs = reinterpret_cast<const float*>(x.A(p.cs));
   void* dn = x.S(p.dn);
   char* dmid = (char*)x.S(p.dmid);
-  void* nws = x.S(p.normws);
   DwList dws;
 
   // The weight gradients of layer l run on the second stream while the walk
@@ -486,6 +489,16 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     pending[k] = false;
     return hip_ok(hipStreamWaitEvent(x.s, aux->done[k], 0), "backward: stream wait");
   };
+  // partials of norm k (0: final norm, 2 l + 1: the layer's second, 2 l + 2:
+  // its first) and their column sums, on the second stream when there is one
+  auto nws = [&](int k) { return static_cast<char*>(x.S(p.normws)) + k * p.normws_each; };
+  auto norm_sums = [&](int k, float* dg, float* db) -> slt_status {
+    if (!aux) return SLT_OK;  // the norm launch summed them itself
+    SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
+    SLT_TRY(hip_ok(hipStreamWaitEvent(aux->s, aux->ready, 0), "backward: stream wait"));
+    return launch_norm_colsum(nws(k), N, C, dg, db, aux->s, x.gw);
+  };
+  const bool defer = aux != nullptr;
   auto launch_dw = [&](int k) -> slt_status {
     if (aux) {
       SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
@@ -516,11 +529,12 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
   SLT_TRY(proj_dx(x, N, c.V, C, x.A(p.z), c.V, x.P(p.head), C, dn, C));
   if (p.llama)
     SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.rf), dn, nullptr, dxL,
-                               grads + p.normf, N, C, x.dt, nws, x.s, x.gw));
+                               grads + p.normf, N, C, x.dt, nws(0), x.s, x.gw, defer));
   else
     SLT_TRY(launch_layernorm_bwd(x.A(p.xs.back()), x.P(p.normf), (const float*)x.A(p.muf),
                                  (const float*)x.A(p.rf), dn, nullptr, dxL, grads + p.normf, grads + p.normfb, N, C,
-                                 x.dt, nws, x.s, x.gw));
+                                 x.dt, nws(0), x.s, x.gw, defer));
+  SLT_TRY(norm_sums(0, grads + p.normf, p.llama ? nullptr : grads + p.normfb));
 
   for (int l = c.L - 1; l >= 0; --l) {
     const LayerP& W = p.lp[l];
@@ -556,7 +570,8 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       dws.add(N, 2 * c.F, C, dbig, 2 * c.F, x.A(A.n2), C, grads + W.w1, C);
       SLT_TRY(proj_dx(x, N, 2 * c.F, C, dbig, 2 * c.F, x.P(W.w1), C, dn, C));
       SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l + 1]), x.P(W.norm2), (const float*)x.A(A.r2), dn, dx, dx2,
-                                 grads + W.norm2, N, C, x.dt, nws, x.s, x.gw));
+                                 grads + W.norm2, N, C, x.dt, nws(2 * l + 1), x.s, x.gw, defer));
+      SLT_TRY(norm_sums(2 * l + 1, grads + W.norm2, nullptr));
       // x_mid = x_in + drop(o W_o^T)
       const void* dy1 = dx2;
       if (p.dy1[sl] >= 0) {
@@ -577,7 +592,8 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(proj_dx(x, N, p.qkv_w, C, dqkv, p.qkv_w, x.P(W.qkvw), C, dn, C));
       SLT_TRY(wait_set(si));
       SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l]), x.P(W.norm1), (const float*)x.A(A.r1), dn, dx2, dxi,
-                                 grads + W.norm1, N, C, x.dt, nws, x.s, x.gw));
+                                 grads + W.norm1, N, C, x.dt, nws(2 * l + 2), x.s, x.gw, defer));
+      SLT_TRY(norm_sums(2 * l + 2, grads + W.norm1, nullptr));
     } else {
       char* ou = (char*)x.A(A.o);
       // x_out = x_in + drop([o | u] W_out^T)
@@ -602,16 +618,20 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(proj_dx(x, N, p.in_w, C, dbig, p.in_w, x.P(W.qkvw), C, dn, C));
       SLT_TRY(wait_set(si));
       SLT_TRY(launch_layernorm_bwd(x.A(p.xs[l]), x.P(W.norm1), (const float*)x.A(A.mu1), (const float*)x.A(A.r1),
-                                   dn, dx, dxi, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws, x.s, x.gw));
+                                   dn, dx, dxi, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws(2 * l + 2), x.s,
+                                   x.gw, defer));
+      SLT_TRY(norm_sums(2 * l + 2, grads + W.norm1, grads + W.norm1b));
     }
   }
   if (sort_ahead) SLT_TRY(hip_ok(hipStreamWaitEvent(x.s, aux->sort_done, 0), "backward: stream wait"));
   SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, x.S(p.dx[2]), grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s,
                                x.gw, make_drop(c, 0, 0), sort_ahead));
-  // the walk's stream ends after every weight gradient (launched in order on
-  // the second stream, so the last one's event covers them all)
-  SLT_TRY(wait_set(0));
-  for (int k = 0; k < 3; ++k) SLT_TRY(wait_set(k));
+  // the walk's stream ends after everything on the second stream (in order
+  // there, so one event after the last launch covers it all)
+  if (aux) {
+    SLT_TRY(hip_ok(hipEventRecord(aux->fin, aux->s), "backward: event record"));
+    SLT_TRY(hip_ok(hipStreamWaitEvent(x.s, aux->fin, 0), "backward: stream wait"));
+  }
   return SLT_OK;
 }
 

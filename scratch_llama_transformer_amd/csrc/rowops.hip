@@ -1056,10 +1056,18 @@ int64_t norm_bwd_ws(int rows, int C) {
   return (int64_t)2 * nb * C * 4;
 }
 
+slt_status launch_norm_colsum(const void* ws, int rows, int C, float* dg, float* db, hipStream_t s, GradW gw) {
+  const int nb = std::max(1, std::min(kNormBwdBlocks, cdiv(rows, 4)));
+  const float* part = static_cast<const float*>(ws);
+  norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part, nb, C, dg, gw);
+  if (db) norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part + (int64_t)nb * C, nb, C, db, gw);
+  return check_launch("norm_colsum");
+}
+
 template <bool LN>
 static slt_status norm_bwd_common(const void* x, const void* g, const float* mean, const float* rstd,
                                   const void* dy, const void* dres, void* dx, float* dg, float* db, int rows,
-                                  int C, int dtype, void* ws, hipStream_t s, GradW gw) {
+                                  int C, int dtype, void* ws, hipStream_t s, GradW gw, bool defer_sums) {
   const int nb = std::max(1, std::min(kNormBwdBlocks, cdiv(rows, 4)));
   float* part = static_cast<float*>(ws);
   const size_t smem = (size_t)(LN ? 2 : 1) * C * sizeof(float);
@@ -1073,21 +1081,21 @@ static slt_status norm_bwd_common(const void* x, const void* g, const float* mea
     });
   };
   slt_status st = dtype == SLT_BF16 ? go(bf16{}) : go(float{});
-  if (st != SLT_OK) return st;
-  norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part, nb, C, dg, gw);
-  if (LN) norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part + (int64_t)nb * C, nb, C, db, gw);
-  return check_launch("norm_colsum");
+  if (st != SLT_OK || defer_sums) return st;
+  return launch_norm_colsum(ws, rows, C, dg, LN ? db : nullptr, s, gw);
 }
 
 slt_status launch_rmsnorm_bwd(const void* x, const void* g, const float* rstd, const void* dy, const void* dres,
-                              void* dx, float* dg, int rows, int C, int dtype, void* ws, hipStream_t s, GradW gw) {
-  return norm_bwd_common<false>(x, g, nullptr, rstd, dy, dres, dx, dg, nullptr, rows, C, dtype, ws, s, gw);
+                              void* dx, float* dg, int rows, int C, int dtype, void* ws, hipStream_t s, GradW gw,
+                              bool defer_sums) {
+  return norm_bwd_common<false>(x, g, nullptr, rstd, dy, dres, dx, dg, nullptr, rows, C, dtype, ws, s, gw,
+                                defer_sums);
 }
 
 slt_status launch_layernorm_bwd(const void* x, const void* gm, const float* mean, const float* rstd,
                                 const void* dy, const void* dres, void* dx, float* dgm, float* dbt, int rows,
-                                int C, int dtype, void* ws, hipStream_t s, GradW gw) {
-  return norm_bwd_common<true>(x, gm, mean, rstd, dy, dres, dx, dgm, dbt, rows, C, dtype, ws, s, gw);
+                                int C, int dtype, void* ws, hipStream_t s, GradW gw, bool defer_sums) {
+  return norm_bwd_common<true>(x, gm, mean, rstd, dy, dres, dx, dgm, dbt, rows, C, dtype, ws, s, gw, defer_sums);
 }
 
 slt_status launch_rope_table(int T_, int R, float base, float* cs, hipStream_t s) {

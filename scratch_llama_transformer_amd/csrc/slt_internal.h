@@ -260,14 +260,20 @@ slt_status launch_drop_apply(const void* g, void* out, int rows, int C, int dtyp
 int64_t norm_bwd_ws(int rows, int C);
 slt_status launch_rmsnorm_fwd(const void* x, const void* g, void* y, float* rstd, int rows, int C,
                               float eps, int dtype, hipStream_t s);
+// Norm backward: the row kernel writes dx and per-block partials of the gain
+// (and bias) gradients into ws; launch_norm_colsum reduces them, which the
+// launch does itself unless defer_sums (the caller then runs it, on any
+// stream ordered after this launch, before ws is reused).
+slt_status launch_norm_colsum(const void* ws, int rows, int C, float* dg, float* db, hipStream_t s, GradW gw);
 slt_status launch_rmsnorm_bwd(const void* x, const void* g, const float* rstd, const void* dy,
                               const void* dres, void* dx, float* dg, int rows, int C, int dtype,
-                              void* ws, hipStream_t s, GradW gw = {});
+                              void* ws, hipStream_t s, GradW gw = {}, bool defer_sums = false);
 slt_status launch_layernorm_fwd(const void* x, const void* gm, const void* bt, void* y, float* mean,
                                 float* rstd, int rows, int C, float eps, int dtype, hipStream_t s);
 slt_status launch_layernorm_bwd(const void* x, const void* gm, const float* mean, const float* rstd,
                                 const void* dy, const void* dres, void* dx, float* dgm, float* dbt,
-                                int rows, int C, int dtype, void* ws, hipStream_t s, GradW gw = {});
+                                int rows, int C, int dtype, void* ws, hipStream_t s, GradW gw = {},
+                                bool defer_sums = false);
 slt_status launch_rope_table(int T, int R, float base, float* cs, hipStream_t s);
 slt_status launch_swiglu_fwd(const void* a, const void* b, void* h, int rows, int F, int64_t lda,
                              int64_t ldb, int64_t ldh, int dtype, hipStream_t s);
