@@ -79,6 +79,33 @@ def test_full_step_parity(TS, ci, Bn, L):
     print(f"[result] {w.name} loss gpu {loss:.7f} oracle {ref['loss']:.7f}; tie-exempt weights {ties}")
 
 
+# The widest model the library accepts (C = 4096, 64 heads of 64): every norm,
+# GEMM and attention kernel at its largest row width, one layer, 64 tokens.
+MAX_WIDTH_CASES = [
+    dict(V=384, C=4096, H=64, Hkv=8, L=1, T=64, B=1, F=11008, R=64),
+    dict(V=384, C=4096, H=64, Hkv=64, L=1, T=64, B=1, F=4096, R=32),
+]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ci,over", [(4, MAX_WIDTH_CASES[0]), (5, MAX_WIDTH_CASES[1])])
+def test_full_step_at_maximum_width(TS, ci, over):
+    w = W.get_config(ci).with_(**over)
+    say("maximum-width step", w)
+    params, tokens, ts, loss = run_step(TS, w, 1700 + ci)
+    ref = O.train_step(w, params, tokens)
+    assert abs(loss - ref["loss"]) <= LOSS_TOL[w.act] * abs(ref["loss"]), (loss, ref["loss"])
+    grads = ts.unpack(ts.grads)
+    new = ts.unpack(ts.master)
+    _, ccache = O.forward(w, params, tokens, jitter=2.0 ** -24, seed=1)
+    comp = O.backward(w, ccache)
+    for name in params:
+        check_bf16_step_tensor(grads[name], ref["grads"][name], comp[name], f"grad {name}")
+        check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
+                                f"weight {name}", w.adam_eps)
+    print(f"[result] {w.name} C={w.C}: loss gpu {loss:.7f} oracle {ref['loss']:.7f}")
+
+
 @pytest.mark.timeout(900)
 def test_full_batch_step_one_layer(TS):
     """The d=384 workload's whole 64-sequence batch (16384 tokens) through one
