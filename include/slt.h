@@ -161,7 +161,15 @@ slt_status slt_forward_loss(const slt_config* cfg, const void* params, const int
                             void* acts, void* scratch, float* loss, void* stream);
 
 /* Backward pass after slt_forward_loss with the same params/tokens/acts.
- * grads: fp32 flat buffer in the parameter layout, every element written. */
+ * grads: fp32 flat buffer in the parameter layout, every element written.
+ * Besides `stream`, the call enqueues work on a second stream the library
+ * creates for the current device on first use (each layer's weight
+ * gradients, the norm-gain column sums, the token sort of the embedding
+ * gradient), ordered by events both ways: work enqueued on `stream` after
+ * the call runs after all of it, and the call's reads of acts/scratch/tokens
+ * happen after what `stream` held before it.  Several host threads may call
+ * it for one device; their enqueues take turns.  Results do not depend on
+ * the overlap (the same kernels in the same order). */
 slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t* tokens,
                         void* acts, void* scratch, float* grads, void* stream);
 
