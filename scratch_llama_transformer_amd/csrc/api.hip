@@ -180,7 +180,7 @@ static slt_status make_plan(const slt_config* cfg, Plan& p) {
     A.lse = take((int64_t)c.B * c.H * c.T * 4);
     A.ores = p.bf ? take(N * p.qd * es) : -1;  // bf16 rounding residual of the attention output
     // rotated hi/lo copies of q and k, made by the forward, reused by the backward
-    A.rot = flash_eligible(c.act, p.d) ? take(flash_rot_elems(c.B, c.T, c.H, c.Hkv) * 2) : -1;
+    A.rot = flash_eligible(c.act, p.d) ? take(flash_rot_elems(c.B, c.T, c.H, c.Hkv, p.d) * 2) : -1;
     if (p.llama) {
       A.qkv = take(N * p.qkv_w * es);
       A.o = take(N * p.qd * es);
@@ -672,7 +672,7 @@ static CachePlan cache_plan(const Plan& p, int B, int Tq, int Tmax) {
   q.ab = p.llama ? take(M * 2 * c.F * es) : -1;
   q.h = p.llama ? take(M * c.F * es) : -1;
   q.lse = take((int64_t)B * c.H * Tq * 4);
-  q.rot = flash_eligible(c.act, p.d) ? take(flash_rot_elems(B, Tq, c.H, c.Hkv) * 2) : -1;
+  q.rot = flash_eligible(c.act, p.d) ? take(flash_rot_elems(B, Tq, c.H, c.Hkv, p.d) * 2) : -1;
   q.part = take(decode_attention_ws(B, Tq, c.H, c.Hkv, p.d, Tmax));
   q.ws_bytes = a;
   return q;
@@ -979,7 +979,7 @@ static slt_status attn_check(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32
 
 static int64_t attn_rot_bytes(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t dtype) {
   if (B <= 0 || T <= 0 || H <= 0 || Hkv <= 0 || !flash_eligible(dtype, d)) return 0;
-  return a256(flash_rot_elems(B, T, H, Hkv) * 2);
+  return a256(flash_rot_elems(B, T, H, Hkv, d) * 2);
 }
 
 int64_t slt_attention_fwd_workspace(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t dtype) {

@@ -7,7 +7,7 @@
 // Work split:
 //  * fl_prep_k rotates q and k once (RoPE, fp32) and stores each rotated
 //    value as a bf16 pair hi + lo (lo = bf16(x - hi)) in head-major copies
-//    [B][heads][T][64], zero-padded to 64 dims; the query copy also carries
+//    [B][heads][T][d] (tiles zero-pad them to 64 dims); the query copy also carries
 //    the factor log2(e)/sqrt(d), so that q.k comes out as the score in base-2
 //    units the softmax exponentiates.  The attention kernels then
 //    only copy tiles: every tile (64 rows x 64 dims, 8 KiB) goes HBM -> LDS
@@ -47,7 +47,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int FD = 64;                // padded head dim of the rotated copies and of LDS tiles
+constexpr int FD = 64;                // padded head dim of LDS tiles
 constexpr int FR = 64;                // rows per tile and per workgroup
 constexpr int FTB = FR * FD * 2;      // bytes per LDS tile (8 KiB)
 constexpr int FS = FD + 4;            // fp32 row stride of the epilogue staging tile
@@ -275,18 +275,18 @@ __global__ __launch_bounds__(128) void fl_prep_k(const bf16* __restrict__ q, int
                                                  int64_t ldk, bf16* qh, bf16* ql, bf16* kh, bf16* kl, int B, int T,
                                                  int H, int Hkv, int d, int R, int mode, const float* cs,
                                                  float qscale) {
-  // grid (B T, ceil(8 (H + Hkv) / 128)): one token per block row, one
+  // grid (B T, ceil(d/8 (H + Hkv) / 128)): one token per block row, one
   // (head slot, 8-dim chunk) per thread
-  const int slots = H + Hkv;
+  const int slots = H + Hkv, nch = d / 8;
   const int j = blockIdx.y * blockDim.x + threadIdx.x;
-  if (j < slots * 8) {
-    const int c = j & 7;
-    const int slot = j >> 3;
+  if (j < slots * nch) {
+    const int c = j % nch;
+    const int slot = j / nch;
     const int64_t bt = blockIdx.x;
     const int t = (int)(bt % T), b = (int)(bt / T);
     const bool isq = slot < H;
     const int hd = isq ? slot : slot - H;
-    const int64_t drow = ((int64_t)(b * (isq ? H : Hkv) + hd) * T + t) * FD + c * 8;
+    const int64_t drow = ((int64_t)(b * (isq ? H : Hkv) + hd) * T + t) * d + c * 8;
     bf16* dh = (isq ? qh : kh) + drow;
     bf16* dl = (isq ? ql : kl) + drow;
     uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
@@ -404,11 +404,15 @@ __global__ __launch_bounds__(256, 2) void fl_fwd2_k(FlArgs a) {
     const int qc = min(c0 + 16 * (wave + 4 * i) + li, T - 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      qh[i][s] = *reinterpret_cast<const u32x4*>(a.qh + (qb + qc) * FD + 32 * s + 8 * g);
-      ql[i][s] = *reinterpret_cast<const u32x4*>(a.ql + (qb + qc) * FD + 32 * s + 8 * g);
+      const int j0 = 32 * s + 8 * g;
+      qh[i][s] = ql[i][s] = u32x4{0u, 0u, 0u, 0u};
+      if (j0 < a.d) {
+        qh[i][s] = *reinterpret_cast<const u32x4*>(a.qh + (qb + qc) * a.d + j0);
+        ql[i][s] = *reinterpret_cast<const u32x4*>(a.ql + (qb + qc) * a.d + j0);
+      }
     }
   }
-  const int64_t kbase = (int64_t)(b * a.Hkv + kvh) * T * FD;
+  const int64_t kbase = (int64_t)(b * a.Hkv + kvh) * T * a.d;
   const bf16* kh = a.kh + kbase;
   const bf16* kl = a.kl + kbase;
   const bf16* vb = a.v + (int64_t)b * T * a.ldv + (int64_t)kvh * a.d;
@@ -426,8 +430,8 @@ __global__ __launch_bounds__(256, 2) void fl_fwd2_k(FlArgs a) {
   // key tiles 0 .. nt-1 cover keys up to the chunk's last query
   const int nt = (min(T, c0 + FC) + FR - 1) / FR;
   auto issue = [&](int j, char* st) {
-    fl_issue(kh, FD, j * FR, T, 8, st, wave, lane);
-    fl_issue(kl, FD, j * FR, T, 8, st + FTB, wave, lane);
+    fl_issue(kh, a.d, j * FR, T, nch, st, wave, lane);
+    fl_issue(kl, a.d, j * FR, T, nch, st + FTB, wave, lane);
     fl_issue(vb, a.ldv, j * FR, T, nch, st + 2 * FTB, wave, lane);
   };
   issue(0, lds[0]);
@@ -622,15 +626,18 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
   const int nch = a.d / 8;
   const FlOff off(lane);
 
-  const int64_t qrow = ((int64_t)(b * a.H + h) * T + qc) * FD;
+  const int64_t qrow = ((int64_t)(b * a.H + h) * T + qc) * a.d;
   u32x4 qh[2], ql[2], gf[2];
   float D = 0.f;
   const int64_t tok = (int64_t)b * T + qc;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    qh[s] = *reinterpret_cast<const u32x4*>(a.qh + qrow + 32 * s + 8 * g);
-    ql[s] = *reinterpret_cast<const u32x4*>(a.ql + qrow + 32 * s + 8 * g);
     const int j0 = 32 * s + 8 * g;
+    qh[s] = ql[s] = u32x4{0u, 0u, 0u, 0u};
+    if (j0 < a.d) {
+      qh[s] = *reinterpret_cast<const u32x4*>(a.qh + qrow + j0);
+      ql[s] = *reinterpret_cast<const u32x4*>(a.ql + qrow + j0);
+    }
     gf[s] = u32x4{0u, 0u, 0u, 0u};
     if (j0 < a.d) {
       const int64_t col = (int64_t)h * a.d + j0;
@@ -651,7 +658,7 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
   const float lse2 = a.lse_in[((int64_t)b * a.H + h) * T + qc] * kLog2e;
   if (g == 0 && qi < T) a.delta[((int64_t)b * a.H + h) * T + qi] = D;
 
-  const int64_t kbase = (int64_t)(b * a.Hkv + kvh) * T * FD;
+  const int64_t kbase = (int64_t)(b * a.Hkv + kvh) * T * a.d;
   const bf16* kh = a.kh + kbase;
   const bf16* kl = a.kl + kbase;
   const bf16* vb = a.v + (int64_t)b * T * a.ldv + (int64_t)kvh * a.d;
@@ -661,8 +668,8 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nt = qt + 1;
-  fl_issue(kh, FD, 0, T, 8, lds[0], wave, lane);
-  fl_issue(kl, FD, 0, T, 8, lds[0] + FTB, wave, lane);
+  fl_issue(kh, a.d, 0, T, nch, lds[0], wave, lane);
+  fl_issue(kl, a.d, 0, T, nch, lds[0] + FTB, wave, lane);
   fl_issue(vb, a.ldv, 0, T, nch, lds[0] + 2 * FTB, wave, lane);
   for (int kt = 0; kt < nt; ++kt) {
     SLT_WAIT_VMCNT(0);
@@ -670,8 +677,8 @@ __global__ __launch_bounds__(256) void fl_dq_k(FlArgs a) {
     if (kt + 1 < nt) {
       char* nx = lds[(kt + 1) & 1];
       const int r0 = (kt + 1) * FR;
-      fl_issue(kh, FD, r0, T, 8, nx, wave, lane);
-      fl_issue(kl, FD, r0, T, 8, nx + FTB, wave, lane);
+      fl_issue(kh, a.d, r0, T, nch, nx, wave, lane);
+      fl_issue(kl, a.d, r0, T, nch, nx + FTB, wave, lane);
       fl_issue(vb, a.ldv, r0, T, nch, nx + 2 * FTB, wave, lane);
     }
     const unsigned base = lds_off(lds[kt & 1]);
@@ -768,15 +775,18 @@ __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
   const int nch = a.d / 8;
   const FlOff off(lane);
 
-  const int64_t krow = ((int64_t)(b * a.Hkv + kvh) * T + kc) * FD;
+  const int64_t krow = ((int64_t)(b * a.Hkv + kvh) * T + kc) * a.d;
   u32x4 kh[2], kl[2], vf[2];
   const bf16* vrow = a.v + ((int64_t)b * T + kc) * a.ldv + (int64_t)kvh * a.d;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    kh[s] = *reinterpret_cast<const u32x4*>(a.kh + krow + 32 * s + 8 * g);
-    kl[s] = *reinterpret_cast<const u32x4*>(a.kl + krow + 32 * s + 8 * g);
     const int j0 = 32 * s + 8 * g;
-    vf[s] = j0 < a.d ? *reinterpret_cast<const u32x4*>(vrow + j0) : u32x4{0u, 0u, 0u, 0u};
+    kh[s] = kl[s] = vf[s] = u32x4{0u, 0u, 0u, 0u};
+    if (j0 < a.d) {
+      kh[s] = *reinterpret_cast<const u32x4*>(a.kh + krow + j0);
+      kl[s] = *reinterpret_cast<const u32x4*>(a.kl + krow + j0);
+      vf[s] = *reinterpret_cast<const u32x4*>(vrow + j0);
+    }
   }
 
   f32x4 dva[4], dka[4];
@@ -791,9 +801,9 @@ __global__ __launch_bounds__(256) void fl_dkdv_k(FlArgs a) {
   const int nsteps = G * per;
   auto issue = [&](int n, char* st) {
     const int hh = kvh * G + n / per, qt = kt + n % per;
-    const int64_t hb = (int64_t)(b * a.H + hh) * T * FD;
-    fl_issue(a.qh + hb, FD, qt * FR, T, 8, st, wave, lane);
-    fl_issue(a.ql + hb, FD, qt * FR, T, 8, st + FTB, wave, lane);
+    const int64_t hb = (int64_t)(b * a.H + hh) * T * a.d;
+    fl_issue(a.qh + hb, a.d, qt * FR, T, nch, st, wave, lane);
+    fl_issue(a.ql + hb, a.d, qt * FR, T, nch, st + FTB, wave, lane);
     fl_issue(a.dout + (int64_t)b * T * a.lddo + (int64_t)hh * a.d, a.lddo, qt * FR, T, nch, st + 2 * FTB, wave,
              lane);
   };
@@ -988,14 +998,17 @@ __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int kc_ = min(k0 + 16 * (wave + 8 * i) + li, T - 1);
-    const int64_t krow = ((int64_t)(b * a.Hkv + kvh) * T + kc_) * FD;
+    const int64_t krow = ((int64_t)(b * a.Hkv + kvh) * T + kc_) * a.d;
     const bf16* vrow = a.v + ((int64_t)b * T + kc_) * a.ldv + (int64_t)kvh * a.d;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      kh[i][s] = *reinterpret_cast<const u32x4*>(a.kh + krow + 32 * s + 8 * g);
-      kl[i][s] = *reinterpret_cast<const u32x4*>(a.kl + krow + 32 * s + 8 * g);
       const int j0 = 32 * s + 8 * g;
-      vf[i][s] = j0 < a.d ? *reinterpret_cast<const u32x4*>(vrow + j0) : u32x4{0u, 0u, 0u, 0u};
+      kh[i][s] = kl[i][s] = vf[i][s] = u32x4{0u, 0u, 0u, 0u};
+      if (j0 < a.d) {
+        kh[i][s] = *reinterpret_cast<const u32x4*>(a.kh + krow + j0);
+        kl[i][s] = *reinterpret_cast<const u32x4*>(a.kl + krow + j0);
+        vf[i][s] = *reinterpret_cast<const u32x4*>(vrow + j0);
+      }
     }
   }
   f32x4 dva[2][4], dka[2][4];
@@ -1014,8 +1027,8 @@ __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
   auto issue = [&](int n, char* st) {
     const int hh = kvh * G + n / per, qt = qt0 + n % per;
     const int64_t hb = (int64_t)(b * a.H + hh) * T;
-    fl_issue8(a.qh + hb * FD, FD, qt * FR, T, 8, st, wave, lane);
-    fl_issue8(a.ql + hb * FD, FD, qt * FR, T, 8, st + FTB, wave, lane);
+    fl_issue8(a.qh + hb * a.d, a.d, qt * FR, T, nch, st, wave, lane);
+    fl_issue8(a.ql + hb * a.d, a.d, qt * FR, T, nch, st + FTB, wave, lane);
     fl_issue8(a.dout + (int64_t)b * T * a.lddo + (int64_t)hh * a.d, a.lddo, qt * FR, T, nch, st + 2 * FTB, wave,
               lane);
     if (wave == 0) {  // lse then D of the 64 rows: 16 + 16 chunks (lanes 32..63 repeat into the pad)
@@ -1155,7 +1168,7 @@ inline bool al(const void* p, int n) { return reinterpret_cast<uintptr_t>(p) % n
 
 FlArgs to_fl(const AttnArgs& a) {
   FlArgs f{};
-  const int64_t nq = (int64_t)a.B * a.H * a.T * FD, nk = (int64_t)a.B * a.Hkv * a.T * FD;
+  const int64_t nq = (int64_t)a.B * a.H * a.T * a.d, nk = (int64_t)a.B * a.Hkv * a.T * a.d;
   bf16* rot = static_cast<bf16*>(a.rot);
   f.qh = rot;
   f.ql = rot + nq;
@@ -1193,7 +1206,7 @@ FlArgs to_fl(const AttnArgs& a) {
 }
 
 slt_status prep(const AttnArgs& a, const FlArgs& f, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.B * a.T), (unsigned)(((a.H + a.Hkv) * 8 + 127) / 128));
+  const dim3 grid((unsigned)((int64_t)a.B * a.T), (unsigned)(((a.H + a.Hkv) * (a.d / 8) + 127) / 128));
   const bool vec = al(a.q, 16) && al(a.k, 16) && a.ldq % 8 == 0 && a.ldk % 8 == 0 && (a.R == 0 || a.cs != nullptr) &&
                    (a.R == 0 || (a.rope_mode == SLT_ROPE_HALF ? (a.R / 2) % 8 == 0 : a.R % 8 == 0));
   auto* kern = vec ? fl_prep_k<true> : fl_prep_k<false>;
@@ -1206,7 +1219,7 @@ slt_status prep(const AttnArgs& a, const FlArgs& f, hipStream_t s) {
 
 }  // namespace
 
-int64_t flash_rot_elems(int B, int T, int H, int Hkv) { return 2 * (int64_t)B * (H + Hkv) * T * FD; }
+int64_t flash_rot_elems(int B, int T, int H, int Hkv, int d) { return 2 * (int64_t)B * (H + Hkv) * T * d; }
 
 bool flash_eligible(int dtype, int d) { return dtype == SLT_BF16 && d > 0 && d % 16 == 0 && d <= FD; }
 

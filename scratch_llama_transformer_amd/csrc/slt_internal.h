@@ -317,7 +317,7 @@ slt_status launch_attention_bwd(const AttnArgs& a, hipStream_t s);
 int64_t attention_bwd_ws(int B, int H, int T);
 // bf16 attention with pre-rotated q/k copies and LDS tiles copied straight
 // from HBM (flash.hip)
-int64_t flash_rot_elems(int B, int T, int H, int Hkv);
+int64_t flash_rot_elems(int B, int T, int H, int Hkv, int d);
 bool flash_eligible(int dtype, int d);
 bool flash_ok(const AttnArgs& a, bool bwd);
 slt_status flash_fwd(const AttnArgs& a, hipStream_t s);

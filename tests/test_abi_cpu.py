@@ -119,7 +119,7 @@ def test_host_calls_reject_bad_arguments_before_launch():
     assert lib.slt_attention_fwd(None, None, None, None, None, None, 8, 8, 8, 8, 1, 4, 2, 1, 128, 0, 0, None, 1,
                                  None, None) == 2
     # a bf16 head dim the rotated-copy path takes needs its workspace
-    assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 48, 1) == 2 * 2 * 6 * 64 * 64 * 2
+    assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 48, 1) == 2 * 2 * 6 * 64 * 48 * 2
     assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 48, 0) == 0
     assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 24, 1) == 0
     assert B.slt_attention_bwd_workspace(2, 64, 4, 2, 24, 1) == 2 * 4 * 64 * 4
