@@ -617,8 +617,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_k(const T* __restrict__ a, con
   }
 }
 
-constexpr float kGeluK = 0.7978845608028654f;  // sqrt(2/pi)
-constexpr float kGeluC = 0.044715f;
 
 template <typename T, int VEC>
 __global__ __launch_bounds__(256) void gelu_fwd_k(const T* __restrict__ a, T* __restrict__ u, int rows, int F,
@@ -652,10 +650,7 @@ __global__ __launch_bounds__(256) void gelu_bwd_k(const T* __restrict__ a, const
     load_f<T, VEC>(du + r * lddu + c, gv);
 #pragma unroll
     for (int q = 0; q < VEC; ++q) {
-      const float x = av[q];
-      const float t = tanhf(kGeluK * (x + kGeluC * x * x * x));
-      const float dt = (1.0f - t * t) * kGeluK * (1.0f + 3.0f * kGeluC * x * x);
-      out[q] = gv[q] * (0.5f * (1.0f + t) + 0.5f * x * dt);
+      out[q] = gv[q] * gelu_tanh_grad(av[q]);
     }
     store_f<T, VEC>(da + r * ldda + c, out);
   }

@@ -157,9 +157,19 @@ __device__ __forceinline__ void swiglu_grad(float a, float b, float dh, float& d
   da = dh * b * sg * (1.0f + a * (1.0f - sg));
 }
 
-// GELU, tanh form (the GPT-2 / CodeGen family's).
-__device__ __forceinline__ float gelu_tanh(float x) {
-  return 0.5f * x * (1.0f + tanhf(0.7978845608028654f * (x + 0.044715f * x * x * x)));
+// GELU, tanh form (the GPT-2 / CodeGen family's): 0.5 x (1 + tanh(y)),
+// y = sqrt(2/pi) (x + 0.044715 x^3), evaluated as x sigmoid(2y) -- the same
+// function with one exponential and one reciprocal instead of a tanh (the
+// element kernels are otherwise bound by its instruction count).  Derivative:
+// s + x s (1 - s) 2 sqrt(2/pi) (1 + 3 * 0.044715 x^2), s = sigmoid(2y).
+__device__ __forceinline__ float gelu_sig(float x) {
+  const float y2 = 1.5957691216057308f * (x + 0.044715f * x * x * x);
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-y2));
+}
+__device__ __forceinline__ float gelu_tanh(float x) { return x * gelu_sig(x); }
+__device__ __forceinline__ float gelu_tanh_grad(float x) {
+  const float s = gelu_sig(x);
+  return s + 1.5957691216057308f * x * (1.0f + 0.134145f * x * x) * s * (1.0f - s);
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
