@@ -290,6 +290,51 @@ def test_step_is_deterministic(TS):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.timeout(300)
+def test_backward_from_two_host_threads(TS):
+    """Two models stepped from two host threads at once, each on its own
+    torch stream: the backward's second stream and events are shared per
+    device (enqueues take turns), and every gradient equals the one a single
+    thread computes."""
+    import threading
+    cases = [W.get_config(3).with_(B=2, L=2, T=128), W.get_config(5).with_(B=1, L=1, T=256)]
+    toks = [torch.from_numpy(W.make_tokens(w, 31 + i)).cuda() for i, w in enumerate(cases)]
+    params = [W.make_params(w, 31 + i) for i, w in enumerate(cases)]
+    ref = []
+    for w, p, tok in zip(cases, params, toks):
+        ts = TS(w, params=p)
+        ts.forward(tok)
+        ts.backward(tok)
+        torch.cuda.synchronize()
+        ref.append(ts.grads.clone())
+    steppers = [TS(w, params=p) for w, p in zip(cases, params)]
+    torch.cuda.synchronize()  # their set-up ran on the default stream
+    got, errors = [None, None], []
+
+    def run(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                from scratch_llama_transformer_amd import binding as B
+                ts = steppers[i]
+                for _ in range(3):
+                    B.slt_forward_loss(ts.cfg, ts.compute_params, toks[i], ts.acts, ts.scratch, ts.loss, s)
+                    B.slt_backward(ts.cfg, ts.compute_params, toks[i], ts.acts, ts.scratch, ts.grads, s)
+                s.synchronize()
+                got[i] = ts.grads.clone()
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    th = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors
+    for i in range(2):
+        assert torch.equal(got[i], ref[i]), i
+
+
 @pytest.mark.parametrize("ci", [3, 5])
 def test_full_size_forward_rows_match_oracle_on_sampled_sequences(TS, ci):
     """At the full benchmark shape, the per-position losses of a few sampled
