@@ -430,14 +430,15 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
   return SLT_OK;
 }
 
-// A second stream per device for the layer weight gradients (and the token
-// sort of the embedding gradient), and the events that order it against the
-// backward walk's stream: `ready` is recorded on the walk's stream before
-// each launch, done[k] after the launch that reads buffer set k, sort_done
-// after the sort, fin after the last launch of a walk.  Created on first use (default priority, non-blocking);
-// host calls that enqueue backward walks on one device take turns (mutex),
-// so an event is never re-recorded before the waits on its last record are
-// enqueued.
+// A second stream per device for the work of the backward that nothing in
+// the walk reads (the layer weight gradients, the norm-gain column sums, the
+// token sort of the embedding gradient), and the events that order it
+// against the walk's stream: `ready` is recorded on the walk's stream before
+// each launch there, done[k] after the launch that reads buffer set k,
+// sort_done after the sort, fin after the last launch of a walk.  Created on
+// first use (default priority, non-blocking); host calls that enqueue
+// backward walks on one device take turns (mutex), so an event is never
+// re-recorded before the waits on its last record are enqueued.
 struct DwStream {
   hipStream_t s = nullptr;
   hipEvent_t ready = nullptr, done[3] = {nullptr, nullptr, nullptr}, sort_done = nullptr, fin = nullptr;
@@ -456,8 +457,10 @@ static DwStream* dw_stream() {
     for (int k = 0; k < 3 && ok; ++k) ok = hipEventCreateWithFlags(&a.done[k], hipEventDisableTiming) == hipSuccess;
     ok = ok && hipEventCreateWithFlags(&a.sort_done, hipEventDisableTiming) == hipSuccess;
     ok = ok && hipEventCreateWithFlags(&a.fin, hipEventDisableTiming) == hipSuccess;
-    if (!ok) a = DwStream{};  // fall back to the walk's stream (what was created stays until exit)
-    (void)hipGetLastError();
+    if (!ok) {  // fall back to the walk's stream (what was created stays until exit)
+      a = DwStream{};
+      (void)hipGetLastError();
+    }
     it = per_dev.emplace(dev, a).first;
   }
   return it->second.s ? &it->second : nullptr;
