@@ -173,6 +173,22 @@ slt_status slt_forward_loss(const slt_config* cfg, const void* params, const int
 slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t* tokens,
                         void* acts, void* scratch, float* grads, void* stream);
 
+/* slt_backward followed by the AdamW update of slt_adamw_step (no gradient
+ * scale), fused: each layer's parameters are updated as soon as its
+ * gradients are final, on the library's second stream while the walk goes
+ * through the layers below (the final norm and lm_head after the last
+ * layer's weight gradients, the embedding table last).  grads, master,
+ * shadow (bf16 configurations; NULL for fp32), m, v and decay_mask (or
+ * NULL) are the buffers of slt_adamw_step over the whole layout, with the
+ * same alignment; t, lr, beta1, beta2, eps, wd as there.  Results equal
+ * slt_backward then slt_adamw_step bit for bit.  For clipped steps (the
+ * factor needs the whole gradient) use the separate calls. */
+slt_status slt_backward_adamw(const slt_config* cfg, const void* params, const int32_t* tokens,
+                              void* acts, void* scratch, float* grads, float* master,
+                              uint16_t* shadow, float* m, float* v, int64_t t, float lr, float beta1,
+                              float beta2, float eps, float wd, const uint8_t* decay_mask,
+                              void* stream);
+
 /* Gradient accumulation over micro-batches (Transformer in Rust,
  * "Configuration" and "Features": forward passes per optimizer step): the
  * same backward, but grads += scale * (gradient of this micro-batch's mean

@@ -67,6 +67,7 @@ SIGNATURES = {
     "slt_adamw_step": (_I32, [_I64, _P, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P, _P]),
     "slt_clip_workspace_bytes": (_I64, []),
     "slt_clip_grad_norm": (_I32, [_I64, _P, _I32, _F, _P, _P, _P, _P]),
+    "slt_backward_adamw": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _P, _P]),
     "slt_gemm": (_I32, [_I32, _I32, _I32, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _P, _I64,
                         _I32, _I32, _P, _I64, _P]),
     "slt_mlp_swiglu_fwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _I32, _P]),
@@ -207,6 +208,13 @@ def slt_cast_bf16(src, dst, n, stream=None):
 def slt_forward_loss(cfg, params, tokens, acts, scratch, loss, stream=None):
     _check("slt_forward_loss", load().slt_forward_loss(ct.byref(cfg), _ptr(params), _ptr(tokens), _ptr(acts),
                                                        _ptr(scratch), _ptr(loss), _stream(stream)))
+
+
+def slt_backward_adamw(cfg, params, tokens, acts, scratch, grads, master, shadow, m, v, t, lr, beta1, beta2, eps,
+                       wd, decay_mask=None, stream=None):
+    _check("slt_backward_adamw", load().slt_backward_adamw(
+        ct.byref(cfg), _ptr(params), _ptr(tokens), _ptr(acts), _ptr(scratch), _ptr(grads), _ptr(master),
+        _ptr(shadow), _ptr(m), _ptr(v), t, lr, beta1, beta2, eps, wd, _ptr(decay_mask), _stream(stream)))
 
 
 def slt_backward(cfg, params, tokens, acts, scratch, grads, stream=None):

@@ -470,7 +470,19 @@ static slt_status hip_ok(hipError_t e, const char* what) {
   return e == hipSuccess ? SLT_OK : fail(SLT_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, float* grads) {
+// AdamW folded into the backward (slt_backward_adamw): each layer's update
+// is enqueued as soon as its gradients are final.
+struct AdamArgs {
+  float* master;
+  uint16_t* shadow;
+  float *m, *v;
+  int64_t t;
+  float lr, b1, b2, eps, wd;
+  const uint8_t* mask;
+};
+
+static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, float* grads,
+                           const AdamArgs* opt = nullptr) {
   const slt_config& c = p.c;
   const int N = p.N, C = c.C;
   const int64_t ldt = c.T + 1;
@@ -502,6 +514,16 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     return launch_norm_colsum(nws(k), N, C, dg, db, aux->s, x.gw);
   };
   const bool defer = aux != nullptr;
+  // AdamW over parameters [off, end) on stream s (ranges start on 4-element
+  // boundaries, or one update of the whole buffer runs at the end)
+  bool ranges_ok = opt != nullptr && p.lp[0].norm1 % 4 == 0 && p.normf % 4 == 0;
+  for (int l = 0; l < c.L && ranges_ok; ++l) ranges_ok = p.lp[l].norm1 % 4 == 0;
+  auto adam = [&](int64_t off, int64_t end, hipStream_t s) -> slt_status {
+    if (!opt || !ranges_ok || end <= off) return SLT_OK;
+    return launch_adamw(end - off, opt->master + off, opt->shadow ? opt->shadow + off : nullptr, grads + off,
+                        opt->m + off, opt->v + off, opt->t, opt->lr, opt->b1, opt->b2, opt->eps, opt->wd,
+                        opt->mask ? opt->mask + off : nullptr, nullptr, s);
+  };
   auto launch_dw = [&](int k) -> slt_status {
     if (aux) {
       SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
@@ -592,11 +614,13 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(launch_attention_bwd(at, x.s));
       dws.add(N, p.qkv_w, C, dqkv, p.qkv_w, x.A(A.n1), C, grads + W.qkvw, C);
       SLT_TRY(launch_dw(sl));
+      if (l == c.L - 1) SLT_TRY(adam(p.normf, p.n_params, xw.s));  // final norm and lm_head are final
       SLT_TRY(proj_dx(x, N, p.qkv_w, C, dqkv, p.qkv_w, x.P(W.qkvw), C, dn, C));
       SLT_TRY(wait_set(si));
       SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l]), x.P(W.norm1), (const float*)x.A(A.r1), dn, dx2, dxi,
                                  grads + W.norm1, N, C, x.dt, nws(2 * l + 2), x.s, x.gw, defer));
       SLT_TRY(norm_sums(2 * l + 2, grads + W.norm1, nullptr));
+      SLT_TRY(adam(W.norm1, l + 1 < c.L ? p.lp[l + 1].norm1 : p.normf, xw.s));  // the layer's gradients are final
     } else {
       char* ou = (char*)x.A(A.o);
       // x_out = x_in + drop([o | u] W_out^T)
@@ -618,23 +642,29 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(launch_attention_bwd(at, x.s));
       dws.add(N, p.in_w, C, dbig, p.in_w, x.A(A.n1), C, grads + W.qkvw, C);
       SLT_TRY(launch_dw(sl));
+      if (l == c.L - 1) SLT_TRY(adam(p.normf, p.n_params, xw.s));  // final norm and lm_head are final
       SLT_TRY(proj_dx(x, N, p.in_w, C, dbig, p.in_w, x.P(W.qkvw), C, dn, C));
       SLT_TRY(wait_set(si));
       SLT_TRY(launch_layernorm_bwd(x.A(p.xs[l]), x.P(W.norm1), (const float*)x.A(A.mu1), (const float*)x.A(A.r1),
                                    dn, dx, dxi, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws(2 * l + 2), x.s,
                                    x.gw, defer));
       SLT_TRY(norm_sums(2 * l + 2, grads + W.norm1, grads + W.norm1b));
+      SLT_TRY(adam(W.norm1, l + 1 < c.L ? p.lp[l + 1].norm1 : p.normf, xw.s));  // the layer's gradients are final
     }
   }
   if (sort_ahead) SLT_TRY(hip_ok(hipStreamWaitEvent(x.s, aux->sort_done, 0), "backward: stream wait"));
   SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, x.S(p.dx[2]), grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s,
                                x.gw, make_drop(c, 0, 0), sort_ahead));
+  SLT_TRY(adam(p.wte, p.lp[0].norm1, x.s));
   // the walk's stream ends after everything on the second stream (in order
   // there, so one event after the last launch covers it all)
   if (aux) {
     SLT_TRY(hip_ok(hipEventRecord(aux->fin, aux->s), "backward: event record"));
     SLT_TRY(hip_ok(hipStreamWaitEvent(x.s, aux->fin, 0), "backward: stream wait"));
   }
+  if (opt && !ranges_ok)  // offsets not on 4-element boundaries: one update at the end
+    SLT_TRY(launch_adamw(p.n_params, opt->master, opt->shadow, grads, opt->m, opt->v, opt->t, opt->lr, opt->b1,
+                         opt->b2, opt->eps, opt->wd, opt->mask, nullptr, x.s));
   return SLT_OK;
 }
 
@@ -835,6 +865,27 @@ slt_status slt_backward(const slt_config* cfg, const void* params, const int32_t
   if (!params || !tokens || !acts || !scratch || !grads) return fail(SLT_EINVAL, "backward: NULL pointer");
   Ctx x{p, as_stream(stream), (char*)acts, (char*)scratch, (const char*)params, cfg->act};
   return backward(p, x, tokens, grads);
+}
+
+slt_status slt_backward_adamw(const slt_config* cfg, const void* params, const int32_t* tokens, void* acts,
+                              void* scratch, float* grads, float* master, uint16_t* shadow, float* m, float* v,
+                              int64_t t, float lr, float beta1, float beta2, float eps, float wd,
+                              const uint8_t* decay_mask, void* stream) {
+  Plan p;
+  SLT_TRY(make_plan(cfg, p));
+  if (!params || !tokens || !acts || !scratch || !grads || !master || !m || !v)
+    return fail(SLT_EINVAL, "backward_adamw: NULL pointer");
+  if (cfg->act == SLT_BF16 && !shadow) return fail(SLT_EINVAL, "backward_adamw: bf16 configurations need the shadow");
+  if (t < 1) return fail(SLT_EINVAL, "backward_adamw: t must be >= 1");
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps >= 0.f))
+    return fail(SLT_EINVAL, "backward_adamw: betas must lie in [0, 1) and eps >= 0");
+  auto al16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  if (!al16(master) || !al16(grads) || !al16(m) || !al16(v) || (shadow && reinterpret_cast<uintptr_t>(shadow) % 8) ||
+      (decay_mask && reinterpret_cast<uintptr_t>(decay_mask) % 4))
+    return fail(SLT_EINVAL, "backward_adamw: buffers must be 16-byte aligned (shadow 8, mask 4)");
+  Ctx x{p, as_stream(stream), (char*)acts, (char*)scratch, (const char*)params, cfg->act};
+  const AdamArgs opt{master, shadow, m, v, t, lr, beta1, beta2, eps, wd, decay_mask};
+  return backward(p, x, tokens, grads, &opt);
 }
 
 slt_status slt_backward_accumulate(const slt_config* cfg, const void* params, const int32_t* tokens, void* acts,

@@ -96,10 +96,25 @@ class TrainStep:
         key: the backward regenerates the forward's masks from it)."""
         self.cfg.dropout_seed = (self.cfg.dropout_seed + 1) & 0xFFFFFFFFFFFFFFFF
 
+    def backward_adamw(self, tokens: torch.Tensor, lr=None, wd=None) -> None:
+        """The backward with AdamW folded in (slt_backward_adamw): each
+        layer's update runs as soon as its gradients are final; the same
+        result as backward() then adamw() without clipping."""
+        self.t += 1
+        w = self.w
+        B.slt_backward_adamw(self.cfg, self.compute_params, tokens, self.acts, self.scratch, self.grads, self.master,
+                             self.shadow, self.m, self.v, self.t, w.lr if lr is None else lr, w.beta1, w.beta2,
+                             w.adam_eps, w.wd if wd is None else wd)
+
+    fuse_adamw = True  # step() folds AdamW into the backward when there is no clipping
+
     def step(self, tokens: torch.Tensor) -> None:
         self.forward(tokens)
-        self.backward(tokens)
-        self.adamw()
+        if self.clip is None and self.fuse_adamw:
+            self.backward_adamw(tokens)
+        else:
+            self.backward(tokens)
+            self.adamw()
         if self.cfg.dropout > 0:
             self.next_masks()
 

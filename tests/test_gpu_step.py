@@ -291,6 +291,32 @@ def test_step_is_deterministic(TS):
 
 
 @pytest.mark.timeout(300)
+@pytest.mark.parametrize("ci,over", [(1, {}), (3, dict(B=4, L=2)), (5, dict(B=1, L=1, T=256)),
+                                     (2, dict(B=2, L=2, dropout=0.125, dropout_seed=5))])
+def test_backward_adamw_equals_separate_calls(TS, ci, over):
+    """slt_backward_adamw (each layer's update enqueued as its gradients
+    become final) against slt_backward then slt_adamw_step: gradients,
+    master weights, moments and the bf16 copy bitwise equal over two steps."""
+    w = W.get_config(ci).with_(**over)
+    say("fused AdamW", w)
+    params = W.make_params(w, 41 + ci)
+    tok = torch.from_numpy(W.make_tokens(w, 41 + ci)).cuda()
+    a, b = TS(w, params=params), TS(w, params=params)
+    for _ in range(2):
+        a.forward(tok)
+        a.backward(tok)
+        a.adamw()
+        b.forward(tok)
+        b.backward_adamw(tok)
+    torch.cuda.synchronize()
+    for name in ("grads", "master", "m", "v", "shadow"):
+        x, y = getattr(a, name), getattr(b, name)
+        assert (x is None) == (y is None), name
+        if x is not None:
+            assert torch.equal(x, y), name
+
+
+@pytest.mark.timeout(300)
 def test_backward_from_two_host_threads(TS):
     """Two models stepped from two host threads at once, each on its own
     torch stream: the backward's second stream and events are shared per
