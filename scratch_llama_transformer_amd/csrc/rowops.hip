@@ -444,23 +444,30 @@ __global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const
                                                   const T* __restrict__ dy, const T* dres, T* dx,
                                                   float* __restrict__ part, int rows, int C) {
   extern __shared__ float red[];  // [C] (x2 for LayerNorm)
+  using P = Pack<T, VEC>;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  float pg[NCH][VEC], pb[NCH][VEC], gv[NCH][VEC];
+  float pg[NCH][VEC], pb[NCH][VEC];
+  P gp[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = (lane + j * kWave) * VEC;
 #pragma unroll
-    for (int q = 0; q < VEC; ++q) pg[j][q] = pb[j][q] = gv[j][q] = 0.f;
-    if (c < C) load_f<T, VEC>(g + c, gv[j]);
+    for (int q = 0; q < VEC; ++q) pg[j][q] = pb[j][q] = 0.f;
+    gp[j] = c < C ? *reinterpret_cast<const P*>(g + c) : P{};
   }
 
-  // Four rows per iteration, every load of them issued before any use, so
-  // that each wave keeps four rows of x, dy and the incoming gradient in
-  // flight (the grid is small: its block count sets the number of dg partials).
-  constexpr int RP = 4;
+  // RP rows per iteration, every load of them issued before any use, so that
+  // each wave keeps RP rows of x, dy and the incoming gradient in flight (the
+  // grid is small: its block count sets the number of dg partials).  The rows
+  // stay in registers as loaded (bf16 where T is bf16) and are widened where
+  // used, so that wide rows do not push the kernel to one wave per SIMD.  A
+  // wave visits rows blockIdx*4 + wave + m*step in increasing m whatever RP is,
+  // so the partial sums do not depend on it.
+  constexpr int RP = NCH >= 4 ? 1 : 4 / NCH;
   const int step = gridDim.x * 4;
   for (int row0 = blockIdx.x * 4 + wave; row0 < rows; row0 += RP * step) {
-    float xv[RP][NCH][VEC], dv[RP][NCH][VEC], rv[RP][NCH][VEC], r[RP], mu[RP];
+    P xr[RP][NCH], dr[RP][NCH], rr[RP][NCH];
+    float r[RP], mu[RP];
 #pragma unroll
     for (int k = 0; k < RP; ++k) {
       const int row = row0 + k * step;
@@ -471,12 +478,11 @@ __global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int c = (lane + j * kWave) * VEC;
-#pragma unroll
-        for (int q = 0; q < VEC; ++q) xv[k][j][q] = dv[k][j][q] = rv[k][j][q] = 0.f;
+        xr[k][j] = dr[k][j] = rr[k][j] = P{};
         if (c < C && ok) {
-          load_f<T, VEC>(x + base + c, xv[k][j]);
-          load_f<T, VEC>(dy + base + c, dv[k][j]);
-          if (dres != nullptr) load_f<T, VEC>(dres + base + c, rv[k][j]);
+          xr[k][j] = *reinterpret_cast<const P*>(x + base + c);
+          dr[k][j] = *reinterpret_cast<const P*>(dy + base + c);
+          if (dres != nullptr) rr[k][j] = *reinterpret_cast<const P*>(dres + base + c);
         }
       }
     }
@@ -492,13 +498,11 @@ __global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const
         if (c < C) {
 #pragma unroll
           for (int q = 0; q < VEC; ++q) {
-            const float xh = (xv[k][j][q] - mu[k]) * r[k];
-            const float dyv = dv[k][j][q];
-            const float dxh = dyv * gv[j][q];
+            const float xh = (to_f32(xr[k][j].e[q]) - mu[k]) * r[k];
+            const float dyv = to_f32(dr[k][j].e[q]);
+            const float dxh = dyv * to_f32(gp[j].e[q]);
             pg[j][q] += dyv * xh;
             pb[j][q] += dyv;
-            xv[k][j][q] = xh;
-            dv[k][j][q] = dxh;
             s1 += dxh;
             s2 += dxh * xh;
           }
@@ -513,8 +517,9 @@ __global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const
           float out[VEC];
 #pragma unroll
           for (int q = 0; q < VEC; ++q) {
-            const float xh = xv[k][j][q], dxh = dv[k][j][q];
-            out[q] = rv[k][j][q] + r[k] * (dxh - m1 - xh * m2);
+            const float xh = (to_f32(xr[k][j].e[q]) - mu[k]) * r[k];
+            const float dxh = to_f32(dr[k][j].e[q]) * to_f32(gp[j].e[q]);
+            out[q] = to_f32(rr[k][j].e[q]) + r[k] * (dxh - m1 - xh * m2);
           }
           store_f<T, VEC>(dx + base + c, out);
         }
