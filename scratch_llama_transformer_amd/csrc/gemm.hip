@@ -107,37 +107,44 @@ template <> __device__ __forceinline__ float zero_v<float>() { return 0.f; }
 // Register staging for one operand tile (128 rows x BK).
 template <typename T, bool KMAJOR> struct Stage;
 
+// Load width of the register-staged copies: whole 16-byte groups (k-major) or
+// 4-wide m/n groups, element pairs (for an odd number of pairs along the
+// vector dimension, e.g. an MLP width of 682), or single elements.
+constexpr int kVecFull = 2, kVecPair = 1, kVecOne = 0;
+
+template <typename T, int N>
+__device__ __forceinline__ void ld_group(const T* g, bool ok, T* out) {
+  Pk<T, N> x;
+  if (ok) {
+    x = *reinterpret_cast<const Pk<T, N>*>(g);
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) x.e[e] = zero_v<T>();
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) out[e] = x.e[e];
+}
+
 template <typename T> struct Stage<T, true> {
   static constexpr int EPV = Tr<T>::EPV;
   static constexpr int VPR = Tr<T>::BK / EPV;      // 16-byte vectors per tile row
   static constexpr int NV = BM * VPR / NT;         // vectors per thread
   Pk<T, EPV> r[NV];
-  template <bool VEC>
+  template <int VL>
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows, int K, int row0, int k0, int tid) {
-    if (VEC && row0 + BM <= rows && k0 + Tr<T>::BK <= K) {  // whole tile inside: no bounds checks
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int idx = tid + v * NT;
-        r[v] = *reinterpret_cast<const Pk<T, EPV>*>(g + (int64_t)(row0 + idx / VPR) * ld + k0 + (idx % VPR) * EPV);
-      }
-      return;
-    }
+    const bool inside = row0 + BM <= rows && k0 + Tr<T>::BK <= K;  // whole tile inside: no bounds checks
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int idx = tid + v * NT;
       const int row = row0 + idx / VPR;
       const int k = k0 + (idx % VPR) * EPV;
-      if (VEC) {
-        if (row < rows && k < K) {
-          r[v] = *reinterpret_cast<const Pk<T, EPV>*>(g + (int64_t)row * ld + k);
-        } else {
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) r[v].e[e] = zero_v<T>();
-        }
+      const T* src = g + (int64_t)row * ld + k;
+      if constexpr (VL == kVecFull) {
+        ld_group<T, EPV>(src, inside || (row < rows && k < K), r[v].e);
       } else {
+        constexpr int W = VL == kVecPair ? 2 : 1;  // K a multiple of W: a group is wholly in or out
 #pragma unroll
-        for (int e = 0; e < EPV; ++e)
-          r[v].e[e] = (row < rows && k + e < K) ? g[(int64_t)row * ld + k + e] : zero_v<T>();
+        for (int e = 0; e < EPV; e += W) ld_group<T, W>(src + e, inside || (row < rows && k + e < K), r[v].e + e);
       }
     }
   }
@@ -153,29 +160,21 @@ template <typename T> struct Stage<T, true> {
 template <typename T> struct Stage<T, false> {
   static constexpr int KV = Tr<T>::KV;
   Pk<T, 4> r[KV];  // r[kk] = 4 consecutive m/n values at k = kg + kk
-  template <bool VEC>
+  template <int VL>
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows, int K, int row0, int k0, int tid) {
     const int mn = row0 + 4 * (tid >> 3);
     const int kg = k0 + (tid & 7) * KV;
-    if (VEC && row0 + BM <= rows && k0 + Tr<T>::BK <= K) {  // whole tile inside: no bounds checks
-#pragma unroll
-      for (int kk = 0; kk < KV; ++kk) r[kk] = *reinterpret_cast<const Pk<T, 4>*>(g + (int64_t)(kg + kk) * ld + mn);
-      return;
-    }
+    const bool inside = row0 + BM <= rows && k0 + Tr<T>::BK <= K;  // whole tile inside: no bounds checks
 #pragma unroll
     for (int kk = 0; kk < KV; ++kk) {
       const int k = kg + kk;
-      if (VEC) {
-        if (k < K && mn < rows) {
-          r[kk] = *reinterpret_cast<const Pk<T, 4>*>(g + (int64_t)k * ld + mn);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[kk].e[e] = zero_v<T>();
-        }
+      const T* src = g + (int64_t)k * ld + mn;
+      if constexpr (VL == kVecFull) {
+        ld_group<T, 4>(src, inside || (k < K && mn < rows), r[kk].e);
       } else {
+        constexpr int W = VL == kVecPair ? 2 : 1;  // rows a multiple of W: a group is wholly in or out
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          r[kk].e[e] = (k < K && mn + e < rows) ? g[(int64_t)k * ld + mn + e] : zero_v<T>();
+        for (int e = 0; e < 4; e += W) ld_group<T, W>(src + e, inside || (k < K && mn + e < rows), r[kk].e + e);
       }
     }
   }
@@ -224,7 +223,7 @@ __device__ __forceinline__ void load4(const TO* p, float (&v)[4]) {
   for (int r = 0; r < 4; ++r) v[r] = to_f32(pk.e[r]);
 }
 
-template <typename T, typename TO, bool AK, bool BKM, bool VEC, bool SPLIT>
+template <typename T, typename TO, bool AK, bool BKM, int VL, bool SPLIT>
 __global__ __launch_bounds__(NT) void gemm_k(KArgs a) {
   constexpr int BK = Tr<T>::BK, EPV = Tr<T>::EPV, STR = kStride<T>;
   __shared__ __attribute__((aligned(16))) T As[2][BM * STR];
@@ -256,8 +255,8 @@ __global__ __launch_bounds__(NT) void gemm_k(KArgs a) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nk > 0) {
-    sa.template load<VEC>(A, a.lda, a.M, a.K, m0, kbeg, tid);
-    sb.template load<VEC>(B, a.ldb, a.N, a.K, n0, kbeg, tid);
+    sa.template load<VL>(A, a.lda, a.M, a.K, m0, kbeg, tid);
+    sb.template load<VL>(B, a.ldb, a.N, a.K, n0, kbeg, tid);
     sa.store(As[0], tid);
     sb.store(Bs[0], tid);
   }
@@ -268,8 +267,8 @@ __global__ __launch_bounds__(NT) void gemm_k(KArgs a) {
     const bool more = it + 1 < nk;
     if (more) {
       const int k = kbeg + (it + 1) * BK;
-      sa.template load<VEC>(A, a.lda, a.M, a.K, m0, k, tid);
-      sb.template load<VEC>(B, a.ldb, a.N, a.K, n0, k, tid);
+      sa.template load<VL>(A, a.lda, a.M, a.K, m0, k, tid);
+      sb.template load<VL>(B, a.ldb, a.N, a.K, n0, k, tid);
     }
 #pragma unroll
     for (int ks = 0; ks < kSub<T>; ++ks) {
@@ -1169,9 +1168,9 @@ __global__ __launch_bounds__(256) void gemm_group_reduce_k(GArgs a, int splits) 
 
 inline bool al(const void* p, int b) { return (reinterpret_cast<uintptr_t>(p) % b) == 0; }
 
-template <typename T, typename TO, bool AK, bool BKM, bool VEC, bool SPLIT>
+template <typename T, typename TO, bool AK, bool BKM, int VL, bool SPLIT>
 void launch_one(const KArgs& ka, dim3 grid, hipStream_t s) {
-  gemm_k<T, TO, AK, BKM, VEC, SPLIT><<<grid, NT, 0, s>>>(ka);
+  gemm_k<T, TO, AK, BKM, VL, SPLIT><<<grid, NT, 0, s>>>(ka);
 }
 
 // After the main kernel: the fixed-order sum of split-K partials, if any.
@@ -1201,12 +1200,18 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
   const int tiles = tiles_m * tiles_n;
   ka.tiles = tiles;
 
-  // Vector loads need every vector wholly inside or outside the operand.
-  auto op_ok = [&](const void* p, int64_t ld, bool kmajor, int rows) {
-    if (kmajor) return g.K % EPV == 0 && ld % EPV == 0 && al(p, 16);
-    return rows % 4 == 0 && ld % 4 == 0 && al(p, 4 * (int)sizeof(T));
+  // Vector loads need every vector wholly inside or outside the operand:
+  // whole groups where the vector dimension (K for a k-major operand, its
+  // rows otherwise) and the row stride are multiples of the group, else
+  // element pairs (fp32) where they are even, else single elements.
+  auto op_vl = [&](const void* p, int64_t ld, bool kmajor, int rows) {
+    const int full = kmajor ? EPV : 4;
+    const int64_t q = kmajor ? g.K : rows;
+    if (q % full == 0 && ld % full == 0 && al(p, full * (int)sizeof(T))) return kVecFull;
+    if (sizeof(T) == 4 && q % 2 == 0 && ld % 2 == 0 && al(p, 2 * (int)sizeof(T))) return kVecPair;
+    return kVecOne;
   };
-  const bool vec = op_ok(g.A, g.lda, g.a_kmajor, g.M) && op_ok(g.B, g.ldb, g.b_kmajor, g.N);
+  const int vl = std::min(op_vl(g.A, g.lda, g.a_kmajor, g.M), op_vl(g.B, g.ldb, g.b_kmajor, g.N));
 
   // Split K when the output grid cannot fill the 256 compute units and K is
   // long; the partials must fit the workspace.
@@ -1298,15 +1303,16 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
     }
   }
 
-#define SLT_GEMM_GO(AKv, BKv)                                                     \
-  do {                                                                            \
-    if (split) {                                                                  \
-      if (vec) launch_one<T, float, AKv, BKv, true, true>(ka, grid, s);           \
-      else launch_one<T, float, AKv, BKv, false, true>(ka, grid, s);              \
-    } else {                                                                      \
-      if (vec) launch_one<T, TO, AKv, BKv, true, false>(ka, grid, s);             \
-      else launch_one<T, TO, AKv, BKv, false, false>(ka, grid, s);                \
-    }                                                                             \
+#define SLT_GEMM_VL(TOv, AKv, BKv, SPv)                                                   \
+  do {                                                                                    \
+    if (vl == kVecFull) launch_one<T, TOv, AKv, BKv, kVecFull, SPv>(ka, grid, s);         \
+    else if (vl == kVecOne) launch_one<T, TOv, AKv, BKv, kVecOne, SPv>(ka, grid, s);      \
+    else if constexpr (sizeof(T) == 4) launch_one<T, TOv, AKv, BKv, kVecPair, SPv>(ka, grid, s); \
+  } while (0)
+#define SLT_GEMM_GO(AKv, BKv)                  \
+  do {                                         \
+    if (split) SLT_GEMM_VL(float, AKv, BKv, true); \
+    else SLT_GEMM_VL(TO, AKv, BKv, false);     \
   } while (0)
 
   if (g.a_kmajor && g.b_kmajor) SLT_GEMM_GO(true, true);
@@ -1314,6 +1320,7 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
   else if (g.b_kmajor) SLT_GEMM_GO(false, true);
   else SLT_GEMM_GO(false, false);
 #undef SLT_GEMM_GO
+#undef SLT_GEMM_VL
   return finish<TO>(g, split, splits, s);
 }
 

@@ -1105,28 +1105,39 @@ slt_status launch_rope_table(int T_, int R, float base, float* cs, hipStream_t s
   return check_launch("rope_table");
 }
 
+// Widest vector (in elements) for the element kernels: 16 bytes, else 8, else
+// 4, else single elements -- the first width that divides F and every row
+// stride, with every pointer aligned to it.
 template <typename T>
-static bool ew_vec_ok(int F, std::initializer_list<int64_t> lds, std::initializer_list<const void*> ptrs) {
+static int ew_vec(int F, std::initializer_list<int64_t> lds, std::initializer_list<const void*> ptrs) {
+  for (int v = full_vec<T>(); v >= 2; v /= 2) {
+    bool ok = F % v == 0;
+    for (auto l : lds) ok = ok && l % v == 0;
+    for (auto p : ptrs) ok = ok && aligned(p, v * (int)sizeof(T));
+    if (ok) return v;
+  }
+  return 1;
+}
+
+// Calls f(std::integral_constant<int, v>) for the width ew_vec chose.
+template <typename T, typename Fn>
+static void ew_dispatch(int v, Fn&& f) {
   constexpr int FV = full_vec<T>();
-  if (F % FV) return false;
-  for (auto l : lds)
-    if (l % FV) return false;
-  for (auto p : ptrs)
-    if (!aligned(p, 16)) return false;
-  return true;
+  if (v == FV) f(std::integral_constant<int, FV>{});
+  else if (v == FV / 2) f(std::integral_constant<int, FV / 2>{});
+  else if (FV >= 8 && v == FV / 4) f(std::integral_constant<int, (FV >= 8 ? FV / 4 : 1)>{});
+  else f(std::integral_constant<int, 1>{});
 }
 
 slt_status launch_swiglu_fwd(const void* a, const void* b, void* h, int rows, int F, int64_t lda, int64_t ldb,
                              int64_t ldh, int dtype, hipStream_t s) {
   auto go = [&](auto tag) {
     using T = decltype(tag);
-    constexpr int FV = full_vec<T>();
-    if (ew_vec_ok<T>(F, {lda, ldb, ldh}, {a, b, h}))
-      swiglu_fwd_k<T, FV><<<grid_for((int64_t)rows * F / FV), 256, 0, s>>>((const T*)a, (const T*)b, (T*)h, rows,
-                                                                          F, lda, ldb, ldh);
-    else
-      swiglu_fwd_k<T, 1><<<grid_for((int64_t)rows * F), 256, 0, s>>>((const T*)a, (const T*)b, (T*)h, rows, F, lda,
-                                                                     ldb, ldh);
+    ew_dispatch<T>(ew_vec<T>(F, {lda, ldb, ldh}, {a, b, h}), [&](auto vec) {
+      constexpr int V = decltype(vec)::value;
+      swiglu_fwd_k<T, V><<<grid_for((int64_t)rows * F / V), 256, 0, s>>>((const T*)a, (const T*)b, (T*)h, rows, F,
+                                                                         lda, ldb, ldh);
+    });
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
   return check_launch("swiglu_fwd");
@@ -1137,13 +1148,11 @@ slt_status launch_swiglu_bwd(const void* a, const void* b, const void* dh, void*
                              hipStream_t s) {
   auto go = [&](auto tag) {
     using T = decltype(tag);
-    constexpr int FV = full_vec<T>();
-    if (ew_vec_ok<T>(F, {lda, ldb, lddh, ldda, lddb}, {a, b, dh, da, db}))
-      swiglu_bwd_k<T, FV><<<grid_for((int64_t)rows * F / FV), 256, 0, s>>>(
+    ew_dispatch<T>(ew_vec<T>(F, {lda, ldb, lddh, ldda, lddb}, {a, b, dh, da, db}), [&](auto vec) {
+      constexpr int V = decltype(vec)::value;
+      swiglu_bwd_k<T, V><<<grid_for((int64_t)rows * F / V), 256, 0, s>>>(
           (const T*)a, (const T*)b, (const T*)dh, (T*)da, (T*)db, rows, F, lda, ldb, lddh, ldda, lddb);
-    else
-      swiglu_bwd_k<T, 1><<<grid_for((int64_t)rows * F), 256, 0, s>>>(
-          (const T*)a, (const T*)b, (const T*)dh, (T*)da, (T*)db, rows, F, lda, ldb, lddh, ldda, lddb);
+    });
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
   return check_launch("swiglu_bwd");
@@ -1153,11 +1162,10 @@ slt_status launch_gelu_fwd(const void* a, void* u, int rows, int F, int64_t lda,
                            hipStream_t s) {
   auto go = [&](auto tag) {
     using T = decltype(tag);
-    constexpr int FV = full_vec<T>();
-    if (ew_vec_ok<T>(F, {lda, ldu}, {a, u}))
-      gelu_fwd_k<T, FV><<<grid_for((int64_t)rows * F / FV), 256, 0, s>>>((const T*)a, (T*)u, rows, F, lda, ldu);
-    else
-      gelu_fwd_k<T, 1><<<grid_for((int64_t)rows * F), 256, 0, s>>>((const T*)a, (T*)u, rows, F, lda, ldu);
+    ew_dispatch<T>(ew_vec<T>(F, {lda, ldu}, {a, u}), [&](auto vec) {
+      constexpr int V = decltype(vec)::value;
+      gelu_fwd_k<T, V><<<grid_for((int64_t)rows * F / V), 256, 0, s>>>((const T*)a, (T*)u, rows, F, lda, ldu);
+    });
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
   return check_launch("gelu_fwd");
@@ -1167,13 +1175,11 @@ slt_status launch_gelu_bwd(const void* a, const void* du, void* da, int rows, in
                            int64_t ldda, int dtype, hipStream_t s) {
   auto go = [&](auto tag) {
     using T = decltype(tag);
-    constexpr int FV = full_vec<T>();
-    if (ew_vec_ok<T>(F, {lda, lddu, ldda}, {a, du, da}))
-      gelu_bwd_k<T, FV><<<grid_for((int64_t)rows * F / FV), 256, 0, s>>>((const T*)a, (const T*)du, (T*)da, rows,
-                                                                        F, lda, lddu, ldda);
-    else
-      gelu_bwd_k<T, 1><<<grid_for((int64_t)rows * F), 256, 0, s>>>((const T*)a, (const T*)du, (T*)da, rows, F,
-                                                                   lda, lddu, ldda);
+    ew_dispatch<T>(ew_vec<T>(F, {lda, lddu, ldda}, {a, du, da}), [&](auto vec) {
+      constexpr int V = decltype(vec)::value;
+      gelu_bwd_k<T, V><<<grid_for((int64_t)rows * F / V), 256, 0, s>>>((const T*)a, (const T*)du, (T*)da, rows, F,
+                                                                       lda, lddu, ldda);
+    });
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
   return check_launch("gelu_bwd");

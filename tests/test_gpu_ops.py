@@ -85,11 +85,17 @@ def gemm_case(B, rng, M, N, K, a_k, b_k, ind, outd, resid=False, ws=False, sampl
 @pytest.mark.parametrize("ind,outd", [(BF16, BF16), (BF16, F32), (F32, F32)])
 def test_gemm_small_ragged(B, a_k, b_k, ind, outd):
     rng = np.random.default_rng(1)
-    for (M, N, K) in [(37, 50, 29), (1, 1, 1), (130, 260, 96), (256, 128, 64), (200, 136, 520)]:
+    # fp32 loads: 4-wide groups where the vector dimension (K of a k-major
+    # operand, M or N of the others) and the stride are multiples of 4, pairs
+    # where they are even (66, 682, 3002), single elements otherwise
+    for (M, N, K) in [(37, 50, 29), (1, 1, 1), (130, 260, 96), (256, 128, 64), (200, 136, 520), (66, 682, 682),
+                      (130, 66, 258)]:
         gemm_case(B, rng, M, N, K, a_k, b_k, ind, outd)
     gemm_case(B, rng, 131, 77, 45, a_k, b_k, ind, outd, resid=True)
+    gemm_case(B, rng, 66, 138, 682, a_k, b_k, ind, outd, resid=True)
     gemm_case(B, rng, 96, 72, 3000, a_k, b_k, ind, outd, ws=True)
     gemm_case(B, rng, 96, 72, 3000, a_k, b_k, ind, outd, ws=True, resid=True)
+    gemm_case(B, rng, 98, 74, 3002, a_k, b_k, ind, outd, ws=True)
 
 
 @pytest.mark.parametrize("a_k,b_k", [(1, 1), (1, 0), (0, 0), (0, 1)])
@@ -451,7 +457,8 @@ def test_attention_fwd_bwd(B, case, pad):
 # MLP activations
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", [F32, BF16])
-@pytest.mark.parametrize("rows,F", [(16, 42), (300, 682), (4096, 1024)])
+# widths: 16-byte vectors (1024), 4 or 2 elements (44, 42, 682), single elements (43)
+@pytest.mark.parametrize("rows,F", [(16, 42), (300, 682), (4096, 1024), (33, 44), (17, 43)])
 def test_swiglu_and_gelu(B, dtype, rows, F):
     say("swiglu/gelu", rows, F, dtype)
     rng = np.random.default_rng(9)
