@@ -452,11 +452,16 @@ static DwStream* dw_stream() {
   auto it = per_dev.find(dev);
   if (it == per_dev.end()) {
     DwStream a;
+    // The events only order the two streams of one device: a device-scope
+    // release suffices, not the system-scope fence (write-back and invalidate
+    // for host visibility) of a default event.  The caller's own
+    // synchronisation still makes the results visible to the host.
+    const unsigned ef = hipEventDisableTiming | hipEventDisableSystemFence;
     bool ok = hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking) == hipSuccess &&
-              hipEventCreateWithFlags(&a.ready, hipEventDisableTiming) == hipSuccess;
-    for (int k = 0; k < 3 && ok; ++k) ok = hipEventCreateWithFlags(&a.done[k], hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&a.sort_done, hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&a.fin, hipEventDisableTiming) == hipSuccess;
+              hipEventCreateWithFlags(&a.ready, ef) == hipSuccess;
+    for (int k = 0; k < 3 && ok; ++k) ok = hipEventCreateWithFlags(&a.done[k], ef) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&a.sort_done, ef) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&a.fin, ef) == hipSuccess;
     if (!ok) {  // fall back to the walk's stream (what was created stays until exit)
       a = DwStream{};
       (void)hipGetLastError();
