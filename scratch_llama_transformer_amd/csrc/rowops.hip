@@ -185,8 +185,15 @@ __global__ __launch_bounds__(1024) void emb_scan_k(int V, EmbWs w) {
   const int t = threadIdx.x;
   const int per = (V + 1023) / 1024;
   const int b = t * per, e = min(V, b + per);
+  constexpr int G = 16;  // totals loaded per batch (independent loads in flight)
   int s = 0;
-  for (int k = b; k < e; ++k) s += w.total[k];
+  for (int k0 = b; k0 < e; k0 += G) {
+    int x[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) x[j] = k0 + j < e ? w.total[k0 + j] : 0;
+#pragma unroll
+    for (int j = 0; j < G; ++j) s += x[j];
+  }
   part[t] = s;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
@@ -196,9 +203,16 @@ __global__ __launch_bounds__(1024) void emb_scan_k(int V, EmbWs w) {
     __syncthreads();
   }
   int run = t == 0 ? 0 : part[t - 1];
-  for (int k = b; k < e; ++k) {
-    w.start[k] = run;
-    run += w.total[k];
+  for (int k0 = b; k0 < e; k0 += G) {
+    int x[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) x[j] = k0 + j < e ? w.total[k0 + j] : 0;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (k0 + j < e) {
+        w.start[k0 + j] = run;
+        run += x[j];
+      }
   }
   if (t == 1023) w.start[V] = part[1023];
 }
@@ -229,6 +243,19 @@ __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict_
     pos[k] = s + k < e ? w.sorted[s + k] : 0;
     ids[k] = s + k < e ? tok[(int64_t)(pos[k] / T_) * ld + (pos[k] % T_)] : -1;
   }
+  // where each run ends and where its sum goes, read up front for every
+  // entry (inside the column loop these reads would wait one by one)
+  int kind[kEmbTile];  // 0: the run goes on; 1: head partial; 2: tail partial; 3: final row
+#pragma unroll
+  for (int k = 0; k < kEmbTile; ++k) {
+    const bool last = (k == kEmbTile - 1) || (s + k + 1 >= e) || (ids[k + 1 < kEmbTile ? k + 1 : k] != ids[k]);
+    int rs = 0, re = 0;
+    if (s + k < e && last) {
+      rs = w.start[ids[k]];
+      re = w.start[ids[k] + 1];
+    }
+    kind[k] = !(s + k < e && last) ? 0 : rs < s ? 1 : re > e ? 2 : 3;
+  }
   for (int c0 = lane * VEC; c0 < C; c0 += kWave * VEC) {
     float acc[VEC];
 #pragma unroll
@@ -257,18 +284,12 @@ __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict_
         }
 #pragma unroll
         for (int q = 0; q < VEC; ++q) acc[q] += f[q];
-        const bool last = (k == kEmbTile - 1) || (s + k + 1 >= e) || (ids[k + 1] != ids[k]);
-        if (last) {
-          const int id = ids[k];
-          const int rs = w.start[id], re = w.start[id + 1];
+        if (kind[k] != 0) {
           float* dst;
-          bool final_row = false;
-          if (rs < s) dst = w.head + (int64_t)tile * C;          // continues from an earlier tile
-          else if (re > e) dst = w.tail + (int64_t)tile * C;     // continues into a later tile
-          else {                                                 // complete inside this tile
-            dst = dwte + (int64_t)id * C;
-            final_row = true;
-          }
+          const bool final_row = kind[k] == 3;
+          if (kind[k] == 1) dst = w.head + (int64_t)tile * C;       // continues from an earlier tile
+          else if (kind[k] == 2) dst = w.tail + (int64_t)tile * C;  // continues into a later tile
+          else dst = dwte + (int64_t)ids[k] * C;                    // complete inside this tile
 #pragma unroll
           for (int q = 0; q < VEC; ++q) {
             dst[c0 + q] = final_row ? gw.alpha * acc[q] + (gw.accumulate ? dst[c0 + q] : 0.f) : acc[q];
@@ -283,13 +304,17 @@ __global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict_
 // One 256-thread block per vocabulary row: zero rows, and rows spanning
 // several tiles.  For the latter the 4 waves take contiguous quarters of the
 // pieces (tail of the first tile, then heads in tile order); a lane owns 8
-// columns of a 512-column pass and sums 4 pieces per step into 4
-// interleaved accumulators, so that 32 loads are in flight per step; the
-// quarters are added in order.
+// columns of a 512-column pass (two 16-byte groups when the row width allows)
+// and sums 8 pieces per step into 8 interleaved accumulators, so that 16
+// 16-byte loads are in flight per lane (a frequent id of a skewed token mix
+// spans a tenth of all tiles: its row is the critical path); the quarters are
+// added in order.
+template <bool V4>
 __global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte, int V, int C, EmbWs w,
                                                         GradW gw) {
   constexpr int QN = 8;  // columns per lane per pass
-  __shared__ float part[4][kWave * QN];
+  constexpr int P = 8;   // pieces per step
+  __shared__ __attribute__((aligned(16))) float part[4][kWave * QN];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int v = blockIdx.x;
   const int rs = w.start[v], re = w.start[v + 1];
@@ -304,29 +329,46 @@ __global__ __launch_bounds__(256) void emb_row_finish_k(float* __restrict__ dwte
   // pieces: index 0 = tail[t0], index k >= 1 = head[t0 + k]
   const int np = t1 - t0 + 1;
   const int per = (np + 3) / 4;
-  const int pb = wave * per, pe = min(np, pb + per);
+  const int pb = min(np, wave * per), pe = min(np, pb + per);
+  // column of a lane's value q in a pass: 4-wide groups at 4 lane + 256 (q / 4)
+  // (V4), else single columns at lane + 64 q
+  auto col = [&](int q) { return V4 ? 4 * lane + 256 * (q / 4) + (q % 4) : lane + kWave * q; };
   for (int c0 = 0; c0 < C; c0 += kWave * QN) {
-    float acc[4][QN];
+    float acc[P][QN];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < P; ++u)
 #pragma unroll
       for (int q = 0; q < QN; ++q) acc[u][q] = 0.f;
-    for (int k = pb; k < pe; k += 4) {
+    for (int k = pb; k < pe; k += P) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < P; ++u) {
         const int kk = k + u;
         if (kk < pe) {
-          const float* src = kk == 0 ? w.tail + (int64_t)t0 * C : w.head + (int64_t)(t0 + kk) * C;
+          const float* src = (kk == 0 ? w.tail + (int64_t)t0 * C : w.head + (int64_t)(t0 + kk) * C) + c0;
+          if (V4) {
 #pragma unroll
-          for (int q = 0; q < QN; ++q) {
-            const int c = c0 + q * kWave + lane;
-            if (c < C) acc[u][q] += src[c];
+            for (int g = 0; g < QN / 4; ++g) {
+              const int c = col(4 * g);
+              if (c0 + c < C) {
+                const float4 f = *reinterpret_cast<const float4*>(src + c);
+                acc[u][4 * g] += f.x;
+                acc[u][4 * g + 1] += f.y;
+                acc[u][4 * g + 2] += f.z;
+                acc[u][4 * g + 3] += f.w;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < QN; ++q)
+              if (c0 + col(q) < C) acc[u][q] += src[col(q)];
           }
         }
       }
     }
 #pragma unroll
-    for (int q = 0; q < QN; ++q) part[wave][q * kWave + lane] = (acc[0][q] + acc[1][q]) + (acc[2][q] + acc[3][q]);
+    for (int q = 0; q < QN; ++q)
+      part[wave][col(q)] = ((acc[0][q] + acc[1][q]) + (acc[2][q] + acc[3][q])) +
+                           ((acc[4][q] + acc[5][q]) + (acc[6][q] + acc[7][q]));
     __syncthreads();
     for (int c = threadIdx.x; c < kWave * QN; c += blockDim.x)
       if (c0 + c < C) {
@@ -965,7 +1007,10 @@ slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, c
       emb_tile_sum_k<T, 1><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w, gw, drop);
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
-  emb_row_finish_k<<<V, 256, 0, s>>>(dwte, V, C, w, gw);
+  if (C % 4 == 0 && aligned(dwte, 16) && aligned(ws, 16))  // the partials sit at 256-byte offsets in ws
+    emb_row_finish_k<true><<<V, 256, 0, s>>>(dwte, V, C, w, gw);
+  else
+    emb_row_finish_k<false><<<V, 256, 0, s>>>(dwte, V, C, w, gw);
   return check_launch("embedding_bwd");
 }
 

@@ -264,7 +264,8 @@ def test_proj_gelu_fwd(B, M, N, K, col0, dtype):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", [F32, BF16])
 @pytest.mark.parametrize("Bn,T,V,C,zipf", [(1, 16, 27, 16, False), (3, 37, 50, 24, False),
-                                          (64, 256, 4096, 384, True), (16, 1024, 32000, 1024, False)])
+                                          (64, 256, 4096, 384, True), (16, 1024, 32000, 1024, False),
+                                          (8, 2048, 51200, 64, False)])
 def test_embedding_fwd_bwd(B, dtype, Bn, T, V, C, zipf):
     say("embedding", Bn, T, V, C, zipf, dtype)
     import slt_workloads as W
