@@ -476,18 +476,30 @@ __global__ __launch_bounds__(256, 2) void fl_fwd2_k(FlArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sv[tt][r]);
         }
-        const float mn = fmaxf(m[i], max4lanes(tmax));
-        const float alpha = ex2(m[i] - mn);
+        // The running maximum moves only where a row's new maximum exceeds it
+        // by more than 8 (base 2), so the weights stay below 2^8; a wave whose
+        // rows all keep theirs skips rescaling its accumulators.  (The first
+        // half processed holds key 0, which no query masks, so m is finite
+        // from then on.)
+        const float mt = max4lanes(tmax);
+        const bool grow = mt > m[i] + 8.f;
+        if (__ballot(grow) != 0) {
+          const float mn = grow ? mt : m[i];
+          const float alpha = ex2(m[i] - mn);  // 1 where the maximum stays, 0 on the first half
+          l[i] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) oacc[i][dt] *= alpha;
+          m[i] = mn;
+        }
         float rs = 0.f;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            sv[tt][r] = ex2(sv[tt][r] - mn);
+            sv[tt][r] = ex2(sv[tt][r] - m[i]);
             rs += sv[tt][r];
           }
-        l[i] = l[i] * alpha + rs;  // this lane's keys only; the four lanes are summed at the end
-        m[i] = mn;
+        l[i] += rs;  // this lane's keys only; the four lanes are summed at the end
         if (DROP) {  // the normaliser keeps every weight; the values see the dropped ones
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
@@ -499,10 +511,7 @@ __global__ __launch_bounds__(256, 2) void fl_fwd2_k(FlArgs a) {
         }
         const u32x4 pb = pack_k(sv[0], sv[1]);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          oacc[i][dt] *= alpha;
-          oacc[i][dt] = mma(vf[dt], pb, oacc[i][dt]);
-        }
+        for (int dt = 0; dt < 4; ++dt) oacc[i][dt] = mma(vf[dt], pb, oacc[i][dt]);
       }
     }
   }
