@@ -339,10 +339,12 @@ def main():
                           for k, v in cl.items()}
         # the dominant kernel class of the step (largest time in the
         # breakdown): the forward-projection GEMMs, both operands k-major
-        # (gemm_d64_k for 384 to 1152 output columns, gemm_w8_k's 256 x 256
-        # tiles for the wide ones at this workload)
+        # (bf16: gemm_d64_k for 384 to 1152 output columns, gemm_w8_k's
+        # 256 x 256 tiles for the wide ones; fp32: gemm_k on the fp32 matrix
+        # instructions)
         c = cl["gemm_fwd"]
-        out["roofline"] = {"kernel": "forward-projection GEMMs (gemm_d64_k, gemm_w8_k; k-major x k-major)",
+        kern = "gemm_k, fp32" if w.act == "f32" else "gemm_d64_k, gemm_w8_k"
+        out["roofline"] = {"kernel": f"forward-projection GEMMs ({kern}; k-major x k-major)",
                            "bound": c["bound"],
                            "achieved": round(c["tflops"], 2), "peak": c["peak"], "unit": "TFLOP/s",
                            "frac": round(c["tflops"] / c["peak"], 4), "traffic": measured_traffic(w),
