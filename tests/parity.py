@@ -2,17 +2,51 @@
 
 fp32 paths: normwise relative error per tensor <= 1e-5 (two fp32 summation
 orders differ elementwise by more than that on cancelling sums, so the bound is
-read normwise).  bf16 paths: per element |got - ref| <= 2e-2 (|ref| + rms(ref));
-the rms term is the floor near zero, taken over the entries the reference does
-not fix at exactly zero (the embedding gradient's rows of absent ids are
-structural zeros; the GPU must return exact zeros there, which is checked on
-its own).  Loss: relative 1e-5 (fp32), 2e-3 (bf16).
+read normwise).  Loss: relative 1e-5 (fp32), 2e-3 (bf16).
+
+bf16 paths.  The band of an element is
+
+    band = 2e-2 (|ref| + s),   s = max(rms of the tensor, rms of the element's row)
+
+(rms over the entries the reference does not fix at exactly zero for the
+tensor term).  The floor s stands for the size of the terms summed into the
+element: an element that is small by cancellation inside a large row (the
+lm_head and embedding rows of frequent tokens are 50x the tensor's rms) has
+an error proportional to its row, not to its own value.  Rows are the first
+axis (for a weight [out, in]: one output unit).
+
+* One rounding stage (every per-op test): every element within its band.
+* A whole bf16 step: every stored activation is rounded to 8 significant bits,
+  a value within an fp32 summation-order difference of a rounding boundary
+  may round either way, and later layers amplify such flips.  The oracle
+  alone shows how far two valid computations drift apart (the plain oracle
+  against its companion, the same step with 2^-20 relative jitter in front of
+  each activation store): up to 6 bands on 0.3 % of a tensor's elements and
+  0.8 % normwise at the GQA width.  The fixed rule for each gradient tensor:
+  normwise error <= 2e-2, at most 0.5 % of the elements beyond their band,
+  and no element beyond 8 bands.
+* Post-AdamW weights (t = 1): the update is close to lr sign(g), so where the
+  reference gradient lies within the gradient's own tolerance of zero
+  (|g| <= 2e-2 s / (1 - 2e-2)), or the GPU's gradient element is one of the
+  bounded outliers above, both signs are valid results: those weights are
+  exempt from the band (counted; nonzero reference gradients only).  Every
+  other weight must lie within its band, and every weight, exempt or not,
+  must equal the oracle's AdamW applied to the GPU's own gradient.
 """
+import json
+import os
+
 import numpy as np
 
 F32_TOL = 1e-5
 BF16_TOL = 2e-2
 LOSS_TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+# fixed limits of the whole-step bf16 rule (see the module docstring)
+STEP_NORMWISE_MAX = 2e-2
+STEP_FRAC_MAX = 5e-3
+STEP_WORST_MAX = 8.0
+COMPANION_JITTER = 2.0 ** -20
 
 
 def rms(x):
@@ -29,6 +63,8 @@ def normwise(got, ref):
 
 
 def check(got, ref, act, name="", tol=None):
+    """Per-op comparison: fp32 normwise; bf16 every element within
+    tol (|ref| + rms) with the tensor's rms (over nonzero entries) as floor."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -49,9 +85,9 @@ def check(got, ref, act, name="", tol=None):
 
 
 def check_weights(got, ref, gref, act, name=""):
-    """Post-AdamW weights.  Where the reference gradient is within the tie band
-    (|g| <= tau rms(g)) both signs of the first AdamW update are correct, so
-    those elements are exempted (and counted)."""
+    """Post-AdamW weights of an fp32 step.  Where the reference gradient is
+    within 1e-3 rms(g) of zero both signs of the first AdamW update are
+    correct, so those elements are exempted (and counted)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     g = np.asarray(gref, np.float64)
@@ -63,66 +99,91 @@ def check_weights(got, ref, gref, act, name=""):
 
 
 # ---------------------------------------------------------------------------
-# Whole-step comparison for bf16 configurations.
-#
-# A bf16 step rounds every stored activation to 8 significant bits; a value
-# that lands within an fp32 summation-order difference of a rounding boundary
-# can round either way, and later layers amplify such 1-ulp flips.  Two valid
-# bf16 computations of the same step therefore differ: running the oracle a
-# second time with 2^-24 relative jitter in front of each storage rounding
-# (the "companion") gives 0.2-0.8 % normwise differences in the gradients and
-# a few % of elements outside any fixed per-element band.  The GPU result is
-# accepted when, for every tensor, it is within 3x of that spread (normwise
-# error, and the 99.9th percentile and maximum of |error| / band over the
-# elements) and never beyond 2e-2 normwise.  The band of an element is
-# 2e-2 (|ref| + rms of its row).
+# Whole-step comparison for bf16 configurations
 # ---------------------------------------------------------------------------
-def band_stats(got, ref):
-    """(normwise error, 99.9th percentile of |error| / band, worst ratio)."""
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    r2 = ref.reshape(ref.shape[0], -1) if ref.ndim > 1 else ref.reshape(1, -1)
-    g2 = got.reshape(r2.shape)
-    rowrms = np.sqrt(np.mean(r2 * r2, axis=1, keepdims=True))
-    band = BF16_TOL * (np.abs(r2) + rowrms)
+def _rows(x):
+    x = np.asarray(x, np.float64)
+    return x.reshape(x.shape[0], -1) if x.ndim > 1 else x.reshape(1, -1)
+
+
+def floor_of(ref):
+    """s = max(rms of the tensor's nonzero entries, rms of each row), shaped
+    like ref's [rows, -1] view."""
+    r2 = _rows(ref)
+    nz = r2[r2 != 0.0]
+    trms = float(np.sqrt(np.mean(nz * nz))) if nz.size else 0.0
+    rrms = np.sqrt(np.mean(r2 * r2, axis=1, keepdims=True))
+    return np.maximum(trms, rrms)
+
+
+def band_ratio(got, ref):
+    """|got - ref| / band per element ([rows, -1] view); 0 where both are
+    exactly zero, inf where the reference is exactly zero and got is not."""
+    r2 = _rows(ref)
+    g2 = np.asarray(got, np.float64).reshape(r2.shape)
+    band = BF16_TOL * (np.abs(r2) + floor_of(ref))
     diff = np.abs(g2 - r2)
     live = band > 0
-    ratio = np.where(live, diff / np.where(live, band, 1.0), np.where(diff > 0, np.inf, 0.0))
-    return normwise(got, ref), float(np.quantile(ratio, 0.999)), float(ratio.max())
+    return np.where(live, diff / np.where(live, band, 1.0), np.where(diff > 0, np.inf, 0.0))
 
 
-def check_bf16_step_tensor(got, ref, comp, name=""):
+def step_stats(got, ref):
+    """(normwise error, 99.9th percentile of |error| / band, worst ratio,
+    fraction of elements beyond their band)."""
+    r = band_ratio(got, ref)
+    return (normwise(got, ref), float(np.quantile(r, 0.999)), float(r.max()), float(np.mean(r > 1.0)))
+
+
+def record(case, name, **fields):
+    """Append one result line to the file SLT_PARITY_LOG names (if set)."""
+    path = os.environ.get("SLT_PARITY_LOG")
+    if not path:
+        return
+    with open(path, "a") as f:
+        f.write(json.dumps(dict(case=case, tensor=name, **fields)) + "\n")
+
+
+def check_bf16_step_tensor(got, ref, name="", comp=None, case=""):
+    """A gradient (or other whole-step result) of a bf16 step under the fixed
+    rule; comp, if given, is the oracle's companion result, reported beside
+    the GPU's numbers.  Returns (normwise, 99.9 %, worst, fraction)."""
     got = np.asarray(got, np.float64)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    nw, q, worst = band_stats(got, ref)
-    cnw, cq, cworst = band_stats(comp, ref)
-    assert nw <= min(BF16_TOL, max(3 * cnw, 2e-3)), f"{name}: normwise {nw:.3e} (companion {cnw:.3e})"
-    assert q <= max(3 * cq, 1.0), f"{name}: 99.9% quantile {q:.2f}x band (companion {cq:.2f}x)"
-    assert worst <= max(3 * cworst, 1.0), f"{name}: worst {worst:.2f}x band (companion {cworst:.2f}x)"
-    return nw, q, worst
+    st = step_stats(got, ref)
+    extra = {}
+    if comp is not None:
+        cst = step_stats(comp, ref)
+        extra = dict(comp_normwise=cst[0], comp_q999=cst[1], comp_worst=cst[2], comp_frac=cst[3])
+    record(case, name, normwise=st[0], q999=st[1], worst=st[2], frac=st[3], **extra)
+    nw, q, worst, frac = st
+    assert nw <= STEP_NORMWISE_MAX, f"{name}: normwise {nw:.3e} > {STEP_NORMWISE_MAX}"
+    assert frac <= STEP_FRAC_MAX, f"{name}: {frac:.2e} of the elements beyond their band (> {STEP_FRAC_MAX})"
+    assert worst <= STEP_WORST_MAX, f"{name}: worst element {worst:.2f} bands (> {STEP_WORST_MAX})"
+    return st
 
 
-def check_bf16_step_weights(got, ref, ggot, gref, name="", adam_eps=1e-8):
-    """Post-AdamW weights.  At t = 1 the update is lr (g / (|g| + eps) + wd
-    theta): close to lr sign(g), but steep in g where |g| is within a few
-    orders of eps.  Where the GPU's gradient differs from the oracle's by half
-    of it or more (the spread of valid bf16 computations reaches that on
-    elements that are small by cancellation) or either gradient is <= 100 eps,
-    the update is not determined at the gradient's precision: those elements
-    are exempt (and counted).  Every other element must lie within the band.
-    Every element, exempt or not, is also checked against the oracle's AdamW
-    applied to the GPU gradient."""
+def check_bf16_step_weights(got, ref, ggot, gref, theta0, cfg, name="", case="", grad_scale=1.0):
+    """Post-AdamW weights of a bf16 step at t = 1 (see the module docstring).
+    theta0: the weights before the step; cfg: the workload (AdamW
+    hyperparameters); grad_scale: the clipping factor the GPU applied.
+    Returns the number of exempt (sign-tie) elements."""
+    from oracle import adamw  # test infrastructure: the oracle's update rule
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     gg = np.asarray(ggot, np.float64)
     gr = np.asarray(gref, np.float64)
-    tie = ((np.abs(gg - gr) >= 0.5 * np.abs(gr)) | (np.abs(gr) <= 100.0 * adam_eps)
-           | (np.abs(gg) <= 100.0 * adam_eps))
+    # every element: the oracle's AdamW applied to the GPU's own gradient
+    own, _, _ = adamw(theta0, grad_scale * gg, 0.0, 0.0, 1, cfg.lr, cfg.beta1, cfg.beta2, cfg.adam_eps, cfg.wd)
+    check(got, own, "f32", f"{name} from the GPU gradient")
+    s = np.broadcast_to(floor_of(gr), _rows(gr).shape).reshape(gr.shape)
+    tie = ((np.abs(gr) <= BF16_TOL / (1.0 - BF16_TOL) * s) & (gr != 0.0)) | (band_ratio(gg, gr).reshape(gr.shape) > 1.0)
     masked = np.where(tie, ref, got)
-    _, _, worst = band_stats(masked, ref)
-    if worst > 1.0:
-        i = int(np.argmax(np.abs(masked - ref)))
-        raise AssertionError(f"{name}: worst {worst:.2f}x band outside the sign-tie set; element {i}: "
-                             f"weight {got.flat[i]:.8g} vs {ref.flat[i]:.8g}, grad {gg.flat[i]:.6g} vs "
-                             f"{gr.flat[i]:.6g}")
-    return int(tie.sum())
+    r = band_ratio(masked, ref)
+    n_tie = int(tie.sum())
+    record(case, name, exempt=n_tie, n=int(tie.size), worst_outside=float(r.max()))
+    if r.max() > 1.0:
+        i = int(np.argmax(r))
+        raise AssertionError(f"{name}: {int((r > 1).sum())} weights outside the sign-tie set beyond their band "
+                             f"(worst {float(r.max()):.2f}); element {i}: weight {got.flat[i]:.8g} vs "
+                             f"{ref.flat[i]:.8g}, grad {gg.flat[i]:.6g} vs {gr.flat[i]:.6g}")
+    return n_tie

@@ -8,15 +8,16 @@ Comparators: fp32 logits normwise 1e-5.  bf16 logits come out of several
 layers of stored bf16 activations, where a value within an fp32 summation-
 order difference of a rounding boundary may round either way and later
 layers amplify the flip; as for the whole training step, the GPU logits are
-accepted within 3x of the spread between the oracle and its companion (the
-same cached forward with 2^-24 relative jitter before each activation
-store), and never beyond 2e-2 normwise."""
+held to the fixed whole-step rule of tests/parity.py (normwise 2e-2, at most
+0.5 % of the elements beyond their band, none beyond 8 bands); the spread
+between the oracle and its companion (the same cached forward with 2^-20
+relative jitter before each activation store) is reported beside it."""
 import numpy as np
 import pytest
 
 import oracle as O
 import slt_workloads as W
-from parity import check, check_bf16_step_tensor
+from parity import COMPANION_JITTER, check, check_bf16_step_tensor
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -57,7 +58,7 @@ class OracleRun:
         comp = None
         if self.comp is not None:
             self.calls += 1
-            comp = O.forward_cached(self.w, self.params, self.comp, ids, jitter=2.0 ** -24, seed=self.calls)
+            comp = O.forward_cached(self.w, self.params, self.comp, ids, jitter=COMPANION_JITTER, seed=self.calls)
         return ref, comp
 
 
@@ -68,8 +69,9 @@ def check_logits(got, ref, comp, act, name):
     if act == "f32":
         check(got, ref, act, name)
     else:
-        nw, q, worst = check_bf16_step_tensor(got, ref, comp.reshape(-1, V), name)
-        print(f"[result] {name}: normwise {nw:.2e}, 99.9% {q:.2f}x band, worst {worst:.2f}x band")
+        nw, q, worst, frac = check_bf16_step_tensor(got, ref, name, comp.reshape(-1, V), "kv-cache forward")
+        print(f"[result] {name}: normwise {nw:.2e}, 99.9% {q:.2f} bands, worst {worst:.2f} bands, "
+              f"beyond band {frac:.2e}")
 
 
 # (config, batch, layers, prompt, chunk after the prompt, single-token steps, Tmax)

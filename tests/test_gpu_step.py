@@ -9,7 +9,8 @@ import pytest
 
 import oracle as O
 import slt_workloads as W
-from parity import LOSS_TOL, band_stats, check, check_bf16_step_tensor, check_bf16_step_weights, check_weights
+from parity import (COMPANION_JITTER, LOSS_TOL, check, check_bf16_step_tensor, check_bf16_step_weights,
+                    check_weights)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -63,20 +64,30 @@ def test_full_step_parity(TS, ci, Bn, L):
             check(grads[name], ref["grads"][name], w.act, f"grad {name}")
             ties += check_weights(new[name], ref["params"][name], ref["grads"][name], w.act, f"weight {name}")
     else:
-        _, ccache = O.forward(w, params, tokens, jitter=2.0 ** -24, seed=1)
-        comp = O.backward(w, ccache)
-        worst = (0.0, 0.0, 0.0)
-        for name in params:
-            st = check_bf16_step_tensor(grads[name], ref["grads"][name], comp[name], f"grad {name}")
-            worst = tuple(max(a, b) for a, b in zip(worst, st))
-            ties += check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
-                                            f"weight {name}", w.adam_eps)
-            # every element: the update equals the oracle's AdamW applied to the GPU's gradient
-            own, _, _ = O.adamw(params[name], grads[name], 0.0, 0.0, 1, w.lr, w.beta1, w.beta2, w.adam_eps, w.wd)
-            check(new[name], own, "f32", f"weight {name} from the GPU gradient")
-        print(f"[result] worst over gradients: normwise {worst[0]:.2e}, 99.9% quantile {worst[1]:.2f}x band, "
-              f"worst element {worst[2]:.2f}x band")
+        ties = check_bf16_step(w, params, tokens, grads, new, ref, f"step {w.name} B={w.B} L={w.L}")
     print(f"[result] {w.name} loss gpu {loss:.7f} oracle {ref['loss']:.7f}; tie-exempt weights {ties}")
+
+
+def check_bf16_step(w, params, tokens, grads, new, ref, case, companion=True, grad_scale=1.0):
+    """Every gradient and post-AdamW weight of a bf16 step under the fixed
+    whole-step rule (tests/parity.py); the oracle's companion (2^-20 jitter
+    in front of each activation store) is computed for the record only.
+    Returns the number of sign-tie exempt weights."""
+    comp = None
+    if companion:
+        _, ccache = O.forward(w, params, tokens, jitter=COMPANION_JITTER, seed=1)
+        comp = O.backward(w, ccache)
+    worst, ties, n = (0.0, 0.0, 0.0, 0.0), 0, 0
+    for name in params:
+        st = check_bf16_step_tensor(grads[name], ref["grads"][name], f"grad {name}",
+                                    comp[name] if comp else None, case)
+        worst = tuple(max(a, b) for a, b in zip(worst, st))
+        ties += check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
+                                        params[name], w, f"weight {name}", case, grad_scale)
+        n += np.asarray(params[name]).size
+    print(f"[result] {case}: worst over gradients: normwise {worst[0]:.2e}, 99.9% quantile {worst[1]:.2f} bands, "
+          f"worst element {worst[2]:.2f} bands, beyond band {worst[3]:.2e}; exempt weights {ties} of {n}")
+    return ties
 
 
 # The widest model the library accepts (C = 4096, 64 heads of 64): every norm,
@@ -97,47 +108,27 @@ def test_full_step_at_maximum_width(TS, ci, over):
     assert abs(loss - ref["loss"]) <= LOSS_TOL[w.act] * abs(ref["loss"]), (loss, ref["loss"])
     grads = ts.unpack(ts.grads)
     new = ts.unpack(ts.master)
-    _, ccache = O.forward(w, params, tokens, jitter=2.0 ** -24, seed=1)
-    comp = O.backward(w, ccache)
-    for name in params:
-        check_bf16_step_tensor(grads[name], ref["grads"][name], comp[name], f"grad {name}")
-        check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
-                                f"weight {name}", w.adam_eps)
+    check_bf16_step(w, params, tokens, grads, new, ref, f"maximum width {w.name} C={w.C}")
     print(f"[result] {w.name} C={w.C}: loss gpu {loss:.7f} oracle {ref['loss']:.7f}")
 
 
-@pytest.mark.timeout(900)
-def test_full_batch_step_one_layer(TS):
-    """The d=384 workload's whole 64-sequence batch (16384 tokens) through one
-    layer: every product at its full token count (the fused SwiGLU launches,
-    the grouped weight gradients with split K, the 256 x 256 tiles).  Loss,
-    every gradient and every post-AdamW weight against the oracle.  Gradients:
-    normwise and 99.9th-percentile rules as for the reduced cases; the worst
-    element is held to 3 bands instead of 3x the companion's worst, because
-    16384-token weight-gradient sums also carry the GPU's in-register
-    roundings (P in the forward's P V feeds n2), which the storage-rounding
-    companion does not model -- measured ~2-2.5 bands on w1/w2/w3 for both the
-    fused and the unfused MLP kernels (bitwise equal)."""
-    w = W.get_config(3).with_(B=64, L=1)
+# The whole batch of each bf16 workload (16384 tokens) through one layer:
+# every product at its full token count (the fused SwiGLU launches, the
+# grouped weight gradients, the 256 x 256 tiles, the attention kernels at the
+# full sequence length).  Loss, every gradient and every post-AdamW weight
+# against the oracle under the fixed whole-step rule (no companion: the
+# oracle alone takes a minute or two at these sizes).
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("ci", [3, 4, 5])
+def test_full_batch_step_one_layer(TS, ci):
+    w = W.get_config(ci).with_(L=1)
     say("full-batch step", w)
-    params, tokens, ts, loss = run_step(TS, w, 1003)
+    params, tokens, ts, loss = run_step(TS, w, 1000 + ci)
     ref = O.train_step(w, params, tokens)
     assert abs(loss - ref["loss"]) <= LOSS_TOL[w.act] * abs(ref["loss"]), (loss, ref["loss"])
     grads = ts.unpack(ts.grads)
     new = ts.unpack(ts.master)
-    _, ccache = O.forward(w, params, tokens, jitter=2.0 ** -24, seed=1)
-    comp = O.backward(w, ccache)
-    for name in params:
-        g = np.asarray(grads[name], np.float64)
-        assert np.all(np.isfinite(g)), name
-        nw, q, worst = band_stats(g, ref["grads"][name])
-        cnw, cq, _ = band_stats(comp[name], ref["grads"][name])
-        print(f"[result] {name}: normwise {nw:.2e} (companion {cnw:.2e}), 99.9% {q:.2f}, worst {worst:.2f} bands")
-        assert nw <= min(2e-2, max(3 * cnw, 2e-3)), (name, nw, cnw)
-        assert q <= max(3 * cq, 1.0), (name, q, cq)
-        assert worst <= 3.0, (name, worst)
-        check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
-                                f"weight {name}", w.adam_eps)
+    check_bf16_step(w, params, tokens, grads, new, ref, f"full batch {w.name} B={w.B} L=1", companion=False)
 
 
 # (config index, overrides, dropout p): p exactly representable in binary32,
@@ -174,12 +165,7 @@ def test_full_step_with_dropout(TS, ci, over, pdrop):
             check(grads[name], ref["grads"][name], w.act, f"grad {name}")
             check_weights(new[name], ref["params"][name], ref["grads"][name], w.act, f"weight {name}")
     else:
-        _, ccache = O.forward(w, params, tokens, jitter=2.0 ** -24, seed=1)
-        comp = O.backward(w, ccache)
-        for name in params:
-            check_bf16_step_tensor(grads[name], ref["grads"][name], comp[name], f"grad {name}")
-            check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
-                                    f"weight {name}", w.adam_eps)
+        check_bf16_step(w, params, tokens, grads, new, ref, f"dropout {w.name} p={pdrop} T={w.T}")
     print(f"[result] {w.name} p={pdrop} loss gpu {loss:.7f} oracle {ref['loss']:.7f} (no dropout "
           f"{plain['loss']:.7f}); gradient change {gd / gn:.2f} of its norm")
 
@@ -234,12 +220,14 @@ def test_full_step_with_gradient_clipping(TS, ci, Bn, kind):
     for name in params:
         if w.act == "f32":
             check_weights(new[name], ref["params"][name], ref["grads"][name], w.act, f"weight {name}")
+            # every element: the oracle's AdamW on the GPU's gradient times the GPU's factor
+            own, _, _ = O.adamw(params[name], sc * grads[name], 0.0, 0.0, 1, w.lr, w.beta1, w.beta2, w.adam_eps,
+                                w.wd)
+            check(new[name], own, "f32", f"weight {name} from the GPU gradient")
         else:
-            check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name],
-                                    f"weight {name}", w.adam_eps)
-        # every element: the oracle's AdamW on the GPU's gradient times the GPU's factor
-        own, _, _ = O.adamw(params[name], sc * grads[name], 0.0, 0.0, 1, w.lr, w.beta1, w.beta2, w.adam_eps, w.wd)
-        check(new[name], own, "f32", f"weight {name} from the GPU gradient")
+            check_bf16_step_tensor(grads[name], ref["grads"][name], f"grad {name}", None, f"clipped {w.name}")
+            check_bf16_step_weights(new[name], ref["params"][name], grads[name], ref["grads"][name], params[name],
+                                    w, f"weight {name}", f"clipped {w.name}", sc)
 
 
 @pytest.mark.timeout(900)
@@ -270,9 +258,11 @@ def test_gradient_accumulation(TS, ci, Bn, S):
         check(gacc[name], gfull[name], "f32", f"accumulated vs full-batch {name}")
     ref_loss, ref = O.accumulated_grads(wm, params, np.split(tokens, S, axis=0))
     assert abs(loss - ref_loss) <= LOSS_TOL[w.act] * abs(ref_loss)
-    if w.act == "f32":
-        for name in ref:
+    for name in ref:
+        if w.act == "f32":
             check(gacc[name], ref[name], "f32", f"accumulated vs oracle {name}")
+        else:
+            check_bf16_step_tensor(gacc[name], ref[name], f"accumulated {name}", None, f"accumulation {w.name} S={S}")
 
 
 def test_step_is_deterministic(TS):
