@@ -146,9 +146,12 @@ def kernel_classes(w, ts, torch, reps, only=None):
                     "frac_of_peak": flops / sec / 1e12 / peak, "flops": flops, "avg_launch_us": sec * 1e6 / len(launches),
                     "bound": "mfma", "peak": peak}
         del bufs
-    if only is not None:
+    if only is not None and only.startswith("gemm"):
         return out
-    # attention: forward, and backward (dQ then dK/dV) on the step's strides
+    # attention: forward, and backward (dQ then dK/dV) on the step's strides,
+    # with q and k taken as already rotated (R = 0), as the step's projection
+    # epilogue leaves them (the per-op calls would otherwise rotate them into
+    # their workspace first)
     d = w.C // w.H
     qd, kd = w.H * d, w.Hkv * d
     ld = qd + 2 * kd + (w.F if w.block != "llama" else 0)
@@ -169,24 +172,156 @@ def kernel_classes(w, ts, torch, reps, only=None):
     def fwd():
         for _ in range(w.L):
             B.slt_attention_fwd(p, p + qd * es, p + (qd + kd) * es, o, lse, ores, ld, ld, ld, qd,
-                                w.B, w.T, w.H, w.Hkv, d, w.R, mode, cs, dt, fw)
+                                w.B, w.T, w.H, w.Hkv, d, 0, mode, cs, dt, fw)
 
     def bwd():
         for _ in range(w.L):
             B.slt_attention_bwd(p, p + qd * es, p + (qd + kd) * es, o, ores, g, lse, dp, dp + qd * es,
-                                dp + (qd + kd) * es, ld, ld, ld, qd, qd, ld, ld, ld, w.B, w.T, w.H, w.Hkv, d, w.R,
+                                dp + (qd + kd) * es, ld, ld, ld, qd, qd, ld, ld, ld, w.B, w.T, w.H, w.Hkv, d, 0,
                                 mode, cs, dt, aws)
 
     fa, ba = attn_flops(w)
+    fwd()  # lse for the backward
     for name, fn, fl, nl in [("attention_fwd", fwd, fa, w.L), ("attention_bwd", bwd, ba, 2 * w.L)]:
+        if only is not None and name != only:
+            continue
         sec = time_block(fn, reps, torch)
         out[name] = {"ms_per_step": sec * 1e3, "launches": nl, "tflops": fl / sec / 1e12,
                      "frac_of_peak": fl / sec / 1e12 / peak, "flops": fl, "avg_launch_us": sec * 1e6 / nl,
                      "bound": "mfma", "peak": peak}
     del qkv, o, ores, g, dqkv, aws
-    # HBM-bound optimizer-side kernels over the flat parameter buffer: AdamW
-    # (theta, g, m, v read; theta, m, v written; the bf16 copy written) and
-    # the global gradient norm used for clipping (g read once)
+    return out
+
+
+def time_cold(fn, reps, torch, evict):
+    """Median and best seconds of single fn() launches, each timed alone with
+    HIP events on the current stream, with a 512 MiB copy between them (not
+    timed) so that the 256 MB Infinity Cache holds none of fn's data: the
+    HBM rate, not the cache's."""
+    src, dst = evict
+    from scratch_llama_transformer_amd import binding as B
+    s = torch.cuda.current_stream()
+    fn()
+    times = []
+    for _ in range(reps):
+        B.slt_stream_copy(src, dst, src.numel())
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        fn()
+        b.record(s)
+        b.synchronize()
+        times.append(a.elapsed_time(b) / 1e3)
+    times.sort()
+    return times[len(times) // 2], times[0]
+
+
+def machine_bounds(torch):
+    """The library's own streaming copy over 2 x 2 GiB (read + write GB/s,
+    best of 5) and its MFMA loop (bf16 TFLOP/s, best of 5): the measured
+    bounds the kernels are also reported against."""
+    from scratch_llama_transformer_amd import binding as B
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    s = torch.cuda.current_stream()
+    best = None
+    for _ in range(6):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        B.slt_stream_copy(src, dst, n)
+        b.record(s)
+        b.synchronize()
+        t = a.elapsed_time(b) / 1e3
+        best = t if best is None else min(best, t)
+    del src, dst
+    blocks, iters = 256 * 8, 4096
+    out = torch.empty(blocks * 256, device="cuda")
+    bestm = None
+    for _ in range(6):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        B.slt_mfma_loop(blocks, iters, out)
+        b.record(s)
+        b.synchronize()
+        t = a.elapsed_time(b) / 1e3
+        bestm = t if bestm is None else min(bestm, t)
+    return {"copy_gbps": round(2.0 * n / best / 1e9, 1), "copy_bytes": 2 * n,
+            "mfma_bf16_tflops": round(B.slt_mfma_loop_flops(blocks, iters) / bestm / 1e12, 1),
+            "copy_kernel": "slt_stream_copy (16-byte loads and stores, 2 GiB each way)",
+            "mfma_kernel": "slt_mfma_loop (8 independent v_mfma_f32_16x16x32_bf16 chains per wave, 8 waves per CU)"}
+
+
+def hbm_classes(w, torch, reps, machine):
+    """Every HBM-bound kernel of the step at the step's sizes and strides,
+    each launch timed alone on a cold cache (time_cold): norm forward and
+    backward, SwiGLU or GELU forward and backward, softmax cross-entropy,
+    embedding forward and backward, AdamW and the gradient norm.  Bytes are
+    the algorithmic ones (each operand read or written once)."""
+    from scratch_llama_transformer_amd import binding as B
+    import slt_workloads as W
+    dt = B.BF16 if w.act == "bf16" else B.F32
+    tdt = torch.bfloat16 if dt == B.BF16 else torch.float32
+    e = 2 if dt == B.BF16 else 4
+    N, C, F, V = w.N, w.C, w.F, w.V
+    ev = (torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(0),
+          torch.empty(512 << 20, dtype=torch.uint8, device="cuda"))
+    rnd = lambda *shape: torch.empty(*shape, dtype=tdt, device="cuda").normal_()
+    out = {}
+
+    def add(name, fn, byt):
+        med, best = time_cold(fn, reps, torch, ev)
+        gbs = byt / med / 1e9
+        out[name] = {"us_per_launch": round(med * 1e6, 2), "best_us": round(best * 1e6, 2), "bytes": int(byt),
+                     "gbps": round(gbs, 1), "frac_of_peak": round(gbs / PEAK["hbm"], 4),
+                     "frac_of_copy": round(gbs / machine["copy_gbps"], 4), "bound": "hbm"}
+
+    x, dy, dres = rnd(N, C), rnd(N, C), rnd(N, C)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    g, bta = torch.ones(C, dtype=tdt, device="cuda"), torch.zeros(C, dtype=tdt, device="cuda")
+    r, mu = torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
+    dg, db = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
+    nws = torch.empty(B.slt_norm_bwd_workspace(N, C), dtype=torch.uint8, device="cuda")
+    if w.block == "llama":
+        B.slt_rmsnorm_fwd(x, g, y, r, N, C, w.eps, dt)
+        add("rmsnorm_fwd", lambda: B.slt_rmsnorm_fwd(x, g, y, r, N, C, w.eps, dt), N * (2 * C * e + 4) + C * e)
+        add("rmsnorm_bwd", lambda: B.slt_rmsnorm_bwd(x, g, r, dy, dres, dx, dg, N, C, dt, nws),
+            N * (4 * C * e + 4) + C * (e + 4))
+        ab, h = rnd(N, 2 * F), torch.empty(N, F, dtype=tdt, device="cuda")
+        dh, dab = rnd(N, F), torch.empty(N, 2 * F, dtype=tdt, device="cuda")
+        pa, pd = ab.data_ptr(), dab.data_ptr()
+        add("swiglu_fwd", lambda: B.slt_swiglu_fwd(pa, pa + F * e, h, N, F, 2 * F, 2 * F, F, dt), 3 * N * F * e)
+        add("swiglu_bwd", lambda: B.slt_swiglu_bwd(pa, pa + F * e, dh, pd, pd + F * e, N, F, 2 * F, 2 * F, F, 2 * F,
+                                                   2 * F, dt), 5 * N * F * e)
+        del ab, h, dh, dab
+    else:
+        B.slt_layernorm_fwd(x, g, bta, y, mu, r, N, C, w.eps, dt)
+        add("layernorm_fwd", lambda: B.slt_layernorm_fwd(x, g, bta, y, mu, r, N, C, w.eps, dt),
+            N * (2 * C * e + 8) + 2 * C * e)
+        add("layernorm_bwd", lambda: B.slt_layernorm_bwd(x, g, mu, r, dy, dres, dx, dg, db, N, C, dt, nws),
+            N * (4 * C * e + 8) + C * (e + 8))
+        a, u, du, da = rnd(N, F), torch.empty(N, F, dtype=tdt, device="cuda"), rnd(N, F), torch.empty(N, F, dtype=tdt,
+                                                                                                        device="cuda")
+        add("gelu_fwd", lambda: B.slt_gelu_fwd(a, u, N, F, F, F, dt), 2 * N * F * e)
+        add("gelu_bwd", lambda: B.slt_gelu_bwd(a, du, da, N, F, F, F, F, dt), 3 * N * F * e)
+        del a, u, du, da
+    del x, dy, dres, y, dx, nws
+    tok = torch.from_numpy(W.make_tokens(w, 1000)).cuda()
+    z = rnd(N, V)
+    loss = torch.empty(1, device="cuda")
+    rl = torch.empty(4 * N, dtype=torch.uint8, device="cuda")
+    add("softmax_xent", lambda: B.slt_softmax_xent(z, V, tok, w.B, w.T, w.T + 1, V, loss, None, dt, rl),
+        2 * N * V * e + 4 * N)
+    del z
+    wte, xe = rnd(V, C), torch.empty(N, C, dtype=tdt, device="cuda")
+    add("embedding_fwd", lambda: B.slt_embedding_fwd(tok, w.B, w.T, w.T + 1, wte, xe, V, C, dt), N * (2 * C * e + 4))
+    dwte = torch.empty(V, C, device="cuda")
+    ews = torch.empty(B.slt_embedding_bwd_workspace(N, V), dtype=torch.uint8, device="cuda")
+    add("embedding_bwd", lambda: B.slt_embedding_bwd(tok, w.B, w.T, w.T + 1, xe, dwte, V, C, dt, ews),
+        N * (C * e + 4) + V * C * 4)
+    del wte, xe, dwte, ews
     _, n = B.slt_param_layout(B.make_config(w))
     th = torch.empty(n, device="cuda").normal_(0, 0.02)
     gr = torch.empty(n, device="cuda").normal_(0, 1e-3)
@@ -195,34 +330,29 @@ def kernel_classes(w, ts, torch, reps, only=None):
     sh = torch.empty(n, dtype=torch.int16, device="cuda") if dt == B.BF16 else None
     cws = torch.empty(B.slt_clip_workspace_bytes(), dtype=torch.uint8, device="cuda")
     nrm = torch.empty(2, device="cuda")
-    byt_adamw = n * (30 if sh is not None else 28)
-    hbm = PEAK["hbm"]
-    for name, fn, byt, nl in [
-        ("adamw", lambda: B.slt_adamw_step(n, th, sh, gr, m, v, 1, 1e-3, 0.9, 0.999, 1e-8, 0.1), byt_adamw, 1),
-        ("grad_norm", lambda: B.slt_clip_grad_norm(n, gr, B.NORM_L2, 1.0, nrm, nrm.data_ptr() + 4, cws), 4 * n, 1),
-    ]:
-        sec = time_block(fn, reps, torch)
-        gbs = byt / sec / 1e9
-        out[name] = {"ms_per_step": sec * 1e3, "launches": nl, "gbps": gbs, "frac_of_peak": gbs / hbm,
-                     "bytes": byt, "avg_launch_us": sec * 1e6 / nl, "bound": "hbm", "peak": hbm}
+    add("adamw", lambda: B.slt_adamw_step(n, th, sh, gr, m, v, 1, 1e-3, 0.9, 0.999, 1e-8, 0.1),
+        n * (30 if sh is not None else 28))
+    add("grad_norm", lambda: B.slt_clip_grad_norm(n, gr, B.NORM_L2, 1.0, nrm, nrm.data_ptr() + 4, cws), 4 * n)
     return out
 
 
-def measured_traffic(w):
-    """HBM bytes per launch of the forward-projection GEMM from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by a plain copy's
-    counts; None when that summary is for another workload or for a GEMM
-    source other than the one built now."""
+def measured_traffic(w, cls):
+    """HBM bytes per launch of a kernel class from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (profiles/<class>_traffic.json), scaled by
+    a plain copy's counts; None when that summary is for another workload or
+    for kernel sources other than the ones built now."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gemm_fwd_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{cls}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
-        with open(os.path.join(ROOT, "scratch_llama_transformer_amd", "csrc", "gemm.hip"), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = hashlib.sha256()
+        for src in rec.get("sources", ["gemm.hip"]):
+            with open(os.path.join(ROOT, "scratch_llama_transformer_amd", "csrc", src), "rb") as f:
+                sha.update(f.read())
     except OSError:
         return None
-    if rec.get("gemm_hip_sha256") != sha or rec.get("workload") != w.name:
+    if rec.get("sources_sha256") != sha.hexdigest() or rec.get("workload") != w.name:
         return None
     return rec.get("bytes_per_launch")
 
@@ -245,7 +375,17 @@ def cpu_baseline(w):
     t0 = time.perf_counter()
     O.train_step(ws, params, tokens)
     dt = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(Bs * w.T / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"one full step (forward, backward, AdamW on all {W.n_params(ws)} parameters) on {Bs} of "
                       f"the {w.B} sequences ({Bs * w.T} tokens), float64 numpy; {dt:.1f} s"}
 
@@ -259,7 +399,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
-    ap.add_argument("--only-class", choices=["gemm_fwd", "gemm_dx", "gemm_dw"], default=None,
+    ap.add_argument("--only-class", choices=["gemm_fwd", "gemm_dx", "gemm_dw", "attention_fwd", "attention_bwd"],
+                    default=None,
                     help="only time one GEMM class of the breakdown (for hardware-counter runs) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (for scaling HBM byte counters) and exit")
@@ -297,15 +438,15 @@ def main():
         ts.step(tok)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for _ in range(args.steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(s)
+    for i in range(args.steps):
         ts.step(tok)
-    e1.record(s)
-    e1.synchronize()
+        ev[i + 1].record(s)
+    ev[-1].synchronize()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     loss = float(ts.loss.item())
     tps = w.N / (ms / 1e3)
     flops = step_flops(w)
@@ -318,6 +459,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
+        "ms_per_step_best": round(per_step[0], 4),
+        "tokens_per_s_median": round(w.N / (per_step[len(per_step) // 2] / 1e3), 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -333,21 +477,33 @@ def main():
     del ts
     torch.cuda.empty_cache()
     if not args.no_breakdown:
+        machine = machine_bounds(torch)
+        out["machine"] = machine
         cl = kernel_classes(w, None, torch, args.kernel_reps)
+        mpeak = machine["mfma_bf16_tflops"] if w.act == "bf16" else None
+        for v in cl.values():
+            if mpeak:
+                v["frac_of_measured"] = v["tflops"] / mpeak
         out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
-                              if kk in ("ms_per_step", "launches", "tflops", "gbps", "frac_of_peak", "avg_launch_us")}
+                              if kk in ("ms_per_step", "launches", "tflops", "frac_of_peak", "frac_of_measured",
+                                        "avg_launch_us")}
                           for k, v in cl.items()}
-        # the dominant kernel class of the step (largest time in the
-        # breakdown): the forward-projection GEMMs, both operands k-major
-        # (bf16: gemm_d64_k for 384 to 1152 output columns, gemm_w8_k's
-        # 256 x 256 tiles for the wide ones; fp32: gemm_k on the fp32 matrix
-        # instructions)
-        c = cl["gemm_fwd"]
-        kern = "gemm_k, fp32" if w.act == "f32" else "gemm_d64_k, gemm_w8_k"
-        out["roofline"] = {"kernel": f"forward-projection GEMMs ({kern}; k-major x k-major)",
-                           "bound": c["bound"],
+        out["hbm_kernels"] = hbm_classes(w, torch, max(args.kernel_reps, 5), machine)
+        # the dominant kernel class of the step: the largest time per step in
+        # the breakdown (MFMA classes; the HBM-bound kernels above each take
+        # a smaller share)
+        name = max(cl, key=lambda k: cl[k]["ms_per_step"])
+        c = cl[name]
+        kern = {"gemm_fwd": "forward-projection GEMMs (k-major x k-major)",
+                "gemm_dx": "activation-gradient GEMMs dX = dY W",
+                "gemm_dw": "grouped weight-gradient GEMMs dW = dY^T X",
+                "attention_fwd": "causal attention forward (fl_fwd_k)",
+                "attention_bwd": "causal attention backward (fl_dq_k + fl_dkdv2_k)"}[name]
+        out["roofline"] = {"kernel": kern, "class": name, "bound": c["bound"],
                            "achieved": round(c["tflops"], 2), "peak": c["peak"], "unit": "TFLOP/s",
-                           "frac": round(c["tflops"] / c["peak"], 4), "traffic": measured_traffic(w),
+                           "frac": round(c["tflops"] / c["peak"], 4),
+                           "frac_of_measured": round(c["tflops"] / mpeak, 4) if mpeak else None,
+                           "traffic": measured_traffic(w, name),
                            "avg_launch_us": round(c["avg_launch_us"], 2), "launches_per_step": c["launches"]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

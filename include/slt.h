@@ -30,7 +30,11 @@
  *   - "bf16" storage is the upper 16 bits of an IEEE binary32 (uint16_t in
  *     this header); rounding to it is to nearest, ties to even.
  *   - Device pointers point to memory the caller allocated and owns; the
- *     library allocates no device memory and keeps no device state.
+ *     library allocates no device memory.  Its only device state is, per
+ *     device, one second stream (default priority, non-blocking) and six
+ *     events that the three backward calls create on their first use and
+ *     keep until the process ends; every other call uses only the caller's
+ *     stream.
  *   - Calls taking a stream only enqueue work on it (a hipStream_t passed as
  *     void*; NULL is the null stream) and return without synchronising.
  *     Faults inside kernels surface at the caller's next synchronisation.
@@ -196,9 +200,13 @@ slt_status slt_backward_adamw(const slt_config* cfg, const void* params, const i
  * scale = 1/S, starting from zeroed grads, the result is the gradient of the
  * mean loss over all S micro-batches -- the full batch's gradient, up to the
  * summation order.  Activation gradients are not scaled; only the writes of
- * parameter gradients are. */
+ * parameter gradients are.  loss / loss_sum (device fp32 scalars, both given
+ * or both NULL): *loss_sum += scale * *loss, on the device, with loss the
+ * micro-batch's mean loss that slt_forward_loss wrote -- from a zeroed
+ * loss_sum, the mean loss over the micro-batches. */
 slt_status slt_backward_accumulate(const slt_config* cfg, const void* params, const int32_t* tokens,
-                                   void* acts, void* scratch, float* grads, float scale, void* stream);
+                                   void* acts, void* scratch, float* grads, float scale, const float* loss,
+                                   float* loss_sum, void* stream);
 
 /* Key/value-cache forward (randyGPT, "Features": the prompt is run once and
  * each further token costs one single-token forward; Transformer in Rust,
@@ -324,6 +332,19 @@ slt_status slt_mlp_swiglu_fwd(int32_t M, int32_t F, int32_t C, const void* x, co
 slt_status slt_proj_gelu_fwd(int32_t M, int32_t N, int32_t K, const void* x, const void* w, void* y, int64_t ldy,
                              int32_t col0, void* u, int64_t ldu, int32_t dtype, void* stream);
 
+/* QKV projection with RoPE in its epilogue (Hephaistos, "Architecture at a
+ * glance": RoPE on q and k; Transformer in Rust, "Key Features"):
+ *   y[M, N] = x[M, K] w[N, K]^T   (row stride ldy)
+ * where columns [0, H d) are the query heads and [H d, (H + Hkv) d) the key
+ * heads of d dims: their first R dims are rotated as slt_rope_fwd does, with
+ * row m at position m % T, in fp32 before the one rounding to dtype.  The
+ * remaining columns (values, and any further projection) are the plain
+ * product.  This is the training forward's QKV step: the stored q and k are
+ * the rotated ones. */
+slt_status slt_qkv_rope_fwd(int32_t M, int32_t N, int32_t K, const void* x, const void* w, void* y, int64_t ldy,
+                            int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R, int32_t rope_mode, const float* cs,
+                            int32_t dtype, void* stream);
+
 /* Its backward into the projection outputs:
  *   dh = dy[M, C] W2[C, F]  -> dh_workspace [M, F] in dtype (row stride F)
  *   da, db from a, b (ab, row stride 2F) and dh  ->  dab[M, 2F] = [da | db]
@@ -378,6 +399,21 @@ slt_status slt_layernorm_bwd(const void* x, const void* gamma, const float* mean
  * [T, R] on the device. */
 slt_status slt_rope_table(int32_t T, int32_t R, float base, float* cs, void* stream);
 
+/* RoPE (Hephaistos, "Architecture at a glance": rotary embedding of q and
+ * k; Transformer in Rust, "Key Features": even-odd pairs, "Model
+ * Configurations": rotary dims 32 of 64).  Row r = b*T + t (position t) of x
+ * holds nheads heads of d dims (head h at x + r*ldx + h*d); each pair (u, w)
+ * of its first R dims -- (j, j + R/2) for SLT_ROPE_HALF, (2j, 2j+1) for
+ * SLT_ROPE_PAIRS, j < R/2 -- becomes (u c - w s, u s + w c) with (c, s) =
+ * cs[t*R + 2j], cs[t*R + 2j + 1] (the table of slt_rope_table), computed in
+ * fp32 and rounded once to dtype.  Dims >= R are copied.  y may equal x
+ * (then ldy = ldx).  slt_rope_bwd applies the transposed rotation (angle
+ * -t theta_j): the gradient with respect to the un-rotated input. */
+slt_status slt_rope_fwd(const void* x, int64_t ldx, void* y, int64_t ldy, int32_t B, int32_t T, int32_t nheads,
+                        int32_t d, int32_t R, int32_t rope_mode, const float* cs, int32_t dtype, void* stream);
+slt_status slt_rope_bwd(const void* dy, int64_t lddy, void* dx, int64_t lddx, int32_t B, int32_t T, int32_t nheads,
+                        int32_t d, int32_t R, int32_t rope_mode, const float* cs, int32_t dtype, void* stream);
+
 /* Causal attention forward, RoPE applied to q and k as they are loaded
  * (Hephaistos, "Architecture at a glance"; strata, flash-style attention with
  * online softmax and no T x T scores).  Head h of token b*T+t reads
@@ -387,10 +423,12 @@ slt_status slt_rope_table(int32_t T, int32_t R, float base, float* cs, void* str
  * o_res (may be NULL): dense [B*T, H*d] in dtype, receives o - round(o), the
  * part of the output its storage type dropped; the backward uses it.
  * cs: the RoPE table of slt_rope_table for (T, R); R = 0 disables RoPE.
- * workspace: slt_attention_fwd_workspace(...) bytes of device memory owned by
- * the caller (16-byte aligned; NULL allowed when that size is 0), scratch for
- * the call only: bf16 operands with d a multiple of 16 (d <= 64) rotate q and
- * k once into it before the tiled kernel runs. */
+ * bf16: the rotated q and k are rounded once to bf16 before the products (as
+ * the training step stores them).  workspace: slt_attention_fwd_workspace(...)
+ * bytes of device memory owned by the caller (16-byte aligned; NULL allowed
+ * when that size is 0), scratch for the call only: bf16 operands with d a
+ * multiple of 16 (d <= 64) and R > 0 are rotated once into it (slt_rope_fwd)
+ * before the tiled kernel runs. */
 int64_t slt_attention_fwd_workspace(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d,
                                     int32_t dtype);
 slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -405,7 +443,7 @@ slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* 
  * written by the forward, or NULL.  workspace: at least
  * slt_attention_bwd_workspace(B, T, H, Hkv, d, dtype) bytes of caller-owned,
  * 16-byte aligned device memory (per-row D = dO.O, and for bf16 the rotated
- * q/k copies), scratch for the call only. */
+ * q/k copies, rounded once as in the forward), scratch for the call only. */
 int64_t slt_attention_bwd_workspace(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d,
                                     int32_t dtype);
 slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -441,6 +479,23 @@ slt_status slt_gelu_bwd(const void* a, const void* du, void* da, int32_t rows, i
 slt_status slt_softmax_xent(void* z, int64_t ldz, const int32_t* tokens, int32_t B, int32_t T,
                             int64_t ld_tokens, int32_t V, float* loss, float* lse, int32_t dtype,
                             void* workspace, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Machine bounds (strata, benchmark methodology: kernels are reported as a
+ * fraction of a measured machine bound)
+ * ---------------------------------------------------------------------- */
+
+/* dst = src over `bytes` bytes (a multiple of 16; both 16-byte aligned, not
+ * overlapping) with 16-byte loads and stores: the read + write rate a
+ * streaming kernel reaches on this GPU. */
+slt_status slt_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* `blocks` workgroups of 4 waves, each wave running `iters` rounds of 8
+ * independent v_mfma_f32_16x16x32_bf16 on register operands; out receives
+ * 256 * blocks floats (so the work is not dead).  slt_mfma_loop_flops gives
+ * the FLOPs one call performs.  Host only / device call. */
+int64_t slt_mfma_loop_flops(int32_t blocks, int32_t iters);
+slt_status slt_mfma_loop(int32_t blocks, int32_t iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,10 +28,11 @@ Readings taken where the pages are silent are stated next to the code.
 Precision model.  For fp32 configurations the oracle runs in float64 without
 rounding.  For bf16 configurations it applies ``bf16_round`` at every point
 where the GPU path stores a bf16 tensor in memory (weights' compute copy,
-residual stream, norm outputs, projections, attention output, MLP
-activations, logits, and every activation gradient); statistics, weight
-gradients, optimizer state and the loss stay float64.  Values a GPU kernel
-rounds only inside registers (rotated q/k, probabilities) are not rounded here.
+residual stream, norm outputs, projections -- q and k after RoPE --, attention
+output, MLP activations, logits, and every activation gradient); statistics,
+weight gradients, optimizer state and the loss stay float64.  Values a GPU
+kernel rounds only inside registers (probabilities, score gradients) are not
+rounded here.
 """
 from __future__ import annotations
 
@@ -422,10 +423,13 @@ def forward(cfg, params, tokens, jitter=0.0, seed=0):
                  x += W_2 (silu(a) * b) with a, b = RMSNorm(x) W_1^T, RMSNorm(x) W_3^T.
     Parallel block: n = LayerNorm(x); x += [attn(n) | gelu(n W_in^T)] W_out^T.
     Final norm, then z = n_f W_head^T and the mean cross-entropy.
-    jitter/seed: see store_fn (0 for the reference computation).
+    jitter/seed: see store_fn (0 for the reference computation).  Jitter
+    applies to stored activations and activation gradients only: the bf16
+    compute copy of the weights is one rounding of the fp32 master with no
+    summation in front of it, so every valid computation holds the same copy.
     Returns (loss, cache) where cache holds what the backward reads."""
     S = store_fn(cfg.act, jitter, seed)
-    W = {k: S(np.asarray(v, np.float64)) for k, v in params.items()}
+    W = {k: store_fn(cfg.act)(np.asarray(v, np.float64)) for k, v in params.items()}
     tokens = np.asarray(tokens)
     B, T = tokens.shape[0], tokens.shape[1] - 1
     X, Y = tokens[:, :T].reshape(-1), tokens[:, 1:].reshape(-1)
@@ -455,16 +459,19 @@ def forward(cfg, params, tokens, jitter=0.0, seed=0):
         if cfg.block == "llama":
             n1, r1 = rmsnorm_fwd(x, W[p + "attn_norm"], cfg.eps)
             n1 = S(n1)
-            qkv = S(n1 @ W[p + "qkvw"].T)
+            qkv = n1 @ W[p + "qkvw"].T
         else:
             n1, mu1, r1 = layernorm_fwd(x, W[p + "ln_g"], W[p + "ln_b"], cfg.eps)
             n1 = S(n1)
-            qkv = S(n1 @ W[p + "qkvw"].T)
+            qkv = n1 @ W[p + "qkvw"].T
             a = S(n1 @ W[p + "fc_in"].T)
             c.update(mu1=mu1, a=a)
-        q = rope_apply(_heads(qkv[:, :qd], B, T, H, d), cos, sin, R, cfg.rope_mode)
-        k = rope_apply(_heads(qkv[:, qd:qd + kd], B, T, Hkv, d), cos, sin, R, cfg.rope_mode)
-        v = _heads(qkv[:, qd + kd:], B, T, Hkv, d)
+        # RoPE belongs to the q/k projection's output (Hephaistos, "Architecture
+        # at a glance": RoPE applied to q and k inside attention): the stored
+        # activation is the rotated q and k, rounded once, and v
+        q = S(rope_apply(_heads(qkv[:, :qd], B, T, H, d), cos, sin, R, cfg.rope_mode))
+        k = S(rope_apply(_heads(qkv[:, qd:qd + kd], B, T, Hkv, d), cos, sin, R, cfg.rope_mode))
+        v = S(_heads(qkv[:, qd + kd:], B, T, Hkv, d))
         ma = None if p_drop <= 0 else dropout_multiplier(p_drop, seed_drop, 3, l, B * H * T, T).reshape(B, H, T, T)
         o4, lse = attention_fwd(q, k, v, ma)
         o = S(_unheads(o4))

@@ -60,7 +60,7 @@ SIGNATURES = {
     "slt_cast_bf16": (_I32, [_P, _P, _I64, _P]),
     "slt_forward_loss": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _P]),
     "slt_backward": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _P]),
-    "slt_backward_accumulate": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _F, _P]),
+    "slt_backward_accumulate": (_I32, [ct.POINTER(slt_config), _P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "slt_kv_cache_bytes": (_I32, [ct.POINTER(slt_config), _I32, _I32, _I32, ct.POINTER(_I64), ct.POINTER(_I64)]),
     "slt_forward_cached": (_I32, [ct.POINTER(slt_config), _P, _P, _I32, _I32, _I64, _I32, _P, _I32, _P, _I32,
                                   _P, _I64, _P]),
@@ -73,6 +73,8 @@ SIGNATURES = {
     "slt_mlp_swiglu_fwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _I32, _P]),
     "slt_proj_gelu_fwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I64, _I32, _P]),
     "slt_mlp_swiglu_bwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _P]),
+    "slt_qkv_rope_fwd": (_I32, [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32,
+                                _P]),
     "slt_gemm_dw_group": (_I32, [ct.POINTER(slt_gemm_group_item), _I32, _I32, _P, _I64, _P]),
     "slt_embedding_fwd": (_I32, [_P, _I32, _I32, _I64, _P, _P, _I32, _I32, _I32, _P]),
     "slt_embedding_bwd_workspace": (_I64, [_I64, _I32]),
@@ -83,6 +85,8 @@ SIGNATURES = {
     "slt_layernorm_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _F, _I32, _P]),
     "slt_layernorm_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P]),
     "slt_rope_table": (_I32, [_I32, _I32, _F, _P, _P]),
+    "slt_rope_fwd": (_I32, [_P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
+    "slt_rope_bwd": (_I32, [_P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
     "slt_attention_fwd_workspace": (_I64, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "slt_attention_fwd": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
                                  _I32, _I32, _I32, _P, _I32, _P, _P]),
@@ -95,6 +99,9 @@ SIGNATURES = {
     "slt_gelu_fwd": (_I32, [_P, _P, _I32, _I32, _I64, _I64, _I32, _P]),
     "slt_gelu_bwd": (_I32, [_P, _P, _P, _I32, _I32, _I64, _I64, _I64, _I32, _P]),
     "slt_softmax_xent": (_I32, [_P, _I64, _P, _I32, _I32, _I64, _I32, _P, _P, _I32, _P, _P]),
+    "slt_stream_copy": (_I32, [_P, _P, _I64, _P]),
+    "slt_mfma_loop_flops": (_I64, [_I32, _I32]),
+    "slt_mfma_loop": (_I32, [_I32, _I32, _P, _P]),
 }
 
 _lib = None
@@ -222,10 +229,10 @@ def slt_backward(cfg, params, tokens, acts, scratch, grads, stream=None):
                                                _ptr(scratch), _ptr(grads), _stream(stream)))
 
 
-def slt_backward_accumulate(cfg, params, tokens, acts, scratch, grads, scale, stream=None):
+def slt_backward_accumulate(cfg, params, tokens, acts, scratch, grads, scale, loss=None, loss_sum=None, stream=None):
     _check("slt_backward_accumulate", load().slt_backward_accumulate(
-        ct.byref(cfg), _ptr(params), _ptr(tokens), _ptr(acts), _ptr(scratch), _ptr(grads), scale,
-        _stream(stream)))
+        ct.byref(cfg), _ptr(params), _ptr(tokens), _ptr(acts), _ptr(scratch), _ptr(grads), scale, _ptr(loss),
+        _ptr(loss_sum), _stream(stream)))
 
 
 def slt_kv_cache_bytes(cfg, B, Tq, Tmax):
@@ -273,6 +280,11 @@ def slt_mlp_swiglu_fwd(M, F, C, x, w13, ab, h, dtype, stream=None):
 def slt_proj_gelu_fwd(M, N, K, x, w, y, ldy, col0, u, ldu, dtype, stream=None):
     _check("slt_proj_gelu_fwd", load().slt_proj_gelu_fwd(M, N, K, _ptr(x), _ptr(w), _ptr(y), ldy, col0, _ptr(u), ldu,
                                                          dtype, _stream(stream)))
+
+
+def slt_qkv_rope_fwd(M, N, K, x, w, y, ldy, T, H, Hkv, d, R, rope_mode, cs, dtype, stream=None):
+    _check("slt_qkv_rope_fwd", load().slt_qkv_rope_fwd(M, N, K, _ptr(x), _ptr(w), _ptr(y), ldy, T, H, Hkv, d, R,
+                                                       rope_mode, _ptr(cs), dtype, _stream(stream)))
 
 
 def slt_mlp_swiglu_bwd(M, F, C, dy, w2, ab, dab, dh_workspace, dtype, stream=None):
@@ -324,6 +336,16 @@ def slt_rope_table(T, R, base, cs, stream=None):
     _check("slt_rope_table", load().slt_rope_table(T, R, base, _ptr(cs), _stream(stream)))
 
 
+def slt_rope_fwd(x, ldx, y, ldy, B, T, nheads, d, R, rope_mode, cs, dtype, stream=None):
+    _check("slt_rope_fwd", load().slt_rope_fwd(_ptr(x), ldx, _ptr(y), ldy, B, T, nheads, d, R, rope_mode, _ptr(cs),
+                                               dtype, _stream(stream)))
+
+
+def slt_rope_bwd(dy, lddy, dx, lddx, B, T, nheads, d, R, rope_mode, cs, dtype, stream=None):
+    _check("slt_rope_bwd", load().slt_rope_bwd(_ptr(dy), lddy, _ptr(dx), lddx, B, T, nheads, d, R, rope_mode,
+                                               _ptr(cs), dtype, _stream(stream)))
+
+
 def slt_attention_fwd(q, k, v, o, lse, o_res, ldq, ldk, ldv, ldo, B, T, H, Hkv, d, R, rope_mode, cs, dtype,
                       workspace=None, stream=None):
     _check("slt_attention_fwd", load().slt_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(o_res),
@@ -362,3 +384,15 @@ def slt_gelu_bwd(a, du, da, rows, F, lda, lddu, ldda, dtype, stream=None):
 def slt_softmax_xent(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtype, workspace, stream=None):
     _check("slt_softmax_xent", load().slt_softmax_xent(_ptr(z), ldz, _ptr(tokens), B, T, ld_tokens, V, _ptr(loss),
                                                        _ptr(lse), dtype, _ptr(workspace), _stream(stream)))
+
+
+def slt_stream_copy(src, dst, nbytes, stream=None):
+    _check("slt_stream_copy", load().slt_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def slt_mfma_loop_flops(blocks, iters) -> int:
+    return int(load().slt_mfma_loop_flops(blocks, iters))
+
+
+def slt_mfma_loop(blocks, iters, out, stream=None):
+    _check("slt_mfma_loop", load().slt_mfma_loop(blocks, iters, _ptr(out), _stream(stream)))

@@ -51,7 +51,7 @@ struct LayerP {
 };
 
 struct LayerA {
-  int64_t n1, r1, mu1, qkv, o, ores, lse, n2, r2, ab, h, rot;  // byte offsets in the arena (-1: absent)
+  int64_t n1, r1, mu1, qkv, o, ores, lse, n2, r2, ab, h;  // byte offsets in the arena (-1: absent)
 };
 
 struct Plan {
@@ -179,8 +179,6 @@ static slt_status make_plan(const slt_config* cfg, Plan& p) {
     A.mu1 = p.llama ? -1 : take(N * 4);
     A.lse = take((int64_t)c.B * c.H * c.T * 4);
     A.ores = p.bf ? take(N * p.qd * es) : -1;  // bf16 rounding residual of the attention output
-    // rotated hi/lo copies of q and k, made by the forward, reused by the backward
-    A.rot = flash_eligible(c.act, p.d) ? take(flash_rot_elems(c.B, c.T, c.H, c.Hkv, p.d) * 2) : -1;
     if (p.llama) {
       A.qkv = take(N * p.qkv_w * es);
       A.o = take(N * p.qd * es);
@@ -316,6 +314,40 @@ static slt_status proj_gelu(int M, int N, int K, const void* n, const void* w, c
   return launch_gelu_fwd(y + col0 * es, u, M, N - col0, ldy, ldu, dt, s);
 }
 
+// Whether the step stores q and k rotated: the bf16 attention kernels read
+// them rotated and rounded once (RoPE in the QKV projection's epilogue).
+static bool rope_in_projection(const Plan& p) { return flash_eligible(p.c.act, p.d); }
+
+// y[M, N] = n W^T (row stride ldy) whose first (H + Hkv) d columns are the q
+// and k heads, RoPE'd by row position m % T before the one rounding: the
+// projection's epilogue where it applies, else the plain product and RoPE in
+// place.  R = 0: the plain product.
+static slt_status rope_proj(int M, int N, int K, const void* n, const void* w, char* y, int64_t ldy, int T, int H,
+                            int Hkv, int d, int R, int mode, const float* cs, int dt, hipStream_t s) {
+  GemmArgs g{M, N, K, n, K, true, w, K, true, y, ldy, nullptr, 0, dt, dt, nullptr, 0};
+  if (R == 0) return launch_gemm(g, s);
+  RopeEpi r;
+  r.cs = cs;
+  r.T = T;
+  r.d = d;
+  r.R = R;
+  r.end = (H + Hkv) * d;
+  r.half = mode == SLT_ROPE_HALF;
+  const slt_status st = launch_gemm_rope(g, r, s);
+  if (st != SLT_EUNSUPPORTED) return st;
+  SLT_TRY(launch_gemm(g, s));
+  const int64_t es = dt == SLT_BF16 ? 2 : 4;
+  SLT_TRY(launch_rope(y, ldy, y, ldy, M, T, H, d, R, mode, cs, 1.0f, dt, s));
+  return launch_rope(y + (int64_t)H * d * es, ldy, y + (int64_t)H * d * es, ldy, M, T, Hkv, d, R, mode, cs, 1.0f,
+                     dt, s);
+}
+
+static slt_status proj_rope(const Plan& p, const Ctx& x, int M, int N, int K, const void* n, const void* w, char* y,
+                            int64_t ldy, const float* cs) {
+  const slt_config& c = p.c;
+  return rope_proj(M, N, K, n, w, y, ldy, c.T, c.H, c.Hkv, p.d, c.R, c.rope_mode, cs, x.dt, x.s);
+}
+
 // [da | db] from dh = dY W2 (stored in dh_buf) and the cached [a | b].
 static slt_status mlp_in_bwd(int M, int F, int C, const void* dy, const void* w2, const char* ab, char* dab,
                              void* dh_buf, int dt, hipStream_t s) {
@@ -374,6 +406,7 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
   const int N = p.N, C = c.C;
   const int64_t ldt = c.T + 1;
   float* cs = reinterpret_cast<float*>(x.A(p.cs));
+  const bool rot = rope_in_projection(p);
   if (c.R > 0) SLT_TRY(launch_rope_table(c.T, c.R, c.rope_base, cs, x.s));
   SLT_TRY(launch_embedding_fwd(tok, c.B, c.T, ldt, x.P(p.wte), x.A(p.xs[0]), c.V, C, x.dt, x.s, make_drop(c, 0, 0)));
   for (int l = 0; l < c.L; ++l) {
@@ -384,15 +417,17 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
     at.dtype = x.dt; at.cs = cs;
     at.lse = reinterpret_cast<float*>(x.A(A.lse));
     at.ores_out = A.ores >= 0 ? x.A(A.ores) : nullptr;
-    at.rot = A.rot >= 0 ? x.A(A.rot) : nullptr;
-    at.rot_ready = false;
+    at.qk_rotated = rot;
     at.drop = make_drop(c, 3, l);
     if (p.llama) {
       void* xin = x.A(p.xs[2 * l]);
       void* xmid = x.A(p.xs[2 * l + 1]);
       void* xout = x.A(p.xs[2 * l + 2]);
       SLT_TRY(launch_rmsnorm_fwd(xin, x.P(W.norm1), x.A(A.n1), (float*)x.A(A.r1), N, C, c.eps, x.dt, x.s));
-      SLT_TRY(proj(x, N, p.qkv_w, C, x.A(A.n1), C, x.P(W.qkvw), x.A(A.qkv), p.qkv_w, nullptr, 0));
+      if (rot)
+        SLT_TRY(proj_rope(p, x, N, p.qkv_w, C, x.A(A.n1), x.P(W.qkvw), (char*)x.A(A.qkv), p.qkv_w, cs));
+      else
+        SLT_TRY(proj(x, N, p.qkv_w, C, x.A(A.n1), C, x.P(W.qkvw), x.A(A.qkv), p.qkv_w, nullptr, 0));
       char* qkv = (char*)x.A(A.qkv);
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
       at.ldq = at.ldk = at.ldv = p.qkv_w;
@@ -409,9 +444,15 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
                                    (float*)x.A(A.r1), N, C, c.eps, x.dt, x.s));
       char* qkv = (char*)x.A(A.qkv);
       char* ou = (char*)x.A(A.o);
-      // [q | k | v | a] = n W^T and u = gelu(a) into [o | u]
-      SLT_TRY(proj_gelu(N, p.in_w, C, x.A(A.n1), x.P(W.qkvw), qkv, p.in_w, p.qkv_w, ou + p.qd * p.es, p.ou_w, x.dt,
-                        x.s));
+      // [q | k | v | a] = n W^T (q and k RoPE'd in the epilogue when the
+      // attention reads them rotated) and u = gelu(a) into [o | u]
+      if (rot) {
+        SLT_TRY(proj_rope(p, x, N, p.in_w, C, x.A(A.n1), x.P(W.qkvw), qkv, p.in_w, cs));
+        SLT_TRY(launch_gelu_fwd(qkv + p.qkv_w * p.es, ou + p.qd * p.es, N, c.F, p.in_w, p.ou_w, x.dt, x.s));
+      } else {
+        SLT_TRY(proj_gelu(N, p.in_w, C, x.A(A.n1), x.P(W.qkvw), qkv, p.in_w, p.qkv_w, ou + p.qd * p.es, p.ou_w, x.dt,
+                          x.s));
+      }
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
       at.ldq = at.ldk = at.ldv = p.in_w;
       at.out = ou; at.ldo = p.ou_w;
@@ -503,6 +544,16 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
   DwStream* aux = dw_stream();
   Ctx xw = x;
   if (aux) xw.s = aux->s;
+  // Whatever path leaves this function, the caller's stream ends after all
+  // of the second stream's work (on an error return too, so that the
+  // caller's next call cannot overwrite buffers that work still reads).
+  struct Join {
+    DwStream* aux;
+    hipStream_t s;
+    ~Join() {
+      if (aux && hipEventRecord(aux->fin, aux->s) == hipSuccess) (void)hipStreamWaitEvent(s, aux->fin, 0);
+    }
+  } join{aux, x.s};
   bool pending[3] = {false, false, false};
   auto wait_set = [&](int k) -> slt_status {
     if (!aux || !pending[k]) return SLT_OK;
@@ -581,8 +632,7 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     at.lse_in = (const float*)x.A(A.lse);
     at.delta = (float*)x.S(p.delta);
     at.ores_in = A.ores >= 0 ? x.A(A.ores) : nullptr;
-    at.rot = A.rot >= 0 ? x.A(A.rot) : nullptr;
-    at.rot_ready = true;
+    at.qk_rotated = rope_in_projection(p);
     at.drop = make_drop(c, 3, l);
     char* qkv = (char*)x.A(A.qkv);
     if (p.llama) {
@@ -664,6 +714,7 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
   // the walk's stream ends after everything on the second stream (in order
   // there, so one event after the last launch covers it all)
   if (aux) {
+    join.aux = nullptr;
     SLT_TRY(hip_ok(hipEventRecord(aux->fin, aux->s), "backward: event record"));
     SLT_TRY(hip_ok(hipStreamWaitEvent(x.s, aux->fin, 0), "backward: stream wait"));
   }
@@ -710,7 +761,7 @@ static CachePlan cache_plan(const Plan& p, int B, int Tq, int Tmax) {
   q.ab = p.llama ? take(M * 2 * c.F * es) : -1;
   q.h = p.llama ? take(M * c.F * es) : -1;
   q.lse = take((int64_t)B * c.H * Tq * 4);
-  q.rot = flash_eligible(c.act, p.d) ? take(flash_rot_elems(B, Tq, c.H, c.Hkv, p.d) * 2) : -1;
+  q.rot = flash_eligible(c.act, p.d) ? take(flash_rot_elems(B, Tq, c.H, c.Hkv, p.d) * 2) : -1;  // prefill's rotated q, k
   q.part = take(decode_attention_ws(B, Tq, c.H, c.Hkv, p.d, Tmax));
   q.ws_bytes = a;
   return q;
@@ -754,6 +805,7 @@ static slt_status forward_cached(const Plan& p, const Ctx& x, const CachePlan& q
       at.B = B; at.T = Tq; at.H = c.H; at.Hkv = c.Hkv; at.d = p.d; at.R = c.R; at.rope_mode = c.rope_mode;
       at.dtype = x.dt; at.cs = cs;
       at.lse = (float*)x.A(q.lse);
+      at.qk_rotated = false;
       at.rot = q.rot >= 0 ? x.A(q.rot) : nullptr;
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
       at.ldq = at.ldk = at.ldv = ldqkv;
@@ -894,14 +946,18 @@ slt_status slt_backward_adamw(const slt_config* cfg, const void* params, const i
 }
 
 slt_status slt_backward_accumulate(const slt_config* cfg, const void* params, const int32_t* tokens, void* acts,
-                                   void* scratch, float* grads, float scale, void* stream) {
+                                   void* scratch, float* grads, float scale, const float* loss, float* loss_sum,
+                                   void* stream) {
   Plan p;
   SLT_TRY(make_plan(cfg, p));
   if (!params || !tokens || !acts || !scratch || !grads) return fail(SLT_EINVAL, "backward_accumulate: NULL pointer");
   if (!(scale == scale)) return fail(SLT_EINVAL, "backward_accumulate: scale is NaN");
+  if ((loss == nullptr) != (loss_sum == nullptr))
+    return fail(SLT_EINVAL, "backward_accumulate: loss and loss_sum are both given or both NULL");
   Ctx x{p, as_stream(stream), (char*)acts, (char*)scratch, (const char*)params, cfg->act};
   x.gw.alpha = scale;
   x.gw.accumulate = true;
+  if (loss) SLT_TRY(launch_scalar_axpy(loss_sum, scale, loss, x.s));
   return backward(p, x, tokens, grads);
 }
 
@@ -1025,6 +1081,31 @@ slt_status slt_rope_table(int32_t T, int32_t R, float base, float* cs, void* str
   return launch_rope_table(T, R, base, cs, as_stream(stream));
 }
 
+static slt_status rope_call(const char* what, const void* x, int64_t ldx, void* y, int64_t ldy, int32_t B, int32_t T,
+                            int32_t nheads, int32_t d, int32_t R, int32_t mode, const float* cs, int32_t dtype,
+                            float sign, void* stream) {
+  if (B < 0 || T < 0 || nheads < 0 || d <= 0 || R < 0 || R > d || (R & 1) || !is_dtype(dtype))
+    return fail(SLT_EINVAL, std::string(what) + ": bad sizes (R must be even and <= d)");
+  if (mode != SLT_ROPE_HALF && mode != SLT_ROPE_PAIRS) return fail(SLT_EINVAL, std::string(what) + ": bad rope_mode");
+  if ((int64_t)B * T * nheads == 0) return SLT_OK;
+  if (ldx < (int64_t)nheads * d || ldy < (int64_t)nheads * d)
+    return fail(SLT_EINVAL, std::string(what) + ": row stride smaller than the heads it holds");
+  if (!x || !y || (R > 0 && !cs)) return fail(SLT_EINVAL, std::string(what) + ": NULL pointer");
+  if (x == y && ldx != ldy) return fail(SLT_EINVAL, std::string(what) + ": in place needs equal row strides");
+  if (R == 0 && x == y) return SLT_OK;
+  return launch_rope(x, ldx, y, ldy, (int64_t)B * T, T, nheads, d, R, mode, cs, sign, dtype, as_stream(stream));
+}
+
+slt_status slt_rope_fwd(const void* x, int64_t ldx, void* y, int64_t ldy, int32_t B, int32_t T, int32_t nheads,
+                        int32_t d, int32_t R, int32_t rope_mode, const float* cs, int32_t dtype, void* stream) {
+  return rope_call("rope_fwd", x, ldx, y, ldy, B, T, nheads, d, R, rope_mode, cs, dtype, 1.0f, stream);
+}
+
+slt_status slt_rope_bwd(const void* dy, int64_t lddy, void* dx, int64_t lddx, int32_t B, int32_t T, int32_t nheads,
+                        int32_t d, int32_t R, int32_t rope_mode, const float* cs, int32_t dtype, void* stream) {
+  return rope_call("rope_bwd", dy, lddy, dx, lddx, B, T, nheads, d, R, rope_mode, cs, dtype, -1.0f, stream);
+}
+
 static slt_status attn_check(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R, int32_t mode,
                              int32_t dtype, const float* cs) {
   if (B < 0 || T < 0 || H <= 0 || Hkv <= 0 || d <= 0 || H % Hkv || !is_dtype(dtype))
@@ -1060,8 +1141,8 @@ slt_status slt_attention_fwd(const void* q, const void* k, const void* v, void* 
   a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.d = d; a.R = R; a.rope_mode = rope_mode; a.dtype = dtype; a.cs = cs;
   if (attn_rot_bytes(B, T, H, Hkv, d, dtype) > 0 && !workspace)
     return fail(SLT_EINVAL, "attention_fwd: workspace is NULL (slt_attention_fwd_workspace is non-zero)");
+  a.qk_rotated = false;
   a.rot = workspace;
-  a.rot_ready = false;
   return launch_attention_fwd(a, as_stream(stream));
 }
 
@@ -1091,7 +1172,7 @@ slt_status slt_attention_bwd(const void* q, const void* k, const void* v, const 
   a.delta = static_cast<float*>(workspace);
   a.rot = attn_rot_bytes(B, T, H, Hkv, d, dtype) > 0 ? static_cast<char*>(workspace) + a256(attention_bwd_ws(B, H, T))
                                                       : nullptr;
-  a.rot_ready = false;
+  a.qk_rotated = false;
   return launch_attention_bwd(a, as_stream(stream));
 }
 
@@ -1156,6 +1237,21 @@ slt_status slt_proj_gelu_fwd(int32_t M, int32_t N, int32_t K, const void* x, con
   if (M == 0) return SLT_OK;
   if (!x || !w || !y || !u) return fail(SLT_EINVAL, "proj_gelu_fwd: NULL pointer");
   return proj_gelu(M, N, K, x, w, static_cast<char*>(y), ldy, col0, static_cast<char*>(u), ldu, dtype,
+                   as_stream(stream));
+}
+
+slt_status slt_qkv_rope_fwd(int32_t M, int32_t N, int32_t K, const void* x, const void* w, void* y, int64_t ldy,
+                            int32_t T, int32_t H, int32_t Hkv, int32_t d, int32_t R, int32_t rope_mode, const float* cs,
+                            int32_t dtype, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0 || T <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || ldy < N)
+    return fail(SLT_EINVAL, "qkv_rope_fwd: bad sizes");
+  if ((int64_t)(H + Hkv) * d > N) return fail(SLT_EINVAL, "qkv_rope_fwd: (H + Hkv) d exceeds N");
+  if (R < 0 || R > d || (R & 1)) return fail(SLT_EINVAL, "qkv_rope_fwd: R must be even and <= d");
+  if (rope_mode != SLT_ROPE_HALF && rope_mode != SLT_ROPE_PAIRS) return fail(SLT_EINVAL, "qkv_rope_fwd: bad rope_mode");
+  if (!is_dtype(dtype)) return fail(SLT_EINVAL, "qkv_rope_fwd: bad dtype");
+  if (M == 0) return SLT_OK;
+  if (!x || !w || !y || (R > 0 && !cs)) return fail(SLT_EINVAL, "qkv_rope_fwd: NULL pointer");
+  return rope_proj(M, N, K, x, w, static_cast<char*>(y), ldy, T, H, Hkv, d, R, rope_mode, cs, dtype,
                    as_stream(stream));
 }
 

@@ -26,11 +26,11 @@
 // transposed, the 4-row columns (8-byte stores).  Shapes whose pairs do not
 // fall on 16-byte groups take the element-wise path.
 //
-// Precision (bf16): the rotated q and k, and the probability gradient dS,
-// enter their products as bf16 hi + lo pairs: dS sums to zero along a row and
-// the score differences set the softmax, so a single rounding of either would
-// leave errors proportional to the mean key / query rather than to the
-// result.  D = dO.O uses O with its bf16 rounding residual (see the forward).
+// Precision (bf16): the rotated q and k are rounded once to bf16, as the
+// step stores them (the low parts of their two-term expansions are zero
+// here); the probability gradient dS enters its products as a bf16 hi + lo
+// pair (dS sums to zero along a row).  D = dO.O uses O with its bf16 rounding
+// residual (see the forward).
 #include "slt_internal.h"
 
 #include <math.h>
@@ -213,7 +213,7 @@ __device__ __forceinline__ void stage(const T* base, int64_t ld, int row0, int T
 #pragma unroll
         for (int e = 0; e < G; ++e) {
           hi[rr].e[e] = from_f32<T>(v[rr][e]);
-          lo[rr].e[e] = from_f32<T>(v[rr][e] - to_f32(hi[rr].e[e]));
+          lo[rr].e[e] = zero_v<T>();  // rotated operands are rounded once
         }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -246,7 +246,7 @@ __device__ __forceinline__ void stage(const T* base, int64_t ld, int row0, int T
         f = (ROT && R > 0) ? rope_elem(row, j, t, R, mode, cs, 1.0f) : to_f32(row[j]);
       }
       const T hv = from_f32<T>(f);
-      const T lv = from_f32<T>(f - to_f32(hv));
+      const T lv = zero_v<T>();  // rotated operands are rounded once
       if (X) X[r * XS + j] = hv;
       if (Xl) Xl[r * XS + j] = lv;
       if (Xt) Xt[j * XTS + r] = hv;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void attn_fwd_k(AttnArgs a) {
     float f[4];
     frag_load<T, VEC, true>(qb + (int64_t)qi * a.ldq, qi < T_, 16 * c + g4, d, qi, a.R, a.rope_mode, a.cs, f);
     qf[c] = pack4<T>(f);
-    qfl[c] = low_part<T>(qf[c], f);
+    qfl[c] = Pk<T, 4>{};  // rotated q rounded once
   }
 
   float m = -INFINITY, l = 0.f;
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_k(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dpart += (o[i] + r4[i]) * g[i];
     qf[c] = pack4<T>(f);
-    qfl[c] = low_part<T>(qf[c], f);
+    qfl[c] = Pk<T, 4>{};  // rotated q rounded once
     gf[c] = pack4<T>(g);
   }
   dpart += __shfl_xor(dpart, 16, 64);
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_k(AttnArgs a) {
     frag_load<T, VEC, true>(kb + (int64_t)ki * a.ldk, ki < T_, 16 * c + g4, d, ki, a.R, a.rope_mode, a.cs, f);
     frag_load<T, VEC, false>(vb + (int64_t)ki * a.ldv, ki < T_, 16 * c + g4, d, ki, 0, 0, nullptr, g);
     kf[c] = pack4<T>(f);
-    kfl[c] = low_part<T>(kf[c], f);
+    kfl[c] = Pk<T, 4>{};  // rotated k rounded once
     vf[c] = pack4<T>(g);
   }
 
@@ -788,6 +788,7 @@ static slt_status attn_bwd_t(const AttnArgs& a, hipStream_t s) {
 slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return SLT_OK;
   if (flash_ok(a, false)) return flash_fwd(a, s);
+  if (a.qk_rotated) return fail(SLT_EUNSUPPORTED, "attention: pre-rotated q/k need the bf16 tiled kernels");
   if (a.dtype == SLT_BF16)
     return vec_path_ok<bf16>(a, false) ? attn_fwd_t<bf16, true>(a, s) : attn_fwd_t<bf16, false>(a, s);
   return vec_path_ok<float>(a, false) ? attn_fwd_t<float, true>(a, s) : attn_fwd_t<float, false>(a, s);
@@ -796,6 +797,7 @@ slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s) {
 slt_status launch_attention_bwd(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return SLT_OK;
   if (flash_ok(a, true)) return flash_bwd(a, s);
+  if (a.qk_rotated) return fail(SLT_EUNSUPPORTED, "attention: pre-rotated q/k need the bf16 tiled kernels");
   if (a.dtype == SLT_BF16)
     return vec_path_ok<bf16>(a, true) ? attn_bwd_t<bf16, true>(a, s) : attn_bwd_t<bf16, false>(a, s);
   return vec_path_ok<float>(a, true) ? attn_bwd_t<float, true>(a, s) : attn_bwd_t<float, false>(a, s);

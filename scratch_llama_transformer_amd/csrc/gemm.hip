@@ -206,7 +206,20 @@ struct KArgs {
   int64_t ldc2;
   int F;              // fused SwiGLU epilogues: MLP width (b at column F + f)
   Drop drop;          // C = drop(alpha A B) + R, element (m, n) = e m N + n
+  RopeEpi rope;       // RoPE epilogue (kernels instantiated with it only)
 };
+
+// B-operand row (output column) whose weights a tile column holds under the
+// RoPE epilogue: for rotate-half pairs (j, j + R/2) of a head, tile columns
+// 2i and 2i + 1 hold output dims i and i + R/2, so that each pair lands in
+// one lane's four consecutive accumulator columns; other columns map to
+// themselves (the even-odd pairing is already adjacent).
+__device__ __forceinline__ int rope_row(const RopeEpi& r, int n) {
+  if (!r.half || n >= r.end) return n;
+  const int c = n % r.d;
+  if (c >= r.R) return n;
+  return n - c + ((c & 1) ? (r.R >> 1) + (c >> 1) : (c >> 1));
+}
 
 template <typename TO>
 __device__ __forceinline__ void store4(TO* p, const float (&v)[4]) {
@@ -405,9 +418,9 @@ __device__ __forceinline__ void band_coords(int idx, int tiles, int tiles_n, int
 
 // Copy the 128 x 32 tile at (row0, k0) of an operand into `tile`: 2 copies per
 // wave (512 chunks of 16 bytes over 4 waves).
-template <bool KM>
+template <bool KM, bool MAP = false>
 __device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
-                                         int lane) {
+                                         int lane, const RopeEpi* rp = nullptr) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = (wave * 2 + i) * 64 + lane;  // 16-byte chunk position in the tile
@@ -415,7 +428,9 @@ __device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, in
     if constexpr (KM) {
       const int r = p >> 2;
       const int lc = (p & 3) ^ dl_swz(r);
-      src = g + (int64_t)min(row0 + r, rows - 1) * ld + k0 + lc * 8;
+      int row = min(row0 + r, rows - 1);
+      if constexpr (MAP) row = rope_row(*rp, row);
+      src = g + (int64_t)row * ld + k0 + lc * 8;
     } else {
       const int kr = p >> 4;
       const int c = (p & 15) ^ dl_swz_mn(kr);
@@ -548,21 +563,23 @@ struct DlCtx {
   const bf16* B;
   int64_t lda, ldb;
   int M, N, m0, n0, kbeg, nk, wave, lane;
+  RopeEpi rp;  // B-row map of the RoPE epilogue
 };
 
 // Copy the (NS x 128) x 32 operand tile at (row0, k0) into NS sub-tiles.
-template <bool KM, int NS>
+template <bool KM, int NS, bool MAP = false>
 __device__ __forceinline__ void dl_issue_tile(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile,
-                                              int wave, int lane) {
+                                              int wave, int lane, const RopeEpi* rp = nullptr) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s) dl_issue<KM>(g, ld, rows, row0 + 128 * s, k0, tile + s * DL_TILE, wave, lane);
+  for (int s = 0; s < NS; ++s)
+    dl_issue<KM, MAP>(g, ld, rows, row0 + 128 * s, k0, tile + s * DL_TILE, wave, lane, rp);
 }
 
 // One k-step: wait for this wave's part of tile `it`, barrier, read the
 // current stage, refill the stage freed in step it-1 with tile it+2 (past the
 // end: the last tile again, into a stage nobody reads, so that the same
 // number of copies per wave is in flight at every wait), multiply.
-template <bool AK, bool BK, int FM, int FN>
+template <bool AK, bool BK, int FM, int FN, bool MAP = false>
 __device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK, FM>& da, const DlAddr<BK, FN>& db,
                                         unsigned as, unsigned bs, bf16* An, bf16* Bn, f32x4 (&acc)[FM][FN]) {
   constexpr int NSA = FM / 4, NSB = FN / 4;
@@ -572,7 +589,7 @@ __device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK,
   dl_read<AK, BK, FM, FN>(da.at(as), db.at(bs), af, bfr);
   const int kn = c.kbeg + min(it + 2, c.nk - 1) * DL_BK;
   dl_issue_tile<AK, NSA>(c.A, c.lda, c.M, c.m0, kn, An, c.wave, c.lane);
-  dl_issue_tile<BK, NSB>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
+  dl_issue_tile<BK, NSB, MAP>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane, &c.rp);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -583,18 +600,45 @@ __device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK,
 
 // Block epilogue: lane holds C[m][n .. n+3] of each 16 x 16 fragment; split-K
 // blocks write fp32 partials, the others alpha C (+ R) in the output type.
-template <typename TO, bool SPLIT, int FM, int FN>
+// RoPE epilogue (RP): accumulator columns n .. n+3 of a rotated head hold
+// two pairs (output dims i, i + R/2, i + 1, i + 1 + R/2 for rotate-half, by
+// the B-row map; dims c .. c+3 for even-odd), rotated in fp32 by the angle of
+// row m's position t = m % T before the one rounding to bf16.
+template <typename TO, bool SPLIT, int FM, int FN, bool RP = false>
 __device__ __forceinline__ void dl_epilogue(const KArgs& a, const f32x4 (&acc)[FM][FN], int m0, int n0, int wm, int wn,
                                             int lane) {
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * 16 * FM + i * 16 + (lane & 15);
     if (m >= a.M) continue;
+    const float* tb = nullptr;
+    if constexpr (RP) tb = a.rope.cs + (int64_t)(m % a.rope.T) * a.rope.R;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + wn * 16 * FN + j * 16 + 4 * (lane >> 4);
       if (n >= a.N) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      if constexpr (RP) {
+        const int c = n % a.rope.d;
+        if (n < a.rope.end && c < a.rope.R) {
+          const float4 cs = *reinterpret_cast<const float4*>(tb + c);  // pairs c/2 and c/2 + 1
+          const float y0 = v[0] * cs.x - v[1] * cs.y, y1 = v[0] * cs.y + v[1] * cs.x;
+          const float y2 = v[2] * cs.z - v[3] * cs.w, y3 = v[2] * cs.w + v[3] * cs.z;
+          TO* row = static_cast<TO*>(a.C) + (int64_t)m * a.ldc + (n - c);
+          if (a.rope.half) {
+            const int i0 = c >> 1;
+            Pk<TO, 2> lo, hi;
+            lo.e[0] = from_f32<TO>(y0); lo.e[1] = from_f32<TO>(y2);
+            hi.e[0] = from_f32<TO>(y1); hi.e[1] = from_f32<TO>(y3);
+            *reinterpret_cast<Pk<TO, 2>*>(row + i0) = lo;
+            *reinterpret_cast<Pk<TO, 2>*>(row + i0 + (a.rope.R >> 1)) = hi;
+          } else {
+            const float y[4] = {y0, y1, y2, y3};
+            store4<TO>(row + c, y);
+          }
+          continue;
+        }
+      }
       if (SPLIT) {
         float* dst = a.ws + ((int64_t)blockIdx.z * a.M + m) * a.N + n;
         if (a.evec && n + 3 < a.N) {
@@ -634,7 +678,7 @@ __device__ __forceinline__ void dl_epilogue(const KArgs& a, const f32x4 (&acc)[F
 }
 
 // Block tile (32 FM) x (32 FN): 2 x 2 waves, each 16 FM x 16 FN.
-template <typename TO, bool AK, bool BK, bool SPLIT, int FM, int FN>
+template <typename TO, bool AK, bool BK, bool SPLIT, int FM, int FN, bool RP = false>
 __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a) {
   constexpr int NSA = FM / 4, NSB = FN / 4;
   constexpr int TBM = 32 * FM, TBN = 32 * FN;
@@ -664,6 +708,7 @@ __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a)
   c.nk = (min(a.K, c.kbeg + a.kchunk) - c.kbeg) / DL_BK;
   c.wave = wave;
   c.lane = lane;
+  c.rp = a.rope;
   const DlAddr<AK, FM> da(wm * 16 * FM, lane);
   const DlAddr<BK, FN> db(wn * 16 * FN, lane);
 
@@ -674,23 +719,24 @@ __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a)
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   dl_issue_tile<AK, NSA>(c.A, c.lda, c.M, c.m0, c.kbeg, A0, wave, lane);
-  dl_issue_tile<BK, NSB>(c.B, c.ldb, c.N, c.n0, c.kbeg, B0, wave, lane);
+  dl_issue_tile<BK, NSB, RP>(c.B, c.ldb, c.N, c.n0, c.kbeg, B0, wave, lane, &c.rp);
   dl_issue_tile<AK, NSA>(c.A, c.lda, c.M, c.m0, c.kbeg + min(1, c.nk - 1) * DL_BK, A1, wave, lane);
-  dl_issue_tile<BK, NSB>(c.B, c.ldb, c.N, c.n0, c.kbeg + min(1, c.nk - 1) * DL_BK, B1, wave, lane);
+  dl_issue_tile<BK, NSB, RP>(c.B, c.ldb, c.N, c.n0, c.kbeg + min(1, c.nk - 1) * DL_BK, B1, wave, lane, &c.rp);
   const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
   const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
   for (int it = 0; it < c.nk; it += 3) {
-    dl_step<AK, BK, FM, FN>(c, it, da, db, a0, b0, A2, B2, acc);
-    if (it + 1 < c.nk) dl_step<AK, BK, FM, FN>(c, it + 1, da, db, a1, b1, A0, B0, acc);
-    if (it + 2 < c.nk) dl_step<AK, BK, FM, FN>(c, it + 2, da, db, a2, b2, A1, B1, acc);
+    dl_step<AK, BK, FM, FN, RP>(c, it, da, db, a0, b0, A2, B2, acc);
+    if (it + 1 < c.nk) dl_step<AK, BK, FM, FN, RP>(c, it + 1, da, db, a1, b1, A0, B0, acc);
+    if (it + 2 < c.nk) dl_step<AK, BK, FM, FN, RP>(c, it + 2, da, db, a2, b2, A1, B1, acc);
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
-  dl_epilogue<TO, SPLIT, FM, FN>(a, acc, c.m0, c.n0, wm, wn, lane);
+  dl_epilogue<TO, SPLIT, FM, FN, RP>(a, acc, c.m0, c.n0, wm, wn, lane);
 }
 
 
 // ---------------------------------------------------------------------------
 // 256 x 256 block tile, 8 waves (512 threads) as 2 x 4, each wave 128 x 64
+// (EPI 0: plain; EPI 1: the fused SwiGLU projection; EPI 2: the RoPE epilogue)
 // (8 x 4 MFMA tiles).  Per 32-deep k-step a block copies 32 KiB for 4 MFLOP
 // -- half the bytes per FLOP of the 128 x 128 tile, whose copy path is the
 // limit -- and two waves per SIMD let one wave's LDS reads overlap the
@@ -702,9 +748,9 @@ __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a)
 // ---------------------------------------------------------------------------
 constexpr int W8_NT = 512;
 
-template <bool KM>
+template <bool KM, bool MAP = false>
 __device__ __forceinline__ void w8_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
-                                         int lane) {
+                                         int lane, const RopeEpi* rp = nullptr) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int p = wave * 64 + lane;  // 16-byte chunk position in the 128 x 32 sub-tile
@@ -713,7 +759,9 @@ __device__ __forceinline__ void w8_issue(const bf16* g, int64_t ld, int rows, in
     if constexpr (KM) {
       const int r = p >> 2;
       const int lc = (p & 3) ^ dl_swz(r);
-      src = g + (int64_t)min(r0 + r, rows - 1) * ld + k0 + lc * 8;
+      int row = min(r0 + r, rows - 1);
+      if constexpr (MAP) row = rope_row(*rp, row);
+      src = g + (int64_t)row * ld + k0 + lc * 8;
     } else {
       const int kr = p >> 4;
       const int c = (p & 15) ^ dl_swz_mn(kr);
@@ -750,7 +798,7 @@ __device__ __forceinline__ void w8_step(const DlCtx& c, int it, const DlAddr<AK,
   const int kn = c.kbeg + min(it + 2, c.nk - 1) * DL_BK;
   w8_issue<AK>(c.A, c.lda, c.M, c.m0, kn, An, c.wave, c.lane);
   if constexpr (EPI == 1) w8_issue_pair(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
-  else w8_issue<BK>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
+  else w8_issue<BK, EPI == 2>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane, &c.rp);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -820,6 +868,7 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
   c.nk = a.K / DL_BK;
   c.wave = wave;
   c.lane = lane;
+  c.rp = a.rope;
   const DlAddr<AK, 8> da(wm * 128, lane);
   const DlAddr<BK, 4> db(wn * 64, lane);
 
@@ -836,7 +885,7 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
     const int k0 = min(t, c.nk - 1) * DL_BK;
     w8_issue<AK>(c.A, c.lda, c.M, c.m0, k0, t ? A1 : A0, wave, lane);
     if constexpr (EPI == 1) w8_issue_pair(c.B, c.ldb, c.N, c.n0, k0, t ? B1 : B0, wave, lane);
-    else w8_issue<BK>(c.B, c.ldb, c.N, c.n0, k0, t ? B1 : B0, wave, lane);
+    else w8_issue<BK, EPI == 2>(c.B, c.ldb, c.N, c.n0, k0, t ? B1 : B0, wave, lane, &c.rp);
   }
   const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
   const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
@@ -847,7 +896,7 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
   if constexpr (EPI == 1) w8_epilogue_swiglu_fwd(a, acc, c.m0, c.n0, wm, wn, lane);
-  else dl_epilogue<TO, false, 8, 4>(a, acc, c.m0, c.n0, wm, wn, lane);
+  else dl_epilogue<TO, false, 8, 4, EPI == 2>(a, acc, c.m0, c.n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -866,15 +915,17 @@ constexpr int D64_TILE = 128 * 64;  // elements per 128-row operand tile (16 KiB
 __device__ __forceinline__ int d64_swz(int r) { return 2 * ((r >> 1) & 3); }
 
 // Copy the (32 F) x 64 tile at (row0, k0): F copies per lane.
-template <int F>
+template <int F, bool MAP = false>
 __device__ __forceinline__ void d64_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
-                                          int lane) {
+                                          int lane, const RopeEpi* rp = nullptr) {
 #pragma unroll
   for (int i = 0; i < F; ++i) {
     const int p = (wave * F + i) * 64 + lane;  // 16-byte chunk position in the tile
     const int r = p >> 3;
     const int lc = (p & 7) ^ d64_swz(r);
-    lds_copy16(g + (int64_t)min(row0 + r, rows - 1) * ld + k0 + lc * 8, tile + (wave * F + i) * 512);
+    int row = min(row0 + r, rows - 1);
+    if constexpr (MAP) row = rope_row(*rp, row);
+    lds_copy16(g + (int64_t)row * ld + k0 + lc * 8, tile + (wave * F + i) * 512);
   }
 }
 
@@ -894,7 +945,7 @@ __device__ __forceinline__ void d64_read(unsigned pa, unsigned pb, u32x4 (&af)[4
 #undef D64_OKM
 #undef D64_OUT_KM4
 
-template <typename TO, bool SPLIT>
+template <typename TO, bool SPLIT, bool RP = false>
 __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
   constexpr int FM = 4;
   __shared__ __attribute__((aligned(16))) bf16 A0[D64_TILE], A1[D64_TILE];
@@ -929,14 +980,14 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   d64_issue<FM>(A, a.lda, a.M, m0, kbeg, A0, wave, lane);
-  d64_issue<4>(B, a.ldb, a.N, n0, kbeg, B0, wave, lane);
+  d64_issue<4, RP>(B, a.ldb, a.N, n0, kbeg, B0, wave, lane, &a.rope);
   for (int it = 0; it < nk; ++it) {
     SLT_WAIT_VMCNT(0);  // this wave's copies of tile it have landed
     lds_barrier();      // ... everyone's have, and the other stage is free
     if (it + 1 < nk) {
       const int kn = kbeg + (it + 1) * 64;
       d64_issue<FM>(A, a.lda, a.M, m0, kn, (it & 1) ? A0 : A1, wave, lane);
-      d64_issue<4>(B, a.ldb, a.N, n0, kn, (it & 1) ? B0 : B1, wave, lane);
+      d64_issue<4, RP>(B, a.ldb, a.N, n0, kn, (it & 1) ? B0 : B1, wave, lane, &a.rope);
     }
     const unsigned as = lds_off((it & 1) ? A1 : A0), bs = lds_off((it & 1) ? B1 : B0);
 #pragma unroll
@@ -952,7 +1003,7 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
     }
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
-  dl_epilogue<TO, SPLIT, FM, 4>(a, acc, m0, n0, wm, wn, lane);
+  dl_epilogue<TO, SPLIT, FM, 4, RP>(a, acc, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1332,6 +1383,43 @@ static bool w8_fits(int M, int N) {
   const bool edges = (int64_t)t8 * 256 * 256 <= (int64_t)M * N * 9 / 8;
   const bool rounds = t8 * 20 >= ((t8 + 255) / 256) * 256 * 17;
   return SLT_GEMM_W8 && t8 >= SLT_W8_MIN && edges && rounds;
+}
+
+slt_status launch_gemm_rope(const GemmArgs& g, const RopeEpi& r, hipStream_t s) {
+  const bool ok = g.in_dtype == SLT_BF16 && g.out_dtype == SLT_BF16 && g.a_kmajor && g.b_kmajor && g.M > 0 &&
+                  g.N > 0 && g.K > 0 && g.K % DL_BK == 0 && al(g.A, 16) && g.lda % 8 == 0 && al(g.B, 16) &&
+                  g.ldb % 8 == 0 && g.N % 4 == 0 && g.ldc % 4 == 0 && al(g.C, 8) && g.R == nullptr &&
+                  g.alpha == 1.0f && !g.drop.on && r.cs && al(r.cs, 16) && r.T > 0 && r.d > 0 && r.d % 4 == 0 &&
+                  r.R > 0 && r.R % 4 == 0 && r.R <= r.d && r.end > 0 && r.end % r.d == 0 && r.end <= g.N;
+  if (!ok) return fail(SLT_EUNSUPPORTED, "projection with RoPE epilogue: shape or alignment");
+  KArgs ka{};
+  ka.M = g.M; ka.N = g.N; ka.K = g.K;
+  ka.A = g.A; ka.lda = g.lda; ka.B = g.B; ka.ldb = g.ldb;
+  ka.C = g.C; ka.ldc = g.ldc;
+  ka.alpha = 1.0f;
+  ka.kchunk = g.K;
+  ka.evec = true;
+  ka.rope = r;
+  if (w8_fits(g.M, g.N)) {
+    ka.tiles_n = (g.N + 255) / 256;
+    ka.tiles = ((g.M + 255) / 256) * ka.tiles_n;
+    gemm_w8_k<bf16, true, true, 2><<<ka.tiles, W8_NT, 0, s>>>(ka);
+    return check_launch("gemm with RoPE epilogue");
+  }
+  auto ntiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
+  int fm = 4, fn = 4;
+  if (SLT_GEMM_BIG) {
+    if (g.M >= g.N && ntiles(256, 128) >= 768) fm = 8;
+    else if (ntiles(128, 256) >= 768) fn = 8;
+  }
+  ka.tiles_n = (g.N + 32 * fn - 1) / (32 * fn);
+  ka.tiles = ((g.M + 32 * fm - 1) / (32 * fm)) * ka.tiles_n;
+  const dim3 grid(ka.tiles, 1, 1);
+  if (fm == 8) gemm_dl_k<bf16, true, true, false, 8, 4, true><<<grid, NT, 0, s>>>(ka);
+  else if (fn == 8) gemm_dl_k<bf16, true, true, false, 4, 8, true><<<grid, NT, 0, s>>>(ka);
+  else if (SLT_GEMM_D64 && g.K % 64 == 0) gemm_d64_k<bf16, false, true><<<grid, NT, 0, s>>>(ka);
+  else gemm_dl_k<bf16, true, true, false, 4, 4, true><<<grid, NT, 0, s>>>(ka);
+  return check_launch("gemm with RoPE epilogue");
 }
 
 slt_status launch_gemm_swiglu_fwd(int M, int F, int K, const void* X, int64_t ldx, const void* W13, void* ab,

@@ -917,6 +917,47 @@ __global__ void rope_table_k(int T_, int R, double base, float* cs) {
   cs[(int64_t)t * R + 2 * j + 1] = (float)sin(ang);
 }
 
+// *dst += a * (*x): the running mean loss of gradient accumulation.
+__global__ void scalar_axpy_k(float* dst, float a, const float* x) { *dst += a * *x; }
+
+// RoPE (Hephaistos, "Architecture at a glance"; Transformer in Rust, "Key
+// Features": even-odd pairs): one thread per rotated pair (a, b) of one head
+// of one row, (a, b) -> (a c - b s, a s + b c) with s times `sign` (-1: the
+// transposed rotation, RoPE's backward); both values read before either is
+// written, so y may equal x.  Then, when y is another buffer, the dims >= R
+// are copied.
+template <typename T>
+__global__ void rope_apply_k(const T* x, int64_t ldx, T* y, int64_t ldy, int64_t rows, int T_, int nh, int d, int R,
+                             int mode, const float* cs, float sign) {
+  const int hr = R >> 1;
+  const int64_t npair = rows * nh * hr;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < npair; idx += stride) {
+    const int j = (int)(idx % hr);
+    const int64_t rh = idx / hr;
+    const int h = (int)(rh % nh);
+    const int64_t r = rh / nh;
+    const int t = (int)(r % T_);
+    const int ia = mode == SLT_ROPE_HALF ? j : 2 * j, ib = mode == SLT_ROPE_HALF ? j + hr : 2 * j + 1;
+    const T* xr = x + r * ldx + (int64_t)h * d;
+    T* yr = y + r * ldy + (int64_t)h * d;
+    const float a = to_f32(xr[ia]), b = to_f32(xr[ib]);
+    const float c = cs[(int64_t)t * R + 2 * j], sn = sign * cs[(int64_t)t * R + 2 * j + 1];
+    yr[ia] = from_f32<T>(a * c - b * sn);
+    yr[ib] = from_f32<T>(a * sn + b * c);
+  }
+  if (x == y || R >= d) return;
+  const int rest = d - R;
+  const int64_t ncopy = rows * nh * rest;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < ncopy; idx += stride) {
+    const int j = R + (int)(idx % rest);
+    const int64_t rh = idx / rest;
+    const int h = (int)(rh % nh);
+    const int64_t r = rh / nh;
+    y[r * ldy + (int64_t)h * d + j] = x[r * ldx + (int64_t)h * d + j];
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -1141,6 +1182,25 @@ slt_status launch_layernorm_bwd(const void* x, const void* gm, const float* mean
                                 const void* dy, const void* dres, void* dx, float* dgm, float* dbt, int rows,
                                 int C, int dtype, void* ws, hipStream_t s, GradW gw, bool defer_sums) {
   return norm_bwd_common<true>(x, gm, mean, rstd, dy, dres, dx, dgm, dbt, rows, C, dtype, ws, s, gw, defer_sums);
+}
+
+slt_status launch_rope(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int T_, int nh, int d, int R,
+                       int mode, const float* cs, float sign, int dtype, hipStream_t s) {
+  if (rows == 0 || nh == 0 || d == 0) return SLT_OK;
+  const int64_t work = rows * nh * std::max(R / 2, d - R);
+  const int blocks = (int)std::min<int64_t>(cdiv(work, 256), 65536);
+  if (dtype == SLT_BF16)
+    rope_apply_k<bf16><<<blocks, 256, 0, s>>>(static_cast<const bf16*>(x), ldx, static_cast<bf16*>(y), ldy, rows, T_,
+                                              nh, d, R, mode, cs, sign);
+  else
+    rope_apply_k<float><<<blocks, 256, 0, s>>>(static_cast<const float*>(x), ldx, static_cast<float*>(y), ldy, rows,
+                                               T_, nh, d, R, mode, cs, sign);
+  return check_launch("rope");
+}
+
+slt_status launch_scalar_axpy(float* dst, float a, const float* x, hipStream_t s) {
+  scalar_axpy_k<<<1, 1, 0, s>>>(dst, a, x);
+  return check_launch("scalar axpy");
 }
 
 slt_status launch_rope_table(int T_, int R, float base, float* cs, hipStream_t s) {

@@ -216,6 +216,16 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 // ---------------------------------------------------------------------------
 // Kernel launchers (return hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
+// RoPE applied in a projection's epilogue: output columns [0, end) are heads
+// of d dims whose first R dims are rotated by the angle of row m's position
+// m % T (cs: the [T][R] table of (cos, sin) pairs), in fp32 before the
+// rounding to bf16.  half: rotate-half pairs (j, j + R/2), else even-odd.
+struct RopeEpi {
+  const float* cs = nullptr;
+  int T = 1, d = 1, R = 0, end = 0;
+  int half = 0;
+};
+
 struct GemmArgs {
   int M, N, K;
   const void* A; int64_t lda; bool a_kmajor;
@@ -235,6 +245,15 @@ struct GradW {
   bool accumulate = false;
 };
 slt_status launch_gemm(const GemmArgs& g, hipStream_t s);
+// y = x W^T with the RoPE epilogue (bf16, both operands k-major, no residual,
+// alpha 1); SLT_EUNSUPPORTED, nothing enqueued, where it does not apply.
+slt_status launch_gemm_rope(const GemmArgs& g, const RopeEpi& r, hipStream_t s);
+// RoPE on the first R dims of each of nh heads (d dims, head h at column h d)
+// of rows r = b T + t, position t = r % T: y = rotate(x) (sign 1) or the
+// transposed rotation (sign -1, RoPE's backward); dims >= R are copied.
+// y may equal x (in place).
+slt_status launch_rope(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int T, int nh, int d, int R,
+                       int mode, const float* cs, float sign, int dtype, hipStream_t s);
 
 // [W1; W3] projection fused with SwiGLU: ab[M, 2F] = X[M, K] W13[2F, K]^T
 // (a | b, bf16, row stride ldab) and h[M, F] = swiglu(bf16(a), bf16(b)).
@@ -304,6 +323,8 @@ slt_status launch_grad_norm(int64_t n, const float* g, int kind, float max_norm,
                             void* ws, hipStream_t s);
 slt_status launch_cast_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t s);
 slt_status launch_fill_f32(float* dst, float value, int64_t n, hipStream_t s);
+// *dst += a * (*x) on the device (one value)
+slt_status launch_scalar_axpy(float* dst, float a, const float* x, hipStream_t s);
 slt_status launch_model_init_range(float* dst, int64_t n, int64_t index0, uint64_t seed, float std,
                                    int kind, hipStream_t s);
 
@@ -318,15 +339,17 @@ struct AttnArgs {
   float* delta;        // workspace [B, H, T] for the backward
   void* ores_out;      // forward: optional o - bf16(o), dense [B*T, H*d]
   const void* ores_in; // backward: that residual (NULL: treat as 0)
-  void* rot;           // bf16 path: rotated hi/lo copies of q and k (flash_rot_elems bf16 values)
-  bool rot_ready;      // rot already holds them for these q, k (skip the RoPE pass)
+  bool qk_rotated;     // q and k already carry RoPE (the projection's epilogue applied it; bf16 path only):
+                       // no rotation on load, but dq and dk are still rotated back
+  void* rot;           // bf16 path with q, k not yet rotated: workspace for their rotated copies
+                       // (flash_rot_elems bf16 values)
   Drop drop{};         // dropout of the attention weights: element ((b H + h) T + i) T + j
 };
 slt_status launch_attention_fwd(const AttnArgs& a, hipStream_t s);
 slt_status launch_attention_bwd(const AttnArgs& a, hipStream_t s);
 int64_t attention_bwd_ws(int B, int H, int T);
-// bf16 attention with pre-rotated q/k copies and LDS tiles copied straight
-// from HBM (flash.hip)
+// bf16 attention on rotated bf16 q/k with LDS tiles copied straight from HBM
+// (flash.hip)
 int64_t flash_rot_elems(int B, int T, int H, int Hkv, int d);
 bool flash_eligible(int dtype, int d);
 bool flash_ok(const AttnArgs& a, bool bwd);

@@ -121,19 +121,19 @@ class TrainStep:
     def accumulate(self, micro_tokens) -> float:
         """Gradient of the mean loss over several equal micro-batches, each run
         through the arena in turn (this object's batch size is the
-        micro-batch size): grads = sum_s (1/S) grad_s.  Returns the mean loss
-        (one host synchronisation)."""
+        micro-batch size): grads = sum_s (1/S) grad_s, and the mean loss
+        sum_s (1/S) loss_s kept on the device by the library.  Returns the
+        mean loss (one host synchronisation)."""
         S = len(micro_tokens)
         self.grads.zero_()
-        total = torch.zeros(1, dtype=torch.float32, device=self.device)
+        mean_loss = torch.zeros(1, dtype=torch.float32, device=self.device)
         for tok in micro_tokens:
             self.forward(tok)
-            total += self.loss
             B.slt_backward_accumulate(self.cfg, self.compute_params, tok, self.acts, self.scratch, self.grads,
-                                      1.0 / S)
+                                      1.0 / S, self.loss, mean_loss)
             if self.cfg.dropout > 0:
                 self.next_masks()
-        return float(total.item()) / S
+        return float(mean_loss.item())
 
 
 class CachedForward:

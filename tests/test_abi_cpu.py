@@ -118,12 +118,22 @@ def test_host_calls_reject_bad_arguments_before_launch():
     assert B.slt_clip_workspace_bytes() > 0
     assert lib.slt_attention_fwd(None, None, None, None, None, None, 8, 8, 8, 8, 1, 4, 2, 1, 128, 0, 0, None, 1,
                                  None, None) == 2
-    # a bf16 head dim the rotated-copy path takes needs its workspace
-    assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 48, 1) == 2 * 2 * 6 * 64 * 48 * 2
+    # a bf16 head dim the tiled kernels take needs room for one rotated bf16 copy of q and k
+    assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 48, 1) == 2 * 6 * 64 * 48 * 2
     assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 48, 0) == 0
     assert B.slt_attention_fwd_workspace(2, 64, 4, 2, 24, 1) == 0
     assert B.slt_attention_bwd_workspace(2, 64, 4, 2, 24, 1) == 2 * 4 * 64 * 4
     assert lib.slt_softmax_xent(None, 10, None, 1, 4, 5, 10, None, None, 1, None, None) == 1
+    # RoPE: odd R, R > d, bad mode, narrow strides, NULL pointers
+    assert lib.slt_rope_fwd(None, 16, None, 16, 1, 4, 2, 8, 7, 0, None, 1, None) == 1
+    assert lib.slt_rope_bwd(None, 16, None, 16, 1, 4, 2, 8, 10, 0, None, 1, None) == 1
+    assert lib.slt_rope_fwd(None, 16, None, 16, 1, 4, 2, 8, 8, 5, None, 1, None) == 1
+    assert lib.slt_rope_fwd(None, 12, None, 16, 1, 4, 2, 8, 8, 0, None, 1, None) == 1
+    assert lib.slt_rope_fwd(None, 16, None, 16, 1, 4, 2, 8, 8, 0, None, 1, None) == 1
+    assert lib.slt_rope_fwd(None, 16, None, 16, 0, 4, 2, 8, 8, 0, None, 1, None) == 0   # nothing to do
+    # QKV with RoPE: heads wider than N, odd R
+    assert lib.slt_qkv_rope_fwd(4, 16, 8, None, None, None, 16, 4, 2, 2, 8, 8, 0, None, 1, None) == 1
+    assert lib.slt_qkv_rope_fwd(4, 64, 8, None, None, None, 64, 4, 2, 2, 8, 7, 0, None, 1, None) == 1
 
 
 def test_kv_cache_sizes():

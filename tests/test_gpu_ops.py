@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from parity import check, normwise, rms
+from parity import check, check_rows, normwise, rms
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -192,6 +192,42 @@ def test_gemm_full_size_sampled_rows(B, shape):
     rng = np.random.default_rng(3)
     M, N, K, a_k, b_k, ind, outd, resid, ws = shape
     gemm_case(B, rng, M, N, K, a_k, b_k, ind, outd, resid, ws, sample=48)
+
+
+@pytest.mark.parametrize("M,T,H,Hkv,d,R,mode,extra,K,dtype", [
+    (16384, 256, 8, 8, 48, 48, "half", 0, 384, BF16),        # d=384 workload's QKV: 128 x 128 64-deep tiles
+    (16384, 1024, 16, 4, 64, 64, "half", 0, 1024, BF16),     # GQA workload's QKV: 256 x 128 tiles
+    (16384, 2048, 16, 16, 64, 32, "pairs", 4096, 1024, BF16),  # parallel block's [q|k|v|fc_in]: 256 x 256 tiles
+    (200, 100, 4, 2, 32, 16, "half", 40, 64, BF16),          # ragged M and N: 128 x 128 tiles with edge blocks
+    (96, 48, 2, 2, 16, 6, "pairs", 0, 32, BF16),             # R % 4 != 0: the product, then RoPE in place
+    (130, 65, 4, 4, 16, 16, "half", 0, 40, F32),             # fp32: the product, then RoPE in place
+])
+def test_qkv_rope_projection(B, M, T, H, Hkv, d, R, mode, extra, K, dtype):
+    """The QKV projection with RoPE in its epilogue (slt_qkv_rope_fwd): the
+    q and k columns of sampled rows equal the oracle's rotation of x W^T at
+    the row's position, rounded once; v (and trailing columns) the plain
+    product."""
+    say("qkv rope", M, T, H, Hkv, d, R, mode, extra, K, dtype)
+    rng = np.random.default_rng(12)
+    N = (H + 2 * Hkv) * d + extra
+    x = rnd(rng, (M, K), dtype)
+    w = rnd(rng, (N, K), dtype, 0.05)
+    cs = torch.empty((T, max(R, 2)), device="cuda")
+    if R:
+        B.slt_rope_table(T, R, 10000.0, cs)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16 if dtype == BF16 else torch.float32, device="cuda")
+    B.slt_qkv_rope_fwd(M, N, K, dev(x, dtype), dev(w, dtype), y, N, T, H, Hkv, d, R, 0 if mode == "half" else 1, cs,
+                       dtype)
+    rows = np.union1d(np.unique(rng.integers(0, M, 64)), [0, M - 1])
+    got = host(y)[rows]
+    full = x[rows] @ w.T
+    c, s = O.rope_tables(T, max(R, 2), 10000.0)
+    pos = rows % T
+    qk = full[:, :(H + Hkv) * d].reshape(len(rows), H + Hkv, 1, d)  # [rows, heads, 1 position, d]
+    rot = np.concatenate([O.rope_apply(qk[i:i + 1], c[pos[i]:pos[i] + 1], s[pos[i]:pos[i] + 1], R, mode)
+                          for i in range(len(rows))]).reshape(len(rows), -1) if R else qk.reshape(len(rows), -1)
+    check(got[:, :(H + Hkv) * d], ref_round(rot, dtype), act(dtype), "rotated q and k")
+    check(got[:, (H + Hkv) * d:], ref_round(full[:, (H + Hkv) * d:], dtype), act(dtype), "v and trailing columns")
 
 
 @pytest.mark.parametrize("M,F,C,dtype", [
@@ -381,6 +417,8 @@ ATTN_CASES = [
     (1, 40, 2, 2, 24, 24, "half", BF16),      # head dim not a multiple of 16: register-staged kernels
     (2, 50, 4, 2, 32, 12, "half", BF16),      # rotate-half pairs straddling 8-dim chunks: element-wise RoPE pass
     (1, 33, 2, 2, 16, 6, "pairs", BF16),      # R % 4 == 2: the rotated dims end inside a 4-dim group
+    (1, 2100, 4, 2, 64, 32, "pairs", BF16),   # 128-query chunks (T >= 2048) with a part-filled last chunk, GQA
+    (1, 2049, 2, 1, 48, 48, "half", BF16),    # the same at d = 48 (three 16-dim output tiles), T % 4 != 0
 ]
 
 
@@ -420,17 +458,18 @@ def test_attention_fwd_bwd(B, case, pad):
     k = heads(qkv[:, qd:qd + kd], Hkv)
     v = heads(qkv[:, qd + kd:qd + 2 * kd], Hkv)
     if R:
-        q = O.rope_apply(q, c, s, R, mode)
-        k = O.rope_apply(k, c, s, R, mode)
+        # bf16: the rotated q and k are rounded once before the products
+        q = ref_round(O.rope_apply(q, c, s, R, mode), dtype)
+        k = ref_round(O.rope_apply(k, c, s, R, mode), dtype)
     o_ref, lse_ref = O.attention_fwd(q, k, v)
     o_ref2 = o_ref.transpose(0, 2, 1, 3).reshape(Bn * T, qd)
-    check(host(o), ref_round(o_ref2, dtype), act(dtype), "attn o")
+    check_rows(host(o), ref_round(o_ref2, dtype), act(dtype), "attn o")
     check(host(lse), lse_ref, act(dtype), "attn lse")
     if ores is not None:
         # the residual is what rounding o to bf16 dropped: at most half a bf16 ulp of o
         oh, rh = host(o), host(ores)
         assert np.all(np.abs(rh) <= 2.0 ** -8 * np.abs(oh) + 1e-30)
-        check(oh + rh, o_ref2, "bf16", "attn o + residual")
+        check_rows(oh + rh, o_ref2, "bf16", "attn o + residual")
 
     do = rnd(rng, (Bn * T, qd), dtype)
     # the backward reads o (and its rounding residual): give it the oracle's
@@ -449,9 +488,62 @@ def test_attention_fwd_bwd(B, case, pad):
         dk = O.rope_apply(dk, c, s, R, mode, inverse=True)
     got = host(dqkv)
     un = lambda x: x.transpose(0, 2, 1, 3).reshape(Bn * T, -1)
-    check(got[:, :qd], ref_round(un(dq), dtype), act(dtype), "attn dq")
-    check(got[:, qd:qd + kd], ref_round(un(dk), dtype), act(dtype), "attn dk")
-    check(got[:, qd + kd:qd + 2 * kd], ref_round(un(dv), dtype), act(dtype), "attn dv")
+    check_rows(got[:, :qd], ref_round(un(dq), dtype), act(dtype), "attn dq")
+    check_rows(got[:, qd:qd + kd], ref_round(un(dk), dtype), act(dtype), "attn dk")
+    check_rows(got[:, qd + kd:qd + 2 * kd], ref_round(un(dv), dtype), act(dtype), "attn dv")
+
+
+ROPE_CASES = [
+    # Bn, T, nheads, d, R, mode, dtype, pad
+    (2, 37, 4, 48, 48, "half", BF16, 8),
+    (1, 64, 3, 64, 32, "pairs", BF16, 0),
+    (2, 16, 4, 16, 6, "pairs", F32, 3),
+    (1, 20, 2, 32, 12, "half", F32, 1),
+    (1, 5, 2, 8, 0, "half", BF16, 2),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES)
+@pytest.mark.parametrize("inplace", [False, True])
+def test_rope_fwd_bwd(B, case, inplace):
+    """slt_rope_fwd / slt_rope_bwd against the oracle's rotation (and its
+    transpose) on strided rows, out of place and in place; dims past R are
+    copied unchanged."""
+    Bn, T, nh, d, R, mode, dtype, pad = case
+    say("rope", case, inplace)
+    rng = np.random.default_rng(21)
+    ld = nh * d + pad
+    x = rnd(rng, (Bn * T, ld), dtype)
+    cs = torch.empty((T, max(R, 2)), device="cuda")
+    if R:
+        B.slt_rope_table(T, R, 10000.0, cs)
+    c, s = O.rope_tables(T, max(R, 2), 10000.0)
+    mode_i = 0 if mode == "half" else 1
+    heads = lambda a: a[:, :nh * d].reshape(Bn, T, nh, d).transpose(0, 2, 1, 3)
+    un = lambda a: a.transpose(0, 2, 1, 3).reshape(Bn * T, nh * d)
+    for fn, inverse in [(B.slt_rope_fwd, False), (B.slt_rope_bwd, True)]:
+        tx = dev(x, dtype)
+        ty = tx if inplace else torch.full_like(tx, float("nan"))
+        fn(tx, ld, ty, ld, Bn, T, nh, d, R, mode_i, cs, dtype)
+        got = host(ty)[:, :nh * d]
+        ref = un(O.rope_apply(heads(x), c, s, R, mode, inverse=inverse)) if R else x[:, :nh * d]
+        check(got, ref_round(ref, dtype), act(dtype), f"rope {'bwd' if inverse else 'fwd'}")
+        if R < d:  # untouched dims are copied exactly
+            tail = np.concatenate([np.arange(h * d + R, (h + 1) * d) for h in range(nh)])
+            assert np.array_equal(got[:, tail], x[:, tail])
+        if pad and not inplace:
+            assert np.all(np.isnan(host(ty)[:, nh * d:]))  # the row padding is not written
+
+
+def test_rope_rejects_bad_arguments(B):
+    cs = torch.zeros((4, 8), device="cuda")
+    x = torch.zeros((4, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.SltError):
+        B.slt_rope_fwd(x, 16, x, 16, 1, 4, 2, 8, 9, 0, cs, BF16)   # R odd
+    with pytest.raises(B.SltError):
+        B.slt_rope_fwd(x, 16, x, 8, 1, 4, 2, 8, 8, 0, cs, BF16)    # in place, strides differ
+    with pytest.raises(B.SltError):
+        B.slt_rope_fwd(x, 12, x, 12, 1, 4, 2, 8, 8, 0, cs, BF16)   # row stride below nheads * d
 
 
 # ---------------------------------------------------------------------------
