@@ -480,6 +480,21 @@ slt_status slt_softmax_xent(void* z, int64_t ldz, const int32_t* tokens, int32_t
                             int64_t ld_tokens, int32_t V, float* loss, float* lse, int32_t dtype,
                             void* workspace, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): slt_softmax_xent
+ * with its per-row loss scratch in a static device array of the library
+ * instead of a workspace argument -- same kernels, same results bit for bit.
+ * At most 1048576 rows (B*T); larger inputs return SLT_EINVAL before any
+ * launch.  Calls no hipMalloc/hipFree: the array (4 MiB) lives on every
+ * device the library runs on until the process ends, and its address is
+ * looked up once per device on the first call there.  Every call on a device
+ * shares that device's array, so calls that overlap on one GPU (two streams
+ * at once) race; calls in one stream order are safe.  Other arguments as
+ * slt_softmax_xent. */
+slt_status slt_softmax_xent_noalloc(void* z, int64_t ldz, const int32_t* tokens, int32_t B, int32_t T,
+                                    int64_t ld_tokens, int32_t V, float* loss, float* lse, int32_t dtype,
+                                    void* stream);
+
 /* ------------------------------------------------------------------------
  * Machine bounds (strata, benchmark methodology: kernels are reported as a
  * fraction of a measured machine bound)

@@ -99,6 +99,7 @@ SIGNATURES = {
     "slt_gelu_fwd": (_I32, [_P, _P, _I32, _I32, _I64, _I64, _I32, _P]),
     "slt_gelu_bwd": (_I32, [_P, _P, _P, _I32, _I32, _I64, _I64, _I64, _I32, _P]),
     "slt_softmax_xent": (_I32, [_P, _I64, _P, _I32, _I32, _I64, _I32, _P, _P, _I32, _P, _P]),
+    "slt_softmax_xent_noalloc": (_I32, [_P, _I64, _P, _I32, _I32, _I64, _I32, _P, _P, _I32, _P]),
     "slt_stream_copy": (_I32, [_P, _P, _I64, _P]),
     "slt_mfma_loop_flops": (_I64, [_I32, _I32]),
     "slt_mfma_loop": (_I32, [_I32, _I32, _P, _P]),
@@ -384,6 +385,11 @@ def slt_gelu_bwd(a, du, da, rows, F, lda, lddu, ldda, dtype, stream=None):
 def slt_softmax_xent(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtype, workspace, stream=None):
     _check("slt_softmax_xent", load().slt_softmax_xent(_ptr(z), ldz, _ptr(tokens), B, T, ld_tokens, V, _ptr(loss),
                                                        _ptr(lse), dtype, _ptr(workspace), _stream(stream)))
+
+
+def slt_softmax_xent_noalloc(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtype, stream=None):
+    _check("slt_softmax_xent_noalloc", load().slt_softmax_xent_noalloc(_ptr(z), ldz, _ptr(tokens), B, T, ld_tokens, V,
+                                                                       _ptr(loss), _ptr(lse), dtype, _stream(stream)))
 
 
 def slt_stream_copy(src, dst, nbytes, stream=None):

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libslt.so")
-SOURCES = ["rowops.hip", "gemm.hip", "attention.hip", "flash.hip", "decode.hip", "api.hip", "calib.hip"]
+SOURCES = ["rowops.hip", "gemm.hip", "attention.hip", "flash.hip", "decode.hip", "api.hip", "calib.hip", "noalloc.hip"]
 ARCH = os.environ.get("SLT_OFFLOAD_ARCH", "gfx950")
 
 
