@@ -204,7 +204,7 @@ def time_cold(fn, reps, torch, evict):
     fn()
     times = []
     for _ in range(reps):
-        B.slt_stream_copy(src, dst, src.numel())
+        B.slt_stream_copy(src, dst, src.numel())  # evict
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(s)
@@ -218,40 +218,48 @@ def time_cold(fn, reps, torch, evict):
 
 def machine_bounds(torch):
     """The library's own streaming copy over 2 x 2 GiB (read + write GB/s,
-    best of 5) and its MFMA loop (bf16 TFLOP/s, best of 5): the measured
-    bounds the kernels are also reported against."""
+    best of its launch shapes) and its MFMA loop (bf16 TFLOP/s, best of 6):
+    the measured bounds the kernels are also reported against."""
     from scratch_llama_transformer_amd import binding as B
     n = 2 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     s = torch.cuda.current_stream()
-    best = None
-    for _ in range(6):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(s)
-        B.slt_stream_copy(src, dst, n)
-        b.record(s)
-        b.synchronize()
-        t = a.elapsed_time(b) / 1e3
-        best = t if best is None else min(best, t)
+    best, best_v = None, 0
+    for v in range(3):
+        for _ in range(4):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            B.slt_stream_copy(src, dst, n, v)
+            b.record(s)
+            b.synchronize()
+            t = a.elapsed_time(b) / 1e3
+            if best is None or t < best:
+                best, best_v = t, v
     del src, dst
     blocks, iters = 256 * 8, 4096
     out = torch.empty(blocks * 256, device="cuda")
-    bestm = None
-    for _ in range(6):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(s)
-        B.slt_mfma_loop(blocks, iters, out)
-        b.record(s)
-        b.synchronize()
-        t = a.elapsed_time(b) / 1e3
-        bestm = t if bestm is None else min(bestm, t)
+    rates = {}
+    for var in range(3):
+        bestm = None
+        for _ in range(4):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            B.slt_mfma_loop(blocks, iters, out, var)
+            b.record(s)
+            b.synchronize()
+            t = a.elapsed_time(b) / 1e3
+            bestm = t if bestm is None else min(bestm, t)
+        rates[var] = B.slt_mfma_loop_flops(blocks, iters, var) / bestm / 1e12
     return {"copy_gbps": round(2.0 * n / best / 1e9, 1), "copy_bytes": 2 * n,
-            "mfma_bf16_tflops": round(B.slt_mfma_loop_flops(blocks, iters) / bestm / 1e12, 1),
-            "copy_kernel": "slt_stream_copy (16-byte loads and stores, 2 GiB each way)",
-            "mfma_kernel": "slt_mfma_loop (8 independent v_mfma_f32_16x16x32_bf16 chains per wave, 8 waves per CU)"}
+            "mfma_bf16_tflops": round(max(rates.values()), 1),
+            "mfma_loop_tflops": {"16x16x32 x8": round(rates[0], 1), "32x32x16 x8": round(rates[1], 1),
+                                 "16x16x32 x16": round(rates[2], 1)},
+            "copy_kernel": f"slt_stream_copy variant {best_v} (16-byte non-temporal loads and stores, 2 GiB each "
+                           "way; best of 3 launch shapes x 4)",
+            "mfma_kernel": "slt_mfma_loop (independent MFMA chains per wave, 32 waves per CU; best variant)"}
 
 
 def hbm_classes(w, torch, reps, machine):

@@ -501,16 +501,21 @@ slt_status slt_softmax_xent_noalloc(void* z, int64_t ldz, const int32_t* tokens,
  * ---------------------------------------------------------------------- */
 
 /* dst = src over `bytes` bytes (a multiple of 16; both 16-byte aligned, not
- * overlapping) with 16-byte loads and stores: the read + write rate a
- * streaming kernel reaches on this GPU. */
-slt_status slt_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+ * overlapping) with 16-byte non-temporal loads and stores: the read + write
+ * rate a streaming kernel reaches on this GPU.  variant selects the launch
+ * shape (0: 4 words per thread per iteration on 8192 blocks; 1: 8 words on
+ * 4096 blocks; 2: one pass over the buffer, 4 words per thread); the best of
+ * them is the measured bound. */
+slt_status slt_stream_copy(const void* src, void* dst, int64_t bytes, int32_t variant, void* stream);
 
-/* `blocks` workgroups of 4 waves, each wave running `iters` rounds of 8
- * independent v_mfma_f32_16x16x32_bf16 on register operands; out receives
- * 256 * blocks floats (so the work is not dead).  slt_mfma_loop_flops gives
- * the FLOPs one call performs.  Host only / device call. */
-int64_t slt_mfma_loop_flops(int32_t blocks, int32_t iters);
-slt_status slt_mfma_loop(int32_t blocks, int32_t iters, float* out, void* stream);
+/* `blocks` workgroups of 4 waves, each wave running `iters` rounds of
+ * independent MFMAs on register operands: variant 0 = 8 chains of
+ * v_mfma_f32_16x16x32_bf16, 1 = 8 chains of v_mfma_f32_32x32x16_bf16, 2 = 16
+ * chains of v_mfma_f32_16x16x32_bf16.  out receives 256 * blocks floats (so
+ * the work is not dead).  slt_mfma_loop_flops (host only) gives the FLOPs
+ * one call performs. */
+int64_t slt_mfma_loop_flops(int32_t blocks, int32_t iters, int32_t variant);
+slt_status slt_mfma_loop(int32_t blocks, int32_t iters, int32_t variant, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -100,9 +100,9 @@ SIGNATURES = {
     "slt_gelu_bwd": (_I32, [_P, _P, _P, _I32, _I32, _I64, _I64, _I64, _I32, _P]),
     "slt_softmax_xent": (_I32, [_P, _I64, _P, _I32, _I32, _I64, _I32, _P, _P, _I32, _P, _P]),
     "slt_softmax_xent_noalloc": (_I32, [_P, _I64, _P, _I32, _I32, _I64, _I32, _P, _P, _I32, _P]),
-    "slt_stream_copy": (_I32, [_P, _P, _I64, _P]),
-    "slt_mfma_loop_flops": (_I64, [_I32, _I32]),
-    "slt_mfma_loop": (_I32, [_I32, _I32, _P, _P]),
+    "slt_stream_copy": (_I32, [_P, _P, _I64, _I32, _P]),
+    "slt_mfma_loop_flops": (_I64, [_I32, _I32, _I32]),
+    "slt_mfma_loop": (_I32, [_I32, _I32, _I32, _P, _P]),
 }
 
 _lib = None
@@ -392,13 +392,13 @@ def slt_softmax_xent_noalloc(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtyp
                                                                        _ptr(loss), _ptr(lse), dtype, _stream(stream)))
 
 
-def slt_stream_copy(src, dst, nbytes, stream=None):
-    _check("slt_stream_copy", load().slt_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+def slt_stream_copy(src, dst, nbytes, variant=0, stream=None):
+    _check("slt_stream_copy", load().slt_stream_copy(_ptr(src), _ptr(dst), nbytes, variant, _stream(stream)))
 
 
-def slt_mfma_loop_flops(blocks, iters) -> int:
-    return int(load().slt_mfma_loop_flops(blocks, iters))
+def slt_mfma_loop_flops(blocks, iters, variant=0) -> int:
+    return int(load().slt_mfma_loop_flops(blocks, iters, variant))
 
 
-def slt_mfma_loop(blocks, iters, out, stream=None):
-    _check("slt_mfma_loop", load().slt_mfma_loop(blocks, iters, _ptr(out), _stream(stream)))
+def slt_mfma_loop(blocks, iters, out, variant=0, stream=None):
+    _check("slt_mfma_loop", load().slt_mfma_loop(blocks, iters, variant, _ptr(out), _stream(stream)))

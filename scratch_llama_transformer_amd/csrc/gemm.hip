@@ -420,7 +420,7 @@ __device__ __forceinline__ void band_coords(int idx, int tiles, int tiles_n, int
 // wave (512 chunks of 16 bytes over 4 waves).
 template <bool KM, bool MAP = false>
 __device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
-                                         int lane, const RopeEpi* rp = nullptr) {
+                                         int lane, const int* rmap = nullptr) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int p = (wave * 2 + i) * 64 + lane;  // 16-byte chunk position in the tile
@@ -428,8 +428,7 @@ __device__ __forceinline__ void dl_issue(const bf16* g, int64_t ld, int rows, in
     if constexpr (KM) {
       const int r = p >> 2;
       const int lc = (p & 3) ^ dl_swz(r);
-      int row = min(row0 + r, rows - 1);
-      if constexpr (MAP) row = rope_row(*rp, row);
+      const int row = MAP ? rmap[i] : min(row0 + r, rows - 1);
       src = g + (int64_t)row * ld + k0 + lc * 8;
     } else {
       const int kr = p >> 4;
@@ -563,16 +562,27 @@ struct DlCtx {
   const bf16* B;
   int64_t lda, ldb;
   int M, N, m0, n0, kbeg, nk, wave, lane;
-  RopeEpi rp;  // B-row map of the RoPE epilogue
+  int brow[4];  // B rows this lane copies under the RoPE epilogue's row map (sub-tile s, copy i at 2 s + i)
 };
+
+// The B rows (output columns) a lane copies for the (NS x 128)-row tile at
+// n0 under the RoPE epilogue's row map, computed once per block.
+template <int NS>
+__device__ __forceinline__ void dl_rope_rows(const RopeEpi& r, int N, int n0, int wave, int lane, int (&out)[4]) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      out[2 * s + i] = rope_row(r, min(n0 + 128 * s + (((wave * 2 + i) * 64 + lane) >> 2), N - 1));
+}
 
 // Copy the (NS x 128) x 32 operand tile at (row0, k0) into NS sub-tiles.
 template <bool KM, int NS, bool MAP = false>
 __device__ __forceinline__ void dl_issue_tile(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile,
-                                              int wave, int lane, const RopeEpi* rp = nullptr) {
+                                              int wave, int lane, const int* rmap = nullptr) {
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    dl_issue<KM, MAP>(g, ld, rows, row0 + 128 * s, k0, tile + s * DL_TILE, wave, lane, rp);
+    dl_issue<KM, MAP>(g, ld, rows, row0 + 128 * s, k0, tile + s * DL_TILE, wave, lane, MAP ? rmap + 2 * s : nullptr);
 }
 
 // One k-step: wait for this wave's part of tile `it`, barrier, read the
@@ -589,7 +599,7 @@ __device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK,
   dl_read<AK, BK, FM, FN>(da.at(as), db.at(bs), af, bfr);
   const int kn = c.kbeg + min(it + 2, c.nk - 1) * DL_BK;
   dl_issue_tile<AK, NSA>(c.A, c.lda, c.M, c.m0, kn, An, c.wave, c.lane);
-  dl_issue_tile<BK, NSB, MAP>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane, &c.rp);
+  dl_issue_tile<BK, NSB, MAP>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane, c.brow);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -598,12 +608,39 @@ __device__ __forceinline__ void dl_step(const DlCtx& c, int it, const DlAddr<AK,
                                                           __builtin_bit_cast(bf16x8_t, af[i]), acc[i][j], 0, 0, 0);
 }
 
+// RoPE epilogue (RP), first phase: accumulator columns n .. n+3 of a rotated
+// head hold two pairs (output dims i, i + R/2, i + 1, i + 1 + R/2 for
+// rotate-half, by the B-row map; dims c .. c+3 for even-odd), rotated in
+// place in fp32 by the angle of row m's position t = m % T.  No store runs
+// in this phase, so every table read may be issued ahead of the others (a
+// store to C between them would have to be assumed to alias the table).
+template <int FM, int FN>
+__device__ __forceinline__ void rope_rotate_acc(const KArgs& a, f32x4 (&acc)[FM][FN], int m0, int n0, int wm, int wn,
+                                                int lane) {
+  const RopeEpi& r = a.rope;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = min(m0 + wm * 16 * FM + i * 16 + (lane & 15), a.M - 1);
+    const float* tb = r.cs + (int64_t)(m % r.T) * r.R;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * 16 * FN + j * 16 + 4 * (lane >> 4);
+      const int c = n % r.d;
+      if (n < r.end && c < r.R) {
+        const float4 cs = *reinterpret_cast<const float4*>(tb + c);  // pairs c/2 and c/2 + 1
+        const f32x4 v = acc[i][j];
+        acc[i][j] = f32x4{v[0] * cs.x - v[1] * cs.y, v[0] * cs.y + v[1] * cs.x, v[2] * cs.z - v[3] * cs.w,
+                          v[2] * cs.w + v[3] * cs.z};
+      }
+    }
+  }
+}
+
 // Block epilogue: lane holds C[m][n .. n+3] of each 16 x 16 fragment; split-K
 // blocks write fp32 partials, the others alpha C (+ R) in the output type.
-// RoPE epilogue (RP): accumulator columns n .. n+3 of a rotated head hold
-// two pairs (output dims i, i + R/2, i + 1, i + 1 + R/2 for rotate-half, by
-// the B-row map; dims c .. c+3 for even-odd), rotated in fp32 by the angle of
-// row m's position t = m % T before the one rounding to bf16.
+// RP: the accumulators were rotated by rope_rotate_acc; a rotated
+// rotate-half group (y0, y1, y2, y3) = dims (i, i + R/2, i + 1, i + 1 + R/2)
+// is stored as two pairs.
 template <typename TO, bool SPLIT, int FM, int FN, bool RP = false>
 __device__ __forceinline__ void dl_epilogue(const KArgs& a, const f32x4 (&acc)[FM][FN], int m0, int n0, int wm, int wn,
                                             int lane) {
@@ -611,8 +648,6 @@ __device__ __forceinline__ void dl_epilogue(const KArgs& a, const f32x4 (&acc)[F
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * 16 * FM + i * 16 + (lane & 15);
     if (m >= a.M) continue;
-    const float* tb = nullptr;
-    if constexpr (RP) tb = a.rope.cs + (int64_t)(m % a.rope.T) * a.rope.R;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + wn * 16 * FN + j * 16 + 4 * (lane >> 4);
@@ -620,22 +655,13 @@ __device__ __forceinline__ void dl_epilogue(const KArgs& a, const f32x4 (&acc)[F
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       if constexpr (RP) {
         const int c = n % a.rope.d;
-        if (n < a.rope.end && c < a.rope.R) {
-          const float4 cs = *reinterpret_cast<const float4*>(tb + c);  // pairs c/2 and c/2 + 1
-          const float y0 = v[0] * cs.x - v[1] * cs.y, y1 = v[0] * cs.y + v[1] * cs.x;
-          const float y2 = v[2] * cs.z - v[3] * cs.w, y3 = v[2] * cs.w + v[3] * cs.z;
-          TO* row = static_cast<TO*>(a.C) + (int64_t)m * a.ldc + (n - c);
-          if (a.rope.half) {
-            const int i0 = c >> 1;
-            Pk<TO, 2> lo, hi;
-            lo.e[0] = from_f32<TO>(y0); lo.e[1] = from_f32<TO>(y2);
-            hi.e[0] = from_f32<TO>(y1); hi.e[1] = from_f32<TO>(y3);
-            *reinterpret_cast<Pk<TO, 2>*>(row + i0) = lo;
-            *reinterpret_cast<Pk<TO, 2>*>(row + i0 + (a.rope.R >> 1)) = hi;
-          } else {
-            const float y[4] = {y0, y1, y2, y3};
-            store4<TO>(row + c, y);
-          }
+        if (a.rope.half && n < a.rope.end && c < a.rope.R) {
+          TO* row = static_cast<TO*>(a.C) + (int64_t)m * a.ldc + (n - c) + (c >> 1);
+          Pk<TO, 2> lo, hi;
+          lo.e[0] = from_f32<TO>(v[0]); lo.e[1] = from_f32<TO>(v[2]);
+          hi.e[0] = from_f32<TO>(v[1]); hi.e[1] = from_f32<TO>(v[3]);
+          *reinterpret_cast<Pk<TO, 2>*>(row) = lo;
+          *reinterpret_cast<Pk<TO, 2>*>(row + (a.rope.R >> 1)) = hi;
           continue;
         }
       }
@@ -708,7 +734,7 @@ __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a)
   c.nk = (min(a.K, c.kbeg + a.kchunk) - c.kbeg) / DL_BK;
   c.wave = wave;
   c.lane = lane;
-  c.rp = a.rope;
+  if constexpr (RP) dl_rope_rows<NSB>(a.rope, a.N, c.n0, wave, lane, c.brow);
   const DlAddr<AK, FM> da(wm * 16 * FM, lane);
   const DlAddr<BK, FN> db(wn * 16 * FN, lane);
 
@@ -719,9 +745,9 @@ __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a)
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   dl_issue_tile<AK, NSA>(c.A, c.lda, c.M, c.m0, c.kbeg, A0, wave, lane);
-  dl_issue_tile<BK, NSB, RP>(c.B, c.ldb, c.N, c.n0, c.kbeg, B0, wave, lane, &c.rp);
+  dl_issue_tile<BK, NSB, RP>(c.B, c.ldb, c.N, c.n0, c.kbeg, B0, wave, lane, c.brow);
   dl_issue_tile<AK, NSA>(c.A, c.lda, c.M, c.m0, c.kbeg + min(1, c.nk - 1) * DL_BK, A1, wave, lane);
-  dl_issue_tile<BK, NSB, RP>(c.B, c.ldb, c.N, c.n0, c.kbeg + min(1, c.nk - 1) * DL_BK, B1, wave, lane, &c.rp);
+  dl_issue_tile<BK, NSB, RP>(c.B, c.ldb, c.N, c.n0, c.kbeg + min(1, c.nk - 1) * DL_BK, B1, wave, lane, c.brow);
   const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
   const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
   for (int it = 0; it < c.nk; it += 3) {
@@ -730,6 +756,7 @@ __global__ __launch_bounds__(NT, (FM * FN > 16) ? 2 : 1) void gemm_dl_k(KArgs a)
     if (it + 2 < c.nk) dl_step<AK, BK, FM, FN, RP>(c, it + 2, da, db, a2, b2, A1, B1, acc);
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+  if constexpr (RP) rope_rotate_acc<FM, FN>(a, acc, c.m0, c.n0, wm, wn, lane);
   dl_epilogue<TO, SPLIT, FM, FN, RP>(a, acc, c.m0, c.n0, wm, wn, lane);
 }
 
@@ -750,7 +777,7 @@ constexpr int W8_NT = 512;
 
 template <bool KM, bool MAP = false>
 __device__ __forceinline__ void w8_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
-                                         int lane, const RopeEpi* rp = nullptr) {
+                                         int lane, const int* rmap = nullptr) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int p = wave * 64 + lane;  // 16-byte chunk position in the 128 x 32 sub-tile
@@ -759,8 +786,7 @@ __device__ __forceinline__ void w8_issue(const bf16* g, int64_t ld, int rows, in
     if constexpr (KM) {
       const int r = p >> 2;
       const int lc = (p & 3) ^ dl_swz(r);
-      int row = min(r0 + r, rows - 1);
-      if constexpr (MAP) row = rope_row(*rp, row);
+      const int row = MAP ? rmap[s] : min(r0 + r, rows - 1);
       src = g + (int64_t)row * ld + k0 + lc * 8;
     } else {
       const int kr = p >> 4;
@@ -798,7 +824,7 @@ __device__ __forceinline__ void w8_step(const DlCtx& c, int it, const DlAddr<AK,
   const int kn = c.kbeg + min(it + 2, c.nk - 1) * DL_BK;
   w8_issue<AK>(c.A, c.lda, c.M, c.m0, kn, An, c.wave, c.lane);
   if constexpr (EPI == 1) w8_issue_pair(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane);
-  else w8_issue<BK, EPI == 2>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane, &c.rp);
+  else w8_issue<BK, EPI == 2>(c.B, c.ldb, c.N, c.n0, kn, Bn, c.wave, c.lane, c.brow);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -868,7 +894,10 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
   c.nk = a.K / DL_BK;
   c.wave = wave;
   c.lane = lane;
-  c.rp = a.rope;
+  if constexpr (EPI == 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) c.brow[s] = rope_row(a.rope, min(c.n0 + 128 * s + ((wave * 64 + lane) >> 2), a.N - 1));
+  }
   const DlAddr<AK, 8> da(wm * 128, lane);
   const DlAddr<BK, 4> db(wn * 64, lane);
 
@@ -885,7 +914,7 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
     const int k0 = min(t, c.nk - 1) * DL_BK;
     w8_issue<AK>(c.A, c.lda, c.M, c.m0, k0, t ? A1 : A0, wave, lane);
     if constexpr (EPI == 1) w8_issue_pair(c.B, c.ldb, c.N, c.n0, k0, t ? B1 : B0, wave, lane);
-    else w8_issue<BK, EPI == 2>(c.B, c.ldb, c.N, c.n0, k0, t ? B1 : B0, wave, lane, &c.rp);
+    else w8_issue<BK, EPI == 2>(c.B, c.ldb, c.N, c.n0, k0, t ? B1 : B0, wave, lane, c.brow);
   }
   const unsigned a0 = lds_off(A0), a1 = lds_off(A1), a2 = lds_off(A2);
   const unsigned b0 = lds_off(B0), b1 = lds_off(B1), b2 = lds_off(B2);
@@ -895,6 +924,7 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
     if (it + 2 < c.nk) w8_step<AK, BK, EPI>(c, it + 2, da, db, a2, b2, A1, B1, acc);
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+  if constexpr (EPI == 2) rope_rotate_acc<8, 4>(a, acc, c.m0, c.n0, wm, wn, lane);
   if constexpr (EPI == 1) w8_epilogue_swiglu_fwd(a, acc, c.m0, c.n0, wm, wn, lane);
   else dl_epilogue<TO, false, 8, 4, EPI == 2>(a, acc, c.m0, c.n0, wm, wn, lane);
 }
@@ -917,14 +947,13 @@ __device__ __forceinline__ int d64_swz(int r) { return 2 * ((r >> 1) & 3); }
 // Copy the (32 F) x 64 tile at (row0, k0): F copies per lane.
 template <int F, bool MAP = false>
 __device__ __forceinline__ void d64_issue(const bf16* g, int64_t ld, int rows, int row0, int k0, bf16* tile, int wave,
-                                          int lane, const RopeEpi* rp = nullptr) {
+                                          int lane, const int* rmap = nullptr) {
 #pragma unroll
   for (int i = 0; i < F; ++i) {
     const int p = (wave * F + i) * 64 + lane;  // 16-byte chunk position in the tile
     const int r = p >> 3;
     const int lc = (p & 7) ^ d64_swz(r);
-    int row = min(row0 + r, rows - 1);
-    if constexpr (MAP) row = rope_row(*rp, row);
+    const int row = MAP ? rmap[i] : min(row0 + r, rows - 1);
     lds_copy16(g + (int64_t)row * ld + k0 + lc * 8, tile + (wave * F + i) * 512);
   }
 }
@@ -979,15 +1008,20 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  int brow[4] = {0, 0, 0, 0};  // B rows this lane copies under the RoPE epilogue's row map
+  if constexpr (RP) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) brow[i] = rope_row(a.rope, min(n0 + (((wave * 4 + i) * 64 + lane) >> 3), a.N - 1));
+  }
   d64_issue<FM>(A, a.lda, a.M, m0, kbeg, A0, wave, lane);
-  d64_issue<4, RP>(B, a.ldb, a.N, n0, kbeg, B0, wave, lane, &a.rope);
+  d64_issue<4, RP>(B, a.ldb, a.N, n0, kbeg, B0, wave, lane, brow);
   for (int it = 0; it < nk; ++it) {
     SLT_WAIT_VMCNT(0);  // this wave's copies of tile it have landed
     lds_barrier();      // ... everyone's have, and the other stage is free
     if (it + 1 < nk) {
       const int kn = kbeg + (it + 1) * 64;
       d64_issue<FM>(A, a.lda, a.M, m0, kn, (it & 1) ? A0 : A1, wave, lane);
-      d64_issue<4, RP>(B, a.ldb, a.N, n0, kn, (it & 1) ? B0 : B1, wave, lane, &a.rope);
+      d64_issue<4, RP>(B, a.ldb, a.N, n0, kn, (it & 1) ? B0 : B1, wave, lane, brow);
     }
     const unsigned as = lds_off((it & 1) ? A1 : A0), bs = lds_off((it & 1) ? B1 : B0);
 #pragma unroll
@@ -1003,6 +1037,7 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
     }
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
+  if constexpr (RP) rope_rotate_acc<FM, 4>(a, acc, m0, n0, wm, wn, lane);
   dl_epilogue<TO, SPLIT, FM, 4, RP>(a, acc, m0, n0, wm, wn, lane);
 }
 
