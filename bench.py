@@ -142,9 +142,11 @@ def kernel_classes(w, ts, torch, reps, only=None):
 
         sec = time_block(run, reps, torch)
         flops = sum(2.0 * M * N * K for (M, N, K, _) in launches)
+        oes = 4 if cls == "gemm_dw" else es  # weight gradients are written in fp32
+        byt = sum((M * K + N * K) * es + M * N * oes * (2 if r else 1) for (M, N, K, r) in launches)
         out[cls] = {"ms_per_step": sec * 1e3, "launches": len(launches), "tflops": flops / sec / 1e12,
-                    "frac_of_peak": flops / sec / 1e12 / peak, "flops": flops, "avg_launch_us": sec * 1e6 / len(launches),
-                    "bound": "mfma", "peak": peak}
+                    "frac_of_peak": flops / sec / 1e12 / peak, "flops": flops, "bytes": byt,
+                    "avg_launch_us": sec * 1e6 / len(launches), "bound": "mfma", "peak": peak}
         del bufs
     if only is not None and only.startswith("gemm"):
         return out
@@ -181,37 +183,47 @@ def kernel_classes(w, ts, torch, reps, only=None):
                                 mode, cs, dt, aws)
 
     fa, ba = attn_flops(w)
+    # algorithmic bytes per layer: forward reads q, k, v and writes o and the
+    # log-sum-exp; backward reads q, k, v, o, dO and the log-sum-exp and
+    # writes dQ, dK, dV
+    qb, kb = w.N * qd * es, w.N * kd * es
+    ab = {"attention_fwd": 2 * qb + 2 * kb + 4 * w.B * w.H * w.T,
+          "attention_bwd": 5 * qb + 4 * kb + 4 * w.B * w.H * w.T}
     fwd()  # lse for the backward
     for name, fn, fl, nl in [("attention_fwd", fwd, fa, w.L), ("attention_bwd", bwd, ba, 2 * w.L)]:
         if only is not None and name != only:
             continue
         sec = time_block(fn, reps, torch)
         out[name] = {"ms_per_step": sec * 1e3, "launches": nl, "tflops": fl / sec / 1e12,
-                     "frac_of_peak": fl / sec / 1e12 / peak, "flops": fl, "avg_launch_us": sec * 1e6 / nl,
-                     "bound": "mfma", "peak": peak}
+                     "frac_of_peak": fl / sec / 1e12 / peak, "flops": fl, "bytes": ab[name] * w.L,
+                     "avg_launch_us": sec * 1e6 / nl, "bound": "mfma", "peak": peak}
     del qkv, o, ores, g, dqkv, aws
     return out
 
 
-def time_cold(fn, reps, torch, evict):
-    """Median and best seconds of single fn() launches, each timed alone with
-    HIP events on the current stream, with a 512 MiB copy between them (not
-    timed) so that the 256 MB Infinity Cache holds none of fn's data: the
-    HBM rate, not the cache's."""
-    src, dst = evict
-    from scratch_llama_transformer_amd import binding as B
+TRAIN_BYTES = 1 << 30  # footprint of one timed train of an HBM-bound kernel
+
+
+def time_train(fns, reps, torch):
+    """Median and best seconds per launch of a train of launches fns[0],
+    fns[1], ... (each on its own buffers) timed as one with HIP events on
+    the current stream.  With the buffers' total footprint at 1 GiB or more,
+    the 256 MB Infinity Cache holds none of a launch's inputs when it starts,
+    and lines written by one launch are written back to HBM during the
+    following ones: the train runs at the sustained HBM rate, not the cache's."""
     s = torch.cuda.current_stream()
-    fn()
+    for f in fns:
+        f()
     times = []
     for _ in range(reps):
-        B.slt_stream_copy(src, dst, src.numel())  # evict
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(s)
-        fn()
+        for f in fns:
+            f()
         b.record(s)
         b.synchronize()
-        times.append(a.elapsed_time(b) / 1e3)
+        times.append(a.elapsed_time(b) / 1e3 / len(fns))
     times.sort()
     return times[len(times) // 2], times[0]
 
@@ -226,7 +238,7 @@ def machine_bounds(torch):
     dst = torch.empty_like(src)
     s = torch.cuda.current_stream()
     best, best_v = None, 0
-    for v in range(3):
+    for v in range(4):
         for _ in range(4):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
@@ -257,90 +269,126 @@ def machine_bounds(torch):
             "mfma_bf16_tflops": round(max(rates.values()), 1),
             "mfma_loop_tflops": {"16x16x32 x8": round(rates[0], 1), "32x32x16 x8": round(rates[1], 1),
                                  "16x16x32 x16": round(rates[2], 1)},
-            "copy_kernel": f"slt_stream_copy variant {best_v} (16-byte non-temporal loads and stores, 2 GiB each "
-                           "way; best of 3 launch shapes x 4)",
+            "copy_kernel": f"slt_stream_copy variant {best_v} (16-byte loads and stores, 2 GiB each way; best of "
+                           "4 launch shapes x 4)",
             "mfma_kernel": "slt_mfma_loop (independent MFMA chains per wave, 32 waves per CU; best variant)"}
 
 
 def hbm_classes(w, torch, reps, machine):
-    """Every HBM-bound kernel of the step at the step's sizes and strides,
-    each launch timed alone on a cold cache (time_cold): norm forward and
-    backward, SwiGLU or GELU forward and backward, softmax cross-entropy,
-    embedding forward and backward, AdamW and the gradient norm.  Bytes are
-    the algorithmic ones (each operand read or written once)."""
+    """Every HBM-bound kernel of the step at the step's sizes and strides:
+    norm forward and backward, SwiGLU or GELU forward and backward, softmax
+    cross-entropy, embedding forward and backward, AdamW and the gradient
+    norm.  Each is timed in trains of launches over as many copies of its
+    operands as make 1 GiB (time_train).  Bytes are the algorithmic ones
+    (each operand read or written once)."""
     from scratch_llama_transformer_amd import binding as B
     import slt_workloads as W
     dt = B.BF16 if w.act == "bf16" else B.F32
     tdt = torch.bfloat16 if dt == B.BF16 else torch.float32
     e = 2 if dt == B.BF16 else 4
     N, C, F, V = w.N, w.C, w.F, w.V
-    ev = (torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(0),
-          torch.empty(512 << 20, dtype=torch.uint8, device="cuda"))
     rnd = lambda *shape: torch.empty(*shape, dtype=tdt, device="cuda").normal_()
+    emp = lambda *shape, dtype=tdt: torch.empty(*shape, dtype=dtype, device="cuda")
     out = {}
 
-    def add(name, fn, byt):
-        med, best = time_cold(fn, reps, torch, ev)
+    def add(name, factory, byt):
+        k = max(1, min(64, -(-TRAIN_BYTES // int(byt))))
+        fns = [factory() for _ in range(k)]
+        med, best = time_train(fns, reps, torch)
+        del fns
         gbs = byt / med / 1e9
         out[name] = {"us_per_launch": round(med * 1e6, 2), "best_us": round(best * 1e6, 2), "bytes": int(byt),
                      "gbps": round(gbs, 1), "frac_of_peak": round(gbs / PEAK["hbm"], 4),
-                     "frac_of_copy": round(gbs / machine["copy_gbps"], 4), "bound": "hbm"}
+                     "frac_of_copy": round(gbs / machine["copy_gbps"], 4), "bound": "hbm", "train": k}
 
-    x, dy, dres = rnd(N, C), rnd(N, C), rnd(N, C)
-    y, dx = torch.empty_like(x), torch.empty_like(x)
     g, bta = torch.ones(C, dtype=tdt, device="cuda"), torch.zeros(C, dtype=tdt, device="cuda")
-    r, mu = torch.empty(N, device="cuda"), torch.empty(N, device="cuda")
-    dg, db = torch.empty(C, device="cuda"), torch.empty(C, device="cuda")
-    nws = torch.empty(B.slt_norm_bwd_workspace(N, C), dtype=torch.uint8, device="cuda")
     if w.block == "llama":
-        B.slt_rmsnorm_fwd(x, g, y, r, N, C, w.eps, dt)
-        add("rmsnorm_fwd", lambda: B.slt_rmsnorm_fwd(x, g, y, r, N, C, w.eps, dt), N * (2 * C * e + 4) + C * e)
-        add("rmsnorm_bwd", lambda: B.slt_rmsnorm_bwd(x, g, r, dy, dres, dx, dg, N, C, dt, nws),
-            N * (4 * C * e + 4) + C * (e + 4))
-        ab, h = rnd(N, 2 * F), torch.empty(N, F, dtype=tdt, device="cuda")
-        dh, dab = rnd(N, F), torch.empty(N, 2 * F, dtype=tdt, device="cuda")
-        pa, pd = ab.data_ptr(), dab.data_ptr()
-        add("swiglu_fwd", lambda: B.slt_swiglu_fwd(pa, pa + F * e, h, N, F, 2 * F, 2 * F, F, dt), 3 * N * F * e)
-        add("swiglu_bwd", lambda: B.slt_swiglu_bwd(pa, pa + F * e, dh, pd, pd + F * e, N, F, 2 * F, 2 * F, F, 2 * F,
-                                                   2 * F, dt), 5 * N * F * e)
-        del ab, h, dh, dab
+        def rms_fwd():
+            x, y, r = rnd(N, C), emp(N, C), emp(N, dtype=torch.float32)
+            return lambda: B.slt_rmsnorm_fwd(x, g, y, r, N, C, w.eps, dt)
+
+        def rms_bwd():
+            x, dy, dres, dx = rnd(N, C), rnd(N, C), rnd(N, C), emp(N, C)
+            r, dg = emp(N, dtype=torch.float32), emp(C, dtype=torch.float32)
+            nws = emp(B.slt_norm_bwd_workspace(N, C), dtype=torch.uint8)
+            B.slt_rmsnorm_fwd(x, g, dx, r, N, C, w.eps, dt)
+            return lambda: B.slt_rmsnorm_bwd(x, g, r, dy, dres, dx, dg, N, C, dt, nws)
+
+        def swi_fwd():
+            ab, h = rnd(N, 2 * F), emp(N, F)
+            pa = ab.data_ptr()
+            return lambda ab=ab: B.slt_swiglu_fwd(pa, pa + F * e, h, N, F, 2 * F, 2 * F, F, dt)
+
+        def swi_bwd():
+            ab, dh, dab = rnd(N, 2 * F), rnd(N, F), emp(N, 2 * F)
+            pa, pd = ab.data_ptr(), dab.data_ptr()
+            return lambda ab=ab, dab=dab: B.slt_swiglu_bwd(pa, pa + F * e, dh, pd, pd + F * e, N, F, 2 * F, 2 * F, F,
+                                                           2 * F, 2 * F, dt)
+
+        add("rmsnorm_fwd", rms_fwd, N * (2 * C * e + 4) + C * e)
+        add("rmsnorm_bwd", rms_bwd, N * (4 * C * e + 4) + C * (e + 4))
+        add("swiglu_fwd", swi_fwd, 3 * N * F * e)
+        add("swiglu_bwd", swi_bwd, 5 * N * F * e)
     else:
-        B.slt_layernorm_fwd(x, g, bta, y, mu, r, N, C, w.eps, dt)
-        add("layernorm_fwd", lambda: B.slt_layernorm_fwd(x, g, bta, y, mu, r, N, C, w.eps, dt),
-            N * (2 * C * e + 8) + 2 * C * e)
-        add("layernorm_bwd", lambda: B.slt_layernorm_bwd(x, g, mu, r, dy, dres, dx, dg, db, N, C, dt, nws),
-            N * (4 * C * e + 8) + C * (e + 8))
-        a, u, du, da = rnd(N, F), torch.empty(N, F, dtype=tdt, device="cuda"), rnd(N, F), torch.empty(N, F, dtype=tdt,
-                                                                                                        device="cuda")
-        add("gelu_fwd", lambda: B.slt_gelu_fwd(a, u, N, F, F, F, dt), 2 * N * F * e)
-        add("gelu_bwd", lambda: B.slt_gelu_bwd(a, du, da, N, F, F, F, F, dt), 3 * N * F * e)
-        del a, u, du, da
-    del x, dy, dres, y, dx, nws
+        def ln_fwd():
+            x, y = rnd(N, C), emp(N, C)
+            mu, r = emp(N, dtype=torch.float32), emp(N, dtype=torch.float32)
+            return lambda: B.slt_layernorm_fwd(x, g, bta, y, mu, r, N, C, w.eps, dt)
+
+        def ln_bwd():
+            x, dy, dres, dx = rnd(N, C), rnd(N, C), rnd(N, C), emp(N, C)
+            mu, r = emp(N, dtype=torch.float32), emp(N, dtype=torch.float32)
+            dg, db = emp(C, dtype=torch.float32), emp(C, dtype=torch.float32)
+            nws = emp(B.slt_norm_bwd_workspace(N, C), dtype=torch.uint8)
+            B.slt_layernorm_fwd(x, g, bta, dx, mu, r, N, C, w.eps, dt)
+            return lambda: B.slt_layernorm_bwd(x, g, mu, r, dy, dres, dx, dg, db, N, C, dt, nws)
+
+        def gelu_fwd():
+            a, u = rnd(N, F), emp(N, F)
+            return lambda: B.slt_gelu_fwd(a, u, N, F, F, F, dt)
+
+        def gelu_bwd():
+            a, du, da = rnd(N, F), rnd(N, F), emp(N, F)
+            return lambda: B.slt_gelu_bwd(a, du, da, N, F, F, F, F, dt)
+
+        add("layernorm_fwd", ln_fwd, N * (2 * C * e + 8) + 2 * C * e)
+        add("layernorm_bwd", ln_bwd, N * (4 * C * e + 8) + C * (e + 8))
+        add("gelu_fwd", gelu_fwd, 2 * N * F * e)
+        add("gelu_bwd", gelu_bwd, 3 * N * F * e)
     tok = torch.from_numpy(W.make_tokens(w, 1000)).cuda()
-    z = rnd(N, V)
-    loss = torch.empty(1, device="cuda")
-    rl = torch.empty(4 * N, dtype=torch.uint8, device="cuda")
-    add("softmax_xent", lambda: B.slt_softmax_xent(z, V, tok, w.B, w.T, w.T + 1, V, loss, None, dt, rl),
-        2 * N * V * e + 4 * N)
-    del z
-    wte, xe = rnd(V, C), torch.empty(N, C, dtype=tdt, device="cuda")
-    add("embedding_fwd", lambda: B.slt_embedding_fwd(tok, w.B, w.T, w.T + 1, wte, xe, V, C, dt), N * (2 * C * e + 4))
-    dwte = torch.empty(V, C, device="cuda")
-    ews = torch.empty(B.slt_embedding_bwd_workspace(N, V), dtype=torch.uint8, device="cuda")
-    add("embedding_bwd", lambda: B.slt_embedding_bwd(tok, w.B, w.T, w.T + 1, xe, dwte, V, C, dt, ews),
-        N * (C * e + 4) + V * C * 4)
-    del wte, xe, dwte, ews
+
+    def xent():
+        z, loss, rl = rnd(N, V), emp(1, dtype=torch.float32), emp(4 * N, dtype=torch.uint8)
+        return lambda: B.slt_softmax_xent(z, V, tok, w.B, w.T, w.T + 1, V, loss, None, dt, rl)
+
+    def emb_fwd():
+        wte, xe = rnd(V, C), emp(N, C)
+        return lambda: B.slt_embedding_fwd(tok, w.B, w.T, w.T + 1, wte, xe, V, C, dt)
+
+    def emb_bwd():
+        dxe, dwte = rnd(N, C), emp(V, C, dtype=torch.float32)
+        ews = emp(B.slt_embedding_bwd_workspace(N, V), dtype=torch.uint8)
+        return lambda: B.slt_embedding_bwd(tok, w.B, w.T, w.T + 1, dxe, dwte, V, C, dt, ews)
+
+    add("softmax_xent", xent, 2 * N * V * e + 4 * N)
+    add("embedding_fwd", emb_fwd, N * (2 * C * e + 4))
+    add("embedding_bwd", emb_bwd, N * (C * e + 4) + V * C * 4)
     _, n = B.slt_param_layout(B.make_config(w))
-    th = torch.empty(n, device="cuda").normal_(0, 0.02)
-    gr = torch.empty(n, device="cuda").normal_(0, 1e-3)
-    m = torch.zeros(n, device="cuda")
-    v = torch.zeros(n, device="cuda")
-    sh = torch.empty(n, dtype=torch.int16, device="cuda") if dt == B.BF16 else None
-    cws = torch.empty(B.slt_clip_workspace_bytes(), dtype=torch.uint8, device="cuda")
-    nrm = torch.empty(2, device="cuda")
-    add("adamw", lambda: B.slt_adamw_step(n, th, sh, gr, m, v, 1, 1e-3, 0.9, 0.999, 1e-8, 0.1),
-        n * (30 if sh is not None else 28))
-    add("grad_norm", lambda: B.slt_clip_grad_norm(n, gr, B.NORM_L2, 1.0, nrm, nrm.data_ptr() + 4, cws), 4 * n)
+    bf = dt == B.BF16
+
+    def adamw():
+        th, gr = torch.empty(n, device="cuda").normal_(0, 0.02), torch.empty(n, device="cuda").normal_(0, 1e-3)
+        m, v = torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+        sh = emp(n, dtype=torch.int16) if bf else None
+        return lambda: B.slt_adamw_step(n, th, sh, gr, m, v, 1, 1e-3, 0.9, 0.999, 1e-8, 0.1)
+
+    def gnorm():
+        gr = torch.empty(n, device="cuda").normal_(0, 1e-3)
+        cws, nrm = emp(B.slt_clip_workspace_bytes(), dtype=torch.uint8), emp(2, dtype=torch.float32)
+        return lambda: B.slt_clip_grad_norm(n, gr, B.NORM_L2, 1.0, nrm, nrm.data_ptr() + 4, cws)
+
+    add("adamw", adamw, n * (30 if bf else 28))
+    add("grad_norm", gnorm, 4 * n)
     return out
 
 
@@ -411,7 +459,7 @@ def main():
                     default=None,
                     help="only time one GEMM class of the breakdown (for hardware-counter runs) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only copy MIB MiB device-to-device 5 times (for scaling HBM byte counters) and exit")
+                    help="only copy MIB MiB 5 times with slt_stream_copy (for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -421,6 +469,7 @@ def main():
 
     import torch
     import slt_workloads as W
+    from scratch_llama_transformer_amd import binding as B
     from scratch_llama_transformer_amd.trainer import TrainStep
 
     if args.calibrate_copy:
@@ -428,7 +477,7 @@ def main():
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            B.slt_stream_copy(src, dst, n, 2)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
         return
@@ -494,7 +543,7 @@ def main():
                 v["frac_of_measured"] = v["tflops"] / mpeak
         out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
                               if kk in ("ms_per_step", "launches", "tflops", "frac_of_peak", "frac_of_measured",
-                                        "avg_launch_us")}
+                                        "avg_launch_us", "bytes")}
                           for k, v in cl.items()}
         out["hbm_kernels"] = hbm_classes(w, torch, max(args.kernel_reps, 5), machine)
         # the dominant kernel class of the step: the largest time per step in
@@ -502,16 +551,28 @@ def main():
         # a smaller share)
         name = max(cl, key=lambda k: cl[k]["ms_per_step"])
         c = cl[name]
+        # the roof that bounds it: HBM when its arithmetic intensity (FLOPs
+        # per algorithmic byte) is below the ridge point peak FLOP/s / peak
+        # HBM bytes/s, the matrix cores otherwise
+        ai = c["flops"] / c["bytes"]
+        ridge = c["peak"] * 1e12 / (PEAK["hbm"] * 1e9)
         kern = {"gemm_fwd": "forward-projection GEMMs (k-major x k-major)",
                 "gemm_dx": "activation-gradient GEMMs dX = dY W",
                 "gemm_dw": "grouped weight-gradient GEMMs dW = dY^T X",
                 "attention_fwd": "causal attention forward (fl_fwd_k)",
                 "attention_bwd": "causal attention backward (fl_dq_k + fl_dkdv2_k)"}[name]
-        out["roofline"] = {"kernel": kern, "class": name, "bound": c["bound"],
-                           "achieved": round(c["tflops"], 2), "peak": c["peak"], "unit": "TFLOP/s",
-                           "frac": round(c["tflops"] / c["peak"], 4),
-                           "frac_of_measured": round(c["tflops"] / mpeak, 4) if mpeak else None,
+        if ai >= ridge:
+            ach, pk, unit, mp = c["tflops"], c["peak"], "TFLOP/s", mpeak
+        else:
+            ach, pk, unit, mp = c["bytes"] / (c["ms_per_step"] / 1e3) / 1e9, PEAK["hbm"], "GB/s", machine["copy_gbps"]
+        out["roofline"] = {"kernel": kern, "class": name, "bound": "mfma" if ai >= ridge else "hbm",
+                           "achieved": round(ach, 2), "peak": pk, "unit": unit, "frac": round(ach / pk, 4),
+                           "frac_of_measured": round(ach / mp, 4) if mp else None,
                            "traffic": measured_traffic(w, name),
+                           "algorithmic_bytes_per_launch": int(c["bytes"] / c["launches"]),
+                           "flops_per_launch": int(c["flops"] / c["launches"]),
+                           "arithmetic_intensity": round(ai, 1), "ridge": round(ridge, 1),
+                           "tflops": round(c["tflops"], 2),
                            "avg_launch_us": round(c["avg_launch_us"], 2), "launches_per_step": c["launches"]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

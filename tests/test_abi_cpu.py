@@ -134,6 +134,16 @@ def test_host_calls_reject_bad_arguments_before_launch():
     # QKV with RoPE: heads wider than N, odd R
     assert lib.slt_qkv_rope_fwd(4, 16, 8, None, None, None, 16, 4, 2, 2, 8, 8, 0, None, 1, None) == 1
     assert lib.slt_qkv_rope_fwd(4, 64, 8, None, None, None, 64, 4, 2, 2, 8, 7, 0, None, 1, None) == 1
+    # machine-bound kernels: bad variant, size not a multiple of 16, NULL
+    assert lib.slt_stream_copy(None, None, 32, 4, None) == 1
+    assert lib.slt_stream_copy(None, None, 24, 0, None) == 1
+    assert lib.slt_stream_copy(None, None, 32, 0, None) == 1
+    assert lib.slt_stream_copy(None, None, 0, 0, None) == 0
+    assert lib.slt_mfma_loop(8, 4, 3, None, None) == 1
+    assert lib.slt_mfma_loop(0, 4, 0, None, None) == 1
+    assert B.slt_mfma_loop_flops(8, 4, 0) == 8 * 4 * 4 * 8 * 16384
+    assert B.slt_mfma_loop_flops(8, 4, 1) == 8 * 4 * 4 * 8 * 32768
+    assert B.slt_mfma_loop_flops(8, 4, 2) == 8 * 4 * 4 * 16 * 16384
 
 
 def test_kv_cache_sizes():

@@ -699,3 +699,22 @@ def test_model_init_statistics(B):
     B.slt_model_init(cfg, 1234, 0.02, 1.0 / math.sqrt(2 * w.L), again)
     torch.cuda.synchronize()
     assert torch.equal(master, again)
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_stream_copy_and_mfma_loop(B, variant):
+    """The machine-bound kernels do the work they are timed for: the copy
+    moves every byte (sizes that leave partial iterations and a tail), and
+    the MFMA loop writes finite accumulators for every lane."""
+    print(f"stream_copy variant {variant}", flush=True)
+    for nbytes in (16, 16 * 1000003, (3 << 20) + 48):
+        src = torch.randint(-128, 127, (nbytes,), dtype=torch.int8, device="cuda")
+        dst = torch.zeros_like(src)
+        B.slt_stream_copy(src, dst, nbytes, variant)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst), nbytes
+    if variant < 3:
+        out = torch.full((4 * 256,), float("nan"), device="cuda")
+        B.slt_mfma_loop(4, 3, out, variant)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all())
