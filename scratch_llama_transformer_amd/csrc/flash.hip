@@ -29,7 +29,8 @@
 //    zero-padded dims; the score products contract over 64 padded dims.
 //  * Precision: one bf16 operand per product.  The probabilities P (into
 //    P V and dV) and the score gradient dS (into dQ and dK) are rounded to
-//    bf16 in registers; D = dO.O uses O plus its stored bf16 rounding
+//    bf16 in registers (at d = 64 the forward's softmax denominators are the
+//    sums of those rounded P); D = dO.O uses O plus its stored bf16 rounding
 //    residual, so that sum_j dS_ij stays zero to fp32 accuracy.
 //  * Tiles: LDS tile rows are 8 chunks of 16 bytes with chunk position XOR
 //    2((row >> 1) & 3), so both the row-fragment reads (ds_read_b128) and the
@@ -73,11 +74,14 @@ __device__ __forceinline__ float bf_hi(float x) { return __uint_as_float((uint32
 // one query's keys) with gfx950's v_permlane32_swap / v_permlane16_swap: with
 // both operands equal, the swap leaves each lane its own value in one result
 // and its partner's in the other, so no LDS round trip is needed.
+// fmax: IEEE maximum (NaN-propagating; the scores hold no NaN), which gfx950
+// runs as v_maximum3_f32 with no canonicalising step per operand.
+__device__ __forceinline__ float fmx(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float max4lanes(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  v = fmx(__uint_as_float(r[0]), __uint_as_float(r[1]));
   const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  return fmx(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ __forceinline__ float sum4lanes(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -300,12 +304,22 @@ __global__ __launch_bounds__(256, 2) void fl_fwd_k(FlArgs a) {
   const bf16* kb = a.k + (int64_t)b * T * a.ldk + (int64_t)kvh * a.d;
   const bf16* vb = a.v + (int64_t)b * T * a.ldv + (int64_t)kvh * a.d;
 
-  f32x4 oacc[FNS][4];
+  // At d = 64 without dropout the row sums l come from the matrix cores: a
+  // product of P with an all-ones "V" tile leaves each lane the sum over the
+  // half's keys of its query's bf16 probabilities -- the weights P V uses --
+  // in every element of lacc (measured: no slower than the lanes' adds at
+  // d = 64, slower at d = 48, where P V is one MFMA shorter).  Otherwise the
+  // lanes add the weights (l; with dropout, the weights before the mask, as
+  // the normaliser must see them) and combine them at the end.
+  constexpr bool MSUM = !DROP && ND == 4;
+  f32x4 oacc[FNS][4], lacc[FNS];
   float m[FNS], l[FNS];
+  const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
   for (int i = 0; i < FNS; ++i) {
     m[i] = -INFINITY;
     l[i] = 0.f;
+    lacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -331,6 +345,81 @@ __global__ __launch_bounds__(256, 2) void fl_fwd_k(FlArgs a) {
       u32x4 kf[2][2], vf[4];
       rd_rows4(base + off.row[0] + 4096 * hf, base + off.row[1] + 4096 * hf, kf);
       rd_chalf<ND>(base + FTB + 4096 * hf, off, vf);
+      if (k0 + 31 < c0 + 16 * wave) {
+        // Every query of every subtile of the wave comes after the half's
+        // last key: no mask and no subtile to skip, so the subtiles' steps
+        // run side by side (all scores, all maxima, all probabilities, all
+        // products), giving each dependent step independent work from the
+        // other subtiles.  Same arithmetic as the masked path below.
+        float sv[FNS][2][4];
+#pragma unroll
+        for (int i = 0; i < FNS; ++i)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+            st = mma(kf[tt][0], qf[i][0], st);
+            st = mma(kf[tt][1], qf[i][1], st);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[i][tt][r] = st[r];
+          }
+        float mt[FNS];
+        bool grow[FNS], any = false;
+#pragma unroll
+        for (int i = 0; i < FNS; ++i) {
+          float tmax = sv[i][0][0];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tmax = fmx(tmax, sv[i][tt][r]);
+          mt[i] = max4lanes(tmax) * c2;
+          grow[i] = mt[i] > m[i] + 8.f;
+          any |= grow[i];
+        }
+        if (__ballot(any) != 0) {
+#pragma unroll
+          for (int i = 0; i < FNS; ++i) {
+            const float mn = grow[i] ? mt[i] : m[i];
+            const float alpha = grow[i] ? ex2(m[i] - mn) : 1.f;
+            if (MSUM) lacc[i] *= alpha;
+            else l[i] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) oacc[i][dt] *= alpha;
+            m[i] = mn;
+          }
+        }
+        u32x4 pb[FNS];
+#pragma unroll
+        for (int i = 0; i < FNS; ++i) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[i][tt][r] = ex2(fmaf(sv[i][tt][r], c2, -m[i]));
+          if (!MSUM) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) l[i] += sv[i][tt][r];
+          }
+          if (DROP) {
+            const int qi = c0 + 16 * (wave + 4 * i) + li;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              float dm[4];
+              drop_mults<4>(a.drop, att_elem(b, a.H, h, T, qi, k0 + 16 * tt + 4 * g), dm);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sv[i][tt][r] *= dm[r];
+            }
+          }
+          pb[i] = pack_k(sv[i][0], sv[i][1]);
+        }
+#pragma unroll
+        for (int i = 0; i < FNS; ++i) {
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) oacc[i][dt] = mma(vf[dt], pb[i], oacc[i][dt]);
+          if (MSUM) lacc[i] = mma(ones, pb[i], lacc[i]);
+        }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < FNS; ++i) {
         const int u0 = c0 + 16 * (wave + 4 * i);  // first query of subtile i
@@ -351,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void fl_fwd_k(FlArgs a) {
               if (k0 + 16 * tt + 4 * g + r > qi) sv[tt][r] = -INFINITY;
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sv[tt][r]);
+          for (int r = 0; r < 4; ++r) tmax = fmx(tmax, sv[tt][r]);
         }
         // The running maximum (base-2 units) moves only where a row's new
         // maximum exceeds it by more than 8, so the weights stay below 2^8;
@@ -363,20 +452,22 @@ __global__ __launch_bounds__(256, 2) void fl_fwd_k(FlArgs a) {
         if (__ballot(grow) != 0) {
           const float mn = grow ? mt : m[i];
           const float alpha = ex2(m[i] - mn);  // 1 where the maximum stays, 0 on the first half
-          l[i] *= alpha;
+          if (MSUM) lacc[i] *= alpha;
+          else l[i] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < ND; ++dt) oacc[i][dt] *= alpha;
           m[i] = mn;
         }
-        float rs = 0.f;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sv[tt][r] = ex2(fmaf(sv[tt][r], c2, -m[i]));
-            rs += sv[tt][r];
-          }
-        l[i] += rs;  // this lane's keys only; the four lanes are summed at the end
+          for (int r = 0; r < 4; ++r) sv[tt][r] = ex2(fmaf(sv[tt][r], c2, -m[i]));
+        if (!MSUM) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) l[i] += sv[tt][r];  // this lane's keys; the four lanes are summed at the end
+        }
         if (DROP) {  // the normaliser keeps every weight; the values see the dropped ones
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
@@ -389,13 +480,14 @@ __global__ __launch_bounds__(256, 2) void fl_fwd_k(FlArgs a) {
         const u32x4 pb = pack_k(sv[0], sv[1]);
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) oacc[i][dt] = mma(vf[dt], pb, oacc[i][dt]);
+        if (MSUM) lacc[i] = mma(ones, pb, lacc[i]);
       }
     }
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
 
 #pragma unroll
-  for (int i = 0; i < FNS; ++i) l[i] = sum4lanes(l[i]);
+  for (int i = 0; i < FNS; ++i) l[i] = MSUM ? lacc[i][0] : sum4lanes(l[i]);
 #pragma unroll
   for (int i = 0; i < FNS; ++i) {
     const int qi = c0 + 16 * (wave + 4 * i) + li;
