@@ -274,7 +274,11 @@ def machine_bounds(torch):
             "mfma_kernel": "slt_mfma_loop (independent MFMA chains per wave, 32 waves per CU; best variant)"}
 
 
-def hbm_classes(w, torch, reps, machine):
+HBM_CLASSES = ["rmsnorm_fwd", "rmsnorm_bwd", "swiglu_fwd", "swiglu_bwd", "layernorm_fwd", "layernorm_bwd", "gelu_fwd",
+               "gelu_bwd", "softmax_xent", "embedding_fwd", "embedding_bwd", "adamw", "grad_norm"]
+
+
+def hbm_classes(w, torch, reps, machine, only=None):
     """Every HBM-bound kernel of the step at the step's sizes and strides:
     norm forward and backward, SwiGLU or GELU forward and backward, softmax
     cross-entropy, embedding forward and backward, AdamW and the gradient
@@ -292,6 +296,8 @@ def hbm_classes(w, torch, reps, machine):
     out = {}
 
     def add(name, factory, byt):
+        if only is not None and name != only:
+            return
         k = max(1, min(64, -(-TRAIN_BYTES // int(byt))))
         fns = [factory() for _ in range(k)]
         med, best = time_train(fns, reps, torch)
@@ -455,9 +461,9 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
-    ap.add_argument("--only-class", choices=["gemm_fwd", "gemm_dx", "gemm_dw", "attention_fwd", "attention_bwd"],
-                    default=None,
-                    help="only time one GEMM class of the breakdown (for hardware-counter runs) and exit")
+    ap.add_argument("--only-class", choices=["gemm_fwd", "gemm_dx", "gemm_dw", "attention_fwd", "attention_bwd"]
+                    + HBM_CLASSES, default=None,
+                    help="only time one kernel class of the breakdown (for hardware-counter runs) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB 5 times with slt_stream_copy (for scaling HBM byte counters) and exit")
     args = ap.parse_args()
@@ -483,6 +489,12 @@ def main():
         return
 
     w = W.get_config(args.config)
+    if args.only_class in HBM_CLASSES:
+        r = hbm_classes(w, torch, max(args.kernel_reps, 1), {"copy_gbps": float("nan")}, only=args.only_class)
+        r = r[args.only_class]
+        print(json.dumps({"workload": w.name, "class": args.only_class, "us_per_launch": r["us_per_launch"],
+                          "gbps": r["gbps"], "train": r["train"]}), flush=True)
+        return
     if args.only_class:
         cl = kernel_classes(w, None, torch, args.kernel_reps, only=args.only_class)[args.only_class]
         print(json.dumps({"workload": w.name, "class": args.only_class, "launches": cl["launches"],

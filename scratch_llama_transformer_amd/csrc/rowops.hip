@@ -89,7 +89,11 @@ __global__ __launch_bounds__(256) void embedding_fwd_k(const int32_t* __restrict
 //  3. exclusive scan of the totals -> start of each id in the sorted order;
 //  4. scatter: position i goes to start[id] + prefix[chunk][id] + rank
 //     (a stable counting sort by id, so positions of an id are increasing);
-//  5. tiles of 16 sorted entries: one wave sums each run of equal ids in
+//     with it goes the slot's id and what its tile does at the slot (the run
+//     goes on, or ends there as a head partial, a tail partial or a final
+//     row), so that step 5 gathers rows with no lookups in between;
+//  5. tiles of 16 sorted entries, one wave per tile and 64-lane column slab:
+//     all 16 rows are loaded at once, then each run of equal ids is summed in
 //     order; runs wholly inside a tile are final, the others leave a head or
 //     tail partial;
 //  6. per id: zero if absent; for ids spanning tiles, tail + heads in tile
@@ -104,6 +108,7 @@ struct EmbWs {
   int32_t* start;   // [V + 1]
   int32_t* total;   // [V]
   int32_t* sorted;  // [N]
+  int32_t* skind;   // [N]: id << 2 | what the tile does at the slot (0 go on, 1 head, 2 tail, 3 final row)
   float* head;      // [ntile][C]
   float* tail;      // [ntile][C]
 };
@@ -120,6 +125,7 @@ EmbWs emb_ws_layout(void* base, int64_t N, int V, int C) {
   w.start = reinterpret_cast<int32_t*>(p); p += align256((int64_t)(V + 1) * 4);
   w.total = reinterpret_cast<int32_t*>(p); p += align256((int64_t)V * 4);
   w.sorted = reinterpret_cast<int32_t*>(p); p += align256(N * 4);
+  w.skind = reinterpret_cast<int32_t*>(p); p += align256(N * 4);
   w.head = reinterpret_cast<float*>(p); p += align256(ntile * C * 4);
   w.tail = reinterpret_cast<float*>(p); p += align256(ntile * C * 4);
   return w;
@@ -128,7 +134,7 @@ EmbWs emb_ws_layout(void* base, int64_t N, int V, int C) {
 int64_t emb_ws_bytes(int64_t N, int V, int C) {
   const int64_t nchunk = (N + kEmbChunk - 1) / kEmbChunk;
   const int64_t ntile = (N + kEmbTile - 1) / kEmbTile;
-  return align256(nchunk * V * 4) + 2 * align256(N * 4) + align256((int64_t)(V + 1) * 4) +
+  return align256(nchunk * V * 4) + 3 * align256(N * 4) + align256((int64_t)(V + 1) * 4) +
          align256((int64_t)V * 4) + 2 * align256(ntile * C * 4);
 }
 
@@ -223,79 +229,80 @@ __global__ void emb_scatter_k(const int32_t* __restrict__ tok, int T_, int64_t l
   const int id = tok[(int64_t)(i / T_) * ld + (i % T_)];
   if (id < 0 || id >= V) return;
   const int chunk = i / kEmbChunk;
-  w.sorted[w.start[id] + w.cnt[(int64_t)chunk * V + id] + w.rank[i]] = i;
+  const int rs = w.start[id], re = w.start[id + 1], nvalid = w.start[V];
+  const int j = rs + w.cnt[(int64_t)chunk * V + id] + w.rank[i];
+  w.sorted[j] = i;
+  // the slot's tile [ts, te): does the run end here, and where does its sum go
+  const int ts = j / kEmbTile * kEmbTile, te = min(nvalid, ts + kEmbTile);
+  const bool last = j == re - 1 || j == te - 1;
+  const int kind = !last ? 0 : rs < ts ? 1 : re > te ? 2 : 3;
+  w.skind[j] = (id << 2) | kind;
 }
 
-// One wave per tile of kEmbTile sorted entries; lane owns VEC-column groups.
+// One wave per (tile of kEmbTile sorted entries, slab of 64 VEC columns):
+// the tile's slot records are uniform loads, its 16 rows are loaded at once,
+// then runs are summed in order and stored where the slot record says.
 template <typename T, int VEC>
-__global__ __launch_bounds__(256) void emb_tile_sum_k(const int32_t* __restrict__ tok, int T_, int64_t ld,
-                                                      const T* __restrict__ dx, float* __restrict__ dwte,
-                                                      int N, int V_, int C, EmbWs w, GradW gw, Drop drop) {
+__global__ __launch_bounds__(256) void emb_tile_sum_k(const T* __restrict__ dx, float* __restrict__ dwte, int N,
+                                                      int V_, int C, int nslab, EmbWs w, GradW gw, Drop drop) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int tile = blockIdx.x * 4 + wave;
+  const int item = blockIdx.x * 4 + wave;
+  const int tile = item / nslab, slab = item % nslab;
   const int s = tile * kEmbTile;
   const int nvalid = min(N, w.start[V_]);  // ids outside [0, V) are not sorted
   if (s >= nvalid) return;
   const int e = min(nvalid, s + kEmbTile);
-  int pos[kEmbTile], ids[kEmbTile];
+  const int c0 = (slab * kWave + lane) * VEC;
+  const int32_t* __restrict__ srt = w.sorted;
+  const int32_t* __restrict__ skd = w.skind;
+  int pos[kEmbTile], sk[kEmbTile];
 #pragma unroll
   for (int k = 0; k < kEmbTile; ++k) {
-    pos[k] = s + k < e ? w.sorted[s + k] : 0;
-    ids[k] = s + k < e ? tok[(int64_t)(pos[k] / T_) * ld + (pos[k] % T_)] : -1;
+    pos[k] = s + k < e ? srt[s + k] : 0;
+    sk[k] = s + k < e ? skd[s + k] : 0;
   }
-  // where each run ends and where its sum goes, read up front for every
-  // entry (inside the column loop these reads would wait one by one)
-  int kind[kEmbTile];  // 0: the run goes on; 1: head partial; 2: tail partial; 3: final row
+  if (c0 >= C) return;
+  using P = Pack<T, VEC>;
+  P fr[kEmbTile];
+#pragma unroll
+  for (int k = 0; k < kEmbTile; ++k)
+    if (s + k < e) fr[k] = *reinterpret_cast<const P*>(dx + (int64_t)pos[k] * C + c0);
+  float acc[VEC];
+#pragma unroll
+  for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
 #pragma unroll
   for (int k = 0; k < kEmbTile; ++k) {
-    const bool last = (k == kEmbTile - 1) || (s + k + 1 >= e) || (ids[k + 1 < kEmbTile ? k + 1 : k] != ids[k]);
-    int rs = 0, re = 0;
-    if (s + k < e && last) {
-      rs = w.start[ids[k]];
-      re = w.start[ids[k] + 1];
+    if (s + k >= e) continue;
+    float f[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) f[q] = to_f32(fr[k].e[q]);
+    if (drop.on) {  // the embedding output's dropout mask (site 0), regenerated
+      float m[VEC];
+      drop_mults<VEC>(drop, (uint64_t)pos[k] * C + c0, m);
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) f[q] *= m[q];
     }
-    kind[k] = !(s + k < e && last) ? 0 : rs < s ? 1 : re > e ? 2 : 3;
-  }
-  for (int c0 = lane * VEC; c0 < C; c0 += kWave * VEC) {
-    float acc[VEC];
 #pragma unroll
-    for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
-    // rows are loaded 8 at a time before the partials they end are stored (the
-    // stores could alias the rows as far as the compiler knows, which would
-    // otherwise serialise every load)
-    constexpr int KB = 8;
-    float fr[KB][VEC];
+    for (int q = 0; q < VEC; ++q) acc[q] += f[q];
+    const int kind = sk[k] & 3;
+    if (kind != 0) {
+      float* dst;
+      if (kind == 1) dst = w.head + (int64_t)tile * C + c0;       // continues from an earlier tile
+      else if (kind == 2) dst = w.tail + (int64_t)tile * C + c0;  // continues into a later tile
+      else dst = dwte + (int64_t)(sk[k] >> 2) * C + c0;           // complete inside this tile
+      float o[VEC];
 #pragma unroll
-    for (int k = 0; k < kEmbTile; ++k) {
-      if (k % KB == 0) {
-#pragma unroll
-        for (int j = 0; j < KB; ++j)
-          if (s + k + j < e) load_f<T, VEC>(dx + (int64_t)pos[k + j] * C + c0, fr[j]);
+      for (int q = 0; q < VEC; ++q) {
+        o[q] = kind == 3 ? gw.alpha * acc[q] + (gw.accumulate ? dst[q] : 0.f) : acc[q];
+        acc[q] = 0.f;
       }
-      if (s + k < e) {
-        float f[VEC];
+      if constexpr (VEC == 4 || VEC == 8) {
 #pragma unroll
-        for (int q = 0; q < VEC; ++q) f[q] = fr[k % KB][q];
-        if (drop.on) {  // the embedding output's dropout mask (site 0), regenerated
-          float m[VEC];
-          drop_mults<VEC>(drop, (uint64_t)pos[k] * C + c0, m);
+        for (int q = 0; q < VEC; q += 4)
+          *reinterpret_cast<float4*>(dst + q) = make_float4(o[q], o[q + 1], o[q + 2], o[q + 3]);
+      } else {
 #pragma unroll
-          for (int q = 0; q < VEC; ++q) f[q] *= m[q];
-        }
-#pragma unroll
-        for (int q = 0; q < VEC; ++q) acc[q] += f[q];
-        if (kind[k] != 0) {
-          float* dst;
-          const bool final_row = kind[k] == 3;
-          if (kind[k] == 1) dst = w.head + (int64_t)tile * C;       // continues from an earlier tile
-          else if (kind[k] == 2) dst = w.tail + (int64_t)tile * C;  // continues into a later tile
-          else dst = dwte + (int64_t)ids[k] * C;                    // complete inside this tile
-#pragma unroll
-          for (int q = 0; q < VEC; ++q) {
-            dst[c0 + q] = final_row ? gw.alpha * acc[q] + (gw.accumulate ? dst[c0 + q] : 0.f) : acc[q];
-            acc[q] = 0.f;
-          }
-        }
+        for (int q = 0; q < VEC; ++q) dst[q] = o[q];
       }
     }
   }
@@ -1042,10 +1049,15 @@ slt_status launch_embedding_bwd(const int32_t* tok, int B, int T_, int64_t ld, c
   auto go = [&](auto tag) {
     using T = decltype(tag);
     constexpr int VEC = full_vec<T>();
-    if (C % VEC == 0 && aligned(dx, 16))
-      emb_tile_sum_k<T, VEC><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w, gw, drop);
-    else
-      emb_tile_sum_k<T, 1><<<cdiv(ntile, 4), 256, 0, s>>>(tok, T_, ld, (const T*)dx, dwte, N, V, C, w, gw, drop);
+    // float4 stores of the partials and rows need 16-byte aligned rows of
+    // dwte and of the workspace's partials (at 256-byte offsets)
+    if (C % VEC == 0 && aligned(dx, 16) && aligned(dwte, 16) && aligned(ws, 16) && C % 4 == 0) {
+      const int nslab = cdiv(C, kWave * VEC);
+      emb_tile_sum_k<T, VEC><<<cdiv(ntile * nslab, 4), 256, 0, s>>>((const T*)dx, dwte, N, V, C, nslab, w, gw, drop);
+    } else {
+      const int nslab = cdiv(C, kWave);
+      emb_tile_sum_k<T, 1><<<cdiv(ntile * nslab, 4), 256, 0, s>>>((const T*)dx, dwte, N, V, C, nslab, w, gw, drop);
+    }
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
   if (C % 4 == 0 && aligned(dwte, 16) && aligned(ws, 16))  // the partials sit at 256-byte offsets in ws
