@@ -896,17 +896,6 @@ __device__ __forceinline__ void fl_issue8(const bf16* g, int64_t ld, int row0, i
 // ---------------------------------------------------------------------------
 // dK, dV over 256-key chunks.  One 8-wave workgroup per (key chunk, KV head,
 // batch), chunks with the most queries first; wave w owns the key subtiles
-// u = w and w + 8 (16 keys each) of the chunk, their rotated keys, values and
-// dK / dV accumulators held in registers.  Query tiles of 64 rows of every
-// query head of the group stream through a three-stage LDS ring ([Q hi | Q lo
-// | dO | lse, D] per stage); each 32-query half is read from LDS once per
-// wave and applied to both subtiles: S = Q K^T (hi/lo), P = exp2(S - lse),
-// dP = dO V^T, dS = P (dP - D), then dV^T += dO^T P (P as hi/lo) and
-// dK^T += Q^T dS (hi/lo).  Needs T % 4 == 0 (16-byte lse / D rows).
-
-// ---------------------------------------------------------------------------
-// dK, dV over 256-key chunks.  One 8-wave workgroup per (key chunk, KV head,
-// batch), chunks with the most queries first; wave w owns the key subtiles
 // u = w and w + 8 (16 keys each) of the chunk, their keys, values and
 // dK / dV accumulators held in registers.  Query tiles of 64 rows of every
 // query head of the group stream through a three-stage LDS ring ([Q | dO |
