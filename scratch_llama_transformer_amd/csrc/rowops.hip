@@ -769,6 +769,83 @@ __global__ __launch_bounds__(256) void xent_rows_k(T* z, int64_t ldz, const int3
   }
 }
 
+// The same row operation for bf16 rows of at most NIT x 2048 logits, the row
+// held in registers as loaded (NIT 16-byte groups per thread): one read of
+// the logits from HBM instead of two (measured: the two-pass form ran at
+// 3.9 TB/s of algorithmic bytes on 51200-wide rows).  Max over the row,
+// the sum of exp(z - max), then dz = exp(z - max) / sum - onehot, all over
+// 1 / rows.  The bf16 -> fp32 widening is an asm statement at each use so
+// that the widened row is never kept in registers (it would not fit).
+__device__ __forceinline__ float bf_lo(uint32_t u) {
+  float f;
+  asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(f) : "v"(u));
+  return f;
+}
+__device__ __forceinline__ float bf_hi(uint32_t u) {
+  float f;
+  asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(f) : "v"(u));
+  return f;
+}
+
+template <int NIT>
+__global__ __launch_bounds__(256) void xent_rows_reg_k(bf16* z, int64_t ldz, const int32_t* __restrict__ tok, int T_,
+                                                       int64_t ld, int V, int rows, float* __restrict__ rowloss,
+                                                       float* lse_out) {
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ float sm[4], ss[4];
+  const int row = blockIdx.x;
+  bf16* zr = z + (int64_t)row * ldz;
+  const int y = tok[(int64_t)(row / T_) * ld + (row % T_) + 1];
+  const int t = threadIdx.x, wave = t / kWave, lane = t % kWave;
+  u32x4_t x[NIT];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int c = (t + 256 * k) * 8;
+    x[k] = c < V ? *reinterpret_cast<const u32x4_t*>(zr + c) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NIT; ++k)
+    if ((t + 256 * k) * 8 < V)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) m = fmaxf(m, fmaxf(bf_lo(x[k][q]), bf_hi(x[k][q])));
+  m = wave_max(m);
+  if (lane == 0) sm[wave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NIT; ++k)
+    if ((t + 256 * k) * 8 < V)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += __expf(bf_lo(x[k][q]) - M) + __expf(bf_hi(x[k][q]) - M);
+  s = wave_sum(s);
+  if (lane == 0) ss[wave] = s;
+  __syncthreads();
+  const float S = (ss[0] + ss[1]) + (ss[2] + ss[3]);
+  const float lse = M + logf(S);
+  const float inv_rows = 1.0f / (float)rows, scale = inv_rows / S;
+  if (t == 0) {
+    rowloss[row] = (y >= 0 && y < V) ? lse - to_f32(zr[y]) : __builtin_nanf("");
+    if (lse_out) lse_out[row] = lse;
+  }
+  __syncthreads();  // the target logit is read before its row is overwritten
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int c = (t + 256 * k) * 8;
+    if (c < V) {
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = __expf(bf_lo(x[k][q]) - M) * scale;
+        f[2 * q + 1] = __expf(bf_hi(x[k][q]) - M) * scale;
+      }
+      if (y >= c && y < c + 8) f[y - c] -= inv_rows;
+      store_f<bf16, 8>(zr + c, f);
+    }
+  }
+}
+
 __global__ __launch_bounds__(1024) void xent_mean_k(const float* __restrict__ rowloss, int rows,
                                                     float* __restrict__ loss) {
   __shared__ float part[1024];
@@ -1309,7 +1386,20 @@ slt_status launch_softmax_xent(void* z, int64_t ldz, const int32_t* tok, int B, 
   auto go = [&](auto tag) {
     using T = decltype(tag);
     constexpr int FV = full_vec<T>();
-    if (V % FV == 0 && ldz % FV == 0 && aligned(z, 16))
+    const bool vec = V % FV == 0 && ldz % FV == 0 && aligned(z, 16);
+    if constexpr (sizeof(T) == 2) {
+      const int nit = cdiv(V, 2048);  // 16-byte groups per thread
+      auto reg = [&](auto n) {
+        xent_rows_reg_k<decltype(n)::value><<<rows, 256, 0, s>>>((bf16*)z, ldz, tok, T_, ld, V, rows, rowloss, lse);
+      };
+      // register footprint follows the row length (occupancy 8 .. 2)
+      if (vec && nit > 2 && nit <= 8) return reg(std::integral_constant<int, 8>{});
+      if (vec && nit > 8 && nit <= 16) return reg(std::integral_constant<int, 16>{});
+      if (vec && nit > 16 && nit <= 20) return reg(std::integral_constant<int, 20>{});
+      if (vec && nit > 20 && nit <= 26) return reg(std::integral_constant<int, 26>{});
+      if (vec && nit > 26 && nit <= 32) return reg(std::integral_constant<int, 32>{});
+    }
+    if (vec)
       xent_rows_k<T, FV><<<rows, 256, 0, s>>>((T*)z, ldz, tok, T_, ld, V, rows, rowloss, lse);
     else
       xent_rows_k<T, 1><<<rows, 256, 0, s>>>((T*)z, ldz, tok, T_, ld, V, rows, rowloss, lse);

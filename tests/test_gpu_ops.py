@@ -582,7 +582,8 @@ def test_swiglu_and_gelu(B, dtype, rows, F):
 # Cross-entropy
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", [F32, BF16])
-@pytest.mark.parametrize("Bn,T,V", [(1, 16, 27), (4, 33, 500), (8, 256, 4096), (2, 32, 51200)])
+@pytest.mark.parametrize("Bn,T,V", [(1, 16, 27), (4, 33, 500), (8, 256, 4096), (3, 7, 6152), (2, 16, 32000),
+                                    (2, 32, 51200), (1, 5, 65536)])
 def test_softmax_xent(B, dtype, Bn, T, V):
     say("xent", Bn, T, V, dtype)
     rng = np.random.default_rng(10)
