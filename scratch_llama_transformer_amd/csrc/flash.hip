@@ -979,6 +979,59 @@ __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
       rd_rows4(base + FTB + off.row[0] + 4096 * hf, base + FTB + off.row[1] + 4096 * hf, gr);
       u32x4 pb[2], db[2];
       bool act[2];
+      if (qh0 >= k0 + 16 * (wave + 8) + 15 && qh0 + 31 < T) {
+        // Every query of the half comes after every key of both subtiles and
+        // before T: no mask and both subtiles active, so their steps run
+        // side by side (all products, then all probabilities and score
+        // gradients).  Same arithmetic as the general path below.
+        f32x4 st[2][2], dp[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            st[i][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[i][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              st[i][tt] = mma(qf[tt][s], kf[i][s], st[i][tt]);
+              dp[i][tt] = mma(gr[tt][s], vf[i][s], dp[i][tt]);
+            }
+          }
+        float l2[2][4], dn[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const float4 l4 = *reinterpret_cast<const float4*>(lsd + 32 * hf + 16 * tt + 4 * g);
+          const float4 d4 = *reinterpret_cast<const float4*>(lsd + 64 + 32 * hf + 16 * tt + 4 * g);
+          l2[tt][0] = l4.x * kLog2e; l2[tt][1] = l4.y * kLog2e; l2[tt][2] = l4.z * kLog2e; l2[tt][3] = l4.w * kLog2e;
+          dn[tt][0] = d4.x; dn[tt][1] = d4.y; dn[tt][2] = d4.z; dn[tt][3] = d4.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int ki = k0 + 16 * (wave + 8 * i) + li;
+          float p[2][4], ds[2][4];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[tt][r] = ex2(fmaf(st[i][tt][r], c2, -l2[tt][r]));
+            if (DROP) {
+              float dm[4];
+              drop_mults_strided<4>(a.drop, att_elem(b, a.H, kvh * G + n / per, T, qh0 + 16 * tt + 4 * g, ki),
+                                    (uint64_t)T, dm);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                ds[tt][r] = p[tt][r] * (dm[r] * dp[i][tt][r] - dn[tt][r]);
+                p[tt][r] *= dm[r];
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) ds[tt][r] = p[tt][r] * (dp[i][tt][r] - dn[tt][r]);
+            }
+          }
+          pb[i] = pack_k(p[0], p[1]);
+          db[i] = pack_k(ds[0], ds[1]);
+          act[i] = true;
+        }
+      } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int kf0 = k0 + 16 * (wave + 8 * i);  // first key of subtile i
@@ -1026,6 +1079,7 @@ __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
         }
         pb[i] = pack_k(p[0], p[1]);
         db[i] = pack_k(ds[0], ds[1]);
+      }
       }
       {
         u32x4 gt[4];
