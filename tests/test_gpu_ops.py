@@ -172,6 +172,29 @@ def test_gemm_dw_group(B):
         B.slt_gemm_dw_group([(12, 12, A, 12, A, 12, C, 12, 1.0, 0)], 32)
 
 
+def test_gemm_dw_group_full_size(B):
+    """A layer's weight gradients at the d=1024 parallel-block workload's full
+    size, as the step launches them: dW of [q|k|v|fc_in] (7168 x 1024) and of
+    [W_o|W_fc2] (1024 x 5120) over K = 16384 tokens in one grouped launch on
+    256 x 256 tiles (whole K per block); sampled rows against the oracle's
+    products."""
+    rng = np.random.default_rng(9)
+    K = 16384
+    items, refs = [], []
+    for (M, N) in [(7168, 1024), (1024, 5120)]:
+        say("gemm group full size", M, N, K)
+        A = rnd(rng, (K, M), BF16)
+        Bm = rnd(rng, (K, N), BF16)
+        C = torch.full((M, N), float("nan"), device="cuda")
+        rows = np.unique(rng.integers(0, M, 40))
+        items.append((M, N, dev(A, BF16), M, dev(Bm, BF16), N, C, N, 1.0, 0))
+        refs.append((rows, A[:, rows].T @ Bm))
+        del A, Bm
+    B.slt_gemm_dw_group(items, K)
+    for it, (rows, ref) in zip(items, refs):
+        check(host(it[6])[rows], ref, "bf16", f"group product {it[0]}x{it[1]} K={K}")
+
+
 def test_gemm_zero_k_gives_residual_or_zero(B):
     rng = np.random.default_rng(2)
     gemm_case(B, rng, 17, 9, 0, 1, 1, F32, F32)
@@ -187,6 +210,13 @@ def test_gemm_zero_k_gives_residual_or_zero(B):
     (4096, 384, 16384, 0, 0, BF16, F32, False, True),       # dW of lm_head
     (16384, 1364, 256, 1, 1, F32, F32, False, False),       # fp32 [W1;W3], ragged N
     (256, 682, 16384, 0, 0, F32, F32, False, True),         # fp32 dW of W2, ragged
+    # the d=1024 parallel-block workload's products on the 256 x 256 kernel
+    # (staged epilogue): [q|k|v|fc_in], [W_o|W_fc2] with the residual, and
+    # the dX of both (n-major weights)
+    (16384, 7168, 1024, 1, 1, BF16, BF16, False, False),
+    (16384, 1024, 5120, 1, 1, BF16, BF16, True, False),
+    (16384, 5120, 1024, 1, 0, BF16, BF16, False, False),
+    (16384, 1024, 7168, 1, 0, BF16, BF16, False, False),
 ])
 def test_gemm_full_size_sampled_rows(B, shape):
     rng = np.random.default_rng(3)
