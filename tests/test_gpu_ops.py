@@ -166,6 +166,24 @@ def test_gemm_dw_group(B):
         B.slt_gemm_dw_group(items, K)
         for it, ref in zip(items, refs):
             check(host(it[6]), ref, "bf16", f"group product {it[0]}x{it[1]} K={K}")
+    # a layer's weight gradients at the d=384 workload over 16384 tokens with a
+    # workspace (K split over the 128 x 128 tiles, partials added in split
+    # order), one product scaled and one accumulating; sampled rows
+    say("gemm group, d=384 layer, K split")
+    K = 16384
+    items, refs = [], []
+    for i, (M, N) in enumerate([(1152, 384), (384, 384), (2048, 384), (384, 1024)]):
+        A = rnd(rng, (K, M), BF16)
+        Bm = rnd(rng, (K, N), BF16)
+        old = rng.standard_normal((M, N)).astype(np.float32)
+        C = torch.from_numpy(old).cuda()
+        rows = np.unique(rng.integers(0, M, 24))
+        items.append((M, N, dev(A, BF16), M, dev(Bm, BF16), N, C, N, 0.5 if i == 1 else 1.0, i == 3))
+        refs.append((rows, (0.5 if i == 1 else 1.0) * (A[:, rows].T @ Bm) + (old[rows] if i == 3 else 0.0)))
+    W = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    B.slt_gemm_dw_group(items, K, W, W.numel())
+    for it, (rows, ref) in zip(items, refs):
+        check(host(it[6])[rows], ref, "bf16", f"group product {it[0]}x{it[1]} K={K}")
     A = torch.zeros(32, 12, dtype=torch.bfloat16, device="cuda")
     C = torch.zeros(12, 12, device="cuda")
     with pytest.raises(B.SltError):  # M and N not multiples of 8
