@@ -1128,7 +1128,6 @@ __global__ __launch_bounds__(W8_NT, 1) void gemm_w8_k(KArgs a) {
 // columns; it loses on the m/n-major layouts and, as a 256 x 128 tile, on the
 // wider forward projections, where it is not used.
 // ---------------------------------------------------------------------------
-constexpr int D64_TILE = 128 * 64;  // elements per 128-row operand tile (16 KiB)
 
 __device__ __forceinline__ int d64_swz(int r) { return 2 * ((r >> 1) & 3); }
 
@@ -1157,19 +1156,32 @@ __device__ __forceinline__ void d64_read(unsigned pa, unsigned pb, u32x4 (&af)[4
   asm volatile(D64_KM4(a) D64_KM4(b) "s_waitcnt lgkmcnt(0)"
                : D64_OUT_KM4(a, af), D64_OUT_KM4(b, bf) : [ap] "v"(pa), [bp] "v"(pb) : "memory");
 }
+// Fragments 0..3 of A and 0..2 of B (the 64 x 192 tile's waves).
+__device__ __forceinline__ void d64_read43(unsigned pa, unsigned pb, u32x4 (&af)[4], u32x4 (&bf)[3]) {
+  asm volatile(D64_KM4(a) D64_R128(b, 0, 0) D64_R128(b, 1, 2048) D64_R128(b, 2, 4096) "s_waitcnt lgkmcnt(0)"
+               : D64_OUT_KM4(a, af), D64_OKM(b, 0, bf), D64_OKM(b, 1, bf), D64_OKM(b, 2, bf)
+               : [ap] "v"(pa), [bp] "v"(pb)
+               : "memory");
+}
 #undef D64_R128
 #undef D64_KM4
 #undef D64_OKM
 #undef D64_OUT_KM4
 
-template <typename TO, bool SPLIT, bool RP = false>
+// LAY 0: 128 x 128 block tile, 2 x 2 waves of 64 x 64.  LAY 1: 64 x 192,
+// 1 x 4 waves of 64 x 48 (4 x 3 MFMA tiles): a 16384 x 384 output is 512
+// such tiles, one full round of two blocks per CU, where 384 square tiles
+// leave a quarter of the block slots idle.
+template <typename TO, bool SPLIT, bool RP = false, int LAY = 0>
 __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
-  constexpr int FM = 4;
-  __shared__ __attribute__((aligned(16))) bf16 A0[D64_TILE], A1[D64_TILE];
-  __shared__ __attribute__((aligned(16))) bf16 B0[D64_TILE], B1[D64_TILE];
+  constexpr int FM = 4, FN = LAY ? 3 : 4;
+  constexpr int TBM = LAY ? 64 : 128, TBN = LAY ? 192 : 128;
+  constexpr int FA = TBM / 32, FB = TBN / 32;  // copies per lane of an A and a B tile
+  __shared__ __attribute__((aligned(16))) bf16 A0[TBM * 64], A1[TBM * 64];
+  __shared__ __attribute__((aligned(16))) bf16 B0[TBN * 64], B1[TBN * 64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = LAY ? 0 : wave >> 1, wn = LAY ? wave : wave & 1;
   int tile = blockIdx.x;
   if (SLT_GEMM_XCD) {
     const int q = a.tiles >> 3, r = a.tiles & 7, x = tile & 7;
@@ -1178,7 +1190,7 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
   const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
   const bf16* A = static_cast<const bf16*>(a.A);
   const bf16* B = static_cast<const bf16*>(a.B);
-  const int m0 = tm * 32 * FM, n0 = tn * 128;
+  const int m0 = tm * TBM, n0 = tn * TBN;
   const int kbeg = SPLIT ? blockIdx.z * a.kchunk : 0;
   const int nk = (min(a.K, kbeg + a.kchunk) - kbeg) / 64;
   // lane (g, i) reads row i of a fragment, k chunk 4 s + g of half s
@@ -1187,46 +1199,66 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     ra[s] = (wm * 16 * FM + i) * 128 + ((4 * s + g) ^ d64_swz(i)) * 16;
-    rb[s] = (wn * 64 + i) * 128 + ((4 * s + g) ^ d64_swz(i)) * 16;
+    rb[s] = (wn * 16 * FN + i) * 128 + ((4 * s + g) ^ d64_swz(i)) * 16;
   }
 
-  f32x4 acc[FM][4];
+  f32x4 acc[FM][FN];
 #pragma unroll
   for (int x = 0; x < FM; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int y = 0; y < FN; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int brow[4] = {0, 0, 0, 0};  // B rows this lane copies under the RoPE epilogue's row map
+  int brow[FB];  // B rows this lane copies under the RoPE epilogue's row map
+#pragma unroll
+  for (int i = 0; i < FB; ++i) brow[i] = 0;
   if constexpr (RP) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) brow[i] = rope_row(a.rope, min(n0 + (((wave * 4 + i) * 64 + lane) >> 3), a.N - 1));
+    for (int i = 0; i < FB; ++i) brow[i] = rope_row(a.rope, min(n0 + (((wave * FB + i) * 64 + lane) >> 3), a.N - 1));
   }
-  d64_issue<FM>(A, a.lda, a.M, m0, kbeg, A0, wave, lane);
-  d64_issue<4, RP>(B, a.ldb, a.N, n0, kbeg, B0, wave, lane, brow);
+  d64_issue<FA>(A, a.lda, a.M, m0, kbeg, A0, wave, lane);
+  d64_issue<FB, RP>(B, a.ldb, a.N, n0, kbeg, B0, wave, lane, brow);
   for (int it = 0; it < nk; ++it) {
     SLT_WAIT_VMCNT(0);  // this wave's copies of tile it have landed
     lds_barrier();      // ... everyone's have, and the other stage is free
     if (it + 1 < nk) {
       const int kn = kbeg + (it + 1) * 64;
-      d64_issue<FM>(A, a.lda, a.M, m0, kn, (it & 1) ? A0 : A1, wave, lane);
-      d64_issue<4, RP>(B, a.ldb, a.N, n0, kn, (it & 1) ? B0 : B1, wave, lane, brow);
+      d64_issue<FA>(A, a.lda, a.M, m0, kn, (it & 1) ? A0 : A1, wave, lane);
+      d64_issue<FB, RP>(B, a.ldb, a.N, n0, kn, (it & 1) ? B0 : B1, wave, lane, brow);
     }
     const unsigned as = lds_off((it & 1) ? A1 : A0), bs = lds_off((it & 1) ? B1 : B0);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      u32x4 af[FM], bfr[4];
-      d64_read(as + ra[s], bs + rb[s], af, bfr);
+      u32x4 af[FM], bfr[FN];
+      if constexpr (FN == 4) d64_read(as + ra[s], bs + rb[s], af, bfr);
+      else d64_read43(as + ra[s], bs + rb[s], af, bfr);
 #pragma unroll
       for (int x = 0; x < FM; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
+        for (int y = 0; y < FN; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[y]),
                                                               __builtin_bit_cast(bf16x8_t, af[x]), acc[x][y], 0, 0, 0);
     }
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
-  if constexpr (RP) rope_rotate_acc<FM, 4>(a, acc, m0, n0, wm, wn, lane);
-  dl_epilogue<TO, SPLIT, FM, 4, RP>(a, acc, m0, n0, wm, wn, lane);
+  if constexpr (RP) rope_rotate_acc<FM, FN>(a, acc, m0, n0, wm, wn, lane);
+  dl_epilogue<TO, SPLIT, FM, FN, RP>(a, acc, m0, n0, wm, wn, lane);
+}
+
+#ifndef SLT_D64_NARROW
+#define SLT_D64_NARROW 1  // the 64-deep kernel's 64 x 192 layout where it fills the chip better
+#endif
+// Layout of the 64-deep kernel for an M x N output: the 64 x 192 tile when N
+// is a multiple of 192 and its estimated time is lower.  The estimate is
+// tile area x tiles, counted as at least one full round of 512 blocks (two
+// per CU), times 7/6 for the narrow tile (its k-steps stage 256 rows for
+// 3/4 of the MFMA work of a 128 x 128 tile; measured: 16384 x 384 outputs
+// are 13% faster as 512 narrow tiles than as 384 square ones, 16384 x 1152
+// outputs 10% slower as 1536 narrow tiles than as 1152 square ones).
+inline bool d64_narrow(int M, int N) {
+  if (!SLT_D64_NARROW || N % 192 != 0) return false;
+  const int64_t t0 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t t1 = (int64_t)((M + 63) / 64) * (N / 192);
+  return std::max<int64_t>(t1, 512) * (64 * 192) * 7 < std::max<int64_t>(t0, 512) * (128 * 128) * 6;
 }
 
 // ---------------------------------------------------------------------------
@@ -1558,8 +1590,15 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
         grid = dim3(ka.tiles, 1, 1);
       }
       if (SLT_GEMM_D64 && g.a_kmajor && g.b_kmajor && fm == 4 && fn == 4 && g.K % 64 == 0 && ka.kchunk % 64 == 0) {
-        if (split) gemm_d64_k<float, true><<<grid, NT, 0, s>>>(ka);
-        else gemm_d64_k<TO, false><<<grid, NT, 0, s>>>(ka);
+        if (split) {
+          gemm_d64_k<float, true><<<grid, NT, 0, s>>>(ka);
+        } else if (d64_narrow(g.M, g.N)) {
+          ka.tiles_n = g.N / 192;
+          ka.tiles = ((g.M + 63) / 64) * ka.tiles_n;
+          gemm_d64_k<TO, false, false, 1><<<ka.tiles, NT, 0, s>>>(ka);
+        } else {
+          gemm_d64_k<TO, false><<<grid, NT, 0, s>>>(ka);
+        }
       } else if (g.a_kmajor && g.b_kmajor) {
         if (fm == 8) SLT_DL_GO(true, true, 8, 4);
         else if (fn == 8) SLT_DL_GO(true, true, 4, 8);
@@ -1636,6 +1675,12 @@ slt_status launch_gemm_rope(const GemmArgs& g, const RopeEpi& r, hipStream_t s) 
   if (SLT_GEMM_BIG) {
     if (g.M >= g.N && ntiles(256, 128) >= 768) fm = 8;
     else if (ntiles(128, 256) >= 768) fn = 8;
+  }
+  if (fm == 4 && fn == 4 && SLT_GEMM_D64 && g.K % 64 == 0 && d64_narrow(g.M, g.N)) {
+    ka.tiles_n = g.N / 192;
+    ka.tiles = ((g.M + 63) / 64) * ka.tiles_n;
+    gemm_d64_k<bf16, false, true, 1><<<ka.tiles, NT, 0, s>>>(ka);
+    return check_launch("gemm with RoPE epilogue");
   }
   ka.tiles_n = (g.N + 32 * fn - 1) / (32 * fn);
   ka.tiles = ((g.M + 32 * fm - 1) / (32 * fm)) * ka.tiles_n;

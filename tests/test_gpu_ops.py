@@ -114,6 +114,18 @@ def test_gemm_direct_lds_path(B, a_k, b_k, outd):
     gemm_case(B, rng, 264, 136, 4096, a_k, b_k, BF16, outd, ws=True, resid=True)
 
 
+@pytest.mark.parametrize("outd", [BF16, F32])
+def test_gemm_narrow_64x192_tiles(B, outd):
+    # k-major bf16 products whose N is a multiple of 192 and whose 64 x 192
+    # tiles fill their rounds of blocks better than 128 x 128 tiles take the
+    # 64 x 192 layout of the 64-deep kernel: ragged M, N of 1..6 tile
+    # columns, 1..6 k-steps, residual
+    rng = np.random.default_rng(15)
+    for (M, N, K) in [(40, 192, 64), (200, 384, 128), (1000, 576, 384), (63, 1152, 192), (130, 960, 320)]:
+        gemm_case(B, rng, M, N, K, 1, 1, BF16, outd)
+        gemm_case(B, rng, M, N, K, 1, 1, BF16, outd, resid=True)
+
+
 @pytest.mark.parametrize("a_k,b_k,M,N", [(1, 1, 12296, 4000), (1, 1, 4000, 12296), (1, 0, 12296, 4000),
                                          (1, 1, 65560, 296), (1, 0, 65560, 296)])
 def test_gemm_big_tiles(B, a_k, b_k, M, N):
@@ -247,6 +259,8 @@ def test_gemm_full_size_sampled_rows(B, shape):
     (16384, 1024, 16, 4, 64, 64, "half", 0, 1024, BF16),     # GQA workload's QKV: 256 x 128 tiles
     (16384, 2048, 16, 16, 64, 32, "pairs", 4096, 1024, BF16),  # parallel block's [q|k|v|fc_in]: 256 x 256 tiles
     (200, 100, 4, 2, 32, 16, "half", 40, 64, BF16),          # ragged M and N: 128 x 128 tiles with edge blocks
+    (200, 100, 4, 2, 32, 16, "half", 128, 64, BF16),         # N = 384, ragged M: 64 x 192 tiles
+    (136, 64, 2, 1, 128, 128, "half", 64, 128, BF16),        # d = 128: a 192-column tile starts inside a head
     (96, 48, 2, 2, 16, 6, "pairs", 0, 32, BF16),             # R % 4 != 0: the product, then RoPE in place
     (130, 65, 4, 4, 16, 16, "half", 0, 40, F32),             # fp32: the product, then RoPE in place
 ])
