@@ -891,7 +891,7 @@ constexpr int W8_SMEM = W8_SW_BYTES > W8_HALF_BYTES ? W8_SW_BYTES : W8_HALF_BYTE
 static_assert(W8_SMEM >= W8_RING_BYTES, "staging area covers the ring");
 
 // Eight consecutive outputs at (m, n): alpha v, dropout, residual, one rounding.
-template <typename TO>
+template <typename TO, bool NTS = SLT_NT_STORE>
 __device__ __forceinline__ void w8_store8(const KArgs& a, int m, int n, const float (&vin)[8], bool vec) {
   float v[8];
 #pragma unroll
@@ -919,11 +919,8 @@ __device__ __forceinline__ void w8_store8(const KArgs& a, int m, int n, const fl
       Pk<TO, 8> pk;
 #pragma unroll
       for (int r = 0; r < 8; ++r) pk.e[r] = from_f32<TO>(v[r]);
-#if SLT_NT_STORE
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, pk), reinterpret_cast<u32x4*>(dst));
-#else
-      *reinterpret_cast<Pk<TO, 8>*>(dst) = pk;
-#endif
+      if constexpr (NTS) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, pk), reinterpret_cast<u32x4*>(dst));
+      else *reinterpret_cast<Pk<TO, 8>*>(dst) = pk;
     } else {
       const float lo[4] = {v[0], v[1], v[2], v[3]}, hi[4] = {v[4], v[5], v[6], v[7]};
       store4<TO>(dst, lo);
@@ -1168,17 +1165,86 @@ __device__ __forceinline__ void d64_read43(unsigned pa, unsigned pb, u32x4 (&af)
 #undef D64_OKM
 #undef D64_OUT_KM4
 
+#ifndef SLT_D64_STAGED
+#define SLT_D64_STAGED 1  // LDS-staged epilogue in the 64-deep kernel
+#endif
+#ifndef SLT_D64_NT
+#define SLT_D64_NT 0  // ... with non-temporal stores
+#endif
+
+// Staged epilogue of the 64-deep kernel: in passes of 64 rows (two for the
+// 128 x 128 tile, one for 64 x 192) the waves holding those rows write their
+// fp32 accumulators into LDS (rotated RoPE pairs at their output columns:
+// taken for rotate-half only when the head dim divides the tile width, so
+// that every head lies inside one tile), then all 256 threads store 8
+// consecutive columns at a time, each 64-thread wave covering whole rows.
+// Same arithmetic as the direct stores: alpha, dropout and the residual are
+// applied to the fp32 value before its one rounding.
+template <typename TO, int LAY, bool RP>
+__device__ __forceinline__ void d64_epilogue_staged(const KArgs& a, const f32x4 (&acc)[4][LAY ? 3 : 4], int m0,
+                                                    int n0, int wm, int wn, int lane, float* F) {
+  constexpr int FN = LAY ? 3 : 4, TBN = LAY ? 192 : 128, CS = TBN + 4, PASSES = LAY ? 1 : 2;
+  const bool vec = a.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(a.C) % (8 * sizeof(TO))) == 0 &&
+                   (a.R == nullptr ||
+                    (a.ldr % 8 == 0 && (reinterpret_cast<uintptr_t>(a.R) % (8 * sizeof(TO))) == 0));
+  for (int h = 0; h < PASSES; ++h) {
+    __syncthreads();  // the ring (first pass) or the previous pass's rows are no longer read
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = i * 16 + (lane & 15);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int cl = wn * 16 * FN + j * 16 + 4 * (lane >> 4);
+          const f32x4 v = acc[i][j];
+          if constexpr (RP) {
+            const int n = n0 + cl, c = n % a.rope.d;
+            if (a.rope.half && n < a.rope.end && c < a.rope.R) {
+              const int lo = n - c + (c >> 1) - n0, hi = lo + (a.rope.R >> 1);
+              F[rl * CS + lo] = v[0];
+              F[rl * CS + lo + 1] = v[2];
+              F[rl * CS + hi] = v[1];
+              F[rl * CS + hi + 1] = v[3];
+              continue;
+            }
+          }
+          *reinterpret_cast<float4*>(F + rl * CS + cl) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 64 * TBN / 8 / NT; ++k) {
+      const int idx = threadIdx.x + NT * k;
+      const int rl = idx / (TBN / 8), cl = (idx % (TBN / 8)) * 8;
+      const int m = m0 + h * 64 + rl, n = n0 + cl;
+      if (m >= a.M || n >= a.N) continue;
+      const float4 x0 = *reinterpret_cast<const float4*>(F + rl * CS + cl);
+      const float4 x1 = *reinterpret_cast<const float4*>(F + rl * CS + cl + 4);
+      const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      w8_store8<TO, SLT_D64_NT>(a, m, n, v, vec);
+    }
+  }
+}
+
 // LAY 0: 128 x 128 block tile, 2 x 2 waves of 64 x 64.  LAY 1: 64 x 192,
 // 1 x 4 waves of 64 x 48 (4 x 3 MFMA tiles): a 16384 x 384 output is 512
 // such tiles, one full round of two blocks per CU, where 384 square tiles
 // leave a quarter of the block slots idle.
-template <typename TO, bool SPLIT, bool RP = false, int LAY = 0>
+// ST: the staged epilogue (d64_epilogue_staged), else dl_epilogue's direct
+// stores (split-K partials always take those).
+template <typename TO, bool SPLIT, bool RP = false, int LAY = 0, bool ST = false>
 __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
   constexpr int FM = 4, FN = LAY ? 3 : 4;
   constexpr int TBM = LAY ? 64 : 128, TBN = LAY ? 192 : 128;
   constexpr int FA = TBM / 32, FB = TBN / 32;  // copies per lane of an A and a B tile
-  __shared__ __attribute__((aligned(16))) bf16 A0[TBM * 64], A1[TBM * 64];
-  __shared__ __attribute__((aligned(16))) bf16 B0[TBN * 64], B1[TBN * 64];
+  // the two stages of A and B (64 KiB), overlaid by the staged epilogue's rows
+  static_assert(64 * (TBN + 4) * 4 <= 2 * (TBM + TBN) * 64 * 2, "staged rows fit in the ring");
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (TBM + TBN) * 64];
+  bf16* const A0 = smem;
+  bf16* const A1 = A0 + TBM * 64;
+  bf16* const B0 = A1 + TBM * 64;
+  bf16* const B1 = B0 + TBN * 64;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = LAY ? 0 : wave >> 1, wn = LAY ? wave : wave & 1;
@@ -1241,9 +1307,13 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
   if constexpr (RP) rope_rotate_acc<FM, FN>(a, acc, m0, n0, wm, wn, lane);
-  dl_epilogue<TO, SPLIT, FM, FN, RP>(a, acc, m0, n0, wm, wn, lane);
+  if constexpr (ST && !SPLIT) d64_epilogue_staged<TO, LAY, RP>(a, acc, m0, n0, wm, wn, lane, reinterpret_cast<float*>(smem));
+  else dl_epilogue<TO, SPLIT, FM, FN, RP>(a, acc, m0, n0, wm, wn, lane);
 }
 
+#ifndef SLT_D64_ROPE192
+#define SLT_D64_ROPE192 1  // RoPE projections whose rotate-half heads fit 192-wide tiles only: 64 x 192 tiles
+#endif
 #ifndef SLT_D64_NARROW
 #define SLT_D64_NARROW 1  // the 64-deep kernel's 64 x 192 layout where it fills the chip better
 #endif
@@ -1595,9 +1665,9 @@ slt_status run(const GemmArgs& g, hipStream_t s) {
         } else if (d64_narrow(g.M, g.N)) {
           ka.tiles_n = g.N / 192;
           ka.tiles = ((g.M + 63) / 64) * ka.tiles_n;
-          gemm_d64_k<TO, false, false, 1><<<ka.tiles, NT, 0, s>>>(ka);
+          gemm_d64_k<TO, false, false, 1, SLT_D64_STAGED><<<ka.tiles, NT, 0, s>>>(ka);
         } else {
-          gemm_d64_k<TO, false><<<grid, NT, 0, s>>>(ka);
+          gemm_d64_k<TO, false, false, 0, SLT_D64_STAGED><<<grid, NT, 0, s>>>(ka);
         }
       } else if (g.a_kmajor && g.b_kmajor) {
         if (fm == 8) SLT_DL_GO(true, true, 8, 4);
@@ -1676,10 +1746,16 @@ slt_status launch_gemm_rope(const GemmArgs& g, const RopeEpi& r, hipStream_t s) 
     if (g.M >= g.N && ntiles(256, 128) >= 768) fm = 8;
     else if (ntiles(128, 256) >= 768) fn = 8;
   }
-  if (fm == 4 && fn == 4 && SLT_GEMM_D64 && g.K % 64 == 0 && d64_narrow(g.M, g.N)) {
+  // the staged epilogue keeps each rotated head inside its tile: for
+  // rotate-half, the head dim must divide the tile width
+  const bool st128 = SLT_D64_STAGED && (!r.half || 128 % r.d == 0);
+  const bool st192 = SLT_D64_STAGED && (!r.half || 192 % r.d == 0);
+  if (fm == 4 && fn == 4 && SLT_GEMM_D64 && g.K % 64 == 0 &&
+      (d64_narrow(g.M, g.N) || (SLT_D64_ROPE192 && g.N % 192 == 0 && st192 && !st128))) {
     ka.tiles_n = g.N / 192;
     ka.tiles = ((g.M + 63) / 64) * ka.tiles_n;
-    gemm_d64_k<bf16, false, true, 1><<<ka.tiles, NT, 0, s>>>(ka);
+    if (st192) gemm_d64_k<bf16, false, true, 1, true><<<ka.tiles, NT, 0, s>>>(ka);
+    else gemm_d64_k<bf16, false, true, 1, false><<<ka.tiles, NT, 0, s>>>(ka);
     return check_launch("gemm with RoPE epilogue");
   }
   ka.tiles_n = (g.N + 32 * fn - 1) / (32 * fn);
@@ -1687,7 +1763,8 @@ slt_status launch_gemm_rope(const GemmArgs& g, const RopeEpi& r, hipStream_t s) 
   const dim3 grid(ka.tiles, 1, 1);
   if (fm == 8) gemm_dl_k<bf16, true, true, false, 8, 4, true><<<grid, NT, 0, s>>>(ka);
   else if (fn == 8) gemm_dl_k<bf16, true, true, false, 4, 8, true><<<grid, NT, 0, s>>>(ka);
-  else if (SLT_GEMM_D64 && g.K % 64 == 0) gemm_d64_k<bf16, false, true><<<grid, NT, 0, s>>>(ka);
+  else if (SLT_GEMM_D64 && g.K % 64 == 0 && st128) gemm_d64_k<bf16, false, true, 0, true><<<grid, NT, 0, s>>>(ka);
+  else if (SLT_GEMM_D64 && g.K % 64 == 0) gemm_d64_k<bf16, false, true, 0, false><<<grid, NT, 0, s>>>(ka);
   else gemm_dl_k<bf16, true, true, false, 4, 4, true><<<grid, NT, 0, s>>>(ka);
   return check_launch("gemm with RoPE epilogue");
 }

@@ -255,7 +255,7 @@ def test_gemm_full_size_sampled_rows(B, shape):
 
 
 @pytest.mark.parametrize("M,T,H,Hkv,d,R,mode,extra,K,dtype", [
-    (16384, 256, 8, 8, 48, 48, "half", 0, 384, BF16),        # d=384 workload's QKV: 128 x 128 64-deep tiles
+    (16384, 256, 8, 8, 48, 48, "half", 0, 384, BF16),        # d=384 workload's QKV: 64 x 192 tiles, staged epilogue
     (16384, 1024, 16, 4, 64, 64, "half", 0, 1024, BF16),     # GQA workload's QKV: 256 x 128 tiles
     (16384, 2048, 16, 16, 64, 32, "pairs", 4096, 1024, BF16),  # parallel block's [q|k|v|fc_in]: 256 x 256 tiles
     (200, 100, 4, 2, 32, 16, "half", 40, 64, BF16),          # ragged M and N: 128 x 128 tiles with edge blocks
