@@ -239,6 +239,20 @@ __device__ __forceinline__ void rd_chalf(unsigned base, const FlOff& o, u32x4 (&
   rd_chalf_t<ND>(base + o.col[0], base + o.col[1], base + o.col[2], base + o.col[3], f);
 }
 
+// The log-sum-exp and D values of a lane's query rows in a 32-query half,
+// from the stage's [lse | D] rows at byte address a (the half's first row
+// plus the lane's 4 g): v[0], v[1] = lse of rows +0..3 and +16..19, v[2],
+// v[3] = D of the same rows.  One asm block that waits for its own reads: a
+// plain load would make the compiler first wait for every copy in flight
+// into the ring, the next two steps' tiles included.
+__device__ __forceinline__ void rd_lsd(unsigned a, u32x4 (&v)[4]) {
+  asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:64\n\t"
+               "ds_read_b128 %2, %4 offset:256\n\tds_read_b128 %3, %4 offset:320\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+               : "v"(a)
+               : "memory");
+}
+
 // Four probabilities (or gradients) of two neighbouring 16-row results in
 // the k order the transposed reads use, rounded to bf16.
 __device__ __forceinline__ u32x4 pack_k(const float (&x)[4], const float (&y)[4]) {
@@ -969,7 +983,7 @@ __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
     const int q0 = qt * FR;
     char* stg = lds + (n % 3) * STB;
     const unsigned base = lds_off(stg);
-    const float* lsd = reinterpret_cast<const float*>(stg + 2 * FTB);
+    const unsigned lsd = base + 2 * FTB;  // the stage's lse row (64 floats), then D
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int qh0 = q0 + 32 * hf;  // first query of this half
@@ -998,13 +1012,15 @@ __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
             }
           }
         float l2[2][4], dn[2][4];
+        u32x4 ld4[4];
+        rd_lsd(lsd + 4 * (32 * hf + 4 * g), ld4);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const float4 l4 = *reinterpret_cast<const float4*>(lsd + 32 * hf + 16 * tt + 4 * g);
-          const float4 d4 = *reinterpret_cast<const float4*>(lsd + 64 + 32 * hf + 16 * tt + 4 * g);
-          l2[tt][0] = l4.x * kLog2e; l2[tt][1] = l4.y * kLog2e; l2[tt][2] = l4.z * kLog2e; l2[tt][3] = l4.w * kLog2e;
-          dn[tt][0] = d4.x; dn[tt][1] = d4.y; dn[tt][2] = d4.z; dn[tt][3] = d4.w;
-        }
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            l2[tt][r] = __uint_as_float(ld4[tt][r]) * kLog2e;
+            dn[tt][r] = __uint_as_float(ld4[2 + tt][r]);
+          }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int ki = k0 + 16 * (wave + 8 * i) + li;
@@ -1032,6 +1048,8 @@ __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
           act[i] = true;
         }
       } else {
+      u32x4 ld4[4];
+      rd_lsd(lsd + 4 * (32 * hf + 4 * g), ld4);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int kf0 = k0 + 16 * (wave + 8 * i);  // first key of subtile i
@@ -1048,14 +1066,11 @@ __global__ __launch_bounds__(512, 1) void fl_dkdv2_k(FlArgs a) {
             st = mma(qf[tt][s], kf[i][s], st);
             dp = mma(gr[tt][s], vf[i][s], dp);
           }
-          // lse (to base 2) and D of the lane's 4 query rows, read where used
-          const float4 l4 = *reinterpret_cast<const float4*>(lsd + 32 * hf + 16 * tt + 4 * g);
-          const float4 d4 = *reinterpret_cast<const float4*>(lsd + 64 + 32 * hf + 16 * tt + 4 * g);
-          p[tt][0] = ex2(fmaf(st[0], c2, -l4.x * kLog2e));
-          p[tt][1] = ex2(fmaf(st[1], c2, -l4.y * kLog2e));
-          p[tt][2] = ex2(fmaf(st[2], c2, -l4.z * kLog2e));
-          p[tt][3] = ex2(fmaf(st[3], c2, -l4.w * kLog2e));
-          const float dn[4] = {d4.x, d4.y, d4.z, d4.w};
+          // lse (to base 2) and D of the lane's 4 query rows
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[tt][r] = ex2(fmaf(st[r], c2, -__uint_as_float(ld4[tt][r]) * kLog2e));
+          const float dn[4] = {__uint_as_float(ld4[2 + tt][0]), __uint_as_float(ld4[2 + tt][1]),
+                               __uint_as_float(ld4[2 + tt][2]), __uint_as_float(ld4[2 + tt][3])};
           if (qh0 < kf0 + 15 || qh0 + 31 >= T) {  // the diagonal, or rows past T
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
