@@ -563,13 +563,6 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
   // partials of norm k (0: final norm, 2 l + 1: the layer's second, 2 l + 2:
   // its first) and their column sums, on the second stream when there is one
   auto nws = [&](int k) { return static_cast<char*>(x.S(p.normws)) + k * p.normws_each; };
-  auto norm_sums = [&](int k, float* dg, float* db) -> slt_status {
-    if (!aux) return SLT_OK;  // the norm launch summed them itself
-    SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
-    SLT_TRY(hip_ok(hipStreamWaitEvent(aux->s, aux->ready, 0), "backward: stream wait"));
-    return launch_norm_colsum(nws(k), N, C, dg, db, aux->s, x.gw);
-  };
-  const bool defer = aux != nullptr;
   // AdamW over parameters [off, end) on stream s (ranges start on 4-element
   // boundaries, or one update of the whole buffer runs at the end)
   bool ranges_ok = opt != nullptr && p.lp[0].norm1 % 4 == 0 && p.normf % 4 == 0;
@@ -580,6 +573,37 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
                         opt->m + off, opt->v + off, opt->t, opt->lr, opt->b1, opt->b2, opt->eps, opt->wd,
                         opt->mask ? opt->mask + off : nullptr, nullptr, s);
   };
+  // Second-stream work that only waits for the walk up to some point (a
+  // norm's column sums of its partials, a layer's AdamW update once all its
+  // gradients are final) is queued here and enqueued, in order, behind the
+  // next weight-gradient launch, so that one event per layer hands the
+  // second stream everything the walk has finished (each record costs the
+  // walk's stream an idle gap of a few microseconds).
+  struct SideTask {
+    int k;  // >= 0: column sums of norm k into dg (and db); -1: AdamW over [off, end)
+    float *dg, *db;
+    int64_t off, end;
+  };
+  SideTask side_q[8];
+  int side_n = 0;
+  auto run_side = [&](const SideTask& t) -> slt_status {
+    if (t.k >= 0) return launch_norm_colsum(nws(t.k), N, C, t.dg, t.db, xw.s, x.gw);
+    return adam(t.off, t.end, xw.s);
+  };
+  auto side = [&](const SideTask& t) -> slt_status {
+    if (!aux) return t.k >= 0 ? SLT_OK : run_side(t);  // one stream: the norm launch summed its partials itself
+    if (side_n == 8) return fail(SLT_EINVAL, "backward: second-stream queue full");
+    side_q[side_n++] = t;
+    return SLT_OK;
+  };
+  auto drain_side = [&]() -> slt_status {
+    for (int i = 0; i < side_n; ++i) SLT_TRY(run_side(side_q[i]));
+    side_n = 0;
+    return SLT_OK;
+  };
+  auto norm_sums = [&](int k, float* dg, float* db) -> slt_status { return side(SideTask{k, dg, db, 0, 0}); };
+  auto side_adam = [&](int64_t off, int64_t end) -> slt_status { return side(SideTask{-1, nullptr, nullptr, off, end}); };
+  const bool defer = aux != nullptr;
   auto launch_dw = [&](int k) -> slt_status {
     if (aux) {
       SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
@@ -590,7 +614,7 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(hip_ok(hipEventRecord(aux->done[k], aux->s), "backward: event record"));
       pending[k] = true;
     }
-    return SLT_OK;
+    return drain_side();
   };
 
   // the token sort of the embedding gradient (tokens only) runs on the second
@@ -669,13 +693,13 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(launch_attention_bwd(at, x.s));
       dws.add(N, p.qkv_w, C, dqkv, p.qkv_w, x.A(A.n1), C, grads + W.qkvw, C);
       SLT_TRY(launch_dw(sl));
-      if (l == c.L - 1) SLT_TRY(adam(p.normf, p.n_params, xw.s));  // final norm and lm_head are final
+      if (l == c.L - 1) SLT_TRY(side_adam(p.normf, p.n_params));  // final norm and lm_head are final
       SLT_TRY(proj_dx(x, N, p.qkv_w, C, dqkv, p.qkv_w, x.P(W.qkvw), C, dn, C));
       SLT_TRY(wait_set(si));
       SLT_TRY(launch_rmsnorm_bwd(x.A(p.xs[2 * l]), x.P(W.norm1), (const float*)x.A(A.r1), dn, dx2, dxi,
                                  grads + W.norm1, N, C, x.dt, nws(2 * l + 2), x.s, x.gw, defer));
       SLT_TRY(norm_sums(2 * l + 2, grads + W.norm1, nullptr));
-      SLT_TRY(adam(W.norm1, l + 1 < c.L ? p.lp[l + 1].norm1 : p.normf, xw.s));  // the layer's gradients are final
+      SLT_TRY(side_adam(W.norm1, l + 1 < c.L ? p.lp[l + 1].norm1 : p.normf));  // the layer's gradients are final
     } else {
       char* ou = (char*)x.A(A.o);
       // x_out = x_in + drop([o | u] W_out^T)
@@ -697,15 +721,20 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       SLT_TRY(launch_attention_bwd(at, x.s));
       dws.add(N, p.in_w, C, dbig, p.in_w, x.A(A.n1), C, grads + W.qkvw, C);
       SLT_TRY(launch_dw(sl));
-      if (l == c.L - 1) SLT_TRY(adam(p.normf, p.n_params, xw.s));  // final norm and lm_head are final
+      if (l == c.L - 1) SLT_TRY(side_adam(p.normf, p.n_params));  // final norm and lm_head are final
       SLT_TRY(proj_dx(x, N, p.in_w, C, dbig, p.in_w, x.P(W.qkvw), C, dn, C));
       SLT_TRY(wait_set(si));
       SLT_TRY(launch_layernorm_bwd(x.A(p.xs[l]), x.P(W.norm1), (const float*)x.A(A.mu1), (const float*)x.A(A.r1),
                                    dn, dx, dxi, grads + W.norm1, grads + W.norm1b, N, C, x.dt, nws(2 * l + 2), x.s,
                                    x.gw, defer));
       SLT_TRY(norm_sums(2 * l + 2, grads + W.norm1, grads + W.norm1b));
-      SLT_TRY(adam(W.norm1, l + 1 < c.L ? p.lp[l + 1].norm1 : p.normf, xw.s));  // the layer's gradients are final
+      SLT_TRY(side_adam(W.norm1, l + 1 < c.L ? p.lp[l + 1].norm1 : p.normf));  // the layer's gradients are final
     }
+  }
+  if (aux && side_n > 0) {  // the first layer's norm sums and update
+    SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
+    SLT_TRY(hip_ok(hipStreamWaitEvent(aux->s, aux->ready, 0), "backward: stream wait"));
+    SLT_TRY(drain_side());
   }
   if (sort_ahead) SLT_TRY(hip_ok(hipStreamWaitEvent(x.s, aux->sort_done, 0), "backward: stream wait"));
   SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, x.S(p.dx[2]), grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s,
