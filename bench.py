@@ -238,7 +238,7 @@ def machine_bounds(torch):
     dst = torch.empty_like(src)
     s = torch.cuda.current_stream()
     best, best_v = None, 0
-    for v in range(4):
+    for v in range(5):
         for _ in range(4):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
@@ -270,7 +270,7 @@ def machine_bounds(torch):
             "mfma_loop_tflops": {"16x16x32 x8": round(rates[0], 1), "32x32x16 x8": round(rates[1], 1),
                                  "16x16x32 x16": round(rates[2], 1)},
             "copy_kernel": f"slt_stream_copy variant {best_v} (16-byte loads and stores, 2 GiB each way; best of "
-                           "4 launch shapes x 4)",
+                           "5 launch shapes x 4)",
             "mfma_kernel": "slt_mfma_loop (independent MFMA chains per wave, 32 waves per CU; best variant)"}
 
 

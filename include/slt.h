@@ -505,8 +505,8 @@ slt_status slt_softmax_xent_noalloc(void* z, int64_t ldz, const int32_t* tokens,
  * streaming kernel reaches on this GPU.  variant selects the launch shape
  * (0: 4 words per thread per iteration on 8192 blocks; 1: 8 words on 4096
  * blocks; 2: one pass over the buffer, 4 words per thread; these three with
- * non-temporal loads and stores; 3: as 2 with ordinary ones); the best of
- * them is the measured bound.  SLT_EINVAL for another variant, a size that
+ * non-temporal loads and stores; 3: as 2 with ordinary ones; 4: as 2 with
+ * 1024-thread workgroups); the best of them is the measured bound.  SLT_EINVAL for another variant, a size that
  * is not a multiple of 16 or a NULL / misaligned pointer. */
 slt_status slt_stream_copy(const void* src, void* dst, int64_t bytes, int32_t variant, void* stream);
 

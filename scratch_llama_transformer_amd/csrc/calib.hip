@@ -18,8 +18,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // whole KiB), grid-stride.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-template <int U, bool NT = true>
-__global__ __launch_bounds__(256) void stream_copy_k(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+template <int U, bool NT = true, int NTH = 256>
+__global__ __launch_bounds__(NTH) void stream_copy_k(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                      int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -89,7 +89,7 @@ extern "C" {
 
 slt_status slt_stream_copy(const void* src, void* dst, int64_t bytes, int32_t variant, void* stream) {
   if (bytes < 0 || bytes % 16) return fail(SLT_EINVAL, "stream_copy: bytes must be a non-negative multiple of 16");
-  if (variant < 0 || variant > 3) return fail(SLT_EINVAL, "stream_copy: variant must be 0, 1, 2 or 3");
+  if (variant < 0 || variant > 4) return fail(SLT_EINVAL, "stream_copy: variant must be 0, 1, 2, 3 or 4");
   if (bytes == 0) return SLT_OK;
   if (!src || !dst || reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16)
     return fail(SLT_EINVAL, "stream_copy: NULL or misaligned buffer");
@@ -99,12 +99,14 @@ slt_status slt_stream_copy(const void* src, void* dst, int64_t bytes, int32_t va
   hipStream_t st = as_stream(stream);
   // variant 0: 4 words per thread per iteration on 8192 blocks; 1: 8 words on
   // 4096 blocks; 2: one pass, 4 words per thread, as many blocks as that
-  // needs; 3: as 2 with ordinary (cached) loads and stores
+  // needs; 3: as 2 with ordinary (cached) loads and stores; 4: as 2 with
+  // 1024-thread blocks (a quarter of the workgroups to dispatch)
   const int one_pass = (int)std::min<int64_t>((n + 1023) / 1024, 1 << 20);
   if (variant == 0) stream_copy_k<4><<<(int)std::min<int64_t>((n + 1023) / 1024, 8192), 256, 0, st>>>(s, d, n);
   else if (variant == 1) stream_copy_k<8><<<(int)std::min<int64_t>((n + 2047) / 2048, 4096), 256, 0, st>>>(s, d, n);
   else if (variant == 2) stream_copy_k<4><<<one_pass, 256, 0, st>>>(s, d, n);
-  else stream_copy_k<4, false><<<one_pass, 256, 0, st>>>(s, d, n);
+  else if (variant == 3) stream_copy_k<4, false><<<one_pass, 256, 0, st>>>(s, d, n);
+  else stream_copy_k<4, true, 1024><<<(int)std::min<int64_t>((n + 4095) / 4096, 1 << 20), 1024, 0, st>>>(s, d, n);
   return check_launch("stream_copy");
 }
 

@@ -42,6 +42,42 @@ __device__ __forceinline__ void store_f(T* p, const float (&f)[VEC]) {
   *reinterpret_cast<Pack<T, VEC>*>(p) = pk;
 }
 
+// Streaming (non-temporal) forms, for operands read or written once per step
+// that no later kernel of the step reads soon: the lines are not kept in the
+// caches, which measured on gfx950 raises a read stream from 6.3 to 7.1 TB/s
+// and a copy from 5.5 to 5.8 TB/s (2 GiB buffers).
+typedef unsigned ew_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned ew_u32x2 __attribute__((ext_vector_type(2)));
+template <typename W> __device__ __forceinline__ W ld_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const W*>(p));
+}
+template <typename W> __device__ __forceinline__ void st_nt(void* p, W w) {
+  __builtin_nontemporal_store(w, reinterpret_cast<W*>(p));
+}
+template <typename T, int VEC>
+__device__ __forceinline__ Pack<T, VEC> ld_pack_nt(const T* p) {
+  constexpr int B = VEC * (int)sizeof(T);
+  if constexpr (B == 16) return __builtin_bit_cast(Pack<T, VEC>, ld_nt<ew_u32x4>(p));
+  else if constexpr (B == 8) return __builtin_bit_cast(Pack<T, VEC>, ld_nt<ew_u32x2>(p));
+  else if constexpr (B == 4) return __builtin_bit_cast(Pack<T, VEC>, ld_nt<unsigned>(p));
+  else return *reinterpret_cast<const Pack<T, VEC>*>(p);
+}
+template <typename T, int VEC>
+__device__ __forceinline__ void load_f_nt(const T* p, float (&f)[VEC]) {
+  const Pack<T, VEC> pk = ld_pack_nt<T, VEC>(p);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) f[i] = to_f32(pk.e[i]);
+}
+__device__ __forceinline__ float4 ld_f4_nt(const float* p) {
+  return __builtin_bit_cast(float4, ld_nt<ew_u32x4>(p));
+}
+__device__ __forceinline__ void st_f4_nt(float* p, float4 v) { st_nt<ew_u32x4>(p, __builtin_bit_cast(ew_u32x4, v)); }
+
+#ifndef SLT_EW_THREADS
+#define SLT_EW_THREADS 256  // block size of the streaming element kernels (1024 measured: faster alone, slower in the step)
+#endif
+constexpr int kEw = SLT_EW_THREADS;
+
 
 inline bool aligned(const void* p, int bytes) {
   return p == nullptr || (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
@@ -483,12 +519,12 @@ __global__ __launch_bounds__(256) void layernorm_fwd_k(const T* __restrict__ x, 
   }
 }
 
-// Norm backward.  Block b (4 waves) handles rows b*4 + wave + k*gridDim*4 and
-// leaves per-column partial sums of dy*xh (and dy for LayerNorm) in
+// Norm backward.  Block b (NWV waves) handles rows b*NWV + wave + k*gridDim*NWV
+// and leaves per-column partial sums of dy*xh (and dy for LayerNorm) in
 // part[b][C] (and part[nb + b][C]); norm_colsum_k adds the partials in block
 // order.
-template <typename T, int VEC, int NCH, bool LN>
-__global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const T* __restrict__ g,
+template <typename T, int VEC, int NCH, bool LN, int NWV>
+__global__ __launch_bounds__(64 * NWV) void norm_bwd_k(const T* __restrict__ x, const T* __restrict__ g,
                                                   const float* __restrict__ mean, const float* __restrict__ rstd,
                                                   const T* __restrict__ dy, const T* dres, T* dx,
                                                   float* __restrict__ part, int rows, int C) {
@@ -513,8 +549,8 @@ __global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const
   // wave visits rows blockIdx*4 + wave + m*step in increasing m whatever RP is,
   // so the partial sums do not depend on it.
   constexpr int RP = NCH >= 4 ? 1 : 4 / NCH;
-  const int step = gridDim.x * 4;
-  for (int row0 = blockIdx.x * 4 + wave; row0 < rows; row0 += RP * step) {
+  const int step = gridDim.x * NWV;
+  for (int row0 = blockIdx.x * NWV + wave; row0 < rows; row0 += RP * step) {
     P xr[RP][NCH], dr[RP][NCH], rr[RP][NCH];
     float r[RP], mu[RP];
 #pragma unroll
@@ -575,9 +611,9 @@ __global__ __launch_bounds__(256) void norm_bwd_k(const T* __restrict__ x, const
       }
     }
   }
-  // Combine the 4 waves' column partials in wave order, then write this
+  // Combine the waves' column partials in wave order, then write this
   // block's partial row.
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NWV; ++w) {
     if (wave == w) {
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
@@ -625,13 +661,17 @@ __global__ __launch_bounds__(1024) void norm_colsum_k(const float* __restrict__ 
 #define SLT_NORM_BLOCKS 512
 #endif
 constexpr int kNormBwdBlocks = SLT_NORM_BLOCKS;
+#ifndef SLT_NORM_BWD_WAVES
+#define SLT_NORM_BWD_WAVES 4  // waves per block of the norm backward
+#endif
+constexpr int kNormBwdWaves = SLT_NORM_BWD_WAVES;
 
 // ---------------------------------------------------------------------------
 // SwiGLU and GELU on [rows, F] with row strides.
 // ---------------------------------------------------------------------------
 
 template <typename T, int VEC>
-__global__ __launch_bounds__(256) void swiglu_fwd_k(const T* __restrict__ a, const T* __restrict__ b,
+__global__ __launch_bounds__(kEw) void swiglu_fwd_k(const T* __restrict__ a, const T* __restrict__ b,
                                                     T* __restrict__ h, int rows, int F, int64_t lda,
                                                     int64_t ldb, int64_t ldh) {
   const int fv = F / VEC;
@@ -650,7 +690,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd_k(const T* __restrict__ a, con
 }
 
 template <typename T, int VEC>
-__global__ __launch_bounds__(256) void swiglu_bwd_k(const T* __restrict__ a, const T* __restrict__ b,
+__global__ __launch_bounds__(kEw) void swiglu_bwd_k(const T* __restrict__ a, const T* __restrict__ b,
                                                     const T* __restrict__ dh, T* __restrict__ da,
                                                     T* __restrict__ db, int rows, int F, int64_t lda,
                                                     int64_t ldb, int64_t lddh, int64_t ldda, int64_t lddb) {
@@ -661,8 +701,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_k(const T* __restrict__ a, con
     const int64_t r = idx / fv;
     const int c = (int)(idx % fv) * VEC;
     float av[VEC], bv[VEC], hv[VEC], oa[VEC], ob[VEC];
-    load_f<T, VEC>(a + r * lda + c, av);
-    load_f<T, VEC>(b + r * ldb + c, bv);
+    load_f_nt<T, VEC>(a + r * lda + c, av);
+    load_f_nt<T, VEC>(b + r * ldb + c, bv);
     load_f<T, VEC>(dh + r * lddh + c, hv);
 #pragma unroll
     for (int q = 0; q < VEC; ++q) swiglu_grad(av[q], bv[q], hv[q], oa[q], ob[q]);
@@ -673,7 +713,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_k(const T* __restrict__ a, con
 
 
 template <typename T, int VEC>
-__global__ __launch_bounds__(256) void gelu_fwd_k(const T* __restrict__ a, T* __restrict__ u, int rows, int F,
+__global__ __launch_bounds__(kEw) void gelu_fwd_k(const T* __restrict__ a, T* __restrict__ u, int rows, int F,
                                                   int64_t lda, int64_t ldu) {
   const int fv = F / VEC;
   const int64_t total = (int64_t)rows * fv;
@@ -690,7 +730,7 @@ __global__ __launch_bounds__(256) void gelu_fwd_k(const T* __restrict__ a, T* __
 }
 
 template <typename T, int VEC>
-__global__ __launch_bounds__(256) void gelu_bwd_k(const T* __restrict__ a, const T* __restrict__ du,
+__global__ __launch_bounds__(kEw) void gelu_bwd_k(const T* __restrict__ a, const T* __restrict__ du,
                                                   T* __restrict__ da, int rows, int F, int64_t lda,
                                                   int64_t lddu, int64_t ldda) {
   const int fv = F / VEC;
@@ -700,7 +740,7 @@ __global__ __launch_bounds__(256) void gelu_bwd_k(const T* __restrict__ a, const
     const int64_t r = idx / fv;
     const int c = (int)(idx % fv) * VEC;
     float av[VEC], gv[VEC], out[VEC];
-    load_f<T, VEC>(a + r * lda + c, av);
+    load_f_nt<T, VEC>(a + r * lda + c, av);
     load_f<T, VEC>(du + r * lddu + c, gv);
 #pragma unroll
     for (int q = 0; q < VEC; ++q) {
@@ -873,7 +913,7 @@ __device__ __forceinline__ void adamw_one(float& th, float g, float& m, float& v
   th = th - lr * (mh / (sqrtf(vh) + eps) + wd * th);
 }
 
-__global__ __launch_bounds__(256) void adamw_k(int64_t n, float* __restrict__ th, uint16_t* __restrict__ shadow,
+__global__ __launch_bounds__(kEw) void adamw_k(int64_t n, float* __restrict__ th, uint16_t* __restrict__ shadow,
                                                const float* __restrict__ g, float* __restrict__ m,
                                                float* __restrict__ v, float b1, float b2, float ib1, float ib2,
                                                float lr, float eps, float wd, const uint8_t* __restrict__ mask,
@@ -881,28 +921,27 @@ __global__ __launch_bounds__(256) void adamw_k(int64_t n, float* __restrict__ th
   const float gs = gscale ? *gscale : 1.0f;  // gradient clipping factor (1: none)
   const int64_t n4 = n / 4;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    float4 t4 = reinterpret_cast<float4*>(th)[i];
-    float4 g4 = reinterpret_cast<const float4*>(g)[i];
+    float4 t4 = ld_f4_nt(th + 4 * i);
+    float4 g4 = ld_f4_nt(g + 4 * i);
     g4.x *= gs; g4.y *= gs; g4.z *= gs; g4.w *= gs;
-    float4 m4 = reinterpret_cast<float4*>(m)[i];
-    float4 v4 = reinterpret_cast<float4*>(v)[i];
+    float4 m4 = ld_f4_nt(m + 4 * i);
+    float4 v4 = ld_f4_nt(v + 4 * i);
     float w[4] = {wd, wd, wd, wd};
     if (mask) {
-      const uchar4 k = reinterpret_cast<const uchar4*>(mask)[i];
+      const uchar4 k = __builtin_bit_cast(uchar4, ld_nt<unsigned>(mask + 4 * i));
       w[0] = k.x ? wd : 0.f; w[1] = k.y ? wd : 0.f; w[2] = k.z ? wd : 0.f; w[3] = k.w ? wd : 0.f;
     }
     adamw_one(t4.x, g4.x, m4.x, v4.x, b1, b2, ib1, ib2, lr, eps, w[0]);
     adamw_one(t4.y, g4.y, m4.y, v4.y, b1, b2, ib1, ib2, lr, eps, w[1]);
     adamw_one(t4.z, g4.z, m4.z, v4.z, b1, b2, ib1, ib2, lr, eps, w[2]);
     adamw_one(t4.w, g4.w, m4.w, v4.w, b1, b2, ib1, ib2, lr, eps, w[3]);
-    reinterpret_cast<float4*>(th)[i] = t4;
-    reinterpret_cast<float4*>(m)[i] = m4;
-    reinterpret_cast<float4*>(v)[i] = v4;
+    st_f4_nt(th + 4 * i, t4);
+    st_f4_nt(m + 4 * i, m4);
+    st_f4_nt(v + 4 * i, v4);
     if (shadow) {
-      ushort4 s4;
-      s4.x = f32_to_bf16_bits(t4.x); s4.y = f32_to_bf16_bits(t4.y);
-      s4.z = f32_to_bf16_bits(t4.z); s4.w = f32_to_bf16_bits(t4.w);
-      reinterpret_cast<ushort4*>(shadow)[i] = s4;
+      const ew_u32x2 s2 = {(unsigned)f32_to_bf16_bits(t4.x) | ((unsigned)f32_to_bf16_bits(t4.y) << 16),
+                           (unsigned)f32_to_bf16_bits(t4.z) | ((unsigned)f32_to_bf16_bits(t4.w) << 16)};
+      st_nt<ew_u32x2>(shadow + 4 * i, s2);
     }
   }
   // tail elements
@@ -930,7 +969,7 @@ __global__ __launch_bounds__(256) void gnorm_partial_k(int64_t n, const float* _
   const int64_t n4 = n / 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const float4 x = reinterpret_cast<const float4*>(g)[i];
+    const float4 x = ld_f4_nt(g + 4 * i);
     if (LINF) {
       acc = fmax(acc, (double)fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
     } else {
@@ -1226,13 +1265,14 @@ slt_status launch_layernorm_fwd(const void* x, const void* gm, const void* bt, v
   return dtype == SLT_BF16 ? go(bf16{}) : go(float{});
 }
 
-int64_t norm_bwd_ws(int rows, int C) {
-  const int nb = std::min(kNormBwdBlocks, cdiv(rows, 4));
-  return (int64_t)2 * nb * C * 4;
-}
+// Blocks of the norm backward for `rows` rows: one partial row of column
+// sums per block (the workspace, the backward and the column sums all use it).
+static int norm_bwd_blocks(int rows) { return std::max(1, std::min(kNormBwdBlocks, cdiv(rows, kNormBwdWaves))); }
+
+int64_t norm_bwd_ws(int rows, int C) { return (int64_t)2 * norm_bwd_blocks(rows) * C * 4; }
 
 slt_status launch_norm_colsum(const void* ws, int rows, int C, float* dg, float* db, hipStream_t s, GradW gw) {
-  const int nb = std::max(1, std::min(kNormBwdBlocks, cdiv(rows, 4)));
+  const int nb = norm_bwd_blocks(rows);
   const float* part = static_cast<const float*>(ws);
   norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part, nb, C, dg, gw);
   if (db) norm_colsum_k<<<cdiv(C, 32), 1024, 0, s>>>(part + (int64_t)nb * C, nb, C, db, gw);
@@ -1243,14 +1283,14 @@ template <bool LN>
 static slt_status norm_bwd_common(const void* x, const void* g, const float* mean, const float* rstd,
                                   const void* dy, const void* dres, void* dx, float* dg, float* db, int rows,
                                   int C, int dtype, void* ws, hipStream_t s, GradW gw, bool defer_sums) {
-  const int nb = std::max(1, std::min(kNormBwdBlocks, cdiv(rows, 4)));
+  const int nb = norm_bwd_blocks(rows);
   float* part = static_cast<float*>(ws);
   const size_t smem = (size_t)(LN ? 2 : 1) * C * sizeof(float);
   auto go = [&](auto tag) -> slt_status {
     using T = decltype(tag);
     const bool ok = aligned(x, 16) && aligned(g, 16) && aligned(dy, 16) && aligned(dres, 16) && aligned(dx, 16);
     return norm_dispatch<T>(C, ok, [&](auto vec, auto nch) -> slt_status {
-      norm_bwd_k<T, decltype(vec)::value, decltype(nch)::value, LN><<<nb, 256, smem, s>>>(
+      norm_bwd_k<T, decltype(vec)::value, decltype(nch)::value, LN, kNormBwdWaves><<<nb, 64 * kNormBwdWaves, smem, s>>>(
           (const T*)x, (const T*)g, mean, rstd, (const T*)dy, (const T*)dres, (T*)dx, part, rows, C);
       return check_launch("norm_bwd");
     });
@@ -1329,7 +1369,7 @@ slt_status launch_swiglu_fwd(const void* a, const void* b, void* h, int rows, in
     using T = decltype(tag);
     ew_dispatch<T>(ew_vec<T>(F, {lda, ldb, ldh}, {a, b, h}), [&](auto vec) {
       constexpr int V = decltype(vec)::value;
-      swiglu_fwd_k<T, V><<<grid_for((int64_t)rows * F / V), 256, 0, s>>>((const T*)a, (const T*)b, (T*)h, rows, F,
+      swiglu_fwd_k<T, V><<<grid_for((int64_t)rows * F / V, kEw, 1 << 20), kEw, 0, s>>>((const T*)a, (const T*)b, (T*)h, rows, F,
                                                                          lda, ldb, ldh);
     });
   };
@@ -1344,7 +1384,7 @@ slt_status launch_swiglu_bwd(const void* a, const void* b, const void* dh, void*
     using T = decltype(tag);
     ew_dispatch<T>(ew_vec<T>(F, {lda, ldb, lddh, ldda, lddb}, {a, b, dh, da, db}), [&](auto vec) {
       constexpr int V = decltype(vec)::value;
-      swiglu_bwd_k<T, V><<<grid_for((int64_t)rows * F / V), 256, 0, s>>>(
+      swiglu_bwd_k<T, V><<<grid_for((int64_t)rows * F / V, kEw, 1 << 20), kEw, 0, s>>>(
           (const T*)a, (const T*)b, (const T*)dh, (T*)da, (T*)db, rows, F, lda, ldb, lddh, ldda, lddb);
     });
   };
@@ -1358,7 +1398,7 @@ slt_status launch_gelu_fwd(const void* a, void* u, int rows, int F, int64_t lda,
     using T = decltype(tag);
     ew_dispatch<T>(ew_vec<T>(F, {lda, ldu}, {a, u}), [&](auto vec) {
       constexpr int V = decltype(vec)::value;
-      gelu_fwd_k<T, V><<<grid_for((int64_t)rows * F / V), 256, 0, s>>>((const T*)a, (T*)u, rows, F, lda, ldu);
+      gelu_fwd_k<T, V><<<grid_for((int64_t)rows * F / V, kEw, 1 << 20), kEw, 0, s>>>((const T*)a, (T*)u, rows, F, lda, ldu);
     });
   };
   if (dtype == SLT_BF16) go(bf16{}); else go(float{});
@@ -1371,7 +1411,7 @@ slt_status launch_gelu_bwd(const void* a, const void* du, void* da, int rows, in
     using T = decltype(tag);
     ew_dispatch<T>(ew_vec<T>(F, {lda, lddu, ldda}, {a, du, da}), [&](auto vec) {
       constexpr int V = decltype(vec)::value;
-      gelu_bwd_k<T, V><<<grid_for((int64_t)rows * F / V), 256, 0, s>>>((const T*)a, (const T*)du, (T*)da, rows, F,
+      gelu_bwd_k<T, V><<<grid_for((int64_t)rows * F / V, kEw, 1 << 20), kEw, 0, s>>>((const T*)a, (const T*)du, (T*)da, rows, F,
                                                                        lda, lddu, ldda);
     });
   };
@@ -1414,7 +1454,7 @@ slt_status launch_adamw(int64_t n, float* master, uint16_t* shadow, const float*
                         hipStream_t s) {
   const double bc1 = 1.0 - pow((double)b1, (double)t);
   const double bc2 = 1.0 - pow((double)b2, (double)t);
-  adamw_k<<<grid_for(n / 4 + 1, 256, 8192), 256, 0, s>>>(n, master, shadow, g, m, v, b1, b2, (float)(1.0 / bc1),
+  adamw_k<<<grid_for(n / 4 + 1, kEw, 1 << 20), kEw, 0, s>>>(n, master, shadow, g, m, v, b1, b2, (float)(1.0 / bc1),
                                                            (float)(1.0 / bc2), lr, eps, wd, mask, gscale);
   return check_launch("adamw");
 }

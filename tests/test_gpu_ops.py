@@ -764,7 +764,7 @@ def test_model_init_statistics(B):
     assert torch.equal(master, again)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
 def test_stream_copy_and_mfma_loop(B, variant):
     """The machine-bound kernels do the work they are timed for: the copy
     moves every byte (sizes that leave partial iterations and a tail), and
