@@ -601,6 +601,13 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
     side_n = 0;
     return SLT_OK;
   };
+  // hand the queue to the second stream now, behind an event of its own
+  auto flush_side = [&]() -> slt_status {
+    if (!aux || side_n == 0) return SLT_OK;
+    SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
+    SLT_TRY(hip_ok(hipStreamWaitEvent(aux->s, aux->ready, 0), "backward: stream wait"));
+    return drain_side();
+  };
   auto norm_sums = [&](int k, float* dg, float* db) -> slt_status { return side(SideTask{k, dg, db, 0, 0}); };
   auto side_adam = [&](int64_t off, int64_t end) -> slt_status { return side(SideTask{-1, nullptr, nullptr, off, end}); };
   const bool defer = aux != nullptr;
@@ -700,6 +707,9 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
                                  grads + W.norm1, N, C, x.dt, nws(2 * l + 2), x.s, x.gw, defer));
       SLT_TRY(norm_sums(2 * l + 2, grads + W.norm1, nullptr));
       SLT_TRY(side_adam(W.norm1, l + 1 < c.L ? p.lp[l + 1].norm1 : p.normf));  // the layer's gradients are final
+      // the second stream ends the step with the first layer's weight
+      // gradients: give it this layer's queue first, not behind them
+      if (l == 1) SLT_TRY(flush_side());
     } else {
       char* ou = (char*)x.A(A.o);
       // x_out = x_in + drop([o | u] W_out^T)
@@ -729,13 +739,12 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
                                    x.gw, defer));
       SLT_TRY(norm_sums(2 * l + 2, grads + W.norm1, grads + W.norm1b));
       SLT_TRY(side_adam(W.norm1, l + 1 < c.L ? p.lp[l + 1].norm1 : p.normf));  // the layer's gradients are final
+      // the second stream ends the step with the first layer's weight
+      // gradients: give it this layer's queue first, not behind them
+      if (l == 1) SLT_TRY(flush_side());
     }
   }
-  if (aux && side_n > 0) {  // the first layer's norm sums and update
-    SLT_TRY(hip_ok(hipEventRecord(aux->ready, x.s), "backward: event record"));
-    SLT_TRY(hip_ok(hipStreamWaitEvent(aux->s, aux->ready, 0), "backward: stream wait"));
-    SLT_TRY(drain_side());
-  }
+  SLT_TRY(flush_side());  // the first layer's norm sums and update
   if (sort_ahead) SLT_TRY(hip_ok(hipStreamWaitEvent(x.s, aux->sort_done, 0), "backward: stream wait"));
   SLT_TRY(launch_embedding_bwd(tok, c.B, c.T, ldt, x.S(p.dx[2]), grads + p.wte, c.V, C, x.dt, x.S(p.embws), x.s,
                                x.gw, make_drop(c, 0, 0), sort_ahead));
