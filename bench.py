@@ -1,14 +1,16 @@
 #!/usr/bin/env python3
 """Training-step throughput on one MI355X.
 
-One step = slt_forward_loss + slt_backward + slt_adamw_step over one batch of
-synthetic tokens for the Llama-style decoder d=384, 8 layers, 8 heads,
-T=256, B=64, V=4096, SwiGLU 1024 (bf16 activations, fp32 master weights and
-moments), inputs resident in HBM.  Prints one JSON line with tokens/s, a
-per-class kernel breakdown (each class re-launched through the C ABI with the
-step's shapes and timed with HIP events on the current stream, the one the
-library launches on), the roofline position of the dominant class, and the CPU
-oracle timed on a bounded sample of the same workload.
+One step = slt_forward_loss + slt_backward_adamw (the backward with each
+layer's AdamW update folded in) over one batch of synthetic tokens for the
+Llama-style decoder d=384, 8 layers, 8 heads, T=256, B=64, V=4096, SwiGLU 1024
+(bf16 activations, fp32 master weights and moments), inputs resident in HBM.
+Prints one JSON line with tokens/s, a per-class kernel breakdown of the step
+(the library's HIP event brackets around each class's launches, on the stream
+each runs on, over a few steps after the timed ones), the same classes
+re-launched alone through the C ABI for comparison, every HBM-bound kernel in
+GB/s, the roofline position of the dominant class, and the CPU oracle timed on
+a bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -202,6 +204,7 @@ def kernel_classes(w, ts, torch, reps, only=None):
 
 
 TRAIN_BYTES = 1 << 30  # footprint of one timed train of an HBM-bound kernel
+PROF_STEPS = 3  # steps run with the library's per-class launch timing on
 
 
 def time_train(fns, reps, torch):
@@ -517,6 +520,19 @@ def main():
     ms = ev[0].elapsed_time(ev[-1]) / args.steps
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     loss = float(ts.loss.item())
+    # the step's own launches by class: PROF_STEPS more steps with the
+    # library's event brackets on (kept out of the timed steps above: the
+    # events add gaps between launches)
+    in_step = None
+    if not args.no_breakdown:
+        B.slt_timing(True)
+        t0 = time.perf_counter()
+        for _ in range(PROF_STEPS):
+            ts.step(tok)
+        torch.cuda.synchronize()
+        prof_ms = (time.perf_counter() - t0) * 1e3 / PROF_STEPS  # host clock, enqueue to completion
+        B.slt_timing(False)
+        in_step = B.slt_timing_read()
     tps = w.N / (ms / 1e3)
     flops = step_flops(w)
     peak = PEAK["bf16"] if w.act == "bf16" else PEAK["f32"]
@@ -548,15 +564,28 @@ def main():
     if not args.no_breakdown:
         machine = machine_bounds(torch)
         out["machine"] = machine
-        cl = kernel_classes(w, None, torch, args.kernel_reps)
+        sa = kernel_classes(w, None, torch, args.kernel_reps)
         mpeak = machine["mfma_bf16_tflops"] if w.act == "bf16" else None
-        for v in cl.values():
-            if mpeak:
-                v["frac_of_measured"] = v["tflops"] / mpeak
+        # in the step: each class's bracketed launches over the profiling
+        # steps, with the same algorithmic FLOPs and bytes per step
+        cl = {}
+        for k, v in sa.items():
+            ms_tot, n = in_step[k]
+            msps = ms_tot / PROF_STEPS
+            cl[k] = dict(v, ms_per_step=msps, launches=n // PROF_STEPS, avg_launch_us=ms_tot * 1e3 / max(n, 1),
+                         tflops=v["flops"] / (msps / 1e3) / 1e12,
+                         frac_of_peak=v["flops"] / (msps / 1e3) / 1e12 / v["peak"])
+        keep = ("ms_per_step", "launches", "tflops", "frac_of_peak", "frac_of_measured", "avg_launch_us", "bytes")
+        for d_ in (cl, sa):
+            for v in d_.values():
+                if mpeak:
+                    v["frac_of_measured"] = v["tflops"] / mpeak
         out["kernels"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()
-                              if kk in ("ms_per_step", "launches", "tflops", "frac_of_peak", "frac_of_measured",
-                                        "avg_launch_us", "bytes")}
-                          for k, v in cl.items()}
+                              if kk in keep} for k, v in cl.items()}
+        out["kernels_from"] = (f"library event brackets around each class's launches over {PROF_STEPS} steps after "
+                               f"the timed ones ({prof_ms:.4f} ms per step with the brackets on)")
+        out["kernels_standalone"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                                         for kk, vv in v.items() if kk in keep} for k, v in sa.items()}
         out["hbm_kernels"] = hbm_classes(w, torch, max(args.kernel_reps, 5), machine)
         # the dominant kernel class of the step: the largest time per step in
         # the breakdown (MFMA classes; the HBM-bound kernels above each take

@@ -500,6 +500,25 @@ slt_status slt_softmax_xent_noalloc(void* z, int64_t ldz, const int32_t* tokens,
  * fraction of a measured machine bound)
  * ---------------------------------------------------------------------- */
 
+/* Launch timing by class, for measurement.  slt_timing(1) makes the
+ * whole-step calls bracket every launch of five classes with a pair of HIP
+ * events on the stream that launch runs on (the caller's stream, or the
+ * backward's second stream for the weight gradients): 0 = forward
+ * projections (the QKV, output, MLP and lm_head products, their epilogues
+ * included), 1 = activation gradients dX = dY W, 2 = weight gradients
+ * dW = dY^T X (a grouped launch with its split-K reduction counted as one),
+ * 3 = attention forward, 4 = attention backward (dQ then dK / dV as one).
+ * Element-wise, norm, loss and optimizer kernels are not bracketed.  The
+ * events add gaps between launches, so timed runs keep it off (the default);
+ * results do not depend on it.  slt_timing_read waits for the recorded pairs
+ * and writes, for classes 0 .. nclass-1, the summed milliseconds ms[i] and
+ * the number of launches launches[i] since the previous read, then forgets
+ * them.  Host-global state shared by all threads and devices; SLT_EINVAL for
+ * NULL outputs, SLT_EHIP if an event could not be read (the pairs are
+ * forgotten either way). */
+slt_status slt_timing(int32_t on);
+slt_status slt_timing_read(double* ms, int64_t* launches, int32_t nclass);
+
 /* dst = src over `bytes` bytes (a multiple of 16; both 16-byte aligned, not
  * overlapping) with 16-byte loads and stores: the read + write rate a
  * streaming kernel reaches on this GPU.  variant selects the launch shape

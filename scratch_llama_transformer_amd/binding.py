@@ -100,6 +100,8 @@ SIGNATURES = {
     "slt_gelu_bwd": (_I32, [_P, _P, _P, _I32, _I32, _I64, _I64, _I64, _I32, _P]),
     "slt_softmax_xent": (_I32, [_P, _I64, _P, _I32, _I32, _I64, _I32, _P, _P, _I32, _P, _P]),
     "slt_softmax_xent_noalloc": (_I32, [_P, _I64, _P, _I32, _I32, _I64, _I32, _P, _P, _I32, _P]),
+    "slt_timing": (_I32, [_I32]),
+    "slt_timing_read": (_I32, [_P, _P, _I32]),
     "slt_stream_copy": (_I32, [_P, _P, _I64, _I32, _P]),
     "slt_mfma_loop_flops": (_I64, [_I32, _I32, _I32]),
     "slt_mfma_loop": (_I32, [_I32, _I32, _I32, _P, _P]),
@@ -390,6 +392,22 @@ def slt_softmax_xent(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtype, works
 def slt_softmax_xent_noalloc(z, ldz, tokens, B, T, ld_tokens, V, loss, lse, dtype, stream=None):
     _check("slt_softmax_xent_noalloc", load().slt_softmax_xent_noalloc(_ptr(z), ldz, _ptr(tokens), B, T, ld_tokens, V,
                                                                        _ptr(loss), _ptr(lse), dtype, _stream(stream)))
+
+
+TIMING_CLASSES = ("gemm_fwd", "gemm_dx", "gemm_dw", "attention_fwd", "attention_bwd")
+
+
+def slt_timing(on: bool):
+    _check("slt_timing", load().slt_timing(1 if on else 0))
+
+
+def slt_timing_read():
+    """{class: (milliseconds, launches)} recorded since the previous read."""
+    n = len(TIMING_CLASSES)
+    ms = (ct.c_double * n)()
+    cnt = (ct.c_int64 * n)()
+    _check("slt_timing_read", load().slt_timing_read(ms, cnt, n))
+    return {c: (ms[i], int(cnt[i])) for i, c in enumerate(TIMING_CLASSES)}
 
 
 def slt_stream_copy(src, dst, nbytes, variant=0, stream=None):

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -42,6 +43,70 @@ slt_status check_launch(const char* what) {
   } while (0)
 
 static inline int64_t a256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// ---------------------------------------------------------------------------
+// Launch timing by class (slt_timing / slt_timing_read), for measurement:
+// while it is on, a pair of HIP events brackets every launch of a class on
+// the stream that launch runs on; the pairs are kept until they are read.
+// ---------------------------------------------------------------------------
+enum { TM_FWD = 0, TM_DX = 1, TM_DW = 2, TM_AFWD = 3, TM_ABWD = 4 };
+struct TmRec {
+  int cls;
+  hipEvent_t a, b;
+};
+static std::mutex g_tm_mu;
+static std::atomic<bool> g_tm_on{false};
+static std::vector<TmRec> g_tm_recs;
+static std::vector<hipEvent_t> g_tm_pool;  // events for reuse (kept until the process ends)
+
+static hipEvent_t tm_event() {  // with g_tm_mu held
+  if (!g_tm_pool.empty()) {
+    hipEvent_t e = g_tm_pool.back();
+    g_tm_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return e;
+}
+
+struct Timed {
+  int cls;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(int c, hipStream_t st) : cls(c), s(st) {
+    if (!g_tm_on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lk(g_tm_mu);
+    a = tm_event();
+    b = tm_event();
+    if (!a || !b || hipEventRecord(a, s) != hipSuccess) {
+      (void)hipGetLastError();
+      drop_locked();
+    }
+  }
+  // the bracketed call launched nothing: forget the pair
+  void drop() {
+    if (!a && !b) return;
+    std::lock_guard<std::mutex> lk(g_tm_mu);
+    drop_locked();
+  }
+  void drop_locked() {
+    if (a) g_tm_pool.push_back(a);
+    if (b) g_tm_pool.push_back(b);
+    a = b = nullptr;
+  }
+  ~Timed() {
+    if (!a) return;
+    const bool ok = hipEventRecord(b, s) == hipSuccess;
+    if (!ok) (void)hipGetLastError();
+    std::lock_guard<std::mutex> lk(g_tm_mu);
+    if (ok) g_tm_recs.push_back(TmRec{cls, a, b});
+    else drop_locked();
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Planner
@@ -271,6 +336,7 @@ static slt_status proj(const Ctx& x, int M, int N, int K, const void* X, int64_t
                        int64_t ldy, const void* R, int64_t ldr, Drop drop = {}) {
   GemmArgs g{M, N, K, X, ldx, true, W, (int64_t)K, true, Y, ldy, R, ldr, x.dt, x.dt, nullptr, 0};
   g.drop = drop;
+  Timed tm(TM_FWD, x.s);
   return launch_gemm(g, x.s);
 }
 
@@ -278,6 +344,7 @@ static slt_status proj(const Ctx& x, int M, int N, int K, const void* X, int64_t
 static slt_status proj_dx(const Ctx& x, int M, int N, int K, const void* dY, int64_t lddy, const void* W,
                           int64_t ldw, void* dX, int64_t lddx) {
   GemmArgs g{M, K, N, dY, lddy, true, W, ldw, false, dX, lddx, nullptr, 0, x.dt, x.dt, nullptr, 0};
+  Timed tm(TM_DX, x.s);
   return launch_gemm(g, x.s);
 }
 
@@ -296,11 +363,16 @@ static slt_status proj_dw(const Ctx& x, int M, int N, int K, const void* dY, int
 static slt_status mlp_in(int M, int F, int C, const void* n, const void* w13, char* ab, void* h, int dt,
                          hipStream_t s) {
   if (dt == SLT_BF16) {
+    Timed tm(TM_FWD, s);
     const slt_status st = launch_gemm_swiglu_fwd(M, F, C, n, C, w13, ab, 2 * F, h, F, s);
     if (st != SLT_EUNSUPPORTED) return st;
+    tm.drop();
   }
   GemmArgs g{M, 2 * F, C, n, C, true, w13, C, true, ab, 2 * F, nullptr, 0, dt, dt, nullptr, 0};
-  SLT_TRY(launch_gemm(g, s));
+  {
+    Timed tm(TM_FWD, s);
+    SLT_TRY(launch_gemm(g, s));
+  }
   const int64_t es = dt == SLT_BF16 ? 2 : 4;
   return launch_swiglu_fwd(ab, ab + F * es, h, M, F, 2 * F, 2 * F, F, dt, s);
 }
@@ -309,7 +381,10 @@ static slt_status mlp_in(int M, int F, int C, const void* n, const void* w13, ch
 static slt_status proj_gelu(int M, int N, int K, const void* n, const void* w, char* y, int64_t ldy, int col0,
                             char* u, int64_t ldu, int dt, hipStream_t s) {
   GemmArgs g{M, N, K, n, K, true, w, K, true, y, ldy, nullptr, 0, dt, dt, nullptr, 0};
-  SLT_TRY(launch_gemm(g, s));
+  {
+    Timed tm(TM_FWD, s);
+    SLT_TRY(launch_gemm(g, s));
+  }
   const int64_t es = dt == SLT_BF16 ? 2 : 4;
   return launch_gelu_fwd(y + col0 * es, u, M, N - col0, ldy, ldu, dt, s);
 }
@@ -325,7 +400,10 @@ static bool rope_in_projection(const Plan& p) { return flash_eligible(p.c.act, p
 static slt_status rope_proj(int M, int N, int K, const void* n, const void* w, char* y, int64_t ldy, int T, int H,
                             int Hkv, int d, int R, int mode, const float* cs, int dt, hipStream_t s) {
   GemmArgs g{M, N, K, n, K, true, w, K, true, y, ldy, nullptr, 0, dt, dt, nullptr, 0};
-  if (R == 0) return launch_gemm(g, s);
+  if (R == 0) {
+    Timed tm(TM_FWD, s);
+    return launch_gemm(g, s);
+  }
   RopeEpi r;
   r.cs = cs;
   r.T = T;
@@ -333,9 +411,16 @@ static slt_status rope_proj(int M, int N, int K, const void* n, const void* w, c
   r.R = R;
   r.end = (H + Hkv) * d;
   r.half = mode == SLT_ROPE_HALF;
-  const slt_status st = launch_gemm_rope(g, r, s);
-  if (st != SLT_EUNSUPPORTED) return st;
-  SLT_TRY(launch_gemm(g, s));
+  {
+    Timed tm(TM_FWD, s);
+    const slt_status st = launch_gemm_rope(g, r, s);
+    if (st != SLT_EUNSUPPORTED) return st;
+    tm.drop();
+  }
+  {
+    Timed tm(TM_FWD, s);
+    SLT_TRY(launch_gemm(g, s));
+  }
   const int64_t es = dt == SLT_BF16 ? 2 : 4;
   SLT_TRY(launch_rope(y, ldy, y, ldy, M, T, H, d, R, mode, cs, 1.0f, dt, s));
   return launch_rope(y + (int64_t)H * d * es, ldy, y + (int64_t)H * d * es, ldy, M, T, Hkv, d, R, mode, cs, 1.0f,
@@ -352,7 +437,10 @@ static slt_status proj_rope(const Plan& p, const Ctx& x, int M, int N, int K, co
 static slt_status mlp_in_bwd(int M, int F, int C, const void* dy, const void* w2, const char* ab, char* dab,
                              void* dh_buf, int dt, hipStream_t s) {
   GemmArgs g{M, F, C, dy, C, true, w2, F, false, dh_buf, F, nullptr, 0, dt, dt, nullptr, 0};
-  SLT_TRY(launch_gemm(g, s));
+  {
+    Timed tm(TM_DX, s);
+    SLT_TRY(launch_gemm(g, s));
+  }
   const int64_t es = dt == SLT_BF16 ? 2 : 4;
   return launch_swiglu_bwd(ab, ab + F * es, dh_buf, dab, dab + F * es, M, F, 2 * F, 2 * F, F, 2 * F, 2 * F, dt, s);
 }
@@ -379,6 +467,7 @@ struct DwList {
 };
 
 static slt_status flush_dw(const Ctx& x, DwList& L) {
+  Timed tm(TM_DW, x.s);
   bool group = x.dt == SLT_BF16 && L.n > 1;
   GroupItem g[6];
   for (int i = 0; i < L.n && group; ++i) {
@@ -432,7 +521,10 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
       at.ldq = at.ldk = at.ldv = p.qkv_w;
       at.out = x.A(A.o); at.ldo = p.qd;
-      SLT_TRY(launch_attention_fwd(at, x.s));
+      {
+        Timed tm(TM_AFWD, x.s);
+        SLT_TRY(launch_attention_fwd(at, x.s));
+      }
       SLT_TRY(proj(x, N, C, p.qd, x.A(A.o), p.qd, x.P(W.wo), xmid, C, xin, C, make_drop(c, 1, l)));
       SLT_TRY(launch_rmsnorm_fwd(xmid, x.P(W.norm2), x.A(A.n2), (float*)x.A(A.r2), N, C, c.eps, x.dt, x.s));
       SLT_TRY(mlp_in(N, c.F, C, x.A(A.n2), x.P(W.w1), (char*)x.A(A.ab), x.A(A.h), x.dt, x.s));
@@ -456,7 +548,10 @@ static slt_status forward(const Plan& p, const Ctx& x, const int32_t* tok, float
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
       at.ldq = at.ldk = at.ldv = p.in_w;
       at.out = ou; at.ldo = p.ou_w;
-      SLT_TRY(launch_attention_fwd(at, x.s));
+      {
+        Timed tm(TM_AFWD, x.s);
+        SLT_TRY(launch_attention_fwd(at, x.s));
+      }
       SLT_TRY(proj(x, N, C, p.ou_w, ou, p.ou_w, x.P(W.wout), xout, C, xin, C, make_drop(c, 1, l)));
     }
   }
@@ -697,7 +792,10 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       at.dout = dmid; at.lddo = p.qd;
       at.dq = dqkv; at.dk = dqkv + p.qd * p.es; at.dv = dqkv + (p.qd + p.kd) * p.es;
       at.lddq = at.lddk = at.lddv = p.qkv_w;
-      SLT_TRY(launch_attention_bwd(at, x.s));
+      {
+        Timed tm(TM_ABWD, x.s);
+        SLT_TRY(launch_attention_bwd(at, x.s));
+      }
       dws.add(N, p.qkv_w, C, dqkv, p.qkv_w, x.A(A.n1), C, grads + W.qkvw, C);
       SLT_TRY(launch_dw(sl));
       if (l == c.L - 1) SLT_TRY(side_adam(p.normf, p.n_params));  // final norm and lm_head are final
@@ -728,7 +826,10 @@ static slt_status backward(const Plan& p, const Ctx& x, const int32_t* tok, floa
       at.dout = dmid; at.lddo = p.ou_w;
       at.dq = dbig; at.dk = dbig + p.qd * p.es; at.dv = dbig + (p.qd + p.kd) * p.es;
       at.lddq = at.lddk = at.lddv = p.in_w;
-      SLT_TRY(launch_attention_bwd(at, x.s));
+      {
+        Timed tm(TM_ABWD, x.s);
+        SLT_TRY(launch_attention_bwd(at, x.s));
+      }
       dws.add(N, p.in_w, C, dbig, p.in_w, x.A(A.n1), C, grads + W.qkvw, C);
       SLT_TRY(launch_dw(sl));
       if (l == c.L - 1) SLT_TRY(side_adam(p.normf, p.n_params));  // final norm and lm_head are final
@@ -848,7 +949,10 @@ static slt_status forward_cached(const Plan& p, const Ctx& x, const CachePlan& q
       at.q = qkv; at.k = qkv + p.qd * p.es; at.v = qkv + (p.qd + p.kd) * p.es;
       at.ldq = at.ldk = at.ldv = ldqkv;
       at.out = ou; at.ldo = ldo;
-      SLT_TRY(launch_attention_fwd(at, x.s));
+      {
+        Timed tm(TM_AFWD, x.s);
+        SLT_TRY(launch_attention_fwd(at, x.s));
+      }
     } else {
       SLT_TRY(launch_attention_decode((const float*)x.A(q.qrot), Kc, Vc, ou, ldo, B, Tq, pos0, c.H, c.Hkv, p.d, Tmax,
                                       x.dt, (float*)x.A(q.part), x.s));
@@ -882,6 +986,36 @@ using namespace slt;
 // Exported entry points
 // ---------------------------------------------------------------------------
 extern "C" {
+
+slt_status slt_timing(int32_t on) {
+  g_tm_on.store(on != 0);
+  return SLT_OK;
+}
+
+slt_status slt_timing_read(double* ms, int64_t* launches, int32_t nclass) {
+  if (!ms || !launches || nclass < 0) return fail(SLT_EINVAL, "timing_read: NULL output or negative class count");
+  for (int i = 0; i < nclass; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  std::lock_guard<std::mutex> lk(g_tm_mu);
+  hipError_t err = hipSuccess;
+  for (const TmRec& r : g_tm_recs) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    if (e == hipSuccess && r.cls < nclass) {
+      ms[r.cls] += t;
+      launches[r.cls] += 1;
+    }
+    g_tm_pool.push_back(r.a);
+    g_tm_pool.push_back(r.b);
+  }
+  g_tm_recs.clear();
+  if (err != hipSuccess) return fail(SLT_EHIP, std::string("timing_read: ") + hipGetErrorString(err));
+  return SLT_OK;
+}
 
 const char* slt_last_error(void) { return g_err.c_str(); }
 

@@ -407,3 +407,40 @@ def test_full_size_zero_head_properties(TS, ci):
     expect = theta0 - w.lr * (w.wd * theta0)
     diff = (ts.master - expect)[body].abs()
     assert float(diff.max()) <= 2 * 2 ** -23 * float(theta0[body].abs().max())
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("ci,over", [(3, dict(B=4, L=2)), (5, dict(B=1, L=2, T=256)), (2, dict(B=2, L=2))])
+def test_launch_timing_counts_and_leaves_results_unchanged(TS, ci, over):
+    """slt_timing brackets every launch of the five classes in a step (the
+    counts the step's structure fixes: one weight-gradient bracket per layer,
+    around the layer's grouped launch or its separate fp32 products; every
+    class's time positive), and a step with it on gives bitwise the
+    gradients and weights of one with it off."""
+    from scratch_llama_transformer_amd import binding as B
+    w = W.get_config(ci).with_(**over)
+    say("launch timing", w)
+    params = W.make_params(w, 11)
+    tok = torch.from_numpy(W.make_tokens(w, 11)).cuda()
+    outs = []
+    B.slt_timing_read()  # forget earlier records
+    for on in (False, True):
+        ts = TS(w, params=params)
+        B.slt_timing(on)
+        try:
+            ts.step(tok)
+            torch.cuda.synchronize()
+        finally:
+            B.slt_timing(False)
+        outs.append((ts.grads.clone(), ts.master.clone()))
+        rec = B.slt_timing_read()
+        if not on:
+            assert all(n == 0 for _, n in rec.values()), rec
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    per = 4 if w.block == "llama" else 2  # projections per layer
+    want = {"gemm_fwd": per * w.L + 1, "gemm_dx": per * w.L + 1, "gemm_dw": w.L, "attention_fwd": w.L,
+            "attention_bwd": w.L}
+    for k, n in want.items():
+        ms, got = rec[k]
+        assert got == n, (k, got, n)
+        assert ms > 0, (k, ms)
