@@ -135,7 +135,7 @@ def test_host_calls_reject_bad_arguments_before_launch():
     assert lib.slt_qkv_rope_fwd(4, 16, 8, None, None, None, 16, 4, 2, 2, 8, 8, 0, None, 1, None) == 1
     assert lib.slt_qkv_rope_fwd(4, 64, 8, None, None, None, 64, 4, 2, 2, 8, 7, 0, None, 1, None) == 1
     # machine-bound kernels: bad variant, size not a multiple of 16, NULL
-    assert lib.slt_stream_copy(None, None, 32, 4, None) == 1
+    assert lib.slt_stream_copy(None, None, 32, 5, None) == 1
     assert lib.slt_stream_copy(None, None, 24, 0, None) == 1
     assert lib.slt_stream_copy(None, None, 32, 0, None) == 1
     assert lib.slt_stream_copy(None, None, 0, 0, None) == 0
@@ -144,6 +144,13 @@ def test_host_calls_reject_bad_arguments_before_launch():
     assert B.slt_mfma_loop_flops(8, 4, 0) == 8 * 4 * 4 * 8 * 16384
     assert B.slt_mfma_loop_flops(8, 4, 1) == 8 * 4 * 4 * 8 * 32768
     assert B.slt_mfma_loop_flops(8, 4, 2) == 8 * 4 * 4 * 16 * 16384
+    # launch timing: NULL outputs or a negative class count are rejected; with
+    # nothing recorded every class reads zero
+    assert lib.slt_timing_read(None, None, 5) == 1
+    ms, cnt = (ct.c_double * 5)(), (ct.c_int64 * 5)()
+    assert lib.slt_timing_read(ms, cnt, -1) == 1
+    assert lib.slt_timing(0) == 0
+    assert B.slt_timing_read() == {c: (0.0, 0) for c in B.TIMING_CLASSES}
 
 
 def test_kv_cache_sizes():
