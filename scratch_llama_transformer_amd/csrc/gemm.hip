@@ -67,6 +67,9 @@
 #ifndef SLT_GEMM_XCD
 #define SLT_GEMM_XCD 1
 #endif
+#ifndef SLT_ROPE_PRELOAD
+#define SLT_ROPE_PRELOAD 1  // the 64-deep kernel loads its RoPE table entries before the k-loop
+#endif
 
 namespace slt {
 namespace {
@@ -637,6 +640,44 @@ __device__ __forceinline__ void rope_rotate_acc(const KArgs& a, f32x4 (&acc)[FM]
       }
     }
   }
+}
+
+// The same rotation with the table entries loaded ahead (rope_load_cs, before
+// the k-loop, so that their latency overlaps it): cs[i][j] holds the
+// (cos, sin) pairs of fragment (i, j), unused where no pair is rotated.
+template <int FM, int FN>
+__device__ __forceinline__ void rope_load_cs(const KArgs& a, float4 (&cs)[FM][FN], int m0, int n0, int wm, int wn,
+                                             int lane) {
+  const RopeEpi& r = a.rope;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = min(m0 + wm * 16 * FM + i * 16 + (lane & 15), a.M - 1);
+    const float* tb = r.cs + (int64_t)(m % r.T) * r.R;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * 16 * FN + j * 16 + 4 * (lane >> 4);
+      const int c = n % r.d;
+      cs[i][j] = (n < r.end && c < r.R) ? *reinterpret_cast<const float4*>(tb + c) : make_float4(1.f, 0.f, 1.f, 0.f);
+    }
+  }
+}
+template <int FM, int FN>
+__device__ __forceinline__ void rope_rotate_pre(const KArgs& a, f32x4 (&acc)[FM][FN], const float4 (&cs)[FM][FN],
+                                                int n0, int wn, int lane) {
+  const RopeEpi& r = a.rope;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * 16 * FN + j * 16 + 4 * (lane >> 4);
+      const int c = n % r.d;
+      if (n < r.end && c < r.R) {
+        const float4 t = cs[i][j];
+        const f32x4 v = acc[i][j];
+        acc[i][j] = f32x4{v[0] * t.x - v[1] * t.y, v[0] * t.y + v[1] * t.x, v[2] * t.z - v[3] * t.w,
+                          v[2] * t.w + v[3] * t.z};
+      }
+    }
 }
 
 // Block epilogue: lane holds C[m][n .. n+3] of each 16 x 16 fragment; split-K
@@ -1283,6 +1324,8 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
   }
   d64_issue<FA>(A, a.lda, a.M, m0, kbeg, A0, wave, lane);
   d64_issue<FB, RP>(B, a.ldb, a.N, n0, kbeg, B0, wave, lane, brow);
+  float4 csv[RP && SLT_ROPE_PRELOAD ? FM : 1][RP && SLT_ROPE_PRELOAD ? FN : 1];
+  if constexpr (RP && SLT_ROPE_PRELOAD) rope_load_cs<FM, FN>(a, csv, m0, n0, wm, wn, lane);
   for (int it = 0; it < nk; ++it) {
     SLT_WAIT_VMCNT(0);  // this wave's copies of tile it have landed
     lds_barrier();      // ... everyone's have, and the other stage is free
@@ -1306,7 +1349,8 @@ __global__ __launch_bounds__(NT) void gemm_d64_k(KArgs a) {
     }
   }
   SLT_WAIT_VMCNT(0);  // no copy may land after the block ends
-  if constexpr (RP) rope_rotate_acc<FM, FN>(a, acc, m0, n0, wm, wn, lane);
+  if constexpr (RP && SLT_ROPE_PRELOAD) rope_rotate_pre<FM, FN>(a, acc, csv, n0, wn, lane);
+  else if constexpr (RP) rope_rotate_acc<FM, FN>(a, acc, m0, n0, wm, wn, lane);
   if constexpr (ST && !SPLIT) d64_epilogue_staged<TO, LAY, RP>(a, acc, m0, n0, wm, wn, lane, reinterpret_cast<float*>(smem));
   else dl_epilogue<TO, SPLIT, FM, FN, RP>(a, acc, m0, n0, wm, wn, lane);
 }
