@@ -571,6 +571,9 @@ def main():
         cl = {}
         for k, v in sa.items():
             ms_tot, n = in_step[k]
+            if n == 0 or ms_tot <= 0:  # no bracketed launch of the class: keep the standalone figures
+                cl[k] = dict(v)
+                continue
             msps = ms_tot / PROF_STEPS
             cl[k] = dict(v, ms_per_step=msps, launches=n // PROF_STEPS, avg_launch_us=ms_tot * 1e3 / max(n, 1),
                          tflops=v["flops"] / (msps / 1e3) / 1e12,
