@@ -1002,10 +1002,8 @@ __device__ __forceinline__ void w8_epilogue_staged(const KArgs& a, const f32x4 (
             const int n = n0 + cl, c = n % a.rope.d;
             if (a.rope.half && n < a.rope.end && c < a.rope.R) {
               const int lo = n - c + (c >> 1) - n0, hi = lo + (a.rope.R >> 1);
-              F[rl * W8_CS + lo] = v[0];
-              F[rl * W8_CS + lo + 1] = v[2];
-              F[rl * W8_CS + hi] = v[1];
-              F[rl * W8_CS + hi + 1] = v[3];
+              *reinterpret_cast<float2*>(F + rl * W8_CS + lo) = make_float2(v[0], v[2]);
+              *reinterpret_cast<float2*>(F + rl * W8_CS + hi) = make_float2(v[1], v[3]);
               continue;
             }
           }
@@ -1242,10 +1240,10 @@ __device__ __forceinline__ void d64_epilogue_staged(const KArgs& a, const f32x4 
             const int n = n0 + cl, c = n % a.rope.d;
             if (a.rope.half && n < a.rope.end && c < a.rope.R) {
               const int lo = n - c + (c >> 1) - n0, hi = lo + (a.rope.R >> 1);
-              F[rl * CS + lo] = v[0];
-              F[rl * CS + lo + 1] = v[2];
-              F[rl * CS + hi] = v[1];
-              F[rl * CS + hi + 1] = v[3];
+              // lo and hi are even (head starts, R / 2 and the tile origin
+              // are), so each pair is one 8-byte store
+              *reinterpret_cast<float2*>(F + rl * CS + lo) = make_float2(v[0], v[2]);
+              *reinterpret_cast<float2*>(F + rl * CS + hi) = make_float2(v[1], v[3]);
               continue;
             }
           }
