@@ -1002,8 +1002,12 @@ __device__ __forceinline__ void w8_epilogue_staged(const KArgs& a, const f32x4 (
             const int n = n0 + cl, c = n % a.rope.d;
             if (a.rope.half && n < a.rope.end && c < a.rope.R) {
               const int lo = n - c + (c >> 1) - n0, hi = lo + (a.rope.R >> 1);
-              *reinterpret_cast<float2*>(F + rl * W8_CS + lo) = make_float2(v[0], v[2]);
-              *reinterpret_cast<float2*>(F + rl * W8_CS + hi) = make_float2(v[1], v[3]);
+              // four 4-byte stores: 8-byte pair stores push this kernel past
+              // 256 VGPRs into scratch spills
+              F[rl * W8_CS + lo] = v[0];
+              F[rl * W8_CS + lo + 1] = v[2];
+              F[rl * W8_CS + hi] = v[1];
+              F[rl * W8_CS + hi + 1] = v[3];
               continue;
             }
           }
